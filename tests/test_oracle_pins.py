@@ -1,0 +1,457 @@
+"""Pins of the oracle against facts fixed by the pages and by mathematics (CPU only).
+
+Each test checks a property that a plausible mistake in the oracle would break:
+a dropped term, a wrong sign, index or axis, a transposed operand, a wrong
+pairing of RoPE dimensions, a wrong GQA mapping, a wrong tie-break.  None of them
+re-types the oracle's own formula.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import backbone as O
+
+RNG = np.random.default_rng(1234)
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def small_dims(**kw):
+    d = dict(hidden=64, n_heads=4, n_kv_heads=2, head_dim=16, ffn=96, eps=1e-6, theta=1e6)
+    d.update(kw)
+    return O.Dims(**d)
+
+
+def rand_layer(dims, rng, std=0.2, zero=()):
+    hd, H, Hk = dims.head_dim, dims.n_heads, dims.n_kv_heads
+    shapes = dict(attn_norm=(dims.hidden,), wq=(H * hd, dims.hidden), wk=(Hk * hd, dims.hidden),
+                  wv=(Hk * hd, dims.hidden), q_norm=(hd,), k_norm=(hd,), wo=(dims.hidden, H * hd),
+                  ffn_norm=(dims.hidden,), w_gate=(dims.ffn, dims.hidden),
+                  w_up=(dims.ffn, dims.hidden), w_down=(dims.hidden, dims.ffn))
+    a = {}
+    for k, s in shapes.items():
+        if len(s) == 1:
+            a[k] = 1.0 + 0.1 * rng.standard_normal(s)
+        else:
+            a[k] = std * rng.standard_normal(s)
+        if k in zero:
+            a[k] = np.zeros(s)
+    return O.Layer.from_arrays(a)
+
+
+# ---------------------------------------------------------------------------
+# Hyper-parameters: the pages' printed values
+# ---------------------------------------------------------------------------
+
+def read_golden(name):
+    vals = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                k, v = line.split("=", 1)
+                vals[k.strip()] = v.strip()
+    return vals
+
+
+def test_hparams_match_pages():
+    from workload import configs as C
+    g = read_golden("backbone_hparams.txt")
+    s = C.Shape()
+    assert s.n_layers == int(g["block_count"])
+    assert s.hidden == int(g["embedding_length"])
+    assert s.ffn == int(g["feed_forward_length"])
+    assert s.n_heads == int(g["head_count"])
+    assert s.n_kv_heads == int(g["head_count_kv"])
+    assert s.head_dim == int(g["key_length"])
+    assert s.eps == float(g["layer_norm_rms_eps"])
+    assert s.theta == float(g["rope_freq_base"])
+    w = C.c4().extra
+    assert w["n_cb"] == int(g["num_audio_codebook"])
+    assert w["cb_vocab"] == int(g["audio_vocab_size"])
+    assert w["mask_id"] == int(g["audio_mask_id"])
+    assert w["text_vocab"] == int(g["vocab_size"])
+    assert w["layer_penalty"] == float(g["layer_penalty_factor"])
+    assert w["n_steps"] == int(g["num_step"])
+    assert C.c3().shape.n_layers == int(g["code_predictor_layers"])
+    assert C.c3().extra["steps"] == int(g["code_predictor_steps"])
+    assert C.c2().extra["n_cb"] == int(g["talker_codebooks"])
+    assert C.c2().extra["head_vocab"] == int(g["talker_head_vocab"])
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm
+# ---------------------------------------------------------------------------
+
+def test_rmsnorm_unit_rms_before_gain():
+    x = RNG.standard_normal((5, 1024)) * 3.0
+    y = O.rms_norm(x, np.ones(1024), 1e-6)
+    ms = np.mean(x * x, axis=-1)
+    # exact: rms(y) = sqrt(ms / (ms + eps)); for ms ~ 9 this is 1 - 5.6e-8
+    np.testing.assert_allclose(np.sqrt(np.mean(y * y, axis=-1)), np.sqrt(ms / (ms + 1e-6)),
+                               rtol=1e-13)
+    np.testing.assert_allclose(np.sqrt(np.mean(y * y, axis=-1)), 1.0, atol=1e-7)
+
+
+def test_rmsnorm_constant_vector_eps_inside_root():
+    # c * 1 maps to c / sqrt(c^2 + eps); at c = 1e-3 and eps = 1e-6 that is 1/sqrt(2)
+    for c in (1e-3, 0.5, -2.0):
+        y = O.rms_norm(np.full(16, c), np.ones(16), 1e-6)
+        np.testing.assert_allclose(y, c / math.sqrt(c * c + 1e-6), rtol=1e-14)
+    y = O.rms_norm(np.full(16, 1e-3), np.ones(16), 1e-6)
+    np.testing.assert_allclose(y, 1.0 / math.sqrt(2.0), rtol=1e-14)
+
+
+def test_rmsnorm_scale_invariance_and_gain():
+    x = RNG.standard_normal(128)
+    g = 1.0 + 0.3 * RNG.standard_normal(128)
+    y1 = O.rms_norm(x, g, 1e-6)
+    y2 = O.rms_norm(37.0 * x, g, 1e-6)
+    np.testing.assert_allclose(y1, y2, rtol=1e-6)
+    np.testing.assert_allclose(O.rms_norm(x, g, 1e-6), O.rms_norm(x, np.ones(128), 1e-6) * g,
+                               rtol=1e-15)
+    # normalisation is per row (last axis), not over the whole array
+    X = np.stack([x, 10 * x])
+    Y = O.rms_norm(X, np.ones(128), 0.0)
+    np.testing.assert_allclose(Y[0], Y[1], rtol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# RoPE
+# ---------------------------------------------------------------------------
+
+def test_rope_position_zero_is_identity():
+    u = RNG.standard_normal((3, 128))
+    np.testing.assert_array_equal(O.rope(u, 0, 1e6), u)
+
+
+def test_rope_preserves_pair_norms():
+    u = RNG.standard_normal(128)
+    r = O.rope(u, 4321, 1e6)
+    np.testing.assert_allclose(u[:64] ** 2 + u[64:] ** 2, r[:64] ** 2 + r[64:] ** 2, rtol=1e-12)
+
+
+def test_rope_pairs_dim_j_with_j_plus_half():
+    # a unit vector on dimension 0 rotates into dimension 64 (rotate-half), never into 1
+    e0 = np.zeros(128)
+    e0[0] = 1.0
+    r = O.rope(e0, 1.0, 1e6)
+    np.testing.assert_allclose(r[0], math.cos(1.0), rtol=1e-15)
+    np.testing.assert_allclose(r[64], math.sin(1.0), rtol=1e-15)
+    assert np.count_nonzero(r) == 2
+    e64 = np.zeros(128)
+    e64[64] = 1.0
+    r = O.rope(e64, 1.0, 1e6)
+    np.testing.assert_allclose(r[0], -math.sin(1.0), rtol=1e-15)
+    np.testing.assert_allclose(r[64], math.cos(1.0), rtol=1e-15)
+
+
+def test_rope_frequencies_closed_form():
+    # pair j rotates by p * theta^(-2j/128): j=0 -> p rad, j=32 -> p/1000 at theta=1e6,
+    # j=16 -> p * 1e6^(-1/4) = p / 31.6227766...
+    p = 777.0
+    for j, w in ((0, 1.0), (32, 1e-3), (16, 1.0 / 31.622776601683793)):
+        e = np.zeros(128)
+        e[j] = 1.0
+        r = O.rope(e, p, 1e6)
+        np.testing.assert_allclose([r[j], r[j + 64]], [math.cos(p * w), math.sin(p * w)],
+                                   rtol=1e-12, atol=1e-13)
+
+
+def test_rope_relative_position_identity():
+    q = RNG.standard_normal(128)
+    k = RNG.standard_normal(128)
+    for p, pp in ((10, 3), (4000, 3999), (57, 200)):
+        lhs = O.rope(q, p, 1e6) @ O.rope(k, pp, 1e6)
+        rhs = O.rope(q, p - pp, 1e6) @ k
+        np.testing.assert_allclose(lhs, rhs, rtol=1e-9, atol=1e-10)
+
+
+# ---------------------------------------------------------------------------
+# Attention
+# ---------------------------------------------------------------------------
+
+def test_attention_brute_force_tiny():
+    # H=2 query heads sharing H_kv=1 head, d=4, L=3; softmax written out with loops
+    q = RNG.standard_normal((2, 4))
+    K = RNG.standard_normal((3, 1, 4))
+    V = RNG.standard_normal((3, 1, 4))
+    o = O.attend(q, K, V)
+    for h in range(2):
+        s = []
+        for j in range(3):
+            acc = 0.0
+            for i in range(4):
+                acc += q[h, i] * K[j, 0, i]
+            s.append(acc / 2.0)
+        w = [math.exp(v) for v in s]
+        z = sum(w)
+        for i in range(4):
+            ref = sum(w[j] / z * V[j, 0, i] for j in range(3))
+            assert abs(o[h, i] - ref) < 1e-14
+
+
+def test_attention_two_keys_is_logistic():
+    q = RNG.standard_normal((1, 8))
+    K = RNG.standard_normal((2, 1, 8))
+    V = RNG.standard_normal((2, 1, 8))
+    s0 = q[0] @ K[0, 0] / math.sqrt(8)
+    s1 = q[0] @ K[1, 0] / math.sqrt(8)
+    a = 1.0 / (1.0 + math.exp(-(s0 - s1)))
+    np.testing.assert_allclose(O.attend(q, K, V)[0], a * V[0, 0] + (1 - a) * V[1, 0], rtol=1e-13)
+
+
+def test_attention_degenerate_cases():
+    q = RNG.standard_normal((4, 16))
+    V = RNG.standard_normal((5, 2, 16))
+    # L = 1: output is v
+    K1 = RNG.standard_normal((1, 2, 16))
+    o = O.attend(q, K1, V[:1])
+    np.testing.assert_allclose(o, V[0, [0, 0, 1, 1]], rtol=1e-15)
+    # identical keys: mean of V
+    Kid = np.repeat(RNG.standard_normal((1, 2, 16)), 5, axis=0)
+    o = O.attend(q, Kid, V)
+    np.testing.assert_allclose(o, V.mean(axis=0)[[0, 0, 1, 1]], rtol=1e-12)
+    # q = 0: mean of V
+    o = O.attend(np.zeros((4, 16)), RNG.standard_normal((5, 2, 16)), V)
+    np.testing.assert_allclose(o, V.mean(axis=0)[[0, 0, 1, 1]], rtol=1e-12)
+
+
+def test_gqa_equals_mha_with_duplicated_kv():
+    q = RNG.standard_normal((16, 128))
+    K = RNG.standard_normal((9, 8, 128))
+    V = RNG.standard_normal((9, 8, 128))
+    gqa = O.attend(q, K, V)
+    idx = np.arange(16) // 2  # consecutive grouping: heads 2i, 2i+1 read KV head i
+    mha = O.attend(q, K[:, idx, :], V[:, idx, :])
+    np.testing.assert_allclose(gqa, mha, rtol=1e-14)
+    # and per head it is single-head attention on the right KV head
+    for h in (0, 1, 7, 15):
+        one = O.attend(q[h:h + 1], K[:, h // 2:h // 2 + 1], V[:, h // 2:h // 2 + 1])
+        np.testing.assert_allclose(gqa[h], one[0], rtol=1e-14)
+
+
+def test_causal_prefix_unchanged_by_appended_tokens():
+    S, H, Hk, d = 7, 4, 2, 16
+    Q = RNG.standard_normal((S + 3, H, d))
+    K = RNG.standard_normal((S + 3, Hk, d))
+    V = RNG.standard_normal((S + 3, Hk, d))
+    a = O.attention_full(Q[:S], K[:S], V[:S], causal=True)
+    b = O.attention_full(Q, K, V, causal=True)
+    np.testing.assert_allclose(a, b[:S], rtol=1e-14)
+    # while bidirectional attention of the prefix does change
+    c = O.attention_full(Q, K, V, causal=False)
+    assert np.max(np.abs(c[:S] - a)) > 1e-3
+
+
+# ---------------------------------------------------------------------------
+# Whole layer: decode = recompute, bidirectional dependence, special cases
+# ---------------------------------------------------------------------------
+
+def test_decode_steps_equal_causal_recompute():
+    dims = small_dims()
+    rng = np.random.default_rng(5)
+    layers = [rand_layer(dims, rng) for _ in range(2)]
+    S = 6
+    X = rng.standard_normal((S, dims.hidden))
+    full = O.backbone_full(X, layers, dims, causal=True)
+    cache = O.KVCache(2, 1)
+    for p in range(S):
+        out = O.decode_step(X[p:p + 1], [p], cache, layers, dims)
+        np.testing.assert_allclose(out[0], full[p], rtol=1e-11, atol=1e-12)
+
+
+def test_decode_batch_streams_are_independent():
+    dims = small_dims()
+    rng = np.random.default_rng(6)
+    layers = [rand_layer(dims, rng)]
+    X = rng.standard_normal((3, dims.hidden))
+    cache = O.KVCache(1, 3)
+    pre = [rng.standard_normal((n, 2, dims.n_kv_heads, dims.head_dim)) for n in (2, 5, 0)]
+    for b, p in enumerate(pre):
+        if p.shape[0]:
+            cache.set(0, b, p[:, 0], p[:, 1])
+    out = O.decode_step(X, [2, 5, 0], cache, layers, dims)
+    for b, p in enumerate(pre):
+        c1 = O.KVCache(1, 1)
+        if p.shape[0]:
+            c1.set(0, 0, p[:, 0], p[:, 1])
+        one = O.decode_step(X[b:b + 1], [p.shape[0]], c1, layers, dims)
+        np.testing.assert_allclose(out[b], one[0], rtol=1e-12, atol=1e-13)
+
+
+def test_maskgit_attention_is_bidirectional():
+    dims = small_dims()
+    rng = np.random.default_rng(7)
+    layers = [rand_layer(dims, rng)]
+    X = rng.standard_normal((5, dims.hidden))
+    Y = X.copy()
+    Y[-1] += 1.0
+    a = O.backbone_full(X, layers, dims, causal=False)
+    b = O.backbone_full(Y, layers, dims, causal=False)
+    assert np.max(np.abs(a[0] - b[0])) > 1e-4  # the last token reaches position 0
+    a = O.backbone_full(X, layers, dims, causal=True)
+    b = O.backbone_full(Y, layers, dims, causal=True)
+    np.testing.assert_array_equal(a[0], b[0])
+
+
+def test_first_token_layer_closed_form():
+    # At position 0 with an empty cache: RoPE is the identity and softmax over one key
+    # is 1, so o_h = v_{h//2}; with W_down = 0 the layer is x + W_o [v_0, v_0, v_1, ...].
+    dims = small_dims()
+    rng = np.random.default_rng(8)
+    L = rand_layer(dims, rng, zero=("w_down",))
+    x = rng.standard_normal((1, dims.hidden))
+    out = O.decode_step(x, [0], O.KVCache(1, 1), [L], dims)
+    h = x[0] / math.sqrt(np.mean(x[0] ** 2) + dims.eps) * L.attn_norm
+    v = (L.wv @ h).reshape(dims.n_kv_heads, dims.head_dim)
+    o = np.concatenate([v[hq // 2] for hq in range(dims.n_heads)])
+    np.testing.assert_allclose(out[0], x[0] + L.wo @ o, rtol=1e-12, atol=1e-13)
+
+
+def test_swiglu_special_cases():
+    assert O.silu(0.0) == 0.0
+    np.testing.assert_allclose(O.silu(1.0), 0.7310585786300049, rtol=1e-15)  # 1/(1+e^-1)
+    np.testing.assert_allclose(O.silu(-1.0), -0.2689414213699951, rtol=1e-15)
+    np.testing.assert_allclose(O.silu(40.0), 40.0, rtol=1e-15)
+    dims = small_dims()
+    rng = np.random.default_rng(9)
+    # W_gate = 0 -> silu(0) = 0 -> MLP contributes nothing: x2 = x1
+    L = rand_layer(dims, rng, zero=("w_gate",))
+    x = rng.standard_normal((2, dims.hidden))
+    o = rng.standard_normal((2, dims.n_heads, dims.head_dim))
+    post = O.post_attention(x, o, L, dims)
+    np.testing.assert_array_equal(post["x2"], post["x1"])
+    # W_o = 0 -> x1 = x
+    L = rand_layer(dims, rng, zero=("wo",))
+    post = O.post_attention(x, o, L, dims)
+    np.testing.assert_array_equal(post["x1"], x)
+    # gate and up are not swapped: with W_up = 0 the MLP is zero, with a one-hot gate
+    # and up the MLP output is silu(g) * u through W_down
+    L = rand_layer(dims, rng)
+    L.w_gate[:] = 0.0
+    L.w_up[:] = 0.0
+    L.w_gate[0, 0] = 1.0
+    L.w_up[0, 1] = 1.0
+    L.w_down[:] = 0.0
+    L.w_down[3, 0] = 1.0
+    post = O.post_attention(x, o, L, dims)
+    h2 = post["h2"]
+    np.testing.assert_allclose(post["x2"][:, 3] - post["x1"][:, 3],
+                               h2[:, 0] / (1 + np.exp(-h2[:, 0])) * h2[:, 1], rtol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# Embedding
+# ---------------------------------------------------------------------------
+
+def test_codebook_embed_sums_offset_rows():
+    V, K, D = 5, 3, 4
+    table = RNG.standard_normal((K * V, D))
+    codes = np.array([[0, 4, 2], [3, 3, 3]])
+    e = O.codebook_embed(codes, table, V)
+    np.testing.assert_array_equal(e[0], table[0] + table[1 * 5 + 4] + table[2 * 5 + 2])
+    np.testing.assert_array_equal(e[1], table[3] + table[8] + table[13])
+    # K = 1 is a plain lookup
+    np.testing.assert_array_equal(O.codebook_embed(codes[:, :1], table, V), table[[0, 3]])
+
+
+def test_codebook_embed_bf16_sum_is_exact_in_fp64():
+    from workload import gen
+    vals = gen.round_bf16(RNG.standard_normal((16, 64)).astype(np.float32) * 0.02)
+    codes = np.arange(16)[None, :] * 0  # code 0 of each of 16 codebooks
+    table = np.zeros((16 * 2, 64), np.float32)
+    table[np.arange(16) * 2] = vals
+    e = O.codebook_embed(codes, table, 2)
+    # Python's math.fsum is the correctly rounded sum
+    for j in range(64):
+        assert e[0, j] == math.fsum(float(v) for v in vals[:, j])
+
+
+def test_hybrid_embed_text_then_audio_with_mask_row():
+    V, K, D = 4, 2, 3
+    audio = RNG.standard_normal((K * V, D))
+    text = RNG.standard_normal((10, D))
+    codes_kt = np.array([[1, 3], [3, 0]])  # [K][T]; id 3 plays the mask id
+    e = O.hybrid_embed(np.array([7, 2]), text, codes_kt, audio, V)
+    np.testing.assert_array_equal(e[0], text[7])
+    np.testing.assert_array_equal(e[1], text[2])
+    np.testing.assert_array_equal(e[2], audio[1] + audio[4 + 3])
+    np.testing.assert_array_equal(e[3], audio[3] + audio[4 + 0])
+
+
+# ---------------------------------------------------------------------------
+# Heads, scoring, selection, schedule
+# ---------------------------------------------------------------------------
+
+def test_head_one_hot_selects_column_and_argmax_groups():
+    H = RNG.standard_normal((12, 8))
+    x = np.zeros((1, 8))
+    x[0, 3] = 2.0
+    y, lg = O.head_logits(x, np.ones(8), H, 0.0)
+    # rms of x is 2/sqrt(8); y = x / rms = sqrt(8) e_3
+    np.testing.assert_allclose(lg[0], math.sqrt(8) * H[:, 3], rtol=1e-14)
+    am = O.argmax_groups(np.array([[1.0, 5.0, 5.0, 0.0, 2.0, 2.0]]), 2, 3)
+    np.testing.assert_array_equal(am, [[1, 1]])  # ties go to the lower class id
+
+
+def test_maskgit_scores_properties():
+    K, T, V, mask = 3, 5, 7, 6
+    lg = RNG.standard_normal((T, K * V)) * 3
+    codes = np.array([[6, 1, 6, 6, 2], [6, 6, 6, 0, 6], [3, 6, 6, 6, 6]])
+    pred, conf, lp = O.maskgit_scores(lg, codes, K, V, mask, 5.0)
+    view = lg.reshape(T, K, V)
+    for k in range(K):
+        for t in range(T):
+            row = view[t, k]
+            # softmax probabilities over all V classes sum to one
+            z = sum(math.exp(v) for v in row)
+            assert abs(sum(math.exp(v) / z for v in row) - 1.0) < 1e-12
+            # pred is the best non-mask class of the raw logits
+            assert pred[k, t] == int(np.argmax(row[:mask]))
+            if codes[k, t] == mask:
+                ref = math.log(math.exp(row[pred[k, t]]) / z) - 5.0 * k
+                assert abs(conf[k, t] - ref) < 1e-12
+            else:
+                assert conf[k, t] == -np.inf
+    # shifting all logits of a group by a constant changes nothing
+    lg2 = lg.copy()
+    lg2[:, V:2 * V] += 11.0
+    p2, c2, _ = O.maskgit_scores(lg2, codes, K, V, mask, 5.0)
+    np.testing.assert_array_equal(p2, pred)
+    np.testing.assert_allclose(c2, conf, rtol=1e-12)
+
+
+def test_select_top_matches_brute_force_with_ties():
+    rng = np.random.default_rng(11)
+    for trial in range(20):
+        n_el = int(rng.integers(1, 60))
+        conf = rng.integers(-3, 4, n_el).astype(float)  # many ties
+        conf[rng.random(n_el) < 0.3] = -np.inf
+        n = int(rng.integers(0, n_el + 3))
+        picked = O.select_top(conf, n)
+        finite = [(-conf[i], i) for i in range(n_el) if conf[i] > -np.inf]
+        finite.sort()
+        ref = [i for _, i in finite[:n]] + [-1] * max(0, n - len(finite))
+        np.testing.assert_array_equal(picked, np.array(ref[:n], np.int32))
+
+
+def test_apply_picks_updates_only_picked():
+    codes = np.array([[9, 9, 1], [9, 2, 9]])
+    pred = np.array([[4, 5, 6], [7, 8, 0]])
+    out = O.apply_picks(codes, pred, np.array([3, 0, -1]))
+    np.testing.assert_array_equal(out, [[4, 9, 1], [7, 2, 9]])
+
+
+def test_unmask_schedule():
+    for N, steps in ((3000, 32), (7, 3), (100, 1), (0, 4), (5, 10)):
+        s = O.unmask_schedule(N, steps)
+        assert len(s) == steps and sum(s) == N and min(s) >= 0
+        cum = np.cumsum(s)
+        for i in range(steps - 1):
+            # every step unmasks at least the cosine fraction of the total
+            frac = 1.0 - math.cos(math.pi / 2 * (i + 1) / steps)
+            assert cum[i] >= min(N, math.floor(N * frac - 1e-9))
+    # two steps of 10: t1 = 1 - cos(pi/4) = 0.29289..., ceil(2.93) = 3 then the rest
+    assert O.unmask_schedule(10, 2) == [3, 7]
