@@ -1,0 +1,150 @@
+// K1 gather-sum codebook embedding, K2 RMSNorm, and small helpers.
+//
+// K1 (OmniVoice ARCHITECTURE, "Qwen3 0.6B backbone with custom IO": audio rows are
+// rows k*1025 + code of the flattened table summed over the codebooks, text rows take
+// the text table; ncnn Qwen3-TTS port, "模型结构拆解": the 16 codebook embeddings of a
+// frame are summed).  HBM-bound gather: one 256-thread block per output row, each
+// thread owns 4 consecutive columns (8-byte bf16 or 16-byte fp32 loads, coalesced per
+// table row).  The sum is accumulated in double and rounded once, so the result is the
+// correctly rounded fp32 value of the exact sum.
+//
+// K2 (same page, "GGUF layout": input/post-attention layernorm, llm.norm, eps 1e-6):
+// y = x / sqrt(mean(x^2) + eps) * g, one block per row, fp32 statistics, output in
+// the operand dtype of the next matrix product.
+#include "common.h"
+#include "kernels.h"
+
+namespace ttsbb {
+
+template <typename T>
+__device__ __forceinline__ void load4(const T *p, float v[4]);
+template <>
+__device__ __forceinline__ void load4<float>(const float *p, float v[4]) {
+    float4 t = *reinterpret_cast<const float4 *>(p);
+    v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+}
+template <>
+__device__ __forceinline__ void load4<bf16_t>(const bf16_t *p, float v[4]) {
+    uint2 t = *reinterpret_cast<const uint2 *>(p);
+    v[0] = __uint_as_float(t.x << 16);
+    v[1] = __uint_as_float(t.x & 0xFFFF0000u);
+    v[2] = __uint_as_float(t.y << 16);
+    v[3] = __uint_as_float(t.y & 0xFFFF0000u);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void embed_kernel(EmbedArgs a) {
+    const int r = blockIdx.x;
+    const T *tables = reinterpret_cast<const T *>(a.tables);
+    for (int c0 = threadIdx.x * 4; c0 < a.hidden; c0 += 256 * 4) {
+        const bool text = a.is_text ? (a.is_text[r] != 0) : (r < a.text_prefix);
+        float outv[4];
+        if (text) {
+            int id = a.text_ids[r];
+            if (id < 0 || id >= a.text_vocab) {
+                if (threadIdx.x == 0 && c0 == 0) raise_flag(a.flag, FLAG_TEXT_ID);
+                id = 0;
+            }
+            load4<T>(reinterpret_cast<const T *>(a.text_table) + (int64_t)id * a.hidden + c0, outv);
+        } else {
+            double acc[4] = {0.0, 0.0, 0.0, 0.0};
+            const int32_t *crow = a.codes + (int64_t)(r - a.audio_row0) * a.code_row_stride;
+            for (int k = 0; k < a.n_cb; ++k) {
+                int code = crow[(int64_t)k * a.code_cb_stride];
+                if (code < 0 || code >= a.cb_vocab) {
+                    if (threadIdx.x == 0 && c0 == 0) raise_flag(a.flag, FLAG_CODE);
+                    code = 0;
+                }
+                float v[4];
+                load4<T>(tables + ((int64_t)k * a.cb_vocab + code) * a.hidden + c0, v);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] += (double)v[i];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) outv[i] = (float)acc[i];
+        }
+        *reinterpret_cast<float4 *>(a.out + (int64_t)r * a.hidden + c0) =
+            make_float4(outv[0], outv[1], outv[2], outv[3]);
+    }
+}
+
+void launch_embed(const EmbedArgs &a, DType dt, hipStream_t s) {
+    if (a.n_rows <= 0) return;
+    if (dt == DT_BF16)
+        hipLaunchKernelGGL(embed_kernel<bf16_t>, dim3(a.n_rows), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL(embed_kernel<float>, dim3(a.n_rows), dim3(256), 0, s, a);
+}
+
+template <typename TO>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float *x, int ldx, int hidden,
+                                                      const float *g, float eps, TO *out) {
+    __shared__ float red[4];
+    const int r = blockIdx.x;
+    const float *xr = x + (int64_t)r * ldx;
+    float ss = 0.f;
+    for (int c = threadIdx.x * 4; c < hidden; c += 1024) {
+        float4 v = *reinterpret_cast<const float4 *>(xr + c);
+        ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    }
+    ss = block_sum_256(ss, red);
+    const float inv = 1.0f / sqrtf(ss / (float)hidden + eps);
+    for (int c = threadIdx.x * 4; c < hidden; c += 1024) {
+        float4 v = *reinterpret_cast<const float4 *>(xr + c);
+        float4 gg = *reinterpret_cast<const float4 *>(g + c);
+        TO *o = out + (int64_t)r * hidden + c;
+        o[0] = from_f32<TO>(v.x * inv * gg.x);
+        o[1] = from_f32<TO>(v.y * inv * gg.y);
+        o[2] = from_f32<TO>(v.z * inv * gg.z);
+        o[3] = from_f32<TO>(v.w * inv * gg.w);
+    }
+}
+
+void launch_rmsnorm(const float *x, int ldx, int rows, int hidden, const float *gain, float eps,
+                    void *out, DType out_dt, hipStream_t s) {
+    if (rows <= 0) return;
+    if (out_dt == DT_BF16)
+        hipLaunchKernelGGL(rmsnorm_kernel<bf16_t>, dim3(rows), dim3(256), 0, s, x, ldx, hidden,
+                           gain, eps, reinterpret_cast<bf16_t *>(out));
+    else
+        hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(rows), dim3(256), 0, s, x, ldx, hidden,
+                           gain, eps, reinterpret_cast<float *>(out));
+}
+
+__global__ void increment_kernel(int32_t *v, int n) {
+    int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) v[i] += 1;
+}
+
+void launch_increment(int32_t *v, int n, hipStream_t s) {
+    if (n <= 0) return;
+    hipLaunchKernelGGL(increment_kernel, dim3((n + 255) / 256), dim3(256), 0, s, v, n);
+}
+
+template <typename T>
+__global__ void tap_copy_kernel(const T *src, int64_t s0, int64_t s1, int64_t s2, int d0, int d1,
+                                int d2, float *dst) {
+    int64_t total = (int64_t)d0 * d1 * d2;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        int64_t i2 = i % d2, t = i / d2;
+        int64_t i1 = t % d1, i0 = t / d1;
+        dst[i] = to_f32<T>(src[i0 * s0 + i1 * s1 + i2 * s2]);
+    }
+}
+
+void launch_tap_copy(const void *src, DType dt, int64_t s0, int64_t s1, int64_t s2, int d0,
+                     int d1, int d2, float *dst, hipStream_t s) {
+    int64_t total = (int64_t)d0 * d1 * d2;
+    if (total <= 0) return;
+    int blocks = (int)((total + 255) / 256);
+    if (blocks > 4096) blocks = 4096;
+    if (dt == DT_BF16)
+        hipLaunchKernelGGL(tap_copy_kernel<bf16_t>, dim3(blocks), dim3(256), 0, s,
+                           reinterpret_cast<const bf16_t *>(src), s0, s1, s2, d0, d1, d2, dst);
+    else
+        hipLaunchKernelGGL(tap_copy_kernel<float>, dim3(blocks), dim3(256), 0, s,
+                           reinterpret_cast<const float *>(src), s0, s1, s2, d0, d1, d2, dst);
+}
+
+}  // namespace ttsbb

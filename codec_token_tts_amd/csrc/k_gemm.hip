@@ -1,0 +1,322 @@
+// K3: the bias-free projections of the decoder layer (OmniVoice ARCHITECTURE, "Qwen3
+// 0.6B backbone with custom IO": q/k/v/o and gate/up/down projections without bias, the
+// SwiGLU MLP; "Tensor shape and layout": a Linear weight is [out][in], the product is
+// A @ W^T).
+//
+//   Y[M][N] = A[M][K] * W[N][K]^T, both operands K-contiguous, fp32 accumulation.
+//
+// Two kernels:
+// * gemm_mfma: bf16 MFMA (v_mfma_f32_16x16x32_bf16) with BMxBNx64 block tiles staged
+//   through LDS (rows padded to 72 elements so the 16-byte fragment reads of a
+//   16-row group hit distinct banks), register prefetch of the next K tile while the
+//   current one is multiplied, 4 waves in a 2x2 arrangement.  Used when M > 8.
+// * gemv: weight streaming for M <= 8 and for fp32: each wave owns two output columns,
+//   streams their weight rows once with 16-byte loads and reuses them for all M rows.
+//
+// Epilogues: store fp32, add into the fp32 residual stream (o_proj, down_proj), and
+// SwiGLU, where the gate and up weights are read as interleaved groups of 16 rows so
+// that silu(gate) * up pairs within a lane's own accumulators.
+#include "common.h"
+#include "kernels.h"
+
+namespace ttsbb {
+
+// Pointer to row n (logical) of the weight set.
+template <typename T>
+__device__ __forceinline__ const T *wrow(const WSrc &w, int epi, int n, int K) {
+    if (epi == EPI_SWIGLU) {
+        const int pair = n >> 5, half = (n >> 4) & 1, r = n & 15;
+        const T *base = reinterpret_cast<const T *>(half ? w.p[1] : w.p[0]);
+        return base + (int64_t)(pair * 16 + r) * K;
+    }
+    int s = 0;
+    if (w.nseg > 1 && n >= w.start[1]) s = 1;
+    if (w.nseg > 2 && n >= w.start[2]) s = 2;
+    return reinterpret_cast<const T *>(w.p[s]) + (int64_t)(n - w.start[s]) * K;
+}
+
+__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
+
+// ------------------------------------------------------------------------------------
+// MFMA tile GEMM (bf16)
+// ------------------------------------------------------------------------------------
+constexpr int BK = 64;
+constexpr int LDK = BK + 8;
+
+template <int BM, int BN, int EPI>
+__global__ __launch_bounds__(256) void gemm_mfma(GemmArgs g) {
+    constexpr int WM = BM / 2, WN = BN / 2;
+    constexpr int TM = WM / 16, TN = WN / 16;
+    constexpr int ACH = BM * 8 / 256;  // 16-byte chunks per thread of the A tile
+    constexpr int BCH = BN * 8 / 256;
+    static_assert(ACH >= 1 && BCH >= 1, "tile too small");
+    static_assert(EPI != EPI_SWIGLU || (TN % 2 == 0), "swiglu needs gate/up tile pairs");
+
+    __shared__ __attribute__((aligned(16))) bf16_t sA[2][BM * LDK];
+    __shared__ __attribute__((aligned(16))) bf16_t sB[2][BN * LDK];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int tiles_n = (g.N + BN - 1) / BN;
+    const int tile_m = blockIdx.x / tiles_n, tile_n = blockIdx.x % tiles_n;
+    const int m0 = tile_m * BM, n0 = tile_n * BN;
+
+    const bf16_t *A = reinterpret_cast<const bf16_t *>(g.A);
+    const bf16_t *arow[ACH];
+    const bf16_t *brow[BCH];
+    int aoff[ACH], boff[BCH];
+#pragma unroll
+    for (int c = 0; c < ACH; ++c) {
+        const int ch = tid + 256 * c, r = ch >> 3, kc = (ch & 7) * 8;
+        const int m = m0 + r;
+        arow[c] = (m < g.M) ? A + (int64_t)m * g.lda + kc : nullptr;
+        aoff[c] = r * LDK + kc;
+    }
+#pragma unroll
+    for (int c = 0; c < BCH; ++c) {
+        const int ch = tid + 256 * c, r = ch >> 3, kc = (ch & 7) * 8;
+        const int n = n0 + r;
+        brow[c] = (n < g.N) ? wrow<bf16_t>(g.w, EPI, n, g.K) + kc : nullptr;
+        boff[c] = r * LDK + kc;
+    }
+
+    uint4 ra[ACH], rb[BCH];
+    auto gload = [&](int k0) {
+#pragma unroll
+        for (int c = 0; c < ACH; ++c)
+            ra[c] = arow[c] ? *reinterpret_cast<const uint4 *>(arow[c] + k0) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int c = 0; c < BCH; ++c)
+            rb[c] = brow[c] ? *reinterpret_cast<const uint4 *>(brow[c] + k0) : make_uint4(0, 0, 0, 0);
+    };
+    auto sstore = [&](int buf) {
+#pragma unroll
+        for (int c = 0; c < ACH; ++c) *reinterpret_cast<uint4 *>(&sA[buf][aoff[c]]) = ra[c];
+#pragma unroll
+        for (int c = 0; c < BCH; ++c) *reinterpret_cast<uint4 *>(&sB[buf][boff[c]]) = rb[c];
+    };
+
+    f32x4_t acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    const int KT = g.K / BK;
+    gload(0);
+    sstore(0);
+    __syncthreads();
+
+    const int fr = lane & 15, fk = (lane >> 4) * 8;
+    for (int kt = 0; kt < KT; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < KT) gload((kt + 1) * BK);
+#pragma unroll
+        for (int ks = 0; ks < BK / 32; ++ks) {
+            bf16x8_t af[TM], bfr[TN];
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+                af[i] = *reinterpret_cast<const bf16x8_t *>(
+                    &sA[buf][(wm * WM + i * 16 + fr) * LDK + ks * 32 + fk]);
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                bfr[j] = *reinterpret_cast<const bf16x8_t *>(
+                    &sB[buf][(wn * WN + j * 16 + fr) * LDK + ks * 32 + fk]);
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        }
+        if (kt + 1 < KT) sstore(buf ^ 1);
+        __syncthreads();
+    }
+
+    // Epilogue.  Accumulator element r of tile (i, j) is row 4*(lane/16) + r, column lane%16.
+    const int rbase = m0 + wm * WM + (lane >> 4) * 4;
+    const int cbase = n0 + wn * WN + (lane & 15);
+    if (EPI == EPI_SWIGLU) {
+        bf16_t *C = reinterpret_cast<bf16_t *>(g.C);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; j += 2) {
+                const int ncol = n0 + wn * WN + j * 16;       // first logical column of the gate tile
+                const int ocol = (ncol >> 5) * 16 + (lane & 15);
+                if (ncol >= g.N) continue;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = rbase + i * 16 + r;
+                    if (row < g.M)
+                        C[(int64_t)row * g.ldc + ocol] = f32_to_bf16(silu_f(acc[i][j][r]) * acc[i][j + 1][r]);
+                }
+            }
+    } else {
+        float *C = reinterpret_cast<float *>(g.C);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int col = cbase + j * 16;
+                if (col >= g.N) continue;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = rbase + i * 16 + r;
+                    if (row >= g.M) continue;
+                    float *p = C + (int64_t)row * g.ldc + col;
+                    if (EPI == EPI_ADD) *p += acc[i][j][r];
+                    else *p = acc[i][j][r];
+                }
+            }
+    }
+}
+
+// ------------------------------------------------------------------------------------
+// Weight-streaming GEMV for M <= 8 (bf16 or fp32)
+// ------------------------------------------------------------------------------------
+constexpr int GEMV_MAXM = 8;
+constexpr int GEMV_UNITS = 2;  // output columns per wave
+
+template <typename T> struct Vec;
+template <> struct Vec<bf16_t> {
+    static constexpr int N = 8;
+    __device__ static void load(const bf16_t *p, float v[8]) {
+        uint4 t = *reinterpret_cast<const uint4 *>(p);
+        const uint32_t w[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float(w[i] << 16);
+            v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+        }
+    }
+};
+template <> struct Vec<float> {
+    static constexpr int N = 4;
+    __device__ static void load(const float *p, float v[4]) {
+        float4 t = *reinterpret_cast<const float4 *>(p);
+        v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+    }
+};
+
+template <typename T, int EPI>
+__global__ __launch_bounds__(256) void gemv(GemmArgs g) {
+    constexpr int V = Vec<T>::N;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int unit0 = (blockIdx.x * 4 + wave) * GEMV_UNITS;
+    const int n_units = (EPI == EPI_SWIGLU) ? g.N / 2 : g.N;
+    const T *A = reinterpret_cast<const T *>(g.A);
+
+    const T *wr[2 * GEMV_UNITS];
+    int nw = 0;
+#pragma unroll
+    for (int u = 0; u < GEMV_UNITS; ++u) {
+        const int n = unit0 + u < n_units ? unit0 + u : n_units - 1;
+        if (EPI == EPI_SWIGLU) {
+            wr[2 * u] = reinterpret_cast<const T *>(g.w.p[0]) + (int64_t)n * g.K;
+            wr[2 * u + 1] = reinterpret_cast<const T *>(g.w.p[1]) + (int64_t)n * g.K;
+        } else {
+            wr[u] = wrow<T>(g.w, EPI_STORE, n, g.K);
+        }
+    }
+    nw = (EPI == EPI_SWIGLU) ? 2 * GEMV_UNITS : GEMV_UNITS;
+
+    float acc[GEMV_MAXM][2 * GEMV_UNITS];
+#pragma unroll
+    for (int m = 0; m < GEMV_MAXM; ++m)
+#pragma unroll
+        for (int u = 0; u < 2 * GEMV_UNITS; ++u) acc[m][u] = 0.f;
+
+    for (int k0 = lane * V; k0 < g.K; k0 += 64 * V) {
+        float wv[2 * GEMV_UNITS][V];
+#pragma unroll
+        for (int u = 0; u < 2 * GEMV_UNITS; ++u)
+            if (u < nw) Vec<T>::load(wr[u] + k0, wv[u]);
+#pragma unroll
+        for (int m = 0; m < GEMV_MAXM; ++m) {
+            if (m >= g.M) break;
+            float av[V];
+            Vec<T>::load(A + (int64_t)m * g.lda + k0, av);
+#pragma unroll
+            for (int u = 0; u < 2 * GEMV_UNITS; ++u) {
+                if (u >= nw) continue;
+                float s = acc[m][u];
+#pragma unroll
+                for (int e = 0; e < V; ++e) s = fmaf(av[e], wv[u][e], s);
+                acc[m][u] = s;
+            }
+        }
+    }
+
+#pragma unroll
+    for (int m = 0; m < GEMV_MAXM; ++m) {
+        if (m >= g.M) break;
+#pragma unroll
+        for (int u = 0; u < 2 * GEMV_UNITS; ++u)
+            if (u < nw) acc[m][u] = wave_sum(acc[m][u]);
+    }
+    if (lane != 0) return;
+#pragma unroll
+    for (int m = 0; m < GEMV_MAXM; ++m) {
+        if (m >= g.M) break;
+#pragma unroll
+        for (int u = 0; u < GEMV_UNITS; ++u) {
+            const int n = unit0 + u;
+            if (n >= n_units) continue;
+            if (EPI == EPI_SWIGLU) {
+                T *C = reinterpret_cast<T *>(g.C);
+                C[(int64_t)m * g.ldc + n] = from_f32<T>(silu_f(acc[m][2 * u]) * acc[m][2 * u + 1]);
+            } else {
+                float *C = reinterpret_cast<float *>(g.C);
+                if (EPI == EPI_ADD) C[(int64_t)m * g.ldc + n] += acc[m][u];
+                else C[(int64_t)m * g.ldc + n] = acc[m][u];
+            }
+        }
+    }
+}
+
+template <typename T>
+static void launch_gemv(const GemmArgs &g, hipStream_t s) {
+    const int n_units = (g.epi == EPI_SWIGLU) ? g.N / 2 : g.N;
+    const int blocks = (n_units + 4 * GEMV_UNITS - 1) / (4 * GEMV_UNITS);
+    switch (g.epi) {
+        case EPI_STORE: hipLaunchKernelGGL((gemv<T, EPI_STORE>), dim3(blocks), dim3(256), 0, s, g); break;
+        case EPI_ADD: hipLaunchKernelGGL((gemv<T, EPI_ADD>), dim3(blocks), dim3(256), 0, s, g); break;
+        default: hipLaunchKernelGGL((gemv<T, EPI_SWIGLU>), dim3(blocks), dim3(256), 0, s, g); break;
+    }
+}
+
+template <int BM, int BN>
+static void launch_mfma(const GemmArgs &g, hipStream_t s) {
+    const int blocks = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
+    switch (g.epi) {
+        case EPI_STORE: hipLaunchKernelGGL((gemm_mfma<BM, BN, EPI_STORE>), dim3(blocks), dim3(256), 0, s, g); break;
+        case EPI_ADD: hipLaunchKernelGGL((gemm_mfma<BM, BN, EPI_ADD>), dim3(blocks), dim3(256), 0, s, g); break;
+        default: hipLaunchKernelGGL((gemm_mfma<BM, BN, EPI_SWIGLU>), dim3(blocks), dim3(256), 0, s, g); break;
+    }
+}
+
+void launch_gemm(const GemmArgs &g, DType dt, hipStream_t s) {
+    if (g.M <= 0) return;
+    if (dt == DT_F32) {
+        // fp32 mode streams weights; larger M is processed GEMV_MAXM rows at a time
+        for (int m0 = 0; m0 < g.M; m0 += GEMV_MAXM) {
+            GemmArgs h = g;
+            h.M = g.M - m0 < GEMV_MAXM ? g.M - m0 : GEMV_MAXM;
+            h.A = reinterpret_cast<const float *>(g.A) + (int64_t)m0 * g.lda;
+            h.C = reinterpret_cast<float *>(g.C) + (int64_t)m0 * g.ldc;
+            launch_gemv<float>(h, s);
+        }
+        return;
+    }
+    if (g.M <= GEMV_MAXM) {
+        launch_gemv<bf16_t>(g, s);
+        return;
+    }
+    const long tiles128 = (long)((g.M + 127) / 128) * ((g.N + 127) / 128);
+    if (g.M > 64 && tiles128 >= 200) launch_mfma<128, 128>(g, s);
+    else if (g.M > 32) launch_mfma<64, 64>(g, s);
+    else launch_mfma<32, 64>(g, s);
+}
+
+}  // namespace ttsbb

@@ -1,0 +1,121 @@
+// K7: greedy choice per head group; K8: MaskGIT scoring; K9: top-n unmasking.
+//
+// K7 (ncnn Qwen3-TTS port, "文本前端与生成循环": greedy decoding for strict numerical
+// alignment): argmax over each group of classes, ties to the lowest class id.
+//
+// K8 (OmniVoice ARCHITECTURE, "Qwen3 0.6B backbone with custom IO": logits of the
+// (8200, 1024) audio head viewed per codebook; "MaskGIT decoder": log_softmax, the mask
+// class set to -inf, argmax, score = max log-prob - layer index * layer penalty, scores
+// of already unmasked positions set to -inf).  One wave per (codebook, frame): the
+// 1025 logits of the group are contiguous; max and argmax over non-mask classes in one
+// sweep, sum of exp in a second, all in fp32.
+//
+// K9 (same section: topk over the flattened scores, then tokens[idx] = pred[idx]).
+// The rank of element i is the number of elements that order before it (greater
+// score, or equal score and lower flat index); the n elements of rank < n are the
+// selection and picked[rank] = i.  Every element's rank is independent, so the
+// selection is exact, deterministic and needs no sort; the score array is staged
+// through LDS in tiles and each thread ranks one element.
+#include <math.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace ttsbb {
+
+__global__ __launch_bounds__(256) void argmax_groups_kernel(const float *logits, int rows, int ld,
+                                                            int n_groups, int V, int32_t *out) {
+    const int lane = threadIdx.x & 63;
+    const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (item >= rows * n_groups) return;
+    const int gi = item % n_groups, r = item / n_groups;
+    const float *x = logits + (int64_t)r * ld + (int64_t)gi * V;
+    float best = -INFINITY;
+    int bi = 0x7FFFFFFF;
+    for (int v = lane; v < V; v += 64) argmax_merge(best, bi, x[v], v);
+    wave_argmax(best, bi);
+    if (lane == 0) out[item] = bi;
+}
+
+void launch_argmax_groups(const float *logits, int rows, int ld, int n_groups, int group_vocab,
+                          int32_t *out, hipStream_t s) {
+    const int items = rows * n_groups;
+    if (items <= 0) return;
+    hipLaunchKernelGGL(argmax_groups_kernel, dim3((items + 3) / 4), dim3(256), 0, s, logits, rows, ld,
+                       n_groups, group_vocab, out);
+}
+
+__global__ __launch_bounds__(256) void maskgit_scores_kernel(const float *logits, int T, int ld,
+                                                             int n_cb, int V, int mask_id,
+                                                             float penalty, const int32_t *codes,
+                                                             int32_t *pred, float *conf) {
+    const int lane = threadIdx.x & 63;
+    const int item = blockIdx.x * 4 + (threadIdx.x >> 6);  // flat index k*T + t
+    if (item >= n_cb * T) return;
+    const int k = item / T, t = item % T;
+    const float *x = logits + (int64_t)t * ld + (int64_t)k * V;
+    float mx = -INFINITY, best = -INFINITY;
+    int bi = 0x7FFFFFFF;
+    for (int v = lane; v < V; v += 64) {
+        const float xv = x[v];
+        mx = fmaxf(mx, xv);
+        if (v != mask_id) argmax_merge(best, bi, xv, v);
+    }
+    mx = wave_max(mx);
+    wave_argmax(best, bi);
+    const float LOG2E = 1.4426950408889634f;
+    float se = 0.f;
+    for (int v = lane; v < V; v += 64) se += exp2f((x[v] - mx) * LOG2E);
+    se = wave_sum(se);
+    if (lane == 0) {
+        const float lse = mx + logf(se);
+        pred[item] = bi;
+        conf[item] = (codes[item] == mask_id) ? (best - lse) - (float)k * penalty : -INFINITY;
+    }
+}
+
+void launch_maskgit_scores(const float *logits, int T, int ld, int n_cb, int V, int mask_id,
+                           float penalty, const int32_t *codes, int32_t *pred, float *conf,
+                           hipStream_t s) {
+    const int items = n_cb * T;
+    if (items <= 0) return;
+    hipLaunchKernelGGL(maskgit_scores_kernel, dim3((items + 3) / 4), dim3(256), 0, s, logits, T, ld,
+                       n_cb, V, mask_id, penalty, codes, pred, conf);
+}
+
+constexpr int SEL_TILE = 4096;
+
+__global__ __launch_bounds__(256) void select_update_kernel(const float *conf, const int32_t *pred,
+                                                            int n, int n_unmask, int32_t *codes,
+                                                            int32_t *picked) {
+    __shared__ float tile[SEL_TILE];
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    const float ci = i < n ? conf[i] : -INFINITY;
+    int rank = 0;
+    for (int j0 = 0; j0 < n; j0 += SEL_TILE) {
+        const int cnt = min(SEL_TILE, n - j0);
+        for (int j = threadIdx.x; j < cnt; j += 256) tile[j] = conf[j0 + j];
+        __syncthreads();
+        for (int j = 0; j < cnt; ++j) {
+            const float cj = tile[j];
+            rank += (cj > ci) || (cj == ci && j0 + j < i);
+        }
+        __syncthreads();
+    }
+    if (i >= n || rank >= n_unmask) return;
+    if (ci > -INFINITY) {
+        picked[rank] = i;
+        codes[i] = pred[i];
+    } else {
+        picked[rank] = -1;
+    }
+}
+
+void launch_select_update(const float *conf, const int32_t *pred, int n, int n_unmask,
+                          int32_t *codes, int32_t *picked, hipStream_t s) {
+    if (n <= 0 || n_unmask <= 0) return;
+    hipLaunchKernelGGL(select_update_kernel, dim3((n + 255) / 256), dim3(256), 0, s, conf, pred, n,
+                       n_unmask, codes, picked);
+}
+
+}  // namespace ttsbb

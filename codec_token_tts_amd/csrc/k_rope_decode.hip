@@ -1,0 +1,303 @@
+// K4: per-head q/k RMSNorm + half-rotate RoPE + K/V write, and K5: q_len=1 decode
+// attention over a paged KV cache.
+//
+// K4 (OmniVoice ARCHITECTURE, "Qwen3 0.6B backbone with custom IO": per-head RMSNorm
+// on Q and K before RoPE, theta 1e6; ncnn Qwen3-TTS port, "单token SDPA问题与host
+// attention" and "mRoPE结论": half-rotate RoPE, then the token's K/V are appended to
+// the layer's cache).  One block per token; one wave per head; lane l holds dimensions
+// l and l+64, which is exactly a RoPE pair, so the rotation is lane-local.  cos/sin
+// come from a table computed on the host in double precision.
+//
+// K5 (same ncnn section: GQA attention of the q_len=1 step; the new token attends to
+// positions 0..p).  HBM-bound.  Work item = (stream, KV head, chunk of positions);
+// one wave per item reads each 16-token page of K and V once with 16-byte lane loads
+// (a 4 KB bf16 page block is four fully coalesced wave loads) and serves all query
+// heads of the GQA group from those registers.  Scores reduce over the lanes sharing a
+// token with xor-shuffles; each lane keeps an online-softmax state (max, sum, 8 or 4
+// output dims) in base-2 units; lanes of a chunk merge by shuffles; chunks merge in a
+// fixed order in the combine kernel (deterministic, no atomics).
+#include <math.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace ttsbb {
+
+template <typename TKV>
+__global__ __launch_bounds__(256) void rope_kv_kernel(RopeKvArgs a) {
+    const int m = blockIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int width = (a.H + 2 * a.Hkv) * 128;
+    const float *row = a.qkv + (int64_t)m * width;
+
+    int p = a.dense ? m : a.pos[m];
+    bool ok = true;
+    int page_id = 0, slot = 0;
+    if (p < 0 || p >= a.max_pos) {
+        if (threadIdx.x == 0) raise_flag(a.flag, FLAG_POSITION);
+        p = p < 0 ? 0 : a.max_pos - 1;
+        ok = false;
+    }
+    if (!a.dense) {
+        const int pi = p / a.page;
+        if (pi >= a.max_pages) {
+            if (threadIdx.x == 0) raise_flag(a.flag, FLAG_POSITION);
+            ok = false;
+        } else {
+            page_id = a.page_table[(int64_t)m * a.max_pages + pi];
+            slot = p % a.page;
+            if (page_id < 0 || page_id >= a.n_pages) {
+                if (threadIdx.x == 0) raise_flag(a.flag, FLAG_PAGE);
+                ok = false;
+            }
+        }
+    }
+    const float2 cs = a.rope[(int64_t)p * 64 + lane];
+
+    const int jobs = a.H + 2 * a.Hkv;
+    for (int j = wave; j < jobs; j += 4) {
+        const float *src = row + j * 128;
+        float u = src[lane], u2 = src[lane + 64];
+        if (j < a.H + a.Hkv) {
+            const float *g = j < a.H ? a.q_gain : a.k_gain;
+            const float ss = wave_sum(u * u + u2 * u2);
+            const float inv = 1.0f / sqrtf(ss / 128.0f + a.eps);
+            const float x0 = u * inv * g[lane], x1 = u2 * inv * g[lane + 64];
+            u = x0 * cs.x - x1 * cs.y;
+            u2 = x1 * cs.x + x0 * cs.y;
+        }
+        if (j < a.H) {
+            if (a.dense) {
+                bf16_t *q = reinterpret_cast<bf16_t *>(a.q_out) + (int64_t)m * a.H * 128 + j * 128;
+                q[lane] = f32_to_bf16(u);
+                q[lane + 64] = f32_to_bf16(u2);
+            } else {
+                float *q = reinterpret_cast<float *>(a.q_out) + (int64_t)m * a.H * 128 + j * 128;
+                q[lane] = u;
+                q[lane + 64] = u2;
+            }
+            continue;
+        }
+        const int kv = j < a.H + a.Hkv ? 0 : 1;
+        const int h = j - a.H - kv * a.Hkv;
+        if (a.dense) {
+            if (kv == 0) {
+                bf16_t *k = a.kbuf + ((int64_t)h * a.s_pad + m) * 128;
+                k[lane] = f32_to_bf16(u);
+                k[lane + 64] = f32_to_bf16(u2);
+            } else {
+                bf16_t *vt = a.vtbuf + (int64_t)h * 128 * a.s_pad + m;
+                vt[(int64_t)lane * a.s_pad] = f32_to_bf16(u);
+                vt[(int64_t)(lane + 64) * a.s_pad] = f32_to_bf16(u2);
+            }
+        } else if (ok) {
+            TKV *dst = reinterpret_cast<TKV *>(a.pool_layer) +
+                       ((((int64_t)page_id * 2 + kv) * a.Hkv + h) * a.page + slot) * 128;
+            dst[lane] = from_f32<TKV>(u);
+            dst[lane + 64] = from_f32<TKV>(u2);
+        }
+    }
+}
+
+void launch_rope_kv(const RopeKvArgs &a, DType kv_dt, hipStream_t s) {
+    if (a.M <= 0) return;
+    if (kv_dt == DT_BF16 || a.dense)
+        hipLaunchKernelGGL(rope_kv_kernel<bf16_t>, dim3(a.M), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL(rope_kv_kernel<float>, dim3(a.M), dim3(256), 0, s, a);
+}
+
+// ------------------------------------------------------------------------------------
+// K5
+// ------------------------------------------------------------------------------------
+constexpr int PART_STRIDE = 132;
+
+template <typename T> struct KV16;
+template <> struct KV16<bf16_t> {
+    static constexpr int EPL = 8;  // elements per 16-byte lane load
+    __device__ static void load(const bf16_t *p, float v[8]) {
+        uint4 t = *reinterpret_cast<const uint4 *>(p);
+        const uint32_t w[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float(w[i] << 16);
+            v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+        }
+    }
+};
+template <> struct KV16<float> {
+    static constexpr int EPL = 4;
+    __device__ static void load(const float *p, float v[4]) {
+        float4 t = *reinterpret_cast<const float4 *>(p);
+        v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+    }
+};
+
+template <typename T, int GROUP>
+__global__ __launch_bounds__(256) void decode_attn_kernel(DecodeAttnArgs a) {
+    constexpr int EPL = KV16<T>::EPL;
+    constexpr int LPR = 128 / EPL;  // lanes per 128-dim row
+    constexpr int RPL = 64 / LPR;   // rows (tokens) per wave load
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int item = blockIdx.x * 4 + wave;
+    const int total = a.B * a.Hkv * a.n_chunks;
+    if (item >= total) return;
+    const int c = item % a.n_chunks;
+    const int t = item / a.n_chunks;
+    const int hk = t % a.Hkv, b = t / a.Hkv;
+
+    int L = a.pos[b] + 1;
+    const int cap = a.max_pages * a.page;
+    if (L > cap) L = cap;
+    const int p_begin = c * a.chunk;
+    if (p_begin >= L) return;
+    const int p_end = min(L, p_begin + a.chunk);
+
+    const int d0 = (lane % LPR) * EPL;
+    const int rsub = lane / LPR;
+    float qv[GROUP][EPL];
+#pragma unroll
+    for (int j = 0; j < GROUP; ++j) {
+        const float *q = a.q + (int64_t)b * a.H * 128 + (hk * GROUP + j) * 128 + d0;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) qv[j][e] = q[e] * a.scale_log2;
+    }
+
+    float m_run[GROUP], l_run[GROUP], acc[GROUP][EPL];
+#pragma unroll
+    for (int j = 0; j < GROUP; ++j) {
+        m_run[j] = -INFINITY;
+        l_run[j] = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[j][e] = 0.f;
+    }
+
+    const T *pool = reinterpret_cast<const T *>(a.pool_layer);
+    const int64_t blk = (int64_t)a.page * 128;  // elements of one (page, K|V, head) block
+    for (int p0 = p_begin; p0 < p_end; p0 += a.page) {
+        const int page_id = a.page_table[(int64_t)b * a.max_pages + p0 / a.page];
+        if (page_id < 0 || page_id >= a.n_pages) continue;  // flagged by K4
+        const T *kb = pool + (((int64_t)page_id * 2 + 0) * a.Hkv + hk) * blk;
+        const T *vb = pool + (((int64_t)page_id * 2 + 1) * a.Hkv + hk) * blk;
+        const int nvalid = p_end - p0;  // tokens of this page inside the chunk
+        constexpr int NR = 16 / RPL;
+        float s[NR][GROUP];
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            const int tok = rsub + RPL * r;
+            float kv[EPL];
+            KV16<T>::load(kb + tok * 128 + d0, kv);
+#pragma unroll
+            for (int j = 0; j < GROUP; ++j) {
+                float d = 0.f;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) d = fmaf(qv[j][e], kv[e], d);
+                d = group_sum<LPR>(d);
+                s[r][j] = tok < nvalid ? d : -INFINITY;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < GROUP; ++j) {
+            float mx = m_run[j];
+#pragma unroll
+            for (int r = 0; r < NR; ++r) mx = fmaxf(mx, s[r][j]);
+            if (mx == -INFINITY) continue;  // nothing valid for this lane yet
+            const float sc = exp2f(m_run[j] - mx);
+            l_run[j] *= sc;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[j][e] *= sc;
+            m_run[j] = mx;
+#pragma unroll
+            for (int r = 0; r < NR; ++r) {
+                s[r][j] = exp2f(s[r][j] - mx);
+                l_run[j] += s[r][j];
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            const int tok = rsub + RPL * r;
+            if (tok >= nvalid) continue;  // slots past the length may hold anything
+            float vv[EPL];
+            KV16<T>::load(vb + tok * 128 + d0, vv);
+#pragma unroll
+            for (int j = 0; j < GROUP; ++j) {
+                const float pr = (m_run[j] == -INFINITY) ? 0.f : s[r][j];
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) acc[j][e] = fmaf(pr, vv[e], acc[j][e]);
+            }
+        }
+    }
+
+    // merge the RPL lane groups (same dims, different tokens)
+#pragma unroll
+    for (int j = 0; j < GROUP; ++j) {
+        float mt = m_run[j];
+#pragma unroll
+        for (int o = LPR; o < 64; o <<= 1) mt = fmaxf(mt, __shfl_xor(mt, o, WAVE));
+        const float sc = (m_run[j] == -INFINITY) ? 0.f : exp2f(m_run[j] - mt);
+        float lt = l_run[j] * sc;
+#pragma unroll
+        for (int o = LPR; o < 64; o <<= 1) lt += __shfl_xor(lt, o, WAVE);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            float v = acc[j][e] * sc;
+#pragma unroll
+            for (int o = LPR; o < 64; o <<= 1) v += __shfl_xor(v, o, WAVE);
+            acc[j][e] = v;
+        }
+        float *part = a.part + (((int64_t)b * a.H + hk * GROUP + j) * a.n_chunks + c) * PART_STRIDE;
+        if (lane < LPR) {
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) part[4 + d0 + e] = acc[j][e];
+        }
+        if (lane == 0) {
+            part[0] = mt;
+            part[1] = lt;
+        }
+    }
+}
+
+template <typename TO>
+__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeAttnArgs a) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int item = blockIdx.x * 4 + wave;
+    if (item >= a.B * a.H) return;
+    const int h = item % a.H, b = item / a.H;
+    int L = a.pos[b] + 1;
+    const int cap = a.max_pages * a.page;
+    if (L > cap) L = cap;
+    const int nc = min(a.n_chunks, (L + a.chunk - 1) / a.chunk);
+    const float *part = a.part + ((int64_t)b * a.H + h) * a.n_chunks * PART_STRIDE;
+    float M = -INFINITY;
+    for (int c = 0; c < nc; ++c) M = fmaxf(M, part[c * PART_STRIDE]);
+    float l = 0.f, o0 = 0.f, o1 = 0.f;
+    for (int c = 0; c < nc; ++c) {
+        const float *pc = part + c * PART_STRIDE;
+        const float w = exp2f(pc[0] - M);
+        l += w * pc[1];
+        o0 += w * pc[4 + lane];
+        o1 += w * pc[4 + 64 + lane];
+    }
+    const float inv = 1.0f / l;
+    TO *out = reinterpret_cast<TO *>(a.out) + (int64_t)b * a.H * 128 + h * 128;
+    out[lane] = from_f32<TO>(o0 * inv);
+    out[lane + 64] = from_f32<TO>(o1 * inv);
+}
+
+void launch_decode_attn(const DecodeAttnArgs &a, DType dt, hipStream_t s) {
+    if (a.B <= 0) return;
+    const int group = a.H / a.Hkv;
+    const int items = a.B * a.Hkv * a.n_chunks;
+    const int blocks = (items + 3) / 4;
+    if (dt == DT_BF16) {
+        if (group == 2) hipLaunchKernelGGL((decode_attn_kernel<bf16_t, 2>), dim3(blocks), dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((decode_attn_kernel<bf16_t, 1>), dim3(blocks), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(decode_combine_kernel<bf16_t>, dim3((a.B * a.H + 3) / 4), dim3(256), 0, s, a);
+    } else {
+        if (group == 2) hipLaunchKernelGGL((decode_attn_kernel<float, 2>), dim3(blocks), dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((decode_attn_kernel<float, 1>), dim3(blocks), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(decode_combine_kernel<float>, dim3((a.B * a.H + 3) / 4), dim3(256), 0, s, a);
+    }
+}
+
+}  // namespace ttsbb

@@ -1,0 +1,128 @@
+// Launchers of the ttsbb kernels (host-callable, implemented in the .hip files).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ttsbb {
+
+enum DType { DT_F32 = 0, DT_BF16 = 1 };
+
+// Device-side index check codes (OR-ed into the context flag).
+enum : int { FLAG_CODE = 1, FLAG_TEXT_ID = 2, FLAG_PAGE = 4, FLAG_POSITION = 8 };
+
+// ---- K1: gather-sum codebook embedding ------------------------------------------
+// Row r (< n_rows) is a text row if (is_text ? is_text[r] : r < text_prefix); text rows
+// copy text_table[text_ids[r]].  Audio rows sum over k < n_cb the table row
+// k*cb_vocab + codes[(r - audio_row0)*code_row_stride + k*code_cb_stride].
+struct EmbedArgs {
+    int n_rows, n_cb, hidden;
+    const int32_t *codes;
+    int code_row_stride, code_cb_stride, audio_row0;
+    const void *tables;
+    int cb_vocab;
+    const uint8_t *is_text;
+    int text_prefix;
+    const int32_t *text_ids;
+    const void *text_table;
+    int text_vocab;
+    float *out;
+    int *flag;
+};
+void launch_embed(const EmbedArgs &a, DType dt, hipStream_t s);
+
+// ---- K2: RMSNorm of fp32 rows into the operand dtype ------------------------------
+void launch_rmsnorm(const float *x, int ldx, int rows, int hidden, const float *gain, float eps,
+                    void *out, DType out_dt, hipStream_t s);
+
+// ---- K3: projections  Y[M][N] = A[M][K] * W[N][K]^T with an epilogue --------------
+enum Epi { EPI_STORE = 0, EPI_ADD = 1, EPI_SWIGLU = 2 };
+struct WSrc {
+    // EPI_STORE / EPI_ADD: logical row n lives in p[i] for start[i] <= n < start[i+1]
+    //   (start[0] = 0, nseg <= 3 segments, start[nseg] = N).
+    // EPI_SWIGLU: p[0] = W_gate, p[1] = W_up, each [N/2][K]; logical rows interleave 16
+    //   gate rows and 16 up rows; the output has N/2 columns silu(gate) * up.
+    const void *p[3];
+    int start[4];
+    int nseg;
+};
+struct GemmArgs {
+    const void *A;  // [M][lda] operand dtype
+    int lda, M, K, N;
+    WSrc w;
+    void *C;        // EPI_STORE / EPI_ADD: fp32 [M][ldc]; EPI_SWIGLU: operand dtype [M][ldc]
+    int ldc;
+    int epi;
+};
+void launch_gemm(const GemmArgs &g, DType dt, hipStream_t s);
+
+// ---- K4: per-head RMSNorm + RoPE + K/V write --------------------------------------
+// qkv fp32 [M][(H + 2 Hkv) * 128].  Decode mode (dense == 0): row m is stream m at
+// position pos[m]; K/V go to pool slot (page_table[m][p / page], p % page); q goes to
+// q_out fp32 [M][H*128].  Dense mode: row m is position m; q goes to q_out bf16
+// [M][H*128], K to kbuf [Hkv][s_pad][128] and V transposed to vtbuf [Hkv][128][s_pad].
+struct RopeKvArgs {
+    const float *qkv;
+    int M, H, Hkv;
+    const float *q_gain, *k_gain;
+    float eps;
+    const float2 *rope;  // [max_pos][64] (cos, sin)
+    int max_pos;
+    void *q_out;
+    int dense;
+    const int32_t *pos;
+    const int32_t *page_table;
+    int max_pages, n_pages, page;
+    void *pool_layer;    // [n_pages][2][Hkv][page][128]
+    uint16_t *kbuf, *vtbuf;
+    int s_pad;
+    int *flag;
+};
+void launch_rope_kv(const RopeKvArgs &a, DType kv_dt, hipStream_t s);
+
+// ---- K5: split-sequence decode attention over the paged pool -----------------------
+struct DecodeAttnArgs {
+    const float *q;  // [B][H*128] fp32
+    const void *pool_layer;
+    const int32_t *pos;
+    const int32_t *page_table;
+    int max_pages, n_pages, page;
+    int B, H, Hkv;
+    int chunk, n_chunks;  // positions per chunk (multiple of page), chunks per stream
+    float *part;          // [B][H][n_chunks][132]: m, l, pad, pad, acc[128]
+    void *out;            // [B][H*128] operand dtype
+    float scale_log2;     // log2(e) / sqrt(128)
+};
+void launch_decode_attn(const DecodeAttnArgs &a, DType dt, hipStream_t s);
+
+// ---- K6: bidirectional flash attention (bf16 MFMA) ---------------------------------
+struct FlashArgs {
+    const uint16_t *q;   // [S][H*128] bf16
+    const uint16_t *k;   // [Hkv][s_pad][128] bf16
+    const uint16_t *vt;  // [Hkv][128][s_pad] bf16
+    int S, s_pad, H, Hkv;
+    float scale_log2;
+    uint16_t *out;       // [S][H*128] bf16
+};
+void launch_flash_attn(const FlashArgs &a, hipStream_t s);
+
+// ---- K7: greedy choice per group --------------------------------------------------
+void launch_argmax_groups(const float *logits, int rows, int ld, int n_groups, int group_vocab,
+                          int32_t *out, hipStream_t s);
+
+// ---- K8: MaskGIT scores: log-softmax, mask class excluded, argmax, confidence --------
+void launch_maskgit_scores(const float *logits, int T, int ld, int n_cb, int V, int mask_id,
+                           float penalty, const int32_t *codes, int32_t *pred, float *conf,
+                           hipStream_t s);
+
+// ---- K9: top-n selection by rank + code update -------------------------------------
+void launch_select_update(const float *conf, const int32_t *pred, int n, int n_unmask,
+                          int32_t *codes, int32_t *picked, hipStream_t s);
+
+// ---- misc ---------------------------------------------------------------------------
+void launch_increment(int32_t *v, int n, hipStream_t s);
+// dst[i0][i1][i2] (fp32, dense) = src[i0*s0 + i1*s1 + i2*s2] (element strides)
+void launch_tap_copy(const void *src, DType dt, int64_t s0, int64_t s1, int64_t s2, int d0,
+                     int d1, int d2, float *dst, hipStream_t s);
+
+}  // namespace ttsbb

@@ -1,0 +1,626 @@
+// ttsbb C ABI: context, argument checks, and the order of kernels of each call.
+//
+// Decode step (ncnn Qwen3-TTS port, "单token SDPA问题与host attention": per layer the
+// pre-attention half, then RoPE + KV append + GQA attention, then output projection,
+// MLP and residuals):
+//   K2 norm -> K3 q|k|v -> K4 head norms + RoPE + KV write -> K5 attention -> K3 o_proj
+//   (+x) -> K2 norm -> K3 gate|up with SwiGLU -> K3 down_proj (+x); after the layers
+//   K2 final norm -> K3 head -> K7 argmax; positions += 1.
+// MaskGIT step (OmniVoice ARCHITECTURE, "MaskGIT decoder" and "Inner-loop
+// optimisations"): K1 hybrid embedding -> layers with K6 bidirectional attention ->
+// K2 final norm on the audio window only -> K3 heads -> K8 scores -> K9 top-n update.
+// Every call only enqueues on the context's stream.
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <new>
+#include <vector>
+
+#include "../../include/ttsbb.h"
+#include "kernels.h"
+
+using namespace ttsbb;
+
+#define TTSBB_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr int MAX_CHUNKS = 32;   // decode attention partials per (stream, head)
+constexpr int PART_STRIDE = 132; // floats per partial (m, l, 2 pad, 128 dims)
+
+struct Tap {
+    float *buf = nullptr;
+    int rows = 0, cols = 0;
+};
+
+}  // namespace
+
+struct ttsbb_ctx {
+    ttsbb_config cfg;
+    std::vector<ttsbb_layer> layers;
+    const float *final_norm = nullptr;
+    hipStream_t stream = nullptr;
+    DType dt = DT_BF16;
+    size_t esz = 2;  // bytes per operand element
+    int qkv_w = 0;   // (H + 2 Hkv) * head_dim
+    // workspace
+    void *h = nullptr;
+    float *qkv = nullptr;
+    void *q = nullptr;
+    void *attn = nullptr;
+    void *mlp = nullptr;
+    float *x = nullptr;
+    uint16_t *kbuf = nullptr, *vtbuf = nullptr;
+    int s_pad_cap = 0;
+    float *part = nullptr;
+    float *logits = nullptr;
+    float2 *rope = nullptr;
+    int *flag = nullptr;
+    std::vector<void *> allocs;
+    // taps
+    int tap_layer = -1;
+    Tap taps[TTSBB_TAP_COUNT];
+};
+
+namespace {
+
+bool dev_alloc(ttsbb_ctx *c, void **p, size_t bytes) {
+    if (bytes == 0) bytes = 256;
+    if (hipMalloc(p, bytes) != hipSuccess) {
+        *p = nullptr;
+        return false;
+    }
+    c->allocs.push_back(*p);
+    return true;
+}
+
+void free_all(ttsbb_ctx *c) {
+    for (void *p : c->allocs) hipFree(p);
+    c->allocs.clear();
+    for (auto &t : c->taps) {
+        if (t.buf) hipFree(t.buf);
+        t.buf = nullptr;
+    }
+}
+
+int round_up(int v, int m) { return (v + m - 1) / m * m; }
+
+bool launch_failed() { return hipPeekAtLastError() != hipSuccess; }
+
+int tap_width(const ttsbb_ctx *c, int tap) {
+    const ttsbb_config &g = c->cfg;
+    switch (tap) {
+        case TTSBB_TAP_QKV: return c->qkv_w;
+        case TTSBB_TAP_Q:
+        case TTSBB_TAP_ATTN: return g.n_heads * g.head_dim;
+        case TTSBB_TAP_K:
+        case TTSBB_TAP_V: return g.n_kv_heads * g.head_dim;
+        case TTSBB_TAP_MLP: return g.ffn;
+        case TTSBB_TAP_LOGITS: return g.max_head_cols > 0 ? g.max_head_cols : 1;
+        default: return g.hidden;
+    }
+}
+
+// Record a tap as a dense fp32 [rows][cols] copy of a strided source.
+void tap(ttsbb_ctx *c, int which, const void *src, DType dt, int rows, int cols, int64_t s_row,
+         int64_t s_col_hi, int64_t s_col_lo, int cols_lo) {
+    Tap &t = c->taps[which];
+    if (!t.buf) return;
+    t.rows = rows;
+    t.cols = cols;
+    // view cols as [cols / cols_lo][cols_lo]
+    launch_tap_copy(src, dt, s_row, s_col_hi, s_col_lo, rows, cols / cols_lo, cols_lo, t.buf, c->stream);
+}
+
+void tap_dense(ttsbb_ctx *c, int which, const void *src, DType dt, int rows, int cols, int ld) {
+    tap(c, which, src, dt, rows, cols, ld, cols, 1, cols);
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------------------------
+
+TTSBB_API void ttsbb_default_config(ttsbb_config *cfg) {
+    if (!cfg) return;
+    memset(cfg, 0, sizeof(*cfg));
+    cfg->n_layers = 28;
+    cfg->hidden = 1024;
+    cfg->n_heads = 16;
+    cfg->n_kv_heads = 8;
+    cfg->head_dim = 128;
+    cfg->ffn = 3072;
+    cfg->rms_eps = 1e-6f;
+    cfg->rope_theta = 1e6;
+    cfg->dtype = TTSBB_BF16;
+    cfg->kv_page = 16;
+    cfg->max_rows = 1024;
+    cfg->max_pos = 8192;
+    cfg->max_head_cols = 8200;
+}
+
+TTSBB_API const char *ttsbb_status_str(ttsbb_status s) {
+    switch (s) {
+        case TTSBB_OK: return "ok";
+        case TTSBB_INVALID_ARG: return "invalid argument";
+        case TTSBB_UNSUPPORTED: return "unsupported shape or mode";
+        case TTSBB_OOM: return "out of device memory";
+        case TTSBB_DEVICE_ERROR: return "device error";
+        default: return "unknown status";
+    }
+}
+
+TTSBB_API ttsbb_status ttsbb_create(const ttsbb_config *cfg, const ttsbb_layer *layers,
+                                    const float *final_norm, void *hip_stream, ttsbb_ctx **out) {
+    if (!cfg || !out) return TTSBB_INVALID_ARG;
+    *out = nullptr;
+    const ttsbb_config &g = *cfg;
+    if (g.n_layers < 0 || g.hidden <= 0 || g.n_heads <= 0 || g.n_kv_heads <= 0 || g.head_dim <= 0 ||
+        g.ffn <= 0 || !(g.rms_eps >= 0.f) || !(g.rope_theta > 0.0) || g.kv_page <= 0 ||
+        g.max_rows <= 0 || g.max_pos <= 0 || g.max_head_cols < 0 ||
+        (g.dtype != TTSBB_F32 && g.dtype != TTSBB_BF16))
+        return TTSBB_INVALID_ARG;
+    if (g.n_layers > 0 && !layers) return TTSBB_INVALID_ARG;
+    for (int l = 0; l < g.n_layers; ++l) {
+        const ttsbb_layer &L = layers[l];
+        if (!L.attn_norm || !L.q_norm || !L.k_norm || !L.ffn_norm || !L.wq || !L.wk || !L.wv ||
+            !L.wo || !L.w_gate || !L.w_up || !L.w_down)
+            return TTSBB_INVALID_ARG;
+    }
+    if (g.head_dim != 128 || g.hidden % 128 != 0 || g.ffn % 128 != 0 ||
+        g.n_heads % g.n_kv_heads != 0 || (g.n_heads / g.n_kv_heads > 2) || g.kv_page != 16)
+        return TTSBB_UNSUPPORTED;
+
+    ttsbb_ctx *c = new (std::nothrow) ttsbb_ctx();
+    if (!c) return TTSBB_OOM;
+    c->cfg = g;
+    c->layers.assign(layers, layers + g.n_layers);
+    c->final_norm = final_norm;
+    c->stream = reinterpret_cast<hipStream_t>(hip_stream);
+    c->dt = g.dtype == TTSBB_BF16 ? DT_BF16 : DT_F32;
+    c->esz = g.dtype == TTSBB_BF16 ? 2 : 4;
+    c->qkv_w = (g.n_heads + 2 * g.n_kv_heads) * g.head_dim;
+
+    const size_t R = (size_t)g.max_rows;
+    const size_t hd_all = (size_t)g.n_heads * g.head_dim;
+    c->s_pad_cap = round_up(g.max_rows, 64);
+    bool ok = dev_alloc(c, &c->h, R * g.hidden * c->esz) &&
+              dev_alloc(c, (void **)&c->qkv, R * c->qkv_w * 4) &&
+              dev_alloc(c, &c->q, R * hd_all * 4) &&
+              dev_alloc(c, &c->attn, R * hd_all * c->esz) &&
+              dev_alloc(c, &c->mlp, R * g.ffn * c->esz) &&
+              dev_alloc(c, (void **)&c->x, R * g.hidden * 4) &&
+              dev_alloc(c, (void **)&c->kbuf, (size_t)g.n_kv_heads * c->s_pad_cap * g.head_dim * 2) &&
+              dev_alloc(c, (void **)&c->vtbuf, (size_t)g.n_kv_heads * c->s_pad_cap * g.head_dim * 2) &&
+              dev_alloc(c, (void **)&c->part, R * g.n_heads * MAX_CHUNKS * PART_STRIDE * 4) &&
+              dev_alloc(c, (void **)&c->logits, R * (size_t)(g.max_head_cols > 0 ? g.max_head_cols : 1) * 4) &&
+              dev_alloc(c, (void **)&c->rope, (size_t)g.max_pos * 64 * sizeof(float2)) &&
+              dev_alloc(c, (void **)&c->flag, 256);
+    if (!ok) {
+        free_all(c);
+        delete c;
+        hipGetLastError();
+        return TTSBB_OOM;
+    }
+    // Padding keys of the MaskGIT K/V buffers must hold finite values (they meet a zero
+    // probability); zero them once here.
+    ok = hipMemset(c->kbuf, 0, (size_t)g.n_kv_heads * c->s_pad_cap * g.head_dim * 2) == hipSuccess &&
+         hipMemset(c->vtbuf, 0, (size_t)g.n_kv_heads * c->s_pad_cap * g.head_dim * 2) == hipSuccess &&
+         hipMemset(c->flag, 0, 256) == hipSuccess;
+    // RoPE table: angle p * theta^(-2j/d) in double precision, rounded to fp32.
+    std::vector<float2> tab((size_t)g.max_pos * 64);
+    for (int p = 0; p < g.max_pos; ++p)
+        for (int j = 0; j < 64; ++j) {
+            const double w = pow(g.rope_theta, -2.0 * j / (double)g.head_dim);
+            const double a = (double)p * w;
+            tab[(size_t)p * 64 + j] = make_float2((float)cos(a), (float)sin(a));
+        }
+    ok = ok && hipMemcpy(c->rope, tab.data(), tab.size() * sizeof(float2), hipMemcpyHostToDevice) == hipSuccess;
+    if (!ok) {
+        free_all(c);
+        delete c;
+        hipGetLastError();
+        return TTSBB_DEVICE_ERROR;
+    }
+    *out = c;
+    return TTSBB_OK;
+}
+
+TTSBB_API void ttsbb_destroy(ttsbb_ctx *ctx) {
+    if (!ctx) return;
+    hipStreamSynchronize(ctx->stream);
+    free_all(ctx);
+    delete ctx;
+}
+
+TTSBB_API ttsbb_status ttsbb_sync(ttsbb_ctx *ctx) {
+    if (!ctx) return TTSBB_INVALID_ARG;
+    if (hipStreamSynchronize(ctx->stream) != hipSuccess) return TTSBB_DEVICE_ERROR;
+    int f = 0;
+    if (hipMemcpy(&f, ctx->flag, sizeof(int), hipMemcpyDeviceToHost) != hipSuccess) return TTSBB_DEVICE_ERROR;
+    if (f) {
+        hipMemset(ctx->flag, 0, sizeof(int));
+        return TTSBB_DEVICE_ERROR;
+    }
+    return TTSBB_OK;
+}
+
+TTSBB_API ttsbb_status ttsbb_codebook_embed(ttsbb_ctx *ctx, int32_t n_rows, int32_t n_cb,
+                                            const int32_t *codes, const void *tables,
+                                            int32_t cb_vocab, const uint8_t *is_text,
+                                            const int32_t *text_ids, const void *text_table,
+                                            int32_t text_vocab, float *out) {
+    if (!ctx || n_rows < 0 || n_cb < 0 || cb_vocab <= 0) return TTSBB_INVALID_ARG;
+    if (n_rows == 0) return TTSBB_OK;
+    if (!out || (n_cb > 0 && (!codes || !tables))) return TTSBB_INVALID_ARG;
+    if (is_text && (!text_ids || !text_table || text_vocab <= 0)) return TTSBB_INVALID_ARG;
+    EmbedArgs a;
+    a.n_rows = n_rows;
+    a.n_cb = n_cb;
+    a.hidden = ctx->cfg.hidden;
+    a.codes = codes;
+    a.code_row_stride = n_cb;
+    a.code_cb_stride = 1;
+    a.audio_row0 = 0;
+    a.tables = tables;
+    a.cb_vocab = cb_vocab;
+    a.is_text = is_text;
+    a.text_prefix = 0;
+    a.text_ids = text_ids;
+    a.text_table = text_table;
+    a.text_vocab = text_vocab;
+    a.out = out;
+    a.flag = ctx->flag;
+    launch_embed(a, ctx->dt, ctx->stream);
+    return launch_failed() ? TTSBB_DEVICE_ERROR : TTSBB_OK;
+}
+
+namespace {
+
+// The post-attention half of a layer and the pre-attention projection; shared by both
+// modes.  x is the fp32 residual stream [M][hidden].
+void qkv_projection(ttsbb_ctx *c, const ttsbb_layer &L, const float *x, int M, bool tapit) {
+    const ttsbb_config &g = c->cfg;
+    launch_rmsnorm(x, g.hidden, M, g.hidden, L.attn_norm, g.rms_eps, c->h, c->dt, c->stream);
+    GemmArgs a = {};
+    a.A = c->h;
+    a.lda = g.hidden;
+    a.M = M;
+    a.K = g.hidden;
+    a.N = c->qkv_w;
+    a.w.p[0] = L.wq;
+    a.w.p[1] = L.wk;
+    a.w.p[2] = L.wv;
+    a.w.start[0] = 0;
+    a.w.start[1] = g.n_heads * g.head_dim;
+    a.w.start[2] = (g.n_heads + g.n_kv_heads) * g.head_dim;
+    a.w.start[3] = c->qkv_w;
+    a.w.nseg = 3;
+    a.C = c->qkv;
+    a.ldc = c->qkv_w;
+    a.epi = EPI_STORE;
+    launch_gemm(a, c->dt, c->stream);
+    if (tapit) {
+        tap_dense(c, TTSBB_TAP_H_ATTN, c->h, c->dt, M, g.hidden, g.hidden);
+        tap_dense(c, TTSBB_TAP_QKV, c->qkv, DT_F32, M, c->qkv_w, c->qkv_w);
+    }
+}
+
+void post_attention(ttsbb_ctx *c, const ttsbb_layer &L, float *x, int M, bool tapit) {
+    const ttsbb_config &g = c->cfg;
+    const int hd_all = g.n_heads * g.head_dim;
+    if (tapit) tap_dense(c, TTSBB_TAP_ATTN, c->attn, c->dt, M, hd_all, hd_all);
+    GemmArgs a = {};
+    a.A = c->attn;
+    a.lda = hd_all;
+    a.M = M;
+    a.K = hd_all;
+    a.N = g.hidden;
+    a.w.p[0] = L.wo;
+    a.w.start[0] = 0;
+    a.w.start[1] = g.hidden;
+    a.w.nseg = 1;
+    a.C = x;
+    a.ldc = g.hidden;
+    a.epi = EPI_ADD;
+    launch_gemm(a, c->dt, c->stream);
+    if (tapit) tap_dense(c, TTSBB_TAP_X_MID, x, DT_F32, M, g.hidden, g.hidden);
+
+    launch_rmsnorm(x, g.hidden, M, g.hidden, L.ffn_norm, g.rms_eps, c->h, c->dt, c->stream);
+    if (tapit) tap_dense(c, TTSBB_TAP_H_FFN, c->h, c->dt, M, g.hidden, g.hidden);
+    GemmArgs u = {};
+    u.A = c->h;
+    u.lda = g.hidden;
+    u.M = M;
+    u.K = g.hidden;
+    u.N = 2 * g.ffn;
+    u.w.p[0] = L.w_gate;
+    u.w.p[1] = L.w_up;
+    u.w.nseg = 2;
+    u.C = c->mlp;
+    u.ldc = g.ffn;
+    u.epi = EPI_SWIGLU;
+    launch_gemm(u, c->dt, c->stream);
+    if (tapit) tap_dense(c, TTSBB_TAP_MLP, c->mlp, c->dt, M, g.ffn, g.ffn);
+
+    GemmArgs d = {};
+    d.A = c->mlp;
+    d.lda = g.ffn;
+    d.M = M;
+    d.K = g.ffn;
+    d.N = g.hidden;
+    d.w.p[0] = L.w_down;
+    d.w.start[0] = 0;
+    d.w.start[1] = g.hidden;
+    d.w.nseg = 1;
+    d.C = x;
+    d.ldc = g.hidden;
+    d.epi = EPI_ADD;
+    launch_gemm(d, c->dt, c->stream);
+    if (tapit) tap_dense(c, TTSBB_TAP_X_OUT, x, DT_F32, M, g.hidden, g.hidden);
+}
+
+void head_gemm(ttsbb_ctx *c, const void *head, int M, int N, float *out, int ldc) {
+    const ttsbb_config &g = c->cfg;
+    GemmArgs a = {};
+    a.A = c->h;
+    a.lda = g.hidden;
+    a.M = M;
+    a.K = g.hidden;
+    a.N = N;
+    a.w.p[0] = head;
+    a.w.start[0] = 0;
+    a.w.start[1] = N;
+    a.w.nseg = 1;
+    a.C = out;
+    a.ldc = ldc;
+    a.epi = EPI_STORE;
+    launch_gemm(a, c->dt, c->stream);
+}
+
+}  // namespace
+
+TTSBB_API ttsbb_status ttsbb_decode_step(ttsbb_ctx *ctx, int32_t batch, float *x, int32_t *positions,
+                                         const int32_t *page_table, int32_t max_pages, void *kv_pool,
+                                         int32_t n_pages, const void *head, int32_t n_groups,
+                                         int32_t group_vocab, int32_t *argmax, float *logits) {
+    if (!ctx || batch < 0) return TTSBB_INVALID_ARG;
+    const ttsbb_config &g = ctx->cfg;
+    if (batch > g.max_rows) return TTSBB_INVALID_ARG;
+    if (batch == 0) return TTSBB_OK;
+    if (!x || !positions) return TTSBB_INVALID_ARG;
+    if (g.n_layers > 0 && (!page_table || max_pages <= 0 || !kv_pool || n_pages <= 0))
+        return TTSBB_INVALID_ARG;
+    if (head) {
+        if (n_groups <= 0 || group_vocab <= 0 || !argmax || !ctx->final_norm) return TTSBB_INVALID_ARG;
+        if ((int64_t)n_groups * group_vocab > g.max_head_cols) return TTSBB_INVALID_ARG;
+    }
+    const int H = g.n_heads, Hkv = g.n_kv_heads, hd = g.head_dim;
+    const int hd_all = H * hd;
+    const size_t layer_elems = (size_t)n_pages * 2 * Hkv * g.kv_page * hd;
+
+    // split of each stream's positions into chunks for the decode attention
+    const int cap = max_pages * g.kv_page;
+    int want = (2048 + batch * Hkv - 1) / (batch * Hkv);
+    if (want > MAX_CHUNKS) want = MAX_CHUNKS;
+    if (want < 1) want = 1;
+    int chunk = round_up((cap + want - 1) / want, g.kv_page);
+    int n_chunks = (cap + chunk - 1) / chunk;
+    if (n_chunks > MAX_CHUNKS) return TTSBB_UNSUPPORTED;
+
+    for (int l = 0; l < g.n_layers; ++l) {
+        const ttsbb_layer &L = ctx->layers[l];
+        const bool tapit = (l == ctx->tap_layer);
+        if (tapit) tap_dense(ctx, TTSBB_TAP_X_IN, x, DT_F32, batch, g.hidden, g.hidden);
+        qkv_projection(ctx, L, x, batch, tapit);
+        void *pool_l = reinterpret_cast<char *>(kv_pool) + (size_t)l * layer_elems * ctx->esz;
+
+        RopeKvArgs r = {};
+        r.qkv = ctx->qkv;
+        r.M = batch;
+        r.H = H;
+        r.Hkv = Hkv;
+        r.q_gain = L.q_norm;
+        r.k_gain = L.k_norm;
+        r.eps = g.rms_eps;
+        r.rope = ctx->rope;
+        r.max_pos = g.max_pos;
+        r.q_out = ctx->q;
+        r.dense = 0;
+        r.pos = positions;
+        r.page_table = page_table;
+        r.max_pages = max_pages;
+        r.n_pages = n_pages;
+        r.page = g.kv_page;
+        r.pool_layer = pool_l;
+        r.flag = ctx->flag;
+        launch_rope_kv(r, ctx->dt, ctx->stream);
+        if (tapit) tap_dense(ctx, TTSBB_TAP_Q, ctx->q, DT_F32, batch, hd_all, hd_all);
+
+        DecodeAttnArgs d = {};
+        d.q = reinterpret_cast<const float *>(ctx->q);
+        d.pool_layer = pool_l;
+        d.pos = positions;
+        d.page_table = page_table;
+        d.max_pages = max_pages;
+        d.n_pages = n_pages;
+        d.page = g.kv_page;
+        d.B = batch;
+        d.H = H;
+        d.Hkv = Hkv;
+        d.chunk = chunk;
+        d.n_chunks = n_chunks;
+        d.part = ctx->part;
+        d.out = ctx->attn;
+        d.scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
+        launch_decode_attn(d, ctx->dt, ctx->stream);
+
+        post_attention(ctx, L, x, batch, tapit);
+    }
+    if (head) {
+        const int N = n_groups * group_vocab;
+        launch_rmsnorm(x, g.hidden, batch, g.hidden, ctx->final_norm, g.rms_eps, ctx->h, ctx->dt, ctx->stream);
+        if (ctx->tap_layer >= 0) tap_dense(ctx, TTSBB_TAP_HEAD_IN, ctx->h, ctx->dt, batch, g.hidden, g.hidden);
+        float *lg = logits ? logits : ctx->logits;
+        head_gemm(ctx, head, batch, N, lg, N);
+        if (ctx->tap_layer >= 0) tap_dense(ctx, TTSBB_TAP_LOGITS, lg, DT_F32, batch, N, N);
+        launch_argmax_groups(lg, batch, N, n_groups, group_vocab, argmax, ctx->stream);
+    }
+    launch_increment(positions, batch, ctx->stream);
+    return launch_failed() ? TTSBB_DEVICE_ERROR : TTSBB_OK;
+}
+
+TTSBB_API ttsbb_status ttsbb_maskgit_pass(ttsbb_ctx *ctx, int32_t n_text, const int32_t *text_ids,
+                                          const void *text_table, int32_t text_vocab,
+                                          int32_t n_frames, int32_t n_cb, int32_t cb_vocab,
+                                          int32_t mask_id, const void *audio_tables,
+                                          const void *audio_heads, int32_t *codes,
+                                          int32_t n_unmask, float layer_penalty, int32_t *pred,
+                                          float *conf, int32_t *picked) {
+    if (!ctx) return TTSBB_INVALID_ARG;
+    const ttsbb_config &g = ctx->cfg;
+    if (n_text < 0 || n_frames <= 0 || n_cb <= 0 || cb_vocab <= 0 || mask_id < 0 ||
+        mask_id >= cb_vocab || n_unmask < 0 || (int64_t)n_unmask > (int64_t)n_cb * n_frames)
+        return TTSBB_INVALID_ARG;
+    if ((int64_t)n_text + n_frames > g.max_rows) return TTSBB_INVALID_ARG;
+    if ((int64_t)n_cb * cb_vocab > g.max_head_cols) return TTSBB_INVALID_ARG;
+    if (n_text > 0 && (!text_ids || !text_table || text_vocab <= 0)) return TTSBB_INVALID_ARG;
+    if (!audio_tables || !audio_heads || !codes || !pred || !conf || (n_unmask > 0 && !picked) ||
+        !ctx->final_norm)
+        return TTSBB_INVALID_ARG;
+    if (!(layer_penalty == layer_penalty)) return TTSBB_INVALID_ARG;
+    if (ctx->dt != DT_BF16) return TTSBB_UNSUPPORTED;
+
+    const int S = n_text + n_frames;
+    const int s_pad = round_up(S, 64);
+    const int H = g.n_heads, Hkv = g.n_kv_heads, hd = g.head_dim;
+    const int hd_all = H * hd;
+
+    EmbedArgs e;
+    e.n_rows = S;
+    e.n_cb = n_cb;
+    e.hidden = g.hidden;
+    e.codes = codes;
+    e.code_row_stride = 1;
+    e.code_cb_stride = n_frames;
+    e.audio_row0 = n_text;
+    e.tables = audio_tables;
+    e.cb_vocab = cb_vocab;
+    e.is_text = nullptr;
+    e.text_prefix = n_text;
+    e.text_ids = text_ids;
+    e.text_table = text_table;
+    e.text_vocab = text_vocab;
+    e.out = ctx->x;
+    e.flag = ctx->flag;
+    launch_embed(e, DT_BF16, ctx->stream);
+
+    for (int l = 0; l < g.n_layers; ++l) {
+        const ttsbb_layer &L = ctx->layers[l];
+        const bool tapit = (l == ctx->tap_layer);
+        if (tapit) tap_dense(ctx, TTSBB_TAP_X_IN, ctx->x, DT_F32, S, g.hidden, g.hidden);
+        qkv_projection(ctx, L, ctx->x, S, tapit);
+
+        RopeKvArgs r = {};
+        r.qkv = ctx->qkv;
+        r.M = S;
+        r.H = H;
+        r.Hkv = Hkv;
+        r.q_gain = L.q_norm;
+        r.k_gain = L.k_norm;
+        r.eps = g.rms_eps;
+        r.rope = ctx->rope;
+        r.max_pos = g.max_pos;
+        r.q_out = ctx->q;
+        r.dense = 1;
+        r.kbuf = ctx->kbuf;
+        r.vtbuf = ctx->vtbuf;
+        r.s_pad = s_pad;
+        r.flag = ctx->flag;
+        launch_rope_kv(r, DT_BF16, ctx->stream);
+        if (tapit) {
+            tap_dense(ctx, TTSBB_TAP_Q, ctx->q, DT_BF16, S, hd_all, hd_all);
+            // K [Hkv][s_pad][hd] -> [S][Hkv][hd];  V^T [Hkv][hd][s_pad] -> [S][Hkv][hd]
+            tap(ctx, TTSBB_TAP_K, ctx->kbuf, DT_BF16, S, Hkv * hd, hd, (int64_t)s_pad * hd, 1, hd);
+            tap(ctx, TTSBB_TAP_V, ctx->vtbuf, DT_BF16, S, Hkv * hd, 1, (int64_t)hd * s_pad, s_pad, hd);
+        }
+
+        FlashArgs f;
+        f.q = reinterpret_cast<const uint16_t *>(ctx->q);
+        f.k = ctx->kbuf;
+        f.vt = ctx->vtbuf;
+        f.S = S;
+        f.s_pad = s_pad;
+        f.H = H;
+        f.Hkv = Hkv;
+        f.scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
+        f.out = reinterpret_cast<uint16_t *>(ctx->attn);
+        launch_flash_attn(f, ctx->stream);
+
+        post_attention(ctx, L, ctx->x, S, tapit);
+    }
+
+    // final norm + heads on the audio window only
+    const int N = n_cb * cb_vocab;
+    launch_rmsnorm(ctx->x + (size_t)n_text * g.hidden, g.hidden, n_frames, g.hidden, ctx->final_norm,
+                   g.rms_eps, ctx->h, DT_BF16, ctx->stream);
+    if (ctx->tap_layer >= 0) tap_dense(ctx, TTSBB_TAP_HEAD_IN, ctx->h, DT_BF16, n_frames, g.hidden, g.hidden);
+    head_gemm(ctx, audio_heads, n_frames, N, ctx->logits, N);
+    if (ctx->tap_layer >= 0) tap_dense(ctx, TTSBB_TAP_LOGITS, ctx->logits, DT_F32, n_frames, N, N);
+    launch_maskgit_scores(ctx->logits, n_frames, N, n_cb, cb_vocab, mask_id, layer_penalty, codes, pred,
+                          conf, ctx->stream);
+    launch_select_update(conf, pred, n_cb * n_frames, n_unmask, codes, picked, ctx->stream);
+    return launch_failed() ? TTSBB_DEVICE_ERROR : TTSBB_OK;
+}
+
+TTSBB_API ttsbb_status ttsbb_unmask_schedule(int32_t n_total, int32_t n_steps, int32_t *out) {
+    if (n_total < 0 || n_steps <= 0 || !out) return TTSBB_INVALID_ARG;
+    const double PI = 3.14159265358979323846;
+    int left = n_total;
+    for (int i = 0; i < n_steps; ++i) {
+        int n;
+        if (i == n_steps - 1) {
+            n = left;
+        } else {
+            const double t0 = 1.0 - cos(0.5 * PI * i / n_steps);
+            const double t1 = 1.0 - cos(0.5 * PI * (i + 1) / n_steps);
+            n = (int)ceil((double)n_total * (t1 - t0));
+            if (n > left) n = left;
+        }
+        out[i] = n;
+        left -= n;
+    }
+    return TTSBB_OK;
+}
+
+TTSBB_API ttsbb_status ttsbb_set_tap_layer(ttsbb_ctx *ctx, int32_t layer) {
+    if (!ctx || layer < -1 || layer >= (ctx->cfg.n_layers > 0 ? ctx->cfg.n_layers : 1))
+        return TTSBB_INVALID_ARG;
+    ctx->tap_layer = layer;
+    if (layer < 0) return TTSBB_OK;
+    for (int t = 0; t < TTSBB_TAP_COUNT; ++t) {
+        if (ctx->taps[t].buf) continue;
+        const size_t bytes = (size_t)ctx->cfg.max_rows * tap_width(ctx, t) * sizeof(float);
+        if (hipMalloc((void **)&ctx->taps[t].buf, bytes) != hipSuccess) {
+            ctx->taps[t].buf = nullptr;
+            hipGetLastError();
+            return TTSBB_OOM;
+        }
+    }
+    return TTSBB_OK;
+}
+
+TTSBB_API ttsbb_status ttsbb_read_tap(ttsbb_ctx *ctx, int32_t tap, float *dst, int64_t n_floats,
+                                      int32_t *rows, int32_t *cols) {
+    if (!ctx || tap < 0 || tap >= TTSBB_TAP_COUNT || !dst) return TTSBB_INVALID_ARG;
+    const Tap &t = ctx->taps[tap];
+    if (!t.buf) return TTSBB_INVALID_ARG;
+    const int64_t n = (int64_t)t.rows * t.cols;
+    if (n_floats < n) return TTSBB_INVALID_ARG;
+    if (rows) *rows = t.rows;
+    if (cols) *cols = t.cols;
+    if (n == 0) return TTSBB_OK;
+    if (hipMemcpyAsync(dst, t.buf, (size_t)n * sizeof(float), hipMemcpyDeviceToDevice, ctx->stream) != hipSuccess)
+        return TTSBB_DEVICE_ERROR;
+    return TTSBB_OK;
+}

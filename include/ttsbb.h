@@ -1,0 +1,195 @@
+/* ttsbb — forward pass of a Qwen3-0.6B-shaped TTS backbone on AMD MI355X (gfx950).
+ *
+ * Plain C99 interface (extern "C"), opaque context, integer status codes with 0 = OK
+ * and negative values for errors.  Every tensor argument of a compute call is a
+ * DEVICE pointer owned by the caller; the library never frees it.  Calls enqueue work
+ * on the stream given at creation and return without synchronising, so a sequence
+ * of calls can be captured into a HIP graph.  Argument errors are found on the host
+ * before anything is enqueued; out-of-range indices met on the device (a code, a
+ * page id, a position) are clamped away from memory and raise a device flag that
+ * ttsbb_sync() reports.
+ *
+ * The model (OmniVoice ARCHITECTURE, "Qwen3 0.6B backbone with custom IO" and "GGUF
+ * layout"; ncnn Qwen3-TTS port, "模型结构拆解"): pre-norm decoder layers
+ *   h  = RMSNorm(x; g_attn)                      input_layernorm
+ *   q,k,v = Wq h, Wk h, Wv h                     no biases
+ *   q,k = per-head RMSNorm(g_q / g_k), then half-rotate RoPE at the token position
+ *   o  = softmax(q k^T / sqrt(head_dim)) v       GQA: query head h reads KV head h / (H/H_kv)
+ *   x1 = x + Wo o
+ *   x2 = x1 + Wd (silu(Wg h2) * Wu h2),  h2 = RMSNorm(x1; g_ffn)   SwiGLU, no biases
+ * with RMSNorm(x; g) = x / sqrt(mean(x^2) + eps) * g and RoPE pairing dimension j with
+ * j + head_dim/2 at angle pos * theta^(-2j/head_dim) (ncnn port, "mRoPE结论").
+ * Supported shapes: head_dim 128, hidden and ffn multiples of 128, n_heads a multiple
+ * of n_kv_heads with group size 1 or 2.
+ *
+ * Precision: in TTSBB_BF16 mode the weights, embedding tables, heads, KV cache and the
+ * operands of every matrix product are bf16; the residual stream, all accumulations,
+ * norms and softmax statistics are fp32.  In TTSBB_F32 mode everything is fp32.
+ */
+#ifndef TTSBB_H
+#define TTSBB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ttsbb_ctx ttsbb_ctx;
+
+typedef enum {
+    TTSBB_OK = 0,
+    TTSBB_INVALID_ARG = -1,   /* NULL where a pointer is required, a size out of range */
+    TTSBB_UNSUPPORTED = -2,   /* a shape or mode these kernels do not implement */
+    TTSBB_OOM = -3,           /* device memory could not be allocated (create only) */
+    TTSBB_DEVICE_ERROR = -4   /* a HIP call failed, or a device-side index check fired */
+} ttsbb_status;
+
+typedef enum { TTSBB_F32 = 0, TTSBB_BF16 = 1 } ttsbb_dtype;
+
+/* Model shape and workspace limits.  Fill with ttsbb_default_config() first. */
+typedef struct {
+    int32_t n_layers;      /* decoder layers (0 is allowed: embedding -> final norm -> head) */
+    int32_t hidden;        /* 1024 */
+    int32_t n_heads;       /* 16 query heads */
+    int32_t n_kv_heads;    /* 8 KV heads */
+    int32_t head_dim;      /* 128 */
+    int32_t ffn;           /* 3072 */
+    float rms_eps;         /* 1e-6, all norms */
+    double rope_theta;     /* 1e6 */
+    int32_t dtype;         /* ttsbb_dtype of weights, tables, heads, KV cache */
+    int32_t kv_page;       /* tokens per KV page: 16 */
+    int32_t max_rows;      /* most tokens in one call (decode batch, MaskGIT sequence) */
+    int32_t max_pos;       /* RoPE positions 0..max_pos-1 are usable */
+    int32_t max_head_cols; /* widest head (n_groups * group_vocab) any call will use */
+} ttsbb_config;
+
+/* Borrowed device pointers of one layer; they must outlive the context.
+ * Gains are fp32 vectors; linear weights are [out][in] row-major in cfg.dtype:
+ * wq [H*d][hidden], wk and wv [Hkv*d][hidden], wo [hidden][H*d],
+ * w_gate and w_up [ffn][hidden], w_down [hidden][ffn]. */
+typedef struct {
+    const float *attn_norm; /* [hidden] */
+    const float *q_norm;    /* [head_dim] */
+    const float *k_norm;    /* [head_dim] */
+    const float *ffn_norm;  /* [hidden] */
+    const void *wq, *wk, *wv, *wo, *w_gate, *w_up, *w_down;
+} ttsbb_layer;
+
+/* Qwen3-0.6B backbone defaults (OmniVoice ARCHITECTURE, "GGUF layout"): 28 layers,
+ * hidden 1024, 16/8 heads of 128, ffn 3072, eps 1e-6, theta 1e6, bf16, 16-token pages. */
+void ttsbb_default_config(ttsbb_config *cfg);
+
+/* Create a context on the current HIP device.  `layers` holds cfg->n_layers entries
+ * (copied; the pointers inside are borrowed).  `final_norm` is the fp32 [hidden] gain
+ * of the last RMSNorm (llm.norm); it may be NULL only if no call uses a head.
+ * `hip_stream` is a hipStream_t (NULL = the null stream).  Allocates the workspace
+ * (sized by max_rows, max_pos, max_head_cols) and the fp32 RoPE cos/sin table, which
+ * is computed on the host in double precision.  Returns TTSBB_OOM if that fails. */
+ttsbb_status ttsbb_create(const ttsbb_config *cfg, const ttsbb_layer *layers,
+                          const float *final_norm, void *hip_stream, ttsbb_ctx **out);
+
+void ttsbb_destroy(ttsbb_ctx *ctx);
+
+const char *ttsbb_status_str(ttsbb_status s);
+
+/* Wait for the context's stream; report (and clear) the device-side index flag. */
+ttsbb_status ttsbb_sync(ttsbb_ctx *ctx);
+
+/* Summed codebook embedding (OmniVoice ARCHITECTURE, "Qwen3 0.6B backbone with custom
+ * IO": rows k*cb_vocab + code of a flattened [n_cb*cb_vocab][hidden] table, summed over
+ * the n_cb codebooks; ncnn port, "模型结构拆解": the frame's codebook embeddings are
+ * summed into the next input).
+ *   out[r] = sum_{k<n_cb} tables[k*cb_vocab + codes[r*n_cb + k]]      (audio rows)
+ *   out[r] = text_table[text_ids[r]]               (rows with is_text[r] != 0)
+ * codes int32 [n_rows][n_cb]; tables cfg.dtype; is_text uint8 [n_rows] or NULL (all
+ * audio); text_ids int32 [n_rows] and text_table [text_vocab][hidden] needed only if
+ * is_text is given; out fp32 [n_rows][hidden].  The sum is formed in double precision
+ * in codebook order and rounded once to fp32.  n_rows may be 0 (no work). */
+ttsbb_status ttsbb_codebook_embed(ttsbb_ctx *ctx, int32_t n_rows, int32_t n_cb,
+                                  const int32_t *codes, const void *tables, int32_t cb_vocab,
+                                  const uint8_t *is_text, const int32_t *text_ids,
+                                  const void *text_table, int32_t text_vocab, float *out);
+
+/* One q_len=1 decode step of every layer for `batch` independent streams (ncnn port,
+ * "单token SDPA问题与host attention": RoPE + KV append + GQA attention per layer).
+ *   x          fp32 [batch][hidden], in: the embedded token; out: the residual stream
+ *              after the last layer (before the final norm).
+ *   positions  int32 [batch], in: the position of this token = tokens already cached;
+ *              incremented by one on the device at the end of the call.
+ *   page_table int32 [batch][max_pages]: pool page of each kv_page-token block.
+ *   kv_pool    cfg.dtype [n_layers][n_pages][2 (K, V)][n_kv_heads][kv_page][head_dim];
+ *              K is stored normalised and rotated.  The token's K and V are written at
+ *              (page_table[b][p / kv_page], p % kv_page) before it attends to 0..p.
+ *   head       optional [n_groups*group_vocab][hidden] (cfg.dtype): if not NULL the
+ *              final RMSNorm and the head are applied and argmax int32 [batch][n_groups]
+ *              receives the greedy class of each group (ties: lowest id).
+ *   logits     optional fp32 [batch][n_groups*group_vocab] copy of the head output.
+ * Positions >= max_pages*kv_page or page ids outside [0, n_pages) raise the device
+ * flag and skip the write. */
+ttsbb_status ttsbb_decode_step(ttsbb_ctx *ctx, int32_t batch, float *x, int32_t *positions,
+                               const int32_t *page_table, int32_t max_pages, void *kv_pool,
+                               int32_t n_pages, const void *head, int32_t n_groups,
+                               int32_t group_vocab, int32_t *argmax, float *logits);
+
+/* One MaskGIT step (OmniVoice ARCHITECTURE, "MaskGIT decoder" and "Inner-loop
+ * optimisations"): embed n_text text tokens then n_frames audio frames (sum of n_cb
+ * codebook rows, mask_id included as a code), run every layer with bidirectional
+ * attention over all S = n_text + n_frames positions (RoPE positions 0..S-1, no cache),
+ * apply the final RMSNorm and the per-codebook heads on the audio window only, then
+ *   lp   = logits - logsumexp over the cb_vocab classes of codebook k
+ *   pred = argmax over classes != mask_id (ties: lowest id)
+ *   conf = lp[pred] - k * layer_penalty, or -inf where codes[k][t] != mask_id
+ * and unmask the n_unmask highest conf over the flat index f = k*n_frames + t (ties:
+ * lowest f): codes[f] = pred[f].  picked[r] is the flat index of rank r, or -1 where
+ * fewer than r+1 positions were still masked.
+ *   text_ids int32 [n_text]; text_table [text_vocab][hidden]; audio_tables and
+ *   audio_heads [n_cb*cb_vocab][hidden] (cfg.dtype); codes int32 [n_cb][n_frames]
+ *   in/out; pred int32 and conf fp32 [n_cb][n_frames]; picked int32 [n_unmask].
+ * Requires cfg.dtype == TTSBB_BF16. */
+ttsbb_status ttsbb_maskgit_pass(ttsbb_ctx *ctx, int32_t n_text, const int32_t *text_ids,
+                                const void *text_table, int32_t text_vocab, int32_t n_frames,
+                                int32_t n_cb, int32_t cb_vocab, int32_t mask_id,
+                                const void *audio_tables, const void *audio_heads,
+                                int32_t *codes, int32_t n_unmask, float layer_penalty,
+                                int32_t *pred, float *conf, int32_t *picked);
+
+/* Host helper: how many positions each of n_steps MaskGIT steps unmasks (OmniVoice
+ * ARCHITECTURE, "MaskGIT decoder": ceil(N * (t[i+1] - t[i])) over a time grid), on the
+ * cosine grid t_i = 1 - cos(pi/2 * i/n_steps); each count is capped at what is left and
+ * the last step takes the remainder.  out int32 [n_steps] is HOST memory. */
+ttsbb_status ttsbb_unmask_schedule(int32_t n_total, int32_t n_steps, int32_t *out);
+
+/* Debug taps: fp32 copies of one layer's intermediates from the next calls. */
+typedef enum {
+    TTSBB_TAP_X_IN = 0,    /* residual stream entering the layer   [rows][hidden] */
+    TTSBB_TAP_H_ATTN = 1,  /* input_layernorm output (GEMM operand) [rows][hidden] */
+    TTSBB_TAP_QKV = 2,     /* q|k|v projections before the head norms [rows][(H+2Hkv)*d] */
+    TTSBB_TAP_Q = 3,       /* q after head norm + RoPE, as attention reads it [rows][H*d] */
+    TTSBB_TAP_K = 4,       /* MaskGIT only: K after head norm + RoPE [rows][Hkv*d] */
+    TTSBB_TAP_V = 5,       /* MaskGIT only: V [rows][Hkv*d] */
+    TTSBB_TAP_ATTN = 6,    /* attention output (GEMM operand) [rows][H*d] */
+    TTSBB_TAP_X_MID = 7,   /* x + Wo o                             [rows][hidden] */
+    TTSBB_TAP_H_FFN = 8,   /* post_attention_layernorm output      [rows][hidden] */
+    TTSBB_TAP_MLP = 9,     /* silu(gate) * up (GEMM operand)       [rows][ffn] */
+    TTSBB_TAP_X_OUT = 10,  /* layer output                         [rows][hidden] */
+    TTSBB_TAP_HEAD_IN = 11,/* final-normed head operand (not per layer) [rows][hidden] */
+    TTSBB_TAP_LOGITS = 12, /* head output (not per layer) [rows][head cols] */
+    TTSBB_TAP_COUNT = 13
+} ttsbb_tap;
+
+/* Record taps of `layer` (0-based) in the following calls; -1 turns taps off.
+ * Allocates the tap buffers (not for use under graph capture). */
+ttsbb_status ttsbb_set_tap_layer(ttsbb_ctx *ctx, int32_t layer);
+
+/* Copy tap `tap` of the last call into dst (device fp32, n_floats elements); the rows
+ * and width of the tap are written to *rows and *cols (host, may be NULL). */
+ttsbb_status ttsbb_read_tap(ttsbb_ctx *ctx, int32_t tap, float *dst, int64_t n_floats,
+                            int32_t *rows, int32_t *cols);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TTSBB_H */

@@ -1,0 +1,144 @@
+"""Helpers of the GPU parity tests: build a ttsbb context over seeded device weights, the
+matching oracle layers on the host, and the comparison rules for discrete outputs."""
+from __future__ import annotations
+
+import numpy as np
+
+from oracle import backbone as O
+from workload import configs as CFG
+from workload import device as DEV
+from workload import gen
+
+
+def torch():
+    import torch as _t
+    return _t
+
+
+def widen(a: np.ndarray) -> np.ndarray:
+    return gen.bf16_bits_to_f32(a) if a.dtype == np.uint16 else np.asarray(a, np.float32)
+
+
+def dims_of(shape: CFG.Shape) -> O.Dims:
+    return O.Dims(hidden=shape.hidden, n_heads=shape.n_heads, n_kv_heads=shape.n_kv_heads,
+                  head_dim=shape.head_dim, ffn=shape.ffn, eps=shape.eps, theta=shape.theta)
+
+
+class Model:
+    """Device weights + ttsbb context, and (lazily) the oracle's fp64 layers."""
+
+    def __init__(self, shape: CFG.Shape, n_layers: int, bf16: bool, seed: int = 0,
+                 gains: str = "ones", max_rows: int = 1024, max_pos: int = 8192,
+                 max_head_cols: int = 8200):
+        from codec_token_tts_amd import ttsbb as T
+        self.T = T
+        self.shape, self.n_layers, self.bf16, self.seed, self.gains = shape, n_layers, bf16, seed, gains
+        self.dev = [DEV.layer_weights(seed, shape, l, bf16, gains) for l in range(n_layers)]
+        self.final_norm = DEV.host_to_device(CFG.final_norm(seed, shape, gains))
+        cfg = T.ttsbb_default_config()
+        cfg.n_layers = n_layers
+        cfg.hidden, cfg.n_heads, cfg.n_kv_heads = shape.hidden, shape.n_heads, shape.n_kv_heads
+        cfg.head_dim, cfg.ffn = shape.head_dim, shape.ffn
+        cfg.rms_eps, cfg.rope_theta = shape.eps, shape.theta
+        cfg.dtype = T.BF16 if bf16 else T.F32
+        cfg.max_rows, cfg.max_pos, cfg.max_head_cols = max_rows, max_pos, max_head_cols
+        self.cfg = cfg
+        self.layers = [T.make_layer(d["attn_norm"], d["q_norm"], d["k_norm"], d["ffn_norm"],
+                                    d["wq"], d["wk"], d["wv"], d["wo"], d["w_gate"], d["w_up"],
+                                    d["w_down"]) for d in self.dev]
+        stream = torch().cuda.current_stream().cuda_stream
+        self.ctx = T.ttsbb_create(cfg, self.layers, self.final_norm, stream)
+        self._oracle_layers = None
+
+    def oracle_layers(self):
+        if self._oracle_layers is None:
+            out = []
+            for l in range(self.n_layers):
+                h = CFG.layer_weights(self.seed, self.shape, l, self.bf16, self.gains)
+                out.append(O.Layer.from_arrays({k: widen(v) for k, v in h.items()}))
+            self._oracle_layers = out
+        return self._oracle_layers
+
+    def oracle_final_norm(self):
+        return CFG.final_norm(self.seed, self.shape, self.gains).astype(np.float64)
+
+    def close(self):
+        if self.ctx:
+            self.T.ttsbb_destroy(self.ctx)
+            self.ctx = None
+
+
+def read_tap(model: Model, tap: int, rows: int, cols: int) -> np.ndarray:
+    t = torch().empty(rows * cols, dtype=torch().float32, device="cuda")
+    r, c = model.T.ttsbb_read_tap(model.ctx, tap, t, rows * cols)
+    assert (r, c) == (rows, cols), (r, c, rows, cols)
+    torch().cuda.synchronize()
+    return t.cpu().numpy().reshape(rows, cols).astype(np.float64)
+
+
+def normwise(gpu: np.ndarray, ref: np.ndarray) -> float:
+    """max |gpu - ref| / max |ref| over the tensor."""
+    gpu = np.asarray(gpu, np.float64)
+    ref = np.asarray(ref, np.float64)
+    den = np.max(np.abs(ref))
+    return float(np.max(np.abs(gpu - ref)) / (den if den > 0 else 1.0))
+
+
+def check_argmax_groups(gpu_choice: np.ndarray, gpu_logits: np.ndarray, ref_logits: np.ndarray,
+                        exclude=None):
+    """Discrete parity of a greedy choice.
+
+    1. The GPU's choice is exactly the argmax of the GPU's own logits (ties -> lowest id).
+    2. With delta = max |gpu - ref| over the group, the choice equals the reference argmax
+       wherever the reference's top-2 gap exceeds 2*delta; elsewhere (a near tie) it must
+       be within 2*delta of the reference maximum.
+    Returns the number of near-tie groups.  Arrays are [..., V]."""
+    g = np.asarray(gpu_logits, np.float64)
+    r = np.asarray(ref_logits, np.float64)
+    ch = np.asarray(gpu_choice).reshape(g.shape[:-1])
+    if exclude is not None:
+        g = g.copy()
+        r = r.copy()
+        g[..., exclude] = -np.inf
+        r[..., exclude] = -np.inf
+    own = np.argmax(g, axis=-1)
+    assert np.array_equal(own, ch), "choice is not the argmax of the GPU's own logits"
+    fin = np.isfinite(r)
+    delta = np.max(np.where(fin, np.abs(g - r), 0.0), axis=-1)
+    top2 = np.sort(r, axis=-1)[..., -2:]
+    gap = top2[..., 1] - top2[..., 0]
+    ref_arg = np.argmax(r, axis=-1)
+    clear = gap > 2 * delta
+    assert np.array_equal(ch[clear], ref_arg[clear]), "argmax differs where the margin is clear"
+    chosen = np.take_along_axis(r, ch[..., None], axis=-1)[..., 0]
+    assert np.all(chosen >= top2[..., 1] - 2 * delta - 1e-12), "near-tie choice is not near the top"
+    return int(np.count_nonzero(~clear))
+
+
+def check_topn(picked: np.ndarray, conf_gpu: np.ndarray, conf_ref: np.ndarray, n: int):
+    """Discrete parity of the top-n selection.
+
+    1. picked is exactly the top-n of the GPU's own scores (decreasing, ties -> lower flat
+       index, -1 where fewer than n are finite).
+    2. Against the reference, with eps = max |gpu - ref| over finite scores: every element
+       whose reference score clears the reference's n-th score by 2*eps is picked, and no
+       picked element falls 2*eps below it.  Returns the count of boundary elements."""
+    cg = np.asarray(conf_gpu, np.float64).reshape(-1)
+    cr = np.asarray(conf_ref, np.float64).reshape(-1)
+    order = sorted([(-cg[i], i) for i in range(cg.size) if np.isfinite(cg[i])])
+    own = [i for _, i in order[:n]] + [-1] * max(0, n - len(order))
+    assert list(np.asarray(picked).reshape(-1)) == own[:n], "picked is not the top-n of the GPU scores"
+    assert np.array_equal(np.isfinite(cg), np.isfinite(cr)), "masked positions differ"
+    fin = np.isfinite(cr)
+    if not fin.any() or n == 0:
+        return 0
+    eps = float(np.max(np.abs(cg[fin] - cr[fin])))
+    ranked = np.sort(cr[fin])[::-1]
+    if n > ranked.size:
+        return 0
+    thr = ranked[n - 1]
+    sel = set(int(i) for i in picked if i >= 0)
+    must = np.nonzero(fin & (cr > thr + 2 * eps))[0]
+    assert all(int(i) in sel for i in must), "a clearly winning position was not picked"
+    assert all(cr[i] >= thr - 2 * eps for i in sel), "a clearly losing position was picked"
+    return int(np.count_nonzero(fin & (np.abs(cr - thr) <= 2 * eps)))

@@ -1,0 +1,322 @@
+"""GPU parity of the HIP path against the oracle at small sizes (several tiles, ragged
+tails, degenerate cases).  Every call goes through the C ABI (codec_token_tts_amd.ttsbb).
+
+Tolerances (derived in the design notes):
+* fp32 mode: 1e-4 max-abs on every intermediate and the layer output.
+* bf16 mode: normwise max-relative max|gpu-ref|/max|ref| <= 2e-2 on continuous outputs.
+* discrete outputs: exact argmax / top-n of the GPU's own scores, and agreement with the
+  oracle wherever the oracle's margin exceeds twice the measured score error.
+* the codebook embedding: bit-exact (fp64 sum in codebook order, one rounding).
+"""
+import numpy as np
+import pytest
+
+from oracle import backbone as O
+from workload import configs as CFG
+from workload import device as DEV
+from workload import gen
+from workload.gen import stream_id
+
+from gpu_setup import (Model, check_argmax_groups, check_topn, dims_of, normwise, read_tap,
+                       torch, widen)
+
+pytestmark = pytest.mark.gpu
+
+
+def t_i32(a):
+    return torch().from_numpy(np.ascontiguousarray(a, np.int32)).to("cuda")
+
+
+def t_f32(a):
+    return torch().from_numpy(np.ascontiguousarray(a, np.float32)).to("cuda")
+
+
+# ---------------------------------------------------------------------------------------
+def test_device_inputs_match_host_generator():
+    for bf16 in (True, False):
+        t = DEV.normal((3, 1001), 5, 77, 0.02, bf16, start=9)
+        h = gen.fast_normal(5, 77, (3, 1001), 0.02, start=9, bf16=bf16)
+        a = t.cpu().numpy()
+        assert np.array_equal(a.view(np.uint16) if bf16 else a, h)
+    shape = CFG.Shape(n_layers=2)
+    lengths = [5, 33, 0]
+    pt, n_pages = CFG.page_table(3, [n + 1 for n in lengths], extra_pages=2)
+    pool = DEV.kv_pool(3, shape, 2, lengths, pt, n_pages, True).cpu().numpy().view(np.uint16)
+    used = set()
+    for l in range(2):
+        for b, n in enumerate(lengths):
+            k, v = CFG.kv_prefill(3, shape, l, b, n, True)
+            for p in range(n):
+                pg = pt[b, p // 16]
+                used.add(pg)
+                assert np.array_equal(pool[l, pg, 0, :, p % 16, :], k[p])
+                assert np.array_equal(pool[l, pg, 1, :, p % 16, :], v[p])
+    free = [p for p in range(n_pages) if p not in used]
+    assert np.all(pool[:, free] == 0)
+
+
+# ---------------------------------------------------------------------------------------
+@pytest.mark.parametrize("bf16", [True, False])
+def test_codebook_embed_bit_exact(bf16):
+    m = Model(CFG.Shape(), 0, bf16)
+    T = m.T
+    try:
+        K, V, R, TV = 16, 2048, 37, 500
+        tables_h = CFG.table(0, gen.KIND_CB_TABLE, 0, K * V, 1024, bf16)
+        text_h = CFG.table(0, gen.KIND_TEXT_TABLE, 0, TV, 1024, bf16)
+        codes = gen.uniform_int(0, stream_id(gen.KIND_CODES, 1), (R, K), V)
+        codes[3, :] = V - 1
+        codes[4, :] = 0
+        is_text = np.zeros(R, np.uint8)
+        is_text[[0, 7, 36]] = 1
+        text_ids = gen.uniform_int(0, stream_id(gen.KIND_TEXT_IDS, 1), (R,), TV)
+        out = torch().empty((R, 1024), dtype=torch().float32, device="cuda")
+        T.ttsbb_codebook_embed(m.ctx, R, K, t_i32(codes), DEV.host_to_device(tables_h), V,
+                               DEV.host_to_device(is_text), t_i32(text_ids),
+                               DEV.host_to_device(text_h), TV, out)
+        assert T.ttsbb_sync(m.ctx) == T.OK
+        got = out.cpu().numpy()
+        ref = O.codebook_embed(codes, widen(tables_h), V)
+        ref[is_text == 1] = widen(text_h)[text_ids[is_text == 1]]
+        assert np.array_equal(got, ref.astype(np.float32))
+        # K = 1 is a lookup; zero rows are a no-op
+        out1 = torch().empty((R, 1024), dtype=torch().float32, device="cuda")
+        T.ttsbb_codebook_embed(m.ctx, R, 1, t_i32(codes[:, :1]), DEV.host_to_device(tables_h), V,
+                               None, None, None, 0, out1)
+        assert np.array_equal(out1.cpu().numpy(), widen(tables_h)[codes[:, 0]])
+        assert T.ttsbb_codebook_embed(m.ctx, 0, K, None, None, V, None, None, None, 0, None) == T.OK
+        # an out-of-range code raises the device flag, reported by ttsbb_sync, then clears
+        bad = codes.copy()
+        bad[5, 2] = V
+        T.ttsbb_codebook_embed(m.ctx, R, K, t_i32(bad), DEV.host_to_device(tables_h), V, None,
+                               None, None, 0, out)
+        assert T.ttsbb_sync(m.ctx) == T.DEVICE_ERROR
+        assert T.ttsbb_sync(m.ctx) == T.OK
+    finally:
+        m.close()
+
+
+# ---------------------------------------------------------------------------------------
+def run_decode(m: Model, lengths, seed, head=None, tap_layer=None):
+    """One decode step of len(lengths) streams; returns GPU results and oracle results."""
+    T = m.T
+    shape = m.shape
+    B = len(lengths)
+    pt, n_pages = CFG.page_table(seed, [n + 1 for n in lengths], extra_pages=3)
+    pool = DEV.kv_pool(seed, shape, m.n_layers, lengths, pt, n_pages, m.bf16)
+    x_in = gen.fast_normal(seed, stream_id(gen.KIND_X_IN, 0), (B, shape.hidden), 1.0)
+    x = t_f32(x_in)
+    pos = t_i32(lengths)
+    res = {}
+    if tap_layer is not None:
+        T.ttsbb_set_tap_layer(m.ctx, tap_layer)
+    if head is not None:
+        hd_dev, G, V = head[:3]
+        am = torch().empty((B, G), dtype=torch().int32, device="cuda")
+        lg = torch().empty((B, G * V), dtype=torch().float32, device="cuda")
+        T.ttsbb_decode_step(m.ctx, B, x, pos, t_i32(pt), pt.shape[1], pool, n_pages, hd_dev, G, V, am, lg)
+    else:
+        T.ttsbb_decode_step(m.ctx, B, x, pos, t_i32(pt), pt.shape[1], pool, n_pages)
+    assert T.ttsbb_sync(m.ctx) == T.OK
+    res["x"] = x.cpu().numpy()
+    res["pos"] = pos.cpu().numpy()
+    res["pool"] = DEV.bits_to_f32(pool) if m.bf16 else pool.cpu().numpy()
+    if head is not None:
+        res["argmax"] = am.cpu().numpy()
+        res["logits"] = lg.cpu().numpy()
+    if tap_layer is not None:
+        taps = {}
+        w = dict(h=(T.TAP_H_ATTN, shape.hidden),
+                 qkv=(T.TAP_QKV, (shape.n_heads + 2 * shape.n_kv_heads) * shape.head_dim),
+                 q=(T.TAP_Q, shape.n_heads * shape.head_dim),
+                 o=(T.TAP_ATTN, shape.n_heads * shape.head_dim), x1=(T.TAP_X_MID, shape.hidden),
+                 h2=(T.TAP_H_FFN, shape.hidden), m=(T.TAP_MLP, shape.ffn),
+                 x2=(T.TAP_X_OUT, shape.hidden), x_in=(T.TAP_X_IN, shape.hidden))
+        for k, (tp, cols) in w.items():
+            taps[k] = read_tap(m, tp, B, cols)
+        res["taps"] = taps
+        T.ttsbb_set_tap_layer(m.ctx, -1)
+
+    cache = O.KVCache(m.n_layers, B)
+    for l in range(m.n_layers):
+        for b, n in enumerate(lengths):
+            if n:
+                k, v = CFG.kv_prefill(seed, shape, l, b, n, m.bf16)
+                cache.set(l, b, widen(k), widen(v))
+    rec = {}
+    out = O.decode_step(x_in, list(lengths), cache, m.oracle_layers(), dims_of(shape),
+                        record_layer=tap_layer, record=rec)
+    ref = {"x": out, "rec": rec, "cache": cache, "pt": pt}
+    if head is not None:
+        y, lg_ref = O.head_logits(out, m.oracle_final_norm(), head[3], shape.eps)
+        ref["logits"] = lg_ref
+    return res, ref
+
+
+def rec_as_taps(rec, B):
+    return dict(h=rec["h"], qkv=np.concatenate([rec["q_raw"].reshape(B, -1), rec["k_raw"].reshape(B, -1),
+                                                 rec["v"].reshape(B, -1)], axis=1),
+                q=rec["q"].reshape(B, -1), o=rec["o"].reshape(B, -1), x1=rec["x1"], h2=rec["h2"],
+                m=rec["m"], x2=rec["x2"])
+
+
+def test_decode_fp32_single_layer_kv64():
+    """One layer, fp32, batch 1, KV prefilled to 64 (the fp32 single-layer workload)."""
+    w = CFG.c1()
+    m = Model(w.shape, 1, False, seed=w.seed)
+    try:
+        res, ref = run_decode(m, [64], w.seed, tap_layer=0)
+        assert np.max(np.abs(res["x"] - ref["x"])) <= 1e-4
+        taps, rtaps = res["taps"], rec_as_taps(ref["rec"], 1)
+        for k in rtaps:
+            assert np.max(np.abs(taps[k] - rtaps[k])) <= 1e-4, k
+        # K and V of the new token sit at position 64 of the paged pool
+        pg = ref["pt"][0, 64 // 16]
+        np.testing.assert_allclose(res["pool"][0, pg, 0, :, 0, :], ref["rec"]["k"][0], atol=1e-4)
+        np.testing.assert_allclose(res["pool"][0, pg, 1, :, 0, :], ref["rec"]["v"][0], atol=1e-4)
+        assert res["pos"].tolist() == [65]
+    finally:
+        m.close()
+
+
+def test_decode_fp32_ragged_batch_random_gains():
+    shape = CFG.Shape(n_layers=2)
+    m = Model(shape, 2, False, seed=11, gains="random")
+    try:
+        lengths = [0, 5, 16, 17, 40]
+        res, ref = run_decode(m, lengths, 11, tap_layer=1)
+        assert np.max(np.abs(res["x"] - ref["x"])) <= 1e-4
+        rtaps = rec_as_taps(ref["rec"], len(lengths))
+        for k in rtaps:
+            assert np.max(np.abs(res["taps"][k] - rtaps[k])) <= 1e-4, k
+        assert res["pos"].tolist() == [n + 1 for n in lengths]
+    finally:
+        m.close()
+
+
+@pytest.mark.parametrize("lengths", [[3, 300, 31], [0, 1, 15, 16, 17, 33, 64, 100, 129, 250, 7]])
+def test_decode_bf16_ragged_with_head(lengths):
+    """bf16, 2 layers; batch 3 takes the weight-streaming path, batch 11 the MFMA path."""
+    shape = CFG.Shape(n_layers=2)
+    m = Model(shape, 2, True, seed=5, gains="random")
+    try:
+        G, V = 3, 37
+        head_h = CFG.table(5, gen.KIND_HEAD, 0, G * V, shape.hidden, True)
+        head = (DEV.host_to_device(head_h), G, V, widen(head_h))
+        res, ref = run_decode(m, lengths, 5, head=head, tap_layer=0)
+        assert normwise(res["x"], ref["x"]) <= 2e-2
+        rtaps = rec_as_taps(ref["rec"], len(lengths))
+        for k in rtaps:
+            assert normwise(res["taps"][k], rtaps[k]) <= 2e-2, k
+        assert normwise(res["logits"], ref["logits"]) <= 2e-2
+        B = len(lengths)
+        check_argmax_groups(res["argmax"], res["logits"].reshape(B, G, V),
+                            ref["logits"].reshape(B, G, V))
+    finally:
+        m.close()
+
+
+# ---------------------------------------------------------------------------------------
+def run_maskgit(m: Model, n_text, n_frames, n_cb, V, mask_id, n_unmask, seed, tap_layer=None,
+                text_vocab=500, masked_frac=0.5):
+    T = m.T
+    shape = m.shape
+    text_h = CFG.table(seed, gen.KIND_TEXT_TABLE, 0, text_vocab, shape.hidden, True)
+    tab_h = CFG.table(seed, gen.KIND_CB_TABLE, 0, n_cb * V, shape.hidden, True)
+    head_h = CFG.table(seed, gen.KIND_HEAD, 0, n_cb * V, shape.hidden, True)
+    text_ids = gen.uniform_int(seed, stream_id(gen.KIND_TEXT_IDS, 0), (n_text,), text_vocab)
+    codes = gen.uniform_int(seed, stream_id(gen.KIND_CODES, 0), (n_cb, n_frames), V - 1)
+    perm = gen.permutation(seed, stream_id(gen.KIND_MASK_PERM, 0), n_cb * n_frames)
+    codes.reshape(-1)[perm[:int(masked_frac * n_cb * n_frames)]] = mask_id
+    codes_d = t_i32(codes)
+    pred = torch().empty((n_cb, n_frames), dtype=torch().int32, device="cuda")
+    conf = torch().empty((n_cb, n_frames), dtype=torch().float32, device="cuda")
+    picked = torch().empty(max(1, n_unmask), dtype=torch().int32, device="cuda")
+    T.ttsbb_set_tap_layer(m.ctx, 0 if tap_layer is None else tap_layer)
+    T.ttsbb_maskgit_pass(m.ctx, n_text, t_i32(text_ids), DEV.host_to_device(text_h), text_vocab,
+                         n_frames, n_cb, V, mask_id, DEV.host_to_device(tab_h),
+                         DEV.host_to_device(head_h), codes_d, n_unmask, 5.0, pred, conf, picked)
+    assert T.ttsbb_sync(m.ctx) == T.OK
+    res = dict(codes=codes_d.cpu().numpy(), pred=pred.cpu().numpy(), conf=conf.cpu().numpy(),
+               picked=picked.cpu().numpy()[:n_unmask],
+               logits=read_tap(m, T.TAP_LOGITS, n_frames, n_cb * V),
+               head_in=read_tap(m, T.TAP_HEAD_IN, n_frames, shape.hidden))
+    S = n_text + n_frames
+    if tap_layer is not None:
+        res["taps"] = {k: read_tap(m, tp, S, c) for k, (tp, c) in dict(
+            x_in=(T.TAP_X_IN, shape.hidden), q=(T.TAP_Q, shape.n_heads * 128),
+            k=(T.TAP_K, shape.n_kv_heads * 128), v=(T.TAP_V, shape.n_kv_heads * 128),
+            o=(T.TAP_ATTN, shape.n_heads * 128), x1=(T.TAP_X_MID, shape.hidden),
+            m=(T.TAP_MLP, shape.ffn), x2=(T.TAP_X_OUT, shape.hidden)).items()}
+    T.ttsbb_set_tap_layer(m.ctx, -1)
+
+    rec, lrec = {}, {}
+    x0 = O.hybrid_embed(text_ids, widen(text_h), codes, widen(tab_h), V)
+    if tap_layer is not None:
+        O.backbone_full(x0, m.oracle_layers(), dims_of(shape), causal=False,
+                        record_layer=tap_layer, record=lrec)
+    new_codes, pred_r, conf_r, picked_r = O.maskgit_pass(
+        text_ids, widen(text_h), codes, widen(tab_h), widen(head_h), m.oracle_layers(),
+        m.oracle_final_norm(), dims_of(shape), V, mask_id, 5.0, n_unmask, record=rec)
+    ref = dict(codes_in=codes, rec=rec, lrec=lrec, conf=conf_r, pred=pred_r, x0=x0)
+    return res, ref
+
+
+def check_maskgit(res, ref, n_cb, n_frames, V, mask_id, n_unmask, tol=2e-2):
+    rec = ref["rec"]
+    assert normwise(res["logits"], rec["logits"]) <= tol
+    g = res["logits"].reshape(n_frames, n_cb, V).transpose(1, 0, 2)
+    r = rec["logits"].reshape(n_frames, n_cb, V).transpose(1, 0, 2)
+    check_argmax_groups(res["pred"], g, r, exclude=mask_id)
+    # confidence: same masked set, and within twice the logit error
+    fin = np.isfinite(ref["conf"])
+    assert np.array_equal(np.isfinite(res["conf"]), fin)
+    delta = np.max(np.abs(res["logits"] - rec["logits"]))
+    assert np.max(np.abs(res["conf"][fin] - ref["conf"][fin])) <= 2 * delta + 1e-5
+    check_topn(res["picked"], res["conf"], ref["conf"], n_unmask)
+    # the update writes pred at the picked positions and nothing else
+    assert np.array_equal(res["codes"], O.apply_picks(ref["codes_in"], res["pred"], res["picked"]))
+
+
+def test_maskgit_zero_layers_head_and_selection():
+    """n_layers = 0: embedding -> final norm -> heads -> scores -> selection."""
+    m = Model(CFG.Shape(n_layers=0), 0, True, seed=3, gains="random")
+    try:
+        n_text, n_frames, n_cb, V, mask = 5, 83, 4, 65, 64
+        n = 50
+        res, ref = run_maskgit(m, n_text, n_frames, n_cb, V, mask, n, 3)
+        check_maskgit(res, ref, n_cb, n_frames, V, mask, n, tol=1e-2)
+    finally:
+        m.close()
+
+
+@pytest.mark.parametrize("n_text,n_frames,n_unmask", [(13, 57, 40), (0, 64, 150), (70, 3, 6)])
+def test_maskgit_two_layers(n_text, n_frames, n_unmask):
+    """bf16, 2 bidirectional layers, ragged sequence (several 64-key blocks and a tail),
+    heads whose width is not a tile multiple; n_unmask beyond the masked count -> -1."""
+    m = Model(CFG.Shape(n_layers=2), 2, True, seed=4, gains="random")
+    try:
+        n_cb, V, mask = 3, 33, 32
+        res, ref = run_maskgit(m, n_text, n_frames, n_cb, V, mask, n_unmask, 4, tap_layer=1)
+        check_maskgit(res, ref, n_cb, n_frames, V, mask, n_unmask)
+        lrec = ref["lrec"]
+        S = n_text + n_frames
+        for k, rk in dict(x_in=None, q="q", k="k", v="v", o="o", x1="x1", m="m", x2="x2").items():
+            if rk is None:
+                continue
+            assert normwise(res["taps"][k], lrec[rk].reshape(S, -1)) <= 2e-2, k
+        if n_unmask > (ref["codes_in"] == mask).sum():
+            assert (res["picked"] == -1).sum() == n_unmask - (ref["codes_in"] == mask).sum()
+    finally:
+        m.close()
+
+
+def test_maskgit_deterministic():
+    m = Model(CFG.Shape(n_layers=1), 1, True, seed=9)
+    try:
+        a, _ = run_maskgit(m, 9, 40, 2, 33, 32, 10, 9)
+        b, _ = run_maskgit(m, 9, 40, 2, 33, 32, 10, 9)
+        for k in ("codes", "pred", "conf", "picked", "logits"):
+            assert np.array_equal(a[k], b[k]), k
+    finally:
+        m.close()
