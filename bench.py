@@ -1,0 +1,325 @@
+#!/usr/bin/env python3
+"""Benchmark of the TTS backbone hot path on one MI355X.
+
+Default workload ("c5c4"): one step is
+  * one batched decode iteration: 64 streams, 28 layers, bf16, paged KV cache with
+    16-token pages and per-stream lengths U[200, 4000] (seed 7): embedding of 8 summed
+    codebooks (1025 x 1024 tables) -> 28 layers (q_len = 1) -> final norm -> 8 x 1025
+    heads -> argmax; and
+  * one MaskGIT pass: 200 text tokens + 750 frames x 8 codebooks (half masked), 28
+    bidirectional layers, 8 x 1025 heads, scores, top-n unmasking on a cosine schedule
+    (32 steps; codes are restored every 32 passes).
+Inputs are seeded synthetic tensors resident in HBM before the timed region.  `value` is
+decode tokens/s (64 tokens per step over the decode part of the step); MaskGIT frames/s
+and MFMA utilisation, and decode-attention HBM GB/s are reported beside it.
+
+Other workloads (--workload): c2 (batch-1 decode, 28 layers, KV 1000, 16 x 2048 tables,
+3072 head), c3 (5-layer code predictor, 256 frames x 16 positions), c1 (1 layer, fp32).
+
+    python bench.py [--steps K] [--warmup W] [--workload c5c4|c2|c3|c1] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+METRIC = "decode tokens/s + attn HBM GB/s; MaskGIT frames/s + MFMA util (% peak)"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------------------
+# Setup helpers
+# ---------------------------------------------------------------------------------------
+
+def make_ctx(T, torch, shape, n_layers, bf16, seed, max_rows, max_pos, max_head_cols, DEV, CFG):
+    dev = [DEV.layer_weights(seed, shape, l, bf16) for l in range(n_layers)]
+    fn = DEV.host_to_device(CFG.final_norm(seed, shape))
+    cfg = T.ttsbb_default_config()
+    cfg.n_layers = n_layers
+    cfg.dtype = T.BF16 if bf16 else T.F32
+    cfg.max_rows, cfg.max_pos, cfg.max_head_cols = max_rows, max_pos, max_head_cols
+    layers = [T.make_layer(*[d[k] for k in ("attn_norm", "q_norm", "k_norm", "ffn_norm", "wq", "wk",
+                                             "wv", "wo", "w_gate", "w_up", "w_down")]) for d in dev]
+    ctx = T.ttsbb_create(cfg, layers, fn, torch.cuda.current_stream().cuda_stream)
+    return ctx, (dev, fn)
+
+
+class DecodeC5:
+    """64-stream paged decode iteration with 8 summed codebooks and 8 x 1025 heads."""
+
+    def __init__(self, T, torch, total_steps):
+        from workload import configs as CFG, device as DEV, gen
+        self.T, self.torch = T, torch
+        w = CFG.c5()
+        self.w = w
+        e = w.extra
+        self.B, self.K, self.V = e["batch"], e["n_cb"], e["cb_vocab"]
+        self.lengths = CFG.c5_lengths(w)
+        room = [int(n) + total_steps + 1 for n in self.lengths]
+        self.pt, self.n_pages = CFG.page_table(w.seed, room)
+        self.ctx, self.keep = make_ctx(T, torch, w.shape, 28, True, w.seed, 1024, 8192, 8200, DEV, CFG)
+        self.pool = DEV.kv_pool(w.seed, w.shape, 28, self.lengths, self.pt, self.n_pages, True)
+        self.pt_d = torch.from_numpy(self.pt).cuda()
+        self.tables = DEV.table(w.seed, gen.KIND_CB_TABLE, 0, self.K * self.V, 1024, True)
+        self.heads = DEV.table(w.seed, gen.KIND_HEAD, 0, self.K * self.V, 1024, True)
+        codes = np.stack([gen.uniform_int(w.seed, gen.stream_id(gen.KIND_CODES, s), (self.B, self.K), self.V)
+                          for s in range(total_steps)])
+        self.codes = torch.from_numpy(codes).cuda()
+        self.pos = torch.from_numpy(self.lengths.astype(np.int32)).cuda()
+        self.x = torch.empty((self.B, 1024), dtype=torch.float32, device="cuda")
+        self.am = torch.empty((self.B, self.K), dtype=torch.int32, device="cuda")
+
+    def step(self, s):
+        T = self.T
+        T.ttsbb_codebook_embed(self.ctx, self.B, self.K, self.codes[s], self.tables, self.V, None, None,
+                               None, 0, self.x)
+        T.ttsbb_decode_step(self.ctx, self.B, self.x, self.pos, self.pt_d, self.pt.shape[1], self.pool,
+                            self.n_pages, self.heads, self.K, self.V, self.am)
+
+    def attn_bytes(self, steps_done_before, n_steps):
+        """Algorithmic bytes of one decode-attention launch averaged over the timed steps:
+        K and V of every cached position (incl. the new one) once, q in, o out."""
+        L = self.lengths.astype(np.int64)
+        mean_len = float(np.mean([(L + s + 1).sum() for s in range(steps_done_before,
+                                                                    steps_done_before + n_steps)]))
+        kv = mean_len * 8 * 128 * 2 * 2
+        return kv + self.B * 16 * 128 * 4 + self.B * 16 * 128 * 2
+
+
+class MaskgitC4:
+    def __init__(self, T, torch):
+        from workload import configs as CFG, device as DEV, gen
+        self.T, self.torch = T, torch
+        w = CFG.c4()
+        e = w.extra
+        self.e = e
+        self.ctx, self.keep = make_ctx(T, torch, w.shape, 28, True, w.seed, 1024, 8192, 8200, DEV, CFG)
+        self.text_table = DEV.table(w.seed, gen.KIND_TEXT_TABLE, 0, e["text_vocab"], 1024, True)
+        self.tables = DEV.table(w.seed, gen.KIND_CB_TABLE, 0, e["n_cb"] * e["cb_vocab"], 1024, True)
+        self.heads = DEV.table(w.seed, gen.KIND_HEAD, 0, e["n_cb"] * e["cb_vocab"], 1024, True)
+        self.text_ids = torch.from_numpy(CFG.maskgit_text_ids(w)).cuda()
+        self.codes0 = torch.from_numpy(CFG.maskgit_codes(w)).cuda()
+        self.codes = self.codes0.clone()
+        n_masked = int((CFG.maskgit_codes(w) == e["mask_id"]).sum())
+        self.sched = T.ttsbb_unmask_schedule(n_masked, e["n_steps"])
+        shp = (e["n_cb"], e["n_frames"])
+        self.pred = torch.empty(shp, dtype=torch.int32, device="cuda")
+        self.conf = torch.empty(shp, dtype=torch.float32, device="cuda")
+        self.picked = torch.empty(max(self.sched), dtype=torch.int32, device="cuda")
+
+    def step(self, s):
+        e = self.e
+        i = s % e["n_steps"]
+        if i == 0:
+            self.codes.copy_(self.codes0)
+        self.T.ttsbb_maskgit_pass(self.ctx, e["n_text"], self.text_ids, self.text_table, e["text_vocab"],
+                                  e["n_frames"], e["n_cb"], e["cb_vocab"], e["mask_id"], self.tables,
+                                  self.heads, self.codes, self.sched[i], e["layer_penalty"], self.pred,
+                                  self.conf, self.picked)
+
+    def flops(self):
+        """Algorithmic flops of one pass: projections, attention, heads."""
+        e = self.e
+        S = e["n_text"] + e["n_frames"]
+        per_tok_layer = 2 * (1024 * 4096 + 2048 * 1024 + 1024 * 6144 + 3072 * 1024)
+        gemm = S * per_tok_layer * 28
+        attn = 4 * 16 * 128 * S * S * 28
+        head = 2 * e["n_frames"] * 1024 * e["n_cb"] * e["cb_vocab"]
+        return gemm, attn, head
+
+
+# ---------------------------------------------------------------------------------------
+# CPU baseline: the oracle, untuned, on a bounded sample of the same workload
+# ---------------------------------------------------------------------------------------
+
+def cpu_baseline(n_streams=2):
+    from oracle import backbone as O
+    from workload import configs as CFG, gen
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    w = CFG.c5()
+    e = w.extra
+    shape = w.shape
+    t0 = time.perf_counter()
+    layers = []
+    for l in range(28):
+        h = CFG.layer_weights(w.seed, shape, l, True)
+        layers.append(O.Layer.from_arrays({k: (gen.bf16_bits_to_f32(v) if v.dtype == np.uint16 else v)
+                                           for k, v in h.items()}))
+    lengths = CFG.c5_lengths(w)[:n_streams]
+    cache = O.KVCache(28, n_streams)
+    for l in range(28):
+        for b in range(n_streams):
+            k, v = CFG.kv_prefill(w.seed, shape, l, b, int(lengths[b]), True)
+            cache.set(l, b, gen.bf16_bits_to_f32(k), gen.bf16_bits_to_f32(v))
+    table = CFG.LazyTable(w.seed, gen.KIND_CB_TABLE, 0, e["n_cb"] * e["cb_vocab"], 1024, True)
+    heads = CFG.LazyTable(w.seed, gen.KIND_HEAD, 0, e["n_cb"] * e["cb_vocab"], 1024, True)
+    head_full = heads[np.arange(e["n_cb"] * e["cb_vocab"])]
+    codes = gen.uniform_int(w.seed, gen.stream_id(gen.KIND_CODES, 0), (e["batch"], e["n_cb"]), e["cb_vocab"])
+    setup = time.perf_counter() - t0
+    t1 = time.perf_counter()
+    x = O.codebook_embed(codes[:n_streams], table, e["cb_vocab"])
+    out = O.decode_step(x, [int(n) for n in lengths], cache, layers, O.Dims())
+    _, lg = O.head_logits(out, CFG.final_norm(w.seed, shape).astype(np.float64), head_full, 1e-6)
+    O.argmax_groups(lg, e["n_cb"], e["cb_vocab"])
+    dt = time.perf_counter() - t1
+    return {"value": n_streams / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": "%d of the 64 streams (KV %s), one full 28-layer decode step each, fp64 numpy; "
+                      "input generation (%.1f s) excluded" % (n_streams, lengths.tolist(), setup),
+            "seconds": dt}
+
+
+def cpu_baseline_maskgit():
+    """Oracle time of one full MaskGIT pass (28 layers, S = 950) -> frames/s of a 32-step run."""
+    from oracle import backbone as O
+    from workload import configs as CFG, gen
+    w = CFG.c4()
+    e = w.extra
+    layers = []
+    for l in range(28):
+        h = CFG.layer_weights(w.seed, w.shape, l, True)
+        layers.append(O.Layer.from_arrays({k: (gen.bf16_bits_to_f32(v) if v.dtype == np.uint16 else v)
+                                           for k, v in h.items()}))
+    text = CFG.LazyTable(w.seed, gen.KIND_TEXT_TABLE, 0, e["text_vocab"], 1024, True)
+    tab = CFG.LazyTable(w.seed, gen.KIND_CB_TABLE, 0, e["n_cb"] * e["cb_vocab"], 1024, True)
+    heads = CFG.LazyTable(w.seed, gen.KIND_HEAD, 0, e["n_cb"] * e["cb_vocab"], 1024, True)
+    head_full = heads[np.arange(e["n_cb"] * e["cb_vocab"])]
+    codes = CFG.maskgit_codes(w)
+    t0 = time.perf_counter()
+    O.maskgit_pass(CFG.maskgit_text_ids(w), text, codes, tab, head_full, layers,
+                   CFG.final_norm(w.seed, w.shape).astype(np.float64), O.Dims(), e["cb_vocab"],
+                   e["mask_id"], e["layer_penalty"], 100)
+    dt = time.perf_counter() - t0
+    return {"pass_seconds": dt, "frames_per_s": e["n_frames"] / (dt * e["n_steps"])}
+
+
+# ---------------------------------------------------------------------------------------
+
+def run_c5c4(args, T, torch):
+    total = args.warmup + args.steps
+    log("setup: decode (64 streams, paged KV) ...")
+    dec = DecodeC5(T, torch, total)
+    log("setup: MaskGIT (S = 950) ...")
+    mg = MaskgitC4(T, torch)
+    torch.cuda.synchronize()
+    for s in range(args.warmup):
+        dec.step(s)
+        mg.step(s)
+    torch.cuda.synchronize()
+    if T.ttsbb_sync(dec.ctx) != T.OK or T.ttsbb_sync(mg.ctx) != T.OK:
+        raise RuntimeError("device-side index flag raised during warmup")
+    log("timed: %d steps" % args.steps)
+    T.ttsbb_profile_start(dec.ctx)
+    T.ttsbb_profile_start(mg.ctx)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        s = args.warmup + i
+        ev[i][0].record()
+        dec.step(s)
+        ev[i][1].record()
+        mg.step(s)
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pd = T.ttsbb_profile_stop(dec.ctx)
+    pm = T.ttsbb_profile_stop(mg.ctx)
+    dec_ms = sum(a.elapsed_time(b) for a, b, _ in ev) / args.steps
+    mg_ms = sum(b.elapsed_time(c) for _, b, c in ev) / args.steps
+
+    attn_ms, attn_n = pd["decode_attn"]
+    attn_avg_ms = attn_ms / max(1, attn_n)
+    attn_bytes = dec.attn_bytes(args.warmup, args.steps)
+    attn_gbs = attn_bytes / (attn_avg_ms * 1e-3) / 1e9
+    gemm, attn_f, head_f = mg.flops()
+    mg_mfma_ms = sum(pm[k][0] for k in ("gemm_qkv", "gemm_o", "gemm_gate_up", "gemm_down",
+                                        "flash_attn")) / args.steps
+    mfma_tflops = (gemm + attn_f) / (mg_mfma_ms * 1e-3) / 1e12
+
+    res = {
+        "metric": METRIC,
+        "value": round(dec.B / (dec_ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded Philox inputs, random weights)",
+        "config": {"workload": "c5 paged decode (64 streams, 28 layers, KV U[200,4000], 16-token pages, "
+                               "8x1025) + c4 MaskGIT pass (28 layers, S=950, 8x1025)",
+                   "global_batch": dec.B, "seq_len": int(dec.lengths.max()), "parallelism": "none (1 GPU)"},
+        "decode": {"ms_per_iteration": round(dec_ms, 4), "tokens_per_s": round(dec.B / (dec_ms * 1e-3), 1),
+                   "attn_hbm_gbs": round(attn_gbs, 1), "attn_frac_hbm_peak": round(attn_gbs / HBM_PEAK_GBS, 4)},
+        "maskgit": {"ms_per_pass": round(mg_ms, 4),
+                    "frames_per_s": round(mg.e["n_frames"] / (mg_ms * 1e-3 * mg.e["n_steps"]), 1),
+                    "mfma_tflops": round(mfma_tflops, 1),
+                    "mfma_util": round(mfma_tflops / BF16_PEAK_TFLOPS, 4)},
+        "roofline": {"kernel": "decode_attn (split-sequence paged GQA attention)", "bound": "hbm",
+                     "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "avg_launch_us": round(attn_avg_ms * 1e3, 3),
+                     "algorithmic_bytes_per_launch": int(attn_bytes)},
+        "kernels_ms_per_step": {
+            "decode": {k: round(v[0] / args.steps, 4) for k, v in pd.items() if v[1]},
+            "maskgit": {k: round(v[0] / args.steps, 4) for k, v in pm.items() if v[1]}},
+    }
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c5c4", choices=["c5c4"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-streams", type=int, default=2)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (each GPU would run its own "
+              "streams / utterances with no exchange); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from codec_token_tts_amd import ttsbb as T
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    T.lib()
+    res = run_c5c4(args, T, torch)
+    if not args.no_cpu_baseline:
+        log("cpu baseline: oracle decode sample ...")
+        cb = cpu_baseline(args.cpu_streams)
+        log("cpu baseline: oracle MaskGIT pass ...")
+        cm = cpu_baseline_maskgit()
+        cb["maskgit_frames_per_s"] = round(cm["frames_per_s"], 3)
+        cb["maskgit_pass_seconds"] = round(cm["pass_seconds"], 2)
+        cb["value"] = round(cb["value"], 3)
+        cb["seconds"] = round(cb["seconds"], 2)
+        res["cpu_baseline"] = cb
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

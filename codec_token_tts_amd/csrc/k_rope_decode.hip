@@ -292,12 +292,17 @@ void launch_decode_attn(const DecodeAttnArgs &a, DType dt, hipStream_t s) {
     if (dt == DT_BF16) {
         if (group == 2) hipLaunchKernelGGL((decode_attn_kernel<bf16_t, 2>), dim3(blocks), dim3(256), 0, s, a);
         else hipLaunchKernelGGL((decode_attn_kernel<bf16_t, 1>), dim3(blocks), dim3(256), 0, s, a);
-        hipLaunchKernelGGL(decode_combine_kernel<bf16_t>, dim3((a.B * a.H + 3) / 4), dim3(256), 0, s, a);
     } else {
         if (group == 2) hipLaunchKernelGGL((decode_attn_kernel<float, 2>), dim3(blocks), dim3(256), 0, s, a);
         else hipLaunchKernelGGL((decode_attn_kernel<float, 1>), dim3(blocks), dim3(256), 0, s, a);
-        hipLaunchKernelGGL(decode_combine_kernel<float>, dim3((a.B * a.H + 3) / 4), dim3(256), 0, s, a);
     }
+}
+
+void launch_decode_combine(const DecodeAttnArgs &a, DType dt, hipStream_t s) {
+    if (a.B <= 0) return;
+    const dim3 grid((a.B * a.H + 3) / 4);
+    if (dt == DT_BF16) hipLaunchKernelGGL(decode_combine_kernel<bf16_t>, grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(decode_combine_kernel<float>, grid, dim3(256), 0, s, a);
 }
 
 }  // namespace ttsbb

@@ -94,6 +94,7 @@ struct DecodeAttnArgs {
     float scale_log2;     // log2(e) / sqrt(128)
 };
 void launch_decode_attn(const DecodeAttnArgs &a, DType dt, hipStream_t s);
+void launch_decode_combine(const DecodeAttnArgs &a, DType dt, hipStream_t s);
 
 // ---- K6: bidirectional flash attention (bf16 MFMA) ---------------------------------
 struct FlashArgs {

@@ -34,6 +34,13 @@ struct Tap {
     int rows = 0, cols = 0;
 };
 
+struct Prof {
+    uint32_t mask = 0;
+    int cap = 0, used = 0;
+    std::vector<hipEvent_t> ev;  // 2 per recorded launch
+    std::vector<int> cls;
+};
+
 }  // namespace
 
 struct ttsbb_ctx {
@@ -61,6 +68,7 @@ struct ttsbb_ctx {
     // taps
     int tap_layer = -1;
     Tap taps[TTSBB_TAP_COUNT];
+    Prof prof;
 };
 
 namespace {
@@ -85,6 +93,31 @@ void free_all(ttsbb_ctx *c) {
 }
 
 int round_up(int v, int m) { return (v + m - 1) / m * m; }
+
+// Event pair around one launch of a profiled kernel class.
+struct KScope {
+    ttsbb_ctx *c;
+    int idx = -1;
+    KScope(ttsbb_ctx *ctx, int k) : c(ctx) {
+        Prof &p = c->prof;
+        if (((p.mask >> k) & 1u) && p.used < p.cap) {
+            idx = p.used++;
+            p.cls[idx] = k;
+            hipEventRecord(p.ev[2 * idx], c->stream);
+        }
+    }
+    ~KScope() {
+        if (idx >= 0) hipEventRecord(c->prof.ev[2 * idx + 1], c->stream);
+    }
+};
+
+void prof_release(Prof &p) {
+    for (hipEvent_t e : p.ev) hipEventDestroy(e);
+    p.ev.clear();
+    p.cls.clear();
+    p.cap = p.used = 0;
+    p.mask = 0;
+}
 
 bool launch_failed() { return hipPeekAtLastError() != hipSuccess; }
 
@@ -229,6 +262,7 @@ TTSBB_API ttsbb_status ttsbb_create(const ttsbb_config *cfg, const ttsbb_layer *
 TTSBB_API void ttsbb_destroy(ttsbb_ctx *ctx) {
     if (!ctx) return;
     hipStreamSynchronize(ctx->stream);
+    prof_release(ctx->prof);
     free_all(ctx);
     delete ctx;
 }
@@ -271,7 +305,10 @@ TTSBB_API ttsbb_status ttsbb_codebook_embed(ttsbb_ctx *ctx, int32_t n_rows, int3
     a.text_vocab = text_vocab;
     a.out = out;
     a.flag = ctx->flag;
-    launch_embed(a, ctx->dt, ctx->stream);
+    {
+        KScope k(ctx, TTSBB_K_EMBED);
+        launch_embed(a, ctx->dt, ctx->stream);
+    }
     return launch_failed() ? TTSBB_DEVICE_ERROR : TTSBB_OK;
 }
 
@@ -281,7 +318,10 @@ namespace {
 // modes.  x is the fp32 residual stream [M][hidden].
 void qkv_projection(ttsbb_ctx *c, const ttsbb_layer &L, const float *x, int M, bool tapit) {
     const ttsbb_config &g = c->cfg;
-    launch_rmsnorm(x, g.hidden, M, g.hidden, L.attn_norm, g.rms_eps, c->h, c->dt, c->stream);
+    {
+        KScope k(c, TTSBB_K_RMSNORM);
+        launch_rmsnorm(x, g.hidden, M, g.hidden, L.attn_norm, g.rms_eps, c->h, c->dt, c->stream);
+    }
     GemmArgs a = {};
     a.A = c->h;
     a.lda = g.hidden;
@@ -299,7 +339,10 @@ void qkv_projection(ttsbb_ctx *c, const ttsbb_layer &L, const float *x, int M, b
     a.C = c->qkv;
     a.ldc = c->qkv_w;
     a.epi = EPI_STORE;
-    launch_gemm(a, c->dt, c->stream);
+    {
+        KScope k(c, TTSBB_K_GEMM_QKV);
+        launch_gemm(a, c->dt, c->stream);
+    }
     if (tapit) {
         tap_dense(c, TTSBB_TAP_H_ATTN, c->h, c->dt, M, g.hidden, g.hidden);
         tap_dense(c, TTSBB_TAP_QKV, c->qkv, DT_F32, M, c->qkv_w, c->qkv_w);
@@ -323,10 +366,16 @@ void post_attention(ttsbb_ctx *c, const ttsbb_layer &L, float *x, int M, bool ta
     a.C = x;
     a.ldc = g.hidden;
     a.epi = EPI_ADD;
-    launch_gemm(a, c->dt, c->stream);
+    {
+        KScope k(c, TTSBB_K_GEMM_O);
+        launch_gemm(a, c->dt, c->stream);
+    }
     if (tapit) tap_dense(c, TTSBB_TAP_X_MID, x, DT_F32, M, g.hidden, g.hidden);
 
-    launch_rmsnorm(x, g.hidden, M, g.hidden, L.ffn_norm, g.rms_eps, c->h, c->dt, c->stream);
+    {
+        KScope k(c, TTSBB_K_RMSNORM);
+        launch_rmsnorm(x, g.hidden, M, g.hidden, L.ffn_norm, g.rms_eps, c->h, c->dt, c->stream);
+    }
     if (tapit) tap_dense(c, TTSBB_TAP_H_FFN, c->h, c->dt, M, g.hidden, g.hidden);
     GemmArgs u = {};
     u.A = c->h;
@@ -340,7 +389,10 @@ void post_attention(ttsbb_ctx *c, const ttsbb_layer &L, float *x, int M, bool ta
     u.C = c->mlp;
     u.ldc = g.ffn;
     u.epi = EPI_SWIGLU;
-    launch_gemm(u, c->dt, c->stream);
+    {
+        KScope k(c, TTSBB_K_GEMM_GATE_UP);
+        launch_gemm(u, c->dt, c->stream);
+    }
     if (tapit) tap_dense(c, TTSBB_TAP_MLP, c->mlp, c->dt, M, g.ffn, g.ffn);
 
     GemmArgs d = {};
@@ -356,7 +408,10 @@ void post_attention(ttsbb_ctx *c, const ttsbb_layer &L, float *x, int M, bool ta
     d.C = x;
     d.ldc = g.hidden;
     d.epi = EPI_ADD;
-    launch_gemm(d, c->dt, c->stream);
+    {
+        KScope k(c, TTSBB_K_GEMM_DOWN);
+        launch_gemm(d, c->dt, c->stream);
+    }
     if (tapit) tap_dense(c, TTSBB_TAP_X_OUT, x, DT_F32, M, g.hidden, g.hidden);
 }
 
@@ -375,6 +430,7 @@ void head_gemm(ttsbb_ctx *c, const void *head, int M, int N, float *out, int ldc
     a.C = out;
     a.ldc = ldc;
     a.epi = EPI_STORE;
+    KScope k(c, TTSBB_K_GEMM_HEAD);
     launch_gemm(a, c->dt, c->stream);
 }
 
@@ -434,7 +490,10 @@ TTSBB_API ttsbb_status ttsbb_decode_step(ttsbb_ctx *ctx, int32_t batch, float *x
         r.page = g.kv_page;
         r.pool_layer = pool_l;
         r.flag = ctx->flag;
-        launch_rope_kv(r, ctx->dt, ctx->stream);
+        {
+            KScope k(ctx, TTSBB_K_ROPE_KV);
+            launch_rope_kv(r, ctx->dt, ctx->stream);
+        }
         if (tapit) tap_dense(ctx, TTSBB_TAP_Q, ctx->q, DT_F32, batch, hd_all, hd_all);
 
         DecodeAttnArgs d = {};
@@ -453,18 +512,31 @@ TTSBB_API ttsbb_status ttsbb_decode_step(ttsbb_ctx *ctx, int32_t batch, float *x
         d.part = ctx->part;
         d.out = ctx->attn;
         d.scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
-        launch_decode_attn(d, ctx->dt, ctx->stream);
+        {
+            KScope k(ctx, TTSBB_K_DECODE_ATTN);
+            launch_decode_attn(d, ctx->dt, ctx->stream);
+        }
+        {
+            KScope k(ctx, TTSBB_K_DECODE_COMBINE);
+            launch_decode_combine(d, ctx->dt, ctx->stream);
+        }
 
         post_attention(ctx, L, x, batch, tapit);
     }
     if (head) {
         const int N = n_groups * group_vocab;
-        launch_rmsnorm(x, g.hidden, batch, g.hidden, ctx->final_norm, g.rms_eps, ctx->h, ctx->dt, ctx->stream);
+        {
+            KScope k(ctx, TTSBB_K_RMSNORM);
+            launch_rmsnorm(x, g.hidden, batch, g.hidden, ctx->final_norm, g.rms_eps, ctx->h, ctx->dt, ctx->stream);
+        }
         if (ctx->tap_layer >= 0) tap_dense(ctx, TTSBB_TAP_HEAD_IN, ctx->h, ctx->dt, batch, g.hidden, g.hidden);
         float *lg = logits ? logits : ctx->logits;
         head_gemm(ctx, head, batch, N, lg, N);
         if (ctx->tap_layer >= 0) tap_dense(ctx, TTSBB_TAP_LOGITS, lg, DT_F32, batch, N, N);
-        launch_argmax_groups(lg, batch, N, n_groups, group_vocab, argmax, ctx->stream);
+        {
+            KScope k(ctx, TTSBB_K_ARGMAX);
+            launch_argmax_groups(lg, batch, N, n_groups, group_vocab, argmax, ctx->stream);
+        }
     }
     launch_increment(positions, batch, ctx->stream);
     return launch_failed() ? TTSBB_DEVICE_ERROR : TTSBB_OK;
@@ -513,7 +585,10 @@ TTSBB_API ttsbb_status ttsbb_maskgit_pass(ttsbb_ctx *ctx, int32_t n_text, const 
     e.text_vocab = text_vocab;
     e.out = ctx->x;
     e.flag = ctx->flag;
-    launch_embed(e, DT_BF16, ctx->stream);
+    {
+        KScope k(ctx, TTSBB_K_EMBED);
+        launch_embed(e, DT_BF16, ctx->stream);
+    }
 
     for (int l = 0; l < g.n_layers; ++l) {
         const ttsbb_layer &L = ctx->layers[l];
@@ -537,7 +612,10 @@ TTSBB_API ttsbb_status ttsbb_maskgit_pass(ttsbb_ctx *ctx, int32_t n_text, const 
         r.vtbuf = ctx->vtbuf;
         r.s_pad = s_pad;
         r.flag = ctx->flag;
-        launch_rope_kv(r, DT_BF16, ctx->stream);
+        {
+            KScope k(ctx, TTSBB_K_ROPE_KV);
+            launch_rope_kv(r, DT_BF16, ctx->stream);
+        }
         if (tapit) {
             tap_dense(ctx, TTSBB_TAP_Q, ctx->q, DT_BF16, S, hd_all, hd_all);
             // K [Hkv][s_pad][hd] -> [S][Hkv][hd];  V^T [Hkv][hd][s_pad] -> [S][Hkv][hd]
@@ -555,21 +633,33 @@ TTSBB_API ttsbb_status ttsbb_maskgit_pass(ttsbb_ctx *ctx, int32_t n_text, const 
         f.Hkv = Hkv;
         f.scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
         f.out = reinterpret_cast<uint16_t *>(ctx->attn);
-        launch_flash_attn(f, ctx->stream);
+        {
+            KScope k(ctx, TTSBB_K_FLASH_ATTN);
+            launch_flash_attn(f, ctx->stream);
+        }
 
         post_attention(ctx, L, ctx->x, S, tapit);
     }
 
     // final norm + heads on the audio window only
     const int N = n_cb * cb_vocab;
-    launch_rmsnorm(ctx->x + (size_t)n_text * g.hidden, g.hidden, n_frames, g.hidden, ctx->final_norm,
-                   g.rms_eps, ctx->h, DT_BF16, ctx->stream);
+    {
+        KScope k(ctx, TTSBB_K_RMSNORM);
+        launch_rmsnorm(ctx->x + (size_t)n_text * g.hidden, g.hidden, n_frames, g.hidden, ctx->final_norm,
+                       g.rms_eps, ctx->h, DT_BF16, ctx->stream);
+    }
     if (ctx->tap_layer >= 0) tap_dense(ctx, TTSBB_TAP_HEAD_IN, ctx->h, DT_BF16, n_frames, g.hidden, g.hidden);
     head_gemm(ctx, audio_heads, n_frames, N, ctx->logits, N);
     if (ctx->tap_layer >= 0) tap_dense(ctx, TTSBB_TAP_LOGITS, ctx->logits, DT_F32, n_frames, N, N);
-    launch_maskgit_scores(ctx->logits, n_frames, N, n_cb, cb_vocab, mask_id, layer_penalty, codes, pred,
-                          conf, ctx->stream);
-    launch_select_update(conf, pred, n_cb * n_frames, n_unmask, codes, picked, ctx->stream);
+    {
+        KScope k(ctx, TTSBB_K_SCORES);
+        launch_maskgit_scores(ctx->logits, n_frames, N, n_cb, cb_vocab, mask_id, layer_penalty, codes,
+                              pred, conf, ctx->stream);
+    }
+    {
+        KScope k(ctx, TTSBB_K_SELECT);
+        launch_select_update(conf, pred, n_cb * n_frames, n_unmask, codes, picked, ctx->stream);
+    }
     return launch_failed() ? TTSBB_DEVICE_ERROR : TTSBB_OK;
 }
 
@@ -622,5 +712,45 @@ TTSBB_API ttsbb_status ttsbb_read_tap(ttsbb_ctx *ctx, int32_t tap, float *dst, i
     if (n == 0) return TTSBB_OK;
     if (hipMemcpyAsync(dst, t.buf, (size_t)n * sizeof(float), hipMemcpyDeviceToDevice, ctx->stream) != hipSuccess)
         return TTSBB_DEVICE_ERROR;
+    return TTSBB_OK;
+}
+
+TTSBB_API ttsbb_status ttsbb_profile_start(ttsbb_ctx *ctx, uint32_t mask, int32_t max_launches) {
+    if (!ctx || max_launches < 0) return TTSBB_INVALID_ARG;
+    Prof &p = ctx->prof;
+    if (hipStreamSynchronize(ctx->stream) != hipSuccess) return TTSBB_DEVICE_ERROR;
+    if (p.cap < max_launches) {
+        prof_release(p);
+        p.ev.resize(2 * (size_t)max_launches);
+        for (auto &e : p.ev)
+            if (hipEventCreate(&e) != hipSuccess) {
+                e = nullptr;
+                prof_release(p);
+                return TTSBB_DEVICE_ERROR;
+            }
+        p.cls.assign(max_launches, 0);
+        p.cap = max_launches;
+    }
+    p.used = 0;
+    p.mask = mask;
+    return TTSBB_OK;
+}
+
+TTSBB_API ttsbb_status ttsbb_profile_stop(ttsbb_ctx *ctx, float *ms, int32_t *launches) {
+    if (!ctx) return TTSBB_INVALID_ARG;
+    Prof &p = ctx->prof;
+    p.mask = 0;
+    if (ms)
+        for (int k = 0; k < TTSBB_K_COUNT; ++k) ms[k] = 0.f;
+    if (launches)
+        for (int k = 0; k < TTSBB_K_COUNT; ++k) launches[k] = 0;
+    if (hipStreamSynchronize(ctx->stream) != hipSuccess) return TTSBB_DEVICE_ERROR;
+    for (int i = 0; i < p.used; ++i) {
+        float t = 0.f;
+        if (hipEventElapsedTime(&t, p.ev[2 * i], p.ev[2 * i + 1]) != hipSuccess) return TTSBB_DEVICE_ERROR;
+        if (ms) ms[p.cls[i]] += t;
+        if (launches) launches[p.cls[i]] += 1;
+    }
+    p.used = 0;
     return TTSBB_OK;
 }

@@ -22,7 +22,14 @@ F32, BF16 = 0, 1
 
 EXPORTS = ["ttsbb_default_config", "ttsbb_create", "ttsbb_destroy", "ttsbb_status_str",
            "ttsbb_sync", "ttsbb_codebook_embed", "ttsbb_decode_step", "ttsbb_maskgit_pass",
-           "ttsbb_unmask_schedule", "ttsbb_set_tap_layer", "ttsbb_read_tap"]
+           "ttsbb_unmask_schedule", "ttsbb_set_tap_layer", "ttsbb_read_tap", "ttsbb_profile_start",
+           "ttsbb_profile_stop"]
+
+(K_EMBED, K_RMSNORM, K_GEMM_QKV, K_ROPE_KV, K_DECODE_ATTN, K_DECODE_COMBINE, K_FLASH_ATTN, K_GEMM_O,
+ K_GEMM_GATE_UP, K_GEMM_DOWN, K_GEMM_HEAD, K_ARGMAX, K_SCORES, K_SELECT) = range(14)
+K_COUNT = 14
+K_NAMES = ["embed", "rmsnorm", "gemm_qkv", "rope_kv", "decode_attn", "decode_combine", "flash_attn",
+           "gemm_o", "gemm_gate_up", "gemm_down", "gemm_head", "argmax", "scores", "select"]
 
 
 class TtsbbError(RuntimeError):
@@ -71,6 +78,8 @@ def lib() -> C.CDLL:
         "ttsbb_unmask_schedule": (i32, [i32, i32, C.POINTER(i32)]),
         "ttsbb_set_tap_layer": (i32, [vp, i32]),
         "ttsbb_read_tap": (i32, [vp, i32, vp, i64, C.POINTER(i32), C.POINTER(i32)]),
+        "ttsbb_profile_start": (i32, [vp, C.c_uint32, i32]),
+        "ttsbb_profile_stop": (i32, [vp, C.POINTER(f32), C.POINTER(i32)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -179,3 +188,15 @@ def ttsbb_read_tap(ctx, tap: int, dst, n_floats: int):
     _check(lib().ttsbb_read_tap(ctx, tap, ptr(dst), n_floats, C.byref(rows), C.byref(cols)),
            "ttsbb_read_tap")
     return rows.value, cols.value
+
+
+def ttsbb_profile_start(ctx, mask: int = (1 << 14) - 1, max_launches: int = 65536):
+    _check(lib().ttsbb_profile_start(ctx, mask, max_launches), "ttsbb_profile_start")
+
+
+def ttsbb_profile_stop(ctx):
+    """Returns {kernel class name: (total ms, launches)}."""
+    ms = (C.c_float * K_COUNT)()
+    n = (C.c_int32 * K_COUNT)()
+    _check(lib().ttsbb_profile_stop(ctx, ms, n), "ttsbb_profile_stop")
+    return {K_NAMES[k]: (float(ms[k]), int(n[k])) for k in range(K_COUNT)}

@@ -188,6 +188,36 @@ ttsbb_status ttsbb_set_tap_layer(ttsbb_ctx *ctx, int32_t layer);
 ttsbb_status ttsbb_read_tap(ttsbb_ctx *ctx, int32_t tap, float *dst, int64_t n_floats,
                             int32_t *rows, int32_t *cols);
 
+
+/* Instrumentation: HIP events recorded on the context's stream around every launch of
+ * the kernel classes below, so a caller can measure per-kernel durations live.  Event
+ * creation happens in ttsbb_profile_start (not for use under graph capture). */
+typedef enum {
+    TTSBB_K_EMBED = 0,         /* gather-sum embedding */
+    TTSBB_K_RMSNORM = 1,       /* all RMSNorms */
+    TTSBB_K_GEMM_QKV = 2,      /* q|k|v projection */
+    TTSBB_K_ROPE_KV = 3,       /* head norms + RoPE + K/V write */
+    TTSBB_K_DECODE_ATTN = 4,   /* split-sequence decode attention (main pass) */
+    TTSBB_K_DECODE_COMBINE = 5,/* merge of the decode attention partials */
+    TTSBB_K_FLASH_ATTN = 6,    /* bidirectional attention */
+    TTSBB_K_GEMM_O = 7,        /* o_proj + residual */
+    TTSBB_K_GEMM_GATE_UP = 8,  /* gate|up projection + SwiGLU */
+    TTSBB_K_GEMM_DOWN = 9,     /* down_proj + residual */
+    TTSBB_K_GEMM_HEAD = 10,    /* output heads */
+    TTSBB_K_ARGMAX = 11,       /* greedy choice per group */
+    TTSBB_K_SCORES = 12,       /* MaskGIT log-softmax / argmax / confidence */
+    TTSBB_K_SELECT = 13,       /* MaskGIT top-n + code update */
+    TTSBB_K_COUNT = 14
+} ttsbb_kernel_class;
+
+/* Start recording events for the classes whose bit (1 << class) is set in `mask`;
+ * `max_launches` bounds the launches recorded before ttsbb_profile_stop. */
+ttsbb_status ttsbb_profile_start(ttsbb_ctx *ctx, uint32_t mask, int32_t max_launches);
+
+/* Synchronise, stop recording and return per class the summed milliseconds and launch
+ * count (host arrays of TTSBB_K_COUNT entries; either may be NULL). */
+ttsbb_status ttsbb_profile_stop(ttsbb_ctx *ctx, float *ms, int32_t *launches);
+
 #ifdef __cplusplus
 }
 #endif

@@ -48,6 +48,8 @@ int main(void) {
                               NULL) == TTSBB_INVALID_ARG);
     EXPECT(ttsbb_set_tap_layer(NULL, 0) == TTSBB_INVALID_ARG);
     EXPECT(ttsbb_read_tap(NULL, 0, &dummy, 1, NULL, NULL) == TTSBB_INVALID_ARG);
+    EXPECT(ttsbb_profile_start(NULL, 1u, 16) == TTSBB_INVALID_ARG);
+    EXPECT(ttsbb_profile_stop(NULL, NULL, NULL) == TTSBB_INVALID_ARG);
 
     EXPECT(ttsbb_unmask_schedule(10, 2, sched) == TTSBB_OK && sched[0] == 3 && sched[1] == 7);
     EXPECT(ttsbb_unmask_schedule(10, 0, sched) == TTSBB_INVALID_ARG);

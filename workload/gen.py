@@ -152,7 +152,11 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
-    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+    """bf16 bit patterns -> fp32 values (the bits become the high half of the word)."""
+    b = np.asarray(b, dtype=np.uint16)
+    out = np.zeros(b.shape + (2,), np.uint16)
+    out[..., 1] = b  # little-endian: element 1 is the high half
+    return out.view(np.float32).reshape(b.shape)
 
 
 def round_bf16(x: np.ndarray) -> np.ndarray:
