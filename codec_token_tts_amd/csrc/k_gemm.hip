@@ -5,11 +5,16 @@
 //
 //   Y[M][N] = A[M][K] * W[N][K]^T, both operands K-contiguous, fp32 accumulation.
 //
-// Two kernels:
-// * gemm_mfma: bf16 MFMA (v_mfma_f32_16x16x32_bf16) with BMxBNx64 block tiles staged
-//   through LDS (rows padded to 72 elements so the 16-byte fragment reads of a
-//   16-row group hit distinct banks), register prefetch of the next K tile while the
-//   current one is multiplied, 4 waves in a 2x2 arrangement.  Used when M > 8.
+// Kernels:
+// * gemm_mfma: bf16 MFMA (v_mfma_f32_16x16x32_bf16) on BMxBNx64 block tiles staged
+//   through LDS (rows padded to 72 elements so the 16-byte fragment reads of a 16-row
+//   group hit distinct banks), 4 waves in a 2x2 arrangement.  Two register staging
+//   sets and two LDS buffers: the global loads of K tile k+2 are in flight while tile
+//   k is multiplied, so each load has about two iterations to arrive.  Tiles are
+//   ordered so that each XCD works on a contiguous N range (weight reuse in its L2).
+//   Optional split-K (grid z) writes fp32 partials that splitk_reduce sums in split
+//   order before the epilogue (deterministic; used when there are too few tiles, as
+//   for the batched decode step at M = 64).  Used when M > 8.
 // * gemv: weight streaming for M <= 8 and for fp32: each wave owns two output columns,
 //   streams their weight rows once with 16-byte loads and reuses them for all M rows.
 //
@@ -42,9 +47,21 @@ __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)
 // ------------------------------------------------------------------------------------
 constexpr int BK = 64;
 constexpr int LDK = BK + 8;
+constexpr int EPI_PARTIAL = 3;  // fp32 partial sums of one K split: C + z * M * N
+
+// Tile order: block ids are dealt round-robin to the 8 XCDs, so block b runs on XCD
+// b % 8.  Tiles are renumbered so that each XCD receives a contiguous run of the
+// N-major tile order (all M tiles of a few N tiles): a weight slice is then fetched
+// into one XCD's L2 and reused there by every M tile.
+__device__ __forceinline__ int xcd_tile(int b, int n_tiles) {
+    const int per = n_tiles / 8;
+    const int x = b % 8, i = b / 8;
+    if (i < per) return x * per + i;  // the evenly dealt part
+    return 8 * per + x;               // the n_tiles % 8 remainder, one per XCD
+}
 
 template <int BM, int BN, int EPI>
-__global__ __launch_bounds__(256) void gemm_mfma(GemmArgs g) {
+__global__ __launch_bounds__(256) void gemm_mfma(GemmArgs g, int k_split) {
     constexpr int WM = BM / 2, WN = BN / 2;
     constexpr int TM = WM / 16, TN = WN / 16;
     constexpr int ACH = BM * 8 / 256;  // 16-byte chunks per thread of the A tile
@@ -58,9 +75,13 @@ __global__ __launch_bounds__(256) void gemm_mfma(GemmArgs g) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
+    const int tiles_m = (g.M + BM - 1) / BM;
     const int tiles_n = (g.N + BN - 1) / BN;
-    const int tile_m = blockIdx.x / tiles_n, tile_n = blockIdx.x % tiles_n;
+    const int t = xcd_tile(blockIdx.x, tiles_m * tiles_n);
+    const int tile_n = t / tiles_m, tile_m = t % tiles_m;
     const int m0 = tile_m * BM, n0 = tile_n * BN;
+    const int k_begin = blockIdx.z * k_split;
+    const int KT = min(k_split, g.K - k_begin) / BK;
 
     const bf16_t *A = reinterpret_cast<const bf16_t *>(g.A);
     const bf16_t *arow[ACH];
@@ -70,19 +91,23 @@ __global__ __launch_bounds__(256) void gemm_mfma(GemmArgs g) {
     for (int c = 0; c < ACH; ++c) {
         const int ch = tid + 256 * c, r = ch >> 3, kc = (ch & 7) * 8;
         const int m = m0 + r;
-        arow[c] = (m < g.M) ? A + (int64_t)m * g.lda + kc : nullptr;
+        arow[c] = (m < g.M) ? A + (int64_t)m * g.lda + k_begin + kc : nullptr;
         aoff[c] = r * LDK + kc;
     }
 #pragma unroll
     for (int c = 0; c < BCH; ++c) {
         const int ch = tid + 256 * c, r = ch >> 3, kc = (ch & 7) * 8;
         const int n = n0 + r;
-        brow[c] = (n < g.N) ? wrow<bf16_t>(g.w, EPI, n, g.K) + kc : nullptr;
+        // g.epi (not EPI): a split of a SwiGLU product still reads the interleaved rows
+        brow[c] = (n < g.N) ? wrow<bf16_t>(g.w, g.epi, n, g.K) + k_begin + kc : nullptr;
         boff[c] = r * LDK + kc;
     }
 
-    uint4 ra[ACH], rb[BCH];
-    auto gload = [&](int k0) {
+    // Two register staging sets: the loads of tile k+2 are issued while tile k is
+    // multiplied; tile k+1 (loaded one iteration earlier) goes to LDS after it.
+    uint4 ra0[ACH], rb0[BCH], ra1[ACH], rb1[BCH];
+    auto gload = [&](int kt, uint4 (&ra)[ACH], uint4 (&rb)[BCH]) {
+        const int k0 = kt * BK;
 #pragma unroll
         for (int c = 0; c < ACH; ++c)
             ra[c] = arow[c] ? *reinterpret_cast<const uint4 *>(arow[c] + k0) : make_uint4(0, 0, 0, 0);
@@ -90,7 +115,7 @@ __global__ __launch_bounds__(256) void gemm_mfma(GemmArgs g) {
         for (int c = 0; c < BCH; ++c)
             rb[c] = brow[c] ? *reinterpret_cast<const uint4 *>(brow[c] + k0) : make_uint4(0, 0, 0, 0);
     };
-    auto sstore = [&](int buf) {
+    auto sstore = [&](int buf, const uint4 (&ra)[ACH], const uint4 (&rb)[BCH]) {
 #pragma unroll
         for (int c = 0; c < ACH; ++c) *reinterpret_cast<uint4 *>(&sA[buf][aoff[c]]) = ra[c];
 #pragma unroll
@@ -103,34 +128,42 @@ __global__ __launch_bounds__(256) void gemm_mfma(GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    const int KT = g.K / BK;
-    gload(0);
-    sstore(0);
-    __syncthreads();
-
     const int fr = lane & 15, fk = (lane >> 4) * 8;
-    for (int kt = 0; kt < KT; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < KT) gload((kt + 1) * BK);
+    auto compute = [&](int buf) {
 #pragma unroll
         for (int ks = 0; ks < BK / 32; ++ks) {
             bf16x8_t af[TM], bfr[TN];
 #pragma unroll
             for (int i = 0; i < TM; ++i)
-                af[i] = *reinterpret_cast<const bf16x8_t *>(
-                    &sA[buf][(wm * WM + i * 16 + fr) * LDK + ks * 32 + fk]);
+                af[i] = *reinterpret_cast<const bf16x8_t *>(&sA[buf][(wm * WM + i * 16 + fr) * LDK + ks * 32 + fk]);
 #pragma unroll
             for (int j = 0; j < TN; ++j)
-                bfr[j] = *reinterpret_cast<const bf16x8_t *>(
-                    &sB[buf][(wn * WN + j * 16 + fr) * LDK + ks * 32 + fk]);
+                bfr[j] = *reinterpret_cast<const bf16x8_t *>(&sB[buf][(wn * WN + j * 16 + fr) * LDK + ks * 32 + fk]);
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
                 for (int j = 0; j < TN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
         }
-        if (kt + 1 < KT) sstore(buf ^ 1);
+    };
+
+    if (KT > 0) {
+        gload(0, ra0, rb0);
+        if (KT > 1) gload(1, ra1, rb1);
+        sstore(0, ra0, rb0);
         __syncthreads();
+        // iteration kt multiplies LDS buffer kt % 2; staging set kt % 2 receives tile kt+2
+        for (int kt = 0; kt < KT; kt += 2) {
+            if (kt + 2 < KT) gload(kt + 2, ra0, rb0);
+            compute(0);
+            if (kt + 1 < KT) sstore(1, ra1, rb1);
+            __syncthreads();
+            if (kt + 1 >= KT) break;
+            if (kt + 3 < KT) gload(kt + 3, ra1, rb1);
+            compute(1);
+            if (kt + 2 < KT) sstore(0, ra0, rb0);
+            __syncthreads();
+        }
     }
 
     // Epilogue.  Accumulator element r of tile (i, j) is row 4*(lane/16) + r, column lane%16.
@@ -142,7 +175,7 @@ __global__ __launch_bounds__(256) void gemm_mfma(GemmArgs g) {
         for (int i = 0; i < TM; ++i)
 #pragma unroll
             for (int j = 0; j < TN; j += 2) {
-                const int ncol = n0 + wn * WN + j * 16;       // first logical column of the gate tile
+                const int ncol = n0 + wn * WN + j * 16;  // first logical column of the gate tile
                 const int ocol = (ncol >> 5) * 16 + (lane & 15);
                 if (ncol >= g.N) continue;
 #pragma unroll
@@ -154,6 +187,11 @@ __global__ __launch_bounds__(256) void gemm_mfma(GemmArgs g) {
             }
     } else {
         float *C = reinterpret_cast<float *>(g.C);
+        int64_t ldc = g.ldc;
+        if (EPI == EPI_PARTIAL) {
+            C += (int64_t)blockIdx.z * g.M * g.N;
+            ldc = g.N;
+        }
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -164,11 +202,38 @@ __global__ __launch_bounds__(256) void gemm_mfma(GemmArgs g) {
                 for (int r = 0; r < 4; ++r) {
                     const int row = rbase + i * 16 + r;
                     if (row >= g.M) continue;
-                    float *p = C + (int64_t)row * g.ldc + col;
+                    float *p = C + (int64_t)row * ldc + col;
                     if (EPI == EPI_ADD) *p += acc[i][j][r];
                     else *p = acc[i][j][r];
                 }
             }
+    }
+}
+
+// Sum of the K-split partials in split order, then the real epilogue.
+template <int EPI>
+__global__ __launch_bounds__(256) void splitk_reduce(GemmArgs g, const float *part, int splits) {
+    const int64_t total = (EPI == EPI_SWIGLU) ? (int64_t)g.M * (g.N / 2) : (int64_t)g.M * g.N;
+    const int64_t stride = (int64_t)g.M * g.N;
+    for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+        if (EPI == EPI_SWIGLU) {
+            const int half = g.N / 2;
+            const int m = (int)(i / half), j = (int)(i % half);
+            const int ng = (j >> 4) * 32 + (j & 15);  // logical gate column; up is ng + 16
+            float gs = 0.f, us = 0.f;
+            for (int z = 0; z < splits; ++z) {
+                gs += part[z * stride + (int64_t)m * g.N + ng];
+                us += part[z * stride + (int64_t)m * g.N + ng + 16];
+            }
+            reinterpret_cast<bf16_t *>(g.C)[(int64_t)m * g.ldc + j] = f32_to_bf16(silu_f(gs) * us);
+        } else {
+            const int m = (int)(i / g.N), n = (int)(i % g.N);
+            float v = 0.f;
+            for (int z = 0; z < splits; ++z) v += part[z * stride + i];
+            float *c = reinterpret_cast<float *>(g.C) + (int64_t)m * g.ldc + n;
+            if (EPI == EPI_ADD) *c += v;
+            else *c = v;
+        }
     }
 }
 
@@ -287,16 +352,42 @@ static void launch_gemv(const GemmArgs &g, hipStream_t s) {
 }
 
 template <int BM, int BN>
-static void launch_mfma(const GemmArgs &g, hipStream_t s) {
-    const int blocks = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
+static void launch_mfma(const GemmArgs &g, int splits, float *part, hipStream_t s) {
+    const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
+    const int kt = g.K / BK;
+    const int k_split = ((kt + splits - 1) / splits) * BK;
+    splits = (g.K + k_split - 1) / k_split;
+    if (splits > 1) {
+        hipLaunchKernelGGL((gemm_mfma<BM, BN, EPI_PARTIAL>), dim3(tiles, 1, splits), dim3(256), 0, s, g, k_split);
+        const int64_t outs = (g.epi == EPI_SWIGLU) ? (int64_t)g.M * (g.N / 2) : (int64_t)g.M * g.N;
+        int blocks = (int)((outs + 255) / 256);
+        if (blocks > 2048) blocks = 2048;
+        switch (g.epi) {
+            case EPI_STORE: hipLaunchKernelGGL(splitk_reduce<EPI_STORE>, dim3(blocks), dim3(256), 0, s, g, part, splits); break;
+            case EPI_ADD: hipLaunchKernelGGL(splitk_reduce<EPI_ADD>, dim3(blocks), dim3(256), 0, s, g, part, splits); break;
+            default: hipLaunchKernelGGL(splitk_reduce<EPI_SWIGLU>, dim3(blocks), dim3(256), 0, s, g, part, splits); break;
+        }
+        return;
+    }
     switch (g.epi) {
-        case EPI_STORE: hipLaunchKernelGGL((gemm_mfma<BM, BN, EPI_STORE>), dim3(blocks), dim3(256), 0, s, g); break;
-        case EPI_ADD: hipLaunchKernelGGL((gemm_mfma<BM, BN, EPI_ADD>), dim3(blocks), dim3(256), 0, s, g); break;
-        default: hipLaunchKernelGGL((gemm_mfma<BM, BN, EPI_SWIGLU>), dim3(blocks), dim3(256), 0, s, g); break;
+        case EPI_STORE: hipLaunchKernelGGL((gemm_mfma<BM, BN, EPI_STORE>), dim3(tiles), dim3(256), 0, s, g, g.K); break;
+        case EPI_ADD: hipLaunchKernelGGL((gemm_mfma<BM, BN, EPI_ADD>), dim3(tiles), dim3(256), 0, s, g, g.K); break;
+        default: hipLaunchKernelGGL((gemm_mfma<BM, BN, EPI_SWIGLU>), dim3(tiles), dim3(256), 0, s, g, g.K); break;
     }
 }
 
-void launch_gemm(const GemmArgs &g, DType dt, hipStream_t s) {
+// Split count: enough blocks to cover the 256 CUs once, at least 2 K tiles per
+// split, and a partial buffer that fits the workspace.
+static int choose_splits(const GemmArgs &g, int tiles, int64_t part_cap) {
+    const int kt = g.K / BK;
+    int splits = 1;
+    while (tiles * splits < 256 && 2 * (splits * 2) <= kt &&
+           (int64_t)(splits * 2) * g.M * g.N <= part_cap)
+        splits *= 2;
+    return splits;
+}
+
+void launch_gemm(const GemmArgs &g, DType dt, float *part, int64_t part_cap, hipStream_t s) {
     if (g.M <= 0) return;
     if (dt == DT_F32) {
         // fp32 mode streams weights; larger M is processed GEMV_MAXM rows at a time
@@ -313,10 +404,23 @@ void launch_gemm(const GemmArgs &g, DType dt, hipStream_t s) {
         launch_gemv<bf16_t>(g, s);
         return;
     }
-    const long tiles128 = (long)((g.M + 127) / 128) * ((g.N + 127) / 128);
-    if (g.M > 64 && tiles128 >= 200) launch_mfma<128, 128>(g, s);
-    else if (g.M > 32) launch_mfma<64, 64>(g, s);
-    else launch_mfma<32, 64>(g, s);
+    const int t128 = ((g.M + 127) / 128) * ((g.N + 127) / 128);
+    if (g.M > 64 && t128 >= 200) {
+        launch_mfma<128, 128>(g, 1, part, s);
+        return;
+    }
+    if (g.M > 64) {
+        const int t64 = ((g.M + 63) / 64) * ((g.N + 63) / 64);
+        launch_mfma<64, 64>(g, choose_splits(g, t64, part_cap), part, s);
+        return;
+    }
+    if (g.M > 32) {
+        const int t64 = ((g.M + 63) / 64) * ((g.N + 63) / 64);
+        launch_mfma<64, 64>(g, choose_splits(g, t64, part_cap), part, s);
+        return;
+    }
+    const int t32 = ((g.M + 31) / 32) * ((g.N + 63) / 64);
+    launch_mfma<32, 64>(g, choose_splits(g, t32, part_cap), part, s);
 }
 
 }  // namespace ttsbb

@@ -13,9 +13,10 @@
 // K9 (same section: topk over the flattened scores, then tokens[idx] = pred[idx]).
 // The rank of element i is the number of elements that order before it (greater
 // score, or equal score and lower flat index); the n elements of rank < n are the
-// selection and picked[rank] = i.  Every element's rank is independent, so the
-// selection is exact, deterministic and needs no sort; the score array is staged
-// through LDS in tiles and each thread ranks one element.
+// selection and picked[rank] = i.  Ranks are independent, so the selection is exact
+// and needs no sort.  The count is split over (block of elements) x (tile of 1024
+// scores staged in LDS) and summed with integer atomics, whose result does not
+// depend on their order; a second pass scatters picks and updates the codes.
 #include <math.h>
 
 #include "common.h"
@@ -83,39 +84,60 @@ void launch_maskgit_scores(const float *logits, int T, int ld, int n_cb, int V, 
                        n_cb, V, mask_id, penalty, codes, pred, conf);
 }
 
-constexpr int SEL_TILE = 4096;
+constexpr int SEL_TILE = 1024;  // scores staged in LDS per block
 
-__global__ __launch_bounds__(256) void select_update_kernel(const float *conf, const int32_t *pred,
-                                                            int n, int n_unmask, int32_t *codes,
-                                                            int32_t *picked) {
-    __shared__ float tile[SEL_TILE];
+__global__ void zero_i32_kernel(int32_t *v, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) v[i] = 0;
+}
+
+// rank[i] += #{j in this block's tile : conf[j] > conf[i] or (== and j < i)}
+__global__ __launch_bounds__(256) void rank_count_kernel(const float *conf, int n, int32_t *rank) {
+    __shared__ __attribute__((aligned(16))) float tile[SEL_TILE];
     const int i = blockIdx.x * 256 + threadIdx.x;
-    const float ci = i < n ? conf[i] : -INFINITY;
-    int rank = 0;
-    for (int j0 = 0; j0 < n; j0 += SEL_TILE) {
-        const int cnt = min(SEL_TILE, n - j0);
-        for (int j = threadIdx.x; j < cnt; j += 256) tile[j] = conf[j0 + j];
-        __syncthreads();
-        for (int j = 0; j < cnt; ++j) {
-            const float cj = tile[j];
-            rank += (cj > ci) || (cj == ci && j0 + j < i);
-        }
-        __syncthreads();
+    const int j0 = blockIdx.y * SEL_TILE;
+    const int cnt = min(SEL_TILE, n - j0);
+    for (int j = threadIdx.x; j < SEL_TILE; j += 256) tile[j] = j < cnt ? conf[j0 + j] : -INFINITY;
+    __syncthreads();
+    if (i >= n) return;
+    const float ci = conf[i];
+    int r = 0;
+    const int lim = i - j0;  // tile positions j < lim have a lower flat index than i
+    for (int j = 0; j < cnt; j += 4) {
+        const float4 c = *reinterpret_cast<const float4 *>(&tile[j]);
+        r += (c.x > ci) || (c.x == ci && j < lim);
+        r += (c.y > ci) || (c.y == ci && j + 1 < lim);
+        r += (c.z > ci) || (c.z == ci && j + 2 < lim);
+        r += (c.w > ci) || (c.w == ci && j + 3 < lim);
     }
-    if (i >= n || rank >= n_unmask) return;
-    if (ci > -INFINITY) {
-        picked[rank] = i;
+    // positions past cnt hold -inf: they can only tie with a -inf score, and such a
+    // position has a higher index than every real one, so they never count
+    if (r) atomicAdd(&rank[i], r);
+}
+
+__global__ void select_scatter_kernel(const float *conf, const int32_t *pred, const int32_t *rank, int n,
+                                      int n_unmask, int32_t *codes, int32_t *picked) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const int r = rank[i];
+    if (r >= n_unmask) return;
+    if (conf[i] > -INFINITY) {
+        picked[r] = i;
         codes[i] = pred[i];
     } else {
-        picked[rank] = -1;
+        picked[r] = -1;
     }
 }
 
-void launch_select_update(const float *conf, const int32_t *pred, int n, int n_unmask,
+void launch_select_update(const float *conf, const int32_t *pred, int n, int n_unmask, int32_t *rank,
                           int32_t *codes, int32_t *picked, hipStream_t s) {
     if (n <= 0 || n_unmask <= 0) return;
-    hipLaunchKernelGGL(select_update_kernel, dim3((n + 255) / 256), dim3(256), 0, s, conf, pred, n,
-                       n_unmask, codes, picked);
+    const int blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(zero_i32_kernel, dim3(blocks), dim3(256), 0, s, rank, n);
+    hipLaunchKernelGGL(rank_count_kernel, dim3(blocks, (n + SEL_TILE - 1) / SEL_TILE), dim3(256), 0, s, conf,
+                       n, rank);
+    hipLaunchKernelGGL(select_scatter_kernel, dim3(blocks), dim3(256), 0, s, conf, pred, rank, n, n_unmask,
+                       codes, picked);
 }
 
 }  // namespace ttsbb

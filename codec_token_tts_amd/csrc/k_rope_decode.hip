@@ -112,32 +112,108 @@ void launch_rope_kv(const RopeKvArgs &a, DType kv_dt, hipStream_t s) {
 // ------------------------------------------------------------------------------------
 constexpr int PART_STRIDE = 132;
 
-template <typename T> struct KV16;
-template <> struct KV16<bf16_t> {
-    static constexpr int EPL = 8;  // elements per 16-byte lane load
-    __device__ static void load(const bf16_t *p, float v[8]) {
-        uint4 t = *reinterpret_cast<const uint4 *>(p);
-        const uint32_t w[4] = {t.x, t.y, t.z, t.w};
+template <typename T> struct KVRaw {
+    static constexpr int EPL = 16 / sizeof(T);  // elements per 16-byte lane load
+    __device__ static void unpack(const uint4 &t, float v[EPL]);
+};
+template <> __device__ inline void KVRaw<bf16_t>::unpack(const uint4 &t, float v[8]) {
+    const uint32_t w[4] = {t.x, t.y, t.z, t.w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            v[2 * i] = __uint_as_float(w[i] << 16);
-            v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(w[i] << 16);
+        v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+}
+template <> __device__ inline void KVRaw<float>::unpack(const uint4 &t, float v[4]) {
+    v[0] = __uint_as_float(t.x); v[1] = __uint_as_float(t.y);
+    v[2] = __uint_as_float(t.z); v[3] = __uint_as_float(t.w);
+}
+
+// Issue the 16-byte lane loads of the K and V blocks of page `pg` of a stream.
+template <typename T, int NR, int RPL>
+__device__ __forceinline__ bool load_page(const T *pool, const int32_t *ptab, int pg, int n_pages,
+                                          int Hkv, int hk, int64_t blk, int lane_off, uint4 (&kr)[NR],
+                                          uint4 (&vr)[NR]) {
+    const int page_id = ptab[pg];
+    // An invalid id (flagged by K4) reads page 0, which always exists, and is ignored.
+    const bool ok = page_id >= 0 && page_id < n_pages;
+    const T *kb = pool + (((int64_t)(ok ? page_id : 0) * 2 + 0) * Hkv + hk) * blk + lane_off;
+    const T *vb = kb + (int64_t)Hkv * blk;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        kr[r] = *reinterpret_cast<const uint4 *>(kb + r * RPL * 128);
+        vr[r] = *reinterpret_cast<const uint4 *>(vb + r * RPL * 128);
+    }
+    return ok;
+}
+
+// Online-softmax update of one wave with one 16-token page: scores of the lane's tokens
+// (reduced over the LPR lanes sharing a token), running max / sum, V accumulation.
+template <typename T, int GROUP, int NR, int RPL>
+__device__ __forceinline__ void process_page(const uint4 (&kr)[NR], const uint4 (&vr)[NR], int nvalid,
+                                             int rsub, const float (&qv)[GROUP][KVRaw<T>::EPL],
+                                             float (&m_run)[GROUP], float (&l_run)[GROUP],
+                                             float (&acc)[GROUP][KVRaw<T>::EPL]) {
+    constexpr int EPL = KVRaw<T>::EPL;
+    constexpr int LPR = 128 / EPL;
+    float s[NR][GROUP];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        const int tok = rsub + RPL * r;
+        float kv[EPL];
+        KVRaw<T>::unpack(kr[r], kv);
+#pragma unroll
+        for (int j = 0; j < GROUP; ++j) {
+            float d = 0.f;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) d = fmaf(qv[j][e], kv[e], d);
+            d = group_sum<LPR>(d);
+            s[r][j] = tok < nvalid ? d : -INFINITY;
         }
     }
-};
-template <> struct KV16<float> {
-    static constexpr int EPL = 4;
-    __device__ static void load(const float *p, float v[4]) {
-        float4 t = *reinterpret_cast<const float4 *>(p);
-        v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+#pragma unroll
+    for (int j = 0; j < GROUP; ++j) {
+        float mx = m_run[j];
+#pragma unroll
+        for (int r = 0; r < NR; ++r) mx = fmaxf(mx, s[r][j]);
+        if (mx == -INFINITY) {  // nothing valid for this lane yet
+#pragma unroll
+            for (int r = 0; r < NR; ++r) s[r][j] = 0.f;
+            continue;
+        }
+        const float sc = exp2f(m_run[j] - mx);
+        l_run[j] *= sc;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[j][e] *= sc;
+        m_run[j] = mx;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            s[r][j] = exp2f(s[r][j] - mx);
+            l_run[j] += s[r][j];
+        }
     }
-};
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        const int tok = rsub + RPL * r;
+        if (tok >= nvalid) continue;  // slots past the length may hold anything
+        float vv[EPL];
+        KVRaw<T>::unpack(vr[r], vv);
+#pragma unroll
+        for (int j = 0; j < GROUP; ++j)
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[j][e] = fmaf(s[r][j], vv[e], acc[j][e]);
+    }
+}
 
+// One wave per (stream, KV head, chunk).  The K and V blocks of the next page are
+// loaded into a second register set while the current page is processed, so every
+// wave keeps one page (8 KB in bf16) of loads in flight behind its arithmetic.
 template <typename T, int GROUP>
 __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeAttnArgs a) {
-    constexpr int EPL = KV16<T>::EPL;
+    constexpr int EPL = KVRaw<T>::EPL;
     constexpr int LPR = 128 / EPL;  // lanes per 128-dim row
     constexpr int RPL = 64 / LPR;   // rows (tokens) per wave load
+    constexpr int NR = 16 / RPL;    // wave loads per 16-token page block
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int item = blockIdx.x * 4 + wave;
     const int total = a.B * a.Hkv * a.n_chunks;
@@ -174,58 +250,23 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeAttnArgs a) {
 
     const T *pool = reinterpret_cast<const T *>(a.pool_layer);
     const int64_t blk = (int64_t)a.page * 128;  // elements of one (page, K|V, head) block
-    for (int p0 = p_begin; p0 < p_end; p0 += a.page) {
-        const int page_id = a.page_table[(int64_t)b * a.max_pages + p0 / a.page];
-        if (page_id < 0 || page_id >= a.n_pages) continue;  // flagged by K4
-        const T *kb = pool + (((int64_t)page_id * 2 + 0) * a.Hkv + hk) * blk;
-        const T *vb = pool + (((int64_t)page_id * 2 + 1) * a.Hkv + hk) * blk;
-        const int nvalid = p_end - p0;  // tokens of this page inside the chunk
-        constexpr int NR = 16 / RPL;
-        float s[NR][GROUP];
-#pragma unroll
-        for (int r = 0; r < NR; ++r) {
-            const int tok = rsub + RPL * r;
-            float kv[EPL];
-            KV16<T>::load(kb + tok * 128 + d0, kv);
-#pragma unroll
-            for (int j = 0; j < GROUP; ++j) {
-                float d = 0.f;
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) d = fmaf(qv[j][e], kv[e], d);
-                d = group_sum<LPR>(d);
-                s[r][j] = tok < nvalid ? d : -INFINITY;
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < GROUP; ++j) {
-            float mx = m_run[j];
-#pragma unroll
-            for (int r = 0; r < NR; ++r) mx = fmaxf(mx, s[r][j]);
-            if (mx == -INFINITY) continue;  // nothing valid for this lane yet
-            const float sc = exp2f(m_run[j] - mx);
-            l_run[j] *= sc;
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) acc[j][e] *= sc;
-            m_run[j] = mx;
-#pragma unroll
-            for (int r = 0; r < NR; ++r) {
-                s[r][j] = exp2f(s[r][j] - mx);
-                l_run[j] += s[r][j];
-            }
-        }
-#pragma unroll
-        for (int r = 0; r < NR; ++r) {
-            const int tok = rsub + RPL * r;
-            if (tok >= nvalid) continue;  // slots past the length may hold anything
-            float vv[EPL];
-            KV16<T>::load(vb + tok * 128 + d0, vv);
-#pragma unroll
-            for (int j = 0; j < GROUP; ++j) {
-                const float pr = (m_run[j] == -INFINITY) ? 0.f : s[r][j];
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) acc[j][e] = fmaf(pr, vv[e], acc[j][e]);
-            }
-        }
+    const int32_t *ptab = a.page_table + (int64_t)b * a.max_pages;
+    const int lane_off = rsub * 128 + d0;
+    const int pg_first = p_begin / a.page, pg_last = (p_end - 1) / a.page;
+    uint4 ka[NR], va[NR], kb2[NR], vb2[NR];
+    bool ok_a = load_page<T, NR, RPL>(pool, ptab, pg_first, a.n_pages, a.Hkv, hk, blk, lane_off, ka, va);
+    bool ok_b = false;
+    for (int pg = pg_first; pg <= pg_last; pg += 2) {
+        // ping: page pg in (ka, va); pong: page pg + 1 in (kb2, vb2)
+        if (pg + 1 <= pg_last)
+            ok_b = load_page<T, NR, RPL>(pool, ptab, pg + 1, a.n_pages, a.Hkv, hk, blk, lane_off, kb2, vb2);
+        if (ok_a)
+            process_page<T, GROUP, NR, RPL>(ka, va, p_end - pg * a.page, rsub, qv, m_run, l_run, acc);
+        if (pg + 1 > pg_last) break;
+        if (pg + 2 <= pg_last)
+            ok_a = load_page<T, NR, RPL>(pool, ptab, pg + 2, a.n_pages, a.Hkv, hk, blk, lane_off, ka, va);
+        if (ok_b)
+            process_page<T, GROUP, NR, RPL>(kb2, vb2, p_end - (pg + 1) * a.page, rsub, qv, m_run, l_run, acc);
     }
 
     // merge the RPL lane groups (same dims, different tokens)

@@ -54,7 +54,8 @@ struct GemmArgs {
     int ldc;
     int epi;
 };
-void launch_gemm(const GemmArgs &g, DType dt, hipStream_t s);
+// part: fp32 workspace of part_cap floats for split-K partial sums
+void launch_gemm(const GemmArgs &g, DType dt, float *part, int64_t part_cap, hipStream_t s);
 
 // ---- K4: per-head RMSNorm + RoPE + K/V write --------------------------------------
 // qkv fp32 [M][(H + 2 Hkv) * 128].  Decode mode (dense == 0): row m is stream m at
@@ -117,7 +118,8 @@ void launch_maskgit_scores(const float *logits, int T, int ld, int n_cb, int V, 
                            hipStream_t s);
 
 // ---- K9: top-n selection by rank + code update -------------------------------------
-void launch_select_update(const float *conf, const int32_t *pred, int n, int n_unmask,
+// rank: int32 scratch [n]
+void launch_select_update(const float *conf, const int32_t *pred, int n, int n_unmask, int32_t *rank,
                           int32_t *codes, int32_t *picked, hipStream_t s);
 
 // ---- misc ---------------------------------------------------------------------------

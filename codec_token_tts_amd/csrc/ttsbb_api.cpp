@@ -62,6 +62,10 @@ struct ttsbb_ctx {
     int s_pad_cap = 0;
     float *part = nullptr;
     float *logits = nullptr;
+    int32_t *rank = nullptr;
+    int rank_cap = 0;
+    float *gpart = nullptr;   // split-K partial sums
+    int64_t gpart_cap = 0;    // floats
     float2 *rope = nullptr;
     int *flag = nullptr;
     std::vector<void *> allocs;
@@ -217,6 +221,8 @@ TTSBB_API ttsbb_status ttsbb_create(const ttsbb_config *cfg, const ttsbb_layer *
     const size_t R = (size_t)g.max_rows;
     const size_t hd_all = (size_t)g.n_heads * g.head_dim;
     c->s_pad_cap = round_up(g.max_rows, 64);
+    c->rank_cap = g.max_rows * (g.max_head_cols / 2 + 1);
+    c->gpart_cap = (int64_t)16 << 20;  // 64 MB of split-K partials
     bool ok = dev_alloc(c, &c->h, R * g.hidden * c->esz) &&
               dev_alloc(c, (void **)&c->qkv, R * c->qkv_w * 4) &&
               dev_alloc(c, &c->q, R * hd_all * 4) &&
@@ -227,6 +233,8 @@ TTSBB_API ttsbb_status ttsbb_create(const ttsbb_config *cfg, const ttsbb_layer *
               dev_alloc(c, (void **)&c->vtbuf, (size_t)g.n_kv_heads * c->s_pad_cap * g.head_dim * 2) &&
               dev_alloc(c, (void **)&c->part, R * g.n_heads * MAX_CHUNKS * PART_STRIDE * 4) &&
               dev_alloc(c, (void **)&c->logits, R * (size_t)(g.max_head_cols > 0 ? g.max_head_cols : 1) * 4) &&
+              dev_alloc(c, (void **)&c->rank, (size_t)R * (g.max_head_cols / 2 + 1) * 4) &&
+              dev_alloc(c, (void **)&c->gpart, (size_t)c->gpart_cap * 4) &&
               dev_alloc(c, (void **)&c->rope, (size_t)g.max_pos * 64 * sizeof(float2)) &&
               dev_alloc(c, (void **)&c->flag, 256);
     if (!ok) {
@@ -341,7 +349,7 @@ void qkv_projection(ttsbb_ctx *c, const ttsbb_layer &L, const float *x, int M, b
     a.epi = EPI_STORE;
     {
         KScope k(c, TTSBB_K_GEMM_QKV);
-        launch_gemm(a, c->dt, c->stream);
+        launch_gemm(a, c->dt, c->gpart, c->gpart_cap, c->stream);
     }
     if (tapit) {
         tap_dense(c, TTSBB_TAP_H_ATTN, c->h, c->dt, M, g.hidden, g.hidden);
@@ -368,7 +376,7 @@ void post_attention(ttsbb_ctx *c, const ttsbb_layer &L, float *x, int M, bool ta
     a.epi = EPI_ADD;
     {
         KScope k(c, TTSBB_K_GEMM_O);
-        launch_gemm(a, c->dt, c->stream);
+        launch_gemm(a, c->dt, c->gpart, c->gpart_cap, c->stream);
     }
     if (tapit) tap_dense(c, TTSBB_TAP_X_MID, x, DT_F32, M, g.hidden, g.hidden);
 
@@ -391,7 +399,7 @@ void post_attention(ttsbb_ctx *c, const ttsbb_layer &L, float *x, int M, bool ta
     u.epi = EPI_SWIGLU;
     {
         KScope k(c, TTSBB_K_GEMM_GATE_UP);
-        launch_gemm(u, c->dt, c->stream);
+        launch_gemm(u, c->dt, c->gpart, c->gpart_cap, c->stream);
     }
     if (tapit) tap_dense(c, TTSBB_TAP_MLP, c->mlp, c->dt, M, g.ffn, g.ffn);
 
@@ -410,7 +418,7 @@ void post_attention(ttsbb_ctx *c, const ttsbb_layer &L, float *x, int M, bool ta
     d.epi = EPI_ADD;
     {
         KScope k(c, TTSBB_K_GEMM_DOWN);
-        launch_gemm(d, c->dt, c->stream);
+        launch_gemm(d, c->dt, c->gpart, c->gpart_cap, c->stream);
     }
     if (tapit) tap_dense(c, TTSBB_TAP_X_OUT, x, DT_F32, M, g.hidden, g.hidden);
 }
@@ -431,7 +439,7 @@ void head_gemm(ttsbb_ctx *c, const void *head, int M, int N, float *out, int ldc
     a.ldc = ldc;
     a.epi = EPI_STORE;
     KScope k(c, TTSBB_K_GEMM_HEAD);
-    launch_gemm(a, c->dt, c->stream);
+    launch_gemm(a, c->dt, c->gpart, c->gpart_cap, c->stream);
 }
 
 }  // namespace
@@ -455,14 +463,18 @@ TTSBB_API ttsbb_status ttsbb_decode_step(ttsbb_ctx *ctx, int32_t batch, float *x
     const int hd_all = H * hd;
     const size_t layer_elems = (size_t)n_pages * 2 * Hkv * g.kv_page * hd;
 
-    // split of each stream's positions into chunks for the decode attention
+    // Split of each stream's positions into chunks for the decode attention: 256
+    // positions per wave, halved while there are fewer than 2048 (stream, KV head,
+    // chunk) work items; the partial buffer holds max_rows * MAX_CHUNKS chunks per head.
     const int cap = max_pages * g.kv_page;
-    int want = (2048 + batch * Hkv - 1) / (batch * Hkv);
-    if (want > MAX_CHUNKS) want = MAX_CHUNKS;
-    if (want < 1) want = 1;
-    int chunk = round_up((cap + want - 1) / want, g.kv_page);
+    int chunk = 256;
+    while (chunk > g.kv_page && (int64_t)batch * Hkv * ((cap + chunk - 1) / chunk) < 2048) chunk /= 2;
+    chunk = round_up(chunk, g.kv_page);
     int n_chunks = (cap + chunk - 1) / chunk;
-    if (n_chunks > MAX_CHUNKS) return TTSBB_UNSUPPORTED;
+    while ((int64_t)batch * n_chunks > (int64_t)g.max_rows * MAX_CHUNKS) {
+        chunk *= 2;
+        n_chunks = (cap + chunk - 1) / chunk;
+    }
 
     for (int l = 0; l < g.n_layers; ++l) {
         const ttsbb_layer &L = ctx->layers[l];
@@ -556,6 +568,7 @@ TTSBB_API ttsbb_status ttsbb_maskgit_pass(ttsbb_ctx *ctx, int32_t n_text, const 
         return TTSBB_INVALID_ARG;
     if ((int64_t)n_text + n_frames > g.max_rows) return TTSBB_INVALID_ARG;
     if ((int64_t)n_cb * cb_vocab > g.max_head_cols) return TTSBB_INVALID_ARG;
+    if ((int64_t)n_cb * n_frames > ctx->rank_cap) return TTSBB_INVALID_ARG;
     if (n_text > 0 && (!text_ids || !text_table || text_vocab <= 0)) return TTSBB_INVALID_ARG;
     if (!audio_tables || !audio_heads || !codes || !pred || !conf || (n_unmask > 0 && !picked) ||
         !ctx->final_norm)
@@ -658,7 +671,7 @@ TTSBB_API ttsbb_status ttsbb_maskgit_pass(ttsbb_ctx *ctx, int32_t n_text, const 
     }
     {
         KScope k(ctx, TTSBB_K_SELECT);
-        launch_select_update(conf, pred, n_cb * n_frames, n_unmask, codes, picked, ctx->stream);
+        launch_select_update(conf, pred, n_cb * n_frames, n_unmask, ctx->rank, codes, picked, ctx->stream);
     }
     return launch_failed() ? TTSBB_DEVICE_ERROR : TTSBB_OK;
 }
