@@ -358,7 +358,10 @@ static void launch_mfma(const GemmArgs &g, int splits, float *part, hipStream_t 
     const int k_split = ((kt + splits - 1) / splits) * BK;
     splits = (g.K + k_split - 1) / k_split;
     if (splits > 1) {
-        hipLaunchKernelGGL((gemm_mfma<BM, BN, EPI_PARTIAL>), dim3(tiles, 1, splits), dim3(256), 0, s, g, k_split);
+        GemmArgs gp = g;  // the partial pass writes [splits][M][N] into the workspace
+        gp.C = part;
+        gp.ldc = g.N;
+        hipLaunchKernelGGL((gemm_mfma<BM, BN, EPI_PARTIAL>), dim3(tiles, 1, splits), dim3(256), 0, s, gp, k_split);
         const int64_t outs = (g.epi == EPI_SWIGLU) ? (int64_t)g.M * (g.N / 2) : (int64_t)g.M * g.N;
         int blocks = (int)((outs + 255) / 256);
         if (blocks > 2048) blocks = 2048;
