@@ -9,6 +9,8 @@ namespace ttsbb {
 typedef uint16_t bf16_t;  // bf16 bit pattern
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+// Native 16-byte vector: stays an SSA value (HIP's uint4 class is copied through memory).
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 
 constexpr int WAVE = 64;
 

@@ -59,21 +59,21 @@ __global__ __launch_bounds__(256) void flash_kernel(FlashArgs a) {
 
     const bf16_t *kg = a.k + (int64_t)hk * a.s_pad * 128;
     const bf16_t *vg = a.vt + (int64_t)hk * 128 * a.s_pad;
-    uint4 rk[4], rv[4];
+    u32x4_t rk[4], rv[4];
     auto gload = [&](int kb0) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int ch = tid + 256 * c;
-            rk[c] = *reinterpret_cast<const uint4 *>(kg + (int64_t)(kb0 + (ch >> 4)) * 128 + (ch & 15) * 8);
-            rv[c] = *reinterpret_cast<const uint4 *>(vg + (int64_t)(ch >> 3) * a.s_pad + kb0 + (ch & 7) * 8);
+            rk[c] = *reinterpret_cast<const u32x4_t *>(kg + (int64_t)(kb0 + (ch >> 4)) * 128 + (ch & 15) * 8);
+            rv[c] = *reinterpret_cast<const u32x4_t *>(vg + (int64_t)(ch >> 3) * a.s_pad + kb0 + (ch & 7) * 8);
         }
     };
     auto sstore = [&](int buf) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int ch = tid + 256 * c;
-            *reinterpret_cast<uint4 *>(&sK[buf][(ch >> 4) * LDKF + (ch & 15) * 8]) = rk[c];
-            *reinterpret_cast<uint4 *>(&sV[buf][(ch >> 3) * LDVF + (ch & 7) * 8]) = rv[c];
+            *reinterpret_cast<u32x4_t *>(&sK[buf][(ch >> 4) * LDKF + (ch & 15) * 8]) = rk[c];
+            *reinterpret_cast<u32x4_t *>(&sV[buf][(ch >> 3) * LDVF + (ch & 7) * 8]) = rv[c];
         }
     };
 
@@ -88,7 +88,7 @@ __global__ __launch_bounds__(256) void flash_kernel(FlashArgs a) {
     __syncthreads();
     for (int kb = 0; kb < NB; ++kb) {
         const int buf = kb & 1;
-        if (kb + 1 < NB) gload((kb + 1) * FB);
+        gload(min(kb + 1, NB - 1) * FB);  // unconditional (clamped) so the waits stay counted
 
         f32x4_t s[4];
 #pragma unroll

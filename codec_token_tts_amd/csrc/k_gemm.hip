@@ -34,10 +34,11 @@ __device__ __forceinline__ const T *wrow(const WSrc &w, int epi, int n, int K) {
         const T *base = reinterpret_cast<const T *>(half ? w.p[1] : w.p[0]);
         return base + (int64_t)(pair * 16 + r) * K;
     }
-    int s = 0;
-    if (w.nseg > 1 && n >= w.start[1]) s = 1;
-    if (w.nseg > 2 && n >= w.start[2]) s = 2;
-    return reinterpret_cast<const T *>(w.p[s]) + (int64_t)(n - w.start[s]) * K;
+    // select with branches, not a runtime array index: indexing an array of the kernel
+    // argument struct would move the struct into scratch memory
+    if (w.nseg > 2 && n >= w.start[2]) return reinterpret_cast<const T *>(w.p[2]) + (int64_t)(n - w.start[2]) * K;
+    if (w.nseg > 1 && n >= w.start[1]) return reinterpret_cast<const T *>(w.p[1]) + (int64_t)(n - w.start[1]) * K;
+    return reinterpret_cast<const T *>(w.p[0]) + (int64_t)n * K;
 }
 
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
@@ -58,6 +59,54 @@ __device__ __forceinline__ int xcd_tile(int b, int n_tiles) {
     const int x = b % 8, i = b / 8;
     if (i < per) return x * per + i;  // the evenly dealt part
     return 8 * per + x;               // the n_tiles % 8 remainder, one per XCD
+}
+
+// Pipeline pieces (device functions rather than lambdas: arrays captured by a lambda
+// end up in scratch memory, arrays passed by reference to an inlined function stay in
+// registers).
+template <int ACH, int BCH> struct Stage {
+    u32x4_t a[ACH];
+    u32x4_t b[BCH];
+};
+
+template <int ACH, int BCH>
+__device__ __forceinline__ Stage<ACH, BCH> gemm_gload(const bf16_t *const (&arow)[ACH],
+                                                      const bf16_t *const (&brow)[BCH], int k0) {
+    Stage<ACH, BCH> st;
+#pragma unroll
+    for (int c = 0; c < ACH; ++c) st.a[c] = *reinterpret_cast<const u32x4_t *>(arow[c] + k0);
+#pragma unroll
+    for (int c = 0; c < BCH; ++c) st.b[c] = *reinterpret_cast<const u32x4_t *>(brow[c] + k0);
+    return st;
+}
+
+template <int ACH, int BCH>
+__device__ __forceinline__ void gemm_sstore(bf16_t *sa, bf16_t *sb, const int (&aoff)[ACH], const int (&boff)[BCH],
+                                            const Stage<ACH, BCH> &st) {
+#pragma unroll
+    for (int c = 0; c < ACH; ++c) *reinterpret_cast<u32x4_t *>(&sa[aoff[c]]) = st.a[c];
+#pragma unroll
+    for (int c = 0; c < BCH; ++c) *reinterpret_cast<u32x4_t *>(&sb[boff[c]]) = st.b[c];
+}
+
+template <int TM, int TN>
+__device__ __forceinline__ void gemm_mma(const bf16_t *sa, const bf16_t *sb, int fr, int fk,
+                                         f32x4_t (&acc)[TM][TN]) {
+#pragma unroll
+    for (int ks = 0; ks < 64 / 32; ++ks) {
+        bf16x8_t af[TM], bfr[TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+            af[i] = *reinterpret_cast<const bf16x8_t *>(&sa[(i * 16 + fr) * (64 + 8) + ks * 32 + fk]);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            bfr[j] = *reinterpret_cast<const bf16x8_t *>(&sb[(j * 16 + fr) * (64 + 8) + ks * 32 + fk]);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
 }
 
 template <int BM, int BN, int EPI>
@@ -90,38 +139,27 @@ __global__ __launch_bounds__(256) void gemm_mfma(GemmArgs g, int k_split) {
 #pragma unroll
     for (int c = 0; c < ACH; ++c) {
         const int ch = tid + 256 * c, r = ch >> 3, kc = (ch & 7) * 8;
-        const int m = m0 + r;
-        arow[c] = (m < g.M) ? A + (int64_t)m * g.lda + k_begin + kc : nullptr;
+        // rows past M read row M-1: they only feed output rows that are never stored,
+        // and unconditional loads let the compiler count them in flight
+        const int m = min(m0 + r, g.M - 1);
+        arow[c] = A + (int64_t)m * g.lda + k_begin + kc;
         aoff[c] = r * LDK + kc;
     }
 #pragma unroll
     for (int c = 0; c < BCH; ++c) {
         const int ch = tid + 256 * c, r = ch >> 3, kc = (ch & 7) * 8;
-        const int n = n0 + r;
+        const int n = min(n0 + r, g.N - 1);  // likewise for columns past N
         // g.epi (not EPI): a split of a SwiGLU product still reads the interleaved rows
-        brow[c] = (n < g.N) ? wrow<bf16_t>(g.w, g.epi, n, g.K) + k_begin + kc : nullptr;
+        brow[c] = wrow<bf16_t>(g.w, g.epi, n, g.K) + k_begin + kc;
         boff[c] = r * LDK + kc;
     }
 
     // Two register staging sets: the loads of tile k+2 are issued while tile k is
-    // multiplied; tile k+1 (loaded one iteration earlier) goes to LDS after it.
-    uint4 ra0[ACH], rb0[BCH], ra1[ACH], rb1[BCH];
-    auto gload = [&](int kt, uint4 (&ra)[ACH], uint4 (&rb)[BCH]) {
-        const int k0 = kt * BK;
-#pragma unroll
-        for (int c = 0; c < ACH; ++c)
-            ra[c] = arow[c] ? *reinterpret_cast<const uint4 *>(arow[c] + k0) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-        for (int c = 0; c < BCH; ++c)
-            rb[c] = brow[c] ? *reinterpret_cast<const uint4 *>(brow[c] + k0) : make_uint4(0, 0, 0, 0);
-    };
-    auto sstore = [&](int buf, const uint4 (&ra)[ACH], const uint4 (&rb)[BCH]) {
-#pragma unroll
-        for (int c = 0; c < ACH; ++c) *reinterpret_cast<uint4 *>(&sA[buf][aoff[c]]) = ra[c];
-#pragma unroll
-        for (int c = 0; c < BCH; ++c) *reinterpret_cast<uint4 *>(&sB[buf][boff[c]]) = rb[c];
-    };
-
+    // multiplied; tile k+1 (loaded one iteration earlier) goes to LDS after it.  The
+    // prefetch tile index is clamped to the last tile (a read past the end re-reads it
+    // unused), so the loads are unconditional and their count in flight is static: the
+    // wait before each LDS store covers only the set that is being stored.  Staging
+    // uses native vector types so that it lives in registers.
     f32x4_t acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -129,40 +167,24 @@ __global__ __launch_bounds__(256) void gemm_mfma(GemmArgs g, int k_split) {
         for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     const int fr = lane & 15, fk = (lane >> 4) * 8;
-    auto compute = [&](int buf) {
-#pragma unroll
-        for (int ks = 0; ks < BK / 32; ++ks) {
-            bf16x8_t af[TM], bfr[TN];
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-                af[i] = *reinterpret_cast<const bf16x8_t *>(&sA[buf][(wm * WM + i * 16 + fr) * LDK + ks * 32 + fk]);
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-                bfr[j] = *reinterpret_cast<const bf16x8_t *>(&sB[buf][(wn * WN + j * 16 + fr) * LDK + ks * 32 + fk]);
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-        }
-    };
-
+    const bf16_t *sa0 = &sA[0][wm * WM * LDK], *sa1 = &sA[1][wm * WM * LDK];
+    const bf16_t *sb0 = &sB[0][wn * WN * LDK], *sb1 = &sB[1][wn * WN * LDK];
     if (KT > 0) {
-        gload(0, ra0, rb0);
-        if (KT > 1) gload(1, ra1, rb1);
-        sstore(0, ra0, rb0);
+        Stage<ACH, BCH> s0 = gemm_gload<ACH, BCH>(arow, brow, 0);
+        Stage<ACH, BCH> s1 = gemm_gload<ACH, BCH>(arow, brow, min(1, KT - 1) * BK);
+        gemm_sstore<ACH, BCH>(sA[0], sB[0], aoff, boff, s0);
         __syncthreads();
-        // iteration kt multiplies LDS buffer kt % 2; staging set kt % 2 receives tile kt+2
         for (int kt = 0; kt < KT; kt += 2) {
-            if (kt + 2 < KT) gload(kt + 2, ra0, rb0);
-            compute(0);
-            if (kt + 1 < KT) sstore(1, ra1, rb1);
+            s0 = gemm_gload<ACH, BCH>(arow, brow, min(kt + 2, KT - 1) * BK);
+            gemm_mma<TM, TN>(sa0, sb0, fr, fk, acc);
+            gemm_sstore<ACH, BCH>(sA[1], sB[1], aoff, boff, s1);
             __syncthreads();
-            if (kt + 1 >= KT) break;
-            if (kt + 3 < KT) gload(kt + 3, ra1, rb1);
-            compute(1);
-            if (kt + 2 < KT) sstore(0, ra0, rb0);
-            __syncthreads();
+            if (kt + 1 < KT) {
+                s1 = gemm_gload<ACH, BCH>(arow, brow, min(kt + 3, KT - 1) * BK);
+                gemm_mma<TM, TN>(sa1, sb1, fr, fk, acc);
+                gemm_sstore<ACH, BCH>(sA[0], sB[0], aoff, boff, s0);
+                __syncthreads();
+            }
         }
     }
 

@@ -114,9 +114,9 @@ constexpr int PART_STRIDE = 132;
 
 template <typename T> struct KVRaw {
     static constexpr int EPL = 16 / sizeof(T);  // elements per 16-byte lane load
-    __device__ static void unpack(const uint4 &t, float v[EPL]);
+    __device__ static void unpack(const u32x4_t &t, float v[EPL]);
 };
-template <> __device__ inline void KVRaw<bf16_t>::unpack(const uint4 &t, float v[8]) {
+template <> __device__ inline void KVRaw<bf16_t>::unpack(const u32x4_t &t, float v[8]) {
     const uint32_t w[4] = {t.x, t.y, t.z, t.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -124,7 +124,7 @@ template <> __device__ inline void KVRaw<bf16_t>::unpack(const uint4 &t, float v
         v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
     }
 }
-template <> __device__ inline void KVRaw<float>::unpack(const uint4 &t, float v[4]) {
+template <> __device__ inline void KVRaw<float>::unpack(const u32x4_t &t, float v[4]) {
     v[0] = __uint_as_float(t.x); v[1] = __uint_as_float(t.y);
     v[2] = __uint_as_float(t.z); v[3] = __uint_as_float(t.w);
 }
@@ -132,8 +132,8 @@ template <> __device__ inline void KVRaw<float>::unpack(const uint4 &t, float v[
 // Issue the 16-byte lane loads of the K and V blocks of page `pg` of a stream.
 template <typename T, int NR, int RPL>
 __device__ __forceinline__ bool load_page(const T *pool, const int32_t *ptab, int pg, int n_pages,
-                                          int Hkv, int hk, int64_t blk, int lane_off, uint4 (&kr)[NR],
-                                          uint4 (&vr)[NR]) {
+                                          int Hkv, int hk, int64_t blk, int lane_off, u32x4_t (&kr)[NR],
+                                          u32x4_t (&vr)[NR]) {
     const int page_id = ptab[pg];
     // An invalid id (flagged by K4) reads page 0, which always exists, and is ignored.
     const bool ok = page_id >= 0 && page_id < n_pages;
@@ -141,8 +141,8 @@ __device__ __forceinline__ bool load_page(const T *pool, const int32_t *ptab, in
     const T *vb = kb + (int64_t)Hkv * blk;
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
-        kr[r] = *reinterpret_cast<const uint4 *>(kb + r * RPL * 128);
-        vr[r] = *reinterpret_cast<const uint4 *>(vb + r * RPL * 128);
+        kr[r] = *reinterpret_cast<const u32x4_t *>(kb + r * RPL * 128);
+        vr[r] = *reinterpret_cast<const u32x4_t *>(vb + r * RPL * 128);
     }
     return ok;
 }
@@ -150,7 +150,7 @@ __device__ __forceinline__ bool load_page(const T *pool, const int32_t *ptab, in
 // Online-softmax update of one wave with one 16-token page: scores of the lane's tokens
 // (reduced over the LPR lanes sharing a token), running max / sum, V accumulation.
 template <typename T, int GROUP, int NR, int RPL>
-__device__ __forceinline__ void process_page(const uint4 (&kr)[NR], const uint4 (&vr)[NR], int nvalid,
+__device__ __forceinline__ void process_page(const u32x4_t (&kr)[NR], const u32x4_t (&vr)[NR], int nvalid,
                                              int rsub, const float (&qv)[GROUP][KVRaw<T>::EPL],
                                              float (&m_run)[GROUP], float (&l_run)[GROUP],
                                              float (&acc)[GROUP][KVRaw<T>::EPL]) {
@@ -253,7 +253,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeAttnArgs a) {
     const int32_t *ptab = a.page_table + (int64_t)b * a.max_pages;
     const int lane_off = rsub * 128 + d0;
     const int pg_first = p_begin / a.page, pg_last = (p_end - 1) / a.page;
-    uint4 ka[NR], va[NR], kb2[NR], vb2[NR];
+    u32x4_t ka[NR], va[NR], kb2[NR], vb2[NR];
     bool ok_a = load_page<T, NR, RPL>(pool, ptab, pg_first, a.n_pages, a.Hkv, hk, blk, lane_off, ka, va);
     bool ok_b = false;
     for (int pg = pg_first; pg <= pg_last; pg += 2) {
