@@ -259,6 +259,163 @@ __global__ __launch_bounds__(256) void splitk_reduce(GemmArgs g, const float *pa
     }
 }
 
+
+// ------------------------------------------------------------------------------------
+// 32x32x16 MFMA tile GEMM (bf16), for M > 64 with wide N.  v_mfma_f32_32x32x16_bf16
+// runs at about twice the rate per flop of the 16x16x32 form on gfx950.  A lane of one
+// 32x32x16 product supplies A[row = l%32][k = 8*(l/32)..+7] and B[k = 8*(l/32)..+7]
+// [col = l%32] and receives rows 8*j + 4*(l/32) + i (j, i < 4) of column l%32 as
+// acc[4*j + i].  One register staging set per K tile, issued at the top of the
+// iteration and pinned there (sched_barrier) so it overlaps the tile's MFMAs.  The
+// SwiGLU weights interleave in groups of 32 rows (gate, up) so a lane's pair of
+// accumulator tiles holds matching gate and up columns.
+// ------------------------------------------------------------------------------------
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+
+template <typename T>
+__device__ __forceinline__ const T *wrow32(const WSrc &w, int epi, int n, int K) {
+    if (epi == EPI_SWIGLU) {
+        const int pair = n >> 6, half = (n >> 5) & 1, r = n & 31;
+        const T *base = reinterpret_cast<const T *>(half ? w.p[1] : w.p[0]);
+        return base + (int64_t)(pair * 32 + r) * K;
+    }
+    return wrow<T>(w, EPI_STORE, n, K);
+}
+
+template <int N> struct Regs32 {
+    u32x4_t v[N];
+};
+
+template <int BM, int BN, int EPI>
+__global__ __launch_bounds__(256) void gemm32(GemmArgs g) {
+    constexpr int LD = BK + 8, CPR = BK / 8;
+    constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
+    constexpr int ACH = BM * CPR / 256, BCH = BN * CPR / 256;
+    static_assert(TM >= 1 && TN >= 1 && ACH >= 1 && BCH >= 1, "tile too small");
+    static_assert(EPI != EPI_SWIGLU || TN % 2 == 0, "swiglu needs gate/up tile pairs");
+    __shared__ __attribute__((aligned(16))) bf16_t sA[2][BM * LD];
+    __shared__ __attribute__((aligned(16))) bf16_t sB[2][BN * LD];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+    const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
+    const int t = xcd_tile(blockIdx.x, tiles_m * tiles_n);
+    const int m0 = (t % tiles_m) * BM, n0 = (t / tiles_m) * BN;
+    const bf16_t *A = reinterpret_cast<const bf16_t *>(g.A);
+    const bf16_t *ap[ACH];
+    const bf16_t *bp[BCH];
+    int ao[ACH], bo[BCH];
+#pragma unroll
+    for (int c = 0; c < ACH; ++c) {
+        const int ch = tid + 256 * c, r = ch / CPR, kc = (ch % CPR) * 8;
+        ap[c] = A + (int64_t)min(m0 + r, g.M - 1) * g.lda + kc;  // rows past M feed unstored rows
+        ao[c] = r * LD + kc;
+    }
+#pragma unroll
+    for (int c = 0; c < BCH; ++c) {
+        const int ch = tid + 256 * c, r = ch / CPR, kc = (ch % CPR) * 8;
+        bp[c] = wrow32<bf16_t>(g.w, g.epi, min(n0 + r, g.N - 1), g.K) + kc;
+        bo[c] = r * LD + kc;
+    }
+    f32x16_t acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    const int KT = g.K / BK;
+    const int fr = lane & 31, fk = (lane >> 5) * 8;
+    Regs32<ACH> ra;
+    Regs32<BCH> rb;
+#pragma unroll
+    for (int c = 0; c < ACH; ++c) ra.v[c] = *reinterpret_cast<const u32x4_t *>(ap[c]);
+#pragma unroll
+    for (int c = 0; c < BCH; ++c) rb.v[c] = *reinterpret_cast<const u32x4_t *>(bp[c]);
+#pragma unroll
+    for (int c = 0; c < ACH; ++c) *reinterpret_cast<u32x4_t *>(&sA[0][ao[c]]) = ra.v[c];
+#pragma unroll
+    for (int c = 0; c < BCH; ++c) *reinterpret_cast<u32x4_t *>(&sB[0][bo[c]]) = rb.v[c];
+    __syncthreads();
+    for (int kt = 0; kt < KT; ++kt) {
+        const int buf = kt & 1;
+        const int kn = min(kt + 1, KT - 1) * BK;  // last iteration re-reads its own tile, unused
+#pragma unroll
+        for (int c = 0; c < ACH; ++c) ra.v[c] = *reinterpret_cast<const u32x4_t *>(ap[c] + kn);
+#pragma unroll
+        for (int c = 0; c < BCH; ++c) rb.v[c] = *reinterpret_cast<const u32x4_t *>(bp[c] + kn);
+        __builtin_amdgcn_sched_barrier(0);
+        const bf16_t *sa = &sA[buf][wm * WM * LD], *sb = &sB[buf][wn * WN * LD];
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+            bf16x8_t af[TM], bfr[TN];
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+                af[i] = *reinterpret_cast<const bf16x8_t *>(&sa[(i * 32 + fr) * LD + ks * 16 + fk]);
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                bfr[j] = *reinterpret_cast<const bf16x8_t *>(&sb[(j * 32 + fr) * LD + ks * 16 + fk]);
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int c = 0; c < ACH; ++c) *reinterpret_cast<u32x4_t *>(&sA[buf ^ 1][ao[c]]) = ra.v[c];
+#pragma unroll
+        for (int c = 0; c < BCH; ++c) *reinterpret_cast<u32x4_t *>(&sB[buf ^ 1][bo[c]]) = rb.v[c];
+        __syncthreads();
+    }
+    const int rb0 = m0 + wm * WM + (lane >> 5) * 4, cb0 = n0 + wn * WN + (lane & 31);
+    if (EPI == EPI_SWIGLU) {
+        bf16_t *C = reinterpret_cast<bf16_t *>(g.C);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; j += 2) {
+                const int ncol = n0 + wn * WN + j * 32;  // first logical column of the gate tile
+                if (ncol >= g.N) continue;
+                const int ocol = (ncol >> 6) * 32 + (lane & 31);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = rb0 + i * 32 + (r >> 2) * 8 + (r & 3);
+                    if (row < g.M)
+                        C[(int64_t)row * g.ldc + ocol] = f32_to_bf16(silu_f(acc[i][j][r]) * acc[i][j + 1][r]);
+                }
+            }
+    } else {
+        float *C = reinterpret_cast<float *>(g.C);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int col = cb0 + j * 32;
+                if (col >= g.N) continue;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = rb0 + i * 32 + (r >> 2) * 8 + (r & 3);
+                    if (row >= g.M) continue;
+                    float *p = C + (int64_t)row * g.ldc + col;
+                    if (EPI == EPI_ADD) *p += acc[i][j][r];
+                    else *p = acc[i][j][r];
+                }
+            }
+    }
+}
+
+template <int BM, int BN>
+static void launch_gemm32(const GemmArgs &g, hipStream_t s) {
+    const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
+    switch (g.epi) {
+        case EPI_STORE: hipLaunchKernelGGL((gemm32<BM, BN, EPI_STORE>), dim3(tiles), dim3(256), 0, s, g); break;
+        case EPI_ADD: hipLaunchKernelGGL((gemm32<BM, BN, EPI_ADD>), dim3(tiles), dim3(256), 0, s, g); break;
+        default:
+            if constexpr ((BN / 2 / 32) % 2 == 0)
+                hipLaunchKernelGGL((gemm32<BM, BN, EPI_SWIGLU>), dim3(tiles), dim3(256), 0, s, g);
+            break;
+    }
+}
+
 // ------------------------------------------------------------------------------------
 // Weight-streaming GEMV for M <= 8 (bf16 or fp32)
 // ------------------------------------------------------------------------------------
@@ -429,23 +586,18 @@ void launch_gemm(const GemmArgs &g, DType dt, float *part, int64_t part_cap, hip
         launch_gemv<bf16_t>(g, s);
         return;
     }
-    const int t128 = ((g.M + 127) / 128) * ((g.N + 127) / 128);
-    if (g.M > 64 && t128 >= 200) {
-        launch_mfma<128, 128>(g, 1, part, s);
+    // Tile choice from measured sweeps on MI355X at the backbone's shapes.
+    if (g.M > 64 && g.N > 1024) {
+        const int t128 = ((g.M + 127) / 128) * ((g.N + 127) / 128);
+        if (t128 >= 200) launch_gemm32<128, 128>(g, s);
+        else if (g.epi == EPI_SWIGLU) launch_gemm32<64, 128>(g, s);
+        else launch_gemm32<64, 64>(g, s);
         return;
     }
-    if (g.M > 64) {
-        const int t64 = ((g.M + 63) / 64) * ((g.N + 63) / 64);
-        launch_mfma<64, 64>(g, choose_splits(g, t64, part_cap), part, s);
-        return;
-    }
-    if (g.M > 32) {
-        const int t64 = ((g.M + 63) / 64) * ((g.N + 63) / 64);
-        launch_mfma<64, 64>(g, choose_splits(g, t64, part_cap), part, s);
-        return;
-    }
+    // Small M or N = hidden: 32x64 tiles of the 16x16x32 kernel (more blocks in flight),
+    // split over K only when there are few tiles.
     const int t32 = ((g.M + 31) / 32) * ((g.N + 63) / 64);
-    launch_mfma<32, 64>(g, choose_splits(g, t32, part_cap), part, s);
+    launch_mfma<32, 64>(g, t32 < 64 ? choose_splits(g, t32, part_cap) : 1, part, s);
 }
 
 }  // namespace ttsbb

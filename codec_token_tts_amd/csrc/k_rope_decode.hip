@@ -54,7 +54,8 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(RopeKvArgs a) {
     }
     const float2 cs = a.rope[(int64_t)p * 64 + lane];
 
-    const int jobs = a.H + 2 * a.Hkv;
+    // dense mode leaves V to the transpose kernel below
+    const int jobs = a.dense ? a.H + a.Hkv : a.H + 2 * a.Hkv;
     for (int j = wave; j < jobs; j += 4) {
         const float *src = row + j * 128;
         float u = src[lane], u2 = src[lane + 64];
@@ -81,15 +82,9 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(RopeKvArgs a) {
         const int kv = j < a.H + a.Hkv ? 0 : 1;
         const int h = j - a.H - kv * a.Hkv;
         if (a.dense) {
-            if (kv == 0) {
-                bf16_t *k = a.kbuf + ((int64_t)h * a.s_pad + m) * 128;
-                k[lane] = f32_to_bf16(u);
-                k[lane + 64] = f32_to_bf16(u2);
-            } else {
-                bf16_t *vt = a.vtbuf + (int64_t)h * 128 * a.s_pad + m;
-                vt[(int64_t)lane * a.s_pad] = f32_to_bf16(u);
-                vt[(int64_t)(lane + 64) * a.s_pad] = f32_to_bf16(u2);
-            }
+            bf16_t *k = a.kbuf + ((int64_t)h * a.s_pad + m) * 128;
+            k[lane] = f32_to_bf16(u);
+            k[lane + 64] = f32_to_bf16(u2);
         } else if (ok) {
             TKV *dst = reinterpret_cast<TKV *>(a.pool_layer) +
                        ((((int64_t)page_id * 2 + kv) * a.Hkv + h) * a.page + slot) * 128;
@@ -99,12 +94,34 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(RopeKvArgs a) {
     }
 }
 
+// Dense mode: V^T [Hkv][128][s_pad] (bf16) from the V part of qkv, 64 tokens x 128 dims
+// per block through LDS, so that both the fp32 reads and the bf16 writes (64 tokens =
+// 128 bytes per dim row) are coalesced.
+__global__ __launch_bounds__(256) void dense_vt_kernel(RopeKvArgs a) {
+    __shared__ float tile[64][129];
+    const int t0 = blockIdx.x * 64, h = blockIdx.y;
+    const int width = (a.H + 2 * a.Hkv) * 128;
+    const int off = (a.H + a.Hkv + h) * 128;
+    for (int i = threadIdx.x; i < 64 * 128; i += 256) {
+        const int t = i >> 7, d = i & 127;
+        tile[t][d] = (t0 + t < a.M) ? a.qkv[(int64_t)(t0 + t) * width + off + d] : 0.f;
+    }
+    __syncthreads();
+    bf16_t *vt = a.vtbuf + (int64_t)h * 128 * a.s_pad;
+    for (int i = threadIdx.x; i < 128 * 64; i += 256) {
+        const int d = i >> 6, t = i & 63;
+        if (t0 + t < a.M) vt[(int64_t)d * a.s_pad + t0 + t] = f32_to_bf16(tile[t][d]);
+    }
+}
+
 void launch_rope_kv(const RopeKvArgs &a, DType kv_dt, hipStream_t s) {
     if (a.M <= 0) return;
     if (kv_dt == DT_BF16 || a.dense)
         hipLaunchKernelGGL(rope_kv_kernel<bf16_t>, dim3(a.M), dim3(256), 0, s, a);
     else
         hipLaunchKernelGGL(rope_kv_kernel<float>, dim3(a.M), dim3(256), 0, s, a);
+    if (a.dense)
+        hipLaunchKernelGGL(dense_vt_kernel, dim3((a.M + 63) / 64, a.Hkv), dim3(256), 0, s, a);
 }
 
 // ------------------------------------------------------------------------------------
@@ -298,6 +315,9 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeAttnArgs a) {
     }
 }
 
+// Merge of the chunk partials of one (stream, head): lane c < nc loads (m_c, l_c) so the
+// maximum and the weights come from one wave reduction; the accumulators are then read
+// four chunks at a time so that their loads overlap.
 template <typename TO>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeAttnArgs a) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -309,17 +329,42 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeAttnArgs a) {
     if (L > cap) L = cap;
     const int nc = min(a.n_chunks, (L + a.chunk - 1) / a.chunk);
     const float *part = a.part + ((int64_t)b * a.H + h) * a.n_chunks * PART_STRIDE;
-    float M = -INFINITY;
-    for (int c = 0; c < nc; ++c) M = fmaxf(M, part[c * PART_STRIDE]);
-    float l = 0.f, o0 = 0.f, o1 = 0.f;
-    for (int c = 0; c < nc; ++c) {
-        const float *pc = part + c * PART_STRIDE;
-        const float w = exp2f(pc[0] - M);
-        l += w * pc[1];
-        o0 += w * pc[4 + lane];
-        o1 += w * pc[4 + 64 + lane];
+    float M = -INFINITY, lsum = 0.f;
+    for (int c0 = 0; c0 < nc; c0 += 64) {
+        const int c = c0 + lane;
+        M = fmaxf(M, c < nc ? part[(int64_t)c * PART_STRIDE] : -INFINITY);
     }
-    const float inv = 1.0f / l;
+    M = wave_max(M);
+    for (int c0 = 0; c0 < nc; c0 += 64) {
+        const int c = c0 + lane;
+        if (c < nc) lsum += exp2f(part[(int64_t)c * PART_STRIDE] - M) * part[(int64_t)c * PART_STRIDE + 1];
+    }
+    lsum = wave_sum(lsum);
+    float o0 = 0.f, o1 = 0.f;
+    int c = 0;
+    for (; c + 4 <= nc; c += 4) {
+        float w[4], x0[4], x1[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float *pc = part + (int64_t)(c + u) * PART_STRIDE;
+            w[u] = pc[0];
+            x0[u] = pc[4 + lane];
+            x1[u] = pc[4 + 64 + lane];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float wu = exp2f(w[u] - M);
+            o0 += wu * x0[u];
+            o1 += wu * x1[u];
+        }
+    }
+    for (; c < nc; ++c) {
+        const float *pc = part + (int64_t)c * PART_STRIDE;
+        const float wu = exp2f(pc[0] - M);
+        o0 += wu * pc[4 + lane];
+        o1 += wu * pc[4 + 64 + lane];
+    }
+    const float inv = 1.0f / lsum;
     TO *out = reinterpret_cast<TO *>(a.out) + (int64_t)b * a.H * 128 + h * 128;
     out[lane] = from_f32<TO>(o0 * inv);
     out[lane + 64] = from_f32<TO>(o1 * inv);
