@@ -212,7 +212,7 @@ def cpu_baseline_maskgit():
 # ---------------------------------------------------------------------------------------
 
 def run_c5c4(args, T, torch):
-    total = args.warmup + args.steps
+    total = args.warmup + 2 * args.steps
     log("setup: decode (64 streams, paged KV) ...")
     dec = DecodeC5(T, torch, total)
     log("setup: MaskGIT (S = 950) ...")
@@ -225,8 +225,6 @@ def run_c5c4(args, T, torch):
     if T.ttsbb_sync(dec.ctx) != T.OK or T.ttsbb_sync(mg.ctx) != T.OK:
         raise RuntimeError("device-side index flag raised during warmup")
     log("timed: %d steps" % args.steps)
-    T.ttsbb_profile_start(dec.ctx)
-    T.ttsbb_profile_start(mg.ctx)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -240,14 +238,25 @@ def run_c5c4(args, T, torch):
         ev[i][2].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    pd = T.ttsbb_profile_stop(dec.ctx)
-    pm = T.ttsbb_profile_stop(mg.ctx)
     dec_ms = sum(a.elapsed_time(b) for a, b, _ in ev) / args.steps
     mg_ms = sum(b.elapsed_time(c) for _, b, c in ev) / args.steps
 
+    # Per-kernel durations: HIP events recorded by the library on its stream around each
+    # launch, over the same number of further steps (events add a little time per launch,
+    # so they are kept out of the timed region above).
+    log("profiled: %d steps" % args.steps)
+    T.ttsbb_profile_start(dec.ctx)
+    T.ttsbb_profile_start(mg.ctx)
+    for i in range(args.steps):
+        s = args.warmup + args.steps + i
+        dec.step(s)
+        mg.step(s)
+    pd = T.ttsbb_profile_stop(dec.ctx)
+    pm = T.ttsbb_profile_stop(mg.ctx)
+
     attn_ms, attn_n = pd["decode_attn"]
     attn_avg_ms = attn_ms / max(1, attn_n)
-    attn_bytes = dec.attn_bytes(args.warmup, args.steps)
+    attn_bytes = dec.attn_bytes(args.warmup + args.steps, args.steps)
     attn_gbs = attn_bytes / (attn_avg_ms * 1e-3) / 1e9
     gemm, attn_f, head_f = mg.flops()
     mg_mfma_ms = sum(pm[k][0] for k in ("gemm_qkv", "gemm_o", "gemm_gate_up", "gemm_down",
