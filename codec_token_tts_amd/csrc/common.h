@@ -45,10 +45,30 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 // Sum over aligned groups of `G` lanes (G a power of two <= 64).
+// Cross-lane move inside a 16-lane row through DPP (a VALU operand modifier, no LDS
+// round trip).  Every control used here reads a lane of the same row, so no lane is out
+// of range.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int DPP_XOR1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int DPP_HALF_MIRROR = 0x141; // lane i <- 7 - i inside each 8-lane half row
+constexpr int DPP_MIRROR = 0x140;      // lane i <- 15 - i inside each 16-lane row
+
+// Sum over aligned groups of G lanes; every lane of a group ends with the same value.
+// Up to 16 lanes the steps are DPP (pair, quad, half row, row); wider groups finish
+// with butterfly shuffles.
 template <int G>
 __device__ __forceinline__ float group_sum(float v) {
+    static_assert(G == 1 || G == 2 || G == 4 || G == 8 || G == 16 || G == 32 || G == 64, "group size");
+    if constexpr (G >= 2) v += dpp_f<DPP_XOR1>(v);
+    if constexpr (G >= 4) v += dpp_f<DPP_XOR2>(v);
+    if constexpr (G >= 8) v += dpp_f<DPP_HALF_MIRROR>(v);
+    if constexpr (G >= 16) v += dpp_f<DPP_MIRROR>(v);
 #pragma unroll
-    for (int o = G / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
+    for (int o = 16; o < G; o <<= 1) v += __shfl_xor(v, o, WAVE);
     return v;
 }
 

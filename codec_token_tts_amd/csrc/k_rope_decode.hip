@@ -148,10 +148,8 @@ template <> __device__ inline void KVRaw<float>::unpack(const u32x4_t &t, float 
 
 // Issue the 16-byte lane loads of the K and V blocks of page `pg` of a stream.
 template <typename T, int NR, int RPL>
-__device__ __forceinline__ bool load_page(const T *pool, const int32_t *ptab, int pg, int n_pages,
-                                          int Hkv, int hk, int64_t blk, int lane_off, u32x4_t (&kr)[NR],
-                                          u32x4_t (&vr)[NR]) {
-    const int page_id = ptab[pg];
+__device__ __forceinline__ bool load_page(const T *pool, int page_id, int n_pages, int Hkv, int hk,
+                                          int64_t blk, int lane_off, u32x4_t (&kr)[NR], u32x4_t (&vr)[NR]) {
     // An invalid id (flagged by K4) reads page 0, which always exists, and is ignored.
     const bool ok = page_id >= 0 && page_id < n_pages;
     const T *kb = pool + (((int64_t)(ok ? page_id : 0) * 2 + 0) * Hkv + hk) * blk + lane_off;
@@ -226,18 +224,24 @@ __device__ __forceinline__ void process_page(const u32x4_t (&kr)[NR], const u32x
 // loaded into a second register set while the current page is processed, so every
 // wave keeps one page (8 KB in bf16) of loads in flight behind its arithmetic.
 template <typename T, int GROUP>
-__global__ __launch_bounds__(256) void decode_attn_kernel(DecodeAttnArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 4 : 2)))
+void decode_attn_kernel(DecodeAttnArgs a) {
     constexpr int EPL = KVRaw<T>::EPL;
     constexpr int LPR = 128 / EPL;  // lanes per 128-dim row
     constexpr int RPL = 64 / LPR;   // rows (tokens) per wave load
     constexpr int NR = 16 / RPL;    // wave loads per 16-token page block
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    // wave-uniform by construction; readfirstlane lets the compiler keep the item's
+    // indices in scalar registers (no per-lane page-id selection loops)
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int item = blockIdx.x * 4 + wave;
     const int total = a.B * a.Hkv * a.n_chunks;
     if (item >= total) return;
-    const int c = item % a.n_chunks;
-    const int t = item / a.n_chunks;
-    const int hk = t % a.Hkv, b = t / a.Hkv;
+    // KV heads vary fastest: the waves of a block stream neighbouring 4 KB blocks of the
+    // same pool pages (a page holds all heads' K and V contiguously)
+    const int hk = item % a.Hkv;
+    const int t = item / a.Hkv;
+    const int c = t % a.n_chunks, b = t / a.n_chunks;
 
     int L = a.pos[b] + 1;
     const int cap = a.max_pages * a.page;
@@ -270,20 +274,30 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeAttnArgs a) {
     const int32_t *ptab = a.page_table + (int64_t)b * a.max_pages;
     const int lane_off = rsub * 128 + d0;
     const int pg_first = p_begin / a.page, pg_last = (p_end - 1) / a.page;
+    // The chunk's page ids (at most 64, one per lane) are read once up front: a page-id
+    // load inside the loop would have to complete before the next page's addresses exist,
+    // and loads complete in order, so that wait would also drain the prefetch.
+    const int my_page = (lane <= pg_last - pg_first) ? ptab[pg_first + lane] : 0;
+    auto page_of = [&](int pg) { return __builtin_amdgcn_readlane(my_page, pg - pg_first); };
     u32x4_t ka[NR], va[NR], kb2[NR], vb2[NR];
-    bool ok_a = load_page<T, NR, RPL>(pool, ptab, pg_first, a.n_pages, a.Hkv, hk, blk, lane_off, ka, va);
-    bool ok_b = false;
-    for (int pg = pg_first; pg <= pg_last; pg += 2) {
-        // ping: page pg in (ka, va); pong: page pg + 1 in (kb2, vb2)
-        if (pg + 1 <= pg_last)
-            ok_b = load_page<T, NR, RPL>(pool, ptab, pg + 1, a.n_pages, a.Hkv, hk, blk, lane_off, kb2, vb2);
-        if (ok_a)
-            process_page<T, GROUP, NR, RPL>(ka, va, p_end - pg * a.page, rsub, qv, m_run, l_run, acc);
-        if (pg + 1 > pg_last) break;
-        if (pg + 2 <= pg_last)
-            ok_a = load_page<T, NR, RPL>(pool, ptab, pg + 2, a.n_pages, a.Hkv, hk, blk, lane_off, ka, va);
-        if (ok_b)
-            process_page<T, GROUP, NR, RPL>(kb2, vb2, p_end - (pg + 1) * a.page, rsub, qv, m_run, l_run, acc);
+    // Ping-pong over the chunk's pages.  Every load is issued unconditionally (the index
+    // is clamped to the last page, whose re-read hits L2) and every page is processed
+    // unconditionally (an invalid page counts no valid token), so no branch forces the
+    // outstanding prefetch to drain.
+    const int np = pg_last - pg_first + 1;
+    bool ok_a = load_page<T, NR, RPL>(pool, page_of(pg_first), a.n_pages, a.Hkv, hk, blk, lane_off, ka, va);
+    bool ok_b;
+    for (int i = 0; i < np; i += 2) {
+        // ping: page i in (ka, va); pong: page i + 1 in (kb2, vb2)
+        const int pg = pg_first + i;
+        ok_b = load_page<T, NR, RPL>(pool, page_of(pg_first + min(i + 1, np - 1)), a.n_pages, a.Hkv, hk, blk,
+                                     lane_off, kb2, vb2);
+        process_page<T, GROUP, NR, RPL>(ka, va, ok_a ? p_end - pg * a.page : 0, rsub, qv, m_run, l_run, acc);
+        if (i + 1 >= np) break;
+        ok_a = load_page<T, NR, RPL>(pool, page_of(pg_first + min(i + 2, np - 1)), a.n_pages, a.Hkv, hk, blk,
+                                     lane_off, ka, va);
+        process_page<T, GROUP, NR, RPL>(kb2, vb2, ok_b ? p_end - (pg + 1) * a.page : 0, rsub, qv, m_run, l_run,
+                                        acc);
     }
 
     // merge the RPL lane groups (same dims, different tokens)

@@ -463,11 +463,12 @@ TTSBB_API ttsbb_status ttsbb_decode_step(ttsbb_ctx *ctx, int32_t batch, float *x
     const int hd_all = H * hd;
     const size_t layer_elems = (size_t)n_pages * 2 * Hkv * g.kv_page * hd;
 
-    // Split of each stream's positions into chunks for the decode attention: 256
-    // positions per wave, halved while there are fewer than 2048 (stream, KV head,
-    // chunk) work items; the partial buffer holds max_rows * MAX_CHUNKS chunks per head.
+    // Split of each stream's positions into chunks for the decode attention: 128
+    // positions per wave (measured best on the paged workload), halved while there are
+    // fewer than 2048 (stream, KV head, chunk) work items; the partial buffer holds
+    // max_rows * MAX_CHUNKS chunks per head, and a chunk spans at most 64 pages.
     const int cap = max_pages * g.kv_page;
-    int chunk = 256;
+    int chunk = 128;
     while (chunk > g.kv_page && (int64_t)batch * Hkv * ((cap + chunk - 1) / chunk) < 2048) chunk /= 2;
     chunk = round_up(chunk, g.kv_page);
     int n_chunks = (cap + chunk - 1) / chunk;
@@ -475,6 +476,7 @@ TTSBB_API ttsbb_status ttsbb_decode_step(ttsbb_ctx *ctx, int32_t batch, float *x
         chunk *= 2;
         n_chunks = (cap + chunk - 1) / chunk;
     }
+    if (chunk > 64 * g.kv_page) return TTSBB_UNSUPPORTED;
 
     for (int l = 0; l < g.n_layers; ++l) {
         const ttsbb_layer &L = ctx->layers[l];
