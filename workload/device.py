@@ -48,6 +48,8 @@ def _lib():
                                  C.c_int, C.c_void_p, C.c_int64, C.c_uint64, C.c_uint32, C.c_uint32,
                                  C.c_float, C.c_int, C.c_void_p]
         L.wl_fill_kv.restype = C.c_int
+        L.wl_copy.argtypes = [C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p]
+        L.wl_copy.restype = C.c_int
         _fill = L
     return _fill
 
@@ -131,3 +133,12 @@ def bits_to_f32(t) -> np.ndarray:
     if a.dtype == np.int16:
         return gen.bf16_bits_to_f32(a.view(np.uint16))
     return a.astype(np.float32)
+
+
+def copy(src, dst, nbytes: int) -> None:
+    """Plain device copy of nbytes (multiple of 16) through the workload library's copy kernel."""
+    assert src.is_cuda and dst.is_cuda
+    assert nbytes % 16 == 0 and nbytes <= src.numel() * src.element_size() and \
+        nbytes <= dst.numel() * dst.element_size()
+    if _lib().wl_copy(src.data_ptr(), dst.data_ptr(), nbytes, _stream_ptr()) != 0:
+        raise RuntimeError("wl_copy failed")

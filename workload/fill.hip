@@ -78,6 +78,13 @@ __global__ void fill_kv_kernel(void *pool, int64_t n, int hkv, int page, int hd,
     }
 }
 
+// Plain 16-byte-per-thread copy: the reference kernel of known traffic against which the
+// hardware byte counters (FETCH_SIZE, WRITE_SIZE) are scaled.
+__global__ void copy_kernel(const uint4 *__restrict__ src, uint4 *__restrict__ dst, int64_t n16) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256)
+        dst[i] = src[i];
+}
+
 int grid_for(int64_t n) {
     int64_t g = (n + 255) / 256;
     return (int)(g > 65536 ? 65536 : (g < 1 ? 1 : g));
@@ -105,5 +112,15 @@ extern "C" __attribute__((visibility("default"))) int wl_fill_kv(void *pool_laye
     hipLaunchKernelGGL(fill_kv_kernel, dim3(grid_for(n)), dim3(256), 0, (hipStream_t)hip_stream, pool_layer,
                        n, hkv, page, hd, page_owner, max_pages, lengths, pos_stride, seed, stream_k,
                        stream_v, scale, bf16);
+    return hipPeekAtLastError() == hipSuccess ? 0 : -1;
+}
+
+// Copies `bytes` (a multiple of 16) from src to dst, both device buffers of at least that size.
+extern "C" __attribute__((visibility("default"))) int wl_copy(const void *src, void *dst, int64_t bytes,
+                                                              void *hip_stream) {
+    if (bytes <= 0 || bytes % 16) return bytes == 0 ? 0 : -1;
+    const int64_t n16 = bytes / 16;
+    hipLaunchKernelGGL(copy_kernel, dim3(grid_for(n16)), dim3(256), 0, (hipStream_t)hip_stream,
+                       (const uint4 *)src, (uint4 *)dst, n16);
     return hipPeekAtLastError() == hipSuccess ? 0 : -1;
 }
