@@ -77,20 +77,32 @@ void launch_embed(const EmbedArgs &a, DType dt, hipStream_t s) {
 }
 
 template <typename TO>
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const float *x, int ldx, int hidden,
-                                                      const float *g, float eps, TO *out) {
+__global__ __launch_bounds__(256) void rmsnorm_kernel(float *x, int ldx, int hidden, const float *g, float eps,
+                                                      TO *out, const float *pend, int n_pend, int64_t pend_ld,
+                                                      int64_t pend_stride) {
     __shared__ float red[4];
     const int r = blockIdx.x;
-    const float *xr = x + (int64_t)r * ldx;
+    float *xr = x + (int64_t)r * ldx;
     float ss = 0.f;
     for (int c = threadIdx.x * 4; c < hidden; c += 1024) {
         float4 v = *reinterpret_cast<const float4 *>(xr + c);
+        if (n_pend > 0) {  // deferred residual update, in split order
+            for (int z = 0; z < n_pend; ++z) {
+                const float4 p = *reinterpret_cast<const float4 *>(pend + z * pend_stride + (int64_t)r * pend_ld + c);
+                v.x += p.x;
+                v.y += p.y;
+                v.z += p.z;
+                v.w += p.w;
+            }
+            *reinterpret_cast<float4 *>(xr + c) = v;
+        }
         ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
     }
+    if (g == nullptr) return;
     ss = block_sum_256(ss, red);
     const float inv = 1.0f / sqrtf(ss / (float)hidden + eps);
     for (int c = threadIdx.x * 4; c < hidden; c += 1024) {
-        float4 v = *reinterpret_cast<const float4 *>(xr + c);
+        float4 v = *reinterpret_cast<const float4 *>(xr + c);  // this thread's own columns
         float4 gg = *reinterpret_cast<const float4 *>(g + c);
         TO *o = out + (int64_t)r * hidden + c;
         o[0] = from_f32<TO>(v.x * inv * gg.x);
@@ -100,15 +112,16 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float *x, int ldx, i
     }
 }
 
-void launch_rmsnorm(const float *x, int ldx, int rows, int hidden, const float *gain, float eps,
-                    void *out, DType out_dt, hipStream_t s) {
+void launch_rmsnorm(float *x, int ldx, int rows, int hidden, const float *gain, float eps, void *out,
+                    DType out_dt, hipStream_t s, const float *pend, int n_pend, int64_t pend_ld,
+                    int64_t pend_stride) {
     if (rows <= 0) return;
     if (out_dt == DT_BF16)
-        hipLaunchKernelGGL(rmsnorm_kernel<bf16_t>, dim3(rows), dim3(256), 0, s, x, ldx, hidden,
-                           gain, eps, reinterpret_cast<bf16_t *>(out));
+        hipLaunchKernelGGL(rmsnorm_kernel<bf16_t>, dim3(rows), dim3(256), 0, s, x, ldx, hidden, gain, eps,
+                           reinterpret_cast<bf16_t *>(out), pend, n_pend, pend_ld, pend_stride);
     else
-        hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(rows), dim3(256), 0, s, x, ldx, hidden,
-                           gain, eps, reinterpret_cast<float *>(out));
+        hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(rows), dim3(256), 0, s, x, ldx, hidden, gain, eps,
+                           reinterpret_cast<float *>(out), pend, n_pend, pend_ld, pend_stride);
 }
 
 __global__ void increment_kernel(int32_t *v, int n) {

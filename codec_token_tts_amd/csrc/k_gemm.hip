@@ -417,6 +417,177 @@ static void launch_gemm32(const GemmArgs &g, hipStream_t s) {
 }
 
 // ------------------------------------------------------------------------------------
+// Skinny MFMA GEMM for 8 < M <= 64 (the batched decode step): a weight-streaming kernel.
+// At M = 64 a projection reads each weight once and does 64 flops per weight element,
+// so it is bound by HBM bandwidth and by the latency of getting the weights in flight.
+// A block owns a slice of 16 output columns (16 gate + 16 up for SwiGLU) over one K
+// range, split into four per-wave K ranges of STEPS x 32.  Every lane issues all of its
+// loads up front: its weight row segments (16 bytes per step, straight into the MFMA B
+// operand: lane l holds W[col l%16][k 8*(l/16)..+7]) and the activation fragments of
+// the MT 16-row tiles (A operand: row l%16 of the tile, same k), then runs the
+// STEPS x MT x NT products.  The four waves' accumulators are summed in LDS in wave
+// order.  Only a residual-add product is split over K (grid = slices x splits, to give
+// the N = hidden projections enough blocks): each block writes its fp32 partial sums
+// and the residual update is left to the RMSNorm that reads the residual next, which
+// adds the partials in split order (deterministic, and no extra launch or cross-block
+// synchronisation).
+// ------------------------------------------------------------------------------------
+constexpr int SK_MAX_SPLIT = 8;
+
+template <int MT, int STEPS, int EPI>
+__global__ __launch_bounds__(256) void gemm_skinny(GemmArgs g, float *part, int n_split) {
+    constexpr int NT = (EPI == EPI_SWIGLU) ? 2 : 1;
+    __shared__ float red[4][NT][MT][4][64];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int slice = blockIdx.x / n_split, ks = blockIdx.x % n_split;
+    const int fr = lane & 15;
+    const int k0 = (ks * 4 + wave) * STEPS * 32 + (lane >> 4) * 8;
+    const bf16_t *A = reinterpret_cast<const bf16_t *>(g.A);
+
+    u32x4_t wv[NT][STEPS];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        // columns past N read column N-1: their results are never stored
+        const bf16_t *wp;
+        if (EPI == EPI_SWIGLU)  // tile 0: gate rows, tile 1: up rows of the same 16 outputs
+            wp = reinterpret_cast<const bf16_t *>(g.w.p[nt]) + (int64_t)min(slice * 16 + fr, g.N / 2 - 1) * g.K;
+        else
+            wp = wrow<bf16_t>(g.w, EPI_STORE, min(slice * 16 + fr, g.N - 1), g.K);
+        wp += k0;
+#pragma unroll
+        for (int s = 0; s < STEPS; ++s) wv[nt][s] = *reinterpret_cast<const u32x4_t *>(wp + s * 32);
+    }
+    u32x4_t av[MT][STEPS];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const bf16_t *ap = A + (int64_t)min(mt * 16 + fr, g.M - 1) * g.lda + k0;  // rows past M: unstored
+#pragma unroll
+        for (int s = 0; s < STEPS; ++s) av[mt][s] = *reinterpret_cast<const u32x4_t *>(ap + s * 32);
+    }
+    // keep every load ahead of the products: all of them in flight at once
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4_t acc[NT][MT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8_t, av[mt][s]), __builtin_bit_cast(bf16x8_t, wv[nt][s]), acc[nt][mt],
+                    0, 0, 0);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) red[wave][nt][mt][r][lane] = acc[nt][mt][r];
+    __syncthreads();
+
+    // Thread (r = wave, l = lane) finishes element r of lane l's accumulators in every
+    // M tile: row mt*16 + 4*(l/16) + r, column l%16 of the slice.
+    const int r = wave, l = lane;
+    float v[NT][MT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+            v[nt][mt] = ((red[0][nt][mt][r][l] + red[1][nt][mt][r][l]) + red[2][nt][mt][r][l]) + red[3][nt][mt][r][l];
+    const int col = slice * 16 * NT + (l & 15);  // logical column of the first N tile
+
+    if (EPI == EPI_ADD && n_split > 1) {  // partial sums; the residual update is deferred
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int row = mt * 16 + 4 * (l >> 4) + r;
+            if (row < g.M && col < g.N) part[((int64_t)ks * g.M + row) * g.N + col] = v[0][mt];
+        }
+        return;
+    }
+
+    float prev[MT];  // residual values, all loaded before any store
+    if (EPI == EPI_ADD) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+            prev[mt] = reinterpret_cast<const float *>(g.C)[(int64_t)min(mt * 16 + 4 * (l >> 4) + r, g.M - 1) * g.ldc +
+                                                           min(col, g.N - 1)];
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int row = mt * 16 + 4 * (l >> 4) + r;
+        if (row >= g.M) continue;
+        if (EPI == EPI_SWIGLU) {
+            if (col < g.N)
+                reinterpret_cast<bf16_t *>(g.C)[(int64_t)row * g.ldc + slice * 16 + (l & 15)] =
+                    f32_to_bf16(silu_f(v[0][mt]) * v[NT - 1][mt]);
+        } else if (col < g.N) {
+            float *p = reinterpret_cast<float *>(g.C) + (int64_t)row * g.ldc + col;
+            *p = EPI == EPI_ADD ? prev[mt] + v[0][mt] : v[0][mt];
+        }
+    }
+}
+
+template <int MT, int STEPS>
+static void launch_skinny_mt(const GemmArgs &g, int slices, int n_split, float *part, hipStream_t s) {
+    const dim3 grid(slices * n_split);
+    switch (g.epi) {
+        case EPI_STORE:
+            hipLaunchKernelGGL((gemm_skinny<MT, STEPS, EPI_STORE>), grid, dim3(256), 0, s, g, part, n_split);
+            break;
+        case EPI_ADD:
+            hipLaunchKernelGGL((gemm_skinny<MT, STEPS, EPI_ADD>), grid, dim3(256), 0, s, g, part, n_split);
+            break;
+        default:
+            hipLaunchKernelGGL((gemm_skinny<MT, STEPS, EPI_SWIGLU>), grid, dim3(256), 0, s, g, part, n_split);
+            break;
+    }
+}
+
+// Slices of 16 (SwiGLU: 32) logical columns; each wave runs STEPS = 8 or 4 K steps of
+// 32.  A residual-add product takes the fewest K splits (at most SK_MAX_SPLIT) that
+// give >= 256 blocks; the others are not split.  Returns -1 when the shape does not
+// fit (the tile kernels then run it), else the number of splits.
+static int skinny_plan(const GemmArgs &g, int64_t part_cap, int &slices, int &steps) {
+    const int width = g.epi == EPI_SWIGLU ? 32 : 16;
+    if (g.M > 64 || g.K % 512 != 0 || (g.epi == EPI_SWIGLU && g.N % 32 != 0)) return -1;
+    slices = (g.N + width - 1) / width;
+    int n_split = 0;
+    const int zmax = g.epi == EPI_ADD ? SK_MAX_SPLIT : 1;
+    for (int z = 1; z <= zmax; ++z) {
+        if (g.K % (z * 128) != 0) continue;
+        const int st = g.K / (z * 128);
+        if (st != 8 && st != 4) continue;
+        n_split = z;
+        steps = st;
+        if (slices * z >= 256) break;
+    }
+    if (n_split == 0) return -1;
+    if (n_split > 1 && (int64_t)n_split * g.M * g.N > part_cap) return -1;
+    return n_split;
+}
+
+static int launch_skinny(const GemmArgs &g, float *part, int64_t part_cap, hipStream_t s) {
+    int slices, steps;
+    const int n_split = skinny_plan(g, part_cap, slices, steps);
+    if (n_split < 0) return -1;
+    const int mt = (g.M + 15) / 16;
+    if (steps == 8) {
+        if (mt == 1) launch_skinny_mt<1, 8>(g, slices, n_split, part, s);
+        else if (mt == 2) launch_skinny_mt<2, 8>(g, slices, n_split, part, s);
+        else launch_skinny_mt<4, 8>(g, slices, n_split, part, s);
+    } else {
+        if (mt == 1) launch_skinny_mt<1, 4>(g, slices, n_split, part, s);
+        else if (mt == 2) launch_skinny_mt<2, 4>(g, slices, n_split, part, s);
+        else launch_skinny_mt<4, 4>(g, slices, n_split, part, s);
+    }
+    return n_split > 1 ? n_split : 0;
+}
+
+// ------------------------------------------------------------------------------------
 // Weight-streaming GEMV for M <= 8 (bf16 or fp32)
 // ------------------------------------------------------------------------------------
 constexpr int GEMV_MAXM = 8;
@@ -569,8 +740,8 @@ static int choose_splits(const GemmArgs &g, int tiles, int64_t part_cap) {
     return splits;
 }
 
-void launch_gemm(const GemmArgs &g, DType dt, float *part, int64_t part_cap, hipStream_t s) {
-    if (g.M <= 0) return;
+int launch_gemm(const GemmArgs &g, DType dt, float *part, int64_t part_cap, hipStream_t s) {
+    if (g.M <= 0) return 0;
     if (dt == DT_F32) {
         // fp32 mode streams weights; larger M is processed GEMV_MAXM rows at a time
         for (int m0 = 0; m0 < g.M; m0 += GEMV_MAXM) {
@@ -580,11 +751,15 @@ void launch_gemm(const GemmArgs &g, DType dt, float *part, int64_t part_cap, hip
             h.C = reinterpret_cast<float *>(g.C) + (int64_t)m0 * g.ldc;
             launch_gemv<float>(h, s);
         }
-        return;
+        return 0;
     }
     if (g.M <= GEMV_MAXM) {
         launch_gemv<bf16_t>(g, s);
-        return;
+        return 0;
+    }
+    if (g.M <= 64) {
+        const int pending = launch_skinny(g, part, part_cap, s);
+        if (pending >= 0) return pending;
     }
     // Tile choice from measured sweeps on MI355X at the backbone's shapes.
     if (g.M > 64 && g.N > 1024) {
@@ -592,12 +767,13 @@ void launch_gemm(const GemmArgs &g, DType dt, float *part, int64_t part_cap, hip
         if (t128 >= 200) launch_gemm32<128, 128>(g, s);
         else if (g.epi == EPI_SWIGLU) launch_gemm32<64, 128>(g, s);
         else launch_gemm32<64, 64>(g, s);
-        return;
+        return 0;
     }
     // Small M or N = hidden: 32x64 tiles of the 16x16x32 kernel (more blocks in flight),
     // split over K only when there are few tiles.
     const int t32 = ((g.M + 31) / 32) * ((g.N + 63) / 64);
     launch_mfma<32, 64>(g, t32 < 64 ? choose_splits(g, t32, part_cap) : 1, part, s);
+    return 0;
 }
 
 }  // namespace ttsbb

@@ -32,8 +32,13 @@ struct EmbedArgs {
 void launch_embed(const EmbedArgs &a, DType dt, hipStream_t s);
 
 // ---- K2: RMSNorm of fp32 rows into the operand dtype ------------------------------
-void launch_rmsnorm(const float *x, int ldx, int rows, int hidden, const float *gain, float eps,
-                    void *out, DType out_dt, hipStream_t s);
+// Optional deferred residual update first: with n_pend > 0, row r of x becomes
+// x[r] + pend[0][r] + ... + pend[n_pend-1][r] (summed in that order; pend rows are
+// pend_ld floats apart, splits pend_stride apart) and is written back.  gain == nullptr
+// applies the update only (out unused).
+void launch_rmsnorm(float *x, int ldx, int rows, int hidden, const float *gain, float eps,
+                    void *out, DType out_dt, hipStream_t s, const float *pend = nullptr, int n_pend = 0,
+                    int64_t pend_ld = 0, int64_t pend_stride = 0);
 
 // ---- K3: projections  Y[M][N] = A[M][K] * W[N][K]^T with an epilogue --------------
 enum Epi { EPI_STORE = 0, EPI_ADD = 1, EPI_SWIGLU = 2 };
@@ -54,8 +59,11 @@ struct GemmArgs {
     int ldc;
     int epi;
 };
-// part: fp32 workspace of part_cap floats for split-K partial sums
-void launch_gemm(const GemmArgs &g, DType dt, float *part, int64_t part_cap, hipStream_t s);
+// part: fp32 workspace of part_cap floats for split-K partial sums.  Returns the number
+// of K splits whose partial sums are left in part[z][M][N] for the caller to add (an
+// EPI_ADD product on the skinny path defers its residual update to the next RMSNorm,
+// which sums them in split order); 0 when C holds the result.
+int launch_gemm(const GemmArgs &g, DType dt, float *part, int64_t part_cap, hipStream_t s);
 
 // ---- K4: per-head RMSNorm + RoPE + K/V write --------------------------------------
 // qkv fp32 [M][(H + 2 Hkv) * 128].  Decode mode (dense == 0): row m is stream m at

@@ -66,6 +66,8 @@ struct ttsbb_ctx {
     int rank_cap = 0;
     float *gpart = nullptr;   // split-K partial sums
     int64_t gpart_cap = 0;    // floats
+    int pend_splits = 0;      // K splits of a residual update still held in gpart
+    int pend_rows = 0;
     float2 *rope = nullptr;
     int *flag = nullptr;
     std::vector<void *> allocs;
@@ -324,12 +326,36 @@ namespace {
 
 // The post-attention half of a layer and the pre-attention projection; shared by both
 // modes.  x is the fp32 residual stream [M][hidden].
-void qkv_projection(ttsbb_ctx *c, const ttsbb_layer &L, const float *x, int M, bool tapit) {
+// RMSNorm of rows [0, M) of the residual stream x into c->h, first applying a residual
+// update that a split projection left in gpart (gain == nullptr: the update only).
+void norm_rows(ttsbb_ctx *c, float *x, int M, const float *gain) {
     const ttsbb_config &g = c->cfg;
-    {
+    const int np = c->pend_rows == M ? c->pend_splits : 0;  // rows always match by construction
+    if (gain || np > 0) {
         KScope k(c, TTSBB_K_RMSNORM);
-        launch_rmsnorm(x, g.hidden, M, g.hidden, L.attn_norm, g.rms_eps, c->h, c->dt, c->stream);
+        launch_rmsnorm(x, g.hidden, M, g.hidden, gain, g.rms_eps, c->h, c->dt, c->stream, c->gpart, np, g.hidden,
+                       (int64_t)M * g.hidden);
     }
+    c->pend_splits = 0;
+}
+
+void flush_residual(ttsbb_ctx *c, float *x, int M) {
+    if (c->pend_splits > 0) norm_rows(c, x, M, nullptr);
+}
+
+// Residual-add projection: the product may leave its update pending in gpart.
+void add_projection(ttsbb_ctx *c, const GemmArgs &a) {
+    c->pend_splits = launch_gemm(a, c->dt, c->gpart, c->gpart_cap, c->stream);
+    c->pend_rows = a.M;
+}
+
+void qkv_projection(ttsbb_ctx *c, const ttsbb_layer &L, float *x, int M, bool tapit) {
+    const ttsbb_config &g = c->cfg;
+    if (tapit) {
+        flush_residual(c, x, M);
+        tap_dense(c, TTSBB_TAP_X_IN, x, DT_F32, M, g.hidden, g.hidden);
+    }
+    norm_rows(c, x, M, L.attn_norm);
     GemmArgs a = {};
     a.A = c->h;
     a.lda = g.hidden;
@@ -376,14 +402,13 @@ void post_attention(ttsbb_ctx *c, const ttsbb_layer &L, float *x, int M, bool ta
     a.epi = EPI_ADD;
     {
         KScope k(c, TTSBB_K_GEMM_O);
-        launch_gemm(a, c->dt, c->gpart, c->gpart_cap, c->stream);
+        add_projection(c, a);
     }
-    if (tapit) tap_dense(c, TTSBB_TAP_X_MID, x, DT_F32, M, g.hidden, g.hidden);
-
-    {
-        KScope k(c, TTSBB_K_RMSNORM);
-        launch_rmsnorm(x, g.hidden, M, g.hidden, L.ffn_norm, g.rms_eps, c->h, c->dt, c->stream);
+    if (tapit) {
+        flush_residual(c, x, M);
+        tap_dense(c, TTSBB_TAP_X_MID, x, DT_F32, M, g.hidden, g.hidden);
     }
+    norm_rows(c, x, M, L.ffn_norm);
     if (tapit) tap_dense(c, TTSBB_TAP_H_FFN, c->h, c->dt, M, g.hidden, g.hidden);
     GemmArgs u = {};
     u.A = c->h;
@@ -418,9 +443,12 @@ void post_attention(ttsbb_ctx *c, const ttsbb_layer &L, float *x, int M, bool ta
     d.epi = EPI_ADD;
     {
         KScope k(c, TTSBB_K_GEMM_DOWN);
-        launch_gemm(d, c->dt, c->gpart, c->gpart_cap, c->stream);
+        add_projection(c, d);
     }
-    if (tapit) tap_dense(c, TTSBB_TAP_X_OUT, x, DT_F32, M, g.hidden, g.hidden);
+    if (tapit) {
+        flush_residual(c, x, M);
+        tap_dense(c, TTSBB_TAP_X_OUT, x, DT_F32, M, g.hidden, g.hidden);
+    }
 }
 
 void head_gemm(ttsbb_ctx *c, const void *head, int M, int N, float *out, int ldc) {
@@ -450,6 +478,7 @@ TTSBB_API ttsbb_status ttsbb_decode_step(ttsbb_ctx *ctx, int32_t batch, float *x
                                          int32_t group_vocab, int32_t *argmax, float *logits) {
     if (!ctx || batch < 0) return TTSBB_INVALID_ARG;
     const ttsbb_config &g = ctx->cfg;
+    ctx->pend_splits = 0;
     if (batch > g.max_rows) return TTSBB_INVALID_ARG;
     if (batch == 0) return TTSBB_OK;
     if (!x || !positions) return TTSBB_INVALID_ARG;
@@ -481,7 +510,6 @@ TTSBB_API ttsbb_status ttsbb_decode_step(ttsbb_ctx *ctx, int32_t batch, float *x
     for (int l = 0; l < g.n_layers; ++l) {
         const ttsbb_layer &L = ctx->layers[l];
         const bool tapit = (l == ctx->tap_layer);
-        if (tapit) tap_dense(ctx, TTSBB_TAP_X_IN, x, DT_F32, batch, g.hidden, g.hidden);
         qkv_projection(ctx, L, x, batch, tapit);
         void *pool_l = reinterpret_cast<char *>(kv_pool) + (size_t)l * layer_elems * ctx->esz;
 
@@ -537,12 +565,10 @@ TTSBB_API ttsbb_status ttsbb_decode_step(ttsbb_ctx *ctx, int32_t batch, float *x
 
         post_attention(ctx, L, x, batch, tapit);
     }
+    if (!head) flush_residual(ctx, x, batch);
     if (head) {
         const int N = n_groups * group_vocab;
-        {
-            KScope k(ctx, TTSBB_K_RMSNORM);
-            launch_rmsnorm(x, g.hidden, batch, g.hidden, ctx->final_norm, g.rms_eps, ctx->h, ctx->dt, ctx->stream);
-        }
+        norm_rows(ctx, x, batch, ctx->final_norm);
         if (ctx->tap_layer >= 0) tap_dense(ctx, TTSBB_TAP_HEAD_IN, ctx->h, ctx->dt, batch, g.hidden, g.hidden);
         float *lg = logits ? logits : ctx->logits;
         head_gemm(ctx, head, batch, N, lg, N);
@@ -565,6 +591,7 @@ TTSBB_API ttsbb_status ttsbb_maskgit_pass(ttsbb_ctx *ctx, int32_t n_text, const 
                                           float *conf, int32_t *picked) {
     if (!ctx) return TTSBB_INVALID_ARG;
     const ttsbb_config &g = ctx->cfg;
+    ctx->pend_splits = 0;
     if (n_text < 0 || n_frames <= 0 || n_cb <= 0 || cb_vocab <= 0 || mask_id < 0 ||
         mask_id >= cb_vocab || n_unmask < 0 || (int64_t)n_unmask > (int64_t)n_cb * n_frames)
         return TTSBB_INVALID_ARG;
@@ -608,7 +635,6 @@ TTSBB_API ttsbb_status ttsbb_maskgit_pass(ttsbb_ctx *ctx, int32_t n_text, const 
     for (int l = 0; l < g.n_layers; ++l) {
         const ttsbb_layer &L = ctx->layers[l];
         const bool tapit = (l == ctx->tap_layer);
-        if (tapit) tap_dense(ctx, TTSBB_TAP_X_IN, ctx->x, DT_F32, S, g.hidden, g.hidden);
         qkv_projection(ctx, L, ctx->x, S, tapit);
 
         RopeKvArgs r = {};
@@ -658,6 +684,7 @@ TTSBB_API ttsbb_status ttsbb_maskgit_pass(ttsbb_ctx *ctx, int32_t n_text, const 
 
     // final norm + heads on the audio window only
     const int N = n_cb * cb_vocab;
+    flush_residual(ctx, ctx->x, S);
     {
         KScope k(ctx, TTSBB_K_RMSNORM);
         launch_rmsnorm(ctx->x + (size_t)n_text * g.hidden, g.hidden, n_frames, g.hidden, ctx->final_norm,

@@ -194,9 +194,13 @@ def test_decode_fp32_ragged_batch_random_gains():
         m.close()
 
 
-@pytest.mark.parametrize("lengths", [[3, 300, 31], [0, 1, 15, 16, 17, 33, 64, 100, 129, 250, 7]])
+@pytest.mark.parametrize("lengths", [[3, 300, 31], [0, 1, 15, 16, 17, 33, 64, 100, 129, 250, 7],
+                                     [(37 * i) % 211 for i in range(40)],
+                                     [(53 * i + 5) % 301 for i in range(64)]])
 def test_decode_bf16_ragged_with_head(lengths):
-    """bf16, 2 layers; batch 3 takes the weight-streaming path, batch 11 the MFMA path."""
+    """bf16, 2 layers.  Batch 3 takes the GEMV path; batches 11, 40 and 64 the skinny MFMA
+    path with one, three (padded to four) and four 16-row tiles, its split-K fixup (o and
+    down projections) and a ragged head width (3 x 37 columns)."""
     shape = CFG.Shape(n_layers=2)
     m = Model(shape, 2, True, seed=5, gains="random")
     try:
