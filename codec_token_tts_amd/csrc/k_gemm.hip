@@ -5,16 +5,15 @@
 //
 //   Y[M][N] = A[M][K] * W[N][K]^T, both operands K-contiguous, fp32 accumulation.
 //
-// Kernels:
-// * gemm_mfma: bf16 MFMA (v_mfma_f32_16x16x32_bf16) on BMxBNx64 block tiles staged
-//   through LDS (rows padded to 72 elements so the 16-byte fragment reads of a 16-row
-//   group hit distinct banks), 4 waves in a 2x2 arrangement.  Two register staging
-//   sets and two LDS buffers: the global loads of K tile k+2 are in flight while tile
-//   k is multiplied, so each load has about two iterations to arrive.  Tiles are
-//   ordered so that each XCD works on a contiguous N range (weight reuse in its L2).
-//   Optional split-K (grid z) writes fp32 partials that splitk_reduce sums in split
-//   order before the epilogue (deterministic; used when there are too few tiles, as
-//   for the batched decode step at M = 64).  Used when M > 8.
+// Kernels (routing in launch_gemm):
+// * gemm_lds (M > 64): 32x32x16 MFMA on 128x128 or 64x64 block tiles whose K tiles are
+//   fetched by LDS DMA into a ring of buffers several tiles ahead; XCD-aware tile order
+//   (each XCD works on a contiguous N range: weight reuse in its L2); split-K with
+//   deferred residual update for the hidden-width residual-add products.
+// * gemm_skinny (8 < M <= 64, the batched decode step): weight streaming through MFMA,
+//   every load issued up front, split-K with deferred residual update.
+// * gemm_mfma: 16x16x32 MFMA on register-staged LDS tiles with optional split-K and a
+//   reduce kernel: the fallback for M <= 64 shapes the skinny kernel does not take.
 // * gemv: weight streaming for M <= 8 and for fp32: each wave owns two output columns,
 //   streams their weight rows once with 16-byte loads and reuses them for all M rows.
 //
@@ -261,12 +260,10 @@ __global__ __launch_bounds__(256) void splitk_reduce(GemmArgs g, const float *pa
 
 
 // ------------------------------------------------------------------------------------
-// 32x32x16 MFMA tile GEMM (bf16), for M > 64 with wide N.  v_mfma_f32_32x32x16_bf16
-// runs at about twice the rate per flop of the 16x16x32 form on gfx950.  A lane of one
-// 32x32x16 product supplies A[row = l%32][k = 8*(l/32)..+7] and B[k = 8*(l/32)..+7]
-// [col = l%32] and receives rows 8*j + 4*(l/32) + i (j, i < 4) of column l%32 as
-// acc[4*j + i].  One register staging set per K tile, issued at the top of the
-// iteration and pinned there (sched_barrier) so it overlaps the tile's MFMAs.  The
+// Operand layout of the 32x32x16 MFMA kernels.  v_mfma_f32_32x32x16_bf16 runs at about
+// twice the rate per flop of the 16x16x32 form on gfx950.  A lane of one 32x32x16
+// product supplies A[row = l%32][k = 8*(l/32)..+7] and B[k = 8*(l/32)..+7][col = l%32]
+// and receives rows 8*j + 4*(l/32) + i (j, i < 4) of column l%32 as acc[4*j + i].  The
 // SwiGLU weights interleave in groups of 32 rows (gate, up) so a lane's pair of
 // accumulator tiles holds matching gate and up columns.
 // ------------------------------------------------------------------------------------
@@ -276,45 +273,103 @@ template <typename T>
 __device__ __forceinline__ const T *wrow32(const WSrc &w, int epi, int n, int K) {
     if (epi == EPI_SWIGLU) {
         const int pair = n >> 6, half = (n >> 5) & 1, r = n & 31;
-        const T *base = reinterpret_cast<const T *>(half ? w.p[1] : w.p[0]);
+        // integer select between the two (uniform) bases: a select of the two pointer
+        // arguments would be turned into a per-lane load of the argument array
+        const uintptr_t a0 = reinterpret_cast<uintptr_t>(w.p[0]), a1 = reinterpret_cast<uintptr_t>(w.p[1]);
+        const T *base = reinterpret_cast<const T *>(a0 + (half ? a1 - a0 : (uintptr_t)0));
         return base + (int64_t)(pair * 32 + r) * K;
     }
     return wrow<T>(w, EPI_STORE, n, K);
 }
 
-template <int N> struct Regs32 {
-    u32x4_t v[N];
-};
+// ------------------------------------------------------------------------------------
+// Multi-stage LDS-DMA GEMM (bf16, 32x32x16 MFMA) for M > 64.  With one 128x128 tile
+// per CU (the MaskGIT pass at S = 950 has 256 such tiles in its widest projection) the
+// global-load latency has to be covered by prefetch depth inside the block, not by
+// other blocks.  Operand tiles of 64 K-elements go straight from global memory into
+// LDS (global_load_lds_dwordx4: no staging registers, no LDS store instructions) into a
+// ring of STAGES buffers, STAGES-1 tiles ahead of the products.  A wave's DMA
+// instruction fills 1 KB of LDS in lane order (8 rows x 8 16-byte chunks); the lane ->
+// global chunk assignment applies the XOR swizzle chunk ^ (row % 8), so the 16-byte
+// fragment reads of 8 consecutive rows hit distinct banks.  Each wave waits only for
+// its own DMA of the tile it is about to read (vmcnt), then the block barrier makes
+// every wave's part visible; a buffer is refilled only after the barrier that follows
+// its last use.  Prefetches past the last tile are not issued; the waits count that.
+// ------------------------------------------------------------------------------------
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    // vmcnt[3:0] | expcnt (7: no wait) | lgkmcnt (15: no wait) | vmcnt[5:4]
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
 
-template <int BM, int BN, int EPI>
-__global__ __launch_bounds__(256) void gemm32(GemmArgs g) {
-    constexpr int LD = BK + 8, CPR = BK / 8;
+__device__ __forceinline__ void dma16(const bf16_t *src, bf16_t *lds_wave_dst) {
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(src),
+                                     (__attribute__((address_space(3))) void *)(lds_wave_dst), 16, 0,
+                                     0);
+}
+
+// DMA of K tile kt of both operands into one ring buffer (st).
+template <int BM, int AI, int BI>
+__device__ __forceinline__ void lds_issue(const bf16_t *const (&asrc)[AI], const bf16_t *const (&bsrc)[BI],
+                                          bf16_t *st, int wave, int kt) {
+#pragma unroll
+    for (int c = 0; c < AI; ++c) dma16(asrc[c] + kt * 64, st + (wave * AI + c) * 512);
+#pragma unroll
+    for (int c = 0; c < BI; ++c) dma16(bsrc[c] + kt * 64, st + BM * 64 + (wave * BI + c) * 512);
+}
+
+// 32x32x16 operand fragments of one K step from the swizzled tiles: row (i*32 + lane%32)
+// of the wave's A (B) rows, physical chunk ph (the caller's swizzled K chunk).
+template <int TM, int TN>
+__device__ __forceinline__ void lds_frags(const bf16_t *sa, const bf16_t *sb, int ph, bf16x8_t (&af)[TM],
+                                          bf16x8_t (&bfr)[TN]) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const bf16x8_t *>(sa + i * 32 * 64 + ph);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) bfr[j] = *reinterpret_cast<const bf16x8_t *>(sb + j * 32 * 64 + ph);
+}
+
+template <int BM, int BN, int STAGES, int EPI>
+__global__ __launch_bounds__(256) void gemm_lds(GemmArgs g, int k_split) {
     constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
-    constexpr int ACH = BM * CPR / 256, BCH = BN * CPR / 256;
-    static_assert(TM >= 1 && TN >= 1 && ACH >= 1 && BCH >= 1, "tile too small");
+    constexpr int AI = BM / 32, BI = BN / 32;  // DMA instructions per wave per stage
+    constexpr int LPS = AI + BI;               // vector-memory ops per wave per stage
+    constexpr int TILE = (BM + BN) * 64;       // elements per stage
+    static_assert(TM >= 1 && TN >= 1 && AI >= 1 && BI >= 1, "tile too small");
     static_assert(EPI != EPI_SWIGLU || TN % 2 == 0, "swiglu needs gate/up tile pairs");
-    __shared__ __attribute__((aligned(16))) bf16_t sA[2][BM * LD];
-    __shared__ __attribute__((aligned(16))) bf16_t sB[2][BN * LD];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+    static_assert(STAGES >= 2 && STAGES <= 4, "stages");
+    __shared__ __attribute__((aligned(1024))) bf16_t smem[STAGES * TILE];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
     const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
     const int t = xcd_tile(blockIdx.x, tiles_m * tiles_n);
     const int m0 = (t % tiles_m) * BM, n0 = (t / tiles_m) * BN;
+    const int k_begin = blockIdx.z * k_split;
+    const int KT = min(k_split, g.K - k_begin) / 64;
+
+    // Lane sources: instruction c of this wave covers tile rows (wave*I + c)*8 .. +7;
+    // lane i lands in LDS chunk i of that 1 KB, i.e. row +i/8, physical chunk i%8, and
+    // fetches logical chunk (i%8) ^ (i/8) of its row.
+    const int lrow = lane >> 3, lchunk = (lane & 7) ^ (lane >> 3);
     const bf16_t *A = reinterpret_cast<const bf16_t *>(g.A);
-    const bf16_t *ap[ACH];
-    const bf16_t *bp[BCH];
-    int ao[ACH], bo[BCH];
+    const bf16_t *asrc[AI];
+    const bf16_t *bsrc[BI];
 #pragma unroll
-    for (int c = 0; c < ACH; ++c) {
-        const int ch = tid + 256 * c, r = ch / CPR, kc = (ch % CPR) * 8;
-        ap[c] = A + (int64_t)min(m0 + r, g.M - 1) * g.lda + kc;  // rows past M feed unstored rows
-        ao[c] = r * LD + kc;
+    for (int c = 0; c < AI; ++c) {
+        const int r = (wave * AI + c) * 8 + lrow;
+        asrc[c] = A + (int64_t)min(m0 + r, g.M - 1) * g.lda + k_begin + lchunk * 8;  // rows past M: unstored
     }
 #pragma unroll
-    for (int c = 0; c < BCH; ++c) {
-        const int ch = tid + 256 * c, r = ch / CPR, kc = (ch % CPR) * 8;
-        bp[c] = wrow32<bf16_t>(g.w, g.epi, min(n0 + r, g.N - 1), g.K) + kc;
-        bo[c] = r * LD + kc;
+    for (int c = 0; c < BI; ++c) {
+        const int r = (wave * BI + c) * 8 + lrow;
+        // split partials come only from residual-add products: plain row order
+        bsrc[c] = wrow32<bf16_t>(g.w, EPI == EPI_SWIGLU ? EPI_SWIGLU : EPI_STORE, min(n0 + r, g.N - 1), g.K) +
+                  k_begin + lchunk * 8;
     }
+
     f32x16_t acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -322,50 +377,40 @@ __global__ __launch_bounds__(256) void gemm32(GemmArgs g) {
         for (int j = 0; j < TN; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-    const int KT = g.K / BK;
-    const int fr = lane & 31, fk = (lane >> 5) * 8;
-    Regs32<ACH> ra;
-    Regs32<BCH> rb;
+
 #pragma unroll
-    for (int c = 0; c < ACH; ++c) ra.v[c] = *reinterpret_cast<const u32x4_t *>(ap[c]);
-#pragma unroll
-    for (int c = 0; c < BCH; ++c) rb.v[c] = *reinterpret_cast<const u32x4_t *>(bp[c]);
-#pragma unroll
-    for (int c = 0; c < ACH; ++c) *reinterpret_cast<u32x4_t *>(&sA[0][ao[c]]) = ra.v[c];
-#pragma unroll
-    for (int c = 0; c < BCH; ++c) *reinterpret_cast<u32x4_t *>(&sB[0][bo[c]]) = rb.v[c];
-    __syncthreads();
+    for (int s = 0; s < STAGES - 1; ++s)
+        if (s < KT) lds_issue<BM, AI, BI>(asrc, bsrc, smem + s * TILE, wave, s);
+
+    const int fr = lane & 31, fh = lane >> 5, sw = lane & 7;
     for (int kt = 0; kt < KT; ++kt) {
-        const int buf = kt & 1;
-        const int kn = min(kt + 1, KT - 1) * BK;  // last iteration re-reads its own tile, unused
+        // this wave's DMA of tile kt is done once at most (tiles issued after it) x LPS
+        // operations are outstanding
+        const int after = min(STAGES - 2, KT - 1 - kt);
+        if (after >= 2) wait_vmcnt<2 * LPS>();
+        else if (after == 1) wait_vmcnt<LPS>();
+        else wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        if (kt + STAGES - 1 < KT)  // refills the buffer of tile kt-1
+            lds_issue<BM, AI, BI>(asrc, bsrc, smem + ((kt + STAGES - 1) % STAGES) * TILE, wave, kt + STAGES - 1);
+
+        const bf16_t *sa = smem + (kt % STAGES) * TILE + (wm * WM) * 64 + fr * 64;
+        const bf16_t *sb = smem + (kt % STAGES) * TILE + BM * 64 + (wn * WN) * 64 + fr * 64;
+        // fragments of step ks+1 are read while the products of step ks run
+        bf16x8_t af[2][TM], bfr[2][TN];
+        lds_frags<TM, TN>(sa, sb, ((0 + fh) ^ sw) * 8, af[0], bfr[0]);
 #pragma unroll
-        for (int c = 0; c < ACH; ++c) ra.v[c] = *reinterpret_cast<const u32x4_t *>(ap[c] + kn);
-#pragma unroll
-        for (int c = 0; c < BCH; ++c) rb.v[c] = *reinterpret_cast<const u32x4_t *>(bp[c] + kn);
-        __builtin_amdgcn_sched_barrier(0);
-        const bf16_t *sa = &sA[buf][wm * WM * LD], *sb = &sB[buf][wn * WN * LD];
-#pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
-            bf16x8_t af[TM], bfr[TN];
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-                af[i] = *reinterpret_cast<const bf16x8_t *>(&sa[(i * 32 + fr) * LD + ks * 16 + fk]);
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-                bfr[j] = *reinterpret_cast<const bf16x8_t *>(&sb[(j * 32 + fr) * LD + ks * 16 + fk]);
+        for (int ks = 0; ks < 4; ++ks) {
+            const int cur = ks & 1;
+            if (ks < 3) lds_frags<TM, TN>(sa, sb, ((ks * 2 + 2 + fh) ^ sw) * 8, af[cur ^ 1], bfr[cur ^ 1]);
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
                 for (int j = 0; j < TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfr[cur][j], acc[i][j], 0, 0, 0);
         }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int c = 0; c < ACH; ++c) *reinterpret_cast<u32x4_t *>(&sA[buf ^ 1][ao[c]]) = ra.v[c];
-#pragma unroll
-        for (int c = 0; c < BCH; ++c) *reinterpret_cast<u32x4_t *>(&sB[buf ^ 1][bo[c]]) = rb.v[c];
-        __syncthreads();
     }
+
     const int rb0 = m0 + wm * WM + (lane >> 5) * 4, cb0 = n0 + wn * WN + (lane & 31);
     if (EPI == EPI_SWIGLU) {
         bf16_t *C = reinterpret_cast<bf16_t *>(g.C);
@@ -385,6 +430,11 @@ __global__ __launch_bounds__(256) void gemm32(GemmArgs g) {
             }
     } else {
         float *C = reinterpret_cast<float *>(g.C);
+        int64_t ldc = g.ldc;
+        if (EPI == EPI_PARTIAL) {
+            C += (int64_t)blockIdx.z * g.M * g.N;
+            ldc = g.N;
+        }
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -395,7 +445,7 @@ __global__ __launch_bounds__(256) void gemm32(GemmArgs g) {
                 for (int r = 0; r < 16; ++r) {
                     const int row = rb0 + i * 32 + (r >> 2) * 8 + (r & 3);
                     if (row >= g.M) continue;
-                    float *p = C + (int64_t)row * g.ldc + col;
+                    float *p = C + (int64_t)row * ldc + col;
                     if (EPI == EPI_ADD) *p += acc[i][j][r];
                     else *p = acc[i][j][r];
                 }
@@ -403,17 +453,35 @@ __global__ __launch_bounds__(256) void gemm32(GemmArgs g) {
     }
 }
 
-template <int BM, int BN>
-static void launch_gemm32(const GemmArgs &g, hipStream_t s) {
+// Launch of the LDS-DMA GEMM; splits > 1 writes partials [splits][M][N] into part and
+// returns splits (EPI_ADD only: the caller adds them), else returns 0.
+template <int BM, int BN, int STAGES>
+static int launch_gemm_lds(const GemmArgs &g, int splits, float *part, hipStream_t s) {
     const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
+    const int kt = g.K / 64;
+    const int k_split = ((kt + splits - 1) / splits) * 64;
+    splits = (g.K + k_split - 1) / k_split;
+    const dim3 grid(tiles, 1, splits);
+    if (splits > 1) {
+        GemmArgs gp = g;
+        gp.C = part;
+        gp.ldc = g.N;
+        hipLaunchKernelGGL((gemm_lds<BM, BN, STAGES, EPI_PARTIAL>), grid, dim3(256), 0, s, gp, k_split);
+        return splits;
+    }
     switch (g.epi) {
-        case EPI_STORE: hipLaunchKernelGGL((gemm32<BM, BN, EPI_STORE>), dim3(tiles), dim3(256), 0, s, g); break;
-        case EPI_ADD: hipLaunchKernelGGL((gemm32<BM, BN, EPI_ADD>), dim3(tiles), dim3(256), 0, s, g); break;
+        case EPI_STORE:
+            hipLaunchKernelGGL((gemm_lds<BM, BN, STAGES, EPI_STORE>), grid, dim3(256), 0, s, g, k_split);
+            break;
+        case EPI_ADD:
+            hipLaunchKernelGGL((gemm_lds<BM, BN, STAGES, EPI_ADD>), grid, dim3(256), 0, s, g, k_split);
+            break;
         default:
             if constexpr ((BN / 2 / 32) % 2 == 0)
-                hipLaunchKernelGGL((gemm32<BM, BN, EPI_SWIGLU>), dim3(tiles), dim3(256), 0, s, g);
+                hipLaunchKernelGGL((gemm_lds<BM, BN, STAGES, EPI_SWIGLU>), grid, dim3(256), 0, s, g, k_split);
             break;
     }
+    return 0;
 }
 
 // ------------------------------------------------------------------------------------
@@ -761,13 +829,22 @@ int launch_gemm(const GemmArgs &g, DType dt, float *part, int64_t part_cap, hipS
         const int pending = launch_skinny(g, part, part_cap, s);
         if (pending >= 0) return pending;
     }
-    // Tile choice from measured sweeps on MI355X at the backbone's shapes.
-    if (g.M > 64 && g.N > 1024) {
+    // M > 64 (the MaskGIT pass, prefill-sized products): the LDS-DMA kernel.  Tile
+    // choice from measured sweeps on MI355X at the backbone's shapes: 128x128 tiles with
+    // a two-stage ring (64 KB of LDS: two blocks fit on a CU) when there are >= 128 of
+    // them; otherwise 64x64 tiles, and a residual-add product is split over K (partials
+    // deferred to the next RMSNorm) until there are >= 256 blocks.
+    if (g.M > 64 && g.K % 64 == 0) {
         const int t128 = ((g.M + 127) / 128) * ((g.N + 127) / 128);
-        if (t128 >= 200) launch_gemm32<128, 128>(g, s);
-        else if (g.epi == EPI_SWIGLU) launch_gemm32<64, 128>(g, s);
-        else launch_gemm32<64, 64>(g, s);
-        return 0;
+        if (t128 >= 128) return launch_gemm_lds<128, 128, 2>(g, 1, part, s);
+        if (g.epi == EPI_SWIGLU) return launch_gemm_lds<64, 128, 4>(g, 1, part, s);
+        const int t64 = ((g.M + 63) / 64) * ((g.N + 63) / 64);
+        int splits = 1;
+        if (g.epi == EPI_ADD)
+            while (t64 * splits < 256 && g.K / 64 >= 8 * splits && splits < 4 &&
+                   (int64_t)(splits * 2) * g.M * g.N <= part_cap)
+                splits *= 2;
+        return launch_gemm_lds<64, 64, 4>(g, splits, part, s);
     }
     // Small M or N = hidden: 32x64 tiles of the 16x16x32 kernel (more blocks in flight),
     // split over K only when there are few tiles.
