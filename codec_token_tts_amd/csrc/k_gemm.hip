@@ -48,6 +48,7 @@ __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)
 constexpr int BK = 64;
 constexpr int LDK = BK + 8;
 constexpr int EPI_PARTIAL = 3;  // fp32 partial sums of one K split: C + z * M * N
+constexpr int EPI_QKV = 4;      // fused per-head RMSNorm + RoPE + dense q / K / V^T layout
 
 // Tile order: block ids are dealt round-robin to the 8 XCDs, so block b runs on XCD
 // b % 8.  Tiles are renumbered so that each XCD receives a contiguous run of the
@@ -330,8 +331,104 @@ __device__ __forceinline__ void lds_frags(const bf16_t *sa, const bf16_t *sb, in
     for (int j = 0; j < TN; ++j) bfr[j] = *reinterpret_cast<const bf16x8_t *>(sb + j * 32 * 64 + ph);
 }
 
+// Fused epilogue of the full-sequence q/k/v projection (one 128 x 128 tile = 128
+// tokens x one head of the qkv output; block of 4 waves in 2 x 2, wave tile 64 x 64).
+// The fp32 tile goes through LDS in two halves of 64 tokens (row stride 132 floats);
+// for a q or k head each token's 128 values get the per-head RMSNorm (four threads per
+// token, 16 RoPE pairs each, sum of squares over the quad) and the half-rotate RoPE at
+// position = token index, then go out as bf16 q [S][H*128] or K [Hkv][s_pad][128];
+// a v head goes out transposed, V^T [Hkv][128][s_pad], 8 tokens per 16-byte store.
+template <int TM, int TN>
+__device__ __forceinline__ void qkv_dense_epilogue(const f32x16_t (&acc)[TM][TN], float *tile, int m0, int n0,
+                                                   int M, const RopeKvArgs &rk) {
+    constexpr int LDT = 132;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int head = n0 / 128;
+    const bool is_v = head >= rk.H + rk.Hkv;
+    for (int half = 0; half < 2; ++half) {
+        __syncthreads();  // the previous use of the LDS (ring buffers / first half) is over
+        if (wm == half) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int row = i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                        tile[row * LDT + wn * 64 + j * 32 + (lane & 31)] = acc[i][j][r];
+                    }
+        }
+        __syncthreads();
+        const int t0 = m0 + half * 64;
+        if (!is_v) {
+            const int row = tid >> 2, q4 = tid & 3, m = t0 + row;
+            const float *x = tile + row * LDT + q4 * 16;
+            float lo[16], hi[16];
+            float ss = 0.f;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                lo[e] = x[e];
+                hi[e] = x[64 + e];
+                ss += lo[e] * lo[e] + hi[e] * hi[e];
+            }
+            ss = group_sum<4>(ss);
+            const float inv = 1.0f / sqrtf(ss / 128.0f + rk.eps);
+            const bool is_q = head < rk.H;
+            const float *gain = is_q ? rk.q_gain : rk.k_gain;
+            const float2 *cs = rk.rope + (int64_t)min(m, rk.max_pos - 1) * 64 + q4 * 16;
+            uint32_t wlo[8], whi[8];
+#pragma unroll
+            for (int e = 0; e < 16; e += 2) {
+                float o[2][2];
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int d = q4 * 16 + e + u;
+                    const float x0 = lo[e + u] * inv * gain[d], x1 = hi[e + u] * inv * gain[d + 64];
+                    const float2 c = cs[e + u];
+                    o[0][u] = x0 * c.x - x1 * c.y;
+                    o[1][u] = x1 * c.x + x0 * c.y;
+                }
+                wlo[e / 2] = (uint32_t)f32_to_bf16(o[0][0]) | ((uint32_t)f32_to_bf16(o[0][1]) << 16);
+                whi[e / 2] = (uint32_t)f32_to_bf16(o[1][0]) | ((uint32_t)f32_to_bf16(o[1][1]) << 16);
+            }
+            if (m < M) {
+                bf16_t *dst = is_q ? reinterpret_cast<bf16_t *>(rk.q_out) + ((int64_t)m * rk.H + head) * 128
+                                   : rk.kbuf + ((int64_t)(head - rk.H) * rk.s_pad + m) * 128;
+                u32x4_t *d0 = reinterpret_cast<u32x4_t *>(dst + q4 * 16);
+                u32x4_t *d1 = reinterpret_cast<u32x4_t *>(dst + 64 + q4 * 16);
+                d0[0] = u32x4_t{wlo[0], wlo[1], wlo[2], wlo[3]};
+                d0[1] = u32x4_t{wlo[4], wlo[5], wlo[6], wlo[7]};
+                d1[0] = u32x4_t{whi[0], whi[1], whi[2], whi[3]};
+                d1[1] = u32x4_t{whi[4], whi[5], whi[6], whi[7]};
+            }
+        } else {
+            bf16_t *vt = rk.vtbuf + (int64_t)(head - rk.H - rk.Hkv) * 128 * rk.s_pad;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int item = tid + 256 * u, d = item & 127, sg = item >> 7;  // 8 groups of 8 tokens
+                const int m = t0 + sg * 8;
+                uint32_t w[4];
+#pragma unroll
+                for (int e = 0; e < 8; e += 2)
+                    w[e / 2] = (uint32_t)f32_to_bf16(tile[(sg * 8 + e) * LDT + d]) |
+                               ((uint32_t)f32_to_bf16(tile[(sg * 8 + e + 1) * LDT + d]) << 16);
+                bf16_t *dst = vt + (int64_t)d * rk.s_pad + m;
+                if (m + 8 <= M) {
+                    *reinterpret_cast<u32x4_t *>(dst) = u32x4_t{w[0], w[1], w[2], w[3]};
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (m + e < M) dst[e] = (bf16_t)(w[e / 2] >> (16 * (e & 1)));
+                }
+            }
+        }
+    }
+}
+
 template <int BM, int BN, int STAGES, int EPI>
-__global__ __launch_bounds__(256) void gemm_lds(GemmArgs g, int k_split) {
+__global__ __launch_bounds__(256) void gemm_lds(GemmArgs g, int k_split, RopeKvArgs rk) {
     constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
     constexpr int AI = BM / 32, BI = BN / 32;  // DMA instructions per wave per stage
     constexpr int LPS = AI + BI;               // vector-memory ops per wave per stage
@@ -411,6 +508,11 @@ __global__ __launch_bounds__(256) void gemm_lds(GemmArgs g, int k_split) {
         }
     }
 
+    if constexpr (EPI == EPI_QKV) {
+        static_assert(BM == 128 && BN == 128, "one tile = 128 tokens x one head");
+        qkv_dense_epilogue<TM, TN>(acc, reinterpret_cast<float *>(smem), m0, n0, g.M, rk);
+        return;
+    }
     const int rb0 = m0 + wm * WM + (lane >> 5) * 4, cb0 = n0 + wn * WN + (lane & 31);
     if (EPI == EPI_SWIGLU) {
         bf16_t *C = reinterpret_cast<bf16_t *>(g.C);
@@ -466,19 +568,20 @@ static int launch_gemm_lds(const GemmArgs &g, int splits, float *part, hipStream
         GemmArgs gp = g;
         gp.C = part;
         gp.ldc = g.N;
-        hipLaunchKernelGGL((gemm_lds<BM, BN, STAGES, EPI_PARTIAL>), grid, dim3(256), 0, s, gp, k_split);
+        hipLaunchKernelGGL((gemm_lds<BM, BN, STAGES, EPI_PARTIAL>), grid, dim3(256), 0, s, gp, k_split, RopeKvArgs{});
         return splits;
     }
     switch (g.epi) {
         case EPI_STORE:
-            hipLaunchKernelGGL((gemm_lds<BM, BN, STAGES, EPI_STORE>), grid, dim3(256), 0, s, g, k_split);
+            hipLaunchKernelGGL((gemm_lds<BM, BN, STAGES, EPI_STORE>), grid, dim3(256), 0, s, g, k_split, RopeKvArgs{});
             break;
         case EPI_ADD:
-            hipLaunchKernelGGL((gemm_lds<BM, BN, STAGES, EPI_ADD>), grid, dim3(256), 0, s, g, k_split);
+            hipLaunchKernelGGL((gemm_lds<BM, BN, STAGES, EPI_ADD>), grid, dim3(256), 0, s, g, k_split, RopeKvArgs{});
             break;
         default:
             if constexpr ((BN / 2 / 32) % 2 == 0)
-                hipLaunchKernelGGL((gemm_lds<BM, BN, STAGES, EPI_SWIGLU>), grid, dim3(256), 0, s, g, k_split);
+                hipLaunchKernelGGL((gemm_lds<BM, BN, STAGES, EPI_SWIGLU>), grid, dim3(256), 0, s, g, k_split,
+                                   RopeKvArgs{});
             break;
     }
     return 0;
@@ -806,6 +909,14 @@ static int choose_splits(const GemmArgs &g, int tiles, int64_t part_cap) {
            (int64_t)(splits * 2) * g.M * g.N <= part_cap)
         splits *= 2;
     return splits;
+}
+
+bool launch_qkv_dense(const GemmArgs &g, const RopeKvArgs &rk, hipStream_t s) {
+    // one tile per (128 tokens, head): needs M > 64 (the LDS-DMA kernel), 128-wide heads
+    if (g.M <= 64 || g.K % 64 != 0 || g.N != (rk.H + 2 * rk.Hkv) * 128 || g.epi != EPI_STORE) return false;
+    const int tiles = ((g.M + 127) / 128) * (g.N / 128);
+    hipLaunchKernelGGL((gemm_lds<128, 128, 2, EPI_QKV>), dim3(tiles), dim3(256), 0, s, g, g.K, rk);
+    return true;
 }
 
 int launch_gemm(const GemmArgs &g, DType dt, float *part, int64_t part_cap, hipStream_t s) {

@@ -88,6 +88,10 @@ struct RopeKvArgs {
     int *flag;
 };
 void launch_rope_kv(const RopeKvArgs &a, DType kv_dt, hipStream_t s);
+// Dense mode fused into the q/k/v projection (g: EPI_STORE product of N = (H + 2 Hkv) *
+// 128 columns): writes q_out / kbuf / vtbuf directly, qkv is not written.  Returns
+// false (nothing launched) when the shape is not taken by the fused kernel (M <= 64).
+bool launch_qkv_dense(const GemmArgs &g, const RopeKvArgs &rk, hipStream_t s);
 
 // ---- K5: split-sequence decode attention over the paged pool -----------------------
 struct DecodeAttnArgs {

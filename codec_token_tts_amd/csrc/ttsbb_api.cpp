@@ -349,7 +349,11 @@ void add_projection(ttsbb_ctx *c, const GemmArgs &a) {
     c->pend_rows = a.M;
 }
 
-void qkv_projection(ttsbb_ctx *c, const ttsbb_layer &L, float *x, int M, bool tapit) {
+// RMSNorm + q/k/v projection.  With `dense` (the MaskGIT pass), the per-head norm, RoPE
+// and the dense q / K / V^T layout are fused into the product when the shape allows;
+// returns true when that happened (qkv is then not written).
+bool qkv_projection(ttsbb_ctx *c, const ttsbb_layer &L, float *x, int M, bool tapit,
+                    const RopeKvArgs *dense = nullptr) {
     const ttsbb_config &g = c->cfg;
     if (tapit) {
         flush_residual(c, x, M);
@@ -373,14 +377,17 @@ void qkv_projection(ttsbb_ctx *c, const ttsbb_layer &L, float *x, int M, bool ta
     a.C = c->qkv;
     a.ldc = c->qkv_w;
     a.epi = EPI_STORE;
+    bool fused = false;
     {
         KScope k(c, TTSBB_K_GEMM_QKV);
-        launch_gemm(a, c->dt, c->gpart, c->gpart_cap, c->stream);
+        if (dense) fused = launch_qkv_dense(a, *dense, c->stream);
+        if (!fused) launch_gemm(a, c->dt, c->gpart, c->gpart_cap, c->stream);
     }
     if (tapit) {
         tap_dense(c, TTSBB_TAP_H_ATTN, c->h, c->dt, M, g.hidden, g.hidden);
-        tap_dense(c, TTSBB_TAP_QKV, c->qkv, DT_F32, M, c->qkv_w, c->qkv_w);
+        if (!fused) tap_dense(c, TTSBB_TAP_QKV, c->qkv, DT_F32, M, c->qkv_w, c->qkv_w);
     }
+    return fused;
 }
 
 void post_attention(ttsbb_ctx *c, const ttsbb_layer &L, float *x, int M, bool tapit) {
@@ -595,7 +602,7 @@ TTSBB_API ttsbb_status ttsbb_maskgit_pass(ttsbb_ctx *ctx, int32_t n_text, const 
     if (n_text < 0 || n_frames <= 0 || n_cb <= 0 || cb_vocab <= 0 || mask_id < 0 ||
         mask_id >= cb_vocab || n_unmask < 0 || (int64_t)n_unmask > (int64_t)n_cb * n_frames)
         return TTSBB_INVALID_ARG;
-    if ((int64_t)n_text + n_frames > g.max_rows) return TTSBB_INVALID_ARG;
+    if ((int64_t)n_text + n_frames > g.max_rows || (int64_t)n_text + n_frames > g.max_pos) return TTSBB_INVALID_ARG;
     if ((int64_t)n_cb * cb_vocab > g.max_head_cols) return TTSBB_INVALID_ARG;
     if ((int64_t)n_cb * n_frames > ctx->rank_cap) return TTSBB_INVALID_ARG;
     if (n_text > 0 && (!text_ids || !text_table || text_vocab <= 0)) return TTSBB_INVALID_ARG;
@@ -635,8 +642,6 @@ TTSBB_API ttsbb_status ttsbb_maskgit_pass(ttsbb_ctx *ctx, int32_t n_text, const 
     for (int l = 0; l < g.n_layers; ++l) {
         const ttsbb_layer &L = ctx->layers[l];
         const bool tapit = (l == ctx->tap_layer);
-        qkv_projection(ctx, L, ctx->x, S, tapit);
-
         RopeKvArgs r = {};
         r.qkv = ctx->qkv;
         r.M = S;
@@ -653,7 +658,7 @@ TTSBB_API ttsbb_status ttsbb_maskgit_pass(ttsbb_ctx *ctx, int32_t n_text, const 
         r.vtbuf = ctx->vtbuf;
         r.s_pad = s_pad;
         r.flag = ctx->flag;
-        {
+        if (!qkv_projection(ctx, L, ctx->x, S, tapit, &r)) {
             KScope k(ctx, TTSBB_K_ROPE_KV);
             launch_rope_kv(r, DT_BF16, ctx->stream);
         }
