@@ -1,22 +1,29 @@
 // K6: bidirectional attention of the MaskGIT pass (OmniVoice ARCHITECTURE, "MaskGIT
 // decoder": every step is a full prefill with fully bidirectional attention, no KV
-// cache across steps).  Flash-style: keys stream through LDS in blocks of 64 with an
+// cache across steps).  Flash-style: keys stream through LDS in blocks of 32 with an
 // online softmax, so the S x S score matrix never exists.
 //
-// Both products run on bf16 MFMA (v_mfma_f32_16x16x32_bf16) in transposed form so
-// that a lane's accumulators always belong to one query (column lane % 16):
-//   S^T (16 keys x 16 queries) = K (16 x 128) * Q^T (128 x 16)
-//   O^T (16 dims x 16 queries) = V^T (16 x 64) * P^T (64 x 16)
-// The softmax statistics of a query are then lane-local up to a reduction over the 4
-// lanes sharing it, and P^T feeds the second product straight from registers: the
-// contraction runs over the 32 keys of a step in the order the lane already holds
-// them (keys 4g..4g+3 and 16+4g..16+4g+3 of the step for lane group g), with V^T read
-// from LDS in that same key order.  V is stored transposed by K4 ([Hkv][128][s_pad]),
-// so each V^T row segment is a contiguous LDS read.
+// Both products run on v_mfma_f32_32x32x16_bf16 (on gfx950 about 1.75x the flop rate of
+// the 16x16x32 form) in transposed form, so that a lane's accumulators always belong to
+// one query (column lane % 32):
+//   S^T (32 keys x 32 queries) = K (32 x 128) * Q^T (128 x 32)        8 products
+//   O^T (32 dims x 32 queries) = V^T (32 x 32) * P^T (32 x 32)         2 products / tile
+// Lane l holds S^T rows 8j + 4(l/32) + i (j, i < 4) of query l%32, so the softmax
+// statistics of a query live in lanes l and l^32.  P^T feeds the second product
+// straight from registers: its 16-key contraction slots (h = l/32, i < 8) are mapped
+// to keys 4h + i (i < 4) and 8 + 4h + (i - 4), the keys the lane already holds, and
+// the V^T operand is read from LDS in that same key order (two 8-byte reads).  V is
+// stored transposed ([Hkv][128][s_pad]), so those reads are contiguous.
 //
-// Block = 4 waves = (4/GROUP) query tiles of 16 x GROUP query heads sharing one KV
-// head, so the K and V tiles in LDS serve every head of the GQA group.  Scores are
-// pre-scaled by log2(e)/sqrt(128) and exponentiated with exp2.
+// Block = 8 waves = 4 key quarters x 2 waves.  The two waves of a quarter are the two
+// query heads of a GQA group over the same 32 queries (or, without GQA, two query
+// tiles of one head): they share the quarter's double-buffered K / V^T tiles in LDS.
+// Every quarter runs the same number of iterations (a quarter past its last block
+// processes masked copies) so that the block barriers match; at the end quarters 1-3
+// hand their (max, sum, O^T) to quarter 0 through LDS, which merges the four
+// online-softmax states in quarter order and stores.  Scores are scaled by
+// log2(e)/sqrt(128) inside the exponent (one FMA) and exponentiated with v_exp_f32;
+// the running reference max is raised lazily (see the loop).
 #include <math.h>
 
 #include "common.h"
@@ -24,152 +31,223 @@
 
 namespace ttsbb {
 
-constexpr int FB = 64;          // keys per block
-constexpr int LDKF = 128 + 8;   // K tile row stride (elements)
-constexpr int LDVF = FB + 8;    // V^T tile row stride (elements)
+constexpr int FB = 32;         // keys per block
+constexpr int LDKF = 128 + 8;  // K tile row stride (elements)
+constexpr int LDVF = FB + 8;   // V^T tile row stride (elements)
+constexpr int KTILE = FB * LDKF, VTILE = 128 * LDVF;
 
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+
+// Global -> register staging of one 32-key block of K (8 KB) and V^T (8 KB) by the 128
+// threads of a quarter.
+__device__ __forceinline__ void flash_gload(const bf16_t *kg, const bf16_t *vg, int s_pad, int kb0, int qtid,
+                                            u32x4_t (&rk)[4], u32x4_t (&rv)[4]) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int ch = qtid + 128 * c;
+        rk[c] = *reinterpret_cast<const u32x4_t *>(kg + (int64_t)(kb0 + (ch >> 4)) * 128 + (ch & 15) * 8);
+        rv[c] = *reinterpret_cast<const u32x4_t *>(vg + (int64_t)(ch >> 2) * s_pad + kb0 + (ch & 3) * 8);
+    }
+}
+
+__device__ __forceinline__ void flash_sstore(bf16_t *sk, bf16_t *sv, int qtid, const u32x4_t (&rk)[4],
+                                             const u32x4_t (&rv)[4]) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int ch = qtid + 128 * c;
+        *reinterpret_cast<u32x4_t *>(&sk[(ch >> 4) * LDKF + (ch & 15) * 8]) = rk[c];
+        *reinterpret_cast<u32x4_t *>(&sv[(ch >> 2) * LDVF + (ch & 3) * 8]) = rv[c];
+    }
+}
 
 template <int GROUP>
-__global__ __launch_bounds__(256) void flash_kernel(FlashArgs a) {
-    constexpr int QT = 4 / GROUP;  // query tiles per block
-    __shared__ __attribute__((aligned(16))) bf16_t sK[2][FB * LDKF];
-    __shared__ __attribute__((aligned(16))) bf16_t sV[2][128 * LDVF];
+__global__ __launch_bounds__(512) void flash_kernel(FlashArgs a) {
+    // [quarter][buffer] K tiles, then V^T tiles; reused at the end for the hand-over of
+    // quarters 1-3 (one array, so the hand-over may span both parts)
+    __shared__ __attribute__((aligned(16))) bf16_t smem[8 * (KTILE + VTILE)];
+    bf16_t(*sK)[2][KTILE] = reinterpret_cast<bf16_t(*)[2][KTILE]>(smem);
+    bf16_t(*sV)[2][VTILE] = reinterpret_cast<bf16_t(*)[2][VTILE]>(smem + 8 * KTILE);
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int qt = wave / GROUP, jh = wave % GROUP;
-    const int hk = blockIdx.y;
-    const int head = hk * GROUP + jh;
-    const int q0 = blockIdx.x * 16 * QT + qt * 16;
-    const int fr = lane & 15, g = lane >> 4, fk = g * 8;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int qq = wave >> 1, u = wave & 1, qtid = tid & 127;
+    // blocks are dealt round-robin to the 8 XCDs (block b runs on XCD b % 8): taking the
+    // KV head from b % Hkv keeps each head's K / V^T (486 KB at S = 950) in one XCD's L2
+    const int hk = blockIdx.x % a.Hkv, qtile = blockIdx.x / a.Hkv;
+    const int head = GROUP == 2 ? hk * 2 + u : hk;
+    const int q0 = (GROUP == 2 ? qtile : qtile * 2 + u) * 32;
+    const int fq = lane & 31, h = lane >> 5;
     const int ldq = a.H * 128;
 
-    // Q^T operand: lane -> query q0 + fr, dims ks*32 + fk .. +7
-    bf16x8_t qf[4];
+    // Q^T operand: lane -> query q0 + fq, dims ks*16 + 8h .. +7
+    bf16x8_t qf[8];
     {
-        const int qi = q0 + fr;
+        const int qi = min(q0 + fq, a.S - 1);  // queries past S compute unused columns
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            if (qi < a.S)
-                qf[ks] = *reinterpret_cast<const bf16x8_t *>(a.q + (int64_t)qi * ldq + head * 128 + ks * 32 + fk);
-            else
-                qf[ks] = bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
-        }
+        for (int ks = 0; ks < 8; ++ks)
+            qf[ks] = *reinterpret_cast<const bf16x8_t *>(a.q + (int64_t)qi * ldq + head * 128 + ks * 16 + h * 8);
     }
 
     const bf16_t *kg = a.k + (int64_t)hk * a.s_pad * 128;
     const bf16_t *vg = a.vt + (int64_t)hk * 128 * a.s_pad;
-    u32x4_t rk[4], rv[4];
-    auto gload = [&](int kb0) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int ch = tid + 256 * c;
-            rk[c] = *reinterpret_cast<const u32x4_t *>(kg + (int64_t)(kb0 + (ch >> 4)) * 128 + (ch & 15) * 8);
-            rv[c] = *reinterpret_cast<const u32x4_t *>(vg + (int64_t)(ch >> 3) * a.s_pad + kb0 + (ch & 7) * 8);
-        }
-    };
-    auto sstore = [&](int buf) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int ch = tid + 256 * c;
-            *reinterpret_cast<u32x4_t *>(&sK[buf][(ch >> 4) * LDKF + (ch & 15) * 8]) = rk[c];
-            *reinterpret_cast<u32x4_t *>(&sV[buf][(ch >> 3) * LDVF + (ch & 7) * 8]) = rv[c];
-        }
-    };
+    const int NB = a.s_pad / FB, NBQ = (NB + 3) / 4;
+    const int kb_first = qq * NBQ, nb_mine = max(0, min(NBQ, NB - kb_first));
+    // iteration i works on block blk(i); past this quarter's blocks it re-reads a valid
+    // block and masks every key
+    auto blk = [&](int i) { return min(kb_first + max(0, min(i, nb_mine - 1)), NB - 1); };
+    bf16_t *sk0 = sK[qq][0], *sk1 = sK[qq][1], *sv0 = sV[qq][0], *sv1 = sV[qq][1];
 
-    f32x4_t o[8];
+    f32x16_t o[4];
 #pragma unroll
-    for (int d = 0; d < 8; ++d) o[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[d][r] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
 
-    const int NB = a.s_pad / FB;
-    gload(0);
-    sstore(0);
+    u32x4_t rk[4], rv[4];
+    flash_gload(kg, vg, a.s_pad, blk(0) * FB, qtid, rk, rv);
+    flash_sstore(sk0, sv0, qtid, rk, rv);
     __syncthreads();
-    for (int kb = 0; kb < NB; ++kb) {
-        const int buf = kb & 1;
-        gload(min(kb + 1, NB - 1) * FB);  // unconditional (clamped) so the waits stay counted
+    for (int i = 0; i < NBQ; ++i) {
+        const int buf = i & 1;
+        const bf16_t *sk = buf ? sk1 : sk0;
+        const bf16_t *sv = buf ? sv1 : sv0;
+        flash_gload(kg, vg, a.s_pad, blk(i + 1) * FB, qtid, rk, rv);  // unconditional (clamped)
+        // keep the prefetch at the top of the iteration: it has the whole block to arrive
+        __builtin_amdgcn_sched_barrier(0);
+        const bool valid = i < nb_mine;
+        const int kbase = blk(i) * FB;
 
-        f32x4_t s[4];
+        bf16x8_t kf[8];
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-            s[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int ks = 0; ks < 8; ++ks)
+            kf[ks] = *reinterpret_cast<const bf16x8_t *>(&sk[fq * LDKF + ks * 16 + h * 8]);
+        f32x16_t s;
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const bf16x8_t ka = *reinterpret_cast<const bf16x8_t *>(&sK[buf][(kt * 16 + fr) * LDKF + ks * 32 + fk]);
-                s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[ks], s[kt], 0, 0, 0);
+        for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], s, 0, 0, 0);
+        // V^T fragments are independent of the softmax: their reads overlap it
+        bf16x8_t vfr[4][2];
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const bf16_t *vrow = &sv[(dt * 32 + fq) * LDVF + kk * 16 + h * 4];
+                const bf16x4_t lo = *reinterpret_cast<const bf16x4_t *>(vrow);
+                const bf16x4_t hi = *reinterpret_cast<const bf16x4_t *>(vrow + 8);
+                vfr[dt][kk] = bf16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            }
+        // mask keys past S (and the blocks of a finished quarter): only partial blocks
+        if (!(valid && kbase + FB <= a.S)) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = kbase + (r >> 2) * 8 + h * 4 + (r & 3);
+                if (!(valid && key < a.S)) s[r] = -INFINITY;
             }
         }
-        // scale, mask keys past S, block max of this lane's query
-        float mx = -INFINITY;
+        float mx = s[0];
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE)) * a.scale_log2;  // scale > 0 commutes with max
+        // Lazy rescaling: the weights are taken relative to a reference max m_ref that is
+        // raised (and O, l rescaled) only when some query of the wave sees a score more
+        // than 2^8 above it, so a weight never exceeds 2^8 and most blocks skip the
+        // rescale.  The normalisation by l at the end cancels the reference.
+        if (__any(mx > m_run + 8.0f)) {
+            const float m_new = fmaxf(m_run, mx);
+            const float sc = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
+            m_run = m_new;
+            l_run *= sc;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int key = kb * FB + kt * 16 + g * 4 + r;
-                const float v = key < a.S ? s[kt][r] * a.scale_log2 : -INFINITY;
-                s[kt][r] = v;
-                mx = fmaxf(mx, v);
-            }
-        mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
-        const float m_new = fmaxf(m_run, mx);  // finite: every block holds a key < S
-        const float sc = exp2f(m_run - m_new);
-        m_run = m_new;
-        l_run *= sc;
-#pragma unroll
-        for (int d = 0; d < 8; ++d) o[d] *= sc;
+            for (int d = 0; d < 4; ++d) o[d] *= sc;
+        }
+        const float m_neg = m_run == -INFINITY ? 0.f : -m_run;  // nothing seen yet: all weights 0
 
+        // P^T operand of the 16-key chunk kk: slots i < 4 <- rows 8(2kk) + 4h + i,
+        // slots 4..7 <- rows 8(2kk+1) + 4h + i - 4, i.e. accumulator entries 8kk + i
         bf16x8_t pb[2];
 #pragma unroll
-        for (int ks2 = 0; ks2 < 2; ++ks2) {
+        for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float p = exp2f(s[2 * ks2 + h2][r] - m_new);
-                    l_run += p;
-                    pb[ks2][h2 * 4 + r] = (__bf16)p;
-                }
-        }
-#pragma unroll
-        for (int d = 0; d < 8; ++d) {
-#pragma unroll
-            for (int ks2 = 0; ks2 < 2; ++ks2) {
-                const bf16_t *vrow = &sV[buf][(d * 16 + fr) * LDVF + ks2 * 32 + g * 4];
-                const bf16x4_t lo = *reinterpret_cast<const bf16x4_t *>(vrow);
-                const bf16x4_t hi = *reinterpret_cast<const bf16x4_t *>(vrow + 16);
-                const bf16x8_t va = bf16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[ks2], o[d], 0, 0, 0);
+            for (int e = 0; e < 8; ++e) {
+                const float p = __builtin_amdgcn_exp2f(fmaf(s[8 * kk + e], a.scale_log2, m_neg));
+                l_run += p;
+                pb[kk][e] = (__bf16)p;
             }
-        }
-        if (kb + 1 < NB) sstore(buf ^ 1);
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[dt][kk], pb[kk], o[dt], 0, 0, 0);
+        if (i + 1 < NBQ) flash_sstore(buf ? sk0 : sk1, buf ? sv0 : sv1, qtid, rk, rv);
         __syncthreads();
     }
 
-    l_run += __shfl_xor(l_run, 16, WAVE);
+    // hand-over: quarters 1-3 -> quarter 0 through the (now idle) tiles; 66 values per
+    // lane, stored with a stride of 128 lanes (the two waves of a quarter side by side)
+    float *ex = reinterpret_cast<float *>(smem);
+    constexpr int EXS = 66 * 128;  // floats per quarter
+    static_assert(3 * EXS * 4 <= 8 * (KTILE + VTILE) * 2, "hand-over fits the tiles");
+    if (qq > 0) {
+        float *e = ex + (qq - 1) * EXS + u * 64 + lane;
+        e[0] = m_run;
+        e[128] = l_run;
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) e[(2 + d * 16 + r) * 128] = o[d][r];
+    }
+    __syncthreads();
+    if (qq > 0) return;
+    {
+        float mq[3], M = m_run;  // finite: quarter 0 always holds key 0 (the references merge
+                                 // like maxima: each state is exact relative to its own)
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            mq[k] = ex[k * EXS + u * 64 + lane];
+            M = fmaxf(M, mq[k]);
+        }
+        const float f0 = exp2f(m_run - M);
+        l_run *= f0;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) o[d] *= f0;
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            const float *e = ex + k * EXS + u * 64 + lane;
+            const float f = exp2f(mq[k] - M);  // an empty quarter (reference -inf) weighs 0
+            l_run += e[128] * f;
+#pragma unroll
+            for (int d = 0; d < 4; ++d)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[d][r] += e[(2 + d * 16 + r) * 128] * f;
+        }
+    }
+
     l_run += __shfl_xor(l_run, 32, WAVE);
     const float inv = 1.0f / l_run;
-    const int qi = q0 + fr;
+    const int qi = q0 + fq;
     if (qi < a.S) {
-        bf16_t *out = a.out + (int64_t)qi * ldq + head * 128 + g * 4;
+        bf16_t *out = a.out + (int64_t)qi * ldq + head * 128 + h * 4;
 #pragma unroll
-        for (int d = 0; d < 8; ++d) {
-            uint2 w;
-            w.x = (uint32_t)f32_to_bf16(o[d][0] * inv) | ((uint32_t)f32_to_bf16(o[d][1] * inv) << 16);
-            w.y = (uint32_t)f32_to_bf16(o[d][2] * inv) | ((uint32_t)f32_to_bf16(o[d][3] * inv) << 16);
-            *reinterpret_cast<uint2 *>(out + d * 16) = w;
-        }
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                uint2 w;
+                w.x = (uint32_t)f32_to_bf16(o[dt][4 * j] * inv) | ((uint32_t)f32_to_bf16(o[dt][4 * j + 1] * inv) << 16);
+                w.y = (uint32_t)f32_to_bf16(o[dt][4 * j + 2] * inv) | ((uint32_t)f32_to_bf16(o[dt][4 * j + 3] * inv) << 16);
+                *reinterpret_cast<uint2 *>(out + dt * 32 + j * 8) = w;
+            }
     }
 }
 
 void launch_flash_attn(const FlashArgs &a, hipStream_t s) {
     if (a.S <= 0) return;
     const int group = a.H / a.Hkv;
-    const int qpb = 16 * (4 / group);
-    dim3 grid((a.S + qpb - 1) / qpb, a.Hkv);
-    if (group == 2) hipLaunchKernelGGL(flash_kernel<2>, grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(flash_kernel<1>, grid, dim3(256), 0, s, a);
+    const int qpb = group == 2 ? 32 : 64;  // queries per block
+    const dim3 grid(((a.S + qpb - 1) / qpb) * a.Hkv);
+    if (group == 2) hipLaunchKernelGGL(flash_kernel<2>, grid, dim3(512), 0, s, a);
+    else hipLaunchKernelGGL(flash_kernel<1>, grid, dim3(512), 0, s, a);
 }
 
 }  // namespace ttsbb
