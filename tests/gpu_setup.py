@@ -114,7 +114,9 @@ def check_argmax_groups(gpu_choice: np.ndarray, gpu_logits: np.ndarray, ref_logi
     own = np.argmax(g, axis=-1)
     assert np.array_equal(own, ch), "choice is not the argmax of the GPU's own logits"
     fin = np.isfinite(r)
-    delta = np.max(np.where(fin, np.abs(g - r), 0.0), axis=-1)
+    diff = np.zeros_like(r)
+    diff[fin] = np.abs(g[fin] - r[fin])  # excluded classes are -inf on both sides
+    delta = np.max(diff, axis=-1)
     top2 = np.sort(r, axis=-1)[..., -2:]
     gap = top2[..., 1] - top2[..., 0]
     ref_arg = np.argmax(r, axis=-1)

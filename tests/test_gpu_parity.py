@@ -195,12 +195,14 @@ def test_decode_fp32_ragged_batch_random_gains():
 
 
 @pytest.mark.parametrize("lengths", [[3, 300, 31], [0, 1, 15, 16, 17, 33, 64, 100, 129, 250, 7],
+                                     [(29 * i) % 97 for i in range(9)], [(31 * i) % 160 for i in range(17)],
                                      [(37 * i) % 211 for i in range(40)],
                                      [(53 * i + 5) % 301 for i in range(64)]])
 def test_decode_bf16_ragged_with_head(lengths):
-    """bf16, 2 layers.  Batch 3 takes the GEMV path; batches 11, 40 and 64 the skinny MFMA
-    path with one, three (padded to four) and four 16-row tiles, its split-K fixup (o and
-    down projections) and a ragged head width (3 x 37 columns)."""
+    """bf16, 2 layers.  Batch 3 takes the GEMV path; batches 9, 11, 17, 40 and 64 the skinny
+    MFMA path with one, two, three (padded to four) and four 16-row tiles, its split-K
+    products with the residual update deferred to the next RMSNorm (o and down
+    projections) and a ragged head width (3 x 37 columns)."""
     shape = CFG.Shape(n_layers=2)
     m = Model(shape, 2, True, seed=5, gains="random")
     try:
@@ -294,10 +296,14 @@ def test_maskgit_zero_layers_head_and_selection():
         m.close()
 
 
-@pytest.mark.parametrize("n_text,n_frames,n_unmask", [(13, 57, 40), (0, 64, 150), (70, 3, 6)])
+@pytest.mark.parametrize("n_text,n_frames,n_unmask", [(13, 57, 40), (0, 64, 150), (70, 3, 6), (1, 64, 20),
+                                                    (77, 123, 60), (0, 129, 33)])
 def test_maskgit_two_layers(n_text, n_frames, n_unmask):
-    """bf16, 2 bidirectional layers, ragged sequence (several 64-key blocks and a tail),
-    heads whose width is not a tile multiple; n_unmask beyond the masked count -> -1."""
+    """bf16, 2 bidirectional layers, ragged sequence (several key blocks and a tail), heads
+    whose width is not a tile multiple; n_unmask beyond the masked count -> -1.  S = 64 runs
+    the skinny products and the separate RoPE / V^T kernels; S = 65, 70, 73, 129, 200 the
+    LDS-DMA products with the fused q|k|v epilogue (one or two 128-token tiles, a ragged
+    last tile), split residual products, and attention with empty key quarters (S <= 96)."""
     m = Model(CFG.Shape(n_layers=2), 2, True, seed=4, gains="random")
     try:
         n_cb, V, mask = 3, 33, 32
