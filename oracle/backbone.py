@@ -380,6 +380,13 @@ def apply_picks(codes_kt: np.ndarray, pred: np.ndarray, picked: np.ndarray) -> n
     return c.reshape(np.asarray(codes_kt).shape)
 
 
+def cfg_logits(cond: np.ndarray, uncond: np.ndarray, cfg_scale: float) -> np.ndarray:
+    """Classifier-free guidance on the logits, before the log-softmax:
+    c + s * (c - u).  [OV-MG] (CFG: log_softmax(c + cfg_scale * (c - u)))."""
+    c = as64(cond)
+    return c + float(cfg_scale) * (c - as64(uncond))
+
+
 def unmask_schedule(n_total: int, n_steps: int) -> List[int]:
     """How many positions each step unmasks.  [OV-MG] gives the form
     ceil(N * (t[i+1] - t[i])) over a time grid; the grid used here is the cosine
@@ -416,4 +423,37 @@ def maskgit_pass(text_ids, text_table, codes_kt, audio_table, audio_heads, layer
     new_codes = apply_picks(codes_kt, pred, picked)
     if record is not None:
         record.update(x=x, y=y, logits=logits, pred=pred, conf=conf, picked=picked)
+    return new_codes, pred, conf, picked
+
+
+def maskgit_pass_cfg(text_ids, text_table, codes_kt, n_target: int, audio_table, audio_heads,
+                     layers: List[Layer], final_norm, dims: Dims, cb_vocab: int, mask_id: int,
+                     layer_penalty: float, n_unmask: int, cfg_scale: float,
+                     record: Optional[Dict] = None):
+    """One MaskGIT step with classifier-free guidance.  [OV-MG]:
+    * the conditional prompt is the full sequence (text rows, then every audio frame,
+      the last n_target of which are the target window); its logits are read on the
+      window (the last n_target positions);
+    * the unconditional prompt is the target window's tokens alone (no text, no
+      reference frames), at positions 0..n_target-1; its logits are read on all of it;
+    * guided logits c + s (c - u), then the scoring, selection and token update of the
+      plain step, all restricted to the window.
+    codes_kt [K][n_frames] is updated in place on the window only; pred / conf are
+    [K][n_target] and picked indexes the flattened window (k * n_target + t)."""
+    codes_kt = np.asarray(codes_kt, dtype=np.int32)
+    n_cb, n_frames = codes_kt.shape
+    n_text = len(text_ids)
+    w0 = n_frames - n_target
+    window = codes_kt[:, w0:]
+    xc = backbone_full(hybrid_embed(text_ids, text_table, codes_kt, audio_table, cb_vocab), layers, dims)
+    _, lc = head_logits(xc[n_text + w0:], final_norm, audio_heads, dims.eps)
+    xu = backbone_full(codebook_embed(window.T, audio_table, cb_vocab), layers, dims)
+    _, lu = head_logits(xu, final_norm, audio_heads, dims.eps)
+    guided = cfg_logits(lc, lu, cfg_scale)
+    pred, conf, _ = maskgit_scores(guided, window, n_cb, cb_vocab, mask_id, layer_penalty)
+    picked = select_top(conf.reshape(-1), n_unmask)
+    new_codes = codes_kt.copy()
+    new_codes[:, w0:] = apply_picks(window, pred, picked)
+    if record is not None:
+        record.update(logits_c=lc, logits_u=lu, guided=guided, pred=pred, conf=conf, picked=picked)
     return new_codes, pred, conf, picked

@@ -455,3 +455,76 @@ def test_unmask_schedule():
             assert cum[i] >= min(N, math.floor(N * frac - 1e-9))
     # two steps of 10: t1 = 1 - cos(pi/4) = 0.29289..., ceil(2.93) = 3 then the rest
     assert O.unmask_schedule(10, 2) == [3, 7]
+
+
+# ---------------------------------------------------------------------------
+# Classifier-free guidance (the first NEXT row)
+# ---------------------------------------------------------------------------
+
+def _cfg_setup(rng, n_text=3, n_frames=6, n_cb=2, V=9, mask=8):
+    dims = small_dims()
+    layers = [rand_layer(dims, rng) for _ in range(2)]
+    text_tab = rng.standard_normal((11, dims.hidden))
+    tab = rng.standard_normal((n_cb * V, dims.hidden))
+    heads = 0.3 * rng.standard_normal((n_cb * V, dims.hidden))
+    fnorm = 1.0 + 0.1 * rng.standard_normal(dims.hidden)
+    text = rng.integers(0, 11, n_text)
+    codes = rng.integers(0, V - 1, (n_cb, n_frames))
+    codes[rng.random((n_cb, n_frames)) < 0.5] = mask
+    return dims, layers, text_tab, tab, heads, fnorm, text, codes, V, mask
+
+
+def test_cfg_logits_is_affine_in_the_scale():
+    rng = np.random.default_rng(21)
+    c, u = rng.standard_normal((4, 9)), rng.standard_normal((4, 9))
+    np.testing.assert_array_equal(O.cfg_logits(c, u, 0.0), c)           # no guidance
+    np.testing.assert_array_equal(O.cfg_logits(c, c, 3.7), c)           # nothing to contrast
+    f0, f1, f3 = (O.cfg_logits(c, u, s) for s in (0.0, 1.0, 3.0))
+    np.testing.assert_allclose(f3 - f1, 2.0 * (f1 - f0), rtol=1e-12, atol=1e-12)  # linear in s
+    # a large scale follows the contrast c - u: its argmax wins
+    big = O.cfg_logits(c, u, 1e6)
+    np.testing.assert_array_equal(np.argmax(big, -1), np.argmax(c - u, -1))
+
+
+def test_cfg_without_context_equals_the_plain_step():
+    """No text and a window that covers every frame: the unconditional prompt is the
+    conditional one, so guidance cancels for any scale."""
+    rng = np.random.default_rng(22)
+    dims, layers, text_tab, tab, heads, fnorm, _, codes, V, mask = _cfg_setup(rng)
+    plain = O.maskgit_pass([], text_tab, codes, tab, heads, layers, fnorm, dims, V, mask, 5.0, 4)
+    for s in (0.0, 2.5):
+        guided = O.maskgit_pass_cfg([], text_tab, codes, codes.shape[1], tab, heads, layers, fnorm, dims, V,
+                                    mask, 5.0, 4, s)
+        for a, b in zip(plain, guided):
+            np.testing.assert_array_equal(a, b)
+
+
+def test_cfg_unconditional_prompt_is_the_window_alone():
+    """The unconditional logits depend on the window's tokens only: changing the text or
+    the reference frames moves the conditional logits and leaves them alone; they equal
+    the logits of a plain step run on the window by itself."""
+    rng = np.random.default_rng(23)
+    dims, layers, text_tab, tab, heads, fnorm, text, codes, V, mask = _cfg_setup(rng)
+    nt = 4
+    rec = {}
+    out = O.maskgit_pass_cfg(text, text_tab, codes, nt, tab, heads, layers, fnorm, dims, V, mask, 5.0, 3, 2.0, rec)
+    text2 = (text + 1) % 11
+    codes2 = codes.copy()
+    codes2[:, 0] = (codes2[:, 0] + 1) % (V - 1)  # a reference frame, outside the window
+    rec2 = {}
+    O.maskgit_pass_cfg(text2, text_tab, codes2, nt, tab, heads, layers, fnorm, dims, V, mask, 5.0, 3, 2.0, rec2)
+    np.testing.assert_array_equal(rec["logits_u"], rec2["logits_u"])
+    assert np.max(np.abs(rec["logits_c"] - rec2["logits_c"])) > 1e-6
+    rec3 = {}
+    window = codes[:, -nt:]
+    O.maskgit_pass([], text_tab, window, tab, heads, layers, fnorm, dims, V, mask, 5.0, 0, rec3)
+    np.testing.assert_allclose(rec["logits_u"], rec3["logits"], rtol=1e-12, atol=1e-12)
+    # only the window is updated, and only where the guided scores pick
+    new_codes, pred, conf, picked = out
+    np.testing.assert_array_equal(new_codes[:, :-nt], codes[:, :-nt])
+    assert pred.shape == (codes.shape[0], nt) and conf.shape == pred.shape
+    np.testing.assert_array_equal(new_codes[:, -nt:], O.apply_picks(window, pred, picked))
+    # the scores are those of the guided logits
+    p_ref, c_ref, _ = O.maskgit_scores(rec["guided"], window, codes.shape[0], V, mask, 5.0)
+    np.testing.assert_array_equal(p_ref, pred)
+    np.testing.assert_array_equal(c_ref, conf)
