@@ -46,19 +46,25 @@ void launch_argmax_groups(const float *logits, int rows, int ld, int n_groups, i
                        n_groups, group_vocab, out);
 }
 
-__global__ __launch_bounds__(256) void maskgit_scores_kernel(const float *logits, int T, int ld,
-                                                             int n_cb, int V, int mask_id,
-                                                             float penalty, const int32_t *codes,
-                                                             int32_t *pred, float *conf) {
+__global__ __launch_bounds__(256) void maskgit_scores_kernel(const float *logits, const float *logits_u,
+                                                             float cfg_scale, int T, int ld, int n_cb, int V,
+                                                             int mask_id, float penalty, const int32_t *codes,
+                                                             int codes_ld, int32_t *pred, float *conf) {
     const int lane = threadIdx.x & 63;
     const int item = blockIdx.x * 4 + (threadIdx.x >> 6);  // flat index k*T + t
     if (item >= n_cb * T) return;
     const int k = item / T, t = item % T;
     const float *x = logits + (int64_t)t * ld + (int64_t)k * V;
+    const float *xu = logits_u ? logits_u + (int64_t)t * ld + (int64_t)k * V : nullptr;
+    // the scored logit of class v (guided when an unconditional row is given)
+    auto lg = [&](int v) {
+        const float c = x[v];
+        return xu ? c + cfg_scale * (c - xu[v]) : c;
+    };
     float mx = -INFINITY, best = -INFINITY;
     int bi = 0x7FFFFFFF;
     for (int v = lane; v < V; v += 64) {
-        const float xv = x[v];
+        const float xv = lg(v);
         mx = fmaxf(mx, xv);
         if (v != mask_id) argmax_merge(best, bi, xv, v);
     }
@@ -66,22 +72,22 @@ __global__ __launch_bounds__(256) void maskgit_scores_kernel(const float *logits
     wave_argmax(best, bi);
     const float LOG2E = 1.4426950408889634f;
     float se = 0.f;
-    for (int v = lane; v < V; v += 64) se += exp2f((x[v] - mx) * LOG2E);
+    for (int v = lane; v < V; v += 64) se += exp2f((lg(v) - mx) * LOG2E);
     se = wave_sum(se);
     if (lane == 0) {
         const float lse = mx + logf(se);
         pred[item] = bi;
-        conf[item] = (codes[item] == mask_id) ? (best - lse) - (float)k * penalty : -INFINITY;
+        conf[item] = (codes[(int64_t)k * codes_ld + t] == mask_id) ? (best - lse) - (float)k * penalty : -INFINITY;
     }
 }
 
-void launch_maskgit_scores(const float *logits, int T, int ld, int n_cb, int V, int mask_id,
-                           float penalty, const int32_t *codes, int32_t *pred, float *conf,
-                           hipStream_t s) {
+void launch_maskgit_scores(const float *logits, const float *logits_u, float cfg_scale, int T, int ld,
+                           int n_cb, int V, int mask_id, float penalty, const int32_t *codes, int codes_ld,
+                           int32_t *pred, float *conf, hipStream_t s) {
     const int items = n_cb * T;
     if (items <= 0) return;
-    hipLaunchKernelGGL(maskgit_scores_kernel, dim3((items + 3) / 4), dim3(256), 0, s, logits, T, ld,
-                       n_cb, V, mask_id, penalty, codes, pred, conf);
+    hipLaunchKernelGGL(maskgit_scores_kernel, dim3((items + 3) / 4), dim3(256), 0, s, logits, logits_u, cfg_scale,
+                       T, ld, n_cb, V, mask_id, penalty, codes, codes_ld, pred, conf);
 }
 
 constexpr int SEL_TILE = 1024;  // scores staged in LDS per block
@@ -115,29 +121,30 @@ __global__ __launch_bounds__(256) void rank_count_kernel(const float *conf, int 
     if (r) atomicAdd(&rank[i], r);
 }
 
-__global__ void select_scatter_kernel(const float *conf, const int32_t *pred, const int32_t *rank, int n,
-                                      int n_unmask, int32_t *codes, int32_t *picked) {
+__global__ void select_scatter_kernel(const float *conf, const int32_t *pred, const int32_t *rank, int n, int T,
+                                      int n_unmask, int32_t *codes, int codes_ld, int32_t *picked) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
     const int r = rank[i];
     if (r >= n_unmask) return;
     if (conf[i] > -INFINITY) {
         picked[r] = i;
-        codes[i] = pred[i];
+        codes[(int64_t)(i / T) * codes_ld + i % T] = pred[i];
     } else {
         picked[r] = -1;
     }
 }
 
-void launch_select_update(const float *conf, const int32_t *pred, int n, int n_unmask, int32_t *rank,
-                          int32_t *codes, int32_t *picked, hipStream_t s) {
+void launch_select_update(const float *conf, const int32_t *pred, int n_cb, int T, int n_unmask,
+                          int32_t *rank, int32_t *codes, int codes_ld, int32_t *picked, hipStream_t s) {
+    const int n = n_cb * T;
     if (n <= 0 || n_unmask <= 0) return;
     const int blocks = (n + 255) / 256;
     hipLaunchKernelGGL(zero_i32_kernel, dim3(blocks), dim3(256), 0, s, rank, n);
     hipLaunchKernelGGL(rank_count_kernel, dim3(blocks, (n + SEL_TILE - 1) / SEL_TILE), dim3(256), 0, s, conf,
                        n, rank);
-    hipLaunchKernelGGL(select_scatter_kernel, dim3(blocks), dim3(256), 0, s, conf, pred, rank, n, n_unmask,
-                       codes, picked);
+    hipLaunchKernelGGL(select_scatter_kernel, dim3(blocks), dim3(256), 0, s, conf, pred, rank, n, T, n_unmask,
+                       codes, codes_ld, picked);
 }
 
 }  // namespace ttsbb

@@ -125,14 +125,17 @@ void launch_argmax_groups(const float *logits, int rows, int ld, int n_groups, i
                           int32_t *out, hipStream_t s);
 
 // ---- K8: MaskGIT scores: log-softmax, mask class excluded, argmax, confidence --------
-void launch_maskgit_scores(const float *logits, int T, int ld, int n_cb, int V, int mask_id,
-                           float penalty, const int32_t *codes, int32_t *pred, float *conf,
-                           hipStream_t s);
+// logits [T][ld] (flat k*V + v per row).  With logits_u (same layout) the scored logits
+// are the guided c + cfg_scale * (c - u).  codes: element (k, t) at codes[k*codes_ld + t].
+void launch_maskgit_scores(const float *logits, const float *logits_u, float cfg_scale, int T, int ld,
+                           int n_cb, int V, int mask_id, float penalty, const int32_t *codes, int codes_ld,
+                           int32_t *pred, float *conf, hipStream_t s);
 
 // ---- K9: top-n selection by rank + code update -------------------------------------
 // rank: int32 scratch [n]
-void launch_select_update(const float *conf, const int32_t *pred, int n, int n_unmask, int32_t *rank,
-                          int32_t *codes, int32_t *picked, hipStream_t s);
+// Top-n over conf [n_cb][T] (flat k*T + t); picked codes go to codes[k*codes_ld + t].
+void launch_select_update(const float *conf, const int32_t *pred, int n_cb, int T, int n_unmask,
+                          int32_t *rank, int32_t *codes, int codes_ld, int32_t *picked, hipStream_t s);
 
 // ---- misc ---------------------------------------------------------------------------
 void launch_increment(int32_t *v, int n, hipStream_t s);

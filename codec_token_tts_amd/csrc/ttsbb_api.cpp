@@ -62,6 +62,7 @@ struct ttsbb_ctx {
     int s_pad_cap = 0;
     float *part = nullptr;
     float *logits = nullptr;
+    float *logits_u = nullptr;  // unconditional logits of a guided MaskGIT step
     int32_t *rank = nullptr;
     int rank_cap = 0;
     float *gpart = nullptr;   // split-K partial sums
@@ -136,7 +137,8 @@ int tap_width(const ttsbb_ctx *c, int tap) {
         case TTSBB_TAP_K:
         case TTSBB_TAP_V: return g.n_kv_heads * g.head_dim;
         case TTSBB_TAP_MLP: return g.ffn;
-        case TTSBB_TAP_LOGITS: return g.max_head_cols > 0 ? g.max_head_cols : 1;
+        case TTSBB_TAP_LOGITS:
+        case TTSBB_TAP_LOGITS_U: return g.max_head_cols > 0 ? g.max_head_cols : 1;
         default: return g.hidden;
     }
 }
@@ -235,6 +237,7 @@ TTSBB_API ttsbb_status ttsbb_create(const ttsbb_config *cfg, const ttsbb_layer *
               dev_alloc(c, (void **)&c->vtbuf, (size_t)g.n_kv_heads * c->s_pad_cap * g.head_dim * 2) &&
               dev_alloc(c, (void **)&c->part, R * g.n_heads * MAX_CHUNKS * PART_STRIDE * 4) &&
               dev_alloc(c, (void **)&c->logits, R * (size_t)(g.max_head_cols > 0 ? g.max_head_cols : 1) * 4) &&
+              dev_alloc(c, (void **)&c->logits_u, R * (size_t)(g.max_head_cols > 0 ? g.max_head_cols : 1) * 4) &&
               dev_alloc(c, (void **)&c->rank, (size_t)R * (g.max_head_cols / 2 + 1) * 4) &&
               dev_alloc(c, (void **)&c->gpart, (size_t)c->gpart_cap * 4) &&
               dev_alloc(c, (void **)&c->rope, (size_t)g.max_pos * 64 * sizeof(float2)) &&
@@ -477,6 +480,98 @@ void head_gemm(ttsbb_ctx *c, const void *head, int M, int N, float *out, int ldc
     launch_gemm(a, c->dt, c->gpart, c->gpart_cap, c->stream);
 }
 
+// MaskGIT input rows [0, S) of ctx->x: n_text text rows, then audio frames whose code
+// (k, t) is codes[k * codes_ld + t].
+void maskgit_embed(ttsbb_ctx *ctx, int S, int n_text, const int32_t *text_ids, const void *text_table,
+                   int text_vocab, int n_cb, int cb_vocab, const void *audio_tables, const int32_t *codes,
+                   int codes_ld) {
+    EmbedArgs e;
+    e.n_rows = S;
+    e.n_cb = n_cb;
+    e.hidden = ctx->cfg.hidden;
+    e.codes = codes;
+    e.code_row_stride = 1;
+    e.code_cb_stride = codes_ld;
+    e.audio_row0 = n_text;
+    e.tables = audio_tables;
+    e.cb_vocab = cb_vocab;
+    e.is_text = nullptr;
+    e.text_prefix = n_text;
+    e.text_ids = text_ids;
+    e.text_table = text_table;
+    e.text_vocab = text_vocab;
+    e.out = ctx->x;
+    e.flag = ctx->flag;
+    KScope k(ctx, TTSBB_K_EMBED);
+    launch_embed(e, DT_BF16, ctx->stream);
+}
+
+// Every layer over rows [0, S) of ctx->x with bidirectional attention (RoPE positions
+// 0..S-1, no cache), then the final RMSNorm of rows [row0, row0 + n_out) and the heads
+// into logits [n_out][N].  Per-layer taps only when `taps`.
+void maskgit_backbone(ttsbb_ctx *ctx, int S, int row0, int n_out, const void *heads, int N, float *logits,
+                      bool taps) {
+    const ttsbb_config &g = ctx->cfg;
+    const int s_pad = round_up(S, 64);
+    const int H = g.n_heads, Hkv = g.n_kv_heads, hd = g.head_dim;
+    const int hd_all = H * hd;
+    for (int l = 0; l < g.n_layers; ++l) {
+        const ttsbb_layer &L = ctx->layers[l];
+        const bool tapit = taps && (l == ctx->tap_layer);
+        RopeKvArgs r = {};
+        r.qkv = ctx->qkv;
+        r.M = S;
+        r.H = H;
+        r.Hkv = Hkv;
+        r.q_gain = L.q_norm;
+        r.k_gain = L.k_norm;
+        r.eps = g.rms_eps;
+        r.rope = ctx->rope;
+        r.max_pos = g.max_pos;
+        r.q_out = ctx->q;
+        r.dense = 1;
+        r.kbuf = ctx->kbuf;
+        r.vtbuf = ctx->vtbuf;
+        r.s_pad = s_pad;
+        r.flag = ctx->flag;
+        if (!qkv_projection(ctx, L, ctx->x, S, tapit, &r)) {
+            KScope k(ctx, TTSBB_K_ROPE_KV);
+            launch_rope_kv(r, DT_BF16, ctx->stream);
+        }
+        if (tapit) {
+            tap_dense(ctx, TTSBB_TAP_Q, ctx->q, DT_BF16, S, hd_all, hd_all);
+            // K [Hkv][s_pad][hd] -> [S][Hkv][hd];  V^T [Hkv][hd][s_pad] -> [S][Hkv][hd]
+            tap(ctx, TTSBB_TAP_K, ctx->kbuf, DT_BF16, S, Hkv * hd, hd, (int64_t)s_pad * hd, 1, hd);
+            tap(ctx, TTSBB_TAP_V, ctx->vtbuf, DT_BF16, S, Hkv * hd, 1, (int64_t)hd * s_pad, s_pad, hd);
+        }
+
+        FlashArgs f;
+        f.q = reinterpret_cast<const uint16_t *>(ctx->q);
+        f.k = ctx->kbuf;
+        f.vt = ctx->vtbuf;
+        f.S = S;
+        f.s_pad = s_pad;
+        f.H = H;
+        f.Hkv = Hkv;
+        f.scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
+        f.out = reinterpret_cast<uint16_t *>(ctx->attn);
+        {
+            KScope k(ctx, TTSBB_K_FLASH_ATTN);
+            launch_flash_attn(f, ctx->stream);
+        }
+        post_attention(ctx, L, ctx->x, S, tapit);
+    }
+    // final norm + heads on the rows read out only
+    flush_residual(ctx, ctx->x, S);
+    {
+        KScope k(ctx, TTSBB_K_RMSNORM);
+        launch_rmsnorm(ctx->x + (size_t)row0 * g.hidden, g.hidden, n_out, g.hidden, ctx->final_norm, g.rms_eps,
+                       ctx->h, DT_BF16, ctx->stream);
+    }
+    if (taps && ctx->tap_layer >= 0) tap_dense(ctx, TTSBB_TAP_HEAD_IN, ctx->h, DT_BF16, n_out, g.hidden, g.hidden);
+    head_gemm(ctx, heads, n_out, N, logits, N);
+}
+
 }  // namespace
 
 TTSBB_API ttsbb_status ttsbb_decode_step(ttsbb_ctx *ctx, int32_t batch, float *x, int32_t *positions,
@@ -613,99 +708,63 @@ TTSBB_API ttsbb_status ttsbb_maskgit_pass(ttsbb_ctx *ctx, int32_t n_text, const 
     if (ctx->dt != DT_BF16) return TTSBB_UNSUPPORTED;
 
     const int S = n_text + n_frames;
-    const int s_pad = round_up(S, 64);
-    const int H = g.n_heads, Hkv = g.n_kv_heads, hd = g.head_dim;
-    const int hd_all = H * hd;
-
-    EmbedArgs e;
-    e.n_rows = S;
-    e.n_cb = n_cb;
-    e.hidden = g.hidden;
-    e.codes = codes;
-    e.code_row_stride = 1;
-    e.code_cb_stride = n_frames;
-    e.audio_row0 = n_text;
-    e.tables = audio_tables;
-    e.cb_vocab = cb_vocab;
-    e.is_text = nullptr;
-    e.text_prefix = n_text;
-    e.text_ids = text_ids;
-    e.text_table = text_table;
-    e.text_vocab = text_vocab;
-    e.out = ctx->x;
-    e.flag = ctx->flag;
-    {
-        KScope k(ctx, TTSBB_K_EMBED);
-        launch_embed(e, DT_BF16, ctx->stream);
-    }
-
-    for (int l = 0; l < g.n_layers; ++l) {
-        const ttsbb_layer &L = ctx->layers[l];
-        const bool tapit = (l == ctx->tap_layer);
-        RopeKvArgs r = {};
-        r.qkv = ctx->qkv;
-        r.M = S;
-        r.H = H;
-        r.Hkv = Hkv;
-        r.q_gain = L.q_norm;
-        r.k_gain = L.k_norm;
-        r.eps = g.rms_eps;
-        r.rope = ctx->rope;
-        r.max_pos = g.max_pos;
-        r.q_out = ctx->q;
-        r.dense = 1;
-        r.kbuf = ctx->kbuf;
-        r.vtbuf = ctx->vtbuf;
-        r.s_pad = s_pad;
-        r.flag = ctx->flag;
-        if (!qkv_projection(ctx, L, ctx->x, S, tapit, &r)) {
-            KScope k(ctx, TTSBB_K_ROPE_KV);
-            launch_rope_kv(r, DT_BF16, ctx->stream);
-        }
-        if (tapit) {
-            tap_dense(ctx, TTSBB_TAP_Q, ctx->q, DT_BF16, S, hd_all, hd_all);
-            // K [Hkv][s_pad][hd] -> [S][Hkv][hd];  V^T [Hkv][hd][s_pad] -> [S][Hkv][hd]
-            tap(ctx, TTSBB_TAP_K, ctx->kbuf, DT_BF16, S, Hkv * hd, hd, (int64_t)s_pad * hd, 1, hd);
-            tap(ctx, TTSBB_TAP_V, ctx->vtbuf, DT_BF16, S, Hkv * hd, 1, (int64_t)hd * s_pad, s_pad, hd);
-        }
-
-        FlashArgs f;
-        f.q = reinterpret_cast<const uint16_t *>(ctx->q);
-        f.k = ctx->kbuf;
-        f.vt = ctx->vtbuf;
-        f.S = S;
-        f.s_pad = s_pad;
-        f.H = H;
-        f.Hkv = Hkv;
-        f.scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
-        f.out = reinterpret_cast<uint16_t *>(ctx->attn);
-        {
-            KScope k(ctx, TTSBB_K_FLASH_ATTN);
-            launch_flash_attn(f, ctx->stream);
-        }
-
-        post_attention(ctx, L, ctx->x, S, tapit);
-    }
-
-    // final norm + heads on the audio window only
     const int N = n_cb * cb_vocab;
-    flush_residual(ctx, ctx->x, S);
-    {
-        KScope k(ctx, TTSBB_K_RMSNORM);
-        launch_rmsnorm(ctx->x + (size_t)n_text * g.hidden, g.hidden, n_frames, g.hidden, ctx->final_norm,
-                       g.rms_eps, ctx->h, DT_BF16, ctx->stream);
-    }
-    if (ctx->tap_layer >= 0) tap_dense(ctx, TTSBB_TAP_HEAD_IN, ctx->h, DT_BF16, n_frames, g.hidden, g.hidden);
-    head_gemm(ctx, audio_heads, n_frames, N, ctx->logits, N);
+    maskgit_embed(ctx, S, n_text, text_ids, text_table, text_vocab, n_cb, cb_vocab, audio_tables, codes, n_frames);
+    maskgit_backbone(ctx, S, n_text, n_frames, audio_heads, N, ctx->logits, true);
     if (ctx->tap_layer >= 0) tap_dense(ctx, TTSBB_TAP_LOGITS, ctx->logits, DT_F32, n_frames, N, N);
     {
         KScope k(ctx, TTSBB_K_SCORES);
-        launch_maskgit_scores(ctx->logits, n_frames, N, n_cb, cb_vocab, mask_id, layer_penalty, codes,
-                              pred, conf, ctx->stream);
+        launch_maskgit_scores(ctx->logits, nullptr, 0.f, n_frames, N, n_cb, cb_vocab, mask_id, layer_penalty, codes,
+                              n_frames, pred, conf, ctx->stream);
     }
     {
         KScope k(ctx, TTSBB_K_SELECT);
-        launch_select_update(conf, pred, n_cb * n_frames, n_unmask, ctx->rank, codes, picked, ctx->stream);
+        launch_select_update(conf, pred, n_cb, n_frames, n_unmask, ctx->rank, codes, n_frames, picked, ctx->stream);
+    }
+    return launch_failed() ? TTSBB_DEVICE_ERROR : TTSBB_OK;
+}
+
+TTSBB_API ttsbb_status ttsbb_maskgit_pass_cfg(ttsbb_ctx *ctx, int32_t n_text, const int32_t *text_ids,
+                                              const void *text_table, int32_t text_vocab, int32_t n_frames,
+                                              int32_t n_target, int32_t n_cb, int32_t cb_vocab, int32_t mask_id,
+                                              const void *audio_tables, const void *audio_heads, int32_t *codes,
+                                              int32_t n_unmask, float layer_penalty, float cfg_scale, int32_t *pred,
+                                              float *conf, int32_t *picked) {
+    if (!ctx) return TTSBB_INVALID_ARG;
+    const ttsbb_config &g = ctx->cfg;
+    ctx->pend_splits = 0;
+    if (n_text < 0 || n_frames <= 0 || n_target <= 0 || n_target > n_frames || n_cb <= 0 || cb_vocab <= 0 ||
+        mask_id < 0 || mask_id >= cb_vocab || n_unmask < 0 || (int64_t)n_unmask > (int64_t)n_cb * n_target)
+        return TTSBB_INVALID_ARG;
+    if ((int64_t)n_text + n_frames > g.max_rows || (int64_t)n_text + n_frames > g.max_pos) return TTSBB_INVALID_ARG;
+    if ((int64_t)n_cb * cb_vocab > g.max_head_cols) return TTSBB_INVALID_ARG;
+    if ((int64_t)n_cb * n_target > ctx->rank_cap) return TTSBB_INVALID_ARG;
+    if (n_text > 0 && (!text_ids || !text_table || text_vocab <= 0)) return TTSBB_INVALID_ARG;
+    if (!audio_tables || !audio_heads || !codes || !pred || !conf || (n_unmask > 0 && !picked) ||
+        !ctx->final_norm)
+        return TTSBB_INVALID_ARG;
+    if (!(layer_penalty == layer_penalty) || !(cfg_scale == cfg_scale)) return TTSBB_INVALID_ARG;
+    if (ctx->dt != DT_BF16) return TTSBB_UNSUPPORTED;
+
+    const int S = n_text + n_frames, w0 = n_frames - n_target;
+    const int N = n_cb * cb_vocab;
+    int32_t *window = codes + w0;  // element (k, t) of the window at window[k * n_frames + t]
+    // conditional pass: the whole prompt, logits on the window (its last n_target rows)
+    maskgit_embed(ctx, S, n_text, text_ids, text_table, text_vocab, n_cb, cb_vocab, audio_tables, codes, n_frames);
+    maskgit_backbone(ctx, S, n_text + w0, n_target, audio_heads, N, ctx->logits, true);
+    if (ctx->tap_layer >= 0) tap_dense(ctx, TTSBB_TAP_LOGITS, ctx->logits, DT_F32, n_target, N, N);
+    // unconditional pass: the window's frames alone, positions 0..n_target-1
+    maskgit_embed(ctx, n_target, 0, nullptr, nullptr, 0, n_cb, cb_vocab, audio_tables, window, n_frames);
+    maskgit_backbone(ctx, n_target, 0, n_target, audio_heads, N, ctx->logits_u, false);
+    if (ctx->tap_layer >= 0) tap_dense(ctx, TTSBB_TAP_LOGITS_U, ctx->logits_u, DT_F32, n_target, N, N);
+    {
+        KScope k(ctx, TTSBB_K_SCORES);
+        launch_maskgit_scores(ctx->logits, ctx->logits_u, cfg_scale, n_target, N, n_cb, cb_vocab, mask_id,
+                              layer_penalty, window, n_frames, pred, conf, ctx->stream);
+    }
+    {
+        KScope k(ctx, TTSBB_K_SELECT);
+        launch_select_update(conf, pred, n_cb, n_target, n_unmask, ctx->rank, window, n_frames, picked, ctx->stream);
     }
     return launch_failed() ? TTSBB_DEVICE_ERROR : TTSBB_OK;
 }

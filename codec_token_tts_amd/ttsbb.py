@@ -18,11 +18,11 @@ OK, INVALID_ARG, UNSUPPORTED, OOM, DEVICE_ERROR = 0, -1, -2, -3, -4
 F32, BF16 = 0, 1
 
 (TAP_X_IN, TAP_H_ATTN, TAP_QKV, TAP_Q, TAP_K, TAP_V, TAP_ATTN, TAP_X_MID, TAP_H_FFN, TAP_MLP,
- TAP_X_OUT, TAP_HEAD_IN, TAP_LOGITS) = range(13)
+ TAP_X_OUT, TAP_HEAD_IN, TAP_LOGITS, TAP_LOGITS_U) = range(14)
 
 EXPORTS = ["ttsbb_default_config", "ttsbb_create", "ttsbb_destroy", "ttsbb_status_str",
            "ttsbb_sync", "ttsbb_codebook_embed", "ttsbb_decode_step", "ttsbb_maskgit_pass",
-           "ttsbb_unmask_schedule", "ttsbb_set_tap_layer", "ttsbb_read_tap", "ttsbb_profile_start",
+           "ttsbb_maskgit_pass_cfg", "ttsbb_unmask_schedule", "ttsbb_set_tap_layer", "ttsbb_read_tap", "ttsbb_profile_start",
            "ttsbb_profile_stop"]
 
 (K_EMBED, K_RMSNORM, K_GEMM_QKV, K_ROPE_KV, K_DECODE_ATTN, K_DECODE_COMBINE, K_FLASH_ATTN, K_GEMM_O,
@@ -75,6 +75,8 @@ def lib() -> C.CDLL:
         "ttsbb_decode_step": (i32, [vp, i32, vp, vp, vp, i32, vp, i32, vp, i32, i32, vp, vp]),
         "ttsbb_maskgit_pass": (i32, [vp, i32, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, i32, f32,
                                      vp, vp, vp]),
+        "ttsbb_maskgit_pass_cfg": (i32, [vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp, i32, f32,
+                                         f32, vp, vp, vp]),
         "ttsbb_unmask_schedule": (i32, [i32, i32, C.POINTER(i32)]),
         "ttsbb_set_tap_layer": (i32, [vp, i32]),
         "ttsbb_read_tap": (i32, [vp, i32, vp, i64, C.POINTER(i32), C.POINTER(i32)]),
@@ -181,6 +183,18 @@ def ttsbb_unmask_schedule(n_total: int, n_steps: int):
 
 def ttsbb_set_tap_layer(ctx, layer: int):
     _check(lib().ttsbb_set_tap_layer(ctx, layer), "ttsbb_set_tap_layer")
+
+
+def ttsbb_maskgit_pass_cfg(ctx, n_text, text_ids, text_table, text_vocab, n_frames, n_target, n_cb,
+                           cb_vocab, mask_id, audio_tables, audio_heads, codes, n_unmask, layer_penalty,
+                           cfg_scale, pred, conf, picked, check: bool = True) -> int:
+    st = lib().ttsbb_maskgit_pass_cfg(ctx, n_text, ptr(text_ids), ptr(text_table), text_vocab,
+                                      n_frames, n_target, n_cb, cb_vocab, mask_id, ptr(audio_tables),
+                                      ptr(audio_heads), ptr(codes), n_unmask, float(layer_penalty),
+                                      float(cfg_scale), ptr(pred), ptr(conf), ptr(picked))
+    if check:
+        _check(st, "ttsbb_maskgit_pass_cfg")
+    return st
 
 
 def ttsbb_read_tap(ctx, tap: int, dst, n_floats: int):

@@ -155,6 +155,29 @@ ttsbb_status ttsbb_maskgit_pass(ttsbb_ctx *ctx, int32_t n_text, const int32_t *t
                                 int32_t *codes, int32_t n_unmask, float layer_penalty,
                                 int32_t *pred, float *conf, int32_t *picked);
 
+/* One MaskGIT step with classifier-free guidance (OmniVoice ARCHITECTURE, "MaskGIT
+ * decoder": the unconditional prompt is the trailing target tokens alone; the step
+ * scores log_softmax(c + cfg_scale * (c - u))).  The last n_target of the n_frames audio
+ * frames are the target window (the frames before it are reference audio, conditioning
+ * only).  Two passes of every layer:
+ *   conditional:   n_text text tokens + all n_frames frames, positions 0..S-1, logits c
+ *                  on the window (the last n_target positions);
+ *   unconditional: the window's n_target frames alone, positions 0..n_target-1, logits u;
+ * then, with g = c + cfg_scale * (c - u), the scoring of ttsbb_maskgit_pass on g over the
+ * window, and the update of the n_unmask best window positions.
+ *   codes int32 [n_cb][n_frames] in/out (only the window changes); pred int32 and conf
+ *   fp32 [n_cb][n_target]; picked int32 [n_unmask] holds flat window indices
+ *   f = k*n_target + t (or -1); other arguments as in ttsbb_maskgit_pass.
+ * Requires cfg.dtype == TTSBB_BF16, 0 < n_target <= n_frames and 2 * n_target <=
+ * cfg.max_rows (both passes' logits are kept).  With taps on, the per-layer taps and
+ * TTSBB_TAP_LOGITS come from the conditional pass, TTSBB_TAP_LOGITS_U holds u. */
+ttsbb_status ttsbb_maskgit_pass_cfg(ttsbb_ctx *ctx, int32_t n_text, const int32_t *text_ids,
+                                    const void *text_table, int32_t text_vocab, int32_t n_frames,
+                                    int32_t n_target, int32_t n_cb, int32_t cb_vocab, int32_t mask_id,
+                                    const void *audio_tables, const void *audio_heads, int32_t *codes,
+                                    int32_t n_unmask, float layer_penalty, float cfg_scale, int32_t *pred,
+                                    float *conf, int32_t *picked);
+
 /* Host helper: how many positions each of n_steps MaskGIT steps unmasks (OmniVoice
  * ARCHITECTURE, "MaskGIT decoder": ceil(N * (t[i+1] - t[i])) over a time grid), on the
  * cosine grid t_i = 1 - cos(pi/2 * i/n_steps); each count is capped at what is left and
@@ -176,7 +199,8 @@ typedef enum {
     TTSBB_TAP_X_OUT = 10,  /* layer output                         [rows][hidden] */
     TTSBB_TAP_HEAD_IN = 11,/* final-normed head operand (not per layer) [rows][hidden] */
     TTSBB_TAP_LOGITS = 12, /* head output (not per layer) [rows][head cols] */
-    TTSBB_TAP_COUNT = 13
+    TTSBB_TAP_LOGITS_U = 13, /* guided MaskGIT step: unconditional logits [rows][head cols] */
+    TTSBB_TAP_COUNT = 14
 } ttsbb_tap;
 
 /* Record taps of `layer` (0-based) in the following calls; -1 turns taps off.

@@ -46,6 +46,8 @@ int main(void) {
     EXPECT(ttsbb_decode_step(NULL, 1, &dummy, NULL, NULL, 1, NULL, 1, NULL, 0, 0, NULL, NULL) == TTSBB_INVALID_ARG);
     EXPECT(ttsbb_maskgit_pass(NULL, 0, NULL, NULL, 0, 1, 1, 2, 1, NULL, NULL, NULL, 0, 5.0f, NULL, NULL,
                               NULL) == TTSBB_INVALID_ARG);
+    EXPECT(ttsbb_maskgit_pass_cfg(NULL, 0, NULL, NULL, 0, 4, 2, 1, 2, 1, NULL, NULL, NULL, 0, 5.0f, 2.0f, NULL,
+                                  NULL, NULL) == TTSBB_INVALID_ARG);
     EXPECT(ttsbb_set_tap_layer(NULL, 0) == TTSBB_INVALID_ARG);
     EXPECT(ttsbb_read_tap(NULL, 0, &dummy, 1, NULL, NULL) == TTSBB_INVALID_ARG);
     EXPECT(ttsbb_profile_start(NULL, 1u, 16) == TTSBB_INVALID_ARG);

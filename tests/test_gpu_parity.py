@@ -330,3 +330,105 @@ def test_maskgit_deterministic():
             assert np.array_equal(a[k], b[k]), k
     finally:
         m.close()
+
+
+# ---------------------------------------------------------------------------------------
+# Guided MaskGIT step (classifier-free guidance)
+# ---------------------------------------------------------------------------------------
+def run_maskgit_cfg(m: Model, n_text, n_frames, n_target, n_cb, V, mask_id, n_unmask, cfg_scale, seed,
+                    text_vocab=500, masked_frac=0.5):
+    T = m.T
+    shape = m.shape
+    text_h = CFG.table(seed, gen.KIND_TEXT_TABLE, 0, text_vocab, shape.hidden, True)
+    tab_h = CFG.table(seed, gen.KIND_CB_TABLE, 0, n_cb * V, shape.hidden, True)
+    head_h = CFG.table(seed, gen.KIND_HEAD, 0, n_cb * V, shape.hidden, True)
+    text_ids = gen.uniform_int(seed, stream_id(gen.KIND_TEXT_IDS, 0), (n_text,), text_vocab)
+    codes = gen.uniform_int(seed, stream_id(gen.KIND_CODES, 0), (n_cb, n_frames), V - 1)
+    w0 = n_frames - n_target
+    perm = gen.permutation(seed, stream_id(gen.KIND_MASK_PERM, 0), n_cb * n_target)
+    win = codes[:, w0:].copy().reshape(-1)
+    win[perm[:int(masked_frac * n_cb * n_target)]] = mask_id
+    codes[:, w0:] = win.reshape(n_cb, n_target)
+    codes_d = t_i32(codes)
+    pred = torch().empty((n_cb, n_target), dtype=torch().int32, device="cuda")
+    conf = torch().empty((n_cb, n_target), dtype=torch().float32, device="cuda")
+    picked = torch().empty(max(1, n_unmask), dtype=torch().int32, device="cuda")
+    T.ttsbb_set_tap_layer(m.ctx, 0)
+    T.ttsbb_maskgit_pass_cfg(m.ctx, n_text, t_i32(text_ids), DEV.host_to_device(text_h), text_vocab, n_frames,
+                             n_target, n_cb, V, mask_id, DEV.host_to_device(tab_h), DEV.host_to_device(head_h),
+                             codes_d, n_unmask, 5.0, cfg_scale, pred, conf, picked)
+    assert T.ttsbb_sync(m.ctx) == T.OK
+    res = dict(codes=codes_d.cpu().numpy(), pred=pred.cpu().numpy(), conf=conf.cpu().numpy(),
+               picked=picked.cpu().numpy()[:n_unmask],
+               logits_c=read_tap(m, T.TAP_LOGITS, n_target, n_cb * V),
+               logits_u=read_tap(m, T.TAP_LOGITS_U, n_target, n_cb * V))
+    T.ttsbb_set_tap_layer(m.ctx, -1)
+    rec = {}
+    O.maskgit_pass_cfg(text_ids, widen(text_h), codes, n_target, widen(tab_h), widen(head_h), m.oracle_layers(),
+                       m.oracle_final_norm(), dims_of(shape), V, mask_id, 5.0, n_unmask, cfg_scale, record=rec)
+    return res, dict(codes_in=codes, rec=rec, inputs=(text_ids, text_h, tab_h, head_h, codes))
+
+
+@pytest.mark.parametrize("n_text,n_frames,n_target,n_unmask,scale", [(13, 57, 40, 30, 2.0), (70, 130, 100, 77, 3.0),
+                                                                     (0, 50, 50, 20, 1.5)])
+def test_maskgit_cfg_two_layers(n_text, n_frames, n_target, n_unmask, scale):
+    """bf16, 2 layers: both passes' logits against the oracle's, the guided choice and
+    scores (discrete parity on the guided logits), the top-n picks and the update of the
+    window only.  (13, 57 | 40) runs both passes through the M <= 64 products, (70, 130 |
+    100) both through the LDS-DMA products with the fused q|k|v epilogue."""
+    m = Model(CFG.Shape(n_layers=2), 2, True, seed=6, gains="random")
+    try:
+        n_cb, V, mask = 3, 33, 32
+        res, ref = run_maskgit_cfg(m, n_text, n_frames, n_target, n_cb, V, mask, n_unmask, scale, 6)
+        rec = ref["rec"]
+        assert normwise(res["logits_c"], rec["logits_c"]) <= TOL_LAYER_BF16
+        assert normwise(res["logits_u"], rec["logits_u"]) <= TOL_LAYER_BF16
+        g_gpu = O.cfg_logits(res["logits_c"], res["logits_u"], scale)
+        gv = g_gpu.reshape(n_target, n_cb, V).transpose(1, 0, 2)
+        rv = rec["guided"].reshape(n_target, n_cb, V).transpose(1, 0, 2)
+        check_argmax_groups(res["pred"], gv, rv, exclude=mask)
+        fin = np.isfinite(rec["conf"])
+        assert np.array_equal(np.isfinite(res["conf"]), fin)
+        delta = np.max(np.abs(g_gpu - rec["guided"]))
+        assert np.max(np.abs(res["conf"][fin] - rec["conf"][fin])) <= 2 * delta + 1e-4
+        check_topn(res["picked"], res["conf"], rec["conf"], n_unmask)
+        w0 = n_frames - n_target
+        codes_in = ref["codes_in"]
+        np.testing.assert_array_equal(res["codes"][:, :w0], codes_in[:, :w0])
+        np.testing.assert_array_equal(res["codes"][:, w0:], O.apply_picks(codes_in[:, w0:], res["pred"],
+                                                                          res["picked"]))
+    finally:
+        m.close()
+
+
+def test_maskgit_cfg_without_context_is_the_plain_step():
+    """No text and a window covering every frame: the two passes see the same sequence,
+    compute bit-identical logits, and the guided step returns exactly the plain step's
+    choices, scores, picks and codes, whatever the scale."""
+    m = Model(CFG.Shape(n_layers=1), 1, True, seed=8)
+    try:
+        T = m.T
+        n_cb, V, mask, n_frames, n_unmask = 2, 33, 32, 75, 25
+        tab_h = CFG.table(8, gen.KIND_CB_TABLE, 0, n_cb * V, m.shape.hidden, True)
+        head_h = CFG.table(8, gen.KIND_HEAD, 0, n_cb * V, m.shape.hidden, True)
+        codes = gen.uniform_int(8, stream_id(gen.KIND_CODES, 0), (n_cb, n_frames), V - 1)
+        codes[:, ::2] = mask
+        outs = []
+        for cfg in (None, 0.0, 4.0):
+            cd = t_i32(codes)
+            pred = torch().empty((n_cb, n_frames), dtype=torch().int32, device="cuda")
+            conf = torch().empty((n_cb, n_frames), dtype=torch().float32, device="cuda")
+            picked = torch().empty(n_unmask, dtype=torch().int32, device="cuda")
+            args = (DEV.host_to_device(tab_h), DEV.host_to_device(head_h), cd, n_unmask, 5.0)
+            if cfg is None:
+                T.ttsbb_maskgit_pass(m.ctx, 0, None, None, 0, n_frames, n_cb, V, mask, *args, pred, conf, picked)
+            else:
+                T.ttsbb_maskgit_pass_cfg(m.ctx, 0, None, None, 0, n_frames, n_frames, n_cb, V, mask, *args, cfg,
+                                         pred, conf, picked)
+            assert T.ttsbb_sync(m.ctx) == T.OK
+            outs.append([a.cpu().numpy() for a in (cd, pred, conf, picked)])
+        for o in outs[1:]:
+            for a, b in zip(outs[0], o):
+                np.testing.assert_array_equal(a, b)
+    finally:
+        m.close()
