@@ -130,6 +130,18 @@ class MaskgitC4:
                                   self.heads, self.codes, self.sched[i], e["layer_penalty"], self.pred,
                                   self.conf, self.picked)
 
+    def step_cfg(self, s, cfg_scale=2.0):
+        """The same step with classifier-free guidance: the conditional prompt (200 text
+        tokens + 750 frames) and the 750-frame window alone, guided scores."""
+        e = self.e
+        i = s % e["n_steps"]
+        if i == 0:
+            self.codes.copy_(self.codes0)
+        self.T.ttsbb_maskgit_pass_cfg(self.ctx, e["n_text"], self.text_ids, self.text_table, e["text_vocab"],
+                                      e["n_frames"], e["n_frames"], e["n_cb"], e["cb_vocab"], e["mask_id"],
+                                      self.tables, self.heads, self.codes, self.sched[i], e["layer_penalty"],
+                                      cfg_scale, self.pred, self.conf, self.picked)
+
     def flops(self):
         """Algorithmic flops of one pass: projections, attention, heads."""
         e = self.e
@@ -314,6 +326,18 @@ def run_c5c4(args, T, torch):
     pd = T.ttsbb_profile_stop(dec.ctx)
     pm = T.ttsbb_profile_stop(mg.ctx)
 
+    # Guided MaskGIT step (classifier-free guidance), timed on its own after the step
+    log("timed: %d guided MaskGIT steps" % args.steps)
+    mg.step_cfg(0)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        mg.step_cfg(i)
+    e1.record()
+    torch.cuda.synchronize()
+    cfg_ms = e0.elapsed_time(e1) / args.steps
+
     attn_ms, attn_n = timed_attn
     attn_avg_ms = attn_ms / max(1, attn_n)
     attn_bytes = dec.attn_bytes(args.warmup, args.steps)
@@ -345,6 +369,10 @@ def run_c5c4(args, T, torch):
                     "frames_per_s": round(mg.e["n_frames"] / (mg_ms * 1e-3 * mg.e["n_steps"]), 1),
                     "mfma_tflops": round(mfma_tflops, 1),
                     "mfma_util": round(mfma_tflops / BF16_PEAK_TFLOPS, 4)},
+        "maskgit_cfg": {"ms_per_pass": round(cfg_ms, 4),
+                        "frames_per_s": round(mg.e["n_frames"] / (cfg_ms * 1e-3 * mg.e["n_steps"]), 1),
+                        "note": "guided step: conditional 950-token prompt + unconditional 750-frame window, "
+                                "cfg_scale 2.0"},
         "roofline": {"kernel": "decode_attn (split-sequence paged GQA attention)", "bound": "hbm",
                      "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
