@@ -387,6 +387,55 @@ def cfg_logits(cond: np.ndarray, uncond: np.ndarray, cfg_scale: float) -> np.nda
     return c + float(cfg_scale) * (c - as64(uncond))
 
 
+def gumbel(u: np.ndarray) -> np.ndarray:
+    """Standard Gumbel variate from a uniform in (0, 1): -log(-log u).  [OV-MG]
+    (gumbel_sample; the uniforms are the caller's, drawn from its Philox stream)."""
+    return -np.log(-np.log(as64(u)))
+
+
+def keep_top_k_ratio(lp: np.ndarray, ratio: float) -> np.ndarray:
+    """Keep the floor(ratio * V) (at least 1) largest entries of each row, ties to the lower
+    class id; the others become -inf.  [OV-MG] (keep_top_k_ratio(log_probs, 0.1))."""
+    lp = np.ascontiguousarray(as64(lp))
+    V = lp.shape[-1]
+    k = max(1, int(np.floor(ratio * V)))
+    out = np.full(lp.shape, -np.inf)  # C-contiguous, so the row view below writes into it
+    flat = lp.reshape(-1, V)
+    of = out.reshape(-1, V)
+    for r in range(flat.shape[0]):
+        order = sorted(range(V), key=lambda v: (-flat[r, v], v))  # larger first, then lower id
+        for v in order[:k]:
+            of[r, v] = flat[r, v]
+    return out
+
+
+def sample_scores(logits_flat: np.ndarray, codes_kt: np.ndarray, n_cb: int, cb_vocab: int, mask_id: int,
+                  layer_penalty: float, class_temp: float, pos_temp: float, top_k_ratio: float,
+                  u_class: Optional[np.ndarray], u_pos: Optional[np.ndarray]):
+    """Scoring with the sampler's temperatures.  [OV-MG], in the listing's order, each step
+    acting on the log-probs in place:
+      lp = log_softmax(logits) over all V classes; lp[mask] = -inf;
+      if class_temp > 0: lp = keep_top_k_ratio(lp, ratio); lp = lp / class_temp + G(u_class);
+      pred = argmax lp; score = max lp - k * layer_penalty;
+      if pos_temp > 0: score += pos_temp * G(u_pos);
+      score = -inf where the code is already set.
+    u_class [K][T][V] and u_pos [K][T] are uniforms in (0, 1); G(u) = -log(-log u)."""
+    T = logits_flat.shape[0]
+    lg = as64(logits_flat).reshape(T, n_cb, cb_vocab).transpose(1, 0, 2)
+    m = np.max(lg, axis=-1, keepdims=True)
+    lp = lg - (m + np.log(np.sum(np.exp(lg - m), axis=-1, keepdims=True)))
+    lp[:, :, mask_id] = -np.inf
+    if class_temp > 0:
+        lp = keep_top_k_ratio(lp, top_k_ratio)
+        lp = lp / class_temp + gumbel(u_class)  # -inf stays -inf
+    pred = np.argmax(lp, axis=-1).astype(np.int32)
+    score = np.max(lp, axis=-1) - np.arange(n_cb, dtype=F64)[:, None] * layer_penalty
+    if pos_temp > 0:
+        score = score + pos_temp * gumbel(u_pos)
+    score = np.where(np.asarray(codes_kt) == mask_id, score, -np.inf)
+    return pred, score, lp
+
+
 def unmask_schedule(n_total: int, n_steps: int) -> List[int]:
     """How many positions each step unmasks.  [OV-MG] gives the form
     ceil(N * (t[i+1] - t[i])) over a time grid; the grid used here is the cosine
@@ -456,4 +505,38 @@ def maskgit_pass_cfg(text_ids, text_table, codes_kt, n_target: int, audio_table,
     new_codes[:, w0:] = apply_picks(window, pred, picked)
     if record is not None:
         record.update(logits_c=lc, logits_u=lu, guided=guided, pred=pred, conf=conf, picked=picked)
+    return new_codes, pred, conf, picked
+
+
+def maskgit_step(text_ids, text_table, codes_kt, n_target: int, audio_table, audio_heads,
+                 layers: List[Layer], final_norm, dims: Dims, cb_vocab: int, mask_id: int,
+                 layer_penalty: float, n_unmask: int, cfg_scale: float = 0.0, class_temp: float = 0.0,
+                 pos_temp: float = 0.0, top_k_ratio: float = 0.1, u_class=None, u_pos=None,
+                 record: Optional[Dict] = None):
+    """One MaskGIT step in the general form of [OV-MG]: the conditional prompt (with an
+    unconditional pass on the target window and guided logits when cfg_scale != 0),
+    the sampler's scoring (temperatures, top-k ratio, Gumbel noise from the given
+    uniforms), top-n selection and the update of the window.  With cfg_scale = 0 the
+    unconditional pass is skipped (its weight is zero)."""
+    codes_kt = np.asarray(codes_kt, dtype=np.int32)
+    n_cb, n_frames = codes_kt.shape
+    n_text = len(text_ids)
+    w0 = n_frames - n_target
+    window = codes_kt[:, w0:]
+    xc = backbone_full(hybrid_embed(text_ids, text_table, codes_kt, audio_table, cb_vocab), layers, dims)
+    _, lc = head_logits(xc[n_text + w0:], final_norm, audio_heads, dims.eps)
+    lu = None
+    if cfg_scale != 0.0:
+        xu = backbone_full(codebook_embed(window.T, audio_table, cb_vocab), layers, dims)
+        _, lu = head_logits(xu, final_norm, audio_heads, dims.eps)
+        guided = cfg_logits(lc, lu, cfg_scale)
+    else:
+        guided = lc
+    pred, conf, lp = sample_scores(guided, window, n_cb, cb_vocab, mask_id, layer_penalty, class_temp, pos_temp,
+                                   top_k_ratio, u_class, u_pos)
+    picked = select_top(conf.reshape(-1), n_unmask)
+    new_codes = codes_kt.copy()
+    new_codes[:, w0:] = apply_picks(window, pred, picked)
+    if record is not None:
+        record.update(logits_c=lc, logits_u=lu, guided=guided, lp=lp, pred=pred, conf=conf, picked=picked)
     return new_codes, pred, conf, picked

@@ -528,3 +528,103 @@ def test_cfg_unconditional_prompt_is_the_window_alone():
     p_ref, c_ref, _ = O.maskgit_scores(rec["guided"], window, codes.shape[0], V, mask, 5.0)
     np.testing.assert_array_equal(p_ref, pred)
     np.testing.assert_array_equal(c_ref, conf)
+
+
+# ---------------------------------------------------------------------------
+# Sampler: temperatures, top-k ratio, Gumbel noise (the third NEXT row)
+# ---------------------------------------------------------------------------
+
+def test_gumbel_closed_form():
+    c = np.array([-3.0, -0.5, 0.0, 0.7, 4.0])
+    u = np.exp(-np.exp(-c))  # the Gumbel CDF: G(F(c)) = c
+    np.testing.assert_allclose(O.gumbel(u), c, rtol=1e-12, atol=1e-12)
+    assert O.gumbel(np.array([math.exp(-1.0)]))[0] == pytest.approx(0.0, abs=1e-15)
+    g = O.gumbel(np.linspace(0.01, 0.99, 50))
+    assert np.all(np.diff(g) > 0)
+
+
+def test_gumbel_max_draws_follow_the_tempered_softmax():
+    """Gumbel-max: argmax(lp / temp + G(u)) is distributed as softmax(lp / temp).  A wrong
+    sign, a multiplied temperature or log(u) in place of -log(-log u) fails this."""
+    rng = np.random.default_rng(31)
+    lp = np.log(np.array([0.5, 0.2, 0.15, 0.1, 0.05]))
+    temp, n = 0.7, 40000
+    u = rng.random((n, 5))
+    u = np.clip(u, 1e-12, 1 - 1e-12)
+    draws = np.argmax(lp / temp + O.gumbel(u), axis=1)
+    freq = np.bincount(draws, minlength=5) / n
+    p = np.exp(lp / temp)
+    p /= p.sum()
+    sigma = np.sqrt(p * (1 - p) / n)
+    assert np.all(np.abs(freq - p) < 5 * sigma + 1e-9)
+
+
+def test_keep_top_k_ratio_counts_and_ties():
+    rng = np.random.default_rng(32)
+    for _ in range(20):
+        V = int(rng.integers(1, 40))
+        ratio = float(rng.choice([0.1, 0.25, 0.5, 1.0, 0.01]))
+        row = rng.integers(-3, 3, V).astype(float)  # many ties
+        out = O.keep_top_k_ratio(row[None], ratio)[0]
+        k = max(1, math.floor(ratio * V))
+        kept = [v for v in range(V) if out[v] > -np.inf]
+        assert len(kept) == k
+        for v in range(V):  # rank by (value desc, id asc), counted directly
+            rank = sum(1 for w in range(V) if row[w] > row[v] or (row[w] == row[v] and w < v))
+            assert (v in kept) == (rank < k)
+            if v in kept:
+                assert out[v] == row[v]
+
+
+def test_sampler_reduces_to_greedy_scoring():
+    rng = np.random.default_rng(33)
+    K, T, V, mask = 2, 6, 9, 8
+    lg = rng.standard_normal((T, K * V)) * 2
+    codes = np.full((K, T), mask)
+    codes[0, 1] = 3
+    p0, c0, _ = O.maskgit_scores(lg, codes, K, V, mask, 5.0)
+    p1, c1, _ = O.sample_scores(lg, codes, K, V, mask, 5.0, 0.0, 0.0, 0.1, None, None)
+    np.testing.assert_array_equal(p0, p1)
+    np.testing.assert_array_equal(c0, c1)
+    # zero noise (u = 1/e) and ratio 1: temperature 1 changes nothing either
+    u_c = np.full((K, T, V), math.exp(-1.0))
+    p2, c2, _ = O.sample_scores(lg, codes, K, V, mask, 5.0, 1.0, 0.0, 1.0, u_c, None)
+    np.testing.assert_array_equal(p0, p2)
+    np.testing.assert_allclose(c0, c2, rtol=1e-12, atol=1e-12)
+    # position noise shifts every masked score by pos_temp * G(u_pos), nothing else
+    u_p = rng.random((K, T)) * 0.98 + 0.01
+    p3, c3, _ = O.sample_scores(lg, codes, K, V, mask, 5.0, 0.0, 0.3, 0.1, None, u_p)
+    np.testing.assert_array_equal(p0, p3)
+    fin = np.isfinite(c0)
+    np.testing.assert_allclose(c3[fin] - c0[fin], 0.3 * O.gumbel(u_p)[fin], rtol=1e-12, atol=1e-12)
+    assert np.array_equal(np.isfinite(c3), fin)
+
+
+def test_sampler_picks_inside_the_kept_classes():
+    """With class noise the choice is always one of the top floor(ratio * V) non-mask
+    classes, never the mask class."""
+    rng = np.random.default_rng(34)
+    K, T, V, mask = 2, 40, 50, 49
+    lg = rng.standard_normal((T, K * V)) * 2
+    codes = np.full((K, T), mask)
+    u_c = rng.random((K, T, V)) * 0.999 + 0.0005
+    pred, conf, lp = O.sample_scores(lg, codes, K, V, mask, 5.0, 1.3, 0.0, 0.1, u_c, None)
+    base, _, lp0 = O.maskgit_scores(lg, codes, K, V, mask, 5.0)
+    for k in range(K):
+        for t in range(T):
+            order = sorted(range(V), key=lambda v: (-lp0[k, t, v], v))[:5]  # floor(0.1 * 50)
+            assert pred[k, t] in order and pred[k, t] != mask
+
+
+def test_general_step_reduces_to_the_plain_and_guided_steps():
+    rng = np.random.default_rng(35)
+    dims, layers, text_tab, tab, heads, fnorm, text, codes, V, mask = _cfg_setup(rng)
+    nf = codes.shape[1]
+    a = O.maskgit_pass(text, text_tab, codes, tab, heads, layers, fnorm, dims, V, mask, 5.0, 3)
+    b = O.maskgit_step(text, text_tab, codes, nf, tab, heads, layers, fnorm, dims, V, mask, 5.0, 3)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+    c = O.maskgit_pass_cfg(text, text_tab, codes, 4, tab, heads, layers, fnorm, dims, V, mask, 5.0, 3, 1.5)
+    d = O.maskgit_step(text, text_tab, codes, 4, tab, heads, layers, fnorm, dims, V, mask, 5.0, 3, cfg_scale=1.5)
+    for x, y in zip(c, d):
+        np.testing.assert_array_equal(x, y)
