@@ -90,6 +90,112 @@ void launch_maskgit_scores(const float *logits, const float *logits_u, float cfg
                        T, ld, n_cb, V, mask_id, penalty, codes, codes_ld, pred, conf);
 }
 
+// ------------------------------------------------------------------------------------
+// K8 with the sampler (same page, "MaskGIT decoder": keep_top_k_ratio(log_probs, 0.1),
+// gumbel_sample(temp = class_temp), score += gumbel * pos_temp; the uniforms of the
+// Gumbel noise are the caller's).  One wave per (codebook, frame); the group's V log-probs
+// are kept in LDS (V <= SAMPLE_MAXV).  The top-k threshold is the k-th largest log-prob,
+// found by a bisection on the order-preserving integer image of the floats (counts by
+// wave reductions); ties at the threshold are kept in class order (ballot prefix counts).
+// Then lp' = lp / class_temp + G(u) on the kept classes (-inf elsewhere), pred = argmax
+// lp' (ties: lowest id), score = max lp' - k * penalty + pos_temp * G(u_pos), with
+// G(u) = -log(-log u).
+// ------------------------------------------------------------------------------------
+constexpr int SAMPLE_MAXV = 2048;
+
+// order-preserving map float -> int32 (signed comparison), -inf lowest
+__device__ __forceinline__ int fkey(float f) {
+    const int i = __float_as_int(f);
+    return i >= 0 ? i : i ^ 0x7FFFFFFF;
+}
+
+__device__ __forceinline__ float gumbel_f(float u) { return -logf(-logf(u)); }
+
+__global__ __launch_bounds__(256) void maskgit_sample_kernel(const float *logits, const float *logits_u,
+                                                             float cfg_scale, int T, int ld, int n_cb, int V,
+                                                             int mask_id, float penalty, const int32_t *codes,
+                                                             int codes_ld, float class_temp, float pos_temp,
+                                                             int k_keep, const float *u_class, const float *u_pos,
+                                                             int32_t *pred, float *conf) {
+    __shared__ float lps[4][SAMPLE_MAXV];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int item = blockIdx.x * 4 + wave;  // flat index k*T + t
+    if (item >= n_cb * T) return;
+    const int k = item / T, t = item % T;
+    const float *x = logits + (int64_t)t * ld + (int64_t)k * V;
+    const float *xu = logits_u ? logits_u + (int64_t)t * ld + (int64_t)k * V : nullptr;
+    float *lp = lps[wave];
+    float mx = -INFINITY;
+    for (int v = lane; v < V; v += 64) {
+        const float c = x[v];
+        const float g = xu ? c + cfg_scale * (c - xu[v]) : c;
+        lp[v] = g;
+        mx = fmaxf(mx, g);
+    }
+    mx = wave_max(mx);
+    float se = 0.f;
+    for (int v = lane; v < V; v += 64) se += expf(lp[v] - mx);
+    se = wave_sum(se);
+    const float lse = mx + logf(se);
+    for (int v = lane; v < V; v += 64) lp[v] = v == mask_id ? -INFINITY : lp[v] - lse;  // own entries only
+
+    const float *u = u_class + (int64_t)item * V;
+    float best = -INFINITY;
+    int bi = 0x7FFFFFFF;
+    if (class_temp > 0.f) {
+        // largest key K with #{v : key(lp_v) >= K} >= k_keep (bisection on [lo, hi])
+        int64_t lo = INT32_MIN, hi = INT32_MAX;
+        while (lo < hi) {
+            const int64_t mid = lo + (hi - lo + 1) / 2;
+            int cnt = 0;
+            for (int v = lane; v < V; v += 64) cnt += (int64_t)fkey(lp[v]) >= mid;
+            cnt = (int)wave_sum((float)cnt);
+            if (cnt >= k_keep) lo = mid;
+            else hi = mid - 1;
+        }
+        const int th = (int)lo;
+        int gt = 0;
+        for (int v = lane; v < V; v += 64) gt += fkey(lp[v]) > th;
+        gt = (int)wave_sum((float)gt);
+        const int need = k_keep - gt;  // ties at the threshold kept, lowest class ids first
+        int carry = 0;
+        for (int v0 = 0; v0 < V; v0 += 64) {
+            const int v = v0 + lane;
+            const bool in = v < V;
+            const int key = in ? fkey(lp[v]) : INT32_MIN;
+            const bool eq = in && key == th;
+            const uint64_t bal = __ballot(eq);
+            const int below = __popcll(bal & ((1ull << lane) - 1ull));
+            const bool keep = in && (key > th || (eq && carry + below < need));
+            carry += __popcll(bal);
+            if (in) {
+                const float val = keep ? lp[v] / class_temp + gumbel_f(u[v]) : -INFINITY;
+                argmax_merge(best, bi, val, v);
+            }
+        }
+    } else {
+        for (int v = lane; v < V; v += 64) argmax_merge(best, bi, lp[v], v);
+    }
+    wave_argmax(best, bi);
+    if (lane == 0) {
+        float sc = best - (float)k * penalty;
+        if (pos_temp > 0.f) sc += pos_temp * gumbel_f(u_pos[item]);
+        pred[item] = bi;
+        conf[item] = (codes[(int64_t)k * codes_ld + t] == mask_id) ? sc : -INFINITY;
+    }
+}
+
+void launch_maskgit_sample(const float *logits, const float *logits_u, float cfg_scale, int T, int ld, int n_cb,
+                           int V, int mask_id, float penalty, const int32_t *codes, int codes_ld, float class_temp,
+                           float pos_temp, int k_keep, const float *u_class, const float *u_pos, int32_t *pred,
+                           float *conf, hipStream_t s) {
+    const int items = n_cb * T;
+    if (items <= 0) return;
+    hipLaunchKernelGGL(maskgit_sample_kernel, dim3((items + 3) / 4), dim3(256), 0, s, logits, logits_u, cfg_scale,
+                       T, ld, n_cb, V, mask_id, penalty, codes, codes_ld, class_temp, pos_temp, k_keep, u_class,
+                       u_pos, pred, conf);
+}
+
 constexpr int SEL_TILE = 1024;  // scores staged in LDS per block
 
 __global__ void zero_i32_kernel(int32_t *v, int n) {

@@ -131,6 +131,14 @@ void launch_maskgit_scores(const float *logits, const float *logits_u, float cfg
                            int n_cb, int V, int mask_id, float penalty, const int32_t *codes, int codes_ld,
                            int32_t *pred, float *conf, hipStream_t s);
 
+// With the sampler: class_temp > 0 keeps the k_keep best log-probs of each group and
+// adds Gumbel noise from u_class [n_cb][T][V]; pos_temp > 0 adds noise from u_pos
+// [n_cb][T] to the score.  V <= SAMPLE_MAXV (2048).
+void launch_maskgit_sample(const float *logits, const float *logits_u, float cfg_scale, int T, int ld, int n_cb,
+                           int V, int mask_id, float penalty, const int32_t *codes, int codes_ld, float class_temp,
+                           float pos_temp, int k_keep, const float *u_class, const float *u_pos, int32_t *pred,
+                           float *conf, hipStream_t s);
+
 // ---- K9: top-n selection by rank + code update -------------------------------------
 // rank: int32 scratch [n]
 // Top-n over conf [n_cb][T] (flat k*T + t); picked codes go to codes[k*codes_ld + t].

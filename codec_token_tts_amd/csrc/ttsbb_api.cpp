@@ -15,6 +15,7 @@
 #include <string.h>
 
 #include <new>
+#include <algorithm>
 #include <vector>
 
 #include "../../include/ttsbb.h"
@@ -765,6 +766,64 @@ TTSBB_API ttsbb_status ttsbb_maskgit_pass_cfg(ttsbb_ctx *ctx, int32_t n_text, co
     {
         KScope k(ctx, TTSBB_K_SELECT);
         launch_select_update(conf, pred, n_cb, n_target, n_unmask, ctx->rank, window, n_frames, picked, ctx->stream);
+    }
+    return launch_failed() ? TTSBB_DEVICE_ERROR : TTSBB_OK;
+}
+
+TTSBB_API ttsbb_status ttsbb_maskgit_step(ttsbb_ctx *ctx, const ttsbb_maskgit_step_args *a) {
+    if (!ctx || !a) return TTSBB_INVALID_ARG;
+    const ttsbb_config &g = ctx->cfg;
+    ctx->pend_splits = 0;
+    const int n_text = a->n_text, n_frames = a->n_frames, n_target = a->n_target, n_cb = a->n_cb;
+    const int cb_vocab = a->cb_vocab, mask_id = a->mask_id, n_unmask = a->n_unmask;
+    if (n_text < 0 || n_frames <= 0 || n_target <= 0 || n_target > n_frames || n_cb <= 0 || cb_vocab <= 0 ||
+        mask_id < 0 || mask_id >= cb_vocab || n_unmask < 0 || (int64_t)n_unmask > (int64_t)n_cb * n_target)
+        return TTSBB_INVALID_ARG;
+    if ((int64_t)n_text + n_frames > g.max_rows || (int64_t)n_text + n_frames > g.max_pos) return TTSBB_INVALID_ARG;
+    if ((int64_t)n_cb * cb_vocab > g.max_head_cols) return TTSBB_INVALID_ARG;
+    if ((int64_t)n_cb * n_target > ctx->rank_cap) return TTSBB_INVALID_ARG;
+    if (n_text > 0 && (!a->text_ids || !a->text_table || a->text_vocab <= 0)) return TTSBB_INVALID_ARG;
+    if (!a->audio_tables || !a->audio_heads || !a->codes || !a->pred || !a->conf || (n_unmask > 0 && !a->picked) ||
+        !ctx->final_norm)
+        return TTSBB_INVALID_ARG;
+    const float temps[5] = {a->layer_penalty, a->cfg_scale, a->class_temp, a->pos_temp, a->top_k_ratio};
+    for (float v : temps)
+        if (!(v == v)) return TTSBB_INVALID_ARG;
+    if (a->class_temp < 0.f || a->pos_temp < 0.f) return TTSBB_INVALID_ARG;
+    if (a->class_temp > 0.f && (!a->u_class || !(a->top_k_ratio > 0.f) || cb_vocab > 2048)) return TTSBB_INVALID_ARG;
+    if (a->pos_temp > 0.f && !a->u_pos) return TTSBB_INVALID_ARG;
+    if (ctx->dt != DT_BF16) return TTSBB_UNSUPPORTED;
+
+    const int S = n_text + n_frames, w0 = n_frames - n_target;
+    const int N = n_cb * cb_vocab;
+    int32_t *window = a->codes + w0;
+    maskgit_embed(ctx, S, n_text, a->text_ids, a->text_table, a->text_vocab, n_cb, cb_vocab, a->audio_tables,
+                  a->codes, n_frames);
+    maskgit_backbone(ctx, S, n_text + w0, n_target, a->audio_heads, N, ctx->logits, true);
+    if (ctx->tap_layer >= 0) tap_dense(ctx, TTSBB_TAP_LOGITS, ctx->logits, DT_F32, n_target, N, N);
+    const float *lu = nullptr;
+    if (a->cfg_scale != 0.f) {
+        maskgit_embed(ctx, n_target, 0, nullptr, nullptr, 0, n_cb, cb_vocab, a->audio_tables, window, n_frames);
+        maskgit_backbone(ctx, n_target, 0, n_target, a->audio_heads, N, ctx->logits_u, false);
+        if (ctx->tap_layer >= 0) tap_dense(ctx, TTSBB_TAP_LOGITS_U, ctx->logits_u, DT_F32, n_target, N, N);
+        lu = ctx->logits_u;
+    }
+    {
+        KScope k(ctx, TTSBB_K_SCORES);
+        if (a->class_temp > 0.f || a->pos_temp > 0.f) {
+            const int k_keep = std::max(1, (int)floor((double)a->top_k_ratio * cb_vocab));
+            launch_maskgit_sample(ctx->logits, lu, a->cfg_scale, n_target, N, n_cb, cb_vocab, mask_id,
+                                  a->layer_penalty, window, n_frames, a->class_temp, a->pos_temp, k_keep, a->u_class,
+                                  a->u_pos, a->pred, a->conf, ctx->stream);
+        } else {
+            launch_maskgit_scores(ctx->logits, lu, a->cfg_scale, n_target, N, n_cb, cb_vocab, mask_id,
+                                  a->layer_penalty, window, n_frames, a->pred, a->conf, ctx->stream);
+        }
+    }
+    {
+        KScope k(ctx, TTSBB_K_SELECT);
+        launch_select_update(a->conf, a->pred, n_cb, n_target, n_unmask, ctx->rank, window, n_frames, a->picked,
+                             ctx->stream);
     }
     return launch_failed() ? TTSBB_DEVICE_ERROR : TTSBB_OK;
 }

@@ -22,7 +22,7 @@ F32, BF16 = 0, 1
 
 EXPORTS = ["ttsbb_default_config", "ttsbb_create", "ttsbb_destroy", "ttsbb_status_str",
            "ttsbb_sync", "ttsbb_codebook_embed", "ttsbb_decode_step", "ttsbb_maskgit_pass",
-           "ttsbb_maskgit_pass_cfg", "ttsbb_unmask_schedule", "ttsbb_set_tap_layer", "ttsbb_read_tap", "ttsbb_profile_start",
+           "ttsbb_maskgit_pass_cfg", "ttsbb_maskgit_step", "ttsbb_unmask_schedule", "ttsbb_set_tap_layer", "ttsbb_read_tap", "ttsbb_profile_start",
            "ttsbb_profile_stop"]
 
 (K_EMBED, K_RMSNORM, K_GEMM_QKV, K_ROPE_KV, K_DECODE_ATTN, K_DECODE_COMBINE, K_FLASH_ATTN, K_GEMM_O,
@@ -30,6 +30,17 @@ EXPORTS = ["ttsbb_default_config", "ttsbb_create", "ttsbb_destroy", "ttsbb_statu
 K_COUNT = 14
 K_NAMES = ["embed", "rmsnorm", "gemm_qkv", "rope_kv", "decode_attn", "decode_combine", "flash_attn",
            "gemm_o", "gemm_gate_up", "gemm_down", "gemm_head", "argmax", "scores", "select"]
+
+
+class ttsbb_maskgit_step_args(C.Structure):
+    _fields_ = [("n_text", C.c_int32), ("text_ids", C.c_void_p), ("text_table", C.c_void_p),
+                ("text_vocab", C.c_int32), ("n_frames", C.c_int32), ("n_target", C.c_int32),
+                ("n_cb", C.c_int32), ("cb_vocab", C.c_int32), ("mask_id", C.c_int32),
+                ("audio_tables", C.c_void_p), ("audio_heads", C.c_void_p), ("codes", C.c_void_p),
+                ("n_unmask", C.c_int32), ("layer_penalty", C.c_float), ("cfg_scale", C.c_float),
+                ("class_temp", C.c_float), ("pos_temp", C.c_float), ("top_k_ratio", C.c_float),
+                ("u_class", C.c_void_p), ("u_pos", C.c_void_p), ("pred", C.c_void_p), ("conf", C.c_void_p),
+                ("picked", C.c_void_p)]
 
 
 class TtsbbError(RuntimeError):
@@ -77,6 +88,7 @@ def lib() -> C.CDLL:
                                      vp, vp, vp]),
         "ttsbb_maskgit_pass_cfg": (i32, [vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp, i32, f32,
                                          f32, vp, vp, vp]),
+        "ttsbb_maskgit_step": (i32, [vp, C.POINTER(ttsbb_maskgit_step_args)]),
         "ttsbb_unmask_schedule": (i32, [i32, i32, C.POINTER(i32)]),
         "ttsbb_set_tap_layer": (i32, [vp, i32]),
         "ttsbb_read_tap": (i32, [vp, i32, vp, i64, C.POINTER(i32), C.POINTER(i32)]),
@@ -194,6 +206,20 @@ def ttsbb_maskgit_pass_cfg(ctx, n_text, text_ids, text_table, text_vocab, n_fram
                                       float(cfg_scale), ptr(pred), ptr(conf), ptr(picked))
     if check:
         _check(st, "ttsbb_maskgit_pass_cfg")
+    return st
+
+
+def ttsbb_maskgit_step(ctx, n_text, text_ids, text_table, text_vocab, n_frames, n_target, n_cb, cb_vocab,
+                       mask_id, audio_tables, audio_heads, codes, n_unmask, layer_penalty, pred, conf, picked,
+                       cfg_scale=0.0, class_temp=0.0, pos_temp=0.0, top_k_ratio=0.1, u_class=None, u_pos=None,
+                       check: bool = True) -> int:
+    a = ttsbb_maskgit_step_args(n_text, ptr(text_ids), ptr(text_table), text_vocab, n_frames, n_target, n_cb,
+                                cb_vocab, mask_id, ptr(audio_tables), ptr(audio_heads), ptr(codes), n_unmask,
+                                float(layer_penalty), float(cfg_scale), float(class_temp), float(pos_temp),
+                                float(top_k_ratio), ptr(u_class), ptr(u_pos), ptr(pred), ptr(conf), ptr(picked))
+    st = lib().ttsbb_maskgit_step(ctx, C.byref(a))
+    if check:
+        _check(st, "ttsbb_maskgit_step")
     return st
 
 

@@ -178,6 +178,46 @@ ttsbb_status ttsbb_maskgit_pass_cfg(ttsbb_ctx *ctx, int32_t n_text, const int32_
                                     int32_t n_unmask, float layer_penalty, float cfg_scale, int32_t *pred,
                                     float *conf, int32_t *picked);
 
+/* Arguments of the general MaskGIT step: those of ttsbb_maskgit_pass_cfg plus the
+ * sampler (OmniVoice ARCHITECTURE, "MaskGIT decoder": keep_top_k_ratio, gumbel_sample with
+ * the class temperature, Gumbel noise on the scores with the position temperature).  The
+ * uniforms of the Gumbel noise are inputs, so the step is a pure function of its
+ * arguments: the caller draws them from its counter-based stream (the page threads a
+ * Philox4x32-10 counter across calls). */
+typedef struct {
+    int32_t n_text;
+    const int32_t *text_ids;     /* int32 [n_text] */
+    const void *text_table;      /* [text_vocab][hidden] */
+    int32_t text_vocab;
+    int32_t n_frames, n_target;  /* audio frames; the last n_target are the target window */
+    int32_t n_cb, cb_vocab, mask_id;
+    const void *audio_tables, *audio_heads; /* [n_cb*cb_vocab][hidden] */
+    int32_t *codes;              /* int32 [n_cb][n_frames], in/out (window only changes) */
+    int32_t n_unmask;
+    float layer_penalty;
+    float cfg_scale;             /* 0: no unconditional pass */
+    float class_temp;            /* > 0: top-k ratio filter + Gumbel noise on the classes */
+    float pos_temp;              /* > 0: Gumbel noise on the scores */
+    float top_k_ratio;           /* keeps max(1, floor(top_k_ratio * cb_vocab)) classes */
+    const float *u_class;        /* fp32 [n_cb][n_target][cb_vocab] in (0,1); class_temp > 0 */
+    const float *u_pos;          /* fp32 [n_cb][n_target] in (0,1); pos_temp > 0 */
+    int32_t *pred;               /* int32 [n_cb][n_target] */
+    float *conf;                 /* fp32 [n_cb][n_target] */
+    int32_t *picked;             /* int32 [n_unmask], flat window indices or -1 */
+} ttsbb_maskgit_step_args;
+
+/* One MaskGIT step in general form: the passes of ttsbb_maskgit_pass_cfg (one pass when
+ * cfg_scale == 0), g = c + cfg_scale * (c - u), then on the window
+ *   lp   = g - logsumexp(g) over the cb_vocab classes; lp[mask_id] = -inf
+ *   if class_temp > 0: keep the max(1, floor(top_k_ratio * cb_vocab)) largest lp (ties:
+ *                      lowest id; the others -inf), lp = lp / class_temp + G(u_class)
+ *   pred = argmax lp (ties: lowest id); conf = max lp - k * layer_penalty
+ *   if pos_temp > 0:   conf += pos_temp * G(u_pos)
+ *   conf = -inf where the code is already set
+ * with G(u) = -log(-log(u)), and the top-n update of ttsbb_maskgit_pass_cfg.  All
+ * pointers are device memory; cb_vocab <= 2048 when class_temp > 0. */
+ttsbb_status ttsbb_maskgit_step(ttsbb_ctx *ctx, const ttsbb_maskgit_step_args *args);
+
 /* Host helper: how many positions each of n_steps MaskGIT steps unmasks (OmniVoice
  * ARCHITECTURE, "MaskGIT decoder": ceil(N * (t[i+1] - t[i])) over a time grid), on the
  * cosine grid t_i = 1 - cos(pi/2 * i/n_steps); each count is capped at what is left and

@@ -48,6 +48,11 @@ int main(void) {
                               NULL) == TTSBB_INVALID_ARG);
     EXPECT(ttsbb_maskgit_pass_cfg(NULL, 0, NULL, NULL, 0, 4, 2, 1, 2, 1, NULL, NULL, NULL, 0, 5.0f, 2.0f, NULL,
                                   NULL, NULL) == TTSBB_INVALID_ARG);
+    {
+        ttsbb_maskgit_step_args sa;
+        memset(&sa, 0, sizeof sa);
+        EXPECT(ttsbb_maskgit_step(NULL, &sa) == TTSBB_INVALID_ARG);
+    }
     EXPECT(ttsbb_set_tap_layer(NULL, 0) == TTSBB_INVALID_ARG);
     EXPECT(ttsbb_read_tap(NULL, 0, &dummy, 1, NULL, NULL) == TTSBB_INVALID_ARG);
     EXPECT(ttsbb_profile_start(NULL, 1u, 16) == TTSBB_INVALID_ARG);

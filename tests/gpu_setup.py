@@ -154,3 +154,55 @@ def check_topn(picked: np.ndarray, conf_gpu: np.ndarray, conf_ref: np.ndarray, n
     assert all(int(i) in sel for i in must), "a clearly winning position was not picked"
     assert all(cr[i] >= thr - 2 * eps for i in sel), "a clearly losing position was picked"
     return int(np.count_nonzero(fin & (np.abs(cr - thr) <= 2 * eps)))
+
+
+def check_sampler(gpu_pred, gpu_conf, guided_gpu, guided_ref, window, n_cb, V, mask_id, penalty, class_temp,
+                  pos_temp, ratio, u_class, u_pos, eps=2e-3):
+    """Discrete parity of the sampler's choices, in two stages.
+
+    1. GPU against an fp64 emulation of the same scoring on the GPU's own guided logits
+       (same uniforms): equal choices except where the emulation has a near tie (within
+       eps) or the chosen class sits within eps of the top-k threshold; equal scores to
+       eps where the choices agree (the difference is fp32 arithmetic).
+    2. The emulation against the oracle (guided_ref): equal choices wherever the oracle's
+       margin exceeds twice the perturbed-value error, else the choice is within that
+       margin of the oracle's best or at the threshold boundary.
+    Returns (stage-1 exceptions, stage-2 exceptions)."""
+    T = guided_gpu.shape[0]
+    pe, ce, lpe = O.sample_scores(guided_gpu, window, n_cb, V, mask_id, penalty, class_temp, pos_temp, ratio,
+                                  u_class, u_pos)
+    pr, cr, lpr = O.sample_scores(guided_ref, window, n_cb, V, mask_id, penalty, class_temp, pos_temp, ratio,
+                                  u_class, u_pos)
+    _, _, lp0e = O.maskgit_scores(guided_gpu, window, n_cb, V, mask_id, penalty)
+    _, _, lp0r = O.maskgit_scores(guided_ref, window, n_cb, V, mask_id, penalty)
+    k_keep = max(1, int(np.floor(ratio * V)))
+    thr_e = -np.sort(-lp0e, axis=-1)[..., k_keep - 1] if class_temp > 0 else None
+    thr_r = -np.sort(-lp0r, axis=-1)[..., k_keep - 1] if class_temp > 0 else None
+    gp = np.asarray(gpu_pred)
+    ex1 = ex2 = 0
+    both = np.isfinite(lpe) & np.isfinite(lpr)
+    dl = float(np.max(np.abs(lpe[both] - lpr[both]))) if both.any() else 0.0
+    fin0 = np.isfinite(lp0e) & np.isfinite(lp0r)
+    d0 = float(np.max(np.abs(lp0e[fin0] - lp0r[fin0]))) if fin0.any() else 0.0
+    for k in range(n_cb):
+        for t in range(T):
+            if gp[k, t] != pe[k, t]:
+                # a near tie of the perturbed values, or either choice at the top-k edge
+                # (kept on one side, dropped on the other)
+                c, e = gp[k, t], pe[k, t]
+                near = lpe[k, t, c] >= np.max(lpe[k, t]) - eps
+                edge = class_temp > 0 and min(abs(lp0e[k, t, c] - thr_e[k, t]),
+                                              abs(lp0e[k, t, e] - thr_e[k, t])) <= eps
+                assert near or edge, "GPU choice differs from the emulation without a tie (%d, %d)" % (k, t)
+                ex1 += 1
+            elif np.isfinite(ce[k, t]):
+                assert abs(float(gpu_conf[k, t]) - ce[k, t]) <= eps * (1 + abs(ce[k, t])), (k, t)
+            if pe[k, t] != pr[k, t]:
+                c, r = pe[k, t], pr[k, t]
+                near = lpr[k, t, c] >= np.max(lpr[k, t]) - 2 * dl - 1e-9
+                edge = class_temp > 0 and min(abs(lp0r[k, t, c] - thr_r[k, t]),
+                                              abs(lp0r[k, t, r] - thr_r[k, t])) <= 2 * d0 + 1e-9
+                assert near or edge, "emulated choice differs from the oracle's beyond the margin (%d, %d)" % (k, t)
+                ex2 += 1
+    assert np.array_equal(np.isfinite(np.asarray(gpu_conf)), np.isfinite(cr))
+    return ex1, ex2

@@ -17,7 +17,7 @@ from workload import device as DEV
 from workload import gen
 from workload.gen import stream_id
 
-from gpu_setup import (TOL_LAYER_BF16, Model, check_argmax_groups, check_topn, dims_of, normwise, read_tap,
+from gpu_setup import (TOL_LAYER_BF16, Model, check_argmax_groups, check_sampler, check_topn, dims_of, normwise, read_tap,
                        torch, widen)
 
 pytestmark = pytest.mark.gpu
@@ -430,5 +430,64 @@ def test_maskgit_cfg_without_context_is_the_plain_step():
         for o in outs[1:]:
             for a, b in zip(outs[0], o):
                 np.testing.assert_array_equal(a, b)
+    finally:
+        m.close()
+
+
+@pytest.mark.parametrize("n_text,n_frames,n_target,cfg_scale,class_temp,pos_temp",
+                         [(13, 57, 40, 0.0, 1.0, 0.0), (13, 57, 40, 2.0, 0.7, 0.5), (70, 130, 100, 3.0, 1.5, 1.0),
+                          (0, 45, 45, 0.0, 0.0, 2.0)])
+def test_maskgit_step_sampler(n_text, n_frames, n_target, cfg_scale, class_temp, pos_temp):
+    """The general step with the sampler: top-k ratio filter, class temperature with
+    Gumbel noise and position noise from given uniforms, with and without guidance;
+    choices and scores in two-stage discrete parity (GPU vs an fp64 emulation on its own
+    logits, emulation vs the oracle), picks, and the window update."""
+    m = Model(CFG.Shape(n_layers=2), 2, True, seed=12, gains="random")
+    try:
+        T = m.T
+        shape = m.shape
+        n_cb, V, mask, n_unmask, ratio, seed, tv = 3, 33, 32, 25, 0.25, 12, 500
+        text_h = CFG.table(seed, gen.KIND_TEXT_TABLE, 0, tv, shape.hidden, True)
+        tab_h = CFG.table(seed, gen.KIND_CB_TABLE, 0, n_cb * V, shape.hidden, True)
+        head_h = CFG.table(seed, gen.KIND_HEAD, 0, n_cb * V, shape.hidden, True)
+        text_ids = gen.uniform_int(seed, stream_id(gen.KIND_TEXT_IDS, 0), (n_text,), tv)
+        codes = gen.uniform_int(seed, stream_id(gen.KIND_CODES, 0), (n_cb, n_frames), V - 1)
+        w0 = n_frames - n_target
+        win = codes[:, w0:].copy()
+        win[:, ::2] = mask
+        win[1, 1::4] = mask
+        codes[:, w0:] = win
+        u_class = gen.uniform_open01(seed, stream_id(gen.KIND_U_CLASS, 0), (n_cb, n_target, V))
+        u_pos = gen.uniform_open01(seed, stream_id(gen.KIND_U_POS, 0), (n_cb, n_target))
+        codes_d = t_i32(codes)
+        pred = torch().empty((n_cb, n_target), dtype=torch().int32, device="cuda")
+        conf = torch().empty((n_cb, n_target), dtype=torch().float32, device="cuda")
+        picked = torch().empty(n_unmask, dtype=torch().int32, device="cuda")
+        T.ttsbb_set_tap_layer(m.ctx, 0)
+        T.ttsbb_maskgit_step(m.ctx, n_text, t_i32(text_ids), DEV.host_to_device(text_h), tv, n_frames, n_target,
+                             n_cb, V, mask, DEV.host_to_device(tab_h), DEV.host_to_device(head_h), codes_d, n_unmask,
+                             5.0, pred, conf, picked, cfg_scale=cfg_scale, class_temp=class_temp, pos_temp=pos_temp,
+                             top_k_ratio=ratio, u_class=t_f32(u_class), u_pos=t_f32(u_pos))
+        assert T.ttsbb_sync(m.ctx) == T.OK
+        lc = read_tap(m, T.TAP_LOGITS, n_target, n_cb * V)
+        guided_gpu = O.cfg_logits(lc, read_tap(m, T.TAP_LOGITS_U, n_target, n_cb * V), cfg_scale) \
+            if cfg_scale != 0 else lc
+        T.ttsbb_set_tap_layer(m.ctx, -1)
+        res_codes, res_pred, res_conf = codes_d.cpu().numpy(), pred.cpu().numpy(), conf.cpu().numpy()
+        res_picked = picked.cpu().numpy()
+        rec = {}
+        O.maskgit_step(text_ids, widen(text_h), codes, n_target, widen(tab_h), widen(head_h), m.oracle_layers(),
+                       m.oracle_final_norm(), dims_of(shape), V, mask, 5.0, n_unmask, cfg_scale, class_temp,
+                       pos_temp, ratio, u_class.astype(np.float64), u_pos.astype(np.float64), record=rec)
+        assert normwise(guided_gpu, rec["guided"]) <= 3 * TOL_LAYER_BF16 * (1 + abs(cfg_scale))
+        ex1, ex2 = check_sampler(res_pred, res_conf, guided_gpu, rec["guided"], win, n_cb, V, mask, 5.0,
+                                 class_temp, pos_temp, ratio, u_class.astype(np.float64),
+                                 u_pos.astype(np.float64))
+        # explained exceptions stay rare (fp32 vs fp64 ties; bf16 logit error at the edges)
+        assert ex1 <= 2 and ex2 <= max(3, n_cb * n_target // 20), (ex1, ex2)
+        # picks: exactly the top-n of the GPU's own scores; the update touches the window only
+        check_topn(res_picked, res_conf, res_conf, n_unmask)
+        np.testing.assert_array_equal(res_codes[:, :w0], codes[:, :w0])
+        np.testing.assert_array_equal(res_codes[:, w0:], O.apply_picks(win, res_pred, res_picked))
     finally:
         m.close()

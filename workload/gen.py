@@ -56,6 +56,8 @@ KIND_TEXT_IDS = 20
 KIND_LENGTHS = 21
 KIND_PAGE_PERM = 22
 KIND_MASK_PERM = 23
+KIND_U_CLASS = 24   # uniforms of the sampler's class noise
+KIND_U_POS = 25     # uniforms of the sampler's position noise
 
 
 def stream_id(kind: int, index: int = 0) -> int:
@@ -136,6 +138,14 @@ def uniform_int(seed: int, stream: int, shape, n: int, start: int = 0) -> np.nda
     cnt = int(np.prod(shape)) if len(shape) else 1
     w = words_range(seed, stream, start, cnt).astype(np.uint64)
     return ((w * np.uint64(n)) >> np.uint64(32)).astype(np.int32).reshape(shape)
+
+
+def uniform_open01(seed: int, stream: int, shape, start: int = 0) -> np.ndarray:
+    """fp32 uniforms strictly inside (0, 1): ((w >> 8) + 0.5) * 2^-24 of one word each
+    (exactly representable in fp32; never 0 or 1)."""
+    n = int(np.prod(shape))
+    w = fast_words(seed, stream, start, n).astype(np.uint64)
+    return (((w >> np.uint64(8)).astype(np.float64) + 0.5) * 2.0 ** -24).astype(np.float32).reshape(shape)
 
 
 def permutation(seed: int, stream: int, n: int) -> np.ndarray:
