@@ -142,6 +142,25 @@ class MaskgitC4:
                                       self.tables, self.heads, self.codes, self.sched[i], e["layer_penalty"],
                                       cfg_scale, self.pred, self.conf, self.picked)
 
+    def step_sampled(self, s, cfg_scale=2.0, class_temp=1.0, pos_temp=1.0):
+        """The general step: guidance plus the sampler (top-k ratio 0.1, class and
+        position temperatures); the Gumbel uniforms are resident inputs."""
+        e = self.e
+        i = s % e["n_steps"]
+        if i == 0:
+            self.codes.copy_(self.codes0)
+        if not hasattr(self, "u_class"):
+            from workload import gen
+            self.u_class = self.torch.from_numpy(gen.uniform_open01(
+                3, gen.stream_id(gen.KIND_U_CLASS, 0), (e["n_cb"], e["n_frames"], e["cb_vocab"]))).cuda()
+            self.u_pos = self.torch.from_numpy(gen.uniform_open01(
+                3, gen.stream_id(gen.KIND_U_POS, 0), (e["n_cb"], e["n_frames"]))).cuda()
+        self.T.ttsbb_maskgit_step(self.ctx, e["n_text"], self.text_ids, self.text_table, e["text_vocab"],
+                                  e["n_frames"], e["n_frames"], e["n_cb"], e["cb_vocab"], e["mask_id"], self.tables,
+                                  self.heads, self.codes, self.sched[i], e["layer_penalty"], self.pred, self.conf,
+                                  self.picked, cfg_scale=cfg_scale, class_temp=class_temp, pos_temp=pos_temp,
+                                  top_k_ratio=0.1, u_class=self.u_class, u_pos=self.u_pos)
+
     def flops(self):
         """Algorithmic flops of one pass: projections, attention, heads."""
         e = self.e
@@ -337,6 +356,15 @@ def run_c5c4(args, T, torch):
     e1.record()
     torch.cuda.synchronize()
     cfg_ms = e0.elapsed_time(e1) / args.steps
+    log("timed: %d guided + sampled MaskGIT steps" % args.steps)
+    mg.step_sampled(0)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(args.steps):
+        mg.step_sampled(i)
+    e1.record()
+    torch.cuda.synchronize()
+    smp_ms = e0.elapsed_time(e1) / args.steps
 
     attn_ms, attn_n = timed_attn
     attn_avg_ms = attn_ms / max(1, attn_n)
@@ -373,6 +401,10 @@ def run_c5c4(args, T, torch):
                         "frames_per_s": round(mg.e["n_frames"] / (cfg_ms * 1e-3 * mg.e["n_steps"]), 1),
                         "note": "guided step: conditional 950-token prompt + unconditional 750-frame window, "
                                 "cfg_scale 2.0"},
+        "maskgit_sampled": {"ms_per_pass": round(smp_ms, 4),
+                            "frames_per_s": round(mg.e["n_frames"] / (smp_ms * 1e-3 * mg.e["n_steps"]), 1),
+                            "note": "guided + sampled step: cfg_scale 2.0, top-k ratio 0.1, class and position "
+                                    "temperature 1.0, Gumbel uniforms resident"},
         "roofline": {"kernel": "decode_attn (split-sequence paged GQA attention)", "bound": "hbm",
                      "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
