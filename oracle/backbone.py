@@ -33,6 +33,10 @@ Sources (the pages, cited by title and section):
             1-D half-rotate RoPE with head_dim 128 and theta 1e6.
 * [QTS-T]   rightkit-qts 0.2.0 docs, "Synthetic tests": cached/recompute
             equivalence is the property used to pin the decode path.
+* [OV-CODEC] OmniVoice ARCHITECTURE, "Audio tokenizer pipeline": the decode path's RVQ
+            decode (per-codebook embedding gather, project_out Linear with bias, sum).
+* [NC-CODEC] ncnn Qwen3-TTS port, "Codec Decoder的切分": the codebook lookup and
+            projections run before the codec body, projected and summed per frame.
 
 Readings where the pages are silent (each listed in the design notes):
 * RMSNorm is x / sqrt(mean(x^2) + eps) * g, eps inside the root, same eps for the
@@ -540,3 +544,26 @@ def maskgit_step(text_ids, text_table, codes_kt, n_target: int, audio_table, aud
     if record is not None:
         record.update(logits_c=lc, logits_u=lu, guided=guided, lp=lp, pred=pred, conf=conf, picked=picked)
     return new_codes, pred, conf, picked
+
+
+# ---------------------------------------------------------------------------
+# Codec RVQ decode (the fourth NEXT row)
+# ---------------------------------------------------------------------------
+
+def rvq_decode(codes_qt: np.ndarray, embed: np.ndarray, proj_w: np.ndarray, proj_b: np.ndarray) -> np.ndarray:
+    """Residual-VQ decode of the codec's quantizer: for each codebook k, gather the code's
+    codebook_dim-wide embedding, project it with project_out[k] (W [out][dim], bias
+    [out]) and sum over the codebooks.  [OV-CODEC] (RVQ decode: e_k = embed_k[codes[k]],
+    p_k = e_k W_k^T + b_k, out += p_k), [NC-CODEC] (codebook lookup per frame, projected
+    and summed before the codec body).
+
+    codes_qt int [Q][T]; embed [Q][codebook_size][dim]; proj_w [Q][out][dim];
+    proj_b [Q][out] -> [T][out] (the page then views it as [out][T] for the convolutions)."""
+    codes_qt = np.asarray(codes_qt, dtype=np.int64)
+    Q, T = codes_qt.shape
+    out = None
+    for k in range(Q):
+        e = as64(embed[k])[codes_qt[k]]              # [T][dim]
+        p = e @ as64(proj_w[k]).T + as64(proj_b[k])  # [T][out]
+        out = p if out is None else out + p
+    return out

@@ -628,3 +628,43 @@ def test_general_step_reduces_to_the_plain_and_guided_steps():
     d = O.maskgit_step(text, text_tab, codes, 4, tab, heads, layers, fnorm, dims, V, mask, 5.0, 3, cfg_scale=1.5)
     for x, y in zip(c, d):
         np.testing.assert_array_equal(x, y)
+
+
+# ---------------------------------------------------------------------------
+# Codec RVQ decode (the fourth NEXT row)
+# ---------------------------------------------------------------------------
+
+def test_rvq_decode_identity_projection_sums_embeddings():
+    """With project_out = [I; 0] and zero bias the decode is the sum of the gathered
+    embeddings in the first dim outputs; a bias alone shifts every frame by sum_k b_k."""
+    rng = np.random.default_rng(41)
+    Q, CB, D, OUT, T = 3, 10, 4, 6, 7
+    emb = rng.standard_normal((Q, CB, D))
+    w = np.zeros((Q, OUT, D))
+    w[:, :D, :] = np.eye(D)
+    codes = rng.integers(0, CB, (Q, T))
+    out = O.rvq_decode(codes, emb, w, np.zeros((Q, OUT)))
+    ref = sum(emb[k][codes[k]] for k in range(Q))
+    np.testing.assert_allclose(out[:, :D], ref, rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(out[:, D:], 0.0)
+    b = rng.standard_normal((Q, OUT))
+    out_b = O.rvq_decode(codes, np.zeros_like(emb), w, b)
+    np.testing.assert_allclose(out_b, np.tile(b.sum(0), (T, 1)), rtol=1e-12, atol=1e-12)
+
+
+def test_rvq_decode_frame_by_loops_and_codebook_additivity():
+    rng = np.random.default_rng(42)
+    Q, CB, D, OUT, T = 4, 12, 5, 9, 6
+    emb, w, b = rng.standard_normal((Q, CB, D)), rng.standard_normal((Q, OUT, D)), rng.standard_normal((Q, OUT))
+    codes = rng.integers(0, CB, (Q, T))
+    out = O.rvq_decode(codes, emb, w, b)
+    for t in range(T):  # one frame, plain loops
+        for n in range(OUT):
+            v = 0.0
+            for k in range(Q):
+                v += b[k, n] + sum(emb[k, codes[k, t], d] * w[k, n, d] for d in range(D))
+            assert abs(out[t, n] - v) < 1e-10
+    # decoding codebooks 0..1 and 2..3 separately and adding gives the whole
+    a = O.rvq_decode(codes[:2], emb[:2], w[:2], b[:2])
+    c = O.rvq_decode(codes[2:], emb[2:], w[2:], b[2:])
+    np.testing.assert_allclose(a + c, out, rtol=1e-12, atol=1e-12)
