@@ -16,7 +16,7 @@ OUT_DIR = os.path.join(HERE, "lib")
 LIB = os.path.join(OUT_DIR, "libttsbb.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["k_embed_norm.hip", "k_gemm.hip", "k_rope_decode.hip", "k_flash.hip", "k_head.hip",
+SOURCES = ["k_embed_norm.hip", "k_gemm.hip", "k_rope_decode.hip", "k_flash.hip", "k_head.hip", "k_rvq.hip",
            "ttsbb_api.cpp"]
 
 COMMON = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-fvisibility=hidden",

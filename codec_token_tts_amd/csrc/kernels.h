@@ -145,6 +145,18 @@ void launch_maskgit_sample(const float *logits, const float *logits_u, float cfg
 void launch_select_update(const float *conf, const int32_t *pred, int n_cb, int T, int n_unmask,
                           int32_t *rank, int32_t *codes, int codes_ld, int32_t *picked, hipStream_t s);
 
+// ---- codec RVQ decode (fp32) -----------------------------------------------------------
+struct RvqArgs {
+    int n_frames, n_q, cb_size, dim, out_dim;
+    const int32_t *codes;  // [n_q][n_frames]
+    const float *embed;    // [n_q][cb_size][dim]
+    const float *proj_w;   // [n_q][out_dim][dim]
+    const float *proj_b;   // [n_q][out_dim]
+    float *out;            // [n_frames][out_dim]
+    int *flag;
+};
+void launch_rvq_decode(const RvqArgs &a, hipStream_t s);
+
 // ---- misc ---------------------------------------------------------------------------
 void launch_increment(int32_t *v, int n, hipStream_t s);
 // dst[i0][i1][i2] (fp32, dense) = src[i0*s0 + i1*s1 + i2*s2] (element strides)

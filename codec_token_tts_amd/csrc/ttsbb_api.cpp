@@ -828,6 +828,32 @@ TTSBB_API ttsbb_status ttsbb_maskgit_step(ttsbb_ctx *ctx, const ttsbb_maskgit_st
     return launch_failed() ? TTSBB_DEVICE_ERROR : TTSBB_OK;
 }
 
+TTSBB_API ttsbb_status ttsbb_rvq_decode(ttsbb_ctx *ctx, int32_t n_frames, int32_t n_q, int32_t codebook_size,
+                                        int32_t codebook_dim, int32_t out_dim, const int32_t *codes,
+                                        const float *embed, const float *proj_w, const float *proj_b, float *out) {
+    if (!ctx || n_frames < 0 || n_q <= 0 || codebook_size <= 0 || codebook_dim <= 0 || out_dim <= 0)
+        return TTSBB_INVALID_ARG;
+    if (n_frames == 0) return TTSBB_OK;
+    if (!codes || !embed || !proj_w || !proj_b || !out) return TTSBB_INVALID_ARG;
+    RvqArgs r;
+    r.n_frames = n_frames;
+    r.n_q = n_q;
+    r.cb_size = codebook_size;
+    r.dim = codebook_dim;
+    r.out_dim = out_dim;
+    r.codes = codes;
+    r.embed = embed;
+    r.proj_w = proj_w;
+    r.proj_b = proj_b;
+    r.out = out;
+    r.flag = ctx->flag;
+    {
+        KScope k(ctx, TTSBB_K_RVQ);
+        launch_rvq_decode(r, ctx->stream);
+    }
+    return launch_failed() ? TTSBB_DEVICE_ERROR : TTSBB_OK;
+}
+
 TTSBB_API ttsbb_status ttsbb_unmask_schedule(int32_t n_total, int32_t n_steps, int32_t *out) {
     if (n_total < 0 || n_steps <= 0 || !out) return TTSBB_INVALID_ARG;
     const double PI = 3.14159265358979323846;

@@ -22,14 +22,14 @@ F32, BF16 = 0, 1
 
 EXPORTS = ["ttsbb_default_config", "ttsbb_create", "ttsbb_destroy", "ttsbb_status_str",
            "ttsbb_sync", "ttsbb_codebook_embed", "ttsbb_decode_step", "ttsbb_maskgit_pass",
-           "ttsbb_maskgit_pass_cfg", "ttsbb_maskgit_step", "ttsbb_unmask_schedule", "ttsbb_set_tap_layer", "ttsbb_read_tap", "ttsbb_profile_start",
+           "ttsbb_maskgit_pass_cfg", "ttsbb_maskgit_step", "ttsbb_rvq_decode", "ttsbb_unmask_schedule", "ttsbb_set_tap_layer", "ttsbb_read_tap", "ttsbb_profile_start",
            "ttsbb_profile_stop"]
 
 (K_EMBED, K_RMSNORM, K_GEMM_QKV, K_ROPE_KV, K_DECODE_ATTN, K_DECODE_COMBINE, K_FLASH_ATTN, K_GEMM_O,
  K_GEMM_GATE_UP, K_GEMM_DOWN, K_GEMM_HEAD, K_ARGMAX, K_SCORES, K_SELECT) = range(14)
-K_COUNT = 14
+K_COUNT = 15
 K_NAMES = ["embed", "rmsnorm", "gemm_qkv", "rope_kv", "decode_attn", "decode_combine", "flash_attn",
-           "gemm_o", "gemm_gate_up", "gemm_down", "gemm_head", "argmax", "scores", "select"]
+           "gemm_o", "gemm_gate_up", "gemm_down", "gemm_head", "argmax", "scores", "select", "rvq"]
 
 
 class ttsbb_maskgit_step_args(C.Structure):
@@ -89,6 +89,7 @@ def lib() -> C.CDLL:
         "ttsbb_maskgit_pass_cfg": (i32, [vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp, i32, f32,
                                          f32, vp, vp, vp]),
         "ttsbb_maskgit_step": (i32, [vp, C.POINTER(ttsbb_maskgit_step_args)]),
+        "ttsbb_rvq_decode": (i32, [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp]),
         "ttsbb_unmask_schedule": (i32, [i32, i32, C.POINTER(i32)]),
         "ttsbb_set_tap_layer": (i32, [vp, i32]),
         "ttsbb_read_tap": (i32, [vp, i32, vp, i64, C.POINTER(i32), C.POINTER(i32)]),
@@ -220,6 +221,15 @@ def ttsbb_maskgit_step(ctx, n_text, text_ids, text_table, text_vocab, n_frames, 
     st = lib().ttsbb_maskgit_step(ctx, C.byref(a))
     if check:
         _check(st, "ttsbb_maskgit_step")
+    return st
+
+
+def ttsbb_rvq_decode(ctx, n_frames, n_q, codebook_size, codebook_dim, out_dim, codes, embed, proj_w, proj_b, out,
+                     check: bool = True) -> int:
+    st = lib().ttsbb_rvq_decode(ctx, n_frames, n_q, codebook_size, codebook_dim, out_dim, ptr(codes), ptr(embed),
+                                ptr(proj_w), ptr(proj_b), ptr(out))
+    if check:
+        _check(st, "ttsbb_rvq_decode")
     return st
 
 

@@ -218,6 +218,20 @@ typedef struct {
  * pointers are device memory; cb_vocab <= 2048 when class_temp > 0. */
 ttsbb_status ttsbb_maskgit_step(ttsbb_ctx *ctx, const ttsbb_maskgit_step_args *args);
 
+/* Codec RVQ decode (OmniVoice ARCHITECTURE, "Audio tokenizer pipeline", decode path; ncnn
+ * Qwen3-TTS port, "Codec Decoder的切分"): for every frame t the sum over codebooks k of
+ * the code's embedding projected by that codebook's project_out Linear,
+ *   out[t][n] = sum_k ( sum_d embed[k][codes[k][t]][d] * proj_w[k][n][d] + proj_b[k][n] ),
+ * in fp32 (the codec's quantizer precision).  The page then views out as [out_dim][T] for
+ * the codec body (not part of this library).
+ *   codes int32 [n_q][n_frames]; embed fp32 [n_q][codebook_size][codebook_dim];
+ *   proj_w fp32 [n_q][out_dim][codebook_dim]; proj_b fp32 [n_q][out_dim];
+ *   out fp32 [n_frames][out_dim].  All device pointers; a code outside
+ *   [0, codebook_size) is clamped and raises the device flag (ttsbb_sync). */
+ttsbb_status ttsbb_rvq_decode(ttsbb_ctx *ctx, int32_t n_frames, int32_t n_q, int32_t codebook_size,
+                              int32_t codebook_dim, int32_t out_dim, const int32_t *codes, const float *embed,
+                              const float *proj_w, const float *proj_b, float *out);
+
 /* Host helper: how many positions each of n_steps MaskGIT steps unmasks (OmniVoice
  * ARCHITECTURE, "MaskGIT decoder": ceil(N * (t[i+1] - t[i])) over a time grid), on the
  * cosine grid t_i = 1 - cos(pi/2 * i/n_steps); each count is capped at what is left and
@@ -271,7 +285,8 @@ typedef enum {
     TTSBB_K_ARGMAX = 11,       /* greedy choice per group */
     TTSBB_K_SCORES = 12,       /* MaskGIT log-softmax / argmax / confidence */
     TTSBB_K_SELECT = 13,       /* MaskGIT top-n + code update */
-    TTSBB_K_COUNT = 14
+    TTSBB_K_RVQ = 14,          /* codec RVQ decode */
+    TTSBB_K_COUNT = 15
 } ttsbb_kernel_class;
 
 /* Start recording events for the classes whose bit (1 << class) is set in `mask`;

@@ -491,3 +491,38 @@ def test_maskgit_step_sampler(n_text, n_frames, n_target, cfg_scale, class_temp,
         np.testing.assert_array_equal(res_codes[:, w0:], O.apply_picks(win, res_pred, res_picked))
     finally:
         m.close()
+
+
+# ---------------------------------------------------------------------------------------
+# Codec RVQ decode
+# ---------------------------------------------------------------------------------------
+@pytest.mark.parametrize("n_frames,n_q,cb,dim,out_dim", [(750, 8, 1024, 64, 1024), (37, 3, 100, 48, 200),
+                                                         (1, 1, 5, 130, 7)])
+def test_rvq_decode(n_frames, n_q, cb, dim, out_dim):
+    """fp32 against the oracle to 1e-4 max-abs (the quantizer accuracy the ncnn port reports
+    against PyTorch); the first shape is the 8 x 1024 x 64 -> 1024 quantizer of the
+    OmniVoice codec over 30 s of frames, the others ragged tiles and a codebook dimension
+    that is not a multiple of the 64-wide slices."""
+    m = Model(CFG.Shape(n_layers=1), 0, False, seed=13)
+    try:
+        T = m.T
+        seed = 13
+        emb = gen.normal_f32(seed, stream_id(gen.KIND_CB_TABLE, 3), (n_q, cb, dim), 1.0)
+        w = gen.normal_f32(seed, stream_id(gen.KIND_HEAD, 3), (n_q, out_dim, dim), 0.05)
+        b = gen.normal_f32(seed, stream_id(gen.KIND_FINAL_NORM, 3), (n_q, out_dim), 0.1)
+        codes = gen.uniform_int(seed, stream_id(gen.KIND_CODES, 3), (n_q, n_frames), cb)
+        codes[0, 0] = cb - 1
+        codes[-1, -1] = 0
+        out = torch().empty((n_frames, out_dim), dtype=torch().float32, device="cuda")
+        T.ttsbb_rvq_decode(m.ctx, n_frames, n_q, cb, dim, out_dim, t_i32(codes), t_f32(emb), t_f32(w), t_f32(b), out)
+        assert T.ttsbb_sync(m.ctx) == T.OK
+        ref = O.rvq_decode(codes, emb, w, b)
+        assert np.max(np.abs(out.cpu().numpy() - ref)) <= 1e-4
+        # an out-of-range code is clamped and reported, then the flag clears
+        bad = codes.copy()
+        bad[-1, 0] = cb
+        T.ttsbb_rvq_decode(m.ctx, n_frames, n_q, cb, dim, out_dim, t_i32(bad), t_f32(emb), t_f32(w), t_f32(b), out)
+        assert T.ttsbb_sync(m.ctx) == T.DEVICE_ERROR
+        assert T.ttsbb_sync(m.ctx) == T.OK
+    finally:
+        m.close()
