@@ -296,6 +296,35 @@ def copy_calibration(torch, mib: int):
     del a, b
 
 
+def run_rvq(T, torch, n_frames, iters):
+    """Timed codec RVQ decode: 8 codebooks of 1024 x 64 fp32 projected to 1024."""
+    from workload import gen
+    nq, cb, dim, od = 8, 1024, 64, 1024
+    emb = torch.from_numpy(gen.normal_f32(5, gen.stream_id(gen.KIND_CB_TABLE, 9), (nq, cb, dim))).cuda()
+    w = torch.from_numpy(gen.normal_f32(5, gen.stream_id(gen.KIND_HEAD, 9), (nq, od, dim), 0.05)).cuda()
+    b = torch.from_numpy(gen.normal_f32(5, gen.stream_id(gen.KIND_FINAL_NORM, 9), (nq, od), 0.1)).cuda()
+    codes = torch.from_numpy(gen.uniform_int(5, gen.stream_id(gen.KIND_CODES, 9), (nq, n_frames), cb)).cuda()
+    out = torch.empty((n_frames, od), dtype=torch.float32, device="cuda")
+    cfg = T.ttsbb_default_config()
+    cfg.n_layers = 0
+    cfg.dtype = T.F32
+    ctx = T.ttsbb_create(cfg, [], None, torch.cuda.current_stream().cuda_stream)
+    try:
+        T.ttsbb_rvq_decode(ctx, n_frames, nq, cb, dim, od, codes, emb, w, b, out)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            T.ttsbb_rvq_decode(ctx, n_frames, nq, cb, dim, od, codes, emb, w, b, out)
+        e1.record()
+        torch.cuda.synchronize()
+        if T.ttsbb_sync(ctx) != T.OK:
+            raise RuntimeError("device flag raised by the RVQ decode")
+        return e0.elapsed_time(e1) * 1e3 / iters
+    finally:
+        T.ttsbb_destroy(ctx)
+
+
 def run_c5c4(args, T, torch):
     if args.copy_calibration:
         copy_calibration(torch, args.copy_calibration)
@@ -366,6 +395,9 @@ def run_c5c4(args, T, torch):
     torch.cuda.synchronize()
     smp_ms = e0.elapsed_time(e1) / args.steps
 
+    # Codec RVQ decode of the pass's 750 frames (8 codebooks x 1024 x 64 -> 1024, fp32)
+    rvq_us = run_rvq(T, torch, mg.e["n_frames"], args.steps)
+
     attn_ms, attn_n = timed_attn
     attn_avg_ms = attn_ms / max(1, attn_n)
     attn_bytes = dec.attn_bytes(args.warmup, args.steps)
@@ -401,6 +433,9 @@ def run_c5c4(args, T, torch):
                         "frames_per_s": round(mg.e["n_frames"] / (cfg_ms * 1e-3 * mg.e["n_steps"]), 1),
                         "note": "guided step: conditional 950-token prompt + unconditional 750-frame window, "
                                 "cfg_scale 2.0"},
+        "rvq_decode": {"us_per_call": round(rvq_us, 2), "frames": mg.e["n_frames"],
+                       "gflops_fp32": round(2.0 * mg.e["n_frames"] * 8 * 64 * 1024 / (rvq_us * 1e-6) / 1e9, 1),
+                       "note": "codec RVQ decode, 8 x (1024 x 64) codebooks -> 1024, fp32"},
         "maskgit_sampled": {"ms_per_pass": round(smp_ms, 4),
                             "frames_per_s": round(mg.e["n_frames"] / (smp_ms * 1e-3 * mg.e["n_steps"]), 1),
                             "note": "guided + sampled step: cfg_scale 2.0, top-k ratio 0.1, class and position "
