@@ -264,6 +264,32 @@ def decode_layer(x: np.ndarray, pos: Sequence[int], cache: KVCache, li: int, L: 
     return post["x2"]
 
 
+def prefill_layer(x: np.ndarray, p0: int, cache: KVCache, b: int, li: int, L: Layer, dims: Dims) -> np.ndarray:
+    """One layer of a causal multi-token prefill of stream b: S tokens at positions
+    p0..p0+S-1 (p0 = tokens already cached).  All S rotated K and V are appended, then
+    token i attends to positions 0..p0+i.  [NC-ATTN] (RoPE + KV append + GQA attention),
+    [OV-MG] (the Talker prompt is a prefill; causal, unlike the MaskGIT passes)."""
+    x = as64(x)
+    S = x.shape[0]
+    if cache.length(li, b) != p0:
+        raise ValueError("cache length of stream %d is %d, p0 is %d" % (b, cache.length(li, b), p0))
+    st = qkv_heads(x, L, dims, np.arange(p0, p0 + S))
+    kb = st["k"] if cache.k[li][b] is None else np.concatenate([cache.k[li][b], st["k"]], axis=0)
+    vb = st["v"] if cache.v[li][b] is None else np.concatenate([cache.v[li][b], st["v"]], axis=0)
+    cache.set(li, b, kb, vb)
+    o = np.empty((S, dims.n_heads, dims.head_dim), F64)
+    for i in range(S):
+        o[i] = attend(st["q"][i], kb[:p0 + i + 1], vb[:p0 + i + 1])
+    return post_attention(x, o, L, dims)["x2"]
+
+
+def prefill(x: np.ndarray, p0: int, cache: KVCache, b: int, layers: List[Layer], dims: Dims) -> np.ndarray:
+    """All layers of a causal prefill of S tokens of stream b; returns the residual stream."""
+    for li, L in enumerate(layers):
+        x = prefill_layer(x, p0, cache, b, li, L, dims)
+    return x
+
+
 def decode_step(x: np.ndarray, pos: Sequence[int], cache: KVCache, layers: List[Layer],
                 dims: Dims, record_layer: Optional[int] = None,
                 record: Optional[Dict] = None) -> np.ndarray:

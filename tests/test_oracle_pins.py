@@ -668,3 +668,43 @@ def test_rvq_decode_frame_by_loops_and_codebook_additivity():
     a = O.rvq_decode(codes[:2], emb[:2], w[:2], b[:2])
     c = O.rvq_decode(codes[2:], emb[2:], w[2:], b[2:])
     np.testing.assert_allclose(a + c, out, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Causal multi-token prefill (the second NEXT row)
+# ---------------------------------------------------------------------------
+
+def test_prefill_equals_token_by_token_decode():
+    """A prefill of S tokens after p0 cached ones equals S decode steps of one token each
+    (the cached/recompute equivalence of the rightkit-qts synthetic tests), outputs and
+    cache contents."""
+    rng = np.random.default_rng(51)
+    dims = small_dims()
+    layers = [rand_layer(dims, rng) for _ in range(2)]
+    p0, S = 3, 5
+    pre = rng.standard_normal((p0, dims.hidden))
+    x = rng.standard_normal((S, dims.hidden))
+    c1, c2 = O.KVCache(2, 1), O.KVCache(2, 1)
+    for c in (c1, c2):
+        O.prefill(pre, 0, c, 0, layers, dims)
+    out = O.prefill(x, p0, c1, 0, layers, dims)
+    for i in range(S):
+        step = O.decode_step(x[i:i + 1], [p0 + i], c2, layers, dims)
+        np.testing.assert_allclose(out[i], step[0], rtol=1e-10, atol=1e-12)
+    for li in range(2):
+        np.testing.assert_allclose(c1.k[li][0], c2.k[li][0], rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(c1.v[li][0], c2.v[li][0], rtol=1e-12, atol=1e-14)
+
+
+def test_prefill_from_empty_is_the_causal_full_pass():
+    rng = np.random.default_rng(52)
+    dims = small_dims()
+    layers = [rand_layer(dims, rng) for _ in range(2)]
+    x = rng.standard_normal((7, dims.hidden))
+    out = O.prefill(x, 0, O.KVCache(2, 1), 0, layers, dims)
+    ref = O.backbone_full(x, layers, dims, causal=True)
+    np.testing.assert_allclose(out, ref, rtol=1e-10, atol=1e-12)
+    # a later token never changes an earlier one
+    out2 = O.prefill(np.vstack([x[:4], rng.standard_normal((3, dims.hidden))]), 0, O.KVCache(2, 1), 0, layers,
+                     dims)
+    np.testing.assert_allclose(out2[:4], out[:4], rtol=1e-10, atol=1e-12)
