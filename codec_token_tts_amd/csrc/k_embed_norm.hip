@@ -124,14 +124,14 @@ void launch_rmsnorm(float *x, int ldx, int rows, int hidden, const float *gain, 
                            reinterpret_cast<float *>(out), pend, n_pend, pend_ld, pend_stride);
 }
 
-__global__ void increment_kernel(int32_t *v, int n) {
+__global__ void increment_kernel(int32_t *v, int n, int delta) {
     int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) v[i] += 1;
+    if (i < n) v[i] += delta;
 }
 
-void launch_increment(int32_t *v, int n, hipStream_t s) {
+void launch_increment(int32_t *v, int n, hipStream_t s, int delta) {
     if (n <= 0) return;
-    hipLaunchKernelGGL(increment_kernel, dim3((n + 255) / 256), dim3(256), 0, s, v, n);
+    hipLaunchKernelGGL(increment_kernel, dim3((n + 255) / 256), dim3(256), 0, s, v, n, delta);
 }
 
 template <typename T>

@@ -30,7 +30,7 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(RopeKvArgs a) {
     const int width = (a.H + 2 * a.Hkv) * 128;
     const float *row = a.qkv + (int64_t)m * width;
 
-    int p = a.dense ? m : a.pos[m];
+    int p = a.dense ? m : (a.shared ? a.pos[0] + m : a.pos[m]);
     bool ok = true;
     int page_id = 0, slot = 0;
     if (p < 0 || p >= a.max_pos) {
@@ -44,7 +44,7 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(RopeKvArgs a) {
             if (threadIdx.x == 0) raise_flag(a.flag, FLAG_POSITION);
             ok = false;
         } else {
-            page_id = a.page_table[(int64_t)m * a.max_pages + pi];
+            page_id = a.page_table[(int64_t)(a.shared ? 0 : m) * a.max_pages + pi];
             slot = p % a.page;
             if (page_id < 0 || page_id >= a.n_pages) {
                 if (threadIdx.x == 0) raise_flag(a.flag, FLAG_PAGE);
@@ -243,7 +243,7 @@ void decode_attn_kernel(DecodeAttnArgs a) {
     const int t = item / a.Hkv;
     const int c = t % a.n_chunks, b = t / a.n_chunks;
 
-    int L = a.pos[b] + 1;
+    int L = (a.shared ? a.pos[0] + b : a.pos[b]) + 1;
     const int cap = a.max_pages * a.page;
     if (L > cap) L = cap;
     const int p_begin = c * a.chunk;
@@ -271,7 +271,7 @@ void decode_attn_kernel(DecodeAttnArgs a) {
 
     const T *pool = reinterpret_cast<const T *>(a.pool_layer);
     const int64_t blk = (int64_t)a.page * 128;  // elements of one (page, K|V, head) block
-    const int32_t *ptab = a.page_table + (int64_t)b * a.max_pages;
+    const int32_t *ptab = a.page_table + (int64_t)(a.shared ? 0 : b) * a.max_pages;
     const int lane_off = rsub * 128 + d0;
     const int pg_first = p_begin / a.page, pg_last = (p_end - 1) / a.page;
     // The chunk's page ids (at most 64, one per lane) are read once up front: a page-id
@@ -338,7 +338,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeAttnArgs a) {
     const int item = blockIdx.x * 4 + wave;
     if (item >= a.B * a.H) return;
     const int h = item % a.H, b = item / a.H;
-    int L = a.pos[b] + 1;
+    int L = (a.shared ? a.pos[0] + b : a.pos[b]) + 1;
     const int cap = a.max_pages * a.page;
     if (L > cap) L = cap;
     const int nc = min(a.n_chunks, (L + a.chunk - 1) / a.chunk);

@@ -86,6 +86,8 @@ struct RopeKvArgs {
     uint16_t *kbuf, *vtbuf;
     int s_pad;
     int *flag;
+    int shared;          // decode mode, prefill of one stream: row m is at position pos[0] + m
+                         // and every row uses page-table row 0
 };
 void launch_rope_kv(const RopeKvArgs &a, DType kv_dt, hipStream_t s);
 // Dense mode fused into the q/k/v projection (g: EPI_STORE product of N = (H + 2 Hkv) *
@@ -105,6 +107,8 @@ struct DecodeAttnArgs {
     float *part;          // [B][H][n_chunks][132]: m, l, pad, pad, acc[128]
     void *out;            // [B][H*128] operand dtype
     float scale_log2;     // log2(e) / sqrt(128)
+    int shared;           // prefill of one stream: query b is at position pos[0] + b and
+                          // every query reads page-table row 0 (causal by construction)
 };
 void launch_decode_attn(const DecodeAttnArgs &a, DType dt, hipStream_t s);
 void launch_decode_combine(const DecodeAttnArgs &a, DType dt, hipStream_t s);
@@ -158,7 +162,7 @@ struct RvqArgs {
 void launch_rvq_decode(const RvqArgs &a, hipStream_t s);
 
 // ---- misc ---------------------------------------------------------------------------
-void launch_increment(int32_t *v, int n, hipStream_t s);
+void launch_increment(int32_t *v, int n, hipStream_t s, int delta = 1);  // v[i] += delta, i < n
 // dst[i0][i1][i2] (fp32, dense) = src[i0*s0 + i1*s1 + i2*s2] (element strides)
 void launch_tap_copy(const void *src, DType dt, int64_t s0, int64_t s1, int64_t s2, int d0,
                      int d1, int d2, float *dst, hipStream_t s);

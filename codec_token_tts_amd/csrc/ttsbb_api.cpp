@@ -462,10 +462,10 @@ void post_attention(ttsbb_ctx *c, const ttsbb_layer &L, float *x, int M, bool ta
     }
 }
 
-void head_gemm(ttsbb_ctx *c, const void *head, int M, int N, float *out, int ldc) {
+void head_gemm(ttsbb_ctx *c, const void *head, int M, int N, float *out, int ldc, int row0 = 0) {
     const ttsbb_config &g = c->cfg;
     GemmArgs a = {};
-    a.A = c->h;
+    a.A = reinterpret_cast<const char *>(c->h) + (size_t)row0 * g.hidden * c->esz;
     a.lda = g.hidden;
     a.M = M;
     a.K = g.hidden;
@@ -575,10 +575,14 @@ void maskgit_backbone(ttsbb_ctx *ctx, int S, int row0, int n_out, const void *he
 
 }  // namespace
 
-TTSBB_API ttsbb_status ttsbb_decode_step(ttsbb_ctx *ctx, int32_t batch, float *x, int32_t *positions,
-                                         const int32_t *page_table, int32_t max_pages, void *kv_pool,
-                                         int32_t n_pages, const void *head, int32_t n_groups,
-                                         int32_t group_vocab, int32_t *argmax, float *logits) {
+static // The paged forward shared by the decode step (batch streams, one token each, row b at
+// position positions[b], page-table row b) and the prefill (batch tokens of one stream,
+// row b at position positions[0] + b, page-table row 0, causal by construction since
+// row b attends to positions 0..positions[0] + b).  The prefill's head reads the last
+// row only.
+ttsbb_status paged_forward(ttsbb_ctx *ctx, int32_t batch, float *x, int32_t *positions, const int32_t *page_table,
+                           int32_t max_pages, void *kv_pool, int32_t n_pages, const void *head, int32_t n_groups,
+                           int32_t group_vocab, int32_t *argmax, float *logits, bool prefill) {
     if (!ctx || batch < 0) return TTSBB_INVALID_ARG;
     const ttsbb_config &g = ctx->cfg;
     ctx->pend_splits = 0;
@@ -635,6 +639,7 @@ TTSBB_API ttsbb_status ttsbb_decode_step(ttsbb_ctx *ctx, int32_t batch, float *x
         r.page = g.kv_page;
         r.pool_layer = pool_l;
         r.flag = ctx->flag;
+        r.shared = prefill ? 1 : 0;
         {
             KScope k(ctx, TTSBB_K_ROPE_KV);
             launch_rope_kv(r, ctx->dt, ctx->stream);
@@ -657,6 +662,7 @@ TTSBB_API ttsbb_status ttsbb_decode_step(ttsbb_ctx *ctx, int32_t batch, float *x
         d.part = ctx->part;
         d.out = ctx->attn;
         d.scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
+        d.shared = prefill ? 1 : 0;
         {
             KScope k(ctx, TTSBB_K_DECODE_ATTN);
             launch_decode_attn(d, ctx->dt, ctx->stream);
@@ -672,17 +678,35 @@ TTSBB_API ttsbb_status ttsbb_decode_step(ttsbb_ctx *ctx, int32_t batch, float *x
     if (head) {
         const int N = n_groups * group_vocab;
         norm_rows(ctx, x, batch, ctx->final_norm);
+        const int r0 = prefill ? batch - 1 : 0, rows = prefill ? 1 : batch;  // rows read out
         if (ctx->tap_layer >= 0) tap_dense(ctx, TTSBB_TAP_HEAD_IN, ctx->h, ctx->dt, batch, g.hidden, g.hidden);
         float *lg = logits ? logits : ctx->logits;
-        head_gemm(ctx, head, batch, N, lg, N);
-        if (ctx->tap_layer >= 0) tap_dense(ctx, TTSBB_TAP_LOGITS, lg, DT_F32, batch, N, N);
+        head_gemm(ctx, head, rows, N, lg, N, r0);
+        if (ctx->tap_layer >= 0) tap_dense(ctx, TTSBB_TAP_LOGITS, lg, DT_F32, rows, N, N);
         {
             KScope k(ctx, TTSBB_K_ARGMAX);
-            launch_argmax_groups(lg, batch, N, n_groups, group_vocab, argmax, ctx->stream);
+            launch_argmax_groups(lg, rows, N, n_groups, group_vocab, argmax, ctx->stream);
         }
     }
-    launch_increment(positions, batch, ctx->stream);
+    if (prefill) launch_increment(positions, 1, ctx->stream, batch);
+    else launch_increment(positions, batch, ctx->stream);
     return launch_failed() ? TTSBB_DEVICE_ERROR : TTSBB_OK;
+}
+
+TTSBB_API ttsbb_status ttsbb_decode_step(ttsbb_ctx *ctx, int32_t batch, float *x, int32_t *positions,
+                                         const int32_t *page_table, int32_t max_pages, void *kv_pool,
+                                         int32_t n_pages, const void *head, int32_t n_groups,
+                                         int32_t group_vocab, int32_t *argmax, float *logits) {
+    return paged_forward(ctx, batch, x, positions, page_table, max_pages, kv_pool, n_pages, head, n_groups,
+                         group_vocab, argmax, logits, false);
+}
+
+TTSBB_API ttsbb_status ttsbb_prefill(ttsbb_ctx *ctx, int32_t n_tokens, float *x, int32_t *cache_len,
+                                     const int32_t *page_table, int32_t max_pages, void *kv_pool, int32_t n_pages,
+                                     const void *head, int32_t n_groups, int32_t group_vocab, int32_t *argmax,
+                                     float *logits) {
+    return paged_forward(ctx, n_tokens, x, cache_len, page_table, max_pages, kv_pool, n_pages, head, n_groups,
+                         group_vocab, argmax, logits, true);
 }
 
 TTSBB_API ttsbb_status ttsbb_maskgit_pass(ttsbb_ctx *ctx, int32_t n_text, const int32_t *text_ids,

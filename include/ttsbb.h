@@ -133,6 +133,21 @@ ttsbb_status ttsbb_decode_step(ttsbb_ctx *ctx, int32_t batch, float *x, int32_t 
                                int32_t n_pages, const void *head, int32_t n_groups,
                                int32_t group_vocab, int32_t *argmax, float *logits);
 
+/* Causal multi-token prefill of one stream (ncnn Qwen3-TTS port, "单token SDPA问题与host
+ * attention": RoPE + KV append + GQA attention per layer; the Talker prompt and the code
+ * predictor's two-token start are prefills): n_tokens embedded tokens at positions
+ * cache_len[0] .. cache_len[0] + n_tokens - 1 run through every layer; each token's
+ * rotated K and raw V are written to the stream's pages (page_table row, as in
+ * ttsbb_decode_step) and token i attends to positions 0 .. cache_len[0] + i (the cached
+ * prefix and the tokens before it).  x [n_tokens][hidden] fp32 is the embedded input and
+ * the final residual stream on return; cache_len int32 [1] is advanced by n_tokens on the
+ * device.  With head != NULL the final norm + head + argmax run on the last token only
+ * (argmax [n_groups], logits [n_groups*group_vocab] if not NULL).  n_tokens <= max_rows. */
+ttsbb_status ttsbb_prefill(ttsbb_ctx *ctx, int32_t n_tokens, float *x, int32_t *cache_len,
+                           const int32_t *page_table, int32_t max_pages, void *kv_pool, int32_t n_pages,
+                           const void *head, int32_t n_groups, int32_t group_vocab, int32_t *argmax,
+                           float *logits);
+
 /* One MaskGIT step (OmniVoice ARCHITECTURE, "MaskGIT decoder" and "Inner-loop
  * optimisations"): embed n_text text tokens then n_frames audio frames (sum of n_cb
  * codebook rows, mask_id included as a code), run every layer with bidirectional

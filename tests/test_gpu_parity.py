@@ -526,3 +526,50 @@ def test_rvq_decode(n_frames, n_q, cb, dim, out_dim):
         assert T.ttsbb_sync(m.ctx) == T.OK
     finally:
         m.close()
+
+
+# ---------------------------------------------------------------------------------------
+# Causal prefill of one stream into its paged cache
+# ---------------------------------------------------------------------------------------
+@pytest.mark.parametrize("p0,S", [(0, 5), (21, 37), (0, 100), (300, 64)])
+def test_prefill_bf16(p0, S):
+    """bf16, 2 layers: the prompt's final residual stream, the K/V it leaves in the pool at
+    positions p0..p0+S-1, the advanced cache length and the last token's head choice,
+    against the oracle's prefill (which the oracle pins equal to token-by-token decode)."""
+    shape = CFG.Shape(n_layers=2)
+    m = Model(shape, 2, True, seed=17, gains="random")
+    try:
+        T = m.T
+        seed = 17
+        pt, n_pages = CFG.page_table(seed, [p0 + S + 1], extra_pages=2)
+        pool = DEV.kv_pool(seed, shape, 2, [p0], pt, n_pages, True)
+        x_in = gen.fast_normal(seed, stream_id(gen.KIND_X_IN, 1), (S, shape.hidden), 1.0)
+        x = t_f32(x_in)
+        cl = t_i32(np.array([p0]))
+        G, V = 3, 37
+        head_h = CFG.table(seed, gen.KIND_HEAD, 0, G * V, shape.hidden, True)
+        am = torch().empty(G, dtype=torch().int32, device="cuda")
+        lg = torch().empty(G * V, dtype=torch().float32, device="cuda")
+        T.ttsbb_prefill(m.ctx, S, x, cl, t_i32(pt), pt.shape[1], pool, n_pages, DEV.host_to_device(head_h), G, V,
+                        am, lg)
+        assert T.ttsbb_sync(m.ctx) == T.OK
+        assert cl.cpu().numpy().tolist() == [p0 + S]
+        cache = O.KVCache(2, 1)
+        for l in range(2):
+            if p0:
+                k, v = CFG.kv_prefill(seed, shape, l, 0, p0, True)
+                cache.set(l, 0, widen(k), widen(v))
+        out = O.prefill(x_in, p0, cache, 0, m.oracle_layers(), dims_of(shape))
+        assert normwise(x.cpu().numpy(), out) <= TOL_LAYER_BF16
+        pool_h = DEV.bits_to_f32(pool)
+        for l in range(2):
+            for p in range(p0, p0 + S):
+                pg, slot = pt[0, p // 16], p % 16
+                assert normwise(pool_h[l, pg, 0, :, slot, :], cache.k[l][0][p]) <= TOL_LAYER_BF16
+                assert normwise(pool_h[l, pg, 1, :, slot, :], cache.v[l][0][p]) <= TOL_LAYER_BF16
+        _, lg_ref = O.head_logits(out[-1:], m.oracle_final_norm(), widen(head_h), shape.eps)
+        lg_gpu = lg.cpu().numpy()
+        assert normwise(lg_gpu, lg_ref[0]) <= TOL_LAYER_BF16
+        check_argmax_groups(am.cpu().numpy()[None], lg_gpu.reshape(1, G, V), lg_ref.reshape(1, G, V))
+    finally:
+        m.close()
