@@ -69,7 +69,8 @@ class DecodeC5:
         self.B, self.K, self.V = e["batch"], e["n_cb"], e["cb_vocab"]
         self.lengths = CFG.c5_lengths(w)
         room = [int(n) + total_steps + 1 for n in self.lengths]
-        self.pt, self.n_pages = CFG.page_table(w.seed, room)
+        # 13 spare pages beyond the streams' (a 200-token prefill stream of its own)
+        self.pt, self.n_pages = CFG.page_table(w.seed, room, extra_pages=13)
         self.ctx, self.keep = make_ctx(T, torch, w.shape, 28, True, w.seed, 1024, 8192, 8200, DEV, CFG)
         self.pool = DEV.kv_pool(w.seed, w.shape, 28, self.lengths, self.pt, self.n_pages, True)
         self.pt_d = torch.from_numpy(self.pt).cuda()
@@ -325,6 +326,42 @@ def run_rvq(T, torch, n_frames, iters):
         T.ttsbb_destroy(ctx)
 
 
+def run_prefill(T, torch, dec, n_tokens, iters):
+    """Timed causal prefill of one stream's n_tokens-token prompt through the 28 layers
+    (Talker prompt), on the decode context: a fresh stream (cache length 0) on pages of
+    its own, reset before each call; head + argmax on the last token."""
+    from workload import configs as CFG, gen
+    import numpy as np
+    pt = np.full((1, dec.pt.shape[1]), -1, np.int32)
+    n_need = (n_tokens + 15) // 16
+    spare = np.setdiff1d(np.arange(dec.n_pages), dec.pt[dec.pt >= 0])
+    if spare.size < n_need:
+        raise RuntimeError("not enough spare pages for the prefill stream")
+    pt[0, :n_need] = spare[:n_need]
+    pt_d = torch.from_numpy(pt).cuda()
+    x0 = torch.from_numpy(gen.fast_normal(5, gen.stream_id(gen.KIND_X_IN, 7), (n_tokens, 1024), 1.0)).cuda()
+    x = torch.empty_like(x0)
+    cl = torch.zeros(1, dtype=torch.int32, device="cuda")
+    am = torch.empty(dec.K, dtype=torch.int32, device="cuda")
+    T.ttsbb_prefill(dec.ctx, n_tokens, x0.clone(), cl, pt_d, pt.shape[1], dec.pool, dec.n_pages, dec.heads, dec.K,
+                    dec.V, am)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    total = 0.0
+    for _ in range(iters):
+        x.copy_(x0)
+        cl.zero_()
+        e0.record()
+        T.ttsbb_prefill(dec.ctx, n_tokens, x, cl, pt_d, pt.shape[1], dec.pool, dec.n_pages, dec.heads, dec.K,
+                        dec.V, am)
+        e1.record()
+        torch.cuda.synchronize()
+        total += e0.elapsed_time(e1)
+    if T.ttsbb_sync(dec.ctx) != T.OK:
+        raise RuntimeError("device flag raised by the prefill")
+    return total / iters
+
+
 def run_c5c4(args, T, torch):
     if args.copy_calibration:
         copy_calibration(torch, args.copy_calibration)
@@ -395,6 +432,10 @@ def run_c5c4(args, T, torch):
     torch.cuda.synchronize()
     smp_ms = e0.elapsed_time(e1) / args.steps
 
+    # Causal prefill of a 200-token prompt of one stream (28 layers)
+    log("timed: prefill")
+    pf_ms = run_prefill(T, torch, dec, 200, args.steps)
+
     # Codec RVQ decode of the pass's 750 frames (8 codebooks x 1024 x 64 -> 1024, fp32)
     rvq_us = run_rvq(T, torch, mg.e["n_frames"], args.steps)
 
@@ -433,6 +474,10 @@ def run_c5c4(args, T, torch):
                         "frames_per_s": round(mg.e["n_frames"] / (cfg_ms * 1e-3 * mg.e["n_steps"]), 1),
                         "note": "guided step: conditional 950-token prompt + unconditional 750-frame window, "
                                 "cfg_scale 2.0"},
+        "prefill": {"ms_per_call": round(pf_ms, 4), "tokens": 200,
+                    "tokens_per_s": round(200 / (pf_ms * 1e-3), 1),
+                    "note": "causal prefill of one stream's 200-token prompt into fresh pages, 28 layers, "
+                            "head + argmax on the last token"},
         "rvq_decode": {"us_per_call": round(rvq_us, 2), "frames": mg.e["n_frames"],
                        "gflops_fp32": round(2.0 * mg.e["n_frames"] * 8 * 64 * 1024 / (rvq_us * 1e-6) / 1e9, 1),
                        "note": "codec RVQ decode, 8 x (1024 x 64) codebooks -> 1024, fp32"},
