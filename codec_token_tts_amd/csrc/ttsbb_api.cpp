@@ -937,8 +937,11 @@ TTSBB_API ttsbb_status ttsbb_profile_start(ttsbb_ctx *ctx, uint32_t mask, int32_
     if (p.cap < max_launches) {
         prof_release(p);
         p.ev.resize(2 * (size_t)max_launches);
+        // timing-only events: no system-scope fence (cache write-back / invalidate) at
+        // record time, so they perturb the timed kernels less; profile_stop synchronizes
+        // the stream before reading them
         for (auto &e : p.ev)
-            if (hipEventCreate(&e) != hipSuccess) {
+            if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) {
                 e = nullptr;
                 prof_release(p);
                 return TTSBB_DEVICE_ERROR;
