@@ -16,6 +16,7 @@
 // token with xor-shuffles; each lane keeps an online-softmax state (max, sum, 8 or 4
 // output dims) in base-2 units; lanes of a chunk merge by shuffles; chunks merge in a
 // fixed order in the combine kernel (deterministic, no atomics).
+#include <hip/hip_ext.h>
 #include <math.h>
 
 #include "common.h"
@@ -384,17 +385,17 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeAttnArgs a) {
     out[lane + 64] = from_f32<TO>(o1 * inv);
 }
 
-void launch_decode_attn(const DecodeAttnArgs &a, DType dt, hipStream_t s) {
+void launch_decode_attn(const DecodeAttnArgs &a, DType dt, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     if (a.B <= 0) return;
     const int group = a.H / a.Hkv;
     const int items = a.B * a.Hkv * a.n_chunks;
-    const int blocks = (items + 3) / 4;
+    const dim3 grid((items + 3) / 4), block(256);
     if (dt == DT_BF16) {
-        if (group == 2) hipLaunchKernelGGL((decode_attn_kernel<bf16_t, 2>), dim3(blocks), dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((decode_attn_kernel<bf16_t, 1>), dim3(blocks), dim3(256), 0, s, a);
+        if (group == 2) hipExtLaunchKernelGGL((decode_attn_kernel<bf16_t, 2>), grid, block, 0, s, ev0, ev1, 0, a);
+        else hipExtLaunchKernelGGL((decode_attn_kernel<bf16_t, 1>), grid, block, 0, s, ev0, ev1, 0, a);
     } else {
-        if (group == 2) hipLaunchKernelGGL((decode_attn_kernel<float, 2>), dim3(blocks), dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((decode_attn_kernel<float, 1>), dim3(blocks), dim3(256), 0, s, a);
+        if (group == 2) hipExtLaunchKernelGGL((decode_attn_kernel<float, 2>), grid, block, 0, s, ev0, ev1, 0, a);
+        else hipExtLaunchKernelGGL((decode_attn_kernel<float, 1>), grid, block, 0, s, ev0, ev1, 0, a);
     }
 }
 

@@ -110,7 +110,9 @@ struct DecodeAttnArgs {
     int shared;           // prefill of one stream: query b is at position pos[0] + b and
                           // every query reads page-table row 0 (causal by construction)
 };
-void launch_decode_attn(const DecodeAttnArgs &a, DType dt, hipStream_t s);
+// ev0 / ev1 (optional): events stamped with the kernel's own start and end
+void launch_decode_attn(const DecodeAttnArgs &a, DType dt, hipStream_t s, hipEvent_t ev0 = nullptr,
+                        hipEvent_t ev1 = nullptr);
 void launch_decode_combine(const DecodeAttnArgs &a, DType dt, hipStream_t s);
 
 // ---- K6: bidirectional flash attention (bf16 MFMA) ---------------------------------

@@ -102,20 +102,26 @@ void free_all(ttsbb_ctx *c) {
 
 int round_up(int v, int m) { return (v + m - 1) / m * m; }
 
-// Event pair around one launch of a profiled kernel class.
+// Event pair around one launch of a profiled kernel class.  With `attach` the scope
+// records nothing itself: the single launch inside it takes start() / stop() and has
+// the runtime stamp them from its own dispatch (hipExtLaunchKernel), so the pair times
+// the kernel alone, without two extra packets in the stream.
 struct KScope {
     ttsbb_ctx *c;
     int idx = -1;
-    KScope(ttsbb_ctx *ctx, int k) : c(ctx) {
+    bool attach;
+    KScope(ttsbb_ctx *ctx, int k, bool attach_to_launch = false) : c(ctx), attach(attach_to_launch) {
         Prof &p = c->prof;
         if (((p.mask >> k) & 1u) && p.used < p.cap) {
             idx = p.used++;
             p.cls[idx] = k;
-            hipEventRecord(p.ev[2 * idx], c->stream);
+            if (!attach) hipEventRecord(p.ev[2 * idx], c->stream);
         }
     }
+    hipEvent_t start() const { return idx >= 0 ? c->prof.ev[2 * idx] : nullptr; }
+    hipEvent_t stop() const { return idx >= 0 ? c->prof.ev[2 * idx + 1] : nullptr; }
     ~KScope() {
-        if (idx >= 0) hipEventRecord(c->prof.ev[2 * idx + 1], c->stream);
+        if (idx >= 0 && !attach) hipEventRecord(c->prof.ev[2 * idx + 1], c->stream);
     }
 };
 
@@ -664,8 +670,8 @@ ttsbb_status paged_forward(ttsbb_ctx *ctx, int32_t batch, float *x, int32_t *pos
         d.scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
         d.shared = prefill ? 1 : 0;
         {
-            KScope k(ctx, TTSBB_K_DECODE_ATTN);
-            launch_decode_attn(d, ctx->dt, ctx->stream);
+            KScope k(ctx, TTSBB_K_DECODE_ATTN, true);
+            launch_decode_attn(d, ctx->dt, ctx->stream, k.start(), k.stop());
         }
         {
             KScope k(ctx, TTSBB_K_DECODE_COMBINE);
