@@ -13,10 +13,13 @@ Inputs are seeded synthetic tensors resident in HBM before the timed region.  `v
 decode tokens/s (64 tokens per step over the decode part of the step); MaskGIT frames/s
 and MFMA utilisation, and decode-attention HBM GB/s are reported beside it.
 
-Other workloads (--workload): c2 (batch-1 decode, 28 layers, KV 1000, 16 x 2048 tables,
-3072 head), c3 (5-layer code predictor, 256 frames x 16 positions), c1 (1 layer, fp32).
+Further figures, each timed on its own after the step: a guided and a guided + sampled
+MaskGIT step, a 200-token causal prefill, the codec RVQ decode of 750 frames, and the
+batch-1 decode loop (16 x 2048 codebooks, 3072 head, KV 1000, 148 steps) run eagerly and as
+one captured HIP graph.  The other workloads (batch-1 decode, the 5-layer code predictor,
+the single fp32 layer) are parity-test cases.
 
-    python bench.py [--steps K] [--warmup W] [--workload c5c4|c2|c3|c1] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--copy-calibration MIB]
 """
 from __future__ import annotations
 
@@ -362,6 +365,77 @@ def run_prefill(T, torch, dec, n_tokens, iters):
     return total / iters
 
 
+def run_c2_graph(T, torch, dec, n_steps=148):
+    """Batch-1 decode loop of the 16-codebook / 3072-head configuration (28 layers, KV
+    1000 -> 1148, codes drawn up front): timed eagerly, then captured once as ONE HIP graph
+    of all n_steps steps (torch's stream capture on the context's own stream) and timed as
+    one replay.  The layer weights are the decode context's; the two runs' argmax
+    trajectories must agree."""
+    from workload import configs as CFG, device as DEV, gen
+    w = CFG.c2()
+    e = w.extra
+    L0, K, V, HV = e["prefill"][0], e["n_cb"], e["cb_vocab"], e["head_vocab"]
+    side = torch.cuda.Stream()
+    dev, fn = dec.keep
+    cfg = T.ttsbb_default_config()
+    cfg.n_layers = len(dev)
+    cfg.dtype = T.BF16
+    cfg.max_rows, cfg.max_pos, cfg.max_head_cols = 64, 2048, 4096
+    layers = [T.make_layer(*[d[k] for k in ("attn_norm", "q_norm", "k_norm", "ffn_norm", "wq", "wk",
+                                             "wv", "wo", "w_gate", "w_up", "w_down")]) for d in dev]
+    ctx = T.ttsbb_create(cfg, layers, fn, side.cuda_stream)
+    try:
+        pt, n_pages = CFG.page_table(w.seed, [L0 + n_steps + 1])
+        pool = DEV.kv_pool(w.seed, w.shape, len(dev), [L0], pt, n_pages, True)
+        pt_d = torch.from_numpy(pt).cuda()
+        tables = DEV.table(w.seed, gen.KIND_CB_TABLE, 0, K * V, 1024, True)
+        head = DEV.table(w.seed, gen.KIND_HEAD, 0, HV, 1024, True)
+        codes = np.stack([gen.uniform_int(w.seed, gen.stream_id(gen.KIND_CODES, s), (1, K), V)
+                          for s in range(n_steps)])
+        codes_d = torch.from_numpy(codes.astype(np.int32)).cuda()
+        pos = torch.tensor([L0], dtype=torch.int32, device="cuda")
+        x = torch.empty((1, 1024), dtype=torch.float32, device="cuda")
+        am = torch.empty((n_steps, 1), dtype=torch.int32, device="cuda")
+        torch.cuda.synchronize()
+
+        def loop():
+            for s in range(n_steps):
+                T.ttsbb_codebook_embed(ctx, 1, K, codes_d[s], tables, V, None, None, None, 0, x)
+                T.ttsbb_decode_step(ctx, 1, x, pos, pt_d, pt.shape[1], pool, n_pages, head, 1, HV, am[s])
+
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(side):
+            pos.fill_(L0)
+            loop()                                  # warm
+            pos.fill_(L0)
+            e0.record(side)
+            loop()
+            e1.record(side)
+            torch.cuda.synchronize()
+            eager_ms = e0.elapsed_time(e1)
+            am_eager = am.clone()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                loop()
+            pos.fill_(L0)
+            g.replay()                              # warm
+            pos.fill_(L0)
+            e0.record(side)
+            g.replay()
+            e1.record(side)
+            torch.cuda.synchronize()
+            graph_ms = e0.elapsed_time(e1)
+        if not torch.equal(am, am_eager) or int(pos.item()) != L0 + n_steps:
+            raise RuntimeError("graph replay of the batch-1 decode loop differs from the eager loop")
+        if T.ttsbb_sync(ctx) != T.OK:
+            raise RuntimeError("device flag raised by the batch-1 decode loop")
+        del g
+        return eager_ms / n_steps, graph_ms / n_steps
+    finally:
+        torch.cuda.synchronize()
+        T.ttsbb_destroy(ctx)
+
+
 def run_c5c4(args, T, torch):
     if args.copy_calibration:
         copy_calibration(torch, args.copy_calibration)
@@ -439,6 +513,10 @@ def run_c5c4(args, T, torch):
     # Codec RVQ decode of the pass's 750 frames (8 codebooks x 1024 x 64 -> 1024, fp32)
     rvq_us = run_rvq(T, torch, mg.e["n_frames"], args.steps)
 
+    # Batch-1 decode loop (16 codebooks, 3072 head, KV 1000, 148 steps): eager vs one graph
+    log("timed: batch-1 decode loop, eager and as one HIP graph")
+    c2_eager_ms, c2_graph_ms = run_c2_graph(T, torch, dec)
+
     attn_ms, attn_n = timed_attn
     attn_avg_ms = attn_ms / max(1, attn_n)
     attn_bytes = dec.attn_bytes(args.warmup, args.steps)
@@ -485,6 +563,10 @@ def run_c5c4(args, T, torch):
                             "frames_per_s": round(mg.e["n_frames"] / (smp_ms * 1e-3 * mg.e["n_steps"]), 1),
                             "note": "guided + sampled step: cfg_scale 2.0, top-k ratio 0.1, class and position "
                                     "temperature 1.0, Gumbel uniforms resident"},
+        "decode_b1_loop": {"eager_ms_per_step": round(c2_eager_ms, 4), "graph_ms_per_step": round(c2_graph_ms, 4),
+                           "graph_tokens_per_s": round(1.0 / (c2_graph_ms * 1e-3), 1), "steps": 148,
+                           "note": "batch-1 28-layer decode, 16 x 2048 summed codebooks, 3072 head + argmax, "
+                                   "KV 1000 -> 1148: eager launches vs the 148 steps captured as one HIP graph"},
         "roofline": {"kernel": "decode_attn (split-sequence paged GQA attention)", "bound": "hbm",
                      "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),

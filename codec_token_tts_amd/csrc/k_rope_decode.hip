@@ -390,12 +390,16 @@ void launch_decode_attn(const DecodeAttnArgs &a, DType dt, hipStream_t s, hipEve
     const int group = a.H / a.Hkv;
     const int items = a.B * a.Hkv * a.n_chunks;
     const dim3 grid((items + 3) / 4), block(256);
+    auto go = [&](auto kernel) {
+        if (ev0 || ev1) hipExtLaunchKernelGGL(kernel, grid, block, 0, s, ev0, ev1, 0, a);
+        else hipLaunchKernelGGL(kernel, grid, block, 0, s, a);  // plain launch (graph capture)
+    };
     if (dt == DT_BF16) {
-        if (group == 2) hipExtLaunchKernelGGL((decode_attn_kernel<bf16_t, 2>), grid, block, 0, s, ev0, ev1, 0, a);
-        else hipExtLaunchKernelGGL((decode_attn_kernel<bf16_t, 1>), grid, block, 0, s, ev0, ev1, 0, a);
+        if (group == 2) go(decode_attn_kernel<bf16_t, 2>);
+        else go(decode_attn_kernel<bf16_t, 1>);
     } else {
-        if (group == 2) hipExtLaunchKernelGGL((decode_attn_kernel<float, 2>), grid, block, 0, s, ev0, ev1, 0, a);
-        else hipExtLaunchKernelGGL((decode_attn_kernel<float, 1>), grid, block, 0, s, ev0, ev1, 0, a);
+        if (group == 2) go(decode_attn_kernel<float, 2>);
+        else go(decode_attn_kernel<float, 1>);
     }
 }
 

@@ -39,7 +39,7 @@ class Model:
 
     def __init__(self, shape: CFG.Shape, n_layers: int, bf16: bool, seed: int = 0,
                  gains: str = "ones", max_rows: int = 1024, max_pos: int = 8192,
-                 max_head_cols: int = 8200):
+                 max_head_cols: int = 8200, stream=None):
         from codec_token_tts_amd import ttsbb as T
         self.T = T
         self.shape, self.n_layers, self.bf16, self.seed, self.gains = shape, n_layers, bf16, seed, gains
@@ -56,7 +56,8 @@ class Model:
         self.layers = [T.make_layer(d["attn_norm"], d["q_norm"], d["k_norm"], d["ffn_norm"],
                                     d["wq"], d["wk"], d["wv"], d["wo"], d["w_gate"], d["w_up"],
                                     d["w_down"]) for d in self.dev]
-        stream = torch().cuda.current_stream().cuda_stream
+        if stream is None:
+            stream = torch().cuda.current_stream().cuda_stream
         self.ctx = T.ttsbb_create(cfg, self.layers, self.final_norm, stream)
         self._oracle_layers = None
 
