@@ -32,17 +32,6 @@ template <typename T> __device__ __forceinline__ T from_f32(float v);
 template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
 template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) { return f32_to_bf16(v); }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
-    return v;
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
-    return v;
-}
 
 // Sum over aligned groups of `G` lanes (G a power of two <= 64).
 // Cross-lane move inside a 16-lane row through DPP (a VALU operand modifier, no LDS
@@ -70,6 +59,26 @@ __device__ __forceinline__ float group_sum(float v) {
 #pragma unroll
     for (int o = 16; o < G; o <<= 1) v += __shfl_xor(v, o, WAVE);
     return v;
+}
+
+// Whole-wave sum / maximum (all 64 lanes active): DPP inside each 16-lane row, then the
+// four row results are read into scalar registers and combined, so no step goes through
+// LDS.  Every lane receives the result.
+__device__ __forceinline__ float readlane_f(float v, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+    v = group_sum<16>(v);
+    return (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, dpp_f<DPP_XOR1>(v));
+    v = fmaxf(v, dpp_f<DPP_XOR2>(v));
+    v = fmaxf(v, dpp_f<DPP_HALF_MIRROR>(v));
+    v = fmaxf(v, dpp_f<DPP_MIRROR>(v));
+    return fmaxf(fmaxf(readlane_f(v, 0), readlane_f(v, 16)), fmaxf(readlane_f(v, 32), readlane_f(v, 48)));
 }
 
 // (value, index) argmax step: larger value wins, equal values keep the lower index.

@@ -24,73 +24,100 @@
 
 namespace ttsbb {
 
-template <typename TKV>
+template <typename TKV, bool MULTI>
 __global__ __launch_bounds__(256) void rope_kv_kernel(RopeKvArgs a) {
+    constexpr int MAXJ = 8;  // heads per wave per pass (MULTI: more than 4 * MAXJ heads)
     const int m = blockIdx.x;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int width = (a.H + 2 * a.Hkv) * 128;
     const float *row = a.qkv + (int64_t)m * width;
+    // dense mode leaves V to the transpose kernel below
+    const int jobs = a.dense ? a.H + a.Hkv : a.H + 2 * a.Hkv;
 
+    // Loads complete in order: the position goes first, then all of the first pass's
+    // row values (they do not depend on it), and only then the position-dependent
+    // page-table and RoPE-table loads, so no wait drains more than it needs.
     int p = a.dense ? m : (a.shared ? a.pos[0] + m : a.pos[m]);
+    float u[MAXJ], u2[MAXJ];
+#pragma unroll
+    for (int i = 0; i < MAXJ; ++i) {
+        const int j = min(wave + 4 * i, jobs - 1);  // clamped: unconditional loads
+        u[i] = row[j * 128 + lane];
+        u2[i] = row[j * 128 + 64 + lane];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // position-dependent loads, all issued before any check (indices clamped in range)
+    const int pc = min(max(p, 0), a.max_pos - 1);
+    const int pi = a.dense ? 0 : min(pc / a.page, a.max_pages - 1);  // dense mode: no page table
+    const int page_id = a.dense ? 0 : a.page_table[(int64_t)(a.shared ? 0 : m) * a.max_pages + pi];
+    const float2 cs = a.rope[(int64_t)pc * 64 + lane];
+    const float gq0 = a.q_gain[lane], gq1 = a.q_gain[lane + 64];
+    const float gk0 = a.k_gain[lane], gk1 = a.k_gain[lane + 64];
+    const int slot = a.dense ? 0 : pc % a.page;
     bool ok = true;
-    int page_id = 0, slot = 0;
-    if (p < 0 || p >= a.max_pos) {
+    if (p != pc) {
         if (threadIdx.x == 0) raise_flag(a.flag, FLAG_POSITION);
-        p = p < 0 ? 0 : a.max_pos - 1;
         ok = false;
     }
     if (!a.dense) {
-        const int pi = p / a.page;
-        if (pi >= a.max_pages) {
+        if (pc / a.page >= a.max_pages) {
             if (threadIdx.x == 0) raise_flag(a.flag, FLAG_POSITION);
             ok = false;
-        } else {
-            page_id = a.page_table[(int64_t)(a.shared ? 0 : m) * a.max_pages + pi];
-            slot = p % a.page;
-            if (page_id < 0 || page_id >= a.n_pages) {
-                if (threadIdx.x == 0) raise_flag(a.flag, FLAG_PAGE);
-                ok = false;
-            }
+        } else if (page_id < 0 || page_id >= a.n_pages) {
+            if (threadIdx.x == 0) raise_flag(a.flag, FLAG_PAGE);
+            ok = false;
         }
     }
-    const float2 cs = a.rope[(int64_t)p * 64 + lane];
 
-    // dense mode leaves V to the transpose kernel below
-    const int jobs = a.dense ? a.H + a.Hkv : a.H + 2 * a.Hkv;
-    for (int j = wave; j < jobs; j += 4) {
-        const float *src = row + j * 128;
-        float u = src[lane], u2 = src[lane + 64];
-        if (j < a.H + a.Hkv) {
-            const float *g = j < a.H ? a.q_gain : a.k_gain;
-            const float ss = wave_sum(u * u + u2 * u2);
-            const float inv = 1.0f / sqrtf(ss / 128.0f + a.eps);
-            const float x0 = u * inv * g[lane], x1 = u2 * inv * g[lane + 64];
-            u = x0 * cs.x - x1 * cs.y;
-            u2 = x1 * cs.x + x0 * cs.y;
-        }
-        if (j < a.H) {
-            if (a.dense) {
-                bf16_t *q = reinterpret_cast<bf16_t *>(a.q_out) + (int64_t)m * a.H * 128 + j * 128;
-                q[lane] = f32_to_bf16(u);
-                q[lane + 64] = f32_to_bf16(u2);
-            } else {
-                float *q = reinterpret_cast<float *>(a.q_out) + (int64_t)m * a.H * 128 + j * 128;
-                q[lane] = u;
-                q[lane + 64] = u2;
+    // every operand of the first pass has been requested: one wait for all of them, so
+    // that the stores below are never waited on
+    __builtin_amdgcn_s_waitcnt(0);
+    for (int j0 = wave; j0 < (MULTI ? jobs : wave + 1); j0 += 4 * MAXJ) {
+        if (MULTI && j0 != wave) {  // further passes
+#pragma unroll
+            for (int i = 0; i < MAXJ; ++i) {
+                const int j = min(j0 + 4 * i, jobs - 1);
+                u[i] = row[j * 128 + lane];
+                u2[i] = row[j * 128 + 64 + lane];
             }
-            continue;
         }
-        const int kv = j < a.H + a.Hkv ? 0 : 1;
-        const int h = j - a.H - kv * a.Hkv;
-        if (a.dense) {
-            bf16_t *k = a.kbuf + ((int64_t)h * a.s_pad + m) * 128;
-            k[lane] = f32_to_bf16(u);
-            k[lane + 64] = f32_to_bf16(u2);
-        } else if (ok) {
-            TKV *dst = reinterpret_cast<TKV *>(a.pool_layer) +
-                       ((((int64_t)page_id * 2 + kv) * a.Hkv + h) * a.page + slot) * 128;
-            dst[lane] = from_f32<TKV>(u);
-            dst[lane + 64] = from_f32<TKV>(u2);
+#pragma unroll
+        for (int i = 0; i < MAXJ; ++i) {
+            const int j = j0 + 4 * i;
+            if (j >= jobs) continue;
+            float x = u[i], x2 = u2[i];
+            if (j < a.H + a.Hkv) {
+                const float ss = wave_sum(x * x + x2 * x2);
+                const float inv = 1.0f / sqrtf(ss / 128.0f + a.eps);
+                const float x0 = x * inv * (j < a.H ? gq0 : gk0), x1 = x2 * inv * (j < a.H ? gq1 : gk1);
+                x = x0 * cs.x - x1 * cs.y;
+                x2 = x1 * cs.x + x0 * cs.y;
+            }
+            if (j < a.H) {
+                if (a.dense) {
+                    bf16_t *q = reinterpret_cast<bf16_t *>(a.q_out) + (int64_t)m * a.H * 128 + j * 128;
+                    q[lane] = f32_to_bf16(x);
+                    q[lane + 64] = f32_to_bf16(x2);
+                } else {
+                    float *q = reinterpret_cast<float *>(a.q_out) + (int64_t)m * a.H * 128 + j * 128;
+                    q[lane] = x;
+                    q[lane + 64] = x2;
+                }
+                continue;
+            }
+            const int kv = j < a.H + a.Hkv ? 0 : 1;
+            const int h = j - a.H - kv * a.Hkv;
+            if (a.dense) {
+                bf16_t *k = a.kbuf + ((int64_t)h * a.s_pad + m) * 128;
+                k[lane] = f32_to_bf16(x);
+                k[lane + 64] = f32_to_bf16(x2);
+            } else if (ok) {
+                TKV *dst = reinterpret_cast<TKV *>(a.pool_layer) +
+                           ((((int64_t)page_id * 2 + kv) * a.Hkv + h) * a.page + slot) * 128;
+                dst[lane] = from_f32<TKV>(x);
+                dst[lane + 64] = from_f32<TKV>(x2);
+            }
         }
     }
 }
@@ -117,10 +144,14 @@ __global__ __launch_bounds__(256) void dense_vt_kernel(RopeKvArgs a) {
 
 void launch_rope_kv(const RopeKvArgs &a, DType kv_dt, hipStream_t s) {
     if (a.M <= 0) return;
-    if (kv_dt == DT_BF16 || a.dense)
-        hipLaunchKernelGGL(rope_kv_kernel<bf16_t>, dim3(a.M), dim3(256), 0, s, a);
-    else
-        hipLaunchKernelGGL(rope_kv_kernel<float>, dim3(a.M), dim3(256), 0, s, a);
+    const bool multi = (a.dense ? a.H + a.Hkv : a.H + 2 * a.Hkv) > 32;
+    if (kv_dt == DT_BF16 || a.dense) {
+        if (multi) hipLaunchKernelGGL((rope_kv_kernel<bf16_t, true>), dim3(a.M), dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((rope_kv_kernel<bf16_t, false>), dim3(a.M), dim3(256), 0, s, a);
+    } else {
+        if (multi) hipLaunchKernelGGL((rope_kv_kernel<float, true>), dim3(a.M), dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((rope_kv_kernel<float, false>), dim3(a.M), dim3(256), 0, s, a);
+    }
     if (a.dense)
         hipLaunchKernelGGL(dense_vt_kernel, dim3((a.M + 63) / 64, a.Hkv), dim3(256), 0, s, a);
 }
@@ -330,11 +361,14 @@ void decode_attn_kernel(DecodeAttnArgs a) {
     }
 }
 
-// Merge of the chunk partials of one (stream, head): lane c < nc loads (m_c, l_c) so the
-// maximum and the weights come from one wave reduction; the accumulators are then read
-// four chunks at a time so that their loads overlap.
+// Merge of the chunk partials of one (stream, head), 32 chunks per pass: lane c loads
+// (m_c, l_c) while every lane loads its two output dims of all the pass's chunks, so a
+// pass is one round of loads; the maximum and the weights come from wave reductions and
+// the accumulators are added in chunk order.  Passes after the first rescale the running
+// sums (more than 32 chunks: streams split into short chunks).
 template <typename TO>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeAttnArgs a) {
+    constexpr int CB = 32;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int item = blockIdx.x * 4 + wave;
     if (item >= a.B * a.H) return;
@@ -344,40 +378,33 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeAttnArgs a) {
     if (L > cap) L = cap;
     const int nc = min(a.n_chunks, (L + a.chunk - 1) / a.chunk);
     const float *part = a.part + ((int64_t)b * a.H + h) * a.n_chunks * PART_STRIDE;
-    float M = -INFINITY, lsum = 0.f;
-    for (int c0 = 0; c0 < nc; c0 += 64) {
-        const int c = c0 + lane;
-        M = fmaxf(M, c < nc ? part[(int64_t)c * PART_STRIDE] : -INFINITY);
-    }
-    M = wave_max(M);
-    for (int c0 = 0; c0 < nc; c0 += 64) {
-        const int c = c0 + lane;
-        if (c < nc) lsum += exp2f(part[(int64_t)c * PART_STRIDE] - M) * part[(int64_t)c * PART_STRIDE + 1];
-    }
-    lsum = wave_sum(lsum);
-    float o0 = 0.f, o1 = 0.f;
-    int c = 0;
-    for (; c + 4 <= nc; c += 4) {
-        float w[4], x0[4], x1[4];
+    float M = -INFINITY, lsum = 0.f, o0 = 0.f, o1 = 0.f;
+    for (int c0 = 0; c0 < nc; c0 += CB) {
+        const int n = min(CB, nc - c0);
+        const int cl = c0 + min(lane, n - 1);  // clamped: unconditional loads
+        const float ml = part[(int64_t)cl * PART_STRIDE], ll = part[(int64_t)cl * PART_STRIDE + 1];
+        float x0[CB], x1[CB];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const float *pc = part + (int64_t)(c + u) * PART_STRIDE;
-            w[u] = pc[0];
+        for (int u = 0; u < CB; ++u) {
+            const float *pc = part + (int64_t)(c0 + min(u, n - 1)) * PART_STRIDE;
             x0[u] = pc[4 + lane];
             x1[u] = pc[4 + 64 + lane];
         }
+        __builtin_amdgcn_sched_barrier(0);
+        const float mn = fmaxf(M, wave_max(lane < n ? ml : -INFINITY));
+        const float sc = exp2f(M - mn);  // 0 on the first pass (M = -inf)
+        const float wl = lane < n ? exp2f(ml - mn) : 0.f;
+        lsum = lsum * sc + wave_sum(wl * ll);
+        o0 *= sc;
+        o1 *= sc;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const float wu = exp2f(w[u] - M);
-            o0 += wu * x0[u];
-            o1 += wu * x1[u];
+        for (int u = 0; u < CB; ++u) {
+            if (u >= n) continue;
+            const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), u));
+            o0 += w * x0[u];
+            o1 += w * x1[u];
         }
-    }
-    for (; c < nc; ++c) {
-        const float *pc = part + (int64_t)c * PART_STRIDE;
-        const float wu = exp2f(pc[0] - M);
-        o0 += wu * pc[4 + lane];
-        o1 += wu * pc[4 + 64 + lane];
+        M = mn;
     }
     const float inv = 1.0f / lsum;
     TO *out = reinterpret_cast<TO *>(a.out) + (int64_t)b * a.H * 128 + h * 128;
