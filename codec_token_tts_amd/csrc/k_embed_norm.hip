@@ -76,52 +76,92 @@ void launch_embed(const EmbedArgs &a, DType dt, hipStream_t s) {
         hipLaunchKernelGGL(embed_kernel<float>, dim3(a.n_rows), dim3(256), 0, s, a);
 }
 
-template <typename TO>
+template <typename TO, int NP>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(float *x, int ldx, int hidden, const float *g, float eps,
-                                                      TO *out, const float *pend, int n_pend, int64_t pend_ld,
+                                                      TO *out, const float *pend, int64_t pend_ld,
                                                       int64_t pend_stride) {
+    constexpr int MAXC = 4;  // float4 columns per thread held in registers (hidden <= 4096)
     __shared__ float red[4];
     const int r = blockIdx.x;
     float *xr = x + (int64_t)r * ldx;
+    // every load of the row (residual, deferred partials, gains) is issued up front
+    float4 v[MAXC], gg[MAXC], pp[NP > 0 ? NP : 1][MAXC];
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+        const int c = threadIdx.x * 4 + i * 1024;
+        if (c >= hidden) continue;
+        v[i] = *reinterpret_cast<const float4 *>(xr + c);
+#pragma unroll
+        for (int z = 0; z < NP; ++z)
+            pp[z][i] = *reinterpret_cast<const float4 *>(pend + z * pend_stride + (int64_t)r * pend_ld + c);
+        if (g != nullptr) gg[i] = *reinterpret_cast<const float4 *>(g + c);
+    }
     float ss = 0.f;
-    for (int c = threadIdx.x * 4; c < hidden; c += 1024) {
-        float4 v = *reinterpret_cast<const float4 *>(xr + c);
-        if (n_pend > 0) {  // deferred residual update, in split order
-            for (int z = 0; z < n_pend; ++z) {
-                const float4 p = *reinterpret_cast<const float4 *>(pend + z * pend_stride + (int64_t)r * pend_ld + c);
-                v.x += p.x;
-                v.y += p.y;
-                v.z += p.z;
-                v.w += p.w;
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+        const int c = threadIdx.x * 4 + i * 1024;
+        if (c >= hidden) continue;
+        if (NP > 0) {  // deferred residual update, in split order
+#pragma unroll
+            for (int z = 0; z < NP; ++z) {
+                v[i].x += pp[z][i].x;
+                v[i].y += pp[z][i].y;
+                v[i].z += pp[z][i].z;
+                v[i].w += pp[z][i].w;
             }
-            *reinterpret_cast<float4 *>(xr + c) = v;
+            *reinterpret_cast<float4 *>(xr + c) = v[i];
         }
-        ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+        ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
     }
     if (g == nullptr) return;
     ss = block_sum_256(ss, red);
     const float inv = 1.0f / sqrtf(ss / (float)hidden + eps);
-    for (int c = threadIdx.x * 4; c < hidden; c += 1024) {
-        float4 v = *reinterpret_cast<const float4 *>(xr + c);  // this thread's own columns
-        float4 gg = *reinterpret_cast<const float4 *>(g + c);
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+        const int c = threadIdx.x * 4 + i * 1024;
+        if (c >= hidden) continue;
         TO *o = out + (int64_t)r * hidden + c;
-        o[0] = from_f32<TO>(v.x * inv * gg.x);
-        o[1] = from_f32<TO>(v.y * inv * gg.y);
-        o[2] = from_f32<TO>(v.z * inv * gg.z);
-        o[3] = from_f32<TO>(v.w * inv * gg.w);
+        o[0] = from_f32<TO>(v[i].x * inv * gg[i].x);
+        o[1] = from_f32<TO>(v[i].y * inv * gg[i].y);
+        o[2] = from_f32<TO>(v[i].z * inv * gg[i].z);
+        o[3] = from_f32<TO>(v[i].w * inv * gg[i].w);
     }
 }
 
+template <typename TO>
+static void launch_rmsnorm_t(float *x, int ldx, int rows, int hidden, const float *gain, float eps, TO *out,
+                             hipStream_t s, const float *pend, int n_pend, int64_t pend_ld, int64_t pend_stride) {
+    const dim3 grid(rows), block(256);
+    switch (n_pend) {
+#define TTSBB_NORM_CASE(NP)                                                                                    \
+    case NP:                                                                                                   \
+        hipLaunchKernelGGL((rmsnorm_kernel<TO, NP>), grid, block, 0, s, x, ldx, hidden, gain, eps, out, pend, \
+                           pend_ld, pend_stride);                                                              \
+        break;
+        TTSBB_NORM_CASE(0)
+        TTSBB_NORM_CASE(1)
+        TTSBB_NORM_CASE(2)
+        TTSBB_NORM_CASE(3)
+        TTSBB_NORM_CASE(4)
+        TTSBB_NORM_CASE(5)
+        TTSBB_NORM_CASE(6)
+        TTSBB_NORM_CASE(7)
+        TTSBB_NORM_CASE(8)
+#undef TTSBB_NORM_CASE
+    }
+}
+
+// n_pend <= 8 partial buffers, hidden <= 4096 and a multiple of 4 (checked by the caller)
 void launch_rmsnorm(float *x, int ldx, int rows, int hidden, const float *gain, float eps, void *out,
                     DType out_dt, hipStream_t s, const float *pend, int n_pend, int64_t pend_ld,
                     int64_t pend_stride) {
     if (rows <= 0) return;
     if (out_dt == DT_BF16)
-        hipLaunchKernelGGL(rmsnorm_kernel<bf16_t>, dim3(rows), dim3(256), 0, s, x, ldx, hidden, gain, eps,
-                           reinterpret_cast<bf16_t *>(out), pend, n_pend, pend_ld, pend_stride);
+        launch_rmsnorm_t(x, ldx, rows, hidden, gain, eps, reinterpret_cast<bf16_t *>(out), s, pend, n_pend, pend_ld,
+                         pend_stride);
     else
-        hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(rows), dim3(256), 0, s, x, ldx, hidden, gain, eps,
-                           reinterpret_cast<float *>(out), pend, n_pend, pend_ld, pend_stride);
+        launch_rmsnorm_t(x, ldx, rows, hidden, gain, eps, reinterpret_cast<float *>(out), s, pend, n_pend, pend_ld,
+                         pend_stride);
 }
 
 __global__ void increment_kernel(int32_t *v, int n, int delta) {

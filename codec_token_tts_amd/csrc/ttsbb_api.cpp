@@ -215,7 +215,7 @@ TTSBB_API ttsbb_status ttsbb_create(const ttsbb_config *cfg, const ttsbb_layer *
             !L.wo || !L.w_gate || !L.w_up || !L.w_down)
             return TTSBB_INVALID_ARG;
     }
-    if (g.head_dim != 128 || g.hidden % 128 != 0 || g.ffn % 128 != 0 ||
+    if (g.head_dim != 128 || g.hidden % 128 != 0 || g.hidden > 4096 || g.ffn % 128 != 0 ||
         g.n_heads % g.n_kv_heads != 0 || (g.n_heads / g.n_kv_heads > 2) || g.kv_page != 16)
         return TTSBB_UNSUPPORTED;
 

@@ -19,8 +19,8 @@
  *   x2 = x1 + Wd (silu(Wg h2) * Wu h2),  h2 = RMSNorm(x1; g_ffn)   SwiGLU, no biases
  * with RMSNorm(x; g) = x / sqrt(mean(x^2) + eps) * g and RoPE pairing dimension j with
  * j + head_dim/2 at angle pos * theta^(-2j/head_dim) (ncnn port, "mRoPE结论").
- * Supported shapes: head_dim 128, hidden and ffn multiples of 128, n_heads a multiple
- * of n_kv_heads with group size 1 or 2.
+ * Supported shapes: head_dim 128, hidden and ffn multiples of 128 (hidden at most 4096),
+ * n_heads a multiple of n_kv_heads with group size 1 or 2.
  *
  * Precision: in TTSBB_BF16 mode the weights, embedding tables, heads, KV cache and the
  * operands of every matrix product are bf16; the residual stream, all accumulations,
