@@ -785,16 +785,22 @@ template <> struct Vec<float> {
     }
 };
 
-template <typename T, int EPI>
+// KI > 0: K is exactly KI chunks of 64 lanes x V elements and every weight load of the
+// wave is issued up front; KI == 0: any K, one chunk per loop trip.  NORM: the A operand
+// is RMSNorm(x) * gain computed in the prologue from the fp32 residual rows g.nx (the
+// row's sum of squares is reduced with the thread -> column mapping and the order of the
+// RMSNorm kernel, and the operand is rounded to T as that kernel stores it, so the
+// product is bit-identical to RMSNorm followed by the plain GEMV).
+template <typename T, int EPI, int KI, bool NORM>
 __global__ __launch_bounds__(256) void gemv(GemmArgs g) {
-    constexpr int V = Vec<T>::N;
+    constexpr int V = Vec<T>::N, CH = 64 * V;
+    constexpr int KB = KI > 0 ? KI : 1;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int unit0 = (blockIdx.x * 4 + wave) * GEMV_UNITS;
     const int n_units = (EPI == EPI_SWIGLU) ? g.N / 2 : g.N;
     const T *A = reinterpret_cast<const T *>(g.A);
 
     const T *wr[2 * GEMV_UNITS];
-    int nw = 0;
 #pragma unroll
     for (int u = 0; u < GEMV_UNITS; ++u) {
         const int n = unit0 + u < n_units ? unit0 + u : n_units - 1;
@@ -805,7 +811,55 @@ __global__ __launch_bounds__(256) void gemv(GemmArgs g) {
             wr[u] = wrow<T>(g.w, EPI_STORE, n, g.K);
         }
     }
-    nw = (EPI == EPI_SWIGLU) ? 2 * GEMV_UNITS : GEMV_UNITS;
+    constexpr int NW = (EPI == EPI_SWIGLU) ? 2 * GEMV_UNITS : GEMV_UNITS;
+
+    float wv[KB][NW][V];
+    if (KI > 0) {  // every weight load first: they are the long-latency ones
+#pragma unroll
+        for (int c = 0; c < KB; ++c)
+#pragma unroll
+            for (int u = 0; u < NW; ++u) Vec<T>::load(wr[u] + c * CH + lane * V, wv[c][u]);
+    }
+
+    // NORM: the normalized operand rows are built once per block in LDS (bf16 or fp32
+    // as T, [M][K]); each thread normalizes the float4 columns it reduced
+    extern __shared__ __attribute__((aligned(16))) unsigned char gemv_lds[];
+    T *An = reinterpret_cast<T *>(gemv_lds);
+    if (NORM) {
+        __shared__ float red[4];
+        constexpr int MAXC = 4;  // float4 columns per thread (K <= 4096)
+        float4 gg[MAXC];
+#pragma unroll
+        for (int i = 0; i < MAXC; ++i) {
+            const int c = threadIdx.x * 4 + i * 1024;
+            if (c < g.K) gg[i] = *reinterpret_cast<const float4 *>(g.ng + c);
+        }
+        for (int m = 0; m < g.M; ++m) {
+            const float *xr = g.nx + (int64_t)m * g.K;
+            float4 v[MAXC];
+            float ss = 0.f;
+#pragma unroll
+            for (int i = 0; i < MAXC; ++i) {
+                const int c = threadIdx.x * 4 + i * 1024;
+                if (c >= g.K) continue;
+                v[i] = *reinterpret_cast<const float4 *>(xr + c);
+                ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
+            }
+            ss = block_sum_256(ss, red);
+            const float inv = 1.0f / sqrtf(ss / (float)g.K + g.neps);
+#pragma unroll
+            for (int i = 0; i < MAXC; ++i) {
+                const int c = threadIdx.x * 4 + i * 1024;
+                if (c >= g.K) continue;
+                T *o = An + (int64_t)m * g.K + c;
+                o[0] = from_f32<T>(v[i].x * inv * gg[i].x);
+                o[1] = from_f32<T>(v[i].y * inv * gg[i].y);
+                o[2] = from_f32<T>(v[i].z * inv * gg[i].z);
+                o[3] = from_f32<T>(v[i].w * inv * gg[i].w);
+            }
+        }
+        __syncthreads();
+    }
 
     float acc[GEMV_MAXM][2 * GEMV_UNITS];
 #pragma unroll
@@ -813,23 +867,46 @@ __global__ __launch_bounds__(256) void gemv(GemmArgs g) {
 #pragma unroll
         for (int u = 0; u < 2 * GEMV_UNITS; ++u) acc[m][u] = 0.f;
 
-    for (int k0 = lane * V; k0 < g.K; k0 += 64 * V) {
-        float wv[2 * GEMV_UNITS][V];
-#pragma unroll
-        for (int u = 0; u < 2 * GEMV_UNITS; ++u)
-            if (u < nw) Vec<T>::load(wr[u] + k0, wv[u]);
+    if (KI > 0) {
+        // weights are in registers: per row, all of its operand chunks in one round of loads
 #pragma unroll
         for (int m = 0; m < GEMV_MAXM; ++m) {
             if (m >= g.M) break;
-            float av[V];
-            Vec<T>::load(A + (int64_t)m * g.lda + k0, av);
+            float av[KB][V];
 #pragma unroll
-            for (int u = 0; u < 2 * GEMV_UNITS; ++u) {
-                if (u >= nw) continue;
-                float s = acc[m][u];
+            for (int c = 0; c < KB; ++c) {
+                const int k0 = c * CH + lane * V;
+                if (NORM) Vec<T>::load(An + (int64_t)m * g.K + k0, av[c]);
+                else Vec<T>::load(A + (int64_t)m * g.lda + k0, av[c]);
+            }
 #pragma unroll
-                for (int e = 0; e < V; ++e) s = fmaf(av[e], wv[u][e], s);
-                acc[m][u] = s;
+            for (int c = 0; c < KB; ++c)
+#pragma unroll
+                for (int u = 0; u < NW; ++u) {
+                    float s = acc[m][u];
+#pragma unroll
+                    for (int e = 0; e < V; ++e) s = fmaf(av[c][e], wv[c][u][e], s);
+                    acc[m][u] = s;
+                }
+        }
+    } else {
+        for (int k0 = lane * V; k0 < g.K; k0 += CH) {
+            float wl[NW][V];
+#pragma unroll
+            for (int u = 0; u < NW; ++u) Vec<T>::load(wr[u] + k0, wl[u]);
+#pragma unroll
+            for (int m = 0; m < GEMV_MAXM; ++m) {
+                if (m >= g.M) break;
+                float av[V];
+                if (NORM) Vec<T>::load(An + (int64_t)m * g.K + k0, av);
+                else Vec<T>::load(A + (int64_t)m * g.lda + k0, av);
+#pragma unroll
+                for (int u = 0; u < NW; ++u) {
+                    float s = acc[m][u];
+#pragma unroll
+                    for (int e = 0; e < V; ++e) s = fmaf(av[e], wl[u][e], s);
+                    acc[m][u] = s;
+                }
             }
         }
     }
@@ -838,8 +915,7 @@ __global__ __launch_bounds__(256) void gemv(GemmArgs g) {
     for (int m = 0; m < GEMV_MAXM; ++m) {
         if (m >= g.M) break;
 #pragma unroll
-        for (int u = 0; u < 2 * GEMV_UNITS; ++u)
-            if (u < nw) acc[m][u] = wave_sum(acc[m][u]);
+        for (int u = 0; u < NW; ++u) acc[m][u] = wave_sum(acc[m][u]);
     }
     if (lane != 0) return;
 #pragma unroll
@@ -861,14 +937,36 @@ __global__ __launch_bounds__(256) void gemv(GemmArgs g) {
     }
 }
 
+template <typename T, int KI, bool NORM>
+static void launch_gemv_k(const GemmArgs &g, int blocks, hipStream_t s) {
+    const size_t lds = NORM ? (size_t)g.M * g.K * sizeof(T) : 0;  // <= 64 KB (checked by the caller)
+    switch (g.epi) {
+        case EPI_STORE: hipLaunchKernelGGL((gemv<T, EPI_STORE, KI, NORM>), dim3(blocks), dim3(256), lds, s, g); break;
+        case EPI_ADD: hipLaunchKernelGGL((gemv<T, EPI_ADD, KI, NORM>), dim3(blocks), dim3(256), lds, s, g); break;
+        default: hipLaunchKernelGGL((gemv<T, EPI_SWIGLU, KI, NORM>), dim3(blocks), dim3(256), lds, s, g); break;
+    }
+}
+
 template <typename T>
 static void launch_gemv(const GemmArgs &g, hipStream_t s) {
     const int n_units = (g.epi == EPI_SWIGLU) ? g.N / 2 : g.N;
     const int blocks = (n_units + 4 * GEMV_UNITS - 1) / (4 * GEMV_UNITS);
-    switch (g.epi) {
-        case EPI_STORE: hipLaunchKernelGGL((gemv<T, EPI_STORE>), dim3(blocks), dim3(256), 0, s, g); break;
-        case EPI_ADD: hipLaunchKernelGGL((gemv<T, EPI_ADD>), dim3(blocks), dim3(256), 0, s, g); break;
-        default: hipLaunchKernelGGL((gemv<T, EPI_SWIGLU>), dim3(blocks), dim3(256), 0, s, g); break;
+    constexpr int CH = 64 * Vec<T>::N;
+    const int ki = g.K % CH == 0 ? g.K / CH : 0;
+    if (g.nx) {
+        if (ki == 2) launch_gemv_k<T, 2, true>(g, blocks, s);
+        else if (ki == 4) launch_gemv_k<T, 4, true>(g, blocks, s);
+        else launch_gemv_k<T, 0, true>(g, blocks, s);
+        return;
+    }
+    switch (ki) {
+        case 1: launch_gemv_k<T, 1, false>(g, blocks, s); break;
+        case 2: launch_gemv_k<T, 2, false>(g, blocks, s); break;
+        case 3: launch_gemv_k<T, 3, false>(g, blocks, s); break;
+        case 4: launch_gemv_k<T, 4, false>(g, blocks, s); break;
+        case 6: launch_gemv_k<T, 6, false>(g, blocks, s); break;
+        case 8: launch_gemv_k<T, 8, false>(g, blocks, s); break;
+        default: launch_gemv_k<T, 0, false>(g, blocks, s); break;
     }
 }
 
@@ -928,6 +1026,7 @@ int launch_gemm(const GemmArgs &g, DType dt, float *part, int64_t part_cap, hipS
             h.M = g.M - m0 < GEMV_MAXM ? g.M - m0 : GEMV_MAXM;
             h.A = reinterpret_cast<const float *>(g.A) + (int64_t)m0 * g.lda;
             h.C = reinterpret_cast<float *>(g.C) + (int64_t)m0 * g.ldc;
+            if (g.nx) h.nx = g.nx + (int64_t)m0 * g.K;
             launch_gemv<float>(h, s);
         }
         return 0;

@@ -58,6 +58,11 @@ struct GemmArgs {
     void *C;        // EPI_STORE / EPI_ADD: fp32 [M][ldc]; EPI_SWIGLU: operand dtype [M][ldc]
     int ldc;
     int epi;
+    // Fused RMSNorm (GEMV path only: M <= 8 rows in bf16 mode, any M in fp32 mode): when nx
+    // is set, A is RMSNorm(nx rows, fp32 [M][K]) * ng (eps neps) instead of g.A
+    const float *nx;
+    const float *ng;
+    float neps;
 };
 // part: fp32 workspace of part_cap floats for split-K partial sums.  Returns the number
 // of K splits whose partial sums are left in part[z][M][N] for the caller to add (an

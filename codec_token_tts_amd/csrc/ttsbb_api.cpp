@@ -353,6 +353,26 @@ void flush_residual(ttsbb_ctx *c, float *x, int M) {
     if (c->pend_splits > 0) norm_rows(c, x, M, nullptr);
 }
 
+// A product of at most 8 rows (any rows in fp32 mode) runs on the GEMV kernel, which can
+// compute the RMSNorm of its operand rows itself: the separate RMSNorm launch is skipped
+// when no split partials are pending and the normalized rows are not tapped.
+// (The GEMV builds the normalized rows of one launch, at most 8, in 64 KB of LDS.)
+bool gemv_rows_fold(const ttsbb_ctx *c, int M) {
+    const int rows = M < 8 ? M : 8;
+    return (c->dt == DT_F32 || M <= 8) && (int64_t)rows * c->cfg.hidden * (int64_t)c->esz <= 65536;
+}
+
+bool norm_folds(const ttsbb_ctx *c, int M, bool tapit) {
+    const int np = c->pend_rows == M ? c->pend_splits : 0;
+    return !tapit && np == 0 && gemv_rows_fold(c, M);
+}
+
+void fold_norm(const ttsbb_ctx *c, GemmArgs &a, const float *x, const float *gain) {
+    a.nx = x;
+    a.ng = gain;
+    a.neps = c->cfg.rms_eps;
+}
+
 // Residual-add projection: the product may leave its update pending in gpart.
 void add_projection(ttsbb_ctx *c, const GemmArgs &a) {
     c->pend_splits = launch_gemm(a, c->dt, c->gpart, c->gpart_cap, c->stream);
@@ -369,8 +389,10 @@ bool qkv_projection(ttsbb_ctx *c, const ttsbb_layer &L, float *x, int M, bool ta
         flush_residual(c, x, M);
         tap_dense(c, TTSBB_TAP_X_IN, x, DT_F32, M, g.hidden, g.hidden);
     }
-    norm_rows(c, x, M, L.attn_norm);
+    const bool fold = !dense && norm_folds(c, M, tapit);
+    if (!fold) norm_rows(c, x, M, L.attn_norm);
     GemmArgs a = {};
+    if (fold) fold_norm(c, a, x, L.attn_norm);
     a.A = c->h;
     a.lda = g.hidden;
     a.M = M;
@@ -425,9 +447,11 @@ void post_attention(ttsbb_ctx *c, const ttsbb_layer &L, float *x, int M, bool ta
         flush_residual(c, x, M);
         tap_dense(c, TTSBB_TAP_X_MID, x, DT_F32, M, g.hidden, g.hidden);
     }
-    norm_rows(c, x, M, L.ffn_norm);
+    const bool fold = norm_folds(c, M, tapit);
+    if (!fold) norm_rows(c, x, M, L.ffn_norm);
     if (tapit) tap_dense(c, TTSBB_TAP_H_FFN, c->h, c->dt, M, g.hidden, g.hidden);
     GemmArgs u = {};
+    if (fold) fold_norm(c, u, x, L.ffn_norm);
     u.A = c->h;
     u.lda = g.hidden;
     u.M = M;
@@ -468,9 +492,13 @@ void post_attention(ttsbb_ctx *c, const ttsbb_layer &L, float *x, int M, bool ta
     }
 }
 
-void head_gemm(ttsbb_ctx *c, const void *head, int M, int N, float *out, int ldc, int row0 = 0) {
+// Head product of rows [row0, row0 + M); with norm_x the final RMSNorm is folded into it
+// (norm_x = the residual rows, which must hold no pending split partials).
+void head_gemm(ttsbb_ctx *c, const void *head, int M, int N, float *out, int ldc, int row0 = 0,
+               const float *norm_x = nullptr) {
     const ttsbb_config &g = c->cfg;
     GemmArgs a = {};
+    if (norm_x) fold_norm(c, a, norm_x + (size_t)row0 * g.hidden, c->final_norm);
     a.A = reinterpret_cast<const char *>(c->h) + (size_t)row0 * g.hidden * c->esz;
     a.lda = g.hidden;
     a.M = M;
@@ -683,11 +711,14 @@ ttsbb_status paged_forward(ttsbb_ctx *ctx, int32_t batch, float *x, int32_t *pos
     if (!head) flush_residual(ctx, x, batch);
     if (head) {
         const int N = n_groups * group_vocab;
-        norm_rows(ctx, x, batch, ctx->final_norm);
         const int r0 = prefill ? batch - 1 : 0, rows = prefill ? 1 : batch;  // rows read out
-        if (ctx->tap_layer >= 0) tap_dense(ctx, TTSBB_TAP_HEAD_IN, ctx->h, ctx->dt, batch, g.hidden, g.hidden);
+        const bool tap_head = ctx->tap_layer >= 0;
+        const bool fold = !tap_head && gemv_rows_fold(ctx, rows);
+        if (fold) flush_residual(ctx, x, batch);
+        else norm_rows(ctx, x, batch, ctx->final_norm);
+        if (tap_head) tap_dense(ctx, TTSBB_TAP_HEAD_IN, ctx->h, ctx->dt, batch, g.hidden, g.hidden);
         float *lg = logits ? logits : ctx->logits;
-        head_gemm(ctx, head, rows, N, lg, N, r0);
+        head_gemm(ctx, head, rows, N, lg, N, r0, fold ? x : nullptr);
         if (ctx->tap_layer >= 0) tap_dense(ctx, TTSBB_TAP_LOGITS, lg, DT_F32, rows, N, N);
         {
             KScope k(ctx, TTSBB_K_ARGMAX);
