@@ -275,10 +275,17 @@ void decode_attn_kernel(DecodeAttnArgs a) {
     const int t = item / a.Hkv;
     const int c = t % a.n_chunks, b = t / a.n_chunks;
 
+    // The chunk's page ids (one per lane, clamped into the row) do not depend on the
+    // stream's length: they are requested together with it.  A page-id load inside the
+    // page loop would have to complete before the next page's addresses exist, and loads
+    // complete in order, so that wait would also drain the prefetch: they are read once.
+    const int32_t *ptab = a.page_table + (int64_t)(a.shared ? 0 : b) * a.max_pages;
+    const int p_begin = c * a.chunk;
+    const int pg_first = p_begin / a.page;
+    const int my_page = ptab[min(pg_first + lane, a.max_pages - 1)];
     int L = (a.shared ? a.pos[0] + b : a.pos[b]) + 1;
     const int cap = a.max_pages * a.page;
     if (L > cap) L = cap;
-    const int p_begin = c * a.chunk;
     if (p_begin >= L) return;
     const int p_end = min(L, p_begin + a.chunk);
 
@@ -303,13 +310,8 @@ void decode_attn_kernel(DecodeAttnArgs a) {
 
     const T *pool = reinterpret_cast<const T *>(a.pool_layer);
     const int64_t blk = (int64_t)a.page * 128;  // elements of one (page, K|V, head) block
-    const int32_t *ptab = a.page_table + (int64_t)(a.shared ? 0 : b) * a.max_pages;
     const int lane_off = rsub * 128 + d0;
-    const int pg_first = p_begin / a.page, pg_last = (p_end - 1) / a.page;
-    // The chunk's page ids (at most 64, one per lane) are read once up front: a page-id
-    // load inside the loop would have to complete before the next page's addresses exist,
-    // and loads complete in order, so that wait would also drain the prefetch.
-    const int my_page = (lane <= pg_last - pg_first) ? ptab[pg_first + lane] : 0;
+    const int pg_last = (p_end - 1) / a.page;
     auto page_of = [&](int pg) { return __builtin_amdgcn_readlane(my_page, pg - pg_first); };
     u32x4_t ka[NR], va[NR], kb2[NR], vb2[NR];
     // Ping-pong over the chunk's pages.  Every load is issued unconditionally (the index

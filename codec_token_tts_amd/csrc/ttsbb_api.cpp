@@ -635,11 +635,12 @@ ttsbb_status paged_forward(ttsbb_ctx *ctx, int32_t batch, float *x, int32_t *pos
 
     // Split of each stream's positions into chunks for the decode attention: 128
     // positions per wave (measured best on the paged workload), halved while there are
-    // fewer than 2048 (stream, KV head, chunk) work items; the partial buffer holds
+    // fewer than 256 (stream, KV head, chunk) work items (batch 1, KV ~1000: 32-position
+    // chunks, measured best against 16 and 64); the partial buffer holds
     // max_rows * MAX_CHUNKS chunks per head, and a chunk spans at most 64 pages.
     const int cap = max_pages * g.kv_page;
     int chunk = 128;
-    while (chunk > g.kv_page && (int64_t)batch * Hkv * ((cap + chunk - 1) / chunk) < 2048) chunk /= 2;
+    while (chunk > g.kv_page && (int64_t)batch * Hkv * ((cap + chunk - 1) / chunk) < 256) chunk /= 2;
     chunk = round_up(chunk, g.kv_page);
     int n_chunks = (cap + chunk - 1) / chunk;
     while ((int64_t)batch * n_chunks > (int64_t)g.max_rows * MAX_CHUNKS) {
