@@ -45,6 +45,7 @@ constexpr int DPP_XOR1 = 0xB1;         // quad_perm [1,0,3,2]
 constexpr int DPP_XOR2 = 0x4E;         // quad_perm [2,3,0,1]
 constexpr int DPP_HALF_MIRROR = 0x141; // lane i <- 7 - i inside each 8-lane half row
 constexpr int DPP_MIRROR = 0x140;      // lane i <- 15 - i inside each 16-lane row
+constexpr int DPP_ROR8 = 0x128;        // lane i <- (i + 8) mod 16 inside each 16-lane row
 
 // Sum over aligned groups of G lanes; every lane of a group ends with the same value.
 // Up to 16 lanes the steps are DPP (pair, quad, half row, row); wider groups finish

@@ -255,8 +255,38 @@ __device__ __forceinline__ void process_page(const u32x4_t (&kr)[NR], const u32x
 // One wave per (stream, KV head, chunk).  The K and V blocks of the next page are
 // loaded into a second register set while the current page is processed, so every
 // wave keeps one page (8 KB in bf16) of loads in flight behind its arithmetic.
-template <typename T, int GROUP>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 4 : 2)))
+// Value of dimension d +- 64 of the same head (the RoPE partner), held by the lane LPR/2
+// away inside the lane's row group.
+template <int LPR>
+__device__ __forceinline__ float rope_partner(float v) {
+    if constexpr (LPR == 16) return dpp_f<DPP_ROR8>(v);
+    else return __shfl_xor(v, LPR / 2, WAVE);
+}
+
+// Per-head RMSNorm + RoPE of one 128-dim head row of the step's projections, in the decode
+// kernel's lane layout (lane holds dims d0 .. d0 + EPL - 1; the LPR lanes of a row group
+// hold the whole head): y = x / sqrt(mean(x^2) + eps) * g, then dims d and d + 64 rotated
+// by the angle of pair d mod 64.
+template <int EPL, int LPR>
+__device__ __forceinline__ void norm_rope_head(const float *x, const float *gain, int d0, const float (&c)[EPL],
+                                               const float (&sn)[EPL], float eps, float (&out)[EPL]) {
+    float y[EPL], ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) ss = fmaf(x[e], x[e], ss);
+    ss = group_sum<LPR>(ss);
+    const float inv = 1.0f / sqrtf(ss / 128.0f + eps);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) y[e] = x[e] * inv * gain[e];
+    const bool first = d0 < 64;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+        const float pv = rope_partner<LPR>(y[e]);
+        out[e] = first ? y[e] * c[e] - pv * sn[e] : y[e] * c[e] + pv * sn[e];
+    }
+}
+
+template <typename T, int GROUP, bool FUSED>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? (FUSED ? 3 : 4) : 2)))
 void decode_attn_kernel(DecodeAttnArgs a) {
     constexpr int EPL = KVRaw<T>::EPL;
     constexpr int LPR = 128 / EPL;  // lanes per 128-dim row
@@ -283,20 +313,74 @@ void decode_attn_kernel(DecodeAttnArgs a) {
     const int p_begin = c * a.chunk;
     const int pg_first = p_begin / a.page;
     const int my_page = ptab[min(pg_first + lane, a.max_pages - 1)];
-    int L = (a.shared ? a.pos[0] + b : a.pos[b]) + 1;
+    const int p_tok = a.shared ? a.pos[0] + b : a.pos[b];  // position of the step's token
+    int L = p_tok + 1;
     const int cap = a.max_pages * a.page;
     if (L > cap) L = cap;
+    if (FUSED && c == 0 && hk == 0 && lane == 0 && (p_tok < 0 || p_tok >= a.max_pos || p_tok >= cap))
+        raise_flag(a.flag, FLAG_POSITION);
     if (p_begin >= L) return;
     const int p_end = min(L, p_begin + a.chunk);
 
     const int d0 = (lane % LPR) * EPL;
     const int rsub = lane / LPR;
     float qv[GROUP][EPL];
+    if (FUSED) {
+        // q (and, on the last chunk, the token's K / V) from the raw projections
+        const float *row = a.qkv + (int64_t)b * (a.H + 2 * a.Hkv) * 128;
+        const int pc = min(max(p_tok, 0), a.max_pos - 1);
+        float cr[EPL], sr[EPL], x[GROUP][EPL], gq[EPL];
 #pragma unroll
-    for (int j = 0; j < GROUP; ++j) {
-        const float *q = a.q + (int64_t)b * a.H * 128 + (hk * GROUP + j) * 128 + d0;
+        for (int e = 0; e < EPL; ++e) {
+            const float2 t = a.rope[(int64_t)pc * 64 + ((d0 + e) & 63)];
+            cr[e] = t.x;
+            sr[e] = t.y;
+            gq[e] = a.q_gain[d0 + e];
+        }
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) qv[j][e] = q[e] * a.scale_log2;
+        for (int j = 0; j < GROUP; ++j)
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) x[j][e] = row[(hk * GROUP + j) * 128 + d0 + e];
+#pragma unroll
+        for (int j = 0; j < GROUP; ++j) {
+            norm_rope_head<EPL, LPR>(x[j], gq, d0, cr, sr, a.eps, qv[j]);
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) qv[j][e] *= a.scale_log2;
+        }
+        if (p_tok >= p_begin && p_tok < p_end) {  // this chunk holds the token's slot
+            float kx[EPL], vx[EPL], gk[EPL], kn[EPL];
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                kx[e] = row[(a.H + hk) * 128 + d0 + e];
+                vx[e] = row[(a.H + a.Hkv + hk) * 128 + d0 + e];
+                gk[e] = a.k_gain[d0 + e];
+            }
+            norm_rope_head<EPL, LPR>(kx, gk, d0, cr, sr, a.eps, kn);
+            const int page_id = __builtin_amdgcn_readlane(my_page, p_tok / a.page - pg_first);
+            const bool ok = p_tok < a.max_pos && page_id >= 0 && page_id < a.n_pages;
+            if (p_tok < a.max_pos && !ok && hk == 0 && lane == 0) raise_flag(a.flag, FLAG_PAGE);
+            if (ok && rsub == 0) {
+                T *dst = reinterpret_cast<T *>(a.pool_layer) +
+                         ((((int64_t)page_id * 2) * a.Hkv + hk) * a.page + p_tok % a.page) * 128 + d0;
+                T *dsv = dst + (int64_t)a.Hkv * a.page * 128;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) {
+                    dst[e] = from_f32<T>(kn[e]);
+                    dsv[e] = from_f32<T>(vx[e]);
+                }
+            }
+            // the page reads below must see the slot: this wave's stores complete first
+            __builtin_amdgcn_s_waitcnt(0);
+        }
+        // the prologue's temporaries die here, before the page pipeline's registers are live
+        __builtin_amdgcn_sched_barrier(0);
+    } else {
+#pragma unroll
+        for (int j = 0; j < GROUP; ++j) {
+            const float *q = a.q + (int64_t)b * a.H * 128 + (hk * GROUP + j) * 128 + d0;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) qv[j][e] = q[e] * a.scale_log2;
+        }
     }
 
     float m_run[GROUP], l_run[GROUP], acc[GROUP][EPL];
@@ -423,12 +507,13 @@ void launch_decode_attn(const DecodeAttnArgs &a, DType dt, hipStream_t s, hipEve
         if (ev0 || ev1) hipExtLaunchKernelGGL(kernel, grid, block, 0, s, ev0, ev1, 0, a);
         else hipLaunchKernelGGL(kernel, grid, block, 0, s, a);  // plain launch (graph capture)
     };
+    const bool fused = a.qkv != nullptr && !a.shared;
     if (dt == DT_BF16) {
-        if (group == 2) go(decode_attn_kernel<bf16_t, 2>);
-        else go(decode_attn_kernel<bf16_t, 1>);
+        if (group == 2) fused ? go(decode_attn_kernel<bf16_t, 2, true>) : go(decode_attn_kernel<bf16_t, 2, false>);
+        else fused ? go(decode_attn_kernel<bf16_t, 1, true>) : go(decode_attn_kernel<bf16_t, 1, false>);
     } else {
-        if (group == 2) go(decode_attn_kernel<float, 2>);
-        else go(decode_attn_kernel<float, 1>);
+        if (group == 2) fused ? go(decode_attn_kernel<float, 2, true>) : go(decode_attn_kernel<float, 2, false>);
+        else fused ? go(decode_attn_kernel<float, 1, true>) : go(decode_attn_kernel<float, 1, false>);
     }
 }
 

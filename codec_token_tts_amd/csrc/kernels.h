@@ -103,7 +103,7 @@ bool launch_qkv_dense(const GemmArgs &g, const RopeKvArgs &rk, hipStream_t s);
 // ---- K5: split-sequence decode attention over the paged pool -----------------------
 struct DecodeAttnArgs {
     const float *q;  // [B][H*128] fp32
-    const void *pool_layer;
+    void *pool_layer;     // [n_pages][2][Hkv][page][128] (written only by the fused step-token path)
     const int32_t *pos;
     const int32_t *page_table;
     int max_pages, n_pages, page;
@@ -114,6 +114,17 @@ struct DecodeAttnArgs {
     float scale_log2;     // log2(e) / sqrt(128)
     int shared;           // prefill of one stream: query b is at position pos[0] + b and
                           // every query reads page-table row 0 (causal by construction)
+    // Fused step-token preparation (q_len = 1 decode, shared == 0): when qkv is set, q is
+    // the per-head RMSNorm + RoPE of the raw projections qkv [B][(H + 2 Hkv) * 128] (the
+    // q field is not read), and the wave owning each stream's last chunk writes the
+    // token's normed + rotated K and its V to the pool slot of position pos[b] before it
+    // reads that page; flags as the separate kernel raises them.
+    const float *qkv;
+    const float *q_gain, *k_gain;
+    const float2 *rope;   // [max_pos][64] (cos, sin)
+    float eps;
+    int max_pos;
+    int *flag;
 };
 // ev0 / ev1 (optional): events stamped with the kernel's own start and end
 void launch_decode_attn(const DecodeAttnArgs &a, DType dt, hipStream_t s, hipEvent_t ev0 = nullptr,

@@ -675,7 +675,11 @@ ttsbb_status paged_forward(ttsbb_ctx *ctx, int32_t batch, float *x, int32_t *pos
         r.pool_layer = pool_l;
         r.flag = ctx->flag;
         r.shared = prefill ? 1 : 0;
-        {
+        // a q_len = 1 step folds the token's head norms, RoPE and K/V append into the
+        // attention kernel (below); the separate kernel runs for the prefill and when q is
+        // tapped
+        const bool fused = !prefill && !tapit;
+        if (!fused) {
             KScope k(ctx, TTSBB_K_ROPE_KV);
             launch_rope_kv(r, ctx->dt, ctx->stream);
         }
@@ -698,6 +702,15 @@ ttsbb_status paged_forward(ttsbb_ctx *ctx, int32_t batch, float *x, int32_t *pos
         d.out = ctx->attn;
         d.scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
         d.shared = prefill ? 1 : 0;
+        if (fused) {
+            d.qkv = ctx->qkv;
+            d.q_gain = L.q_norm;
+            d.k_gain = L.k_norm;
+            d.rope = ctx->rope;
+            d.eps = g.rms_eps;
+            d.max_pos = g.max_pos;
+            d.flag = ctx->flag;
+        }
         {
             KScope k(ctx, TTSBB_K_DECODE_ATTN, true);
             launch_decode_attn(d, ctx->dt, ctx->stream, k.start(), k.stop());
