@@ -97,8 +97,10 @@ def test_codebook_embed_bit_exact(bf16):
 
 
 # ---------------------------------------------------------------------------------------
-def run_decode(m: Model, lengths, seed, head=None, tap_layer=None):
-    """One decode step of len(lengths) streams; returns GPU results and oracle results."""
+def run_decode(m: Model, lengths, seed, head=None, tap_layer=None, gpu_tap=True):
+    """One decode step of len(lengths) streams; returns GPU results and oracle results.
+    With gpu_tap=False the oracle still records tap_layer but the GPU runs untapped (every
+    layer on the fused q_len = 1 path)."""
     T = m.T
     shape = m.shape
     B = len(lengths)
@@ -108,7 +110,7 @@ def run_decode(m: Model, lengths, seed, head=None, tap_layer=None):
     x = t_f32(x_in)
     pos = t_i32(lengths)
     res = {}
-    if tap_layer is not None:
+    if tap_layer is not None and gpu_tap:
         T.ttsbb_set_tap_layer(m.ctx, tap_layer)
     if head is not None:
         hd_dev, G, V = head[:3]
@@ -124,7 +126,7 @@ def run_decode(m: Model, lengths, seed, head=None, tap_layer=None):
     if head is not None:
         res["argmax"] = am.cpu().numpy()
         res["logits"] = lg.cpu().numpy()
-    if tap_layer is not None:
+    if tap_layer is not None and gpu_tap:
         taps = {}
         w = dict(h=(T.TAP_H_ATTN, shape.hidden),
                  qkv=(T.TAP_QKV, (shape.n_heads + 2 * shape.n_kv_heads) * shape.head_dim),
@@ -175,6 +177,78 @@ def test_decode_fp32_single_layer_kv64():
         np.testing.assert_allclose(res["pool"][0, pg, 0, :, 0, :], ref["rec"]["k"][0], atol=1e-4)
         np.testing.assert_allclose(res["pool"][0, pg, 1, :, 0, :], ref["rec"]["v"][0], atol=1e-4)
         assert res["pos"].tolist() == [65]
+    finally:
+        m.close()
+
+
+@pytest.mark.parametrize("bf16,lengths", [(False, [64]), (False, [0, 5, 16, 17, 40]),
+                                          (True, [0, 1, 15, 16, 17, 33, 64, 100, 129])])
+def test_decode_step_token_fused(bf16, lengths):
+    """No tap: the step token's head norms, RoPE and K/V append run inside the attention
+    kernel.  The layer output and the K / V the kernel wrote to each stream's slot at
+    position L_b match the oracle (fp32: 1e-4 max-abs; bf16: the layer tolerance)."""
+    shape = CFG.Shape(n_layers=1)
+    m = Model(shape, 1, bf16, seed=13, gains="random")
+    try:
+        res, ref = run_decode(m, lengths, 13, tap_layer=0, gpu_tap=False)
+        if bf16:
+            assert normwise(res["x"], ref["x"]) <= TOL_LAYER_BF16
+        else:
+            assert np.max(np.abs(res["x"] - ref["x"])) <= 1e-4
+        assert res["pos"].tolist() == [n + 1 for n in lengths]
+        for b, n in enumerate(lengths):
+            pg, slot = ref["pt"][b, n // 16], n % 16
+            k_got, v_got = res["pool"][0, pg, 0, :, slot, :], res["pool"][0, pg, 1, :, slot, :]
+            k_ref, v_ref = ref["rec"]["k"][b], ref["rec"]["v"][b]
+            if bf16:  # bf16 operands of the projection, then bf16 storage
+                assert normwise(k_got, k_ref) <= TOL_LAYER_BF16, b
+                assert normwise(v_got, v_ref) <= TOL_LAYER_BF16, b
+            else:
+                np.testing.assert_allclose(k_got, k_ref, atol=1e-4)
+                np.testing.assert_allclose(v_got, v_ref, atol=1e-4)
+    finally:
+        m.close()
+
+
+@pytest.mark.parametrize("tap", [False, True])
+def test_decode_bad_page_and_position_raise_flag(tap):
+    """A stream whose slot page id is invalid, or whose position lies past its page-table
+    row, raises the device flag (reported once by ttsbb_sync, then cleared) on both the
+    fused and the separate step-token path; only the valid streams' slots are written and
+    nothing faults."""
+    shape = CFG.Shape(n_layers=1)
+    m = Model(shape, 1, True, seed=3)
+    T = m.T
+    try:
+        lengths = [20, 40]
+        pt, n_pages = CFG.page_table(3, [n + 1 for n in lengths], extra_pages=1)
+        pool = DEV.kv_pool(3, shape, 1, lengths, pt, n_pages, True)
+        x = t_f32(gen.fast_normal(3, stream_id(gen.KIND_X_IN, 0), (2, shape.hidden), 1.0))
+        if tap:
+            T.ttsbb_set_tap_layer(m.ctx, 0)
+
+        def changed(before):
+            d = (pool != before).any(dim=-1).nonzero().cpu().numpy()  # (layer, page, kv, head, slot)
+            return sorted({(int(r[1]), int(r[2]), int(r[4])) for r in d})
+
+        pt_bad = pt.copy()
+        pt_bad[0, 20 // 16] = -1  # stream 0's slot page
+        before = pool.clone()
+        T.ttsbb_decode_step(m.ctx, 2, x.clone(), t_i32(lengths), t_i32(pt_bad), pt.shape[1], pool, n_pages)
+        assert T.ttsbb_sync(m.ctx) == T.DEVICE_ERROR
+        assert T.ttsbb_sync(m.ctx) == T.OK
+        p1 = int(pt[1, 40 // 16])
+        assert changed(before) == [(p1, 0, 40 % 16), (p1, 1, 40 % 16)]
+
+        far = [20, 16 * pt.shape[1] + 5]  # stream 1 past its row (max_pages pages of 16)
+        before = pool.clone()
+        T.ttsbb_decode_step(m.ctx, 2, x.clone(), t_i32(far), t_i32(pt), pt.shape[1], pool, n_pages)
+        assert T.ttsbb_sync(m.ctx) == T.DEVICE_ERROR
+        assert T.ttsbb_sync(m.ctx) == T.OK
+        p0 = int(pt[0, 20 // 16])
+        assert changed(before) == [(p0, 0, 20 % 16), (p0, 1, 20 % 16)]
+        if tap:
+            T.ttsbb_set_tap_layer(m.ctx, -1)
     finally:
         m.close()
 
