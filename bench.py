@@ -95,12 +95,15 @@ class DecodeC5:
 
     def attn_bytes(self, steps_done_before, n_steps):
         """Algorithmic bytes of one decode-attention launch averaged over the timed steps:
-        K and V of every cached position (incl. the new one) once, q in, o out."""
+        K and V (bf16) of every earlier cached position once; the step token's raw q, k, v
+        (fp32) in and its K, V (bf16) out to the slot (the kernel prepares the token);
+        o (bf16) out."""
         L = self.lengths.astype(np.int64)
-        mean_len = float(np.mean([(L + s + 1).sum() for s in range(steps_done_before,
-                                                                    steps_done_before + n_steps)]))
+        mean_len = float(np.mean([(L + s).sum() for s in range(steps_done_before,
+                                                               steps_done_before + n_steps)]))
         kv = mean_len * 8 * 128 * 2 * 2
-        return kv + self.B * 16 * 128 * 4 + self.B * 16 * 128 * 2
+        token = self.B * (16 + 2 * 8) * 128 * 4 + self.B * 8 * 128 * 2 * 2
+        return kv + token + self.B * 16 * 128 * 2
 
 
 class MaskgitC4:
