@@ -647,3 +647,66 @@ def test_prefill_bf16(p0, S):
         check_argmax_groups(am.cpu().numpy()[None], lg_gpu.reshape(1, G, V), lg_ref.reshape(1, G, V))
     finally:
         m.close()
+
+
+# ---------------------------------------------------------------------------------------
+# Edge cases: empty calls, the longest cache a page table allows, a MaskGIT sequence at
+# the workspace's row limit
+# ---------------------------------------------------------------------------------------
+def test_empty_calls_are_no_ops():
+    """Zero streams, zero prompt tokens, zero embedding rows and zero picks succeed and
+    leave every output untouched."""
+    shape = CFG.Shape(n_layers=1)
+    m = Model(shape, 1, True, seed=2)
+    T = m.T
+    try:
+        pt, n_pages = CFG.page_table(2, [17])
+        pool = DEV.kv_pool(2, shape, 1, [16], pt, n_pages, True)
+        before = pool.clone()
+        x = torch().zeros((1, shape.hidden), dtype=torch().float32, device="cuda")
+        pos = t_i32([16])
+        assert T.ttsbb_decode_step(m.ctx, 0, x, pos, t_i32(pt), pt.shape[1], pool, n_pages) == T.OK
+        assert T.ttsbb_prefill(m.ctx, 0, x, pos, t_i32(pt), pt.shape[1], pool, n_pages) == T.OK
+        out = torch().full((1, shape.hidden), 7.0, dtype=torch().float32, device="cuda")
+        tab = DEV.host_to_device(CFG.table(2, gen.KIND_CB_TABLE, 0, 4 * 8, shape.hidden, True))
+        assert T.ttsbb_codebook_embed(m.ctx, 0, 4, t_i32(np.zeros((1, 4))), tab, 8, None, None, None, 0, out) == T.OK
+        assert T.ttsbb_sync(m.ctx) == T.OK
+        assert pos.cpu().tolist() == [16]
+        assert torch().equal(pool, before)
+        assert bool((out == 7.0).all())
+        # a MaskGIT step that unmasks nothing leaves the codes as they were
+        res, ref = run_maskgit(m, 5, 40, 2, 17, 16, 0, 2)
+        assert np.array_equal(res["codes"], ref["codes_in"])
+    finally:
+        m.close()
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_decode_longest_cache(bf16):
+    """One stream at the last position max_pos - 1 (8191: 512 pages, 64 chunks of 128 merged
+    in two passes) next to a short one."""
+    shape = CFG.Shape(n_layers=1)
+    m = Model(shape, 1, bf16, seed=17, max_pos=8192)
+    try:
+        lengths = [8191, 3]
+        res, ref = run_decode(m, lengths, 17, tap_layer=0, gpu_tap=False)
+        if bf16:
+            assert normwise(res["x"], ref["x"]) <= TOL_LAYER_BF16
+        else:
+            assert np.max(np.abs(res["x"] - ref["x"])) <= 1e-4
+        assert res["pos"].tolist() == [8192, 4]
+    finally:
+        m.close()
+
+
+def test_maskgit_at_row_limit():
+    """S = max_rows = 1024 (24 text tokens + 1000 frames): whole 128-row tiles, no ragged
+    tail, 32 key blocks; one layer against the oracle."""
+    shape = CFG.Shape(n_layers=1)
+    m = Model(shape, 1, True, seed=19, max_rows=1024)
+    try:
+        n_cb, V, mask = 2, 33, 32
+        res, ref = run_maskgit(m, 24, 1000, n_cb, V, mask, 300, 19)
+        check_maskgit(res, ref, n_cb, 1000, V, mask, 300)
+    finally:
+        m.close()
