@@ -113,7 +113,8 @@ class MaskgitC4:
         w = CFG.c4()
         e = w.extra
         self.e = e
-        self.ctx, self.keep = make_ctx(T, torch, w.shape, 28, True, w.seed, 1024, 8192, 8200, DEV, CFG)
+        # 2048 rows: a guided step runs its two sequences (950 + 750 rows) as one batch
+        self.ctx, self.keep = make_ctx(T, torch, w.shape, 28, True, w.seed, 2048, 8192, 8200, DEV, CFG)
         self.text_table = DEV.table(w.seed, gen.KIND_TEXT_TABLE, 0, e["text_vocab"], 1024, True)
         self.tables = DEV.table(w.seed, gen.KIND_CB_TABLE, 0, e["n_cb"] * e["cb_vocab"], 1024, True)
         self.heads = DEV.table(w.seed, gen.KIND_HEAD, 0, e["n_cb"] * e["cb_vocab"], 1024, True)

@@ -91,7 +91,10 @@ __global__ __launch_bounds__(512) void flash_kernel(FlashArgs a) {
 
     const bf16_t *kg = a.k + (int64_t)hk * a.s_pad * 128;
     const bf16_t *vg = a.vt + (int64_t)hk * 128 * a.s_pad;
-    const int NB = a.s_pad / FB, NBQ = (NB + 3) / 4;
+    // the keys of the tile's sequence: [kb, ke) (a tile never straddles two sequences)
+    const bool second = a.seg1 > 0 && q0 >= a.seg1;
+    const int kb = second ? a.seg1 : 0, ke = kb + (second ? a.len1 : a.len0);
+    const int NB = (ke - kb + FB - 1) / FB, NBQ = (NB + 3) / 4;
     const int kb_first = qq * NBQ, nb_mine = max(0, min(NBQ, NB - kb_first));
     // iteration i works on block blk(i); past this quarter's blocks it re-reads a valid
     // block and masks every key
@@ -106,18 +109,18 @@ __global__ __launch_bounds__(512) void flash_kernel(FlashArgs a) {
     float m_run = -INFINITY, l_run = 0.f;
 
     u32x4_t rk[4], rv[4];
-    flash_gload(kg, vg, a.s_pad, blk(0) * FB, qtid, rk, rv);
+    flash_gload(kg, vg, a.s_pad, kb + blk(0) * FB, qtid, rk, rv);
     flash_sstore(sk0, sv0, qtid, rk, rv);
     __syncthreads();
     for (int i = 0; i < NBQ; ++i) {
         const int buf = i & 1;
         const bf16_t *sk = buf ? sk1 : sk0;
         const bf16_t *sv = buf ? sv1 : sv0;
-        flash_gload(kg, vg, a.s_pad, blk(i + 1) * FB, qtid, rk, rv);  // unconditional (clamped)
+        flash_gload(kg, vg, a.s_pad, kb + blk(i + 1) * FB, qtid, rk, rv);  // unconditional (clamped)
         // keep the prefetch at the top of the iteration: it has the whole block to arrive
         __builtin_amdgcn_sched_barrier(0);
         const bool valid = i < nb_mine;
-        const int kbase = blk(i) * FB;
+        const int kbase = kb + blk(i) * FB;
 
         bf16x8_t kf[8];
 #pragma unroll
@@ -139,12 +142,12 @@ __global__ __launch_bounds__(512) void flash_kernel(FlashArgs a) {
                 const bf16x4_t hi = *reinterpret_cast<const bf16x4_t *>(vrow + 8);
                 vfr[dt][kk] = bf16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
             }
-        // mask keys past S (and the blocks of a finished quarter): only partial blocks
-        if (!(valid && kbase + FB <= a.S)) {
+        // mask keys past the sequence (and the blocks of a finished quarter): only partial blocks
+        if (!(valid && kbase + FB <= ke)) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int key = kbase + (r >> 2) * 8 + h * 4 + (r & 3);
-                if (!(valid && key < a.S)) s[r] = -INFINITY;
+                if (!(valid && key < ke)) s[r] = -INFINITY;
             }
         }
         float mx = s[0];

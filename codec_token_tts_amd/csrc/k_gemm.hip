@@ -336,7 +336,8 @@ __device__ __forceinline__ void lds_frags(const bf16_t *sa, const bf16_t *sb, in
 // The fp32 tile goes through LDS in two halves of 64 tokens (row stride 132 floats);
 // for a q or k head each token's 128 values get the per-head RMSNorm (four threads per
 // token, 16 RoPE pairs each, sum of squares over the quad) and the half-rotate RoPE at
-// position = token index, then go out as bf16 q [S][H*128] or K [Hkv][s_pad][128];
+// position = token index (minus seg1 in a second sequence), then go out as bf16 q
+// [S][H*128] or K [Hkv][s_pad][128];
 // a v head goes out transposed, V^T [Hkv][128][s_pad], 8 tokens per 16-byte store.
 template <int TM, int TN>
 __device__ __forceinline__ void qkv_dense_epilogue(const f32x16_t (&acc)[TM][TN], float *tile, int m0, int n0,
@@ -347,8 +348,35 @@ __device__ __forceinline__ void qkv_dense_epilogue(const f32x16_t (&acc)[TM][TN]
     const int wm = wave >> 1, wn = wave & 1;
     const int head = n0 / 128;
     const bool is_v = head >= rk.H + rk.Hkv;
+    const bool is_q = head < rk.H;
+    // q / k heads: the gains and both halves' RoPE entries of this thread's token and
+    // dims are requested before the tile goes through LDS (their latency overlaps it)
+    const int q4 = tid & 3;
+    float2 csr[2][16];
+    float glo[16], ghi[16];
+    if (!is_v) {
+        const float *gain = is_q ? rk.q_gain : rk.k_gain;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            glo[e] = gain[q4 * 16 + e];
+            ghi[e] = gain[q4 * 16 + 64 + e];
+        }
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            const int m = m0 + hf * 64 + (tid >> 2);
+            const int pos = rk.seg1 > 0 && m >= rk.seg1 ? m - rk.seg1 : m;  // second sequence
+            const float2 *cs = rk.rope + (int64_t)min(pos, rk.max_pos - 1) * 64 + q4 * 16;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) csr[hf][e] = cs[e];
+        }
+    }
+    // LDS-only barriers: __syncthreads() would also wait for the table loads above
+    auto lds_barrier = []() {
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS accesses are done
+        __builtin_amdgcn_s_barrier();
+    };
     for (int half = 0; half < 2; ++half) {
-        __syncthreads();  // the previous use of the LDS (ring buffers / first half) is over
+        lds_barrier();  // the previous use of the LDS (ring buffers / first half) is over
         if (wm == half) {
 #pragma unroll
             for (int i = 0; i < TM; ++i)
@@ -360,10 +388,10 @@ __device__ __forceinline__ void qkv_dense_epilogue(const f32x16_t (&acc)[TM][TN]
                         tile[row * LDT + wn * 64 + j * 32 + (lane & 31)] = acc[i][j][r];
                     }
         }
-        __syncthreads();
+        lds_barrier();
         const int t0 = m0 + half * 64;
         if (!is_v) {
-            const int row = tid >> 2, q4 = tid & 3, m = t0 + row;
+            const int row = tid >> 2, m = t0 + row;
             const float *x = tile + row * LDT + q4 * 16;
             float lo[16], hi[16];
             float ss = 0.f;
@@ -375,18 +403,14 @@ __device__ __forceinline__ void qkv_dense_epilogue(const f32x16_t (&acc)[TM][TN]
             }
             ss = group_sum<4>(ss);
             const float inv = 1.0f / sqrtf(ss / 128.0f + rk.eps);
-            const bool is_q = head < rk.H;
-            const float *gain = is_q ? rk.q_gain : rk.k_gain;
-            const float2 *cs = rk.rope + (int64_t)min(m, rk.max_pos - 1) * 64 + q4 * 16;
             uint32_t wlo[8], whi[8];
 #pragma unroll
             for (int e = 0; e < 16; e += 2) {
                 float o[2][2];
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
-                    const int d = q4 * 16 + e + u;
-                    const float x0 = lo[e + u] * inv * gain[d], x1 = hi[e + u] * inv * gain[d + 64];
-                    const float2 c = cs[e + u];
+                    const float x0 = lo[e + u] * inv * glo[e + u], x1 = hi[e + u] * inv * ghi[e + u];
+                    const float2 c = csr[half][e + u];
                     o[0][u] = x0 * c.x - x1 * c.y;
                     o[1][u] = x1 * c.x + x0 * c.y;
                 }

@@ -37,7 +37,7 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(RopeKvArgs a) {
     // Loads complete in order: the position goes first, then all of the first pass's
     // row values (they do not depend on it), and only then the position-dependent
     // page-table and RoPE-table loads, so no wait drains more than it needs.
-    int p = a.dense ? m : (a.shared ? a.pos[0] + m : a.pos[m]);
+    int p = a.dense ? (a.seg1 > 0 && m >= a.seg1 ? m - a.seg1 : m) : (a.shared ? a.pos[0] + m : a.pos[m]);
     float u[MAXJ], u2[MAXJ];
 #pragma unroll
     for (int i = 0; i < MAXJ; ++i) {

@@ -93,6 +93,7 @@ struct RopeKvArgs {
     int *flag;
     int shared;          // decode mode, prefill of one stream: row m is at position pos[0] + m
                          // and every row uses page-table row 0
+    int seg1;            // dense mode, two sequences: rows m >= seg1 > 0 are at position m - seg1
 };
 void launch_rope_kv(const RopeKvArgs &a, DType kv_dt, hipStream_t s);
 // Dense mode fused into the q/k/v projection (g: EPI_STORE product of N = (H + 2 Hkv) *
@@ -139,6 +140,10 @@ struct FlashArgs {
     int S, s_pad, H, Hkv;
     float scale_log2;
     uint16_t *out;       // [S][H*128] bf16
+    // Two independent sequences in one launch (seg1 > 0, a multiple of 32): rows [0, len0)
+    // attend to keys [0, len0), rows [seg1, seg1 + len1) to keys [seg1, seg1 + len1); rows
+    // between len0 and seg1 are padding.  seg1 == 0: one sequence, len0 = S.
+    int seg1, len0, len1;
 };
 void launch_flash_attn(const FlashArgs &a, hipStream_t s);
 

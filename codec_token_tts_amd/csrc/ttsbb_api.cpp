@@ -519,7 +519,7 @@ void head_gemm(ttsbb_ctx *c, const void *head, int M, int N, float *out, int ldc
 // (k, t) is codes[k * codes_ld + t].
 void maskgit_embed(ttsbb_ctx *ctx, int S, int n_text, const int32_t *text_ids, const void *text_table,
                    int text_vocab, int n_cb, int cb_vocab, const void *audio_tables, const int32_t *codes,
-                   int codes_ld) {
+                   int codes_ld, int out_row0 = 0) {
     EmbedArgs e;
     e.n_rows = S;
     e.n_cb = n_cb;
@@ -535,19 +535,20 @@ void maskgit_embed(ttsbb_ctx *ctx, int S, int n_text, const int32_t *text_ids, c
     e.text_ids = text_ids;
     e.text_table = text_table;
     e.text_vocab = text_vocab;
-    e.out = ctx->x;
+    e.out = ctx->x + (size_t)out_row0 * ctx->cfg.hidden;
     e.flag = ctx->flag;
     KScope k(ctx, TTSBB_K_EMBED);
     launch_embed(e, DT_BF16, ctx->stream);
 }
 
-// Every layer over rows [0, S) of ctx->x with bidirectional attention (RoPE positions
-// 0..S-1, no cache), then the final RMSNorm of rows [row0, row0 + n_out) and the heads
-// into logits [n_out][N].  Per-layer taps only when `taps`.
-void maskgit_backbone(ttsbb_ctx *ctx, int S, int row0, int n_out, const void *heads, int N, float *logits,
-                      bool taps) {
+// Every layer over rows [0, M) of ctx->x with bidirectional attention and no cache: one
+// sequence (seg1 == 0, len0 == M, RoPE positions 0..M-1), or two independent ones in the
+// same launches (rows [0, len0) and [seg1, seg1 + len1), each at positions from 0, seg1 a
+// multiple of 64; the rows in between are padding).  Per-layer taps (all M rows: the
+// first sequence leads) only when `taps`.  Leaves no split partials pending.
+void maskgit_layers(ttsbb_ctx *ctx, int M, int seg1, int len0, int len1, bool taps) {
     const ttsbb_config &g = ctx->cfg;
-    const int s_pad = round_up(S, 64);
+    const int s_pad = round_up(M, 64);
     const int H = g.n_heads, Hkv = g.n_kv_heads, hd = g.head_dim;
     const int hd_all = H * hd;
     for (int l = 0; l < g.n_layers; ++l) {
@@ -555,7 +556,7 @@ void maskgit_backbone(ttsbb_ctx *ctx, int S, int row0, int n_out, const void *he
         const bool tapit = taps && (l == ctx->tap_layer);
         RopeKvArgs r = {};
         r.qkv = ctx->qkv;
-        r.M = S;
+        r.M = M;
         r.H = H;
         r.Hkv = Hkv;
         r.q_gain = L.q_norm;
@@ -569,35 +570,44 @@ void maskgit_backbone(ttsbb_ctx *ctx, int S, int row0, int n_out, const void *he
         r.vtbuf = ctx->vtbuf;
         r.s_pad = s_pad;
         r.flag = ctx->flag;
-        if (!qkv_projection(ctx, L, ctx->x, S, tapit, &r)) {
+        r.seg1 = seg1;
+        if (!qkv_projection(ctx, L, ctx->x, M, tapit, &r)) {
             KScope k(ctx, TTSBB_K_ROPE_KV);
             launch_rope_kv(r, DT_BF16, ctx->stream);
         }
         if (tapit) {
-            tap_dense(ctx, TTSBB_TAP_Q, ctx->q, DT_BF16, S, hd_all, hd_all);
-            // K [Hkv][s_pad][hd] -> [S][Hkv][hd];  V^T [Hkv][hd][s_pad] -> [S][Hkv][hd]
-            tap(ctx, TTSBB_TAP_K, ctx->kbuf, DT_BF16, S, Hkv * hd, hd, (int64_t)s_pad * hd, 1, hd);
-            tap(ctx, TTSBB_TAP_V, ctx->vtbuf, DT_BF16, S, Hkv * hd, 1, (int64_t)hd * s_pad, s_pad, hd);
+            tap_dense(ctx, TTSBB_TAP_Q, ctx->q, DT_BF16, M, hd_all, hd_all);
+            // K [Hkv][s_pad][hd] -> [M][Hkv][hd];  V^T [Hkv][hd][s_pad] -> [M][Hkv][hd]
+            tap(ctx, TTSBB_TAP_K, ctx->kbuf, DT_BF16, M, Hkv * hd, hd, (int64_t)s_pad * hd, 1, hd);
+            tap(ctx, TTSBB_TAP_V, ctx->vtbuf, DT_BF16, M, Hkv * hd, 1, (int64_t)hd * s_pad, s_pad, hd);
         }
 
         FlashArgs f;
         f.q = reinterpret_cast<const uint16_t *>(ctx->q);
         f.k = ctx->kbuf;
         f.vt = ctx->vtbuf;
-        f.S = S;
+        f.S = M;
         f.s_pad = s_pad;
         f.H = H;
         f.Hkv = Hkv;
         f.scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
         f.out = reinterpret_cast<uint16_t *>(ctx->attn);
+        f.seg1 = seg1;
+        f.len0 = len0;
+        f.len1 = len1;
         {
             KScope k(ctx, TTSBB_K_FLASH_ATTN);
             launch_flash_attn(f, ctx->stream);
         }
-        post_attention(ctx, L, ctx->x, S, tapit);
+        post_attention(ctx, L, ctx->x, M, tapit);
     }
-    // final norm + heads on the rows read out only
-    flush_residual(ctx, ctx->x, S);
+    flush_residual(ctx, ctx->x, M);
+}
+
+// Final RMSNorm of rows [row0, row0 + n_out) of ctx->x and the heads into logits
+// [n_out][N].
+void maskgit_head(ttsbb_ctx *ctx, int row0, int n_out, const void *heads, int N, float *logits, bool taps) {
+    const ttsbb_config &g = ctx->cfg;
     {
         KScope k(ctx, TTSBB_K_RMSNORM);
         launch_rmsnorm(ctx->x + (size_t)row0 * g.hidden, g.hidden, n_out, g.hidden, ctx->final_norm, g.rms_eps,
@@ -607,14 +617,54 @@ void maskgit_backbone(ttsbb_ctx *ctx, int S, int row0, int n_out, const void *he
     head_gemm(ctx, heads, n_out, N, logits, N);
 }
 
+// One sequence of S rows: layers, then the heads of rows [row0, row0 + n_out).
+void maskgit_backbone(ttsbb_ctx *ctx, int S, int row0, int n_out, const void *heads, int N, float *logits,
+                      bool taps) {
+    maskgit_layers(ctx, S, 0, S, 0, taps);
+    maskgit_head(ctx, row0, n_out, heads, N, logits, taps);
+}
+
+// The two passes of a guided step: the conditional sequence (the whole prompt, S rows,
+// logits of its window rows [n_text + w0, n_text + w0 + n_target) into ctx->logits) and
+// the unconditional one (the window's frames alone, into ctx->logits_u).  When both fit
+// the workspace they run as one batch of two sequences (rows [0, S) and [seg1, seg1 +
+// n_target), seg1 = S rounded up to 64): the products see one M = seg1 + n_target, and the
+// attention keeps the sequences apart.  Otherwise two passes.
+void maskgit_guided(ttsbb_ctx *ctx, int n_text, const int32_t *text_ids, const void *text_table, int text_vocab,
+                    int n_frames, int n_target, int n_cb, int cb_vocab, const void *audio_tables,
+                    const void *audio_heads, const int32_t *codes) {
+    const ttsbb_config &g = ctx->cfg;
+    const int S = n_text + n_frames, w0 = n_frames - n_target;
+    const int N = n_cb * cb_vocab;
+    const int32_t *window = codes + w0;
+    const int seg1 = round_up(S, 64), M = seg1 + n_target;
+    if (M <= g.max_rows) {
+        maskgit_embed(ctx, S, n_text, text_ids, text_table, text_vocab, n_cb, cb_vocab, audio_tables, codes, n_frames);
+        if (seg1 > S)  // padding rows: zero (no text, no codebook)
+            maskgit_embed(ctx, seg1 - S, 0, nullptr, nullptr, 0, 0, cb_vocab, audio_tables, nullptr, n_frames, S);
+        maskgit_embed(ctx, n_target, 0, nullptr, nullptr, 0, n_cb, cb_vocab, audio_tables, window, n_frames, seg1);
+        maskgit_layers(ctx, M, seg1, S, n_target, true);
+        maskgit_head(ctx, n_text + w0, n_target, audio_heads, N, ctx->logits, true);
+        if (ctx->tap_layer >= 0) tap_dense(ctx, TTSBB_TAP_LOGITS, ctx->logits, DT_F32, n_target, N, N);
+        maskgit_head(ctx, seg1, n_target, audio_heads, N, ctx->logits_u, false);
+    } else {
+        maskgit_embed(ctx, S, n_text, text_ids, text_table, text_vocab, n_cb, cb_vocab, audio_tables, codes, n_frames);
+        maskgit_backbone(ctx, S, n_text + w0, n_target, audio_heads, N, ctx->logits, true);
+        if (ctx->tap_layer >= 0) tap_dense(ctx, TTSBB_TAP_LOGITS, ctx->logits, DT_F32, n_target, N, N);
+        maskgit_embed(ctx, n_target, 0, nullptr, nullptr, 0, n_cb, cb_vocab, audio_tables, window, n_frames);
+        maskgit_backbone(ctx, n_target, 0, n_target, audio_heads, N, ctx->logits_u, false);
+    }
+    if (ctx->tap_layer >= 0) tap_dense(ctx, TTSBB_TAP_LOGITS_U, ctx->logits_u, DT_F32, n_target, N, N);
+}
+
 }  // namespace
 
-static // The paged forward shared by the decode step (batch streams, one token each, row b at
+// The paged forward shared by the decode step (batch streams, one token each, row b at
 // position positions[b], page-table row b) and the prefill (batch tokens of one stream,
 // row b at position positions[0] + b, page-table row 0, causal by construction since
 // row b attends to positions 0..positions[0] + b).  The prefill's head reads the last
 // row only.
-ttsbb_status paged_forward(ttsbb_ctx *ctx, int32_t batch, float *x, int32_t *positions, const int32_t *page_table,
+static ttsbb_status paged_forward(ttsbb_ctx *ctx, int32_t batch, float *x, int32_t *positions, const int32_t *page_table,
                            int32_t max_pages, void *kv_pool, int32_t n_pages, const void *head, int32_t n_groups,
                            int32_t group_vocab, int32_t *argmax, float *logits, bool prefill) {
     if (!ctx || batch < 0) return TTSBB_INVALID_ARG;
@@ -822,17 +872,13 @@ TTSBB_API ttsbb_status ttsbb_maskgit_pass_cfg(ttsbb_ctx *ctx, int32_t n_text, co
     if (!(layer_penalty == layer_penalty) || !(cfg_scale == cfg_scale)) return TTSBB_INVALID_ARG;
     if (ctx->dt != DT_BF16) return TTSBB_UNSUPPORTED;
 
-    const int S = n_text + n_frames, w0 = n_frames - n_target;
+    const int w0 = n_frames - n_target;
     const int N = n_cb * cb_vocab;
     int32_t *window = codes + w0;  // element (k, t) of the window at window[k * n_frames + t]
-    // conditional pass: the whole prompt, logits on the window (its last n_target rows)
-    maskgit_embed(ctx, S, n_text, text_ids, text_table, text_vocab, n_cb, cb_vocab, audio_tables, codes, n_frames);
-    maskgit_backbone(ctx, S, n_text + w0, n_target, audio_heads, N, ctx->logits, true);
-    if (ctx->tap_layer >= 0) tap_dense(ctx, TTSBB_TAP_LOGITS, ctx->logits, DT_F32, n_target, N, N);
-    // unconditional pass: the window's frames alone, positions 0..n_target-1
-    maskgit_embed(ctx, n_target, 0, nullptr, nullptr, 0, n_cb, cb_vocab, audio_tables, window, n_frames);
-    maskgit_backbone(ctx, n_target, 0, n_target, audio_heads, N, ctx->logits_u, false);
-    if (ctx->tap_layer >= 0) tap_dense(ctx, TTSBB_TAP_LOGITS_U, ctx->logits_u, DT_F32, n_target, N, N);
+    // conditional pass (the whole prompt, logits on the window's rows) and unconditional
+    // pass (the window's frames alone, positions 0..n_target-1)
+    maskgit_guided(ctx, n_text, text_ids, text_table, text_vocab, n_frames, n_target, n_cb, cb_vocab, audio_tables,
+                   audio_heads, codes);
     {
         KScope k(ctx, TTSBB_K_SCORES);
         launch_maskgit_scores(ctx->logits, ctx->logits_u, cfg_scale, n_target, N, n_cb, cb_vocab, mask_id,
@@ -872,16 +918,16 @@ TTSBB_API ttsbb_status ttsbb_maskgit_step(ttsbb_ctx *ctx, const ttsbb_maskgit_st
     const int S = n_text + n_frames, w0 = n_frames - n_target;
     const int N = n_cb * cb_vocab;
     int32_t *window = a->codes + w0;
-    maskgit_embed(ctx, S, n_text, a->text_ids, a->text_table, a->text_vocab, n_cb, cb_vocab, a->audio_tables,
-                  a->codes, n_frames);
-    maskgit_backbone(ctx, S, n_text + w0, n_target, a->audio_heads, N, ctx->logits, true);
-    if (ctx->tap_layer >= 0) tap_dense(ctx, TTSBB_TAP_LOGITS, ctx->logits, DT_F32, n_target, N, N);
     const float *lu = nullptr;
     if (a->cfg_scale != 0.f) {
-        maskgit_embed(ctx, n_target, 0, nullptr, nullptr, 0, n_cb, cb_vocab, a->audio_tables, window, n_frames);
-        maskgit_backbone(ctx, n_target, 0, n_target, a->audio_heads, N, ctx->logits_u, false);
-        if (ctx->tap_layer >= 0) tap_dense(ctx, TTSBB_TAP_LOGITS_U, ctx->logits_u, DT_F32, n_target, N, N);
+        maskgit_guided(ctx, n_text, a->text_ids, a->text_table, a->text_vocab, n_frames, n_target, n_cb, cb_vocab,
+                       a->audio_tables, a->audio_heads, a->codes);
         lu = ctx->logits_u;
+    } else {
+        maskgit_embed(ctx, S, n_text, a->text_ids, a->text_table, a->text_vocab, n_cb, cb_vocab, a->audio_tables,
+                      a->codes, n_frames);
+        maskgit_backbone(ctx, S, n_text + w0, n_target, a->audio_heads, N, ctx->logits, true);
+        if (ctx->tap_layer >= 0) tap_dense(ctx, TTSBB_TAP_LOGITS, ctx->logits, DT_F32, n_target, N, N);
     }
     {
         KScope k(ctx, TTSBB_K_SCORES);

@@ -443,14 +443,18 @@ def run_maskgit_cfg(m: Model, n_text, n_frames, n_target, n_cb, V, mask_id, n_un
     return res, dict(codes_in=codes, rec=rec, inputs=(text_ids, text_h, tab_h, head_h, codes))
 
 
-@pytest.mark.parametrize("n_text,n_frames,n_target,n_unmask,scale", [(13, 57, 40, 30, 2.0), (70, 130, 100, 77, 3.0),
-                                                                     (0, 50, 50, 20, 1.5)])
-def test_maskgit_cfg_two_layers(n_text, n_frames, n_target, n_unmask, scale):
+@pytest.mark.parametrize("n_text,n_frames,n_target,n_unmask,scale,max_rows",
+                         [(13, 57, 40, 30, 2.0, 1024), (70, 130, 100, 77, 3.0, 1024), (0, 50, 50, 20, 1.5, 1024),
+                          (13, 57, 40, 30, 2.0, 100), (70, 130, 100, 77, 3.0, 300), (5, 27, 20, 9, 2.5, 1024)])
+def test_maskgit_cfg_two_layers(n_text, n_frames, n_target, n_unmask, scale, max_rows):
     """bf16, 2 layers: both passes' logits against the oracle's, the guided choice and
     scores (discrete parity on the guided logits), the top-n picks and the update of the
-    window only.  (13, 57 | 40) runs both passes through the M <= 64 products, (70, 130 |
-    100) both through the LDS-DMA products with the fused q|k|v epilogue."""
-    m = Model(CFG.Shape(n_layers=2), 2, True, seed=6, gains="random")
+    window only.  With room in the workspace the two passes run as one batch of two
+    sequences (rows [0, S) and [S rounded up to 64, + n_target): M = 168, 356, 114 and 84,
+    the last with a 32-row first sequence followed by 32 padding rows); max_rows 100 and
+    300 force two separate passes (M <= 64 products for the first, the LDS-DMA products
+    with the fused q|k|v epilogue for the second)."""
+    m = Model(CFG.Shape(n_layers=2), 2, True, seed=6, gains="random", max_rows=max_rows)
     try:
         n_cb, V, mask = 3, 33, 32
         res, ref = run_maskgit_cfg(m, n_text, n_frames, n_target, n_cb, V, mask, n_unmask, scale, 6)
