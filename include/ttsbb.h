@@ -183,9 +183,12 @@ ttsbb_status ttsbb_maskgit_pass(ttsbb_ctx *ctx, int32_t n_text, const int32_t *t
  *   codes int32 [n_cb][n_frames] in/out (only the window changes); pred int32 and conf
  *   fp32 [n_cb][n_target]; picked int32 [n_unmask] holds flat window indices
  *   f = k*n_target + t (or -1); other arguments as in ttsbb_maskgit_pass.
+ * When S rounded up to 64 plus n_target fits cfg.max_rows, the two prompts run as one
+ * batch of two independent sequences (same results up to rounding order; fewer, larger
+ * launches), else as two passes.
  * Requires cfg.dtype == TTSBB_BF16 and 0 < n_target <= n_frames.  With taps on, the
- * per-layer taps and TTSBB_TAP_LOGITS come from the conditional pass, TTSBB_TAP_LOGITS_U
- * holds u. */
+ * per-layer taps and TTSBB_TAP_LOGITS come from the conditional pass (its rows lead the
+ * batch), TTSBB_TAP_LOGITS_U holds u. */
 ttsbb_status ttsbb_maskgit_pass_cfg(ttsbb_ctx *ctx, int32_t n_text, const int32_t *text_ids,
                                     const void *text_table, int32_t text_vocab, int32_t n_frames,
                                     int32_t n_target, int32_t n_cb, int32_t cb_vocab, int32_t mask_id,
