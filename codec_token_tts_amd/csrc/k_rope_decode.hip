@@ -297,65 +297,108 @@ void decode_attn_kernel(DecodeAttnArgs a) {
     // indices in scalar registers (no per-lane page-id selection loops)
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int item = blockIdx.x * 4 + wave;
-    const int total = a.B * a.Hkv * a.n_chunks;
-    if (item >= total) return;
+    // streams below b_small in chunks of `chunk` positions, then the rest in chunks of
+    // chunk2 (dispatched last, so the launch ends on short items)
+    const int items1 = a.b_small * a.Hkv * a.n_chunks;
+    if (item >= items1 + (a.B - a.b_small) * a.Hkv * a.n_chunks2) return;
+    const bool small = item >= items1;
+    const int it = small ? item - items1 : item;
+    const int nch = small ? a.n_chunks2 : a.n_chunks, chunk = small ? a.chunk2 : a.chunk;
     // KV heads vary fastest: the waves of a block stream neighbouring 4 KB blocks of the
     // same pool pages (a page holds all heads' K and V contiguously)
-    const int hk = item % a.Hkv;
-    const int t = item / a.Hkv;
-    const int c = t % a.n_chunks, b = t / a.n_chunks;
+    const int hk = it % a.Hkv;
+    const int t = it / a.Hkv;
+    const int c = t % nch, b = (small ? a.b_small : 0) + t / nch;
 
     // The chunk's page ids (one per lane, clamped into the row) do not depend on the
     // stream's length: they are requested together with it.  A page-id load inside the
     // page loop would have to complete before the next page's addresses exist, and loads
     // complete in order, so that wait would also drain the prefetch: they are read once.
     const int32_t *ptab = a.page_table + (int64_t)(a.shared ? 0 : b) * a.max_pages;
-    const int p_begin = c * a.chunk;
+    const int p_begin = c * chunk;
     const int pg_first = p_begin / a.page;
     const int my_page = ptab[min(pg_first + lane, a.max_pages - 1)];
     const int p_tok = a.shared ? a.pos[0] + b : a.pos[b];  // position of the step's token
+    const int d0 = (lane % LPR) * EPL;
+    const int rsub = lane / LPR;
+    // FUSED: the raw q rows and the q gains do not depend on the position either; they
+    // are requested in the same round as it
+    const float *row = FUSED ? a.qkv + (int64_t)b * (a.H + 2 * a.Hkv) * 128 : nullptr;
+    float x[GROUP][EPL], gq[EPL];
+    if (FUSED) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) gq[e] = a.q_gain[d0 + e];
+#pragma unroll
+        for (int j = 0; j < GROUP; ++j)
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) x[j][e] = row[(hk * GROUP + j) * 128 + d0 + e];
+    }
     int L = p_tok + 1;
     const int cap = a.max_pages * a.page;
     if (L > cap) L = cap;
     if (FUSED && c == 0 && hk == 0 && lane == 0 && (p_tok < 0 || p_tok >= a.max_pos || p_tok >= cap))
         raise_flag(a.flag, FLAG_POSITION);
     if (p_begin >= L) return;
-    const int p_end = min(L, p_begin + a.chunk);
+    const int p_end = min(L, p_begin + chunk);
+    // FUSED: the chunk that holds the token's slot takes the token's K / V from registers
+    // (rounded to the pool's type, as a read-back would give) and scans only the earlier
+    // positions, so its page reads never wait for the slot's store
+    const bool tok_here = FUSED && p_tok >= p_begin && p_tok < p_end;
+    const int scan_end = tok_here ? p_tok : p_end;
 
-    const int d0 = (lane % LPR) * EPL;
-    const int rsub = lane / LPR;
+    const T *pool = reinterpret_cast<const T *>(a.pool_layer);
+    const int64_t blk = (int64_t)a.page * 128;  // elements of one (page, K|V, head) block
+    const int lane_off = rsub * 128 + d0;
+    const int pg_last = (scan_end - 1) / a.page;
+    auto page_of = [&](int pg) { return __builtin_amdgcn_readlane(my_page, pg - pg_first); };
+    u32x4_t ka[NR], va[NR], kb2[NR], vb2[NR];
+
     float qv[GROUP][EPL];
+    float m_run[GROUP], l_run[GROUP], acc[GROUP][EPL];
+#pragma unroll
+    for (int j = 0; j < GROUP; ++j) {
+        m_run[j] = -INFINITY;
+        l_run[j] = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[j][e] = 0.f;
+    }
+    bool ok_a;
     if (FUSED) {
-        // q (and, on the last chunk, the token's K / V) from the raw projections
-        const float *row = a.qkv + (int64_t)b * (a.H + 2 * a.Hkv) * 128;
         const int pc = min(max(p_tok, 0), a.max_pos - 1);
-        float cr[EPL], sr[EPL], x[GROUP][EPL], gq[EPL];
+        float cr[EPL], sr[EPL], kx[EPL], vx[EPL], gk[EPL];
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
             const float2 t = a.rope[(int64_t)pc * 64 + ((d0 + e) & 63)];
             cr[e] = t.x;
             sr[e] = t.y;
-            gq[e] = a.q_gain[d0 + e];
         }
-#pragma unroll
-        for (int j = 0; j < GROUP; ++j)
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) x[j][e] = row[(hk * GROUP + j) * 128 + d0 + e];
-#pragma unroll
-        for (int j = 0; j < GROUP; ++j) {
-            norm_rope_head<EPL, LPR>(x[j], gq, d0, cr, sr, a.eps, qv[j]);
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) qv[j][e] *= a.scale_log2;
-        }
-        if (p_tok >= p_begin && p_tok < p_end) {  // this chunk holds the token's slot
-            float kx[EPL], vx[EPL], gk[EPL], kn[EPL];
+        if (tok_here) {
 #pragma unroll
             for (int e = 0; e < EPL; ++e) {
                 kx[e] = row[(a.H + hk) * 128 + d0 + e];
                 vx[e] = row[(a.H + a.Hkv + hk) * 128 + d0 + e];
                 gk[e] = a.k_gain[d0 + e];
             }
+        }
+        // the first page goes out behind the position-dependent loads: waiting for those
+        // leaves it in flight while q is normalised and rotated
+        ok_a = load_page<T, NR, RPL>(pool, page_of(pg_first), a.n_pages, a.Hkv, hk, blk, lane_off, ka, va);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < GROUP; ++j) {
+            norm_rope_head<EPL, LPR>(x[j], gq, d0, cr, sr, a.eps, qv[j]);
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) qv[j][e] *= a.scale_log2;
+        }
+        if (tok_here) {
+            float kn[EPL];
             norm_rope_head<EPL, LPR>(kx, gk, d0, cr, sr, a.eps, kn);
+            T kt[EPL], vt[EPL];
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                kt[e] = from_f32<T>(kn[e]);
+                vt[e] = from_f32<T>(vx[e]);
+            }
             const int page_id = __builtin_amdgcn_readlane(my_page, p_tok / a.page - pg_first);
             const bool ok = p_tok < a.max_pos && page_id >= 0 && page_id < a.n_pages;
             if (p_tok < a.max_pos && !ok && hk == 0 && lane == 0) raise_flag(a.flag, FLAG_PAGE);
@@ -365,12 +408,25 @@ void decode_attn_kernel(DecodeAttnArgs a) {
                 T *dsv = dst + (int64_t)a.Hkv * a.page * 128;
 #pragma unroll
                 for (int e = 0; e < EPL; ++e) {
-                    dst[e] = from_f32<T>(kn[e]);
-                    dsv[e] = from_f32<T>(vx[e]);
+                    dst[e] = kt[e];
+                    dsv[e] = vt[e];
                 }
             }
-            // the page reads below must see the slot: this wave's stores complete first
-            __builtin_amdgcn_s_waitcnt(0);
+            // the token as the first key of lane group 0 (every lane group holds the
+            // whole row, so every lane gets the same score)
+#pragma unroll
+            for (int j = 0; j < GROUP; ++j) {
+                float d = 0.f;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) d = fmaf(qv[j][e], to_f32<T>(kt[e]), d);
+                d = group_sum<LPR>(d);
+                if (rsub == 0) {
+                    m_run[j] = d;
+                    l_run[j] = 1.f;
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) acc[j][e] = to_f32<T>(vt[e]);
+                }
+            }
         }
         // the prologue's temporaries die here, before the page pipeline's registers are live
         __builtin_amdgcn_sched_barrier(0);
@@ -381,40 +437,25 @@ void decode_attn_kernel(DecodeAttnArgs a) {
 #pragma unroll
             for (int e = 0; e < EPL; ++e) qv[j][e] = q[e] * a.scale_log2;
         }
+        ok_a = load_page<T, NR, RPL>(pool, page_of(pg_first), a.n_pages, a.Hkv, hk, blk, lane_off, ka, va);
     }
 
-    float m_run[GROUP], l_run[GROUP], acc[GROUP][EPL];
-#pragma unroll
-    for (int j = 0; j < GROUP; ++j) {
-        m_run[j] = -INFINITY;
-        l_run[j] = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[j][e] = 0.f;
-    }
-
-    const T *pool = reinterpret_cast<const T *>(a.pool_layer);
-    const int64_t blk = (int64_t)a.page * 128;  // elements of one (page, K|V, head) block
-    const int lane_off = rsub * 128 + d0;
-    const int pg_last = (p_end - 1) / a.page;
-    auto page_of = [&](int pg) { return __builtin_amdgcn_readlane(my_page, pg - pg_first); };
-    u32x4_t ka[NR], va[NR], kb2[NR], vb2[NR];
     // Ping-pong over the chunk's pages.  Every load is issued unconditionally (the index
     // is clamped to the last page, whose re-read hits L2) and every page is processed
     // unconditionally (an invalid page counts no valid token), so no branch forces the
     // outstanding prefetch to drain.
     const int np = pg_last - pg_first + 1;
-    bool ok_a = load_page<T, NR, RPL>(pool, page_of(pg_first), a.n_pages, a.Hkv, hk, blk, lane_off, ka, va);
     bool ok_b;
     for (int i = 0; i < np; i += 2) {
         // ping: page i in (ka, va); pong: page i + 1 in (kb2, vb2)
         const int pg = pg_first + i;
         ok_b = load_page<T, NR, RPL>(pool, page_of(pg_first + min(i + 1, np - 1)), a.n_pages, a.Hkv, hk, blk,
                                      lane_off, kb2, vb2);
-        process_page<T, GROUP, NR, RPL>(ka, va, ok_a ? p_end - pg * a.page : 0, rsub, qv, m_run, l_run, acc);
+        process_page<T, GROUP, NR, RPL>(ka, va, ok_a ? scan_end - pg * a.page : 0, rsub, qv, m_run, l_run, acc);
         if (i + 1 >= np) break;
         ok_a = load_page<T, NR, RPL>(pool, page_of(pg_first + min(i + 2, np - 1)), a.n_pages, a.Hkv, hk, blk,
                                      lane_off, ka, va);
-        process_page<T, GROUP, NR, RPL>(kb2, vb2, ok_b ? p_end - (pg + 1) * a.page : 0, rsub, qv, m_run, l_run,
+        process_page<T, GROUP, NR, RPL>(kb2, vb2, ok_b ? scan_end - (pg + 1) * a.page : 0, rsub, qv, m_run, l_run,
                                         acc);
     }
 
@@ -435,7 +476,7 @@ void decode_attn_kernel(DecodeAttnArgs a) {
             for (int o = LPR; o < 64; o <<= 1) v += __shfl_xor(v, o, WAVE);
             acc[j][e] = v;
         }
-        float *part = a.part + (((int64_t)b * a.H + hk * GROUP + j) * a.n_chunks + c) * PART_STRIDE;
+        float *part = a.part + (((int64_t)b * a.H + hk * GROUP + j) * a.part_stride + c) * PART_STRIDE;
         if (lane < LPR) {
 #pragma unroll
             for (int e = 0; e < EPL; ++e) part[4 + d0 + e] = acc[j][e];
@@ -462,8 +503,10 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeAttnArgs a) {
     int L = (a.shared ? a.pos[0] + b : a.pos[b]) + 1;
     const int cap = a.max_pages * a.page;
     if (L > cap) L = cap;
-    const int nc = min(a.n_chunks, (L + a.chunk - 1) / a.chunk);
-    const float *part = a.part + ((int64_t)b * a.H + h) * a.n_chunks * PART_STRIDE;
+    const bool small = b >= a.b_small;
+    const int chunk = small ? a.chunk2 : a.chunk;
+    const int nc = min(small ? a.n_chunks2 : a.n_chunks, (L + chunk - 1) / chunk);
+    const float *part = a.part + ((int64_t)b * a.H + h) * a.part_stride * PART_STRIDE;
     float M = -INFINITY, lsum = 0.f, o0 = 0.f, o1 = 0.f;
     for (int c0 = 0; c0 < nc; c0 += CB) {
         const int n = min(CB, nc - c0);
@@ -501,7 +544,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeAttnArgs a) {
 void launch_decode_attn(const DecodeAttnArgs &a, DType dt, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     if (a.B <= 0) return;
     const int group = a.H / a.Hkv;
-    const int items = a.B * a.Hkv * a.n_chunks;
+    const int items = a.b_small * a.Hkv * a.n_chunks + (a.B - a.b_small) * a.Hkv * a.n_chunks2;
     const dim3 grid((items + 3) / 4), block(256);
     auto go = [&](auto kernel) {
         if (ev0 || ev1) hipExtLaunchKernelGGL(kernel, grid, block, 0, s, ev0, ev1, 0, a);

@@ -110,7 +110,11 @@ struct DecodeAttnArgs {
     int max_pages, n_pages, page;
     int B, H, Hkv;
     int chunk, n_chunks;  // positions per chunk (multiple of page), chunks per stream
-    float *part;          // [B][H][n_chunks][132]: m, l, pad, pad, acc[128]
+    // streams b >= b_small use chunks of chunk2 positions, n_chunks2 per stream (their
+    // work items are dispatched last); b_small = B: one chunk size
+    int b_small, chunk2, n_chunks2;
+    int part_stride;      // chunks per (stream, head) in part: >= n_chunks, n_chunks2
+    float *part;          // [B][H][part_stride][132]: m, l, pad, pad, acc[128]
     void *out;            // [B][H*128] operand dtype
     float scale_log2;     // log2(e) / sqrt(128)
     int shared;           // prefill of one stream: query b is at position pos[0] + b and
