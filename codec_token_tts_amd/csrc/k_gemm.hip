@@ -1037,7 +1037,11 @@ bool launch_qkv_dense(const GemmArgs &g, const RopeKvArgs &rk, hipStream_t s) {
     // one tile per (128 tokens, head): needs M > 64 (the LDS-DMA kernel), 128-wide heads
     if (g.M <= 64 || g.K % 64 != 0 || g.N != (rk.H + 2 * rk.Hkv) * 128 || g.epi != EPI_STORE) return false;
     const int tiles = ((g.M + 127) / 128) * (g.N / 128);
-    hipLaunchKernelGGL((gemm_lds<128, 128, 2, EPI_QKV>), dim3(tiles), dim3(256), 0, s, g, g.K, rk);
+    // one tile per CU or fewer: the 4-stage ring (128 KB, one block per CU) hides more of
+    // the operand latency (M = 950: 21.8 -> 19.1 us); more tiles: two stages, two blocks
+    // per CU (four stages made the 1728-row guided product slower)
+    if (tiles <= 256) hipLaunchKernelGGL((gemm_lds<128, 128, 4, EPI_QKV>), dim3(tiles), dim3(256), 0, s, g, g.K, rk);
+    else hipLaunchKernelGGL((gemm_lds<128, 128, 2, EPI_QKV>), dim3(tiles), dim3(256), 0, s, g, g.K, rk);
     return true;
 }
 
@@ -1064,14 +1068,27 @@ int launch_gemm(const GemmArgs &g, DType dt, float *part, int64_t part_cap, hipS
         if (pending >= 0) return pending;
     }
     // M > 64 (the MaskGIT pass, prefill-sized products): the LDS-DMA kernel.  Tile
-    // choice from measured sweeps on MI355X at the backbone's shapes: 128x128 tiles with
-    // a two-stage ring (64 KB of LDS: two blocks fit on a CU) when there are >= 128 of
-    // them; otherwise 64x64 tiles, and a residual-add product is split over K (partials
-    // deferred to the next RMSNorm) until there are >= 256 blocks.
+    // choice from measured sweeps and whole-pass runs on MI355X at the backbone's shapes:
+    // * 128x128 tiles with a two-stage ring (64 KB of LDS: two blocks fit on a CU) when
+    //   there are >= 128 of them (256x128 tiles in a three-stage ring were slower for
+    //   gate|up at M = 950: 23.1 -> 25.3 us);
+    // * a residual-add product whose 128x64 tiles, split over K in 2 or 4, make 224..256
+    //   blocks (one per CU): a four-stage ring of those (M = 950: o 12.8 -> 11.9 us, down
+    //   17.1 -> 15.4 us); with fewer or more blocks this lost to the next rule;
+    // * otherwise 64x64 tiles, and a residual-add product is split over K until there
+    //   are >= 256 blocks.
+    // Split partials are deferred to the next RMSNorm.
     if (g.M > 64 && g.K % 64 == 0) {
         const int t128 = ((g.M + 127) / 128) * ((g.N + 127) / 128);
         if (t128 >= 128) return launch_gemm_lds<128, 128, 2>(g, 1, part, s);
         if (g.epi == EPI_SWIGLU) return launch_gemm_lds<64, 128, 4>(g, 1, part, s);
+        if (g.epi == EPI_ADD) {
+            const int t = ((g.M + 127) / 128) * ((g.N + 63) / 64);
+            int sp = 1;
+            while (t * sp * 2 <= 256 && g.K / 64 >= 8 * sp && sp < 4 && (int64_t)(sp * 2) * g.M * g.N <= part_cap)
+                sp *= 2;
+            if (sp >= 2 && t * sp >= 224) return launch_gemm_lds<128, 64, 4>(g, sp, part, s);
+        }
         const int t64 = ((g.M + 63) / 64) * ((g.N + 63) / 64);
         int splits = 1;
         if (g.epi == EPI_ADD)

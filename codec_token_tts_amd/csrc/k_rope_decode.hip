@@ -297,28 +297,23 @@ void decode_attn_kernel(DecodeAttnArgs a) {
     // indices in scalar registers (no per-lane page-id selection loops)
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int item = blockIdx.x * 4 + wave;
-    // streams below b_small in chunks of `chunk` positions, then the rest in chunks of
-    // chunk2 (dispatched last, so the launch ends on short items)
-    const int items1 = a.b_small * a.Hkv * a.n_chunks;
-    if (item >= items1 + (a.B - a.b_small) * a.Hkv * a.n_chunks2) return;
-    const bool small = item >= items1;
-    const int it = small ? item - items1 : item;
-    const int nch = small ? a.n_chunks2 : a.n_chunks, chunk = small ? a.chunk2 : a.chunk;
-    // KV heads vary fastest: the waves of a block stream neighbouring 4 KB blocks of the
-    // same pool pages (a page holds all heads' K and V contiguously)
-    const int hk = it % a.Hkv;
-    const int t = it / a.Hkv;
-    const int c = t % nch, b = (small ? a.b_small : 0) + t / nch;
+    // the step's work list: pair item / Hkv = (stream, chunk, token position); KV heads vary
+    // fastest, so the waves of a block stream neighbouring 4 KB blocks of the same pool
+    // pages (a page holds all heads' K and V contiguously)
+    const int pair = item / a.Hkv, hk = item % a.Hkv;
+    const int n_pairs = *a.plan_n;
+    const int4 w = a.plan[min(pair, a.plan_cap - 1)];
+    if (pair >= n_pairs) return;
+    const int b = w.x, c = w.y, p_tok = w.z;  // p_tok: position of the step's token
+    const int chunk = b >= a.b_small ? a.chunk2 : a.chunk;
 
-    // The chunk's page ids (one per lane, clamped into the row) do not depend on the
-    // stream's length: they are requested together with it.  A page-id load inside the
-    // page loop would have to complete before the next page's addresses exist, and loads
-    // complete in order, so that wait would also drain the prefetch: they are read once.
+    // The chunk's page ids (one per lane, clamped into the row) are read once: a page-id
+    // load inside the page loop would have to complete before the next page's addresses
+    // exist, and loads complete in order, so that wait would also drain the prefetch.
     const int32_t *ptab = a.page_table + (int64_t)(a.shared ? 0 : b) * a.max_pages;
     const int p_begin = c * chunk;
     const int pg_first = p_begin / a.page;
     const int my_page = ptab[min(pg_first + lane, a.max_pages - 1)];
-    const int p_tok = a.shared ? a.pos[0] + b : a.pos[b];  // position of the step's token
     const int d0 = (lane % LPR) * EPL;
     const int rsub = lane / LPR;
     // FUSED: the raw q rows and the q gains do not depend on the position either; they
@@ -333,12 +328,7 @@ void decode_attn_kernel(DecodeAttnArgs a) {
 #pragma unroll
             for (int e = 0; e < EPL; ++e) x[j][e] = row[(hk * GROUP + j) * 128 + d0 + e];
     }
-    int L = p_tok + 1;
-    const int cap = a.max_pages * a.page;
-    if (L > cap) L = cap;
-    if (FUSED && c == 0 && hk == 0 && lane == 0 && (p_tok < 0 || p_tok >= a.max_pos || p_tok >= cap))
-        raise_flag(a.flag, FLAG_POSITION);
-    if (p_begin >= L) return;
+    const int L = min(p_tok + 1, a.max_pages * a.page);  // the plan holds chunks below L only
     const int p_end = min(L, p_begin + chunk);
     // FUSED: the chunk that holds the token's slot takes the token's K / V from registers
     // (rounded to the pool's type, as a read-back would give) and scans only the earlier
@@ -486,6 +476,55 @@ void decode_attn_kernel(DecodeAttnArgs a) {
             part[1] = lt;
         }
     }
+}
+
+// The decode attention's work list, built once per step (the positions are the same in
+// every layer): the (stream, chunk) pairs that hold positions, in dispatch order --
+// streams below b_small in chunks of `chunk`, then the rest in chunks of chunk2 -- each
+// with its stream's token position, and their number in plan_n.  The attention launch is
+// sized for the longest possible streams; with the list no wave is started for an empty
+// chunk (about half of them on a uniform length mix).  With a.flag set, a token outside
+// the cache raises FLAG_POSITION (streams with no valid position get no pair).
+__global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeAttnArgs a, int4 *plan, int *plan_n) {
+    __shared__ int wsum[16];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int cap = a.max_pages * a.page;
+    int base = 0;
+    for (int b0 = 0; b0 < a.B; b0 += 1024) {
+        const int b = b0 + tid;
+        int nc = 0, p_tok = 0;
+        if (b < a.B) {
+            p_tok = a.shared ? a.pos[0] + b : a.pos[b];
+            if (a.flag && (p_tok < 0 || p_tok >= a.max_pos || p_tok >= cap)) raise_flag(a.flag, FLAG_POSITION);
+            const int L = min(p_tok + 1, cap);
+            const bool small = b >= a.b_small;
+            const int chunk = small ? a.chunk2 : a.chunk;
+            nc = L > 0 ? min((L + chunk - 1) / chunk, small ? a.n_chunks2 : a.n_chunks) : 0;
+        }
+        int v = nc;  // inclusive scan: inside the wave, then over the waves' totals
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int t = __shfl_up(v, o, WAVE);
+            if (lane >= o) v += t;
+        }
+        if (lane == 63) wsum[wave] = v;
+        __syncthreads();
+        int off = base + v - nc, total = base;
+        for (int k = 0; k < 16; ++k) {
+            if (k < wave) off += wsum[k];
+            total += wsum[k];
+        }
+        for (int c = 0; c < nc; ++c) plan[off + c] = make_int4(b, c, p_tok, 0);
+        base = total;
+        __syncthreads();  // wsum is reused
+    }
+    if (tid == 0) *plan_n = base;
+}
+
+void launch_decode_plan(const DecodeAttnArgs &a, hipStream_t s) {
+    if (a.B <= 0) return;
+    hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, s, a, const_cast<int4 *>(a.plan),
+                       const_cast<int *>(a.plan_n));
 }
 
 // Merge of the chunk partials of one (stream, head), 32 chunks per pass: lane c loads

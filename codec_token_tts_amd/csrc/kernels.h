@@ -114,6 +114,11 @@ struct DecodeAttnArgs {
     // work items are dispatched last); b_small = B: one chunk size
     int b_small, chunk2, n_chunks2;
     int part_stride;      // chunks per (stream, head) in part: >= n_chunks, n_chunks2
+    // the step's work list (launch_decode_plan): plan_n pairs (stream, chunk, token
+    // position, 0) in dispatch order; plan_cap >= B * max(n_chunks, n_chunks2) entries
+    const int4 *plan;
+    const int *plan_n;
+    int plan_cap;
     float *part;          // [B][H][part_stride][132]: m, l, pad, pad, acc[128]
     void *out;            // [B][H*128] operand dtype
     float scale_log2;     // log2(e) / sqrt(128)
@@ -122,8 +127,9 @@ struct DecodeAttnArgs {
     // Fused step-token preparation (q_len = 1 decode, shared == 0): when qkv is set, q is
     // the per-head RMSNorm + RoPE of the raw projections qkv [B][(H + 2 Hkv) * 128] (the
     // q field is not read), and the wave owning each stream's last chunk writes the
-    // token's normed + rotated K and its V to the pool slot of position pos[b] before it
-    // reads that page; flags as the separate kernel raises them.
+    // token's normed + rotated K and its V to the pool slot of position pos[b] and uses
+    // them from registers; it raises FLAG_PAGE as the separate kernel does (FLAG_POSITION
+    // is raised by the plan kernel).
     const float *qkv;
     const float *q_gain, *k_gain;
     const float2 *rope;   // [max_pos][64] (cos, sin)
@@ -135,6 +141,8 @@ struct DecodeAttnArgs {
 void launch_decode_attn(const DecodeAttnArgs &a, DType dt, hipStream_t s, hipEvent_t ev0 = nullptr,
                         hipEvent_t ev1 = nullptr);
 void launch_decode_combine(const DecodeAttnArgs &a, DType dt, hipStream_t s);
+// Builds a.plan / a.plan_n from the positions (one launch per step, before the layers).
+void launch_decode_plan(const DecodeAttnArgs &a, hipStream_t s);
 
 // ---- K6: bidirectional flash attention (bf16 MFMA) ---------------------------------
 struct FlashArgs {

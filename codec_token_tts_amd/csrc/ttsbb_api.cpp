@@ -74,6 +74,8 @@ struct ttsbb_ctx {
     int pend_rows = 0;
     float2 *rope = nullptr;
     int *flag = nullptr;
+    int4 *plan = nullptr;     // decode attention work list (R * MAX_CHUNKS pairs)
+    int *plan_n = nullptr;
     std::vector<void *> allocs;
     // taps
     int tap_layer = -1;
@@ -250,7 +252,9 @@ TTSBB_API ttsbb_status ttsbb_create(const ttsbb_config *cfg, const ttsbb_layer *
               dev_alloc(c, (void **)&c->rank, (size_t)R * (g.max_head_cols / 2 + 1) * 4) &&
               dev_alloc(c, (void **)&c->gpart, (size_t)c->gpart_cap * 4) &&
               dev_alloc(c, (void **)&c->rope, (size_t)g.max_pos * 64 * sizeof(float2)) &&
-              dev_alloc(c, (void **)&c->flag, 256);
+              dev_alloc(c, (void **)&c->flag, 256) &&
+              dev_alloc(c, (void **)&c->plan, R * MAX_CHUNKS * sizeof(int4)) &&
+              dev_alloc(c, (void **)&c->plan_n, 256);
     if (!ok) {
         free_all(c);
         delete c;
@@ -715,6 +719,35 @@ static ttsbb_status paged_forward(ttsbb_ctx *ctx, int32_t batch, float *x, int32
         }
     }
 
+    // the fields of the attention's arguments that every layer shares, and the step's work
+    // list built from them
+    DecodeAttnArgs da = {};
+    da.pos = positions;
+    da.page_table = page_table;
+    da.max_pages = max_pages;
+    da.n_pages = n_pages;
+    da.page = g.kv_page;
+    da.B = batch;
+    da.H = H;
+    da.Hkv = Hkv;
+    da.chunk = chunk;
+    da.n_chunks = n_chunks;
+    da.b_small = b_small;
+    da.chunk2 = chunk2;
+    da.n_chunks2 = n_chunks2;
+    da.part_stride = max(n_chunks, n_chunks2);
+    da.plan = ctx->plan;
+    da.plan_n = ctx->plan_n;
+    da.plan_cap = (int)(g.max_rows * MAX_CHUNKS);
+    da.part = ctx->part;
+    da.out = ctx->attn;
+    da.scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
+    da.shared = prefill ? 1 : 0;
+    da.max_pos = g.max_pos;
+    if (!prefill) da.flag = ctx->flag;  // the prefill's positions are checked by the rope kernel
+    launch_decode_plan(da, ctx->stream);
+    da.flag = nullptr;
+
     for (int l = 0; l < g.n_layers; ++l) {
         const ttsbb_layer &L = ctx->layers[l];
         const bool tapit = (l == ctx->tap_layer);
@@ -751,27 +784,9 @@ static ttsbb_status paged_forward(ttsbb_ctx *ctx, int32_t batch, float *x, int32
         }
         if (tapit) tap_dense(ctx, TTSBB_TAP_Q, ctx->q, DT_F32, batch, hd_all, hd_all);
 
-        DecodeAttnArgs d = {};
+        DecodeAttnArgs d = da;
         d.q = reinterpret_cast<const float *>(ctx->q);
         d.pool_layer = pool_l;
-        d.pos = positions;
-        d.page_table = page_table;
-        d.max_pages = max_pages;
-        d.n_pages = n_pages;
-        d.page = g.kv_page;
-        d.B = batch;
-        d.H = H;
-        d.Hkv = Hkv;
-        d.chunk = chunk;
-        d.n_chunks = n_chunks;
-        d.b_small = b_small;
-        d.chunk2 = chunk2;
-        d.n_chunks2 = n_chunks2;
-        d.part_stride = max(n_chunks, n_chunks2);
-        d.part = ctx->part;
-        d.out = ctx->attn;
-        d.scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
-        d.shared = prefill ? 1 : 0;
         if (fused) {
             d.qkv = ctx->qkv;
             d.q_gain = L.q_norm;
