@@ -527,14 +527,48 @@ void launch_decode_plan(const DecodeAttnArgs &a, hipStream_t s) {
                        const_cast<int *>(a.plan_n));
 }
 
-// Merge of the chunk partials of one (stream, head), 32 chunks per pass: lane c loads
-// (m_c, l_c) while every lane loads its two output dims of all the pass's chunks, so a
-// pass is one round of loads; the maximum and the weights come from wave reductions and
-// the accumulators are added in chunk order.  Passes after the first rescale the running
-// sums (more than 32 chunks: streams split into short chunks).
+// One pass of the chunk merge over chunks c0 .. c0 + n - 1 (n <= CB): lane c loads
+// (m_c, l_c), and the accumulators arrive as 16-byte loads -- lane l takes dims
+// 4(l % 32) .. +3 of the chunks of parity l / 32 -- so a pass is one round of CB / 2 loads
+// per lane; the maximum and the weights come from wave reductions, each half-wave adds
+// its chunks in chunk order and rescales the running sums of earlier passes (the two
+// halves are added at the end).
+template <int CB>
+__device__ __forceinline__ void combine_pass(const float *part, int c0, int n, int lane, float &M, float &lsum,
+                                             float (&acc)[4]) {
+    const int half = lane >> 5, d4 = (lane & 31) * 4;
+    const int cl = c0 + min(lane, n - 1);  // clamped: unconditional loads
+    const float ml = part[(int64_t)cl * PART_STRIDE], ll = part[(int64_t)cl * PART_STRIDE + 1];
+    float4 x[CB / 2];
+#pragma unroll
+    for (int u = 0; u < CB / 2; ++u)
+        x[u] = *reinterpret_cast<const float4 *>(part + (int64_t)(c0 + min(2 * u + half, n - 1)) * PART_STRIDE + 4 + d4);
+    __builtin_amdgcn_sched_barrier(0);
+    const float mn = fmaxf(M, wave_max(lane < n ? ml : -INFINITY));
+    const float sc = exp2f(M - mn);  // 0 on the first pass (M = -inf)
+    const float wl = lane < n ? exp2f(ml - mn) : 0.f;  // 0 past the pass's chunks
+    lsum = lsum * sc + wave_sum(wl * ll);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] *= sc;
+#pragma unroll
+    for (int u = 0; u < CB / 2; ++u) {
+        if (2 * u >= n) break;
+        const float w0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), 2 * u));
+        const float w1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), 2 * u + 1));
+        const float w = half ? w1 : w0;
+        acc[0] += w * x[u].x;
+        acc[1] += w * x[u].y;
+        acc[2] += w * x[u].z;
+        acc[3] += w * x[u].w;
+    }
+    M = mn;
+}
+
+// Merge of the chunk partials of one (stream, head): one pass of up to 32 chunks, or
+// passes of 64 for streams split into more (the half-size chunks of the last streams),
+// so a stream of up to 64 chunks costs one round of loads.
 template <typename TO>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeAttnArgs a) {
-    constexpr int CB = 32;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int item = blockIdx.x * 4 + wave;
     if (item >= a.B * a.H) return;
@@ -546,38 +580,22 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeAttnArgs a) {
     const int chunk = small ? a.chunk2 : a.chunk;
     const int nc = min(small ? a.n_chunks2 : a.n_chunks, (L + chunk - 1) / chunk);
     const float *part = a.part + ((int64_t)b * a.H + h) * a.part_stride * PART_STRIDE;
-    float M = -INFINITY, lsum = 0.f, o0 = 0.f, o1 = 0.f;
-    for (int c0 = 0; c0 < nc; c0 += CB) {
-        const int n = min(CB, nc - c0);
-        const int cl = c0 + min(lane, n - 1);  // clamped: unconditional loads
-        const float ml = part[(int64_t)cl * PART_STRIDE], ll = part[(int64_t)cl * PART_STRIDE + 1];
-        float x0[CB], x1[CB];
-#pragma unroll
-        for (int u = 0; u < CB; ++u) {
-            const float *pc = part + (int64_t)(c0 + min(u, n - 1)) * PART_STRIDE;
-            x0[u] = pc[4 + lane];
-            x1[u] = pc[4 + 64 + lane];
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        const float mn = fmaxf(M, wave_max(lane < n ? ml : -INFINITY));
-        const float sc = exp2f(M - mn);  // 0 on the first pass (M = -inf)
-        const float wl = lane < n ? exp2f(ml - mn) : 0.f;
-        lsum = lsum * sc + wave_sum(wl * ll);
-        o0 *= sc;
-        o1 *= sc;
-#pragma unroll
-        for (int u = 0; u < CB; ++u) {
-            if (u >= n) continue;
-            const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), u));
-            o0 += w * x0[u];
-            o1 += w * x1[u];
-        }
-        M = mn;
+    float M = -INFINITY, lsum = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
+    if (nc <= 32) {
+        combine_pass<32>(part, 0, nc, lane, M, lsum, acc);
+    } else {
+        for (int c0 = 0; c0 < nc; c0 += 64) combine_pass<64>(part, c0, min(64, nc - c0), lane, M, lsum, acc);
     }
+    // odd chunks (upper half-wave) onto even ones: chunk order within each parity, then
+    // the two parities
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] += __shfl_xor(acc[e], 32, WAVE);
     const float inv = 1.0f / lsum;
-    TO *out = reinterpret_cast<TO *>(a.out) + (int64_t)b * a.H * 128 + h * 128;
-    out[lane] = from_f32<TO>(o0 * inv);
-    out[lane + 64] = from_f32<TO>(o1 * inv);
+    if (lane < 32) {
+        TO *out = reinterpret_cast<TO *>(a.out) + (int64_t)b * a.H * 128 + h * 128 + lane * 4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[e] = from_f32<TO>(acc[e] * inv);
+    }
 }
 
 void launch_decode_attn(const DecodeAttnArgs &a, DType dt, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
