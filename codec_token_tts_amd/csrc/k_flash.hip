@@ -9,11 +9,12 @@
 //   S^T (32 keys x 32 queries) = K (32 x 128) * Q^T (128 x 32)        8 products
 //   O^T (32 dims x 32 queries) = V^T (32 x 32) * P^T (32 x 32)         2 products / tile
 // Lane l holds S^T rows 8j + 4(l/32) + i (j, i < 4) of query l%32, so the softmax
-// statistics of a query live in lanes l and l^32.  P^T feeds the second product
-// straight from registers: its 16-key contraction slots (h = l/32, i < 8) are mapped
-// to keys 4h + i (i < 4) and 8 + 4h + (i - 4), the keys the lane already holds, and
-// the V^T operand is read from LDS in that same key order (two 8-byte reads).  V is
-// stored transposed ([Hkv][128][s_pad]), so those reads are contiguous.
+// statistics of a query live in lanes l and l^32.  The K tile's LDS row r holds key
+// pi(r), pi swapping bits 2 and 3 of the row index, so that the keys of accumulator
+// entries 8kk .. 8kk + 7 of lane l are the 8 consecutive keys 16kk + 8(l/32) ..: P^T
+// feeds the second product straight from registers, and its V^T operand (V stored
+// transposed, [Hkv][128][s_pad]) is one 16-byte LDS read per lane (the 80-byte row
+// stride keeps 8 consecutive rows on distinct banks).
 //
 // Block = 8 waves = 4 key quarters x 2 waves.  The two waves of a quarter are the two
 // query heads of a GQA group over the same 32 queries (or, without GQA, two query
@@ -56,7 +57,9 @@ __device__ __forceinline__ void flash_sstore(bf16_t *sk, bf16_t *sv, int qtid, c
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
         const int ch = qtid + 128 * c;
-        *reinterpret_cast<u32x4_t *>(&sk[(ch >> 4) * LDKF + (ch & 15) * 8]) = rk[c];
+        const int key = ch >> 4;  // stored at row pi(key): bits 2 and 3 swapped
+        const int row = (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
+        *reinterpret_cast<u32x4_t *>(&sk[row * LDKF + (ch & 15) * 8]) = rk[c];
         *reinterpret_cast<u32x4_t *>(&sv[(ch >> 2) * LDVF + (ch & 3) * 8]) = rv[c];
     }
 }
@@ -137,16 +140,13 @@ __global__ __launch_bounds__(512) void flash_kernel(FlashArgs a) {
         for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                const bf16_t *vrow = &sv[(dt * 32 + fq) * LDVF + kk * 16 + h * 4];
-                const bf16x4_t lo = *reinterpret_cast<const bf16x4_t *>(vrow);
-                const bf16x4_t hi = *reinterpret_cast<const bf16x4_t *>(vrow + 8);
-                vfr[dt][kk] = bf16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                vfr[dt][kk] = *reinterpret_cast<const bf16x8_t *>(&sv[(dt * 32 + fq) * LDVF + kk * 16 + h * 8]);
             }
         // mask keys past the sequence (and the blocks of a finished quarter): only partial blocks
         if (!(valid && kbase + FB <= ke)) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int key = kbase + (r >> 2) * 8 + h * 4 + (r & 3);
+                const int key = kbase + (r >> 3) * 16 + h * 8 + (r & 7);
                 if (!(valid && key < ke)) s[r] = -INFINITY;
             }
         }
@@ -168,8 +168,8 @@ __global__ __launch_bounds__(512) void flash_kernel(FlashArgs a) {
         }
         const float m_neg = m_run == -INFINITY ? 0.f : -m_run;  // nothing seen yet: all weights 0
 
-        // P^T operand of the 16-key chunk kk: slots i < 4 <- rows 8(2kk) + 4h + i,
-        // slots 4..7 <- rows 8(2kk+1) + 4h + i - 4, i.e. accumulator entries 8kk + i
+        // P^T operand of the 16-key chunk kk: slot e <- accumulator entry 8kk + e, i.e.
+        // key 16kk + 8h + e
         bf16x8_t pb[2];
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)

@@ -1070,8 +1070,9 @@ int launch_gemm(const GemmArgs &g, DType dt, float *part, int64_t part_cap, hipS
     // M > 64 (the MaskGIT pass, prefill-sized products): the LDS-DMA kernel.  Tile
     // choice from measured sweeps and whole-pass runs on MI355X at the backbone's shapes:
     // * 128x128 tiles with a two-stage ring (64 KB of LDS: two blocks fit on a CU) when
-    //   there are >= 128 of them (256x128 tiles in a three-stage ring were slower for
-    //   gate|up at M = 950: 23.1 -> 25.3 us);
+    //   there are >= 128 of them; but gate|up, when 192x128 tiles fit the CUs once, runs
+    //   those in a three-stage ring (120 KB, one block per CU: M = 950 23.4 -> 21.4 us;
+    //   256x128 tiles were slower, 25.3 us);
     // * a residual-add product whose 128x64 tiles, split over K in 2 or 4, make 224..256
     //   blocks (one per CU): a four-stage ring of those (M = 950: o 12.8 -> 11.9 us, down
     //   17.1 -> 15.4 us); with fewer or more blocks this lost to the next rule;
@@ -1080,7 +1081,11 @@ int launch_gemm(const GemmArgs &g, DType dt, float *part, int64_t part_cap, hipS
     // Split partials are deferred to the next RMSNorm.
     if (g.M > 64 && g.K % 64 == 0) {
         const int t128 = ((g.M + 127) / 128) * ((g.N + 127) / 128);
-        if (t128 >= 128) return launch_gemm_lds<128, 128, 2>(g, 1, part, s);
+        if (t128 >= 128) {
+            if (g.epi == EPI_SWIGLU && ((g.M + 191) / 192) * ((g.N + 127) / 128) <= 256)
+                return launch_gemm_lds<192, 128, 3>(g, 1, part, s);
+            return launch_gemm_lds<128, 128, 2>(g, 1, part, s);
+        }
         if (g.epi == EPI_SWIGLU) return launch_gemm_lds<64, 128, 4>(g, 1, part, s);
         if (g.epi == EPI_ADD) {
             const int t = ((g.M + 127) / 128) * ((g.N + 63) / 64);

@@ -688,7 +688,7 @@ def test_empty_calls_are_no_ops():
 @pytest.mark.parametrize("bf16", [False, True])
 def test_decode_longest_cache(bf16):
     """One stream at the last position max_pos - 1 (8191: 512 pages, 64 chunks of 128 merged
-    in two passes) next to a short one."""
+    in one pass of 64) next to a short one."""
     shape = CFG.Shape(n_layers=1)
     m = Model(shape, 1, bf16, seed=17, max_pos=8192)
     try:
@@ -699,6 +699,26 @@ def test_decode_longest_cache(bf16):
         else:
             assert np.max(np.abs(res["x"] - ref["x"])) <= 1e-4
         assert res["pos"].tolist() == [8192, 4]
+    finally:
+        m.close()
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_decode_split_chunks_multi_pass(bf16):
+    """Six streams: the last sixth (stream 5) is cut into half-size chunks (64 positions) and
+    holds 126 of them, merged in two passes of 64; the others use 128-position chunks (one
+    merge pass of 64 for stream 0's 64 chunks and stream 3's 33, one of 32 for the rest).
+    Every stream's layer output against the oracle."""
+    shape = CFG.Shape(n_layers=1)
+    m = Model(shape, 1, bf16, seed=23, max_pos=8192)
+    try:
+        lengths = [8191, 3, 200, 4097, 1000, 8000]
+        res, ref = run_decode(m, lengths, 23, tap_layer=0, gpu_tap=False)
+        if bf16:
+            assert normwise(res["x"], ref["x"]) <= TOL_LAYER_BF16
+        else:
+            assert np.max(np.abs(res["x"] - ref["x"])) <= 1e-4
+        assert res["pos"].tolist() == [n + 1 for n in lengths]
     finally:
         m.close()
 
