@@ -41,14 +41,19 @@ typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 
 // Global -> register staging of one 32-key block of K (8 KB) and V^T (8 KB) by the 128
-// threads of a quarter.
-__device__ __forceinline__ void flash_gload(const bf16_t *kg, const bf16_t *vg, int s_pad, int kb0, int qtid,
+// threads of a quarter: copy c takes K row 8c + qtid / 16 (16-byte chunk qtid % 16) and
+// V^T row 32c + qtid / 4 (keys 8 (qtid % 4) .. +7).  klane / vlane hold the thread's part
+// of the addresses, so a copy adds only the block's first key and a constant (K) or a
+// scalar stride (V^T) -- no per-copy index arithmetic on the VALU.
+__device__ __forceinline__ void flash_gload(const bf16_t *klane, const bf16_t *vlane, int s_pad, int kb0,
                                             u32x4_t (&rk)[4], u32x4_t (&rv)[4]) {
+    const bf16_t *kl = klane + (int64_t)kb0 * 128;
+    const bf16_t *vl = vlane + kb0;
+    const int64_t vstride = (int64_t)32 * s_pad;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-        const int ch = qtid + 128 * c;
-        rk[c] = *reinterpret_cast<const u32x4_t *>(kg + (int64_t)(kb0 + (ch >> 4)) * 128 + (ch & 15) * 8);
-        rv[c] = *reinterpret_cast<const u32x4_t *>(vg + (int64_t)(ch >> 2) * s_pad + kb0 + (ch & 3) * 8);
+        rk[c] = *reinterpret_cast<const u32x4_t *>(kl + c * 1024);
+        rv[c] = *reinterpret_cast<const u32x4_t *>(vl + c * vstride);
     }
 }
 
@@ -112,14 +117,16 @@ __global__ __launch_bounds__(512) void flash_kernel(FlashArgs a) {
     float m_run = -INFINITY, l_run = 0.f;
 
     u32x4_t rk[4], rv[4];
-    flash_gload(kg, vg, a.s_pad, kb + blk(0) * FB, qtid, rk, rv);
+    const bf16_t *klane = kg + (qtid >> 4) * 128 + (qtid & 15) * 8;
+    const bf16_t *vlane = vg + (int64_t)(qtid >> 2) * a.s_pad + (qtid & 3) * 8;
+    flash_gload(klane, vlane, a.s_pad, kb + blk(0) * FB, rk, rv);
     flash_sstore(sk0, sv0, qtid, rk, rv);
     __syncthreads();
     for (int i = 0; i < NBQ; ++i) {
         const int buf = i & 1;
         const bf16_t *sk = buf ? sk1 : sk0;
         const bf16_t *sv = buf ? sv1 : sv0;
-        flash_gload(kg, vg, a.s_pad, kb + blk(i + 1) * FB, qtid, rk, rv);  // unconditional (clamped)
+        flash_gload(klane, vlane, a.s_pad, kb + blk(i + 1) * FB, rk, rv);  // unconditional (clamped)
         // keep the prefetch at the top of the iteration: it has the whole block to arrive
         __builtin_amdgcn_sched_barrier(0);
         const bool valid = i < nb_mine;
@@ -129,11 +136,17 @@ __global__ __launch_bounds__(512) void flash_kernel(FlashArgs a) {
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks)
             kf[ks] = *reinterpret_cast<const bf16x8_t *>(&sk[fq * LDKF + ks * 16 + h * 8]);
+        // The two waves of a SIMD reach the score products together; the wave that issues
+        // them first at raised priority runs its chain while the other waits for the matrix
+        // core, then its softmax overlaps the other's products (21.7 -> 20.7 us; a fixed
+        // priority per wave, or raising it for the V products too, did no better).
+        __builtin_amdgcn_s_setprio(1);
         f32x16_t s;
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], s, 0, 0, 0);
+        __builtin_amdgcn_s_setprio(0);
         // V^T fragments are independent of the softmax: their reads overlap it
         bf16x8_t vfr[4][2];
 #pragma unroll
