@@ -723,6 +723,22 @@ def test_decode_split_chunks_multi_pass(bf16):
         m.close()
 
 
+def test_decode_more_streams_than_one_plan_pass():
+    """1100 streams (more than the work-list kernel's 1024 threads, so its prefix sum runs
+    over two passes), short caches including empty ones (position 0), bf16: every
+    stream's layer output against the oracle."""
+    shape = CFG.Shape(n_layers=1)
+    m = Model(shape, 1, True, seed=29, max_rows=1200, max_pos=256)
+    try:
+        lengths = [int(v) for v in gen.uniform_int(29, stream_id(gen.KIND_CODES, 1), (1100,), 41)]
+        lengths[0], lengths[1099] = 0, 40
+        res, ref = run_decode(m, lengths, 29, tap_layer=0, gpu_tap=False)
+        assert normwise(res["x"], ref["x"]) <= TOL_LAYER_BF16
+        assert res["pos"].tolist() == [n + 1 for n in lengths]
+    finally:
+        m.close()
+
+
 def test_maskgit_at_row_limit():
     """S = max_rows = 1024 (24 text tokens + 1000 frames): whole 128-row tiles, no ragged
     tail, 32 key blocks; one layer against the oracle."""
