@@ -304,8 +304,7 @@ void decode_attn_kernel(DecodeAttnArgs a) {
     const int n_pairs = *a.plan_n;
     const int4 w = a.plan[min(pair, a.plan_cap - 1)];
     if (pair >= n_pairs) return;
-    const int b = w.x, c = w.y, p_tok = w.z;  // p_tok: position of the step's token
-    const int chunk = b >= a.b_small ? a.chunk2 : a.chunk;
+    const int b = w.x, c = w.y, p_tok = w.z, chunk = w.w;  // p_tok: position of the step's token
 
     // The chunk's page ids (one per lane, clamped into the row) are read once: a page-id
     // load inside the page loop would have to complete before the next page's addresses
@@ -479,16 +478,48 @@ void decode_attn_kernel(DecodeAttnArgs a) {
 }
 
 // The decode attention's work list, built once per step (the positions are the same in
-// every layer): the (stream, chunk) pairs that hold positions, in dispatch order --
-// streams below b_small in chunks of `chunk`, then the rest in chunks of chunk2 -- each
-// with its stream's token position, and their number in plan_n.  The attention launch is
-// sized for the longest possible streams; with the list no wave is started for an empty
-// chunk (about half of them on a uniform length mix).  With a.flag set, a token outside
-// the cache raises FLAG_POSITION (streams with no valid position get no pair).
+// every layer): the (stream, chunk) pairs that hold positions, stream by stream, each
+// with its stream's token position and the chunk size, and their number in plan_n[0].
+// The attention launch is sized for the longest possible streams; with the list no wave
+// is started for an empty chunk.  Balanced split (target_items > 0, q_len = 1 decode):
+// the chunk grows from a.chunk, a page at a time, until the step's work items fit
+// target_items -- two workgroups of four waves per CU -- so every item starts at the
+// launch's beginning, no CU holds more items than another and none waits for a slot (at
+// most 64 pages per chunk); plan_n[1] = the chunk.  With a.flag set, a token outside the
+// cache raises FLAG_POSITION (streams with no valid position get no pair).
 __global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeAttnArgs a, int4 *plan, int *plan_n) {
     __shared__ int wsum[16];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int cap = a.max_pages * a.page;
+    auto length = [&](int b) {  // positions of stream b in the cache (0 for an invalid token)
+        const int p_tok = a.shared ? a.pos[0] + b : a.pos[b];
+        return max(0, min(p_tok + 1, cap));
+    };
+    auto block_sum = [&](int v) {
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o, WAVE);
+        __syncthreads();  // wsum's previous use is over
+        if (lane == 0) wsum[wave] = v;
+        __syncthreads();
+        int t = 0;
+        for (int k = 0; k < 16; ++k) t += wsum[k];
+        return t;
+    };
+    int chunk = a.chunk;
+    if (a.target_items > 0) {
+        int tot = 0;
+        for (int b = tid; b < a.B; b += 1024) tot += length(b);
+        tot = block_sum(tot);
+        const int per = (int)(((int64_t)tot * a.Hkv + a.target_items - 1) / a.target_items);
+        chunk = min(max(a.chunk, (per + a.page - 1) / a.page * a.page), 64 * a.page);
+        for (;;) {
+            int n = 0;
+            for (int b = tid; b < a.B; b += 1024) n += (length(b) + chunk - 1) / chunk;
+            n = block_sum(n);
+            if ((int64_t)n * a.Hkv <= a.target_items || chunk >= 64 * a.page) break;
+            chunk += a.page;
+        }
+    }
     int base = 0;
     for (int b0 = 0; b0 < a.B; b0 += 1024) {
         const int b = b0 + tid;
@@ -497,9 +528,7 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeAttnArgs a, int
             p_tok = a.shared ? a.pos[0] + b : a.pos[b];
             if (a.flag && (p_tok < 0 || p_tok >= a.max_pos || p_tok >= cap)) raise_flag(a.flag, FLAG_POSITION);
             const int L = min(p_tok + 1, cap);
-            const bool small = b >= a.b_small;
-            const int chunk = small ? a.chunk2 : a.chunk;
-            nc = L > 0 ? min((L + chunk - 1) / chunk, small ? a.n_chunks2 : a.n_chunks) : 0;
+            nc = L > 0 ? min((L + chunk - 1) / chunk, a.n_chunks) : 0;
         }
         int v = nc;  // inclusive scan: inside the wave, then over the waves' totals
 #pragma unroll
@@ -507,6 +536,7 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeAttnArgs a, int
             const int t = __shfl_up(v, o, WAVE);
             if (lane >= o) v += t;
         }
+        __syncthreads();  // wsum's previous use is over
         if (lane == 63) wsum[wave] = v;
         __syncthreads();
         int off = base + v - nc, total = base;
@@ -514,11 +544,13 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeAttnArgs a, int
             if (k < wave) off += wsum[k];
             total += wsum[k];
         }
-        for (int c = 0; c < nc; ++c) plan[off + c] = make_int4(b, c, p_tok, 0);
+        for (int c = 0; c < nc; ++c) plan[off + c] = make_int4(b, c, p_tok, chunk);
         base = total;
-        __syncthreads();  // wsum is reused
     }
-    if (tid == 0) *plan_n = base;
+    if (tid == 0) {
+        plan_n[0] = base;
+        plan_n[1] = chunk;
+    }
 }
 
 void launch_decode_plan(const DecodeAttnArgs &a, hipStream_t s) {
@@ -576,9 +608,8 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeAttnArgs a) {
     int L = (a.shared ? a.pos[0] + b : a.pos[b]) + 1;
     const int cap = a.max_pages * a.page;
     if (L > cap) L = cap;
-    const bool small = b >= a.b_small;
-    const int chunk = small ? a.chunk2 : a.chunk;
-    const int nc = min(small ? a.n_chunks2 : a.n_chunks, (L + chunk - 1) / chunk);
+    const int chunk = a.plan_n[1];  // the step's chunk (from the work list)
+    const int nc = min(a.n_chunks, (L + chunk - 1) / chunk);
     const float *part = a.part + ((int64_t)b * a.H + h) * a.part_stride * PART_STRIDE;
     float M = -INFINITY, lsum = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
     if (nc <= 32) {
@@ -601,7 +632,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeAttnArgs a) {
 void launch_decode_attn(const DecodeAttnArgs &a, DType dt, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     if (a.B <= 0) return;
     const int group = a.H / a.Hkv;
-    const int items = a.b_small * a.Hkv * a.n_chunks + (a.B - a.b_small) * a.Hkv * a.n_chunks2;
+    const int items = a.B * a.Hkv * a.n_chunks;  // at most; the work list holds the real ones
     const dim3 grid((items + 3) / 4), block(256);
     auto go = [&](auto kernel) {
         if (ev0 || ev1) hipExtLaunchKernelGGL(kernel, grid, block, 0, s, ev0, ev1, 0, a);

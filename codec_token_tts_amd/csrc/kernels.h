@@ -109,16 +109,16 @@ struct DecodeAttnArgs {
     const int32_t *page_table;
     int max_pages, n_pages, page;
     int B, H, Hkv;
-    int chunk, n_chunks;  // positions per chunk (multiple of page), chunks per stream
-    // streams b >= b_small use chunks of chunk2 positions, n_chunks2 per stream (their
-    // work items are dispatched last); b_small = B: one chunk size
-    int b_small, chunk2, n_chunks2;
-    int part_stride;      // chunks per (stream, head) in part: >= n_chunks, n_chunks2
-    // the step's work list (launch_decode_plan): plan_n pairs (stream, chunk, token
-    // position, 0) in dispatch order; plan_cap >= B * max(n_chunks, n_chunks2) entries
+    int chunk, n_chunks;  // least positions per chunk (multiple of page), most chunks per stream
+    int part_stride;      // chunks per (stream, head) in part: >= n_chunks
+    // the step's work list (launch_decode_plan): plan_n[0] items (stream, chunk index,
+    // token position, chunk size) in dispatch order, plan_n[1] the step's chunk size
+    // (>= chunk); plan_cap >= B * n_chunks entries.  target_items > 0: the plan grows the
+    // chunk until the items fit that many waves.
     const int4 *plan;
     const int *plan_n;
     int plan_cap;
+    int target_items;
     float *part;          // [B][H][part_stride][132]: m, l, pad, pad, acc[128]
     void *out;            // [B][H*128] operand dtype
     float scale_log2;     // log2(e) / sqrt(128)

@@ -28,8 +28,6 @@ using namespace ttsbb;
 namespace {
 
 constexpr int MAX_CHUNKS = 32;   // decode attention partials per (stream, head)
-constexpr int SMALL_CHUNK_STREAMS_NUM = 1, SMALL_CHUNK_STREAMS_DEN = 6;  // streams in short chunks
-constexpr int SMALL_CHUNK_DIV = 2;                                      // their chunk = chunk / 2
 constexpr int PART_STRIDE = 132; // floats per partial (m, l, 2 pad, 128 dims)
 
 struct Tap {
@@ -54,6 +52,7 @@ struct ttsbb_ctx {
     DType dt = DT_BF16;
     size_t esz = 2;  // bytes per operand element
     int qkv_w = 0;   // (H + 2 Hkv) * head_dim
+    int n_cu = 256;  // compute units of the context's device
     // workspace
     void *h = nullptr;
     float *qkv = nullptr;
@@ -232,6 +231,12 @@ TTSBB_API ttsbb_status ttsbb_create(const ttsbb_config *cfg, const ttsbb_layer *
     c->dt = g.dtype == TTSBB_BF16 ? DT_BF16 : DT_F32;
     c->esz = g.dtype == TTSBB_BF16 ? 2 : 4;
     c->qkv_w = (g.n_heads + 2 * g.n_kv_heads) * g.head_dim;
+    {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+            c->n_cu = n;
+    }
 
     const size_t R = (size_t)g.max_rows;
     const size_t hd_all = (size_t)g.n_heads * g.head_dim;
@@ -704,20 +709,6 @@ static ttsbb_status paged_forward(ttsbb_ctx *ctx, int32_t batch, float *x, int32
         n_chunks = (cap + chunk - 1) / chunk;
     }
     if (chunk > 64 * g.kv_page) return TTSBB_UNSUPPORTED;
-    // The last sixth of the streams (their items are dispatched last) use half-size chunks
-    // when the buffer has room: at full memory concurrency a 128-position item takes
-    // 20-40 us, so the launch's tail is set by the items that start last; halving those
-    // shortens it (measured on the 64-stream workload: 99.9 -> 97.4 us; a third, a quarter
-    // or an eighth of the streams, or quarter-size chunks, did no better).
-    int b_small = batch, chunk2 = chunk, n_chunks2 = n_chunks;
-    if (!prefill && chunk / SMALL_CHUNK_DIV >= g.kv_page && batch >= SMALL_CHUNK_STREAMS_DEN) {
-        const int c2 = round_up(chunk / SMALL_CHUNK_DIV, g.kv_page), n2 = (cap + c2 - 1) / c2;
-        if ((int64_t)batch * n2 <= (int64_t)g.max_rows * MAX_CHUNKS && c2 < chunk) {
-            b_small = batch - batch * SMALL_CHUNK_STREAMS_NUM / SMALL_CHUNK_STREAMS_DEN;
-            chunk2 = c2;
-            n_chunks2 = n2;
-        }
-    }
 
     // the fields of the attention's arguments that every layer shares, and the step's work
     // list built from them
@@ -732,13 +723,14 @@ static ttsbb_status paged_forward(ttsbb_ctx *ctx, int32_t batch, float *x, int32
     da.Hkv = Hkv;
     da.chunk = chunk;
     da.n_chunks = n_chunks;
-    da.b_small = b_small;
-    da.chunk2 = chunk2;
-    da.n_chunks2 = n_chunks2;
-    da.part_stride = max(n_chunks, n_chunks2);
+    da.part_stride = n_chunks;
     da.plan = ctx->plan;
     da.plan_n = ctx->plan_n;
     da.plan_cap = (int)(g.max_rows * MAX_CHUNKS);
+    // q_len = 1 decode: the work list balances the items over the CUs, two workgroups of
+    // four waves per CU (measured on the 64-stream workload: 97.7 -> 95.1 us; one or three
+    // workgroups per CU, or targets between the multiples, were slower)
+    da.target_items = prefill ? 0 : 8 * ctx->n_cu;
     da.part = ctx->part;
     da.out = ctx->attn;
     da.scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));

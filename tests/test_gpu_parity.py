@@ -704,15 +704,14 @@ def test_decode_longest_cache(bf16):
 
 
 @pytest.mark.parametrize("bf16", [False, True])
-def test_decode_split_chunks_multi_pass(bf16):
-    """Six streams: the last sixth (stream 5) is cut into half-size chunks (64 positions) and
-    holds 126 of them, merged in two passes of 64; the others use 128-position chunks (one
-    merge pass of 64 for stream 0's 64 chunks and stream 3's 33, one of 32 for the rest).
-    Every stream's layer output against the oracle."""
+def test_decode_long_stream_multi_pass_merge(bf16):
+    """Six streams, one of them at 16000 positions: 125 chunks of 128 (the work list keeps
+    the 128-position chunk at this total), merged in two passes of 64; the others in one
+    pass.  Every stream's layer output against the oracle."""
     shape = CFG.Shape(n_layers=1)
-    m = Model(shape, 1, bf16, seed=23, max_pos=8192)
+    m = Model(shape, 1, bf16, seed=23, max_pos=16384)
     try:
-        lengths = [8191, 3, 200, 4097, 1000, 8000]
+        lengths = [8191, 3, 200, 4097, 1000, 16000]
         res, ref = run_decode(m, lengths, 23, tap_layer=0, gpu_tap=False)
         if bf16:
             assert normwise(res["x"], ref["x"]) <= TOL_LAYER_BF16
