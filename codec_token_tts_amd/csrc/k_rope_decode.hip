@@ -301,18 +301,18 @@ void decode_attn_kernel(DecodeAttnArgs a) {
     // fastest, so the waves of a block stream neighbouring 4 KB blocks of the same pool
     // pages (a page holds all heads' K and V contiguously)
     const int pair = item / a.Hkv, hk = item % a.Hkv;
+    const int pc = min(pair, a.plan_cap - 1);
+    // The chunk's page ids (one per lane) come with the pair, in the same round of loads,
+    // and are read once: a page-id load inside the page loop would have to complete before
+    // the next page's addresses exist, and loads complete in order, so that wait would also
+    // drain the prefetch.
     const int n_pairs = *a.plan_n;
-    const int4 w = a.plan[min(pair, a.plan_cap - 1)];
+    const int4 w = a.plan[pc];
+    const int my_page = a.plan_pages[(int64_t)pc * 64 + lane];
     if (pair >= n_pairs) return;
     const int b = w.x, c = w.y, p_tok = w.z, chunk = w.w;  // p_tok: position of the step's token
-
-    // The chunk's page ids (one per lane, clamped into the row) are read once: a page-id
-    // load inside the page loop would have to complete before the next page's addresses
-    // exist, and loads complete in order, so that wait would also drain the prefetch.
-    const int32_t *ptab = a.page_table + (int64_t)(a.shared ? 0 : b) * a.max_pages;
     const int p_begin = c * chunk;
     const int pg_first = p_begin / a.page;
-    const int my_page = ptab[min(pg_first + lane, a.max_pages - 1)];
     const int d0 = (lane % LPR) * EPL;
     const int rsub = lane / LPR;
     // FUSED: the raw q rows and the q gains do not depend on the position either; they
@@ -546,6 +546,15 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeAttnArgs a, int
         }
         for (int c = 0; c < nc; ++c) plan[off + c] = make_int4(b, c, p_tok, chunk);
         base = total;
+    }
+    // page ids of every pair's chunk, one per lane of the attention wave (clamped into the
+    // stream's page-table row); the pairs written above are visible after the barrier
+    __syncthreads();
+    for (int idx = tid; idx < base * 64; idx += 1024) {
+        const int pr = idx >> 6, j = idx & 63;
+        const int4 w = plan[pr];
+        const int32_t *ptab = a.page_table + (int64_t)(a.shared ? 0 : w.x) * a.max_pages;
+        a.plan_pages[idx] = ptab[min(w.y * w.w / a.page + j, a.max_pages - 1)];
     }
     if (tid == 0) {
         plan_n[0] = base;

@@ -117,6 +117,7 @@ struct DecodeAttnArgs {
     // chunk until the items fit that many waves.
     const int4 *plan;
     const int *plan_n;
+    int *plan_pages;      // [plan_cap][64]: page ids of each item's chunk (one per lane)
     int plan_cap;
     int target_items;
     float *part;          // [B][H][part_stride][132]: m, l, pad, pad, acc[128]

@@ -75,6 +75,7 @@ struct ttsbb_ctx {
     int *flag = nullptr;
     int4 *plan = nullptr;     // decode attention work list (R * MAX_CHUNKS pairs)
     int *plan_n = nullptr;
+    int *plan_pages = nullptr;  // [R * MAX_CHUNKS][64]
     std::vector<void *> allocs;
     // taps
     int tap_layer = -1;
@@ -259,7 +260,8 @@ TTSBB_API ttsbb_status ttsbb_create(const ttsbb_config *cfg, const ttsbb_layer *
               dev_alloc(c, (void **)&c->rope, (size_t)g.max_pos * 64 * sizeof(float2)) &&
               dev_alloc(c, (void **)&c->flag, 256) &&
               dev_alloc(c, (void **)&c->plan, R * MAX_CHUNKS * sizeof(int4)) &&
-              dev_alloc(c, (void **)&c->plan_n, 256);
+              dev_alloc(c, (void **)&c->plan_n, 256) &&
+              dev_alloc(c, (void **)&c->plan_pages, R * MAX_CHUNKS * 64 * sizeof(int));
     if (!ok) {
         free_all(c);
         delete c;
@@ -726,6 +728,7 @@ static ttsbb_status paged_forward(ttsbb_ctx *ctx, int32_t batch, float *x, int32
     da.part_stride = n_chunks;
     da.plan = ctx->plan;
     da.plan_n = ctx->plan_n;
+    da.plan_pages = ctx->plan_pages;
     da.plan_cap = (int)(g.max_rows * MAX_CHUNKS);
     // q_len = 1 decode: the work list balances the items over the CUs, two workgroups of
     // four waves per CU (measured on the 64-stream workload: 97.7 -> 95.1 us; one or three
