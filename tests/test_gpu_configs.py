@@ -208,7 +208,7 @@ def test_c5_paged_decode_64_streams():
         x_h, am_h, lg_h = x.cpu().numpy(), am.cpu().numpy(), lg.cpu().numpy()
         assert pos.cpu().numpy().tolist() == [int(n) + 1 for n in lengths]
         # the longest and the shortest stream, one in between, and the last stream (the
-        # last streams' work is split into half-size chunks)
+        # last items of the work list)
         sample = [int(np.argmax(lengths)), int(np.argmin(lengths)), 5, len(lengths) - 1]
         cache = oracle_cache(m, w.seed, lengths, sample)
         xo = O.codebook_embed(codes[sample], widen(tab_h), V)
