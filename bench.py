@@ -11,7 +11,9 @@ Default workload ("c5c4"): one step is
     (32 steps; codes are restored every 32 passes).
 Inputs are seeded synthetic tensors resident in HBM before the timed region.  `value` is
 decode tokens/s (64 tokens per step over the decode part of the step); MaskGIT frames/s
-and MFMA utilisation, and decode-attention HBM GB/s are reported beside it.
+and MFMA utilisation, and decode-attention HBM GB/s are reported beside it, with per-kernel
+rates: each MaskGIT product and the flash attention in TF/s and against the bf16 MFMA peak,
+the decode projections as weight-streaming GB/s, the embeddings in GB/s.
 
 Further figures, each timed on its own after the step: a guided and a guided + sampled
 MaskGIT step, a 200-token causal prefill, the codec RVQ decode of 750 frames, and the
@@ -531,6 +533,26 @@ def run_c5c4(args, T, torch):
     mg_mfma_ms = sum(pm[k][0] for k in ("gemm_qkv", "gemm_o", "gemm_gate_up", "gemm_down",
                                         "flash_attn")) / args.steps
     mfma_tflops = (gemm + attn_f) / (mg_mfma_ms * 1e-3) / 1e12
+    # per-kernel figures: MaskGIT products and attention against the bf16 MFMA peak; the
+    # decode projections against HBM as weight streaming (31.46 MB of bf16 weights per
+    # layer, each read once per step); the embeddings against HBM (gathered table rows in,
+    # fp32 rows out)
+    S = mg.e["n_text"] + mg.e["n_frames"]
+    per_kernel_flops = {"gemm_qkv": 2 * S * 4096 * 1024 * 28, "gemm_o": 2 * S * 1024 * 2048 * 28,
+                        "gemm_gate_up": 2 * S * 6144 * 1024 * 28, "gemm_down": 2 * S * 1024 * 3072 * 28,
+                        "flash_attn": attn_f}
+    mg_kernels = {}
+    for k, f in per_kernel_flops.items():
+        ms = pm[k][0] / args.steps
+        if ms > 0:
+            mg_kernels[k] = {"tflops": round(f / (ms * 1e-3) / 1e12, 1),
+                             "mfma_util": round(f / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+    w_bytes = 28 * 2 * (1024 * 4096 + 2048 * 1024 + 1024 * 6144 + 3072 * 1024)
+    dec_gemm_ms = sum(pd[k][0] for k in ("gemm_qkv", "gemm_o", "gemm_gate_up", "gemm_down")) / args.steps
+    dec_embed_ms = pd["embed"][0] / args.steps
+    mg_embed_ms = pm["embed"][0] / args.steps
+    dec_embed_bytes = dec.B * (dec.K * 1024 * 2 + 1024 * 4)
+    mg_embed_bytes = mg.e["n_frames"] * mg.e["n_cb"] * 1024 * 2 + mg.e["n_text"] * 1024 * 2 + S * 1024 * 4
 
     res = {
         "metric": METRIC,
@@ -549,11 +571,15 @@ def run_c5c4(args, T, torch):
                                "8x1025) + c4 MaskGIT pass (28 layers, S=950, 8x1025)",
                    "global_batch": dec.B, "seq_len": int(dec.lengths.max()), "parallelism": "none (1 GPU)"},
         "decode": {"ms_per_iteration": round(dec_ms, 4), "tokens_per_s": round(dec.B / (dec_ms * 1e-3), 1),
-                   "attn_hbm_gbs": round(attn_gbs, 1), "attn_frac_hbm_peak": round(attn_gbs / HBM_PEAK_GBS, 4)},
+                   "attn_hbm_gbs": round(attn_gbs, 1), "attn_frac_hbm_peak": round(attn_gbs / HBM_PEAK_GBS, 4),
+                   "projections_weight_gbs": round(w_bytes / (dec_gemm_ms * 1e-3) / 1e9, 1) if dec_gemm_ms else None,
+                   "embed_gbs": round(dec_embed_bytes / (dec_embed_ms * 1e-3) / 1e9, 1) if dec_embed_ms else None},
         "maskgit": {"ms_per_pass": round(mg_ms, 4),
                     "frames_per_s": round(mg.e["n_frames"] / (mg_ms * 1e-3 * mg.e["n_steps"]), 1),
                     "mfma_tflops": round(mfma_tflops, 1),
-                    "mfma_util": round(mfma_tflops / BF16_PEAK_TFLOPS, 4)},
+                    "mfma_util": round(mfma_tflops / BF16_PEAK_TFLOPS, 4),
+                    "kernels": mg_kernels,
+                    "embed_gbs": round(mg_embed_bytes / (mg_embed_ms * 1e-3) / 1e9, 1) if mg_embed_ms else None},
         "maskgit_cfg": {"ms_per_pass": round(cfg_ms, 4),
                         "frames_per_s": round(mg.e["n_frames"] / (cfg_ms * 1e-3 * mg.e["n_steps"]), 1),
                         "note": "guided step: conditional 950-token prompt + unconditional 750-frame window, "
