@@ -15,7 +15,10 @@
 // heads of the GQA group from those registers.  Scores reduce over the lanes sharing a
 // token with xor-shuffles; each lane keeps an online-softmax state (max, sum, 8 or 4
 // output dims) in base-2 units; lanes of a chunk merge by shuffles; chunks merge in a
-// fixed order in the combine kernel (deterministic, no atomics).
+// fixed order in the combine kernel (deterministic, no atomics).  The items come from a
+// work list built once per step on the device (decode_plan_kernel): only chunks that hold
+// positions, each with its page ids, and for q_len = 1 decode a chunk size chosen so that
+// the items fill two workgroups per CU.
 #include <hip/hip_ext.h>
 #include <math.h>
 
