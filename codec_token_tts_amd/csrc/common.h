@@ -107,6 +107,15 @@ __device__ __forceinline__ float block_sum_256(float v, float *red) {
     return t;
 }
 
+// Fragment-major layout of a bf16 activation operand of at most 64 rows, as the skinny
+// decode GEMM loads it: for each 32-wide K step kc and 16-row tile rt (of mt tiles), one
+// contiguous 1 KB block whose 16-byte chunk l holds row rt * 16 + l % 16, elements
+// kc * 32 + 8 (l / 16) .. +7.  A wave then reads each operand fragment as one contiguous
+// 1 KB load instead of 16 row segments.  Element index of (row r, column k):
+__device__ __forceinline__ int64_t frag_index(int r, int k, int mt) {
+    return ((int64_t)(k >> 5) * mt + (r >> 4)) * 512 + (((k >> 3) & 3) * 16 + (r & 15)) * 8 + (k & 7);
+}
+
 __device__ __forceinline__ void raise_flag(int *flag, int code) {
     if (flag) atomicOr(flag, code);
 }

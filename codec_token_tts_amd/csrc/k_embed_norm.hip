@@ -79,7 +79,7 @@ void launch_embed(const EmbedArgs &a, DType dt, hipStream_t s) {
 template <typename TO, int NP>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(float *x, int ldx, int hidden, const float *g, float eps,
                                                       TO *out, const float *pend, int64_t pend_ld,
-                                                      int64_t pend_stride) {
+                                                      int64_t pend_stride, int out_mt) {
     constexpr int MAXC = 4;  // float4 columns per thread held in registers (hidden <= 4096)
     __shared__ float red[4];
     const int r = blockIdx.x;
@@ -120,7 +120,8 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(float *x, int ldx, int hid
     for (int i = 0; i < MAXC; ++i) {
         const int c = threadIdx.x * 4 + i * 1024;
         if (c >= hidden) continue;
-        TO *o = out + (int64_t)r * hidden + c;
+        // fragment-major: the 4 columns c .. c + 3 stay contiguous (c % 4 == 0)
+        TO *o = out + (out_mt > 0 ? frag_index(r, c, out_mt) : (int64_t)r * hidden + c);
         o[0] = from_f32<TO>(v[i].x * inv * gg[i].x);
         o[1] = from_f32<TO>(v[i].y * inv * gg[i].y);
         o[2] = from_f32<TO>(v[i].z * inv * gg[i].z);
@@ -130,13 +131,14 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(float *x, int ldx, int hid
 
 template <typename TO>
 static void launch_rmsnorm_t(float *x, int ldx, int rows, int hidden, const float *gain, float eps, TO *out,
-                             hipStream_t s, const float *pend, int n_pend, int64_t pend_ld, int64_t pend_stride) {
+                             hipStream_t s, const float *pend, int n_pend, int64_t pend_ld, int64_t pend_stride,
+                             int out_mt) {
     const dim3 grid(rows), block(256);
     switch (n_pend) {
 #define TTSBB_NORM_CASE(NP)                                                                                    \
     case NP:                                                                                                   \
         hipLaunchKernelGGL((rmsnorm_kernel<TO, NP>), grid, block, 0, s, x, ldx, hidden, gain, eps, out, pend, \
-                           pend_ld, pend_stride);                                                              \
+                           pend_ld, pend_stride, out_mt);                                                      \
         break;
         TTSBB_NORM_CASE(0)
         TTSBB_NORM_CASE(1)
@@ -154,14 +156,14 @@ static void launch_rmsnorm_t(float *x, int ldx, int rows, int hidden, const floa
 // n_pend <= 8 partial buffers, hidden <= 4096 and a multiple of 4 (checked by the caller)
 void launch_rmsnorm(float *x, int ldx, int rows, int hidden, const float *gain, float eps, void *out,
                     DType out_dt, hipStream_t s, const float *pend, int n_pend, int64_t pend_ld,
-                    int64_t pend_stride) {
+                    int64_t pend_stride, int out_mt) {
     if (rows <= 0) return;
     if (out_dt == DT_BF16)
         launch_rmsnorm_t(x, ldx, rows, hidden, gain, eps, reinterpret_cast<bf16_t *>(out), s, pend, n_pend, pend_ld,
-                         pend_stride);
+                         pend_stride, out_mt);
     else
         launch_rmsnorm_t(x, ldx, rows, hidden, gain, eps, reinterpret_cast<float *>(out), s, pend, n_pend, pend_ld,
-                         pend_stride);
+                         pend_stride, 0);
 }
 
 __global__ void increment_kernel(int32_t *v, int n, int delta) {

@@ -654,11 +654,22 @@ __global__ __launch_bounds__(256) void gemm_skinny(GemmArgs g, float *part, int 
         for (int s = 0; s < STEPS; ++s) wv[nt][s] = *reinterpret_cast<const u32x4_t *>(wp + s * 32);
     }
     u32x4_t av[MT][STEPS];
+    if (g.a_mt > 0) {
+        // fragment-major A (a_mt == MT): fragment (k step kc, tile mt) is one contiguous 1 KB;
+        // rows past M hold anything (their results are never stored)
+        const int kc0 = (ks * 4 + wave) * STEPS;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        const bf16_t *ap = A + (int64_t)min(mt * 16 + fr, g.M - 1) * g.lda + k0;  // rows past M: unstored
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int s = 0; s < STEPS; ++s) av[mt][s] = *reinterpret_cast<const u32x4_t *>(ap + s * 32);
+            for (int s = 0; s < STEPS; ++s)
+                av[mt][s] = *reinterpret_cast<const u32x4_t *>(A + ((int64_t)(kc0 + s) * MT + mt) * 512 + lane * 8);
+    } else {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const bf16_t *ap = A + (int64_t)min(mt * 16 + fr, g.M - 1) * g.lda + k0;  // rows past M: unstored
+#pragma unroll
+            for (int s = 0; s < STEPS; ++s) av[mt][s] = *reinterpret_cast<const u32x4_t *>(ap + s * 32);
+        }
     }
     // keep every load ahead of the products: all of them in flight at once
     __builtin_amdgcn_sched_barrier(0);
@@ -716,8 +727,9 @@ __global__ __launch_bounds__(256) void gemm_skinny(GemmArgs g, float *part, int 
         const int row = mt * 16 + 4 * (l >> 4) + r;
         if (row >= g.M) continue;
         if (EPI == EPI_SWIGLU) {
+            const int oc = slice * 16 + (l & 15);  // output column (the next product's K index)
             if (col < g.N)
-                reinterpret_cast<bf16_t *>(g.C)[(int64_t)row * g.ldc + slice * 16 + (l & 15)] =
+                reinterpret_cast<bf16_t *>(g.C)[g.c_mt > 0 ? frag_index(row, oc, g.c_mt) : (int64_t)row * g.ldc + oc] =
                     f32_to_bf16(silu_f(v[0][mt]) * v[NT - 1][mt]);
         } else if (col < g.N) {
             float *p = reinterpret_cast<float *>(g.C) + (int64_t)row * g.ldc + col;
@@ -763,6 +775,14 @@ static int skinny_plan(const GemmArgs &g, int64_t part_cap, int &slices, int &st
     if (n_split == 0) return -1;
     if (n_split > 1 && (int64_t)n_split * g.M * g.N > part_cap) return -1;
     return n_split;
+}
+
+int skinny_tiles(const GemmArgs &g, int64_t part_cap) {
+    if (g.M <= 8 || g.M > 64) return 0;  // M <= 8: the GEMV
+    int slices, steps;
+    if (skinny_plan(g, part_cap, slices, steps) < 0) return 0;
+    const int mt = (g.M + 15) / 16;
+    return mt <= 2 ? mt : 4;
 }
 
 static int launch_skinny(const GemmArgs &g, float *part, int64_t part_cap, hipStream_t s) {

@@ -635,7 +635,8 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeAttnArgs a) {
     for (int e = 0; e < 4; ++e) acc[e] += __shfl_xor(acc[e], 32, WAVE);
     const float inv = 1.0f / lsum;
     if (lane < 32) {
-        TO *out = reinterpret_cast<TO *>(a.out) + (int64_t)b * a.H * 128 + h * 128 + lane * 4;
+        const int k = h * 128 + lane * 4;  // fragment-major: 4 contiguous columns either way
+        TO *out = reinterpret_cast<TO *>(a.out) + (a.out_mt > 0 ? frag_index(b, k, a.out_mt) : (int64_t)b * a.H * 128 + k);
 #pragma unroll
         for (int e = 0; e < 4; ++e) out[e] = from_f32<TO>(acc[e] * inv);
     }

@@ -36,9 +36,10 @@ void launch_embed(const EmbedArgs &a, DType dt, hipStream_t s);
 // x[r] + pend[0][r] + ... + pend[n_pend-1][r] (summed in that order; pend rows are
 // pend_ld floats apart, splits pend_stride apart) and is written back.  gain == nullptr
 // applies the update only (out unused).
+// out_mt > 0: out (bf16) in the fragment-major layout with out_mt 16-row tiles
 void launch_rmsnorm(float *x, int ldx, int rows, int hidden, const float *gain, float eps,
                     void *out, DType out_dt, hipStream_t s, const float *pend = nullptr, int n_pend = 0,
-                    int64_t pend_ld = 0, int64_t pend_stride = 0);
+                    int64_t pend_ld = 0, int64_t pend_stride = 0, int out_mt = 0);
 
 // ---- K3: projections  Y[M][N] = A[M][K] * W[N][K]^T with an epilogue --------------
 enum Epi { EPI_STORE = 0, EPI_ADD = 1, EPI_SWIGLU = 2 };
@@ -63,12 +64,19 @@ struct GemmArgs {
     const float *nx;
     const float *ng;
     float neps;
+    // Skinny path only (8 < M <= 64, bf16): A (a_mt > 0) and, for EPI_SWIGLU, C (c_mt > 0)
+    // are in the fragment-major layout of frag_index() with that many 16-row tiles (the
+    // kernel's own: 1, 2 or 4) instead of row-major
+    int a_mt, c_mt;
 };
 // part: fp32 workspace of part_cap floats for split-K partial sums.  Returns the number
 // of K splits whose partial sums are left in part[z][M][N] for the caller to add (an
 // EPI_ADD product on the skinny path defers its residual update to the next RMSNorm,
 // which sums them in split order); 0 when C holds the result.
 int launch_gemm(const GemmArgs &g, DType dt, float *part, int64_t part_cap, hipStream_t s);
+// 16-row tiles (1, 2 or 4) of the skinny kernel that a bf16 product of this shape runs on,
+// or 0 when it runs elsewhere (the fragment-major layout is only for that kernel)
+int skinny_tiles(const GemmArgs &g, int64_t part_cap);
 
 // ---- K4: per-head RMSNorm + RoPE + K/V write --------------------------------------
 // qkv fp32 [M][(H + 2 Hkv) * 128].  Decode mode (dense == 0): row m is stream m at
@@ -121,7 +129,8 @@ struct DecodeAttnArgs {
     int plan_cap;
     int target_items;
     float *part;          // [B][H][part_stride][132]: m, l, pad, pad, acc[128]
-    void *out;            // [B][H*128] operand dtype
+    void *out;            // [B][H*128] operand dtype (out_mt > 0: bf16, fragment-major)
+    int out_mt;
     float scale_log2;     // log2(e) / sqrt(128)
     int shared;           // prefill of one stream: query b is at position pos[0] + b and
                           // every query reads page-table row 0 (causal by construction)

@@ -244,11 +244,12 @@ TTSBB_API ttsbb_status ttsbb_create(const ttsbb_config *cfg, const ttsbb_layer *
     c->s_pad_cap = round_up(g.max_rows, 64);
     c->rank_cap = g.max_rows * (g.max_head_cols / 2 + 1);
     c->gpart_cap = (int64_t)16 << 20;  // 64 MB of split-K partials
-    bool ok = dev_alloc(c, &c->h, R * g.hidden * c->esz) &&
+    const size_t RA = R < 64 ? 64 : R;  // activation rows: a fragment-major layout spans 4 x 16
+    bool ok = dev_alloc(c, &c->h, RA * g.hidden * c->esz) &&
               dev_alloc(c, (void **)&c->qkv, R * c->qkv_w * 4) &&
               dev_alloc(c, &c->q, R * hd_all * 4) &&
-              dev_alloc(c, &c->attn, R * hd_all * c->esz) &&
-              dev_alloc(c, &c->mlp, R * g.ffn * c->esz) &&
+              dev_alloc(c, &c->attn, RA * hd_all * c->esz) &&
+              dev_alloc(c, &c->mlp, RA * g.ffn * c->esz) &&
               dev_alloc(c, (void **)&c->x, R * g.hidden * 4) &&
               dev_alloc(c, (void **)&c->kbuf, (size_t)g.n_kv_heads * c->s_pad_cap * g.head_dim * 2) &&
               dev_alloc(c, (void **)&c->vtbuf, (size_t)g.n_kv_heads * c->s_pad_cap * g.head_dim * 2) &&
@@ -351,15 +352,52 @@ namespace {
 // modes.  x is the fp32 residual stream [M][hidden].
 // RMSNorm of rows [0, M) of the residual stream x into c->h, first applying a residual
 // update that a split projection left in gpart (gain == nullptr: the update only).
-void norm_rows(ttsbb_ctx *c, float *x, int M, const float *gain) {
+// out_mt > 0: c->h in the fragment-major layout of the skinny products (out_mt tiles).
+void norm_rows(ttsbb_ctx *c, float *x, int M, const float *gain, int out_mt = 0) {
     const ttsbb_config &g = c->cfg;
     const int np = c->pend_rows == M ? c->pend_splits : 0;  // rows always match by construction
     if (gain || np > 0) {
         KScope k(c, TTSBB_K_RMSNORM);
         launch_rmsnorm(x, g.hidden, M, g.hidden, gain, g.rms_eps, c->h, c->dt, c->stream, c->gpart, np, g.hidden,
-                       (int64_t)M * g.hidden);
+                       (int64_t)M * g.hidden, out_mt);
     }
     c->pend_splits = 0;
+}
+
+// Activation layout of a decode layer's four products over M rows: the skinny kernel's
+// fragment-major layout (its 16-row tiles; every operand fragment one contiguous 1 KB
+// load) when all four run on that kernel and nothing taps the operands, else 0
+// (row-major).  The producers (RMSNorm, chunk merge, SwiGLU epilogue) write it.
+int layer_pack_mt(const ttsbb_ctx *c, int M, bool tapit) {
+    const ttsbb_config &g = c->cfg;
+    if (tapit || c->dt != DT_BF16) return 0;
+    const int shapes[4][3] = {{g.hidden, c->qkv_w, EPI_STORE},
+                              {g.n_heads * g.head_dim, g.hidden, EPI_ADD},
+                              {g.hidden, 2 * g.ffn, EPI_SWIGLU},
+                              {g.ffn, g.hidden, EPI_ADD}};
+    int mt = -1;
+    for (const auto &sh : shapes) {
+        GemmArgs a = {};
+        a.M = M;
+        a.K = sh[0];
+        a.N = sh[1];
+        a.epi = sh[2];
+        const int t = skinny_tiles(a, c->gpart_cap);
+        if (t == 0 || (mt >= 0 && t != mt)) return 0;
+        mt = t;
+    }
+    return mt;
+}
+
+// The same for the head product (K = hidden, N columns).
+int head_pack_mt(const ttsbb_ctx *c, int M, int N, bool tapped) {
+    if (tapped || c->dt != DT_BF16) return 0;
+    GemmArgs a = {};
+    a.M = M;
+    a.K = c->cfg.hidden;
+    a.N = N;
+    a.epi = EPI_STORE;
+    return skinny_tiles(a, c->gpart_cap);
 }
 
 void flush_residual(ttsbb_ctx *c, float *x, int M) {
@@ -396,17 +434,18 @@ void add_projection(ttsbb_ctx *c, const GemmArgs &a) {
 // and the dense q / K / V^T layout are fused into the product when the shape allows;
 // returns true when that happened (qkv is then not written).
 bool qkv_projection(ttsbb_ctx *c, const ttsbb_layer &L, float *x, int M, bool tapit,
-                    const RopeKvArgs *dense = nullptr) {
+                    const RopeKvArgs *dense = nullptr, int pack_mt = 0) {
     const ttsbb_config &g = c->cfg;
     if (tapit) {
         flush_residual(c, x, M);
         tap_dense(c, TTSBB_TAP_X_IN, x, DT_F32, M, g.hidden, g.hidden);
     }
     const bool fold = !dense && norm_folds(c, M, tapit);
-    if (!fold) norm_rows(c, x, M, L.attn_norm);
+    if (!fold) norm_rows(c, x, M, L.attn_norm, pack_mt);
     GemmArgs a = {};
     if (fold) fold_norm(c, a, x, L.attn_norm);
     a.A = c->h;
+    a.a_mt = pack_mt;
     a.lda = g.hidden;
     a.M = M;
     a.K = g.hidden;
@@ -435,12 +474,16 @@ bool qkv_projection(ttsbb_ctx *c, const ttsbb_layer &L, float *x, int M, bool ta
     return fused;
 }
 
-void post_attention(ttsbb_ctx *c, const ttsbb_layer &L, float *x, int M, bool tapit) {
+// attn_mt / pack_mt: layouts of the attention output and of the layer's other
+// activations (0: row-major; see layer_pack_mt).
+void post_attention(ttsbb_ctx *c, const ttsbb_layer &L, float *x, int M, bool tapit, int attn_mt = 0,
+                    int pack_mt = 0) {
     const ttsbb_config &g = c->cfg;
     const int hd_all = g.n_heads * g.head_dim;
     if (tapit) tap_dense(c, TTSBB_TAP_ATTN, c->attn, c->dt, M, hd_all, hd_all);
     GemmArgs a = {};
     a.A = c->attn;
+    a.a_mt = attn_mt;
     a.lda = hd_all;
     a.M = M;
     a.K = hd_all;
@@ -461,11 +504,13 @@ void post_attention(ttsbb_ctx *c, const ttsbb_layer &L, float *x, int M, bool ta
         tap_dense(c, TTSBB_TAP_X_MID, x, DT_F32, M, g.hidden, g.hidden);
     }
     const bool fold = norm_folds(c, M, tapit);
-    if (!fold) norm_rows(c, x, M, L.ffn_norm);
+    if (!fold) norm_rows(c, x, M, L.ffn_norm, pack_mt);
     if (tapit) tap_dense(c, TTSBB_TAP_H_FFN, c->h, c->dt, M, g.hidden, g.hidden);
     GemmArgs u = {};
     if (fold) fold_norm(c, u, x, L.ffn_norm);
     u.A = c->h;
+    u.a_mt = pack_mt;
+    u.c_mt = pack_mt;
     u.lda = g.hidden;
     u.M = M;
     u.K = g.hidden;
@@ -484,6 +529,7 @@ void post_attention(ttsbb_ctx *c, const ttsbb_layer &L, float *x, int M, bool ta
 
     GemmArgs d = {};
     d.A = c->mlp;
+    d.a_mt = pack_mt;
     d.lda = g.ffn;
     d.M = M;
     d.K = g.ffn;
@@ -508,11 +554,12 @@ void post_attention(ttsbb_ctx *c, const ttsbb_layer &L, float *x, int M, bool ta
 // Head product of rows [row0, row0 + M); with norm_x the final RMSNorm is folded into it
 // (norm_x = the residual rows, which must hold no pending split partials).
 void head_gemm(ttsbb_ctx *c, const void *head, int M, int N, float *out, int ldc, int row0 = 0,
-               const float *norm_x = nullptr) {
+               const float *norm_x = nullptr, int a_mt = 0) {
     const ttsbb_config &g = c->cfg;
     GemmArgs a = {};
     if (norm_x) fold_norm(c, a, norm_x + (size_t)row0 * g.hidden, c->final_norm);
     a.A = reinterpret_cast<const char *>(c->h) + (size_t)row0 * g.hidden * c->esz;
+    a.a_mt = a_mt;  // fragment-major only with row0 == 0
     a.lda = g.hidden;
     a.M = M;
     a.K = g.hidden;
@@ -746,7 +793,8 @@ static ttsbb_status paged_forward(ttsbb_ctx *ctx, int32_t batch, float *x, int32
     for (int l = 0; l < g.n_layers; ++l) {
         const ttsbb_layer &L = ctx->layers[l];
         const bool tapit = (l == ctx->tap_layer);
-        qkv_projection(ctx, L, x, batch, tapit);
+        const int pack_mt = layer_pack_mt(ctx, batch, tapit);
+        qkv_projection(ctx, L, x, batch, tapit, nullptr, pack_mt);
         void *pool_l = reinterpret_cast<char *>(kv_pool) + (size_t)l * layer_elems * ctx->esz;
 
         RopeKvArgs r = {};
@@ -782,6 +830,7 @@ static ttsbb_status paged_forward(ttsbb_ctx *ctx, int32_t batch, float *x, int32
         DecodeAttnArgs d = da;
         d.q = reinterpret_cast<const float *>(ctx->q);
         d.pool_layer = pool_l;
+        d.out_mt = pack_mt;  // the merge writes the o-projection's operand
         if (fused) {
             d.qkv = ctx->qkv;
             d.q_gain = L.q_norm;
@@ -800,7 +849,7 @@ static ttsbb_status paged_forward(ttsbb_ctx *ctx, int32_t batch, float *x, int32
             launch_decode_combine(d, ctx->dt, ctx->stream);
         }
 
-        post_attention(ctx, L, x, batch, tapit);
+        post_attention(ctx, L, x, batch, tapit, pack_mt, pack_mt);
     }
     if (!head) flush_residual(ctx, x, batch);
     if (head) {
@@ -808,11 +857,12 @@ static ttsbb_status paged_forward(ttsbb_ctx *ctx, int32_t batch, float *x, int32
         const int r0 = prefill ? batch - 1 : 0, rows = prefill ? 1 : batch;  // rows read out
         const bool tap_head = ctx->tap_layer >= 0;
         const bool fold = !tap_head && gemv_rows_fold(ctx, rows);
+        const int hmt = prefill ? 0 : head_pack_mt(ctx, rows, N, tap_head);
         if (fold) flush_residual(ctx, x, batch);
-        else norm_rows(ctx, x, batch, ctx->final_norm);
+        else norm_rows(ctx, x, batch, ctx->final_norm, hmt);
         if (tap_head) tap_dense(ctx, TTSBB_TAP_HEAD_IN, ctx->h, ctx->dt, batch, g.hidden, g.hidden);
         float *lg = logits ? logits : ctx->logits;
-        head_gemm(ctx, head, rows, N, lg, N, r0, fold ? x : nullptr);
+        head_gemm(ctx, head, rows, N, lg, N, r0, fold ? x : nullptr, hmt);
         if (ctx->tap_layer >= 0) tap_dense(ctx, TTSBB_TAP_LOGITS, lg, DT_F32, rows, N, N);
         {
             KScope k(ctx, TTSBB_K_ARGMAX);

@@ -296,6 +296,29 @@ def test_decode_bf16_ragged_with_head(lengths):
         m.close()
 
 
+@pytest.mark.parametrize("lengths", [[(29 * i) % 97 for i in range(9)], [(31 * i) % 160 for i in range(17)],
+                                     [(37 * i) % 211 for i in range(40)]])
+def test_decode_bf16_untapped_fragment_major(lengths):
+    """bf16, 2 layers and a head, nothing tapped: batches 9, 17 and 40 run every product
+    on the skinny kernel with its operands in the fragment-major layout (one, two, and
+    three 16-row tiles padded to four), written by the RMSNorm, the chunk merge and the
+    SwiGLU epilogue; outputs, logits and choices against the oracle."""
+    shape = CFG.Shape(n_layers=2)
+    m = Model(shape, 2, True, seed=5, gains="random")
+    try:
+        G, V = 3, 37
+        head_h = CFG.table(5, gen.KIND_HEAD, 0, G * V, shape.hidden, True)
+        head = (DEV.host_to_device(head_h), G, V, widen(head_h))
+        res, ref = run_decode(m, lengths, 5, head=head)
+        assert normwise(res["x"], ref["x"]) <= TOL_LAYER_BF16
+        assert normwise(res["logits"], ref["logits"]) <= TOL_LAYER_BF16
+        B = len(lengths)
+        check_argmax_groups(res["argmax"], res["logits"].reshape(B, G, V),
+                            ref["logits"].reshape(B, G, V))
+    finally:
+        m.close()
+
+
 # ---------------------------------------------------------------------------------------
 def run_maskgit(m: Model, n_text, n_frames, n_cb, V, mask_id, n_unmask, seed, tap_layer=None,
                 text_vocab=500, masked_frac=0.5):
