@@ -620,7 +620,7 @@ def main():
     ap.add_argument("--workload", default="c5c4", choices=["c5c4"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-streams", type=int, default=2)
-    ap.add_argument("--cpu-steps", type=int, default=24)
+    ap.add_argument("--cpu-steps", type=int, default=40)
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the graph-captured batch-1 loop (hardware-counter runs: the profiler's "
                          "per-dispatch counter collection does not support stream capture)")
