@@ -708,3 +708,61 @@ def test_prefill_from_empty_is_the_causal_full_pass():
     out2 = O.prefill(np.vstack([x[:4], rng.standard_normal((3, dims.hidden))]), 0, O.KVCache(2, 1), 0, layers,
                      dims)
     np.testing.assert_allclose(out2[:4], out[:4], rtol=1e-10, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# The whole layer stack against an independent implementation of the same
+# architecture: the Qwen3 decoder of the `transformers` library (the pages name the
+# backbone Qwen3-0.6B), built at small sizes in float64 with the oracle's weights.
+# ---------------------------------------------------------------------------
+
+def _library_qwen3(dims, layers, final_gain):
+    torch = pytest.importorskip("torch")
+    tf = pytest.importorskip("transformers")
+    cfg = tf.Qwen3Config(vocab_size=8, hidden_size=dims.hidden, intermediate_size=dims.ffn,
+                         num_hidden_layers=len(layers), num_attention_heads=dims.n_heads,
+                         num_key_value_heads=dims.n_kv_heads, head_dim=dims.head_dim,
+                         rms_norm_eps=dims.eps, rope_theta=dims.theta, max_position_embeddings=64,
+                         attention_bias=False, attn_implementation="eager")
+    m = tf.Qwen3Model(cfg).double().eval()
+
+    def t(a):
+        return torch.from_numpy(np.ascontiguousarray(a))
+
+    with torch.no_grad():
+        for L, hl in zip(layers, m.layers):
+            at = hl.self_attn
+            for mod, w in ((at.q_proj, L.wq), (at.k_proj, L.wk), (at.v_proj, L.wv), (at.o_proj, L.wo),
+                           (at.q_norm, L.q_norm), (at.k_norm, L.k_norm), (hl.input_layernorm, L.attn_norm),
+                           (hl.post_attention_layernorm, L.ffn_norm), (hl.mlp.gate_proj, L.w_gate),
+                           (hl.mlp.up_proj, L.w_up), (hl.mlp.down_proj, L.w_down)):
+                mod.weight.copy_(t(w))
+        m.norm.weight.copy_(t(final_gain))
+
+    def run(x, causal):
+        kw = {} if causal else {"attention_mask": torch.zeros(1, 1, x.shape[0], x.shape[0], dtype=torch.float64)}
+        with torch.no_grad():
+            return m(inputs_embeds=t(x)[None], **kw).last_hidden_state[0].numpy()
+    return run
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_layer_stack_matches_library_qwen3(causal):
+    rng = np.random.default_rng(77)
+    dims = small_dims()
+    layers = [rand_layer(dims, rng) for _ in range(3)]
+    g = 1.0 + 0.1 * rng.standard_normal(dims.hidden)
+    run = _library_qwen3(dims, layers, g)
+    x = rng.standard_normal((11, dims.hidden))
+    ref = O.rms_norm(O.backbone_full(x, layers, dims, causal=causal), g, dims.eps)
+    # the library rounds to float32 inside every RMSNorm (it upcasts its input to float32
+    # whatever the dtype) and takes the RoPE angles in float32; everything else runs in
+    # float64.  Observed ~3e-7 of max |y|; a structural mistake (a dropped term, a wrong
+    # sign, index or operand order) gives errors of order one.
+    err = np.abs(run(x, causal) - ref).max() / np.abs(ref).max()
+    assert err < 3e-6, err
+    # position 0 alone (RoPE is the identity there) and two positions
+    for n in (1, 2):
+        ref_n = O.rms_norm(O.backbone_full(x[:n], layers, dims, causal=causal), g, dims.eps)
+        err = np.abs(run(x[:n], causal) - ref_n).max() / np.abs(ref_n).max()
+        assert err < 3e-6, (n, err)
