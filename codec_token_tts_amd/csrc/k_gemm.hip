@@ -334,8 +334,8 @@ __device__ __forceinline__ void lds_frags(const bf16_t *sa, const bf16_t *sb, in
 // Fused epilogue of the full-sequence q/k/v projection (one 128 x 128 tile = 128
 // tokens x one head of the qkv output; block of 4 waves in 2 x 2, wave tile 64 x 64).
 // The fp32 tile goes through LDS in two halves of 64 tokens (row stride 132 floats);
-// for a q or k head each token's 128 values get the per-head RMSNorm (four threads per
-// token, 16 RoPE pairs each, sum of squares over the quad) and the half-rotate RoPE at
+// for a q or k head each token's 128 values get the per-head RMSNorm (eight threads per
+// token, 8 RoPE pairs each, sum of squares over the eight) and the half-rotate RoPE at
 // position = token index (minus seg1 in a second sequence), then go out as bf16 q
 // [S][H*128] or K [Hkv][s_pad][128];
 // a v head goes out transposed, V^T [Hkv][128][s_pad], 8 tokens per 16-byte store.
@@ -349,26 +349,30 @@ __device__ __forceinline__ void qkv_dense_epilogue(const f32x16_t (&acc)[TM][TN]
     const int head = n0 / 128;
     const bool is_v = head >= rk.H + rk.Hkv;
     const bool is_q = head < rk.H;
-    // q / k heads: the gains and both halves' RoPE entries of this thread's token and
-    // dims are requested before the tile goes through LDS (their latency overlaps it)
-    const int q4 = tid & 3;
-    float2 csr[2][16];
-    float glo[16], ghi[16];
+    // q / k heads: the gains and every RoPE entry of this thread's tokens and dims are
+    // requested before the tile goes through LDS (their latency overlaps it).  Eight
+    // threads per token, each with dims q8*8 .. +7 and their RoPE partners 64 + q8*8 ..,
+    // so that eight consecutive lanes store one whole 128-byte line of each half.
+    const int q8 = tid & 7;
+    float2 csr[2][2][8];
+    float glo[8], ghi[8];
     if (!is_v) {
         const float *gain = is_q ? rk.q_gain : rk.k_gain;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            glo[e] = gain[q4 * 16 + e];
-            ghi[e] = gain[q4 * 16 + 64 + e];
+        for (int e = 0; e < 8; ++e) {
+            glo[e] = gain[q8 * 8 + e];
+            ghi[e] = gain[q8 * 8 + 64 + e];
         }
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-            const int m = m0 + hf * 64 + (tid >> 2);
-            const int pos = rk.seg1 > 0 && m >= rk.seg1 ? m - rk.seg1 : m;  // second sequence
-            const float2 *cs = rk.rope + (int64_t)min(pos, rk.max_pos - 1) * 64 + q4 * 16;
+        for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) csr[hf][e] = cs[e];
-        }
+            for (int ps = 0; ps < 2; ++ps) {
+                const int m = m0 + hf * 64 + ps * 32 + (tid >> 3);
+                const int pos = rk.seg1 > 0 && m >= rk.seg1 ? m - rk.seg1 : m;  // second sequence
+                const float2 *cs = rk.rope + (int64_t)min(pos, rk.max_pos - 1) * 64 + q8 * 8;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) csr[hf][ps][e] = cs[e];
+            }
     }
     // LDS-only barriers: __syncthreads() would also wait for the table loads above
     auto lds_barrier = []() {
@@ -391,41 +395,40 @@ __device__ __forceinline__ void qkv_dense_epilogue(const f32x16_t (&acc)[TM][TN]
         lds_barrier();
         const int t0 = m0 + half * 64;
         if (!is_v) {
-            const int row = tid >> 2, m = t0 + row;
-            const float *x = tile + row * LDT + q4 * 16;
-            float lo[16], hi[16];
-            float ss = 0.f;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                lo[e] = x[e];
-                hi[e] = x[64 + e];
-                ss += lo[e] * lo[e] + hi[e] * hi[e];
-            }
-            ss = group_sum<4>(ss);
-            const float inv = 1.0f / sqrtf(ss / 128.0f + rk.eps);
-            uint32_t wlo[8], whi[8];
+            for (int ps = 0; ps < 2; ++ps) {
+                const int row = ps * 32 + (tid >> 3), m = t0 + row;
+                const float *x = tile + row * LDT + q8 * 8;
+                float lo[8], hi[8];
+                float ss = 0.f;
 #pragma unroll
-            for (int e = 0; e < 16; e += 2) {
-                float o[2][2];
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    const float x0 = lo[e + u] * inv * glo[e + u], x1 = hi[e + u] * inv * ghi[e + u];
-                    const float2 c = csr[half][e + u];
-                    o[0][u] = x0 * c.x - x1 * c.y;
-                    o[1][u] = x1 * c.x + x0 * c.y;
+                for (int e = 0; e < 8; ++e) {
+                    lo[e] = x[e];
+                    hi[e] = x[64 + e];
+                    ss += lo[e] * lo[e] + hi[e] * hi[e];
                 }
-                wlo[e / 2] = (uint32_t)f32_to_bf16(o[0][0]) | ((uint32_t)f32_to_bf16(o[0][1]) << 16);
-                whi[e / 2] = (uint32_t)f32_to_bf16(o[1][0]) | ((uint32_t)f32_to_bf16(o[1][1]) << 16);
-            }
-            if (m < M) {
-                bf16_t *dst = is_q ? reinterpret_cast<bf16_t *>(rk.q_out) + ((int64_t)m * rk.H + head) * 128
-                                   : rk.kbuf + ((int64_t)(head - rk.H) * rk.s_pad + m) * 128;
-                u32x4_t *d0 = reinterpret_cast<u32x4_t *>(dst + q4 * 16);
-                u32x4_t *d1 = reinterpret_cast<u32x4_t *>(dst + 64 + q4 * 16);
-                d0[0] = u32x4_t{wlo[0], wlo[1], wlo[2], wlo[3]};
-                d0[1] = u32x4_t{wlo[4], wlo[5], wlo[6], wlo[7]};
-                d1[0] = u32x4_t{whi[0], whi[1], whi[2], whi[3]};
-                d1[1] = u32x4_t{whi[4], whi[5], whi[6], whi[7]};
+                ss = group_sum<8>(ss);
+                const float inv = 1.0f / sqrtf(ss / 128.0f + rk.eps);
+                uint32_t wlo[4], whi[4];
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    float o[2][2];
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        const float x0 = lo[e + u] * inv * glo[e + u], x1 = hi[e + u] * inv * ghi[e + u];
+                        const float2 c = csr[half][ps][e + u];
+                        o[0][u] = x0 * c.x - x1 * c.y;
+                        o[1][u] = x1 * c.x + x0 * c.y;
+                    }
+                    wlo[e / 2] = (uint32_t)f32_to_bf16(o[0][0]) | ((uint32_t)f32_to_bf16(o[0][1]) << 16);
+                    whi[e / 2] = (uint32_t)f32_to_bf16(o[1][0]) | ((uint32_t)f32_to_bf16(o[1][1]) << 16);
+                }
+                if (m < M) {
+                    bf16_t *dst = is_q ? reinterpret_cast<bf16_t *>(rk.q_out) + ((int64_t)m * rk.H + head) * 128
+                                       : rk.kbuf + ((int64_t)(head - rk.H) * rk.s_pad + m) * 128;
+                    *reinterpret_cast<u32x4_t *>(dst + q8 * 8) = u32x4_t{wlo[0], wlo[1], wlo[2], wlo[3]};
+                    *reinterpret_cast<u32x4_t *>(dst + 64 + q8 * 8) = u32x4_t{whi[0], whi[1], whi[2], whi[3]};
+                }
             }
         } else {
             bf16_t *vt = rk.vtbuf + (int64_t)(head - rk.H - rk.Hkv) * 128 * rk.s_pad;
