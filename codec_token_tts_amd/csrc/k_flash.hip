@@ -242,18 +242,27 @@ __global__ __launch_bounds__(512) void flash_kernel(FlashArgs a) {
 
     l_run += __shfl_xor(l_run, 32, WAVE);
     const float inv = 1.0f / l_run;
-    const int qi = q0 + fq;
-    if (qi < a.S) {
-        bf16_t *out = a.out + (int64_t)qi * ldq + head * 128 + h * 4;
+    // O goes out through LDS, past the hand-over area, each wave in rows of its own (row
+    // stride 272 bytes: 8-byte writes of 32 queries spread over the banks); read back, 16
+    // consecutive lanes then store one query's whole 256-byte row of O (before: each
+    // store touched 32 rows)
+    constexpr int OST = 272;
+    static_assert(3 * EXS * 4 + 2 * 32 * OST <= 8 * (KTILE + VTILE) * 2, "O staging fits");
+    unsigned char *stg = reinterpret_cast<unsigned char *>(smem) + 3 * EXS * 4 + u * 32 * OST;
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
+    for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                uint2 w;
-                w.x = (uint32_t)f32_to_bf16(o[dt][4 * j] * inv) | ((uint32_t)f32_to_bf16(o[dt][4 * j + 1] * inv) << 16);
-                w.y = (uint32_t)f32_to_bf16(o[dt][4 * j + 2] * inv) | ((uint32_t)f32_to_bf16(o[dt][4 * j + 3] * inv) << 16);
-                *reinterpret_cast<uint2 *>(out + dt * 32 + j * 8) = w;
-            }
+        for (int j = 0; j < 4; ++j) {
+            uint2 w;
+            w.x = (uint32_t)f32_to_bf16(o[dt][4 * j] * inv) | ((uint32_t)f32_to_bf16(o[dt][4 * j + 1] * inv) << 16);
+            w.y = (uint32_t)f32_to_bf16(o[dt][4 * j + 2] * inv) | ((uint32_t)f32_to_bf16(o[dt][4 * j + 3] * inv) << 16);
+            *reinterpret_cast<uint2 *>(stg + fq * OST + (dt * 32 + j * 8 + h * 4) * 2) = w;
+        }
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+        const int row = it * 4 + (lane >> 4), c16 = lane & 15, qi = q0 + row;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t *>(stg + row * OST + c16 * 16);
+        if (qi < a.S) *reinterpret_cast<u32x4_t *>(a.out + (int64_t)qi * ldq + head * 128 + c16 * 8) = v;
     }
 }
 
