@@ -541,22 +541,32 @@ __global__ __launch_bounds__(256) void gemm_lds(GemmArgs g, int k_split, RopeKvA
         return;
     }
     const int rb0 = m0 + wm * WM + (lane >> 5) * 4, cb0 = n0 + wn * WN + (lane & 31);
-    if (EPI == EPI_SWIGLU) {
-        bf16_t *C = reinterpret_cast<bf16_t *>(g.C);
+    if constexpr (EPI == EPI_SWIGLU) {
+        // the BM x BN/2 bf16 tile of m goes through the (now idle) ring buffer, row stride
+        // BN/2 + 8 elements, so that eight consecutive lanes store one whole 128-byte line
+        constexpr int OW = BN / 2, LDO = OW + 8;
+        static_assert(BM * LDO <= STAGES * TILE && (BM * OW / 8) % 256 == 0, "m tile staging");
+        __syncthreads();  // every wave's last fragment reads are done
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
             for (int j = 0; j < TN; j += 2) {
-                const int ncol = n0 + wn * WN + j * 32;  // first logical column of the gate tile
-                if (ncol >= g.N) continue;
-                const int ocol = (ncol >> 6) * 32 + (lane & 31);
+                const int ocol = (wn * WN + j * 32) / 2 + (lane & 31);
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int row = rb0 + i * 32 + (r >> 2) * 8 + (r & 3);
-                    if (row < g.M)
-                        C[(int64_t)row * g.ldc + ocol] = f32_to_bf16(silu_f(acc[i][j][r]) * acc[i][j + 1][r]);
+                    const int row = wm * WM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                    smem[row * LDO + ocol] = f32_to_bf16(silu_f(acc[i][j][r]) * acc[i][j + 1][r]);
                 }
             }
+        __syncthreads();
+        bf16_t *C = reinterpret_cast<bf16_t *>(g.C);
+#pragma unroll
+        for (int it = 0; it < BM * OW / 8 / 256; ++it) {
+            const int idx = it * 256 + tid, row = idx / (OW / 8), c8 = (idx % (OW / 8)) * 8;
+            const u32x4_t v = *reinterpret_cast<const u32x4_t *>(smem + row * LDO + c8);
+            if (m0 + row < g.M && n0 / 2 + c8 < g.N / 2)
+                *reinterpret_cast<u32x4_t *>(C + (int64_t)(m0 + row) * g.ldc + n0 / 2 + c8) = v;
+        }
     } else {
         float *C = reinterpret_cast<float *>(g.C);
         int64_t ldc = g.ldc;
