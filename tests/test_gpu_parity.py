@@ -418,6 +418,23 @@ def test_maskgit_two_layers(n_text, n_frames, n_unmask):
         m.close()
 
 
+
+@pytest.mark.parametrize("n_text,n_frames", [(20, 130), (5, 60)])
+def test_maskgit_without_gqa(n_text, n_frames):
+    """bf16, one bidirectional layer with as many KV heads as query heads: the attention
+    kernel's one-head-per-group form (the two waves of a key quarter take two query tiles
+    of one head), and the fused q|k|v epilogue with 8 + 8 + 8 heads."""
+    m = Model(CFG.Shape(n_layers=1, n_heads=8, n_kv_heads=8), 1, True, seed=11, gains="random")
+    try:
+        n_cb, V, mask, n_unmask = 3, 33, 32, 40
+        res, ref = run_maskgit(m, n_text, n_frames, n_cb, V, mask, n_unmask, 6, tap_layer=0)
+        check_maskgit(res, ref, n_cb, n_frames, V, mask, n_unmask)
+        S = n_text + n_frames
+        for k in ("q", "k", "v", "o", "x1", "m", "x2"):
+            assert normwise(res["taps"][k], ref["lrec"][k].reshape(S, -1)) <= TOL_LAYER_BF16, k
+    finally:
+        m.close()
+
 def test_maskgit_deterministic():
     m = Model(CFG.Shape(n_layers=1), 1, True, seed=9)
     try:
