@@ -600,6 +600,46 @@ def test_sampler_reduces_to_greedy_scoring():
     assert np.array_equal(np.isfinite(c3), fin)
 
 
+def test_sampler_tempered_score_hand_example():
+    """A worked case of the sampler's order of operations (OmniVoice ARCHITECTURE, "MaskGIT
+    decoder": log-softmax over all classes, mask class to -inf, keep the top-k ratio,
+    divide by the class temperature, add Gumbel noise, score = max - layer index *
+    penalty, plus position noise), with values chosen so that each plausible mistake
+    changes the answer.  Logits ln[4, 2, 1, 1, 8] (class 4 = mask): the normaliser is 16
+    (mask included), so lp = ln[1/4, 1/8, 1/16, 1/16] on the non-mask classes.
+    Uniforms are u = exp(-exp(-G)), i.e. Gumbel values G chosen by hand."""
+    V, mask = 5, 4
+    ln2 = math.log(2.0)
+    row = np.log(np.array([4.0, 2.0, 1.0, 1.0, 8.0]))
+    lg = np.concatenate([row, row])[None, :]          # T = 1 frame, K = 2 codebooks
+    codes = np.full((2, 1), mask)
+
+    def u_of(G):
+        return np.exp(-np.exp(-np.asarray(G, np.float64)))
+
+    # codebook 0: G = [0, 0.5, 10, 0, 0]; codebook 1: no noise (G = 0)
+    u_c = np.stack([u_of([0.0, 0.5, 10.0, 0.0, 0.0]), u_of([0.0] * 5)])[:, None, :]
+    u_p = u_of([[1.0], [0.0]])
+    # ratio 0.4 keeps floor(2.0) = 2 classes {0, 1}: class 2 (G = 10) is filtered out.
+    # Tempered values (temperature 2): class 0: -ln2 + 0; class 1: -1.5 ln2 + 0.5 = -0.540
+    # -> class 1 wins (with unscaled log-probs class 0 would: -2 ln2 > -3 ln2 + 0.5).
+    pred, score, _ = O.sample_scores(lg, codes, 2, V, mask, 5.0, 2.0, 0.3, 0.4, u_c, u_p)
+    assert pred.tolist() == [[1], [0]]
+    assert abs(score[0, 0] - (-1.5 * ln2 + 0.5 + 0.3 * 1.0)) <= 1e-12       # k = 0, position G = 1
+    assert abs(score[1, 0] - (-1.0 * ln2 - 5.0)) <= 1e-12                   # k = 1: lp0 / 2 - 5
+    # no noise and ratio 1: the greedy choice, score = max lp / temperature - k * penalty
+    u0 = np.full((2, 1, V), math.exp(-1.0))
+    pred, score, _ = O.sample_scores(lg, codes, 2, V, mask, 5.0, 2.0, 0.0, 1.0, u0, None)
+    assert pred.tolist() == [[0], [0]]
+    np.testing.assert_allclose(score[:, 0], [-ln2, -ln2 - 5.0], rtol=0, atol=1e-12)
+    # ties at the threshold keep the lower class id: ratio 0.6 keeps {0, 1, 2} (classes 2
+    # and 3 tie at ln 1/16); class 3 carries G = 10 but is dropped, class 2 (G = 2) wins
+    u_t = np.stack([u_of([0.0, 0.0, 2.0, 10.0, 0.0]), u_of([0.0] * 5)])[:, None, :]
+    pred, score, _ = O.sample_scores(lg, codes, 2, V, mask, 5.0, 2.0, 0.0, 0.6, u_t, None)
+    assert pred[0, 0] == 2
+    assert abs(score[0, 0] - (-2.0 * ln2 + 2.0)) <= 1e-12
+
+
 def test_sampler_picks_inside_the_kept_classes():
     """With class noise the choice is always one of the top floor(ratio * V) non-mask
     classes, never the mask class."""

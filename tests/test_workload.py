@@ -32,12 +32,20 @@ def test_fast_path_equals_definition():
         assert w[i] == gen.words_range(3, 4, int(e), 1)[0]
 
 
-def test_normal_moments_and_bf16_exactness():
+def test_normal_moments_and_grid():
     x = gen.fast_normal(0, 1, (1 << 20,), 1.0)
     assert abs(x.mean()) < 5e-3 and abs(x.std() - 1.0) < 5e-3
-    assert np.all(np.abs(x) <= 191 / 64)
-    # k/64 with |k| < 256 is exact in bf16
-    assert np.array_equal(gen.round_bf16(x), x)
+    assert np.all(np.abs(x) <= 1535 / 512)
+    # unit-variance values sit on the k/512 grid exactly (fp32 product by a power of two)
+    k = x.astype(np.float64) * 512
+    assert np.array_equal(k, np.round(k))
+    # most of them need more than bf16's 8 significant bits: an fp32-mode input rounded
+    # to bf16 anywhere on the way would change
+    assert np.mean(gen.round_bf16(x) != x) > 0.4
+    # the integer variate itself: exact mean 0 and variance 2^18 over all 2^32 words
+    # follow from the uniform parts; check the extremes and a few words by hand
+    assert gen.normal_k(np.array([0, 0xFFFFFFFF], np.uint32)).tolist() == [-1535, 1535]
+    assert gen.normal_k(np.array([1 | (2 << 10) | (3 << 20) | (1 << 30)], np.uint32)).tolist() == [1 + 2 + 3 + 1 - 1535]
 
 
 def test_bf16_round_to_nearest_even():

@@ -1,7 +1,7 @@
 // Device side of the seeded input generator in workload/gen.py (same definition, bit for
 // bit): element e of stream s under seed is word e % 4 of Philox4x32-10 with counter
 // (e/4 lo, e/4 hi, s, 0) and key (seed lo, seed hi); a normal variate is the integer
-// Irwin-Hall k = b0 + b1 + b2 + c - 191 of that word times fp32(std/64).  Holds no model
+// Irwin-Hall k = b0 + b1 + b2 + c - 1535 (10-bit b's) of that word times fp32(std/512).  Holds no model
 // arithmetic.  Used to fill large synthetic inputs (KV caches, tables) in device memory.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -30,8 +30,8 @@ __device__ __forceinline__ uint32_t word_at(uint64_t seed, uint32_t stream, uint
 
 __device__ __forceinline__ float normal_at(uint64_t seed, uint32_t stream, uint64_t e, float scale) {
     const uint32_t w = word_at(seed, stream, e);
-    const int k = (int)(w & 127u) + (int)((w >> 7) & 127u) + (int)((w >> 14) & 127u) +
-                  (int)((w >> 21) & 1u) - 191;
+    const int k = (int)(w & 1023u) + (int)((w >> 10) & 1023u) + (int)((w >> 20) & 1023u) +
+                  (int)((w >> 30) & 1u) - 1535;
     return __fmul_rn((float)k, scale);
 }
 

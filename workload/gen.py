@@ -15,10 +15,12 @@ as easy as 1, 2, 3", SC'11).  Element ``e`` of stream ``s`` under ``seed`` is wo
 Distributions (integer arithmetic only, so host and device agree exactly)
 ------------------------------------------------------------------------
 * ``normal``: an Irwin-Hall approximation of N(0, 1).  From a 32-bit word take
-  three 7-bit uniforms b0, b1, b2 and one coin bit c; ``k = b0+b1+b2+c-191`` lies in
-  [-191, 191] with mean 0 and variance exactly 4096, so ``k/64`` has mean 0 and
-  unit variance.  A tensor of standard deviation ``std`` is ``fp32(k) * fp32(std/64)``
-  (one correctly rounded fp32 product; |k| < 256 so k/64 is exact in bf16 too).
+  three 10-bit uniforms b0, b1, b2 and one coin bit c; ``k = b0+b1+b2+c-1535`` lies
+  in [-1535, 1535] with mean 0 and variance exactly 2^18 (3 * (1024^2 - 1)/12 + 1/4),
+  so ``k/512`` has mean 0 and unit variance.  A tensor of standard deviation ``std``
+  is ``fp32(k) * fp32(std/512)`` (one correctly rounded fp32 product).  |k| needs up
+  to 11 significant bits, so most unit-variance values are not representable in bf16
+  (an fp32-mode input that were rounded to bf16 somewhere would show).
 * ``uniform_int(n)``: ``(w * n) >> 32`` for a 32-bit word w.
 * bf16 values are produced from fp32 by round-to-nearest-even on the bit pattern.
 """
@@ -114,13 +116,13 @@ def words_range(seed: int, stream: int, start: int, n: int) -> np.ndarray:
 
 
 def normal_k(w: np.ndarray) -> np.ndarray:
-    """Integer Irwin-Hall variate in [-191, 191], mean 0, variance 4096."""
+    """Integer Irwin-Hall variate in [-1535, 1535], mean 0, variance 2^18."""
     w = w.astype(np.int64)
-    return (w & 127) + ((w >> 7) & 127) + ((w >> 14) & 127) + ((w >> 21) & 1) - 191
+    return (w & 1023) + ((w >> 10) & 1023) + ((w >> 20) & 1023) + ((w >> 30) & 1) - 1535
 
 
 def normal_scale(std: float) -> np.float32:
-    return np.float32(np.float32(std) / np.float32(64.0))
+    return np.float32(np.float32(std) / np.float32(512.0))
 
 
 def normal_f32(seed: int, stream: int, shape, std: float = 1.0, start: int = 0) -> np.ndarray:

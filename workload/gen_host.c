@@ -2,7 +2,7 @@
  *
  * Same definition: element e of stream s under seed is word (e % 4) of
  * Philox4x32-10(counter = (e/4 lo, e/4 hi, s, 0), key = (seed lo, seed hi)),
- * then the integer Irwin-Hall variate k in [-191, 191] and fp32(k) * scale.
+ * then the integer Irwin-Hall variate k in [-1535, 1535] and fp32(k) * scale.
  * Holds no model arithmetic.  Built with plain gcc; no fast-math.
  */
 #include <stdint.h>
@@ -23,8 +23,8 @@ static void philox(uint32_t c[4], uint32_t k0, uint32_t k1) {
 }
 
 static inline int32_t normal_k(uint32_t w) {
-    return (int32_t)(w & 127u) + (int32_t)((w >> 7) & 127u) + (int32_t)((w >> 14) & 127u) +
-           (int32_t)((w >> 21) & 1u) - 191;
+    return (int32_t)(w & 1023u) + (int32_t)((w >> 10) & 1023u) + (int32_t)((w >> 20) & 1023u) +
+           (int32_t)((w >> 30) & 1u) - 1535;
 }
 
 static inline uint16_t bf16_rne(float f) {
