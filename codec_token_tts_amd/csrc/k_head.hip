@@ -24,8 +24,11 @@
 
 namespace ttsbb {
 
+// A group holding a NaN (no order) has no defined maximum: the kernel raises
+// FLAG_NONFINITE; the choice is the argmax of the group's other values, or class 0 when
+// every value is NaN.
 __global__ __launch_bounds__(256) void argmax_groups_kernel(const float *logits, int rows, int ld,
-                                                            int n_groups, int V, int32_t *out) {
+                                                            int n_groups, int V, int32_t *out, int *flag) {
     const int lane = threadIdx.x & 63;
     const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (item >= rows * n_groups) return;
@@ -33,23 +36,36 @@ __global__ __launch_bounds__(256) void argmax_groups_kernel(const float *logits,
     const float *x = logits + (int64_t)r * ld + (int64_t)gi * V;
     float best = -INFINITY;
     int bi = 0x7FFFFFFF;
-    for (int v = lane; v < V; v += 64) argmax_merge(best, bi, x[v], v);
+    bool nan = false;
+    for (int v = lane; v < V; v += 64) {
+        const float xv = x[v];
+        nan |= xv != xv;
+        argmax_merge(best, bi, xv, v);
+    }
     wave_argmax(best, bi);
-    if (lane == 0) out[item] = bi;
+    nan = __any(nan);
+    if (lane == 0) {
+        if (nan) raise_flag(flag, FLAG_NONFINITE);
+        out[item] = bi == 0x7FFFFFFF ? 0 : bi;
+    }
 }
 
 void launch_argmax_groups(const float *logits, int rows, int ld, int n_groups, int group_vocab,
-                          int32_t *out, hipStream_t s) {
+                          int32_t *out, int *flag, hipStream_t s) {
     const int items = rows * n_groups;
     if (items <= 0) return;
     hipLaunchKernelGGL(argmax_groups_kernel, dim3((items + 3) / 4), dim3(256), 0, s, logits, rows, ld,
-                       n_groups, group_vocab, out);
+                       n_groups, group_vocab, out, flag);
 }
+
+// The choice of a group whose scores have no order (a NaN, or an infinite logit that
+// makes the log-softmax undefined): the lowest class id that is not the mask.
+__device__ __forceinline__ int invalid_group_class(int mask_id) { return mask_id == 0 ? 1 : 0; }
 
 __global__ __launch_bounds__(256) void maskgit_scores_kernel(const float *logits, const float *logits_u,
                                                              float cfg_scale, int T, int ld, int n_cb, int V,
                                                              int mask_id, float penalty, const int32_t *codes,
-                                                             int codes_ld, int32_t *pred, float *conf) {
+                                                             int codes_ld, int32_t *pred, float *conf, int *flag) {
     const int lane = threadIdx.x & 63;
     const int item = blockIdx.x * 4 + (threadIdx.x >> 6);  // flat index k*T + t
     if (item >= n_cb * T) return;
@@ -75,25 +91,94 @@ __global__ __launch_bounds__(256) void maskgit_scores_kernel(const float *logits
     for (int v = lane; v < V; v += 64) se += exp2f((lg(v) - mx) * LOG2E);
     se = wave_sum(se);
     if (lane == 0) {
+        // se >= 1 (the maximum's own term) unless a NaN or an infinite logit entered it:
+        // such a group has no scores, is never unmasked and raises the flag
+        const bool ok = se >= 1.f && se < INFINITY && bi != 0x7FFFFFFF;
+        if (!ok) raise_flag(flag, FLAG_NONFINITE);
         const float lse = mx + logf(se);
-        pred[item] = bi;
-        conf[item] = (codes[(int64_t)k * codes_ld + t] == mask_id) ? (best - lse) - (float)k * penalty : -INFINITY;
+        pred[item] = ok ? bi : invalid_group_class(mask_id);
+        conf[item] = (ok && codes[(int64_t)k * codes_ld + t] == mask_id) ? (best - lse) - (float)k * penalty
+                                                                          : -INFINITY;
     }
 }
 
 void launch_maskgit_scores(const float *logits, const float *logits_u, float cfg_scale, int T, int ld,
                            int n_cb, int V, int mask_id, float penalty, const int32_t *codes, int codes_ld,
-                           int32_t *pred, float *conf, hipStream_t s) {
+                           int32_t *pred, float *conf, int *flag, hipStream_t s) {
     const int items = n_cb * T;
     if (items <= 0) return;
     hipLaunchKernelGGL(maskgit_scores_kernel, dim3((items + 3) / 4), dim3(256), 0, s, logits, logits_u, cfg_scale,
-                       T, ld, n_cb, V, mask_id, penalty, codes, codes_ld, pred, conf);
+                       T, ld, n_cb, V, mask_id, penalty, codes, codes_ld, pred, conf, flag);
+}
+
+// ------------------------------------------------------------------------------------
+// The sampler's random stream (OmniVoice ARCHITECTURE, "MaskGIT decoder", Determinism: a
+// seedable Philox4x32-10 generator whose counter is threaded across calls).
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as 1, 2,
+// 3", SC'11): ten rounds of the 4 x 32-bit Philox bijection, each multiplying words 0
+// and 2 by 0xD2511F53 and 0xCD9E8D57 and mixing the high halves with the other words and
+// the key, whose halves advance by the Weyl constants 0x9E3779B9 and 0xBB67AE85.
+// A uniform is ((w >> 9) + 0.5) * 2^-23 of a 32-bit word w: exact in fp32, strictly
+// inside (0, 1).
+// ------------------------------------------------------------------------------------
+__device__ __forceinline__ u32x4_t philox4x32_10(u32x4_t c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        const uint32_t hi0 = __umulhi(0xD2511F53u, c.x), lo0 = 0xD2511F53u * c.x;
+        const uint32_t hi1 = __umulhi(0xCD9E8D57u, c.z), lo1 = 0xCD9E8D57u * c.z;
+        c = u32x4_t{hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0};
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    return c;
+}
+
+__device__ __forceinline__ float open01(uint32_t w) { return ((float)(w >> 9) + 0.5f) * 0x1p-23f; }
+
+// Word e % 4 of block (base + e / 4) of the call's draws in domain `dom` (word 2 of the
+// counter): counter (lo, hi of the 64-bit block, dom, 0), key (lo, hi of the seed).
+__device__ __forceinline__ float rng_uniform(uint64_t seed, uint64_t base, uint32_t dom, uint64_t e) {
+    const uint64_t b = base + (e >> 2);
+    const u32x4_t w = philox4x32_10(u32x4_t{(uint32_t)b, (uint32_t)(b >> 32), dom, 0u}, (uint32_t)seed,
+                                    (uint32_t)(seed >> 32));
+    const int j = (int)(e & 3);
+    return open01(j == 0 ? w.x : j == 1 ? w.y : j == 2 ? w.z : w.w);
+}
+
+__global__ void rng_words_kernel(uint64_t seed, uint64_t block0, uint32_t w2, uint32_t w3, int n, uint32_t *out) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const uint64_t b = block0 + (uint64_t)i;
+    const u32x4_t w = philox4x32_10(u32x4_t{(uint32_t)b, (uint32_t)(b >> 32), w2, w3}, (uint32_t)seed,
+                                    (uint32_t)(seed >> 32));
+    out[4 * i] = w.x;
+    out[4 * i + 1] = w.y;
+    out[4 * i + 2] = w.z;
+    out[4 * i + 3] = w.w;
+}
+
+void launch_rng_words(uint64_t seed, uint64_t block0, uint32_t w2, uint32_t w3, int n_blocks, uint32_t *out,
+                      hipStream_t s) {
+    if (n_blocks <= 0) return;
+    hipLaunchKernelGGL(rng_words_kernel, dim3((n_blocks + 255) / 256), dim3(256), 0, s, seed, block0, w2, w3,
+                       n_blocks, out);
+}
+
+__global__ void advance_counter_kernel(uint64_t *ctr, uint64_t n) {
+    if (threadIdx.x == 0 && blockIdx.x == 0) *ctr += n;
+}
+
+void launch_advance_counter(uint64_t *ctr, uint64_t n, hipStream_t s) {
+    hipLaunchKernelGGL(advance_counter_kernel, dim3(1), dim3(64), 0, s, ctr, n);
 }
 
 // ------------------------------------------------------------------------------------
 // K8 with the sampler (same page, "MaskGIT decoder": keep_top_k_ratio(log_probs, 0.1),
-// gumbel_sample(temp = class_temp), score += gumbel * pos_temp; the uniforms of the
-// Gumbel noise are the caller's).  One wave per (codebook, frame); the group's V log-probs
+// gumbel_sample(temp = class_temp), score += gumbel * pos_temp).  The uniforms of the
+// Gumbel noise are the caller's arrays, or, where an array is not given, the call's
+// draws of the Philox stream (class noise of element (k, t, v) = flat e = (k T + t) V + v
+// in domain RNG_CLASS, position noise of (k, t) in domain RNG_POS, both from the block
+// *counter at the call).  One wave per (codebook, frame); the group's V log-probs
 // are kept in LDS (V <= SAMPLE_MAXV).  The top-k threshold is the k-th largest log-prob,
 // found by a bisection on the order-preserving integer image of the floats (counts by
 // wave reductions); ties at the threshold are kept in class order (ballot prefix counts).
@@ -116,7 +201,8 @@ __global__ __launch_bounds__(256) void maskgit_sample_kernel(const float *logits
                                                              int mask_id, float penalty, const int32_t *codes,
                                                              int codes_ld, float class_temp, float pos_temp,
                                                              int k_keep, const float *u_class, const float *u_pos,
-                                                             int32_t *pred, float *conf) {
+                                                             uint64_t seed, const uint64_t *counter,
+                                                             int32_t *pred, float *conf, int *flag) {
     __shared__ float lps[4][SAMPLE_MAXV];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int item = blockIdx.x * 4 + wave;  // flat index k*T + t
@@ -138,8 +224,13 @@ __global__ __launch_bounds__(256) void maskgit_sample_kernel(const float *logits
     se = wave_sum(se);
     const float lse = mx + logf(se);
     for (int v = lane; v < V; v += 64) lp[v] = v == mask_id ? -INFINITY : lp[v] - lse;  // own entries only
-
-    const float *u = u_class + (int64_t)item * V;
+    // a NaN or an infinite logit leaves the group without scores (see maskgit_scores_kernel)
+    const bool ok = se >= 1.f && se < INFINITY;
+    const uint64_t base = counter ? *counter : 0;
+    const int64_t e0 = (int64_t)item * V;
+    auto u_class_at = [&](int v) {
+        return u_class ? u_class[e0 + v] : rng_uniform(seed, base, RNG_CLASS, (uint64_t)(e0 + v));
+    };
     float best = -INFINITY;
     int bi = 0x7FFFFFFF;
     if (class_temp > 0.f) {
@@ -169,7 +260,7 @@ __global__ __launch_bounds__(256) void maskgit_sample_kernel(const float *logits
             const bool keep = in && (key > th || (eq && carry + below < need));
             carry += __popcll(bal);
             if (in) {
-                const float val = keep ? lp[v] / class_temp + gumbel_f(u[v]) : -INFINITY;
+                const float val = keep ? lp[v] / class_temp + gumbel_f(u_class_at(v)) : -INFINITY;
                 argmax_merge(best, bi, val, v);
             }
         }
@@ -179,21 +270,24 @@ __global__ __launch_bounds__(256) void maskgit_sample_kernel(const float *logits
     wave_argmax(best, bi);
     if (lane == 0) {
         float sc = best - (float)k * penalty;
-        if (pos_temp > 0.f) sc += pos_temp * gumbel_f(u_pos[item]);
-        pred[item] = bi;
-        conf[item] = (codes[(int64_t)k * codes_ld + t] == mask_id) ? sc : -INFINITY;
+        if (pos_temp > 0.f)
+            sc += pos_temp * gumbel_f(u_pos ? u_pos[item] : rng_uniform(seed, base, RNG_POS, (uint64_t)item));
+        const bool valid = ok && bi != 0x7FFFFFFF;
+        if (!valid) raise_flag(flag, FLAG_NONFINITE);
+        pred[item] = valid ? bi : invalid_group_class(mask_id);
+        conf[item] = (valid && codes[(int64_t)k * codes_ld + t] == mask_id) ? sc : -INFINITY;
     }
 }
 
 void launch_maskgit_sample(const float *logits, const float *logits_u, float cfg_scale, int T, int ld, int n_cb,
                            int V, int mask_id, float penalty, const int32_t *codes, int codes_ld, float class_temp,
-                           float pos_temp, int k_keep, const float *u_class, const float *u_pos, int32_t *pred,
-                           float *conf, hipStream_t s) {
+                           float pos_temp, int k_keep, const float *u_class, const float *u_pos, uint64_t seed,
+                           const uint64_t *counter, int32_t *pred, float *conf, int *flag, hipStream_t s) {
     const int items = n_cb * T;
     if (items <= 0) return;
     hipLaunchKernelGGL(maskgit_sample_kernel, dim3((items + 3) / 4), dim3(256), 0, s, logits, logits_u, cfg_scale,
                        T, ld, n_cb, V, mask_id, penalty, codes, codes_ld, class_temp, pos_temp, k_keep, u_class,
-                       u_pos, pred, conf);
+                       u_pos, seed, counter, pred, conf, flag);
 }
 
 constexpr int SEL_TILE = 1024;  // scores staged in LDS per block

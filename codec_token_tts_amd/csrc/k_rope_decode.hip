@@ -622,6 +622,15 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeAttnArgs a) {
     if (L > cap) L = cap;
     const int chunk = a.plan_n[1];  // the step's chunk (from the work list)
     const int nc = min(a.n_chunks, (L + chunk - 1) / chunk);
+    if (nc <= 0) {  // a token outside the cache (flagged by the plan) has no chunks: zeros
+        if (lane < 32) {
+            const int k = h * 128 + lane * 4;
+            TO *out = reinterpret_cast<TO *>(a.out) + (a.out_mt > 0 ? frag_index(b, k, a.out_mt) : (int64_t)b * a.H * 128 + k);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) out[e] = from_f32<TO>(0.f);
+        }
+        return;
+    }
     const float *part = a.part + ((int64_t)b * a.H + h) * a.part_stride * PART_STRIDE;
     float M = -INFINITY, lsum = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
     if (nc <= 32) {

@@ -9,7 +9,10 @@ namespace ttsbb {
 enum DType { DT_F32 = 0, DT_BF16 = 1 };
 
 // Device-side index check codes (OR-ed into the context flag).
-enum : int { FLAG_CODE = 1, FLAG_TEXT_ID = 2, FLAG_PAGE = 4, FLAG_POSITION = 8 };
+enum : int { FLAG_CODE = 1, FLAG_TEXT_ID = 2, FLAG_PAGE = 4, FLAG_POSITION = 8, FLAG_NONFINITE = 16 };
+
+// Domains (word 2 of the Philox counter) of the sampler's draws.
+enum : uint32_t { RNG_CLASS = 1, RNG_POS = 2 };
 
 // ---- K1: gather-sum codebook embedding ------------------------------------------
 // Row r (< n_rows) is a text row if (is_text ? is_text[r] : r < text_prefix); text rows
@@ -170,23 +173,34 @@ struct FlashArgs {
 void launch_flash_attn(const FlashArgs &a, hipStream_t s);
 
 // ---- K7: greedy choice per group --------------------------------------------------
+// A group holding a NaN raises FLAG_NONFINITE (its choice: the argmax of its other values,
+// or 0 when all are NaN).
 void launch_argmax_groups(const float *logits, int rows, int ld, int n_groups, int group_vocab,
-                          int32_t *out, hipStream_t s);
+                          int32_t *out, int *flag, hipStream_t s);
 
 // ---- K8: MaskGIT scores: log-softmax, mask class excluded, argmax, confidence --------
 // logits [T][ld] (flat k*V + v per row).  With logits_u (same layout) the scored logits
 // are the guided c + cfg_scale * (c - u).  codes: element (k, t) at codes[k*codes_ld + t].
+// A group whose log-softmax is undefined (a NaN or an infinite logit) raises
+// FLAG_NONFINITE, predicts the lowest non-mask class and scores -inf.
 void launch_maskgit_scores(const float *logits, const float *logits_u, float cfg_scale, int T, int ld,
                            int n_cb, int V, int mask_id, float penalty, const int32_t *codes, int codes_ld,
-                           int32_t *pred, float *conf, hipStream_t s);
+                           int32_t *pred, float *conf, int *flag, hipStream_t s);
 
 // With the sampler: class_temp > 0 keeps the k_keep best log-probs of each group and
 // adds Gumbel noise from u_class [n_cb][T][V]; pos_temp > 0 adds noise from u_pos
-// [n_cb][T] to the score.  V <= SAMPLE_MAXV (2048).
+// [n_cb][T] to the score.  A NULL array draws its uniforms from Philox4x32-10 (key
+// seed, blocks from *counter on, domains RNG_CLASS / RNG_POS).  V <= SAMPLE_MAXV (2048).
 void launch_maskgit_sample(const float *logits, const float *logits_u, float cfg_scale, int T, int ld, int n_cb,
                            int V, int mask_id, float penalty, const int32_t *codes, int codes_ld, float class_temp,
-                           float pos_temp, int k_keep, const float *u_class, const float *u_pos, int32_t *pred,
-                           float *conf, hipStream_t s);
+                           float pos_temp, int k_keep, const float *u_class, const float *u_pos, uint64_t seed,
+                           const uint64_t *counter, int32_t *pred, float *conf, int *flag, hipStream_t s);
+// out[4 i + j] = word j of Philox4x32-10(counter (lo, hi of block0 + i, w2, w3), key (lo, hi
+// of seed)), i < n_blocks.
+void launch_rng_words(uint64_t seed, uint64_t block0, uint32_t w2, uint32_t w3, int n_blocks, uint32_t *out,
+                      hipStream_t s);
+// *ctr += n on the device (one thread).
+void launch_advance_counter(uint64_t *ctr, uint64_t n, hipStream_t s);
 
 // ---- K9: top-n selection by rank + code update -------------------------------------
 // rank: int32 scratch [n]

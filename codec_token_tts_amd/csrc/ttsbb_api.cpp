@@ -866,7 +866,7 @@ static ttsbb_status paged_forward(ttsbb_ctx *ctx, int32_t batch, float *x, int32
         if (ctx->tap_layer >= 0) tap_dense(ctx, TTSBB_TAP_LOGITS, lg, DT_F32, rows, N, N);
         {
             KScope k(ctx, TTSBB_K_ARGMAX);
-            launch_argmax_groups(lg, rows, N, n_groups, group_vocab, argmax, ctx->stream);
+            launch_argmax_groups(lg, rows, N, n_groups, group_vocab, argmax, ctx->flag, ctx->stream);
         }
     }
     if (prefill) launch_increment(positions, 1, ctx->stream, batch);
@@ -921,7 +921,7 @@ TTSBB_API ttsbb_status ttsbb_maskgit_pass(ttsbb_ctx *ctx, int32_t n_text, const 
     {
         KScope k(ctx, TTSBB_K_SCORES);
         launch_maskgit_scores(ctx->logits, nullptr, 0.f, n_frames, N, n_cb, cb_vocab, mask_id, layer_penalty, codes,
-                              n_frames, pred, conf, ctx->stream);
+                              n_frames, pred, conf, ctx->flag, ctx->stream);
     }
     {
         KScope k(ctx, TTSBB_K_SELECT);
@@ -962,7 +962,7 @@ TTSBB_API ttsbb_status ttsbb_maskgit_pass_cfg(ttsbb_ctx *ctx, int32_t n_text, co
     {
         KScope k(ctx, TTSBB_K_SCORES);
         launch_maskgit_scores(ctx->logits, ctx->logits_u, cfg_scale, n_target, N, n_cb, cb_vocab, mask_id,
-                              layer_penalty, window, n_frames, pred, conf, ctx->stream);
+                              layer_penalty, window, n_frames, pred, conf, ctx->flag, ctx->stream);
     }
     {
         KScope k(ctx, TTSBB_K_SELECT);
@@ -991,8 +991,9 @@ TTSBB_API ttsbb_status ttsbb_maskgit_step(ttsbb_ctx *ctx, const ttsbb_maskgit_st
     for (float v : temps)
         if (!(v == v)) return TTSBB_INVALID_ARG;
     if (a->class_temp < 0.f || a->pos_temp < 0.f) return TTSBB_INVALID_ARG;
-    if (a->class_temp > 0.f && (!a->u_class || !(a->top_k_ratio > 0.f) || cb_vocab > 2048)) return TTSBB_INVALID_ARG;
-    if (a->pos_temp > 0.f && !a->u_pos) return TTSBB_INVALID_ARG;
+    const bool draw_class = a->class_temp > 0.f && !a->u_class, draw_pos = a->pos_temp > 0.f && !a->u_pos;
+    if (a->class_temp > 0.f && (!(a->top_k_ratio > 0.f) || cb_vocab > 2048)) return TTSBB_INVALID_ARG;
+    if ((draw_class || draw_pos) && !a->rng_counter) return TTSBB_INVALID_ARG;
     if (ctx->dt != DT_BF16) return TTSBB_UNSUPPORTED;
 
     const int S = n_text + n_frames, w0 = n_frames - n_target;
@@ -1015,12 +1016,14 @@ TTSBB_API ttsbb_status ttsbb_maskgit_step(ttsbb_ctx *ctx, const ttsbb_maskgit_st
             const int k_keep = std::max(1, (int)floor((double)a->top_k_ratio * cb_vocab));
             launch_maskgit_sample(ctx->logits, lu, a->cfg_scale, n_target, N, n_cb, cb_vocab, mask_id,
                                   a->layer_penalty, window, n_frames, a->class_temp, a->pos_temp, k_keep, a->u_class,
-                                  a->u_pos, a->pred, a->conf, ctx->stream);
+                                  a->u_pos, a->rng_seed, a->rng_counter, a->pred, a->conf, ctx->flag, ctx->stream);
         } else {
             launch_maskgit_scores(ctx->logits, lu, a->cfg_scale, n_target, N, n_cb, cb_vocab, mask_id,
-                                  a->layer_penalty, window, n_frames, a->pred, a->conf, ctx->stream);
+                                  a->layer_penalty, window, n_frames, a->pred, a->conf, ctx->flag, ctx->stream);
         }
     }
+    if (draw_class || draw_pos)  // the call's draws span ceil(n_cb n_target cb_vocab / 4) counter blocks
+        launch_advance_counter(a->rng_counter, ((uint64_t)n_cb * n_target * cb_vocab + 3) / 4, ctx->stream);
     {
         KScope k(ctx, TTSBB_K_SELECT);
         launch_select_update(a->conf, a->pred, n_cb, n_target, n_unmask, ctx->rank, window, n_frames, a->picked,
@@ -1052,6 +1055,15 @@ TTSBB_API ttsbb_status ttsbb_rvq_decode(ttsbb_ctx *ctx, int32_t n_frames, int32_
         KScope k(ctx, TTSBB_K_RVQ);
         launch_rvq_decode(r, ctx->stream);
     }
+    return launch_failed() ? TTSBB_DEVICE_ERROR : TTSBB_OK;
+}
+
+TTSBB_API ttsbb_status ttsbb_philox_words(ttsbb_ctx *ctx, uint64_t seed, uint64_t block0, uint32_t word2,
+                                          uint32_t word3, int32_t n_blocks, uint32_t *out) {
+    if (!ctx || n_blocks < 0) return TTSBB_INVALID_ARG;
+    if (n_blocks == 0) return TTSBB_OK;
+    if (!out) return TTSBB_INVALID_ARG;
+    launch_rng_words(seed, block0, word2, word3, n_blocks, out, ctx->stream);
     return launch_failed() ? TTSBB_DEVICE_ERROR : TTSBB_OK;
 }
 

@@ -22,7 +22,7 @@ F32, BF16 = 0, 1
 
 EXPORTS = ["ttsbb_default_config", "ttsbb_create", "ttsbb_destroy", "ttsbb_status_str",
            "ttsbb_sync", "ttsbb_codebook_embed", "ttsbb_decode_step", "ttsbb_prefill", "ttsbb_maskgit_pass",
-           "ttsbb_maskgit_pass_cfg", "ttsbb_maskgit_step", "ttsbb_rvq_decode", "ttsbb_unmask_schedule", "ttsbb_set_tap_layer", "ttsbb_read_tap", "ttsbb_profile_start",
+           "ttsbb_maskgit_pass_cfg", "ttsbb_maskgit_step", "ttsbb_rvq_decode", "ttsbb_philox_words", "ttsbb_unmask_schedule", "ttsbb_set_tap_layer", "ttsbb_read_tap", "ttsbb_profile_start",
            "ttsbb_profile_stop"]
 
 (K_EMBED, K_RMSNORM, K_GEMM_QKV, K_ROPE_KV, K_DECODE_ATTN, K_DECODE_COMBINE, K_FLASH_ATTN, K_GEMM_O,
@@ -40,7 +40,7 @@ class ttsbb_maskgit_step_args(C.Structure):
                 ("n_unmask", C.c_int32), ("layer_penalty", C.c_float), ("cfg_scale", C.c_float),
                 ("class_temp", C.c_float), ("pos_temp", C.c_float), ("top_k_ratio", C.c_float),
                 ("u_class", C.c_void_p), ("u_pos", C.c_void_p), ("pred", C.c_void_p), ("conf", C.c_void_p),
-                ("picked", C.c_void_p)]
+                ("picked", C.c_void_p), ("rng_seed", C.c_uint64), ("rng_counter", C.c_void_p)]
 
 
 class TtsbbError(RuntimeError):
@@ -91,6 +91,7 @@ def lib() -> C.CDLL:
                                          f32, vp, vp, vp]),
         "ttsbb_maskgit_step": (i32, [vp, C.POINTER(ttsbb_maskgit_step_args)]),
         "ttsbb_rvq_decode": (i32, [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp]),
+        "ttsbb_philox_words": (i32, [vp, C.c_uint64, C.c_uint64, C.c_uint32, C.c_uint32, i32, vp]),
         "ttsbb_unmask_schedule": (i32, [i32, i32, C.POINTER(i32)]),
         "ttsbb_set_tap_layer": (i32, [vp, i32]),
         "ttsbb_read_tap": (i32, [vp, i32, vp, i64, C.POINTER(i32), C.POINTER(i32)]),
@@ -214,11 +215,12 @@ def ttsbb_maskgit_pass_cfg(ctx, n_text, text_ids, text_table, text_vocab, n_fram
 def ttsbb_maskgit_step(ctx, n_text, text_ids, text_table, text_vocab, n_frames, n_target, n_cb, cb_vocab,
                        mask_id, audio_tables, audio_heads, codes, n_unmask, layer_penalty, pred, conf, picked,
                        cfg_scale=0.0, class_temp=0.0, pos_temp=0.0, top_k_ratio=0.1, u_class=None, u_pos=None,
-                       check: bool = True) -> int:
+                       rng_seed=0, rng_counter=None, check: bool = True) -> int:
     a = ttsbb_maskgit_step_args(n_text, ptr(text_ids), ptr(text_table), text_vocab, n_frames, n_target, n_cb,
                                 cb_vocab, mask_id, ptr(audio_tables), ptr(audio_heads), ptr(codes), n_unmask,
                                 float(layer_penalty), float(cfg_scale), float(class_temp), float(pos_temp),
-                                float(top_k_ratio), ptr(u_class), ptr(u_pos), ptr(pred), ptr(conf), ptr(picked))
+                                float(top_k_ratio), ptr(u_class), ptr(u_pos), ptr(pred), ptr(conf), ptr(picked),
+                                int(rng_seed) & 0xFFFFFFFFFFFFFFFF, ptr(rng_counter))
     st = lib().ttsbb_maskgit_step(ctx, C.byref(a))
     if check:
         _check(st, "ttsbb_maskgit_step")
@@ -231,6 +233,14 @@ def ttsbb_rvq_decode(ctx, n_frames, n_q, codebook_size, codebook_dim, out_dim, c
                                 ptr(proj_w), ptr(proj_b), ptr(out))
     if check:
         _check(st, "ttsbb_rvq_decode")
+    return st
+
+
+def ttsbb_philox_words(ctx, seed, block0, word2, word3, n_blocks, out, check: bool = True) -> int:
+    st = lib().ttsbb_philox_words(ctx, int(seed) & 0xFFFFFFFFFFFFFFFF, int(block0) & 0xFFFFFFFFFFFFFFFF,
+                                  int(word2) & 0xFFFFFFFF, int(word3) & 0xFFFFFFFF, n_blocks, ptr(out))
+    if check:
+        _check(st, "ttsbb_philox_words")
     return st
 
 

@@ -81,7 +81,9 @@ typedef struct {
  * hidden 1024, 16/8 heads of 128, ffn 3072, eps 1e-6, theta 1e6, bf16, 16-token pages. */
 void ttsbb_default_config(ttsbb_config *cfg);
 
-/* Create a context on the current HIP device.  `layers` holds cfg->n_layers entries
+/* Create a context on the current HIP device (OmniVoice ARCHITECTURE, "Public API": one
+ * opaque handle per pipeline, one init and one free; "ABI guarantee": plain C99,
+ * extern "C", only the prefixed symbols exported).  `layers` holds cfg->n_layers entries
  * (copied; the pointers inside are borrowed).  `final_norm` is the fp32 [hidden] gain
  * of the last RMSNorm (llm.norm); it may be NULL only if no call uses a head.
  * `hip_stream` is a hipStream_t (NULL = the null stream).  Allocates the workspace
@@ -90,11 +92,20 @@ void ttsbb_default_config(ttsbb_config *cfg);
 ttsbb_status ttsbb_create(const ttsbb_config *cfg, const ttsbb_layer *layers,
                           const float *final_norm, void *hip_stream, ttsbb_ctx **out);
 
+/* Free a context (OmniVoice ARCHITECTURE, "Public API": the one free of the handle):
+ * waits for its stream, then releases the workspace.  NULL is a no-op; the weights and
+ * every caller buffer stay the caller's. */
 void ttsbb_destroy(ttsbb_ctx *ctx);
 
+/* Static text of a status code (OmniVoice ARCHITECTURE, "Public API": status codes, 0
+ * for success and negative values for failures). */
 const char *ttsbb_status_str(ttsbb_status s);
 
-/* Wait for the context's stream; report (and clear) the device-side index flag. */
+/* Wait for the context's stream; report (and clear) the device-side flag: an index out
+ * of range (a code, a text id, a page id, a position) or a head output without an order
+ * (a NaN, or an infinite logit in a MaskGIT group).  Returns TTSBB_DEVICE_ERROR for a
+ * failed wait or a raised flag (OmniVoice ARCHITECTURE, "Public API": a failed generate
+ * is reported by status). */
 ttsbb_status ttsbb_sync(ttsbb_ctx *ctx);
 
 /* Summed codebook embedding (OmniVoice ARCHITECTURE, "Qwen3 0.6B backbone with custom
@@ -126,8 +137,11 @@ ttsbb_status ttsbb_codebook_embed(ttsbb_ctx *ctx, int32_t n_rows, int32_t n_cb,
  *              final RMSNorm and the head are applied and argmax int32 [batch][n_groups]
  *              receives the greedy class of each group (ties: lowest id).
  *   logits     optional fp32 [batch][n_groups*group_vocab] copy of the head output.
- * Positions >= max_pages*kv_page or page ids outside [0, n_pages) raise the device
- * flag and skip the write. */
+ *              A group holding a NaN raises the device flag; its choice is the argmax
+ *              of its other values, or class 0 if all are NaN.
+ * Positions outside [0, max_pages*kv_page) or page ids outside [0, n_pages) raise the
+ * device flag and skip the write; a stream whose position is negative attends to
+ * nothing (its attention output is zero). */
 ttsbb_status ttsbb_decode_step(ttsbb_ctx *ctx, int32_t batch, float *x, int32_t *positions,
                                const int32_t *page_table, int32_t max_pages, void *kv_pool,
                                int32_t n_pages, const void *head, int32_t n_groups,
@@ -198,10 +212,16 @@ ttsbb_status ttsbb_maskgit_pass_cfg(ttsbb_ctx *ctx, int32_t n_text, const int32_
 
 /* Arguments of the general MaskGIT step: those of ttsbb_maskgit_pass_cfg plus the
  * sampler (OmniVoice ARCHITECTURE, "MaskGIT decoder": keep_top_k_ratio, gumbel_sample with
- * the class temperature, Gumbel noise on the scores with the position temperature).  The
- * uniforms of the Gumbel noise are inputs, so the step is a pure function of its
- * arguments: the caller draws them from its counter-based stream (the page threads a
- * Philox4x32-10 counter across calls). */
+ * the class temperature, Gumbel noise on the scores with the position temperature;
+ * Determinism: a seedable Philox4x32-10 stream whose counter is threaded across calls).
+ * The uniforms of the Gumbel noise come from the caller's arrays when given, else from
+ * the library's Philox4x32-10 stream: uniform e of a call is
+ *   ((w >> 9) + 0.5) * 2^-23,  w = word e % 4 of Philox4x32-10(counter = (lo, hi of
+ *   *rng_counter + e / 4, domain, 0), key = (lo, hi of rng_seed))
+ * with domain 1 and e = (k * n_target + t) * cb_vocab + v for the class noise, domain 2
+ * and e = k * n_target + t for the position noise; ttsbb_philox_words exposes the
+ * words.  The counter lives on the device and the call advances it there, so a captured
+ * step replays with fresh draws. */
 typedef struct {
     int32_t n_text;
     const int32_t *text_ids;     /* int32 [n_text] */
@@ -217,11 +237,16 @@ typedef struct {
     float class_temp;            /* > 0: top-k ratio filter + Gumbel noise on the classes */
     float pos_temp;              /* > 0: Gumbel noise on the scores */
     float top_k_ratio;           /* keeps max(1, floor(top_k_ratio * cb_vocab)) classes */
-    const float *u_class;        /* fp32 [n_cb][n_target][cb_vocab] in (0,1); class_temp > 0 */
-    const float *u_pos;          /* fp32 [n_cb][n_target] in (0,1); pos_temp > 0 */
+    const float *u_class;        /* fp32 [n_cb][n_target][cb_vocab] in (0,1), or NULL: drawn */
+    const float *u_pos;          /* fp32 [n_cb][n_target] in (0,1), or NULL: drawn */
     int32_t *pred;               /* int32 [n_cb][n_target] */
     float *conf;                 /* fp32 [n_cb][n_target] */
     int32_t *picked;             /* int32 [n_unmask], flat window indices or -1 */
+    uint64_t rng_seed;           /* Philox4x32-10 key of the drawn uniforms */
+    uint64_t *rng_counter;       /* device uint64 [1], in/out: the first counter block of
+                                    this call's draws; advanced on the device by
+                                    ceil(n_cb * n_target * cb_vocab / 4) when the call
+                                    draws anything.  Required if a needed array is NULL. */
 } ttsbb_maskgit_step_args;
 
 /* One MaskGIT step in general form: the passes of ttsbb_maskgit_pass_cfg (one pass when
@@ -235,6 +260,13 @@ typedef struct {
  * with G(u) = -log(-log(u)), and the top-n update of ttsbb_maskgit_pass_cfg.  All
  * pointers are device memory; cb_vocab <= 2048 when class_temp > 0. */
 ttsbb_status ttsbb_maskgit_step(ttsbb_ctx *ctx, const ttsbb_maskgit_step_args *args);
+
+/* The sampler's counter-based generator (OmniVoice ARCHITECTURE, "MaskGIT decoder",
+ * Determinism: Philox4x32-10; Salmon, Moraes, Dror, Shaw, SC'11): out [n_blocks][4]
+ * (device uint32) receives, for block i, the four words of Philox4x32-10 with counter
+ * (lo, hi of block0 + i, word2, word3) and key (lo, hi of seed).  n_blocks may be 0. */
+ttsbb_status ttsbb_philox_words(ttsbb_ctx *ctx, uint64_t seed, uint64_t block0, uint32_t word2, uint32_t word3,
+                                int32_t n_blocks, uint32_t *out);
 
 /* Codec RVQ decode (OmniVoice ARCHITECTURE, "Audio tokenizer pipeline", decode path; ncnn
  * Qwen3-TTS port, "Codec Decoder的切分"): for every frame t the sum over codebooks k of

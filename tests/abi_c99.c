@@ -54,6 +54,7 @@ int main(void) {
         EXPECT(ttsbb_maskgit_step(NULL, &sa) == TTSBB_INVALID_ARG);
     }
     EXPECT(ttsbb_rvq_decode(NULL, 1, 8, 1024, 64, 1024, NULL, NULL, NULL, NULL, &dummy) == TTSBB_INVALID_ARG);
+    EXPECT(ttsbb_philox_words(NULL, 42u, 0u, 1u, 0u, 1, NULL) == TTSBB_INVALID_ARG);
     EXPECT(ttsbb_prefill(NULL, 1, &dummy, NULL, NULL, 1, NULL, 1, NULL, 0, 0, NULL, NULL) == TTSBB_INVALID_ARG);
     EXPECT(ttsbb_set_tap_layer(NULL, 0) == TTSBB_INVALID_ARG);
     EXPECT(ttsbb_read_tap(NULL, 0, &dummy, 1, NULL, NULL) == TTSBB_INVALID_ARG);

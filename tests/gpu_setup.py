@@ -11,13 +11,31 @@ from workload import gen
 
 
 # bf16-mode tolerances (normwise max|gpu - ref| / max|ref|):
-# * one layer's output: 2e-2, the bound stated for layer outputs;
-# * a 28-layer stack: 3e-2.  Rounding the operands of the four products and the new K/V
-#   to bf16 in every layer, and nothing else, already moves the 28-layer output of the
-#   batch-1 decode workload by 1.8% (1.95% rms) from the exact result; the bound allows
-#   that plus the fp32 accumulation-order differences of the GPU kernels.
+# * one layer against the exact oracle: 2e-2, the bound stated for layer outputs -- for a
+#   stack, each checked layer on the GPU's own input to that layer (teacher-forced);
+# * one layer against the bf16-storage emulation (tests/bf16_emulation.py: the same bf16
+#   roundings on fp64 arithmetic): 5e-3.  Only fp32-versus-fp64 arithmetic separates the
+#   two, and it reaches a bf16 value only where it flips a rounding (one flip of a
+#   near-maximal element is already 2^-8..2^-7 normwise);
+# * a free-running stack: such flips cascade (a flipped operand moves every output of
+#   the next product, which flips more of the next rounding point); even correctly
+#   rounded fp32 arithmetic drifts 5e-3 from the emulation over the 28-layer batch-1
+#   decode stack (tests/test_bf16_emulation.py), so the GPU is held to at most what an
+#   independent draw of the whole bf16 rounding noise would give: sqrt(2) x the
+#   emulation's own distance from the oracle ("storage"; 1.89% for that stack), and to
+#   (1 + sqrt(2)) x storage from the oracle (triangle inequality); never less than the
+#   one-layer bounds.
 TOL_LAYER_BF16 = 2e-2
-TOL_STACK_BF16 = 3e-2
+TOL_EMUL_BF16 = 5e-3
+# Discrete checks against a reference at a distance delta accept a different choice only
+# at a near tie (a margin below 2 delta); for one or two layers, and for the 6000 groups
+# of the MaskGIT workload, such groups may be at most NEAR_TIE_FRAC of all (more would
+# make the check vacuous), and top-n boundary elements at most BOUNDARY_FRAC of the
+# candidates.  Free-running deep stacks of few groups report their agreement instead:
+# there delta is 1-2% of the largest logit, and the choices are checked bit for bit on
+# the GPU's own head operand (check_head_teacher_forced).
+NEAR_TIE_FRAC = 0.15
+BOUNDARY_FRAC = 0.15
 
 
 def torch():
@@ -95,14 +113,115 @@ def normwise(gpu: np.ndarray, ref: np.ndarray) -> float:
     return float(np.max(np.abs(gpu - ref)) / (den if den > 0 else 1.0))
 
 
+def elementwise(gpu: np.ndarray, ref: np.ndarray, floor: float = 1e-2) -> float:
+    """max |gpu - ref| / |ref| over the elements with |ref| >= floor * max |ref| (the
+    elementwise relative error; it is ill-posed for elements near zero)."""
+    gpu = np.asarray(gpu, np.float64)
+    ref = np.asarray(ref, np.float64)
+    big = np.abs(ref) >= floor * np.max(np.abs(ref))
+    return float(np.max(np.abs(gpu[big] - ref[big]) / np.abs(ref[big]))) if big.any() else 0.0
+
+
+def check_stack(name: str, gpu, emul, exact):
+    """A free-running bf16 stack's output against the emulation and the exact oracle (the
+    bounds above, from the emulation's own distance to the oracle).  Prints normwise and
+    elementwise figures."""
+    d_emul = normwise(gpu, emul)
+    d_exact = normwise(gpu, exact)
+    storage = normwise(emul, exact)
+    print("%s: vs emulation %.2e (elementwise %.2e); vs oracle %.2e (elementwise %.2e); bf16 storage %.2e"
+          % (name, d_emul, elementwise(gpu, emul), d_exact, elementwise(gpu, exact), storage))
+    assert d_emul <= max(TOL_EMUL_BF16, np.sqrt(2.0) * storage), (name, d_emul, storage)
+    assert d_exact <= max(TOL_LAYER_BF16, (1 + np.sqrt(2.0)) * storage), (name, d_exact, storage)
+    return d_emul, d_exact
+
+
+def check_layer(name: str, gpu_out, emul_out, exact_out):
+    """One layer on the GPU's own input: the layer bound against the oracle, TOL_EMUL_BF16
+    against the emulation."""
+    d_emul, d_exact = normwise(gpu_out, emul_out), normwise(gpu_out, exact_out)
+    print("%s (teacher-forced layer): vs emulation %.2e, vs oracle %.2e (elementwise %.2e)"
+          % (name, d_emul, d_exact, elementwise(gpu_out, exact_out)))
+    assert d_emul <= TOL_EMUL_BF16, (name, d_emul)
+    assert d_exact <= TOL_LAYER_BF16, (name, d_exact)
+
+
+def check_head_teacher_forced(y, head, gpu_logits, gpu_choice, n_groups: int, V: int, exclude=None,
+                              gap_rel: float = 1e-6, max_frac: float = 1e-3):
+    """A head and its greedy choice on the GPU's own head operand y (bf16 values, as the
+    GPU read them): the oracle's fp64 head on the same y, so only the order of the fp32
+    accumulation separates the logits.  Checks
+    * every logit within the order-independent bound of an fp32 sum of K exact products,
+      |err| <= (K - 1) 2^-24 sum_i |y_i H_ci| (the bf16 x bf16 products are exact in fp32);
+    * the choice equals the oracle's argmax bit for bit, except in a group whose oracle
+      top-1 / top-2 gap is below gap_rel * max |logit| of the group (a tie fp32 cannot
+      resolve); such groups are at most max_frac of all.
+    Returns (near-tie groups, oracle logits [rows][n_groups * V])."""
+    y = np.asarray(y, np.float64)
+    H = np.asarray(head, np.float64)
+    ref = y @ H.T
+    bound = (y.shape[1] - 1) * 2.0 ** -24 * (np.abs(y) @ np.abs(H).T)
+    err = np.abs(np.asarray(gpu_logits, np.float64) - ref)
+    assert np.all(err <= bound), "logit beyond the fp32 accumulation bound: %g vs %g" % (
+        float(np.max(err - bound)), float(np.max(bound)))
+    rows = y.shape[0]
+    r = ref.reshape(rows, n_groups, V).copy()
+    if exclude is not None:
+        r[..., exclude] = -np.inf
+    ref_arg = np.argmax(r, axis=-1)
+    top2 = np.sort(r, axis=-1)[..., -2:]
+    scale = np.max(np.where(np.isfinite(r), np.abs(r), 0.0), axis=-1)
+    near = (top2[..., 1] - top2[..., 0]) < gap_rel * scale
+    ch = np.asarray(gpu_choice).reshape(rows, n_groups)
+    assert not np.any((ch != ref_arg) & ~near), "choice differs from the oracle's at a resolvable gap"
+    n_near = int(near.sum())
+    print("teacher-forced head: %d groups, %d near ties, max |dlogit| %.2e (bound %.2e)"
+          % (near.size, n_near, float(np.max(err)), float(np.max(bound))))
+    assert n_near <= max_frac * near.size, n_near
+    return n_near, ref
+
+
+def check_scores_teacher_forced(gpu_pred, gpu_conf, gpu_picked, ref_logits, codes_kt, n_cb: int, V: int,
+                                mask_id: int, penalty: float, n_unmask: int, gap_rel: float = 1e-6,
+                                max_frac: float = 1e-3):
+    """MaskGIT scoring and selection on the oracle's fp64 logits of the GPU's own head
+    operand: pred bit-exact except at oracle near ties (as above), conf within the fp32
+    evaluation of the log-softmax (2 max|dlogit| + 2e-5 + 2^-20 |conf|), the same masked
+    set, and picked exactly the oracle's top-n of the GPU's own conf (ties: lower flat
+    index).  Returns the near-tie count."""
+    pred_r, conf_r, lp_r = O.maskgit_scores(ref_logits, codes_kt, n_cb, V, mask_id, penalty)
+    T = ref_logits.shape[0]
+    lg = np.asarray(ref_logits).reshape(T, n_cb, V).transpose(1, 0, 2).copy()
+    lg[..., mask_id] = -np.inf
+    top2 = np.sort(lg, axis=-1)[..., -2:]
+    scale = np.max(np.where(np.isfinite(lg), np.abs(lg), 0.0), axis=-1)
+    near = (top2[..., 1] - top2[..., 0]) < gap_rel * scale
+    gp = np.asarray(gpu_pred)
+    assert not np.any((gp != pred_r) & ~near), "pred differs from the oracle's at a resolvable gap"
+    assert int(near.sum()) <= max_frac * near.size
+    cg = np.asarray(gpu_conf, np.float64)
+    fin = np.isfinite(conf_r)
+    assert np.array_equal(np.isfinite(cg), fin), "masked sets differ"
+    ok = fin & (gp == pred_r)
+    if ok.any():
+        d = np.abs(cg[ok] - conf_r[ok])
+        assert np.all(d <= 2e-5 + 2.0 ** -20 * np.abs(conf_r[ok])), float(np.max(d))
+        print("teacher-forced scores: max |dconf| %.2e" % float(np.max(d)))
+    want = O.select_top(cg.reshape(-1), n_unmask)
+    assert np.array_equal(np.asarray(gpu_picked).reshape(-1), want), "picked is not the top-n of the GPU's scores"
+    return int(near.sum())
+
+
 def check_argmax_groups(gpu_choice: np.ndarray, gpu_logits: np.ndarray, ref_logits: np.ndarray,
-                        exclude=None):
+                        exclude=None, max_near: float = NEAR_TIE_FRAC):
     """Discrete parity of a greedy choice.
 
     1. The GPU's choice is exactly the argmax of the GPU's own logits (ties -> lowest id).
     2. With delta = max |gpu - ref| over the group, the choice equals the reference argmax
        wherever the reference's top-2 gap exceeds 2*delta; elsewhere (a near tie) it must
        be within 2*delta of the reference maximum.
+    3. Near-tie groups are at most max_near of all groups (max_near = None: not capped;
+       only for a reference that is the GPU's own logits).
     Returns the number of near-tie groups.  Arrays are [..., V]."""
     g = np.asarray(gpu_logits, np.float64)
     r = np.asarray(ref_logits, np.float64)
@@ -125,17 +244,26 @@ def check_argmax_groups(gpu_choice: np.ndarray, gpu_logits: np.ndarray, ref_logi
     assert np.array_equal(ch[clear], ref_arg[clear]), "argmax differs where the margin is clear"
     chosen = np.take_along_axis(r, ch[..., None], axis=-1)[..., 0]
     assert np.all(chosen >= top2[..., 1] - 2 * delta - 1e-12), "near-tie choice is not near the top"
-    return int(np.count_nonzero(~clear))
+    n_near = int(np.count_nonzero(~clear))
+    if max_near is not None:
+        assert n_near <= max(1, max_near * clear.size), "near ties: %d of %d groups" % (n_near, clear.size)
+    if clear.size > 1:
+        print("argmax: %d groups, %d near ties, agreement with the reference %.4f"
+              % (clear.size, n_near, float(np.mean(ch == ref_arg))))
+    return n_near
 
 
-def check_topn(picked: np.ndarray, conf_gpu: np.ndarray, conf_ref: np.ndarray, n: int):
+def check_topn(picked: np.ndarray, conf_gpu: np.ndarray, conf_ref: np.ndarray, n: int,
+               max_near: float = BOUNDARY_FRAC):
     """Discrete parity of the top-n selection.
 
     1. picked is exactly the top-n of the GPU's own scores (decreasing, ties -> lower flat
        index, -1 where fewer than n are finite).
     2. Against the reference, with eps = max |gpu - ref| over finite scores: every element
        whose reference score clears the reference's n-th score by 2*eps is picked, and no
-       picked element falls 2*eps below it.  Returns the count of boundary elements."""
+       picked element falls 2*eps below it.
+    3. Boundary elements (within 2*eps of that score) are at most max_near of the
+       finite candidates (at least 2).  Returns their count."""
     cg = np.asarray(conf_gpu, np.float64).reshape(-1)
     cr = np.asarray(conf_ref, np.float64).reshape(-1)
     order = sorted([(-cg[i], i) for i in range(cg.size) if np.isfinite(cg[i])])
@@ -154,7 +282,10 @@ def check_topn(picked: np.ndarray, conf_gpu: np.ndarray, conf_ref: np.ndarray, n
     must = np.nonzero(fin & (cr > thr + 2 * eps))[0]
     assert all(int(i) in sel for i in must), "a clearly winning position was not picked"
     assert all(cr[i] >= thr - 2 * eps for i in sel), "a clearly losing position was picked"
-    return int(np.count_nonzero(fin & (np.abs(cr - thr) <= 2 * eps)))
+    n_near = int(np.count_nonzero(fin & (np.abs(cr - thr) <= 2 * eps)))
+    if max_near is not None:
+        assert n_near <= max(2, max_near * int(fin.sum())), "boundary elements: %d of %d" % (n_near, int(fin.sum()))
+    return n_near
 
 
 def check_sampler(gpu_pred, gpu_conf, guided_gpu, guided_ref, window, n_cb, V, mask_id, penalty, class_temp,

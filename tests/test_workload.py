@@ -48,6 +48,15 @@ def test_normal_moments_and_grid():
     assert gen.normal_k(np.array([1 | (2 << 10) | (3 << 20) | (1 << 30)], np.uint32)).tolist() == [1 + 2 + 3 + 1 - 1535]
 
 
+def test_open01_is_exact_and_strictly_inside():
+    w = np.array([0, 1, 511, 512, 0x80000000, 0xFFFFFE00, 0xFFFFFFFF], np.uint32)
+    u = gen.open01_of_words(w)
+    exact = ((w.astype(np.float64) // 512) + 0.5) * 2.0 ** -23
+    assert np.array_equal(u.astype(np.float64), exact)          # no rounding in fp32
+    assert u[0] == 2.0 ** -24 and u[-1] == 1.0 - 2.0 ** -24       # never 0 or 1
+    assert np.all((u > 0) & (u < 1))
+
+
 def test_bf16_round_to_nearest_even():
     vals = np.array([1.0, 1.0 + 2**-8, 1.0 + 3 * 2**-8, 1.0 + 2**-9, -2.5e-3], np.float32)
     b = gen.bf16_bits_to_f32(gen.f32_to_bf16_bits(vals))

@@ -142,12 +142,18 @@ def uniform_int(seed: int, stream: int, shape, n: int, start: int = 0) -> np.nda
     return ((w * np.uint64(n)) >> np.uint64(32)).astype(np.int32).reshape(shape)
 
 
+def open01_of_words(w: np.ndarray) -> np.ndarray:
+    """fp32 uniforms strictly inside (0, 1) from 32-bit words: ((w >> 9) + 0.5) * 2^-23.
+    (w >> 9) + 0.5 needs 24 significant bits, so the value is exact in fp32; the extremes
+    are 2^-24 and 1 - 2^-24."""
+    w = np.asarray(w, np.uint64)
+    return (((w >> np.uint64(9)).astype(np.float64) + 0.5) * 2.0 ** -23).astype(np.float32)
+
+
 def uniform_open01(seed: int, stream: int, shape, start: int = 0) -> np.ndarray:
-    """fp32 uniforms strictly inside (0, 1): ((w >> 8) + 0.5) * 2^-24 of one word each
-    (exactly representable in fp32; never 0 or 1)."""
+    """open01_of_words of the stream's words, one word per value."""
     n = int(np.prod(shape))
-    w = fast_words(seed, stream, start, n).astype(np.uint64)
-    return (((w >> np.uint64(8)).astype(np.float64) + 0.5) * 2.0 ** -24).astype(np.float32).reshape(shape)
+    return open01_of_words(fast_words(seed, stream, start, n)).reshape(shape)
 
 
 def permutation(seed: int, stream: int, n: int) -> np.ndarray:
