@@ -16,6 +16,7 @@
 
 #include <new>
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "../../include/ttsbb.h"
@@ -29,6 +30,15 @@ namespace {
 
 constexpr int MAX_CHUNKS = 32;   // decode attention partials per (stream, head)
 constexpr int PART_STRIDE = 132; // floats per partial (m, l, 2 pad, 128 dims)
+
+// The decode step without allocation (ttsbb_decode_step_noalloc): its per-call scratch
+// lives in one file-scope device array; every GPU the library runs on holds its own copy
+// until the process ends.  Sized for the limits below at the default backbone shape.
+constexpr size_t STATIC_SCRATCH_BYTES = (size_t)32 << 20;
+constexpr int STATIC_MAX_BATCH = 64;
+constexpr int STATIC_MAX_HEAD_COLS = 8200;
+constexpr int STATIC_GPART_SPLITS = 8;  // the skinny products' largest K split
+constexpr int MAX_DEVICES = 64;
 
 struct Tap {
     float *buf = nullptr;
@@ -73,9 +83,11 @@ struct ttsbb_ctx {
     int pend_rows = 0;
     float2 *rope = nullptr;
     int *flag = nullptr;
-    int4 *plan = nullptr;     // decode attention work list (R * MAX_CHUNKS pairs)
+    int4 *plan = nullptr;     // decode attention work list (work_rows * MAX_CHUNKS pairs)
     int *plan_n = nullptr;
-    int *plan_pages = nullptr;  // [R * MAX_CHUNKS][64]
+    int *plan_pages = nullptr;  // [work_rows * MAX_CHUNKS][64]
+    int work_rows = 0;          // rows the attention work list and partials are sized for
+    void *static_scratch = nullptr;  // this device's copy of the static scratch array
     std::vector<void *> allocs;
     // taps
     int tap_layer = -1;
@@ -83,7 +95,27 @@ struct ttsbb_ctx {
     Prof prof;
 };
 
+// The static scratch of ttsbb_decode_step_noalloc.  Host code never uses this name as an
+// address (it is a host-side stand-in): the device address of each GPU's copy comes from
+// hipGetSymbolAddress, taken once per device with that device current (ttsbb_create).
+static __device__ __align__(256) unsigned char scratch[STATIC_SCRATCH_BYTES];
+
 namespace {
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[MAX_DEVICES] = {};
+
+// Device address of the current device's scratch array (nullptr if it cannot be had).
+void *static_scratch_of(int dev) {
+    if (dev < 0 || dev >= MAX_DEVICES) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess && p) g_scratch_ptr[dev] = p;
+        else hipGetLastError();
+    }
+    return g_scratch_ptr[dev];
+}
 
 bool dev_alloc(ttsbb_ctx *c, void **p, size_t bytes) {
     if (bytes == 0) bytes = 256;
@@ -234,10 +266,13 @@ TTSBB_API ttsbb_status ttsbb_create(const ttsbb_config *cfg, const ttsbb_layer *
     c->qkv_w = (g.n_heads + 2 * g.n_kv_heads) * g.head_dim;
     {
         int dev = 0, n = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-            c->n_cu = n;
+        if (hipGetDevice(&dev) == hipSuccess) {
+            if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+                c->n_cu = n;
+            c->static_scratch = static_scratch_of(dev);
+        }
     }
+    c->work_rows = g.max_rows;
 
     const size_t R = (size_t)g.max_rows;
     const size_t hd_all = (size_t)g.n_heads * g.head_dim;
@@ -753,7 +788,7 @@ static ttsbb_status paged_forward(ttsbb_ctx *ctx, int32_t batch, float *x, int32
     while (chunk > g.kv_page && (int64_t)batch * Hkv * ((cap + chunk - 1) / chunk) < 256) chunk /= 2;
     chunk = round_up(chunk, g.kv_page);
     int n_chunks = (cap + chunk - 1) / chunk;
-    while ((int64_t)batch * n_chunks > (int64_t)g.max_rows * MAX_CHUNKS) {
+    while ((int64_t)batch * n_chunks > (int64_t)ctx->work_rows * MAX_CHUNKS) {
         chunk *= 2;
         n_chunks = (cap + chunk - 1) / chunk;
     }
@@ -776,7 +811,7 @@ static ttsbb_status paged_forward(ttsbb_ctx *ctx, int32_t batch, float *x, int32
     da.plan = ctx->plan;
     da.plan_n = ctx->plan_n;
     da.plan_pages = ctx->plan_pages;
-    da.plan_cap = (int)(g.max_rows * MAX_CHUNKS);
+    da.plan_cap = (int)(ctx->work_rows * MAX_CHUNKS);
     // q_len = 1 decode: the work list balances the items over the CUs, two workgroups of
     // four waves per CU (measured on the 64-stream workload: 97.7 -> 95.1 us; one or three
     // workgroups per CU, or targets between the multiples, were slower)
@@ -880,6 +915,79 @@ TTSBB_API ttsbb_status ttsbb_decode_step(ttsbb_ctx *ctx, int32_t batch, float *x
                                          int32_t group_vocab, int32_t *argmax, float *logits) {
     return paged_forward(ctx, batch, x, positions, page_table, max_pages, kv_pool, n_pages, head, n_groups,
                          group_vocab, argmax, logits, false);
+}
+
+namespace {
+
+// The per-call scratch of a decode step, pointed at the context's workspace or at the
+// static scratch array.
+struct Work {
+    void *h, *q, *attn, *mlp;
+    float *qkv, *part, *logits, *gpart;
+    int64_t gpart_cap;
+    int4 *plan;
+    int *plan_n, *plan_pages;
+    int work_rows;
+};
+
+Work work_of(const ttsbb_ctx *c) {
+    return Work{c->h, c->q, c->attn, c->mlp, c->qkv, c->part, c->logits, c->gpart, c->gpart_cap,
+                c->plan, c->plan_n, c->plan_pages, c->work_rows};
+}
+
+void set_work(ttsbb_ctx *c, const Work &w) {
+    c->h = w.h; c->q = w.q; c->attn = w.attn; c->mlp = w.mlp;
+    c->qkv = w.qkv; c->part = w.part; c->logits = w.logits; c->gpart = w.gpart; c->gpart_cap = w.gpart_cap;
+    c->plan = w.plan; c->plan_n = w.plan_n; c->plan_pages = w.plan_pages; c->work_rows = w.work_rows;
+}
+
+// Carve the static scratch into a decode step's buffers for STATIC_MAX_BATCH rows of this
+// context's shape; false when they do not fit.
+bool static_work(const ttsbb_ctx *c, Work &w) {
+    const ttsbb_config &g = c->cfg;
+    const size_t R = STATIC_MAX_BATCH, hd_all = (size_t)g.n_heads * g.head_dim;
+    unsigned char *base = reinterpret_cast<unsigned char *>(c->static_scratch);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        void *p = base + off;
+        off += (bytes + 255) / 256 * 256;
+        return p;
+    };
+    w.h = take(R * g.hidden * c->esz);
+    w.q = take(R * hd_all * 4);
+    w.attn = take(R * hd_all * c->esz);
+    w.mlp = take(R * g.ffn * c->esz);
+    w.qkv = reinterpret_cast<float *>(take(R * c->qkv_w * 4));
+    w.part = reinterpret_cast<float *>(take(R * g.n_heads * MAX_CHUNKS * PART_STRIDE * 4));
+    w.logits = reinterpret_cast<float *>(take(R * STATIC_MAX_HEAD_COLS * 4));
+    // only the residual-add products (N = hidden) are split over K on these rows
+    w.gpart_cap = (int64_t)STATIC_GPART_SPLITS * R * g.hidden;
+    w.gpart = reinterpret_cast<float *>(take((size_t)w.gpart_cap * 4));
+    w.plan = reinterpret_cast<int4 *>(take(R * MAX_CHUNKS * sizeof(int4)));
+    w.plan_n = reinterpret_cast<int *>(take(256));
+    w.plan_pages = reinterpret_cast<int *>(take(R * MAX_CHUNKS * 64 * sizeof(int)));
+    w.work_rows = (int)R;
+    return base != nullptr && off <= STATIC_SCRATCH_BYTES;
+}
+
+}  // namespace
+
+TTSBB_API ttsbb_status ttsbb_decode_step_noalloc(ttsbb_ctx *ctx, int32_t batch, float *x, int32_t *positions,
+                                                 const int32_t *page_table, int32_t max_pages, void *kv_pool,
+                                                 int32_t n_pages, const void *head, int32_t n_groups,
+                                                 int32_t group_vocab, int32_t *argmax, float *logits) {
+    if (!ctx) return TTSBB_INVALID_ARG;
+    if (batch > STATIC_MAX_BATCH) return TTSBB_UNSUPPORTED;
+    if (head && (int64_t)n_groups * group_vocab > STATIC_MAX_HEAD_COLS) return TTSBB_UNSUPPORTED;
+    if (!ctx->static_scratch) return TTSBB_DEVICE_ERROR;
+    Work w;
+    if (!static_work(ctx, w)) return TTSBB_UNSUPPORTED;  // this context's shape needs more than the array
+    const Work own = work_of(ctx);
+    set_work(ctx, w);
+    const ttsbb_status st = paged_forward(ctx, batch, x, positions, page_table, max_pages, kv_pool, n_pages, head,
+                                          n_groups, group_vocab, argmax, logits, false);
+    set_work(ctx, own);
+    return st;
 }
 
 TTSBB_API ttsbb_status ttsbb_prefill(ttsbb_ctx *ctx, int32_t n_tokens, float *x, int32_t *cache_len,

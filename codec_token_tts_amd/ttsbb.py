@@ -21,7 +21,7 @@ F32, BF16 = 0, 1
  TAP_X_OUT, TAP_HEAD_IN, TAP_LOGITS, TAP_LOGITS_U) = range(14)
 
 EXPORTS = ["ttsbb_default_config", "ttsbb_create", "ttsbb_destroy", "ttsbb_status_str",
-           "ttsbb_sync", "ttsbb_codebook_embed", "ttsbb_decode_step", "ttsbb_prefill", "ttsbb_maskgit_pass",
+           "ttsbb_sync", "ttsbb_codebook_embed", "ttsbb_decode_step", "ttsbb_decode_step_noalloc", "ttsbb_prefill", "ttsbb_maskgit_pass",
            "ttsbb_maskgit_pass_cfg", "ttsbb_maskgit_step", "ttsbb_rvq_decode", "ttsbb_philox_words", "ttsbb_unmask_schedule", "ttsbb_set_tap_layer", "ttsbb_read_tap", "ttsbb_profile_start",
            "ttsbb_profile_stop"]
 
@@ -84,6 +84,7 @@ def lib() -> C.CDLL:
         "ttsbb_sync": (i32, [vp]),
         "ttsbb_codebook_embed": (i32, [vp, i32, i32, vp, vp, i32, vp, vp, vp, i32, vp]),
         "ttsbb_decode_step": (i32, [vp, i32, vp, vp, vp, i32, vp, i32, vp, i32, i32, vp, vp]),
+        "ttsbb_decode_step_noalloc": (i32, [vp, i32, vp, vp, vp, i32, vp, i32, vp, i32, i32, vp, vp]),
         "ttsbb_prefill": (i32, [vp, i32, vp, vp, vp, i32, vp, i32, vp, i32, i32, vp, vp]),
         "ttsbb_maskgit_pass": (i32, [vp, i32, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, i32, f32,
                                      vp, vp, vp]),
@@ -175,6 +176,17 @@ def ttsbb_decode_step(ctx, batch, x, positions, page_table, max_pages, kv_pool, 
                                  ptr(argmax), ptr(logits))
     if check:
         _check(st, "ttsbb_decode_step")
+    return st
+
+
+def ttsbb_decode_step_noalloc(ctx, batch, x, positions, page_table, max_pages, kv_pool, n_pages,
+                              head=None, n_groups=0, group_vocab=0, argmax=None, logits=None,
+                              check: bool = True) -> int:
+    st = lib().ttsbb_decode_step_noalloc(ctx, batch, ptr(x), ptr(positions), ptr(page_table), max_pages,
+                                         ptr(kv_pool), n_pages, ptr(head), n_groups, group_vocab,
+                                         ptr(argmax), ptr(logits))
+    if check:
+        _check(st, "ttsbb_decode_step_noalloc")
     return st
 
 

@@ -147,6 +147,24 @@ ttsbb_status ttsbb_decode_step(ttsbb_ctx *ctx, int32_t batch, float *x, int32_t 
                                int32_t n_pages, const void *head, int32_t n_groups,
                                int32_t group_vocab, int32_t *argmax, float *logits);
 
+/* ttsbb_decode_step for callers that cannot allocate device memory (code under HIP
+ * graph capture, serving loops and harnesses that forbid hipMalloc): same arguments,
+ * kernels and results, but every per-call scratch buffer of the step (normalised and
+ * projected rows, attention work list and partial sums, split products' partial sums,
+ * the head logits when `logits` is NULL) lives in one static device array of the
+ * library, 32 MiB on each GPU it runs on, held until the process ends, instead of the
+ * context's workspace.  It allocates nothing.  Limits: batch <= 64 streams and
+ * n_groups * group_vocab <= 8200 (TTSBB_UNSUPPORTED beyond; also if the context's shape
+ * needs more scratch than the array holds); with max_pages * kv_page > 4096 its
+ * attention may cut the caches into longer chunks than ttsbb_decode_step does (the same
+ * result up to fp32 rounding order).  Every call of this entry point on one GPU shares
+ * that GPU's array and leaves its contents behind: calls that overlap on one GPU (other
+ * streams, contexts or threads) race. */
+ttsbb_status ttsbb_decode_step_noalloc(ttsbb_ctx *ctx, int32_t batch, float *x, int32_t *positions,
+                                       const int32_t *page_table, int32_t max_pages, void *kv_pool,
+                                       int32_t n_pages, const void *head, int32_t n_groups,
+                                       int32_t group_vocab, int32_t *argmax, float *logits);
+
 /* Causal multi-token prefill of one stream (ncnn Qwen3-TTS port, "单token SDPA问题与host
  * attention": RoPE + KV append + GQA attention per layer; the Talker prompt and the code
  * predictor's two-token start are prefills): n_tokens embedded tokens at positions

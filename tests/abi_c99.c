@@ -44,6 +44,8 @@ int main(void) {
     EXPECT(ttsbb_sync(NULL) == TTSBB_INVALID_ARG);
     EXPECT(ttsbb_codebook_embed(NULL, 1, 1, NULL, NULL, 1, NULL, NULL, NULL, 0, &dummy) == TTSBB_INVALID_ARG);
     EXPECT(ttsbb_decode_step(NULL, 1, &dummy, NULL, NULL, 1, NULL, 1, NULL, 0, 0, NULL, NULL) == TTSBB_INVALID_ARG);
+    EXPECT(ttsbb_decode_step_noalloc(NULL, 1, &dummy, NULL, NULL, 1, NULL, 1, NULL, 0, 0, NULL, NULL) ==
+           TTSBB_INVALID_ARG);
     EXPECT(ttsbb_maskgit_pass(NULL, 0, NULL, NULL, 0, 1, 1, 2, 1, NULL, NULL, NULL, 0, 5.0f, NULL, NULL,
                               NULL) == TTSBB_INVALID_ARG);
     EXPECT(ttsbb_maskgit_pass_cfg(NULL, 0, NULL, NULL, 0, 4, 2, 1, 2, 1, NULL, NULL, NULL, 0, 5.0f, 2.0f, NULL,
