@@ -154,22 +154,19 @@ class MaskgitC4:
 
     def step_sampled(self, s, cfg_scale=2.0, class_temp=1.0, pos_temp=1.0):
         """The general step: guidance plus the sampler (top-k ratio 0.1, class and
-        position temperatures); the Gumbel uniforms are resident inputs."""
+        position temperatures); the Gumbel uniforms are drawn on the device from the
+        library's Philox4x32-10 stream, its counter threaded through the calls."""
         e = self.e
         i = s % e["n_steps"]
         if i == 0:
             self.codes.copy_(self.codes0)
-        if not hasattr(self, "u_class"):
-            from workload import gen
-            self.u_class = self.torch.from_numpy(gen.uniform_open01(
-                3, gen.stream_id(gen.KIND_U_CLASS, 0), (e["n_cb"], e["n_frames"], e["cb_vocab"]))).cuda()
-            self.u_pos = self.torch.from_numpy(gen.uniform_open01(
-                3, gen.stream_id(gen.KIND_U_POS, 0), (e["n_cb"], e["n_frames"]))).cuda()
+        if not hasattr(self, "rng_counter"):
+            self.rng_counter = self.torch.zeros(1, dtype=self.torch.int64, device="cuda")
         self.T.ttsbb_maskgit_step(self.ctx, e["n_text"], self.text_ids, self.text_table, e["text_vocab"],
                                   e["n_frames"], e["n_frames"], e["n_cb"], e["cb_vocab"], e["mask_id"], self.tables,
                                   self.heads, self.codes, self.sched[i], e["layer_penalty"], self.pred, self.conf,
                                   self.picked, cfg_scale=cfg_scale, class_temp=class_temp, pos_temp=pos_temp,
-                                  top_k_ratio=0.1, u_class=self.u_class, u_pos=self.u_pos)
+                                  top_k_ratio=0.1, rng_seed=42, rng_counter=self.rng_counter)
 
     def flops(self):
         """Algorithmic flops of one pass: projections, attention, heads."""
@@ -371,6 +368,60 @@ def run_prefill(T, torch, dec, n_tokens, iters):
     return total / iters
 
 
+def run_c3(T, torch, iters):
+    """The 5-layer code predictor: 256 frames in lockstep, a 1-token prefill of the frame's
+    hidden state at position 0, then 15 q_len = 1 steps, step s embedding code s-1 with
+    table s-1 and choosing code s with head s-1 (greedy, fed back on the device).  One
+    frame batch = those 16 calls (and 15 embeddings); returns ms per frame batch.
+    Roofline (HBM-bound, ~200 flop/B): the 5 layers' bf16 weights (157.3 MB) in each of
+    the 16 calls, the 15 heads (4.2 MB each) and the KV of positions 0..s of every frame
+    and layer (4 KB each) in call s: 3.29 GB, 0.412 ms at 8 TB/s."""
+    from workload import configs as CFG, device as DEV, gen
+    w = CFG.c3()
+    e = w.extra
+    F, steps, V = e["batch"], e["steps"], e["cb_vocab"]
+    ctx, keep = make_ctx(T, torch, w.shape, 5, True, w.seed, F, 64, V, DEV, CFG)
+    try:
+        pt, n_pages = CFG.page_table(w.seed, [16] * F)
+        pool = DEV.kv_pool(w.seed, w.shape, 5, [0] * F, pt, n_pages, True)
+        pt_d = torch.from_numpy(pt).cuda()
+        tabs = [DEV.table(w.seed, gen.KIND_CB_TABLE, s, V, 1024, True) for s in range(steps)]
+        heads = [DEV.table(w.seed, gen.KIND_HEAD, s, V, 1024, True) for s in range(steps)]
+        hidden = torch.from_numpy(gen.fast_normal(w.seed, gen.stream_id(gen.KIND_X_IN, 0), (F, 1024), 1.0)).cuda()
+        c0 = torch.from_numpy(gen.uniform_int(w.seed, gen.stream_id(gen.KIND_CODES, 0), (F,), V)).cuda()
+        pos = torch.zeros(F, dtype=torch.int32, device="cuda")
+        x = torch.empty((F, 1024), dtype=torch.float32, device="cuda")
+        codes = torch.empty((steps + 1, F, 1), dtype=torch.int32, device="cuda")
+
+        def frame_batch():
+            pos.zero_()
+            x.copy_(hidden)
+            codes[0, :, 0] = c0
+            T.ttsbb_decode_step(ctx, F, x, pos, pt_d, 1, pool, n_pages)
+            for s in range(1, steps + 1):
+                T.ttsbb_codebook_embed(ctx, F, 1, codes[s - 1], tabs[s - 1], V, None, None, None, 0, x)
+                T.ttsbb_decode_step(ctx, F, x, pos, pt_d, 1, pool, n_pages, heads[s - 1], 1, V, codes[s])
+
+        frame_batch()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            frame_batch()
+        e1.record()
+        torch.cuda.synchronize()
+        if T.ttsbb_sync(ctx) != T.OK:
+            raise RuntimeError("device flag raised by the code predictor")
+        return e0.elapsed_time(e1) / iters
+    finally:
+        torch.cuda.synchronize()
+        T.ttsbb_destroy(ctx)
+
+
+C3_ROOFLINE_BYTES = (16 * 5 * 15728640 * 2 + 15 * 2048 * 1024 * 2
+                     + sum(s + 1 for s in range(16)) * 256 * 4096 * 5)
+
+
 def run_c2_graph(T, torch, dec, n_steps=148):
     """Batch-1 decode loop of the 16-codebook / 3072-head configuration (28 layers, KV
     1000 -> 1148, codes drawn up front): timed eagerly, then captured once as ONE HIP graph
@@ -519,6 +570,10 @@ def run_c5c4(args, T, torch):
     # Codec RVQ decode of the pass's 750 frames (8 codebooks x 1024 x 64 -> 1024, fp32)
     rvq_us = run_rvq(T, torch, mg.e["n_frames"], args.steps)
 
+    # The 5-layer code predictor: 256 frames x (1-token prefill + 15 steps)
+    log("timed: code predictor")
+    c3_ms = run_c3(T, torch, args.steps)
+
     # Batch-1 decode loop (16 codebooks, 3072 head, KV 1000, 148 steps): eager vs one graph
     c2_eager_ms = c2_graph_ms = None
     if not args.no_graph:
@@ -594,7 +649,12 @@ def run_c5c4(args, T, torch):
         "maskgit_sampled": {"ms_per_pass": round(smp_ms, 4),
                             "frames_per_s": round(mg.e["n_frames"] / (smp_ms * 1e-3 * mg.e["n_steps"]), 1),
                             "note": "guided + sampled step: cfg_scale 2.0, top-k ratio 0.1, class and position "
-                                    "temperature 1.0, Gumbel uniforms resident"},
+                                    "temperature 1.0, Gumbel uniforms drawn on the device (Philox4x32-10)"},
+        "code_predictor": {"ms_per_frame_batch": round(c3_ms, 4), "codes_per_s": round(256 * 15 / (c3_ms * 1e-3), 1),
+                           "roofline_ms": round(C3_ROOFLINE_BYTES / (HBM_PEAK_GBS * 1e9) * 1e3, 4),
+                           "frac_of_roofline": round(C3_ROOFLINE_BYTES / (HBM_PEAK_GBS * 1e9) * 1e3 / c3_ms, 4),
+                           "note": "5 layers, 256 frames: 1-token prefill + 15 steps, 15 tables and 2048-way heads, "
+                                   "argmax fed back on the device; roofline = 3.29 GB of weights, heads and KV at 8 TB/s"},
         "decode_b1_loop": None if c2_graph_ms is None else {
             "eager_ms_per_step": round(c2_eager_ms, 4), "graph_ms_per_step": round(c2_graph_ms, 4),
             "graph_tokens_per_s": round(1.0 / (c2_graph_ms * 1e-3), 1), "steps": 148,

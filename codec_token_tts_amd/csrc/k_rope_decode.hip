@@ -288,18 +288,15 @@ __device__ __forceinline__ void norm_rope_head(const float *x, const float *gain
     }
 }
 
+// One work item (stream, KV head, chunk) of the decode attention, on one wave; returns
+// false when `item` lies past the step's work list.
 template <typename T, int GROUP, bool FUSED>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? (FUSED ? 3 : 4) : 2)))
-void decode_attn_kernel(DecodeAttnArgs a) {
+__device__ __forceinline__ bool decode_attn_item(const DecodeAttnArgs &a, int item) {
     constexpr int EPL = KVRaw<T>::EPL;
     constexpr int LPR = 128 / EPL;  // lanes per 128-dim row
     constexpr int RPL = 64 / LPR;   // rows (tokens) per wave load
     constexpr int NR = 16 / RPL;    // wave loads per 16-token page block
     const int lane = threadIdx.x & 63;
-    // wave-uniform by construction; readfirstlane lets the compiler keep the item's
-    // indices in scalar registers (no per-lane page-id selection loops)
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int item = blockIdx.x * 4 + wave;
     // the step's work list: pair item / Hkv = (stream, chunk, token position); KV heads vary
     // fastest, so the waves of a block stream neighbouring 4 KB blocks of the same pool
     // pages (a page holds all heads' K and V contiguously)
@@ -312,7 +309,7 @@ void decode_attn_kernel(DecodeAttnArgs a) {
     const int n_pairs = *a.plan_n;
     const int4 w = a.plan[pc];
     const int my_page = a.plan_pages[(int64_t)pc * 64 + lane];
-    if (pair >= n_pairs) return;
+    if (pair >= n_pairs) return false;
     const int b = w.x, c = w.y, p_tok = w.z, chunk = w.w;  // p_tok: position of the step's token
     const int p_begin = c * chunk;
     const int pg_first = p_begin / a.page;
@@ -478,6 +475,37 @@ void decode_attn_kernel(DecodeAttnArgs a) {
             part[1] = lt;
         }
     }
+    return true;
+}
+
+// The grid holds as many waves as the work list's budget (target_items, or every chunk
+// the caches could hold when there is no budget); each wave takes items wave, wave +
+// (waves in the grid), ... -- one item per wave when the list fits the budget, so no
+// workgroup is dispatched without work.
+template <typename T, int GROUP, bool FUSED>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? (FUSED ? 3 : 4) : 2)))
+void decode_attn_kernel(DecodeAttnArgs a) {
+    // wave-uniform by construction; readfirstlane lets the compiler keep the item's
+    // indices in scalar registers (no per-lane page-id selection loops)
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    for (int item = blockIdx.x * 4 + wave;; item += gridDim.x * 4)
+        if (!decode_attn_item<T, GROUP, FUSED>(a, item)) break;
+}
+
+// The split of a stream's L cached positions for the step's chunk bound c (a multiple of
+// the page): n = ceil(L / c) items would leave a short remainder item, so the positions
+// are spread evenly instead -- every item holds `len` = ceil(L / n) positions rounded up
+// to a page (at most c), the last one the rest -- and n is recounted from len so that no
+// item is empty.  The work list and the merge both use it, so they agree on the items.
+__device__ __forceinline__ void stream_split(int L, int c, int page, int &n, int &len) {
+    if (L <= 0) {
+        n = 0;
+        len = c;
+        return;
+    }
+    const int n0 = (L + c - 1) / c;
+    len = ((L + n0 - 1) / n0 + page - 1) / page * page;
+    n = (L + len - 1) / len;
 }
 
 // The decode attention's work list, built once per step (the positions are the same in
@@ -526,12 +554,12 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeAttnArgs a, int
     int base = 0;
     for (int b0 = 0; b0 < a.B; b0 += 1024) {
         const int b = b0 + tid;
-        int nc = 0, p_tok = 0;
+        int nc = 0, p_tok = 0, len = chunk;
         if (b < a.B) {
             p_tok = a.shared ? a.pos[0] + b : a.pos[b];
             if (a.flag && (p_tok < 0 || p_tok >= a.max_pos || p_tok >= cap)) raise_flag(a.flag, FLAG_POSITION);
             const int L = min(p_tok + 1, cap);
-            nc = L > 0 ? min((L + chunk - 1) / chunk, a.n_chunks) : 0;
+            stream_split(L, chunk, a.page, nc, len);  // nc <= ceil(L / chunk) <= n_chunks
         }
         int v = nc;  // inclusive scan: inside the wave, then over the waves' totals
 #pragma unroll
@@ -547,7 +575,7 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeAttnArgs a, int
             if (k < wave) off += wsum[k];
             total += wsum[k];
         }
-        for (int c = 0; c < nc; ++c) plan[off + c] = make_int4(b, c, p_tok, chunk);
+        for (int c = 0; c < nc; ++c) plan[off + c] = make_int4(b, c, p_tok, len);
         base = total;
     }
     // page ids of every pair's chunk, one per lane of the attention wave (clamped into the
@@ -620,8 +648,9 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeAttnArgs a) {
     int L = (a.shared ? a.pos[0] + b : a.pos[b]) + 1;
     const int cap = a.max_pages * a.page;
     if (L > cap) L = cap;
-    const int chunk = a.plan_n[1];  // the step's chunk (from the work list)
-    const int nc = min(a.n_chunks, (L + chunk - 1) / chunk);
+    const int chunk = a.plan_n[1];  // the step's chunk bound (from the work list)
+    int nc, len;
+    stream_split(L, chunk, a.page, nc, len);  // the stream's items, as the work list made them
     if (nc <= 0) {  // a token outside the cache (flagged by the plan) has no chunks: zeros
         if (lane < 32) {
             const int k = h * 128 + lane * 4;
@@ -654,7 +683,8 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeAttnArgs a) {
 void launch_decode_attn(const DecodeAttnArgs &a, DType dt, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     if (a.B <= 0) return;
     const int group = a.H / a.Hkv;
-    const int items = a.B * a.Hkv * a.n_chunks;  // at most; the work list holds the real ones
+    int items = a.B * a.Hkv * a.n_chunks;  // at most; the work list holds the real ones
+    if (a.target_items > 0 && a.target_items < items) items = a.target_items;  // the list's budget
     const dim3 grid((items + 3) / 4), block(256);
     auto go = [&](auto kernel) {
         if (ev0 || ev1) hipExtLaunchKernelGGL(kernel, grid, block, 0, s, ev0, ev1, 0, a);

@@ -387,7 +387,7 @@ def run_maskgit(m: Model, n_text, n_frames, n_cb, V, mask_id, n_unmask, seed, ta
 def check_maskgit(res, ref, n_cb, n_frames, V, mask_id, n_unmask, tol=2e-2):
     rec = ref["rec"]
     assert normwise(res["logits"], rec["logits"]) <= tol
-    assert normwise(res["logits"], ref["l_emul"]) <= TOL_EMUL_BF16
+    check_stack("MaskGIT logits", res["logits"], ref["l_emul"], rec["logits"])
     # the stage on the GPU's own head operand: head, pred, conf and picks bit for bit
     _, l_y = check_head_teacher_forced(res["head_in"], ref["head"], res["logits"], res["pred"].T, n_cb, V,
                                        exclude=mask_id)
