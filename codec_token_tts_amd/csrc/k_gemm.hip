@@ -49,6 +49,7 @@ constexpr int BK = 64;
 constexpr int LDK = BK + 8;
 constexpr int EPI_PARTIAL = 3;  // fp32 partial sums of one K split: C + z * M * N
 constexpr int EPI_QKV = 4;      // fused per-head RMSNorm + RoPE + dense q / K / V^T layout
+constexpr int EPI_SCORES = 5;   // per-row, per-group partial log-softmax statistics of the tile
 
 // Tile order: block ids are dealt round-robin to the 8 XCDs, so block b runs on XCD
 // b % 8.  Tiles are renumbered so that each XCD receives a contiguous run of the
@@ -454,6 +455,135 @@ __device__ __forceinline__ void qkv_dense_epilogue(const f32x16_t (&acc)[TM][TN]
     }
 }
 
+// Scoring epilogue of the head product (one 128 x 128 tile; block of 4 waves in 2 x 2).
+// The fp32 tile goes through LDS in two halves of 64 rows; there, column c of a row sits
+// at (c / 32) * 36 + c % 32 of a 144-float row, so that the row's four threads, each
+// reading its 32 consecutive columns as eight 16-byte loads, and the next rows' threads
+// fall in distinct banks.  Each thread reduces, per group of g.gv columns met by the
+// tile (at most two: the tile's first group k0, and k0 + 1 from column `cut` on), the
+// maximum over all classes, the best non-mask class (ties: lowest id) and the sum of
+// exp(y - max); the four threads' statistics merge by lane exchanges, and the row's first
+// thread stores them.
+template <int TM, int TN>
+__device__ __forceinline__ void scores_epilogue(const f32x16_t (&acc)[TM][TN], float *tile, int m0, int n0,
+                                                int tiles_n, const GemmArgs &g) {
+    constexpr int LDT = 144, SEG = 36;
+    const float LOG2E = 1.4426950408889634f;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int V = g.gv, k0 = n0 / V;
+    const int cut = min(128, (k0 + 1) * V - n0);  // tile columns [0, cut) are group k0, the rest k0 + 1
+    const int tn = n0 / 128;
+    const int row = tid >> 2, q = tid & 3;
+    const int cbase = q * 32;                           // this thread's columns [cbase, cbase + 32)
+    const int nvalid = min(32, g.N - n0 - cbase);       // of which those below N (may be <= 0)
+    const int cls0 = n0 + cbase - k0 * V;               // class of column cbase in group k0
+    auto lds_barrier = []() {
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+    };
+    for (int half = 0; half < 2; ++half) {
+        lds_barrier();  // the ring's (or the first half's) last reads are done
+        if (wm == half) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int rr = i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                        tile[rr * LDT + (wn * 2 + j) * SEG + (lane & 31)] = acc[i][j][r];
+                    }
+        }
+        lds_barrier();
+        float v[32];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const float4 t = *reinterpret_cast<const float4 *>(tile + row * LDT + q * SEG + c * 4);
+            v[c * 4] = t.x;
+            v[c * 4 + 1] = t.y;
+            v[c * 4 + 2] = t.z;
+            v[c * 4 + 3] = t.w;
+        }
+        // Per thread: (max, sum of exp relative to it, best non-mask value, its class) of
+        // group k0 over its columns [0, lim0) and of group k0 + 1 over [split, nvalid).
+        // Argmax ties go to the first (lowest) class, as argmax_merge orders them.
+        float mx[2] = {-INFINITY, -INFINITY}, best[2] = {-INFINITY, -INFINITY}, se[2] = {0.f, 0.f};
+        int bi[2] = {0x7FFFFFFF, 0x7FFFFFFF};
+        int z;  // an opaque zero: keeps the per-column masks below from being hoisted out of the loop
+        asm volatile("s_mov_b32 %0, 0" : "=s"(z));
+        const int split = min(32, max(0, cut - cbase)) + z;  // columns [0, split) are group k0
+        const int lim0 = min(split, nvalid);
+        const int g0 = g.gmask - cls0 + z, g1 = g0 + V;       // the mask's column in group k0, k0 + 1
+        const int sg = split == 32 ? 0 : 1;                    // a one-group thread's group
+        const bool simple = nvalid == 32 && (split == 0 || split == 32) && (unsigned)(sg ? g1 : g0) >= 32u;
+        if (__builtin_amdgcn_read_exec() == __ballot(simple)) {
+            // whole wave: all 32 columns valid, in one group, none the mask
+            float m = v[0];
+#pragma unroll
+            for (int i = 1; i < 32; ++i) m = fmaxf(m, v[i]);
+            const float mb = m * LOG2E;
+            float e = 0.f;
+            int idx = 0x7FFFFFFF;
+#pragma unroll
+            for (int i = 31; i >= 0; --i) {
+                e += __builtin_amdgcn_exp2f(v[i] * LOG2E - mb);
+                idx = v[i] == m ? i : idx;
+            }
+            const int cls = idx == 0x7FFFFFFF ? idx : cls0 - sg * V + idx;
+            mx[sg] = m;
+            se[sg] = e;
+            best[sg] = m;
+            bi[sg] = cls;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 32; ++i) {
+                const bool a0 = i < lim0, a1 = (i >= split) & (i < nvalid);
+                const float x0 = a0 ? v[i] : -INFINITY, x1 = a1 ? v[i] : -INFINITY;
+                mx[0] = fmaxf(mx[0], x0);
+                mx[1] = fmaxf(mx[1], x1);
+                const bool u0 = a0 & (i != g0) & ((x0 > best[0]) | ((x0 == best[0]) & (bi[0] == 0x7FFFFFFF)));
+                const bool u1 = a1 & (i != g1) & ((x1 > best[1]) | ((x1 == best[1]) & (bi[1] == 0x7FFFFFFF)));
+                best[0] = u0 ? x0 : best[0];
+                bi[0] = u0 ? cls0 + i : bi[0];
+                best[1] = u1 ? x1 : best[1];
+                bi[1] = u1 ? cls0 + i - V : bi[1];
+            }
+            const float mb0 = mx[0] * LOG2E, mb1 = mx[1] * LOG2E;
+            int z2;  // the masks again from fresh bounds, not kept alive from the first loop
+            asm volatile("s_mov_b32 %0, 0" : "=s"(z2));
+            const int split2 = split + z2, lim2 = lim0 + z2, nv2 = nvalid + z2;
+#pragma unroll
+            for (int i = 0; i < 32; ++i) {
+                const bool a0 = i < lim2, a1 = (i >= split2) & (i < nv2);
+                se[0] += a0 ? __builtin_amdgcn_exp2f(v[i] * LOG2E - mb0) : 0.f;
+                se[1] += a1 ? __builtin_amdgcn_exp2f(v[i] * LOG2E - mb1) : 0.f;
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int o = 1; o <= 2; o <<= 1) {
+                const float m2 = __shfl_xor(mx[s], o, WAVE), s2 = __shfl_xor(se[s], o, WAVE);
+                const float b2 = __shfl_xor(best[s], o, WAVE);
+                const int i2 = __shfl_xor(bi[s], o, WAVE);
+                const float M = fmaxf(mx[s], m2);
+                const float f1 = mx[s] == -INFINITY ? 0.f : exp2f((mx[s] - M) * LOG2E);
+                const float f2 = m2 == -INFINITY ? 0.f : exp2f((m2 - M) * LOG2E);
+                se[s] = se[s] * f1 + s2 * f2;
+                mx[s] = M;
+                argmax_merge(best[s], bi[s], b2, i2);
+            }
+        const int m = m0 + half * 64 + row;
+        if (q == 0 && m < g.M) {
+            float4 *dst = g.spart + ((int64_t)m * tiles_n + tn) * 2;
+            dst[0] = make_float4(mx[0], se[0], best[0], __int_as_float(bi[0]));
+            if (cut < 128) dst[1] = make_float4(mx[1], se[1], best[1], __int_as_float(bi[1]));
+        }
+    }
+}
+
 template <int BM, int BN, int STAGES, int EPI>
 __global__ __launch_bounds__(256) void gemm_lds(GemmArgs g, int k_split, RopeKvArgs rk) {
     constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
@@ -538,6 +668,11 @@ __global__ __launch_bounds__(256) void gemm_lds(GemmArgs g, int k_split, RopeKvA
     if constexpr (EPI == EPI_QKV) {
         static_assert(BM == 128 && BN == 128, "one tile = 128 tokens x one head");
         qkv_dense_epilogue<TM, TN>(acc, reinterpret_cast<float *>(smem), m0, n0, g.M, rk);
+        return;
+    }
+    if constexpr (EPI == EPI_SCORES) {
+        static_assert(BM == 128 && BN == 128 && STAGES * TILE * 2 >= 64 * 144 * 4, "64-row halves staged");
+        scores_epilogue<TM, TN>(acc, reinterpret_cast<float *>(smem), m0, n0, tiles_n, g);
         return;
     }
     const int rb0 = m0 + wm * WM + (lane >> 5) * 4, cb0 = n0 + wn * WN + (lane & 31);
@@ -1064,6 +1199,13 @@ static int choose_splits(const GemmArgs &g, int tiles, int64_t part_cap) {
            (int64_t)(splits * 2) * g.M * g.N <= part_cap)
         splits *= 2;
     return splits;
+}
+
+bool launch_head_scores(const GemmArgs &g, hipStream_t s) {
+    if (g.M <= 64 || g.K % 64 != 0 || g.gv < 128 || !g.spart) return false;
+    const int tiles = ((g.M + 127) / 128) * ((g.N + 127) / 128);
+    hipLaunchKernelGGL((gemm_lds<128, 128, 2, EPI_SCORES>), dim3(tiles), dim3(256), 0, s, g, g.K, RopeKvArgs{});
+    return true;
 }
 
 bool launch_qkv_dense(const GemmArgs &g, const RopeKvArgs &rk, hipStream_t s) {

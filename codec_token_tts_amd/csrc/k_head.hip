@@ -111,6 +111,60 @@ void launch_maskgit_scores(const float *logits, const float *logits_u, float cfg
                        T, ld, n_cb, V, mask_id, penalty, codes, codes_ld, pred, conf, flag);
 }
 
+// K8 from the head's partial statistics (launch_head_scores): 16 lanes per (codebook,
+// frame), lane l taking the statistics of tiles j0 + l, j0 + l + 16, ... of the 128-column
+// tiles its group meets; they merge by lane exchanges (max, rescaled sum of exp, best
+// class with ties to the lowest id), then the scores of maskgit_scores_kernel.
+__global__ __launch_bounds__(256) void maskgit_merge_kernel(const float4 *spart, int T, int N, int n_cb, int V,
+                                                            int mask_id, float penalty, const int32_t *codes,
+                                                            int codes_ld, int32_t *pred, float *conf, int *flag) {
+    const int item = blockIdx.x * 16 + (threadIdx.x >> 4);  // flat index k*T + t
+    const int l = threadIdx.x & 15;
+    if (item >= n_cb * T) return;  // whole 16-lane groups leave together
+    const int k = item / T, t = item % T;
+    const int tiles_n = (N + 127) / 128;
+    const int j0 = (k * V) / 128, j1 = (k * V + V - 1) / 128;
+    const float LOG2E = 1.4426950408889634f;
+    float M = -INFINITY, S = 0.f, best = -INFINITY;
+    int bi = 0x7FFFFFFF;
+    for (int j = j0 + l; j <= j1; j += 16) {
+        const int s = k - (j * 128) / V;  // this group's slot in tile j (0 or 1)
+        const float4 p = spart[((int64_t)t * tiles_n + j) * 2 + s];
+        const float M2 = fmaxf(M, p.x);
+        const float f1 = M == -INFINITY ? 0.f : exp2f((M - M2) * LOG2E);
+        const float f2 = p.x == -INFINITY ? 0.f : exp2f((p.x - M2) * LOG2E);
+        S = S * f1 + p.y * f2;
+        M = M2;
+        argmax_merge(best, bi, p.z, __float_as_int(p.w));
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+        const float M2 = __shfl_xor(M, o, WAVE), S2 = __shfl_xor(S, o, WAVE);
+        const float b2 = __shfl_xor(best, o, WAVE);
+        const int i2 = __shfl_xor(bi, o, WAVE);
+        const float Mx = fmaxf(M, M2);
+        const float f1 = M == -INFINITY ? 0.f : exp2f((M - Mx) * LOG2E);
+        const float f2 = M2 == -INFINITY ? 0.f : exp2f((M2 - Mx) * LOG2E);
+        S = S * f1 + S2 * f2;
+        M = Mx;
+        argmax_merge(best, bi, b2, i2);
+    }
+    if (l != 0) return;
+    const bool ok = S >= 1.f && S < INFINITY && bi != 0x7FFFFFFF;
+    if (!ok) raise_flag(flag, FLAG_NONFINITE);
+    const float lse = M + logf(S);
+    pred[item] = ok ? bi : invalid_group_class(mask_id);
+    conf[item] = (ok && codes[(int64_t)k * codes_ld + t] == mask_id) ? (best - lse) - (float)k * penalty : -INFINITY;
+}
+
+void launch_maskgit_merge(const float4 *spart, int T, int N, int n_cb, int V, int mask_id, float penalty,
+                          const int32_t *codes, int codes_ld, int32_t *pred, float *conf, int *flag, hipStream_t s) {
+    const int items = n_cb * T;
+    if (items <= 0) return;
+    hipLaunchKernelGGL(maskgit_merge_kernel, dim3((items + 15) / 16), dim3(256), 0, s, spart, T, N, n_cb, V, mask_id,
+                       penalty, codes, codes_ld, pred, conf, flag);
+}
+
 // ------------------------------------------------------------------------------------
 // The sampler's random stream (OmniVoice ARCHITECTURE, "MaskGIT decoder", Determinism: a
 // seedable Philox4x32-10 generator whose counter is threaded across calls).
@@ -290,42 +344,47 @@ void launch_maskgit_sample(const float *logits, const float *logits_u, float cfg
                        u_pos, seed, counter, pred, conf, flag);
 }
 
-constexpr int SEL_TILE = 1024;  // scores staged in LDS per block
+constexpr int SEL_TILE = 256;  // scores staged in LDS per block
 
-__global__ void zero_i32_kernel(int32_t *v, int n) {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) v[i] = 0;
+// Order key of score c at flat index i: larger key = earlier in the selection order
+// (higher score; equal scores: lower index).  A score's bits are mapped to an unsigned
+// value that orders like the float (sign bit set for >= 0, all bits flipped below 0),
+// and the index fills the low word reversed.  Scores are never NaN; every key exceeds 0.
+__device__ __forceinline__ uint64_t select_key(float c, int i) {
+    const uint32_t b = __float_as_uint(c);
+    const uint32_t o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    return ((uint64_t)o << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
 }
 
-// rank[i] += #{j in this block's tile : conf[j] > conf[i] or (== and j < i)}
+// rank[i] += #{j in this block's tile of SEL_TILE scores : key(j) > key(i)}.  rank holds
+// zeros on entry (the scatter of the previous call, or the context's creation, left it so).
 __global__ __launch_bounds__(256) void rank_count_kernel(const float *conf, int n, int32_t *rank) {
-    __shared__ __attribute__((aligned(16))) float tile[SEL_TILE];
+    __shared__ __attribute__((aligned(16))) uint64_t tile[SEL_TILE];
     const int i = blockIdx.x * 256 + threadIdx.x;
     const int j0 = blockIdx.y * SEL_TILE;
-    const int cnt = min(SEL_TILE, n - j0);
-    for (int j = threadIdx.x; j < SEL_TILE; j += 256) tile[j] = j < cnt ? conf[j0 + j] : -INFINITY;
+    const int j = j0 + threadIdx.x;
+    tile[threadIdx.x] = j < n ? select_key(conf[j], j) : 0;  // 0: below every key
     __syncthreads();
     if (i >= n) return;
-    const float ci = conf[i];
-    int r = 0;
-    const int lim = i - j0;  // tile positions j < lim have a lower flat index than i
-    for (int j = 0; j < cnt; j += 4) {
-        const float4 c = *reinterpret_cast<const float4 *>(&tile[j]);
-        r += (c.x > ci) || (c.x == ci && j < lim);
-        r += (c.y > ci) || (c.y == ci && j + 1 < lim);
-        r += (c.z > ci) || (c.z == ci && j + 2 < lim);
-        r += (c.w > ci) || (c.w == ci && j + 3 < lim);
+    const uint64_t ki = select_key(conf[i], i);
+    int r0 = 0, r1 = 0;
+#pragma unroll 8
+    for (int jj = 0; jj < SEL_TILE; jj += 2) {
+        r0 += tile[jj] > ki;
+        r1 += tile[jj + 1] > ki;
     }
-    // positions past cnt hold -inf: they can only tie with a -inf score, and such a
-    // position has a higher index than every real one, so they never count
+    const int r = r0 + r1;
     if (r) atomicAdd(&rank[i], r);
 }
 
-__global__ void select_scatter_kernel(const float *conf, const int32_t *pred, const int32_t *rank, int n, int T,
+// picked[rank] = i and the code update for the n_unmask best scores (-1 for a rank whose
+// score is -inf); every rank entry is read once and set back to zero for the next call.
+__global__ void select_scatter_kernel(const float *conf, const int32_t *pred, int32_t *rank, int n, int T,
                                       int n_unmask, int32_t *codes, int codes_ld, int32_t *picked) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
     const int r = rank[i];
+    rank[i] = 0;
     if (r >= n_unmask) return;
     if (conf[i] > -INFINITY) {
         picked[r] = i;
@@ -340,7 +399,6 @@ void launch_select_update(const float *conf, const int32_t *pred, int n_cb, int 
     const int n = n_cb * T;
     if (n <= 0 || n_unmask <= 0) return;
     const int blocks = (n + 255) / 256;
-    hipLaunchKernelGGL(zero_i32_kernel, dim3(blocks), dim3(256), 0, s, rank, n);
     hipLaunchKernelGGL(rank_count_kernel, dim3(blocks, (n + SEL_TILE - 1) / SEL_TILE), dim3(256), 0, s, conf,
                        n, rank);
     hipLaunchKernelGGL(select_scatter_kernel, dim3(blocks), dim3(256), 0, s, conf, pred, rank, n, T, n_unmask,

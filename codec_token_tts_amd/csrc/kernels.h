@@ -71,6 +71,9 @@ struct GemmArgs {
     // are in the fragment-major layout of frag_index() with that many 16-row tiles (the
     // kernel's own: 1, 2 or 4) instead of row-major
     int a_mt, c_mt;
+    // launch_head_scores only: groups of gv columns (a head of gv classes per group)
+    int gv, gmask;
+    float4 *spart;
 };
 // part: fp32 workspace of part_cap floats for split-K partial sums.  Returns the number
 // of K splits whose partial sums are left in part[z][M][N] for the caller to add (an
@@ -80,6 +83,16 @@ int launch_gemm(const GemmArgs &g, DType dt, float *part, int64_t part_cap, hipS
 // 16-row tiles (1, 2 or 4) of the skinny kernel that a bf16 product of this shape runs on,
 // or 0 when it runs elsewhere (the fragment-major layout is only for that kernel)
 int skinny_tiles(const GemmArgs &g, int64_t part_cap);
+
+// Head product + MaskGIT scoring statistics (bf16, M > 64, K % 64 == 0): the logits
+// Y = A W^T are never stored; for every row m and every 128-column tile j, each group of
+// g.gv columns that meets the tile gets its partial statistics over the tile's columns
+//   spart[(m * ceil(N / 128) + j) * 2 + s] = (max over all classes, sum of exp(y - max),
+//                                             best class value, its class id as int bits)
+// with s = group - (first group of the tile), s in {0, 1} (a group of >= 128 columns
+// meets a tile in at most two groups); the best excludes class g.gmask (ties: lowest id).
+// Returns false (nothing launched) when the shape is not taken.
+bool launch_head_scores(const GemmArgs &g, hipStream_t s);
 
 // ---- K4: per-head RMSNorm + RoPE + K/V write --------------------------------------
 // qkv fp32 [M][(H + 2 Hkv) * 128].  Decode mode (dense == 0): row m is stream m at
@@ -187,6 +200,12 @@ void launch_maskgit_scores(const float *logits, const float *logits_u, float cfg
                            int n_cb, int V, int mask_id, float penalty, const int32_t *codes, int codes_ld,
                            int32_t *pred, float *conf, int *flag, hipStream_t s);
 
+// The same scores from the head's partial statistics (launch_head_scores, ld = the head
+// width N): the group's tiles are merged in tile order into max, sum of exp, best class.
+void launch_maskgit_merge(const float4 *spart, int T, int N, int n_cb, int V, int mask_id, float penalty,
+                          const int32_t *codes, int codes_ld, int32_t *pred, float *conf, int *flag,
+                          hipStream_t s);
+
 // With the sampler: class_temp > 0 keeps the k_keep best log-probs of each group and
 // adds Gumbel noise from u_class [n_cb][T][V]; pos_temp > 0 adds noise from u_pos
 // [n_cb][T] to the score.  A NULL array draws its uniforms from Philox4x32-10 (key
@@ -203,7 +222,7 @@ void launch_rng_words(uint64_t seed, uint64_t block0, uint32_t w2, uint32_t w3, 
 void launch_advance_counter(uint64_t *ctr, uint64_t n, hipStream_t s);
 
 // ---- K9: top-n selection by rank + code update -------------------------------------
-// rank: int32 scratch [n]
+// rank: int32 scratch [n], all zero on entry, left all zero (the context zeroes it once)
 // Top-n over conf [n_cb][T] (flat k*T + t); picked codes go to codes[k*codes_ld + t].
 void launch_select_update(const float *conf, const int32_t *pred, int n_cb, int T, int n_unmask,
                           int32_t *rank, int32_t *codes, int codes_ld, int32_t *picked, hipStream_t s);

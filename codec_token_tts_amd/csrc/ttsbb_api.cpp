@@ -75,6 +75,7 @@ struct ttsbb_ctx {
     float *part = nullptr;
     float *logits = nullptr;
     float *logits_u = nullptr;  // unconditional logits of a guided MaskGIT step
+    float4 *spart = nullptr;    // head-product scoring statistics [rows][128-column tiles][2]
     int32_t *rank = nullptr;
     int rank_cap = 0;
     float *gpart = nullptr;   // split-K partial sums
@@ -291,6 +292,7 @@ TTSBB_API ttsbb_status ttsbb_create(const ttsbb_config *cfg, const ttsbb_layer *
               dev_alloc(c, (void **)&c->part, R * g.n_heads * MAX_CHUNKS * PART_STRIDE * 4) &&
               dev_alloc(c, (void **)&c->logits, R * (size_t)(g.max_head_cols > 0 ? g.max_head_cols : 1) * 4) &&
               dev_alloc(c, (void **)&c->logits_u, R * (size_t)(g.max_head_cols > 0 ? g.max_head_cols : 1) * 4) &&
+              dev_alloc(c, (void **)&c->spart, R * (size_t)((g.max_head_cols + 127) / 128 + 1) * 2 * sizeof(float4)) &&
               dev_alloc(c, (void **)&c->rank, (size_t)R * (g.max_head_cols / 2 + 1) * 4) &&
               dev_alloc(c, (void **)&c->gpart, (size_t)c->gpart_cap * 4) &&
               dev_alloc(c, (void **)&c->rope, (size_t)g.max_pos * 64 * sizeof(float2)) &&
@@ -305,10 +307,12 @@ TTSBB_API ttsbb_status ttsbb_create(const ttsbb_config *cfg, const ttsbb_layer *
         return TTSBB_OOM;
     }
     // Padding keys of the MaskGIT K/V buffers must hold finite values (they meet a zero
-    // probability); zero them once here.
+    // probability), and the selection's rank counters must start from zero (every
+    // selection leaves them zero again): zero them once here.
     ok = hipMemset(c->kbuf, 0, (size_t)g.n_kv_heads * c->s_pad_cap * g.head_dim * 2) == hipSuccess &&
          hipMemset(c->vtbuf, 0, (size_t)g.n_kv_heads * c->s_pad_cap * g.head_dim * 2) == hipSuccess &&
-         hipMemset(c->flag, 0, 256) == hipSuccess;
+         hipMemset(c->flag, 0, 256) == hipSuccess &&
+         hipMemset(c->rank, 0, (size_t)R * (g.max_head_cols / 2 + 1) * 4) == hipSuccess;
     // RoPE table: angle p * theta^(-2j/d) in double precision, rounded to fp32.
     std::vector<float2> tab((size_t)g.max_pos * 64);
     for (int p = 0; p < g.max_pos; ++p)
@@ -712,6 +716,51 @@ void maskgit_head(ttsbb_ctx *ctx, int row0, int n_out, const void *heads, int N,
     head_gemm(ctx, heads, n_out, N, logits, N);
 }
 
+// Unguided MaskGIT scores of rows [row0, row0 + n_out) (frames of the window, codes
+// window[k * codes_ld + t]) straight from the head product: the final RMSNorm, the head
+// GEMM with the scoring epilogue (logits never stored) and the merge into pred, conf.
+// With taps on, the logits are also materialized by the plain head product for the
+// logits tap.  Returns false (nothing launched) for a shape the fused head does not take
+// (n_out <= 64, a codebook narrower than one 128-column tile).
+bool maskgit_head_scores(ttsbb_ctx *ctx, int row0, int n_out, const void *heads, int n_cb, int V, int mask_id,
+                         float penalty, const int32_t *window, int codes_ld, int32_t *pred, float *conf) {
+    const ttsbb_config &g = ctx->cfg;
+    const int N = n_cb * V;
+    if (n_out <= 64 || V < 128 || g.hidden % 64 != 0) return false;
+    {
+        KScope k(ctx, TTSBB_K_RMSNORM);
+        launch_rmsnorm(ctx->x + (size_t)row0 * g.hidden, g.hidden, n_out, g.hidden, ctx->final_norm, g.rms_eps,
+                       ctx->h, DT_BF16, ctx->stream);
+    }
+    if (ctx->tap_layer >= 0) {
+        tap_dense(ctx, TTSBB_TAP_HEAD_IN, ctx->h, DT_BF16, n_out, g.hidden, g.hidden);
+        head_gemm(ctx, heads, n_out, N, ctx->logits, N);
+        tap_dense(ctx, TTSBB_TAP_LOGITS, ctx->logits, DT_F32, n_out, N, N);
+    }
+    GemmArgs a = {};
+    a.A = ctx->h;
+    a.lda = g.hidden;
+    a.M = n_out;
+    a.K = g.hidden;
+    a.N = N;
+    a.w.p[0] = heads;
+    a.w.start[0] = 0;
+    a.w.start[1] = N;
+    a.w.nseg = 1;
+    a.epi = EPI_STORE;
+    a.gv = V;
+    a.gmask = mask_id;
+    a.spart = ctx->spart;
+    {
+        KScope k(ctx, TTSBB_K_GEMM_HEAD);
+        if (!launch_head_scores(a, ctx->stream)) return false;  // excluded above: never taken
+    }
+    KScope k(ctx, TTSBB_K_SCORES);
+    launch_maskgit_merge(ctx->spart, n_out, N, n_cb, V, mask_id, penalty, window, codes_ld, pred, conf, ctx->flag,
+                         ctx->stream);
+    return true;
+}
+
 // One sequence of S rows: layers, then the heads of rows [row0, row0 + n_out).
 void maskgit_backbone(ttsbb_ctx *ctx, int S, int row0, int n_out, const void *heads, int N, float *logits,
                       bool taps) {
@@ -1024,9 +1073,11 @@ TTSBB_API ttsbb_status ttsbb_maskgit_pass(ttsbb_ctx *ctx, int32_t n_text, const 
     const int S = n_text + n_frames;
     const int N = n_cb * cb_vocab;
     maskgit_embed(ctx, S, n_text, text_ids, text_table, text_vocab, n_cb, cb_vocab, audio_tables, codes, n_frames);
-    maskgit_backbone(ctx, S, n_text, n_frames, audio_heads, N, ctx->logits, true);
-    if (ctx->tap_layer >= 0) tap_dense(ctx, TTSBB_TAP_LOGITS, ctx->logits, DT_F32, n_frames, N, N);
-    {
+    maskgit_layers(ctx, S, 0, S, 0, true);
+    if (!maskgit_head_scores(ctx, n_text, n_frames, audio_heads, n_cb, cb_vocab, mask_id, layer_penalty, codes,
+                             n_frames, pred, conf)) {
+        maskgit_head(ctx, n_text, n_frames, audio_heads, N, ctx->logits, true);
+        if (ctx->tap_layer >= 0) tap_dense(ctx, TTSBB_TAP_LOGITS, ctx->logits, DT_F32, n_frames, N, N);
         KScope k(ctx, TTSBB_K_SCORES);
         launch_maskgit_scores(ctx->logits, nullptr, 0.f, n_frames, N, n_cb, cb_vocab, mask_id, layer_penalty, codes,
                               n_frames, pred, conf, ctx->flag, ctx->stream);
@@ -1108,6 +1159,8 @@ TTSBB_API ttsbb_status ttsbb_maskgit_step(ttsbb_ctx *ctx, const ttsbb_maskgit_st
     const int N = n_cb * cb_vocab;
     int32_t *window = a->codes + w0;
     const float *lu = nullptr;
+    const bool sampled = a->class_temp > 0.f || a->pos_temp > 0.f;
+    bool scored = false;  // pred and conf already written by the fused head
     if (a->cfg_scale != 0.f) {
         maskgit_guided(ctx, n_text, a->text_ids, a->text_table, a->text_vocab, n_frames, n_target, n_cb, cb_vocab,
                        a->audio_tables, a->audio_heads, a->codes);
@@ -1115,12 +1168,17 @@ TTSBB_API ttsbb_status ttsbb_maskgit_step(ttsbb_ctx *ctx, const ttsbb_maskgit_st
     } else {
         maskgit_embed(ctx, S, n_text, a->text_ids, a->text_table, a->text_vocab, n_cb, cb_vocab, a->audio_tables,
                       a->codes, n_frames);
-        maskgit_backbone(ctx, S, n_text + w0, n_target, a->audio_heads, N, ctx->logits, true);
-        if (ctx->tap_layer >= 0) tap_dense(ctx, TTSBB_TAP_LOGITS, ctx->logits, DT_F32, n_target, N, N);
+        maskgit_layers(ctx, S, 0, S, 0, true);
+        scored = !sampled && maskgit_head_scores(ctx, n_text + w0, n_target, a->audio_heads, n_cb, cb_vocab, mask_id,
+                                                 a->layer_penalty, window, n_frames, a->pred, a->conf);
+        if (!scored) {
+            maskgit_head(ctx, n_text + w0, n_target, a->audio_heads, N, ctx->logits, true);
+            if (ctx->tap_layer >= 0) tap_dense(ctx, TTSBB_TAP_LOGITS, ctx->logits, DT_F32, n_target, N, N);
+        }
     }
-    {
+    if (!scored) {
         KScope k(ctx, TTSBB_K_SCORES);
-        if (a->class_temp > 0.f || a->pos_temp > 0.f) {
+        if (sampled) {
             const int k_keep = std::max(1, (int)floor((double)a->top_k_ratio * cb_vocab));
             launch_maskgit_sample(ctx->logits, lu, a->cfg_scale, n_target, N, n_cb, cb_vocab, mask_id,
                                   a->layer_penalty, window, n_frames, a->class_temp, a->pos_temp, k_keep, a->u_class,

@@ -21,7 +21,7 @@ from workload import gen
 from workload.gen import stream_id
 
 import bf16_emulation as E
-from gpu_setup import (TOL_EMUL_BF16, TOL_LAYER_BF16, Model, check_argmax_groups, check_head_teacher_forced,
+from gpu_setup import (BOUNDARY_FRAC, TOL_EMUL_BF16, TOL_LAYER_BF16, Model, check_argmax_groups, check_head_teacher_forced,
                        check_sampler, check_scores_teacher_forced, check_stack, check_topn, dims_of, normwise,
                        read_tap, torch, widen)
 
@@ -384,7 +384,7 @@ def run_maskgit(m: Model, n_text, n_frames, n_cb, V, mask_id, n_unmask, seed, ta
     return res, ref
 
 
-def check_maskgit(res, ref, n_cb, n_frames, V, mask_id, n_unmask, tol=2e-2):
+def check_maskgit(res, ref, n_cb, n_frames, V, mask_id, n_unmask, tol=2e-2, topn_near=BOUNDARY_FRAC):
     rec = ref["rec"]
     assert normwise(res["logits"], rec["logits"]) <= tol
     check_stack("MaskGIT logits", res["logits"], ref["l_emul"], rec["logits"])
@@ -402,7 +402,7 @@ def check_maskgit(res, ref, n_cb, n_frames, V, mask_id, n_unmask, tol=2e-2):
     assert np.array_equal(np.isfinite(res["conf"]), fin)
     delta = np.max(np.abs(res["logits"] - ref["l_emul"]))
     assert np.max(np.abs(res["conf"][fin] - conf_e[fin])) <= 2 * delta + 1e-5
-    check_topn(res["picked"], res["conf"], conf_e, n_unmask)
+    check_topn(res["picked"], res["conf"], conf_e, n_unmask, max_near=topn_near)
     # the update writes pred at the picked positions and nothing else
     assert np.array_equal(res["codes"], O.apply_picks(ref["codes_in"], res["pred"], res["picked"]))
 
@@ -906,6 +906,68 @@ def test_maskgit_workload_shape_one_layer():
         res, ref = run_maskgit(m, 200, 750, 8, 1025, 1024, 4, w.seed, tap_layer=0)
         check_maskgit(res, ref, 8, 750, 1025, 1024, 4)
         check_attention_teacher_forced(res["taps"], 950, 16, 8)
+    finally:
+        m.close()
+
+
+# ---------------------------------------------------------------------------------------
+# The fused head (windows of more than 64 frames, codebooks of >= 128 classes): scores
+# from the head product's per-tile statistics, logits never stored
+# ---------------------------------------------------------------------------------------
+@pytest.mark.parametrize("n_frames,n_cb,V,mask", [(65, 3, 128, 5), (200, 2, 129, 0), (130, 4, 300, 299),
+                                                  (257, 1, 1025, 1024), (100, 8, 1025, 512)])
+def test_maskgit_fused_head_scores(n_frames, n_cb, V, mask):
+    """Codebooks exactly one 128-column tile wide, one column over (a tile holding two
+    codebooks at every boundary), several tiles per codebook with a ragged last one, the
+    mask class first, last and inside; ragged 128-row tiles.  pred is the argmax of the
+    GPU's own (tapped) logits bit for bit, and pred, conf and the picks hold on the
+    oracle's logits of the GPU's head operand.  (With no layers the class distributions
+    are nearly uniform, so the best scores of all frames lie within the GPU-to-emulation
+    distance of each other: the boundary count of the free-running pick check is not
+    capped; the teacher-forced check pins the picks exactly.)"""
+    m = Model(CFG.Shape(n_layers=0), 0, True, seed=41, gains="random")
+    try:
+        n = max(1, n_cb * n_frames // 3)
+        res, ref = run_maskgit(m, 7, n_frames, n_cb, V, mask, n, 41)
+        check_maskgit(res, ref, n_cb, n_frames, V, mask, n, tol=1e-2, topn_near=None)
+    finally:
+        m.close()
+
+
+@pytest.mark.parametrize("mask", [0, 200])
+def test_maskgit_fused_head_ties_and_nonfinite(mask):
+    """Codebook 0: every class has the same head row, so all its logits are equal: the
+    choice is the lowest class that is not the mask (the tie crosses lanes and tiles) and
+    the score is -log(V) exactly up to fp32 rounding.  Codebook 1: NaN head rows: the
+    lowest non-mask class, score -inf, the device flag.  Codebook 2: ordinary."""
+    m = Model(CFG.Shape(n_layers=0), 0, True, seed=43)
+    T = m.T
+    try:
+        n_frames, n_cb, V, n = 90, 3, 260, 40
+        tab_h = CFG.table(43, gen.KIND_CB_TABLE, 0, n_cb * V, 1024, True)
+        head_h = CFG.table(43, gen.KIND_HEAD, 0, n_cb * V, 1024, True)
+        head_h[:V] = head_h[3]
+        head_h[V:2 * V] = 0x7FC0  # bf16 quiet NaN
+        codes = gen.uniform_int(43, stream_id(gen.KIND_CODES, 0), (n_cb, n_frames), V - 1)
+        codes[codes == mask] = (mask + 1) % V
+        codes[:, ::2] = mask
+        cd = t_i32(codes)
+        pred = torch().empty((n_cb, n_frames), dtype=torch().int32, device="cuda")
+        conf = torch().empty((n_cb, n_frames), dtype=torch().float32, device="cuda")
+        picked = torch().empty(n, dtype=torch().int32, device="cuda")
+        T.ttsbb_maskgit_pass(m.ctx, 0, None, None, 0, n_frames, n_cb, V, mask, DEV.host_to_device(tab_h),
+                             DEV.host_to_device(head_h), cd, n, 0.0, pred, conf, picked)
+        assert T.ttsbb_sync(m.ctx) == T.DEVICE_ERROR
+        assert T.ttsbb_sync(m.ctx) == T.OK
+        p, c, pk = pred.cpu().numpy(), conf.cpu().numpy(), picked.cpu().numpy()
+        low = 1 if mask == 0 else 0
+        assert np.all(p[0] == low) and np.all(p[1] == low)
+        masked0 = codes[0] == mask
+        assert np.all(np.abs(c[0][masked0] + np.log(V)) <= 1e-5)
+        assert np.all(c[0][~masked0] == -np.inf) and np.all(c[1] == -np.inf)
+        assert np.array_equal(np.isfinite(c[2]), codes[2] == mask)
+        assert np.array_equal(pk, O.select_top(c.reshape(-1), n))
+        assert np.array_equal(cd.cpu().numpy(), O.apply_picks(codes, p, pk))
     finally:
         m.close()
 
