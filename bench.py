@@ -21,7 +21,8 @@ batch-1 decode loop (16 x 2048 codebooks, 3072 head, KV 1000, 148 steps) run eag
 one captured HIP graph.  The other workloads (batch-1 decode, the 5-layer code predictor,
 the single fp32 layer) are parity-test cases.
 
-    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-graph] [--copy-calibration MIB]
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-graph] [--no-extras]
+                    [--copy-calibration MIB]
 """
 from __future__ import annotations
 
@@ -542,6 +543,15 @@ def run_c5c4(args, T, torch):
     pd = T.ttsbb_profile_stop(dec.ctx)
     pm = T.ttsbb_profile_stop(mg.ctx)
 
+    extras = {}
+    if not args.no_extras:
+        extras = run_extras(args, T, torch, dec, mg)
+    return assemble(args, dec, mg, dec_ms, mg_ms, wall, timed_attn, pd, pm, extras)
+
+
+def run_extras(args, T, torch, dec, mg):
+    """The figures beside the headline workload: guided and sampled MaskGIT steps, the
+    causal prefill, the RVQ decode, the code predictor and the batch-1 decode loop."""
     # Guided MaskGIT step (classifier-free guidance), timed on its own after the step
     log("timed: %d guided MaskGIT steps" % args.steps)
     mg.step_cfg(0)
@@ -579,7 +589,36 @@ def run_c5c4(args, T, torch):
     if not args.no_graph:
         log("timed: batch-1 decode loop, eager and as one HIP graph")
         c2_eager_ms, c2_graph_ms = run_c2_graph(T, torch, dec)
+    return {
+        "maskgit_cfg": {"ms_per_pass": round(cfg_ms, 4),
+                        "frames_per_s": round(mg.e["n_frames"] / (cfg_ms * 1e-3 * mg.e["n_steps"]), 1),
+                        "note": "guided step: conditional 950-token prompt + unconditional 750-frame window, "
+                                "cfg_scale 2.0"},
+        "prefill": {"ms_per_call": round(pf_ms, 4), "tokens": 200,
+                    "tokens_per_s": round(200 / (pf_ms * 1e-3), 1),
+                    "note": "causal prefill of one stream's 200-token prompt into fresh pages, 28 layers, "
+                            "head + argmax on the last token"},
+        "rvq_decode": {"us_per_call": round(rvq_us, 2), "frames": mg.e["n_frames"],
+                       "gflops_fp32": round(2.0 * mg.e["n_frames"] * 8 * 64 * 1024 / (rvq_us * 1e-6) / 1e9, 1),
+                       "note": "codec RVQ decode, 8 x (1024 x 64) codebooks -> 1024, fp32"},
+        "maskgit_sampled": {"ms_per_pass": round(smp_ms, 4),
+                            "frames_per_s": round(mg.e["n_frames"] / (smp_ms * 1e-3 * mg.e["n_steps"]), 1),
+                            "note": "guided + sampled step: cfg_scale 2.0, top-k ratio 0.1, class and position "
+                                    "temperature 1.0, Gumbel uniforms drawn on the device (Philox4x32-10)"},
+        "code_predictor": {"ms_per_frame_batch": round(c3_ms, 4), "codes_per_s": round(256 * 15 / (c3_ms * 1e-3), 1),
+                           "roofline_ms": round(C3_ROOFLINE_BYTES / (HBM_PEAK_GBS * 1e9) * 1e3, 4),
+                           "frac_of_roofline": round(C3_ROOFLINE_BYTES / (HBM_PEAK_GBS * 1e9) * 1e3 / c3_ms, 4),
+                           "note": "5 layers, 256 frames: 1-token prefill + 15 steps, 15 tables and 2048-way heads, "
+                                   "argmax fed back on the device; roofline = 3.29 GB of weights, heads and KV at 8 TB/s"},
+        "decode_b1_loop": None if c2_graph_ms is None else {
+            "eager_ms_per_step": round(c2_eager_ms, 4), "graph_ms_per_step": round(c2_graph_ms, 4),
+            "graph_tokens_per_s": round(1.0 / (c2_graph_ms * 1e-3), 1), "steps": 148,
+            "note": "batch-1 28-layer decode, 16 x 2048 summed codebooks, 3072 head + argmax, "
+                    "KV 1000 -> 1148: eager launches vs the 148 steps captured as one HIP graph"},
+    }
 
+
+def assemble(args, dec, mg, dec_ms, mg_ms, wall, timed_attn, pd, pm, extras):
     attn_ms, attn_n = timed_attn
     attn_avg_ms = attn_ms / max(1, attn_n)
     attn_bytes = dec.attn_bytes(args.warmup, args.steps)
@@ -635,31 +674,6 @@ def run_c5c4(args, T, torch):
                     "mfma_util": round(mfma_tflops / BF16_PEAK_TFLOPS, 4),
                     "kernels": mg_kernels,
                     "embed_gbs": round(mg_embed_bytes / (mg_embed_ms * 1e-3) / 1e9, 1) if mg_embed_ms else None},
-        "maskgit_cfg": {"ms_per_pass": round(cfg_ms, 4),
-                        "frames_per_s": round(mg.e["n_frames"] / (cfg_ms * 1e-3 * mg.e["n_steps"]), 1),
-                        "note": "guided step: conditional 950-token prompt + unconditional 750-frame window, "
-                                "cfg_scale 2.0"},
-        "prefill": {"ms_per_call": round(pf_ms, 4), "tokens": 200,
-                    "tokens_per_s": round(200 / (pf_ms * 1e-3), 1),
-                    "note": "causal prefill of one stream's 200-token prompt into fresh pages, 28 layers, "
-                            "head + argmax on the last token"},
-        "rvq_decode": {"us_per_call": round(rvq_us, 2), "frames": mg.e["n_frames"],
-                       "gflops_fp32": round(2.0 * mg.e["n_frames"] * 8 * 64 * 1024 / (rvq_us * 1e-6) / 1e9, 1),
-                       "note": "codec RVQ decode, 8 x (1024 x 64) codebooks -> 1024, fp32"},
-        "maskgit_sampled": {"ms_per_pass": round(smp_ms, 4),
-                            "frames_per_s": round(mg.e["n_frames"] / (smp_ms * 1e-3 * mg.e["n_steps"]), 1),
-                            "note": "guided + sampled step: cfg_scale 2.0, top-k ratio 0.1, class and position "
-                                    "temperature 1.0, Gumbel uniforms drawn on the device (Philox4x32-10)"},
-        "code_predictor": {"ms_per_frame_batch": round(c3_ms, 4), "codes_per_s": round(256 * 15 / (c3_ms * 1e-3), 1),
-                           "roofline_ms": round(C3_ROOFLINE_BYTES / (HBM_PEAK_GBS * 1e9) * 1e3, 4),
-                           "frac_of_roofline": round(C3_ROOFLINE_BYTES / (HBM_PEAK_GBS * 1e9) * 1e3 / c3_ms, 4),
-                           "note": "5 layers, 256 frames: 1-token prefill + 15 steps, 15 tables and 2048-way heads, "
-                                   "argmax fed back on the device; roofline = 3.29 GB of weights, heads and KV at 8 TB/s"},
-        "decode_b1_loop": None if c2_graph_ms is None else {
-            "eager_ms_per_step": round(c2_eager_ms, 4), "graph_ms_per_step": round(c2_graph_ms, 4),
-            "graph_tokens_per_s": round(1.0 / (c2_graph_ms * 1e-3), 1), "steps": 148,
-            "note": "batch-1 28-layer decode, 16 x 2048 summed codebooks, 3072 head + argmax, "
-                    "KV 1000 -> 1148: eager launches vs the 148 steps captured as one HIP graph"},
         "roofline": {"kernel": "decode_attn (split-sequence paged GQA attention)", "bound": "hbm",
                      "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
@@ -669,6 +683,7 @@ def run_c5c4(args, T, torch):
             "decode": {k: round(v[0] / args.steps, 4) for k, v in pd.items() if v[1]},
             "maskgit": {k: round(v[0] / args.steps, 4) for k, v in pm.items() if v[1]}},
     }
+    res.update(extras)
     return res
 
 
@@ -684,6 +699,8 @@ def main():
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the graph-captured batch-1 loop (hardware-counter runs: the profiler's "
                          "per-dispatch counter collection does not support stream capture)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time only the headline workload (decode step + MaskGIT pass): for counter runs")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="run one plain copy of MIB MiB first (counter calibration)")
     args = ap.parse_args()

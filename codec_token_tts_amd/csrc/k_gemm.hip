@@ -605,20 +605,27 @@ __global__ __launch_bounds__(256) void gemm_lds(GemmArgs g, int k_split, RopeKvA
     const int KT = min(k_split, g.K - k_begin) / 64;
 
     // Lane sources: instruction c of this wave covers tile rows (wave*I + c)*8 .. +7;
-    // lane i lands in LDS chunk i of that 1 KB, i.e. row +i/8, physical chunk i%8, and
-    // fetches logical chunk (i%8) ^ (i/8) of its row.
-    const int lrow = lane >> 3, lchunk = (lane & 7) ^ (lane >> 3);
+    // lane i lands in LDS chunk i of that 1 KB, i.e. row r = +i/8, physical chunk i%8, and
+    // fetches logical chunk (i%8) ^ ((r / 2) % 8) of its row.  A row is 128 bytes, half of
+    // the 64 four-byte banks, and a 16-byte fragment read serves 16 lanes (rows fr..fr+15)
+    // per cycle: with the swizzle taken from row bits 1..3 (rows of one parity share a half
+    // of the banks), those 16 rows' chunks fall in 16 distinct bank quads.  (I is even, so
+    // (r / 2) % 8 = 4 (c % 2) + (i / 8) / 2.)
+    const int lrow = lane >> 3;
     const bf16_t *A = reinterpret_cast<const bf16_t *>(g.A);
     const bf16_t *asrc[AI];
     const bf16_t *bsrc[BI];
+    static_assert(AI % 2 == 0 && BI % 2 == 0, "swizzle assumes an even number of 8-row blocks per wave");
 #pragma unroll
     for (int c = 0; c < AI; ++c) {
         const int r = (wave * AI + c) * 8 + lrow;
+        const int lchunk = (lane & 7) ^ (((c & 1) << 2) | (lrow >> 1));
         asrc[c] = A + (int64_t)min(m0 + r, g.M - 1) * g.lda + k_begin + lchunk * 8;  // rows past M: unstored
     }
 #pragma unroll
     for (int c = 0; c < BI; ++c) {
         const int r = (wave * BI + c) * 8 + lrow;
+        const int lchunk = (lane & 7) ^ (((c & 1) << 2) | (lrow >> 1));
         // split partials come only from residual-add products: plain row order
         bsrc[c] = wrow32<bf16_t>(g.w, EPI == EPI_SWIGLU ? EPI_SWIGLU : EPI_STORE, min(n0 + r, g.N - 1), g.K) +
                   k_begin + lchunk * 8;
@@ -636,7 +643,7 @@ __global__ __launch_bounds__(256) void gemm_lds(GemmArgs g, int k_split, RopeKvA
     for (int s = 0; s < STAGES - 1; ++s)
         if (s < KT) lds_issue<BM, AI, BI>(asrc, bsrc, smem + s * TILE, wave, s);
 
-    const int fr = lane & 31, fh = lane >> 5, sw = lane & 7;
+    const int fr = lane & 31, fh = lane >> 5, sw = (lane >> 1) & 7;  // (fr / 2) % 8: the row's swizzle
     for (int kt = 0; kt < KT; ++kt) {
         // this wave's DMA of tile kt is done once at most (tiles issued after it) x LPS
         // operations are outstanding
@@ -650,19 +657,30 @@ __global__ __launch_bounds__(256) void gemm_lds(GemmArgs g, int k_split, RopeKvA
 
         const bf16_t *sa = smem + (kt % STAGES) * TILE + (wm * WM) * 64 + fr * 64;
         const bf16_t *sb = smem + (kt % STAGES) * TILE + BM * 64 + (wn * WN) * 64 + fr * 64;
-        // fragments of step ks+1 are read while the products of step ks run
-        bf16x8_t af[2][TM], bfr[2][TN];
-        lds_frags<TM, TN>(sa, sb, ((0 + fh) ^ sw) * 8, af[0], bfr[0]);
+        // All four 16-deep steps' fragments in registers of their own, read in two halves:
+        // the second half's reads go out between the first half's products, so the LDS
+        // latency is waited for once per 64-deep step instead of once per 16.
+        bf16x8_t af[4][TM], bfr[4][TN];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const int cur = ks & 1;
-            if (ks < 3) lds_frags<TM, TN>(sa, sb, ((ks * 2 + 2 + fh) ^ sw) * 8, af[cur ^ 1], bfr[cur ^ 1]);
+        for (int ks = 0; ks < 2; ++ks) lds_frags<TM, TN>(sa, sb, ((ks * 2 + fh) ^ sw) * 8, af[ks], bfr[ks]);
+#pragma unroll
+        for (int ks = 2; ks < 4; ++ks) lds_frags<TM, TN>(sa, sb, ((ks * 2 + fh) ^ sw) * 8, af[ks], bfr[ks]);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
                 for (int j = 0; j < TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfr[cur][j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks][i], bfr[ks][j], acc[i][j], 0, 0, 0);
+        constexpr int NR = 2 * (TM + TN), NP = 2 * TM * TN, NI = NR < NP ? NR : NP;
+        __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);  // reads of steps 0, 1
+#pragma unroll
+        for (int q = 0; q < NI; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // a product of steps 0, 1
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // a read of steps 2, 3
         }
+        if (NR > NI) __builtin_amdgcn_sched_group_barrier(0x100, NR - NI, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 4 * TM * TN - NI, 0);  // the rest
     }
 
     if constexpr (EPI == EPI_QKV) {
