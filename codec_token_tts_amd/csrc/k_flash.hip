@@ -22,7 +22,10 @@
 // Every quarter runs the same number of iterations (a quarter past its last block
 // processes masked copies) so that the block barriers match; at the end quarters 1-3
 // hand their (max, sum, O^T) to quarter 0 through LDS, which merges the four
-// online-softmax states in quarter order and stores.  Scores are scaled by
+// online-softmax states in quarter order and stores.  The causal form (the prefill:
+// query row i at position p0 + i sees keys 0..p0 + i, over the stream's whole sequence
+// gathered from the paged pool) is the same loop over the keys below the tile's last
+// query, with the keys past each query masked.  Scores are scaled by
 // log2(e)/sqrt(128) inside the exponent (one FMA) and exponentiated with v_exp_f32;
 // the running reference max is raised lazily (see the loop).
 #include <math.h>
@@ -101,7 +104,14 @@ __global__ __launch_bounds__(512) void flash_kernel(FlashArgs a) {
     const bf16_t *vg = a.vt + (int64_t)hk * 128 * a.s_pad;
     // the keys of the tile's sequence: [kb, ke) (a tile never straddles two sequences)
     const bool second = a.seg1 > 0 && q0 >= a.seg1;
-    const int kb = second ? a.seg1 : 0, ke = kb + (second ? a.len1 : a.len0);
+    // causal: query row i is at position p0 + i and sees keys [0, p0 + i]; the tile needs
+    // keys below p0 + q0 + 32, and every query of it sees the keys below p0 + q0 + 1
+    const bool causal = a.causal_pos != nullptr;
+    const int p0 = causal ? min(max(a.causal_pos[0], 0), a.s_pad - a.S) : 0;
+    const int kb = second ? a.seg1 : 0;
+    const int ke = causal ? min(p0 + a.S, p0 + q0 + 32) : kb + (second ? a.len1 : a.len0);
+    const int k_all = causal ? min(ke, p0 + q0 + 1) : ke;  // keys below: unmasked for the whole tile
+    const int q_pos = p0 + q0 + fq;                           // this lane's query position (causal)
     const int NB = (ke - kb + FB - 1) / FB, NBQ = (NB + 3) / 4;
     const int kb_first = qq * NBQ, nb_mine = max(0, min(NBQ, NB - kb_first));
     // iteration i works on block blk(i); past this quarter's blocks it re-reads a valid
@@ -156,11 +166,11 @@ __global__ __launch_bounds__(512) void flash_kernel(FlashArgs a) {
                 vfr[dt][kk] = *reinterpret_cast<const bf16x8_t *>(&sv[(dt * 32 + fq) * LDVF + kk * 16 + h * 8]);
             }
         // mask keys past the sequence (and the blocks of a finished quarter): only partial blocks
-        if (!(valid && kbase + FB <= ke)) {
+        if (!(valid && kbase + FB <= k_all)) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int key = kbase + (r >> 3) * 16 + h * 8 + (r & 7);
-                if (!(valid && key < ke)) s[r] = -INFINITY;
+                if (!(valid && key < ke && (!causal || key <= q_pos))) s[r] = -INFINITY;
             }
         }
         float mx = s[0];

@@ -98,7 +98,7 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(RopeKvArgs a) {
                 x2 = x1 * cs.x + x0 * cs.y;
             }
             if (j < a.H) {
-                if (a.dense) {
+                if (a.dense || a.q_bf16) {
                     bf16_t *q = reinterpret_cast<bf16_t *>(a.q_out) + (int64_t)m * a.H * 128 + j * 128;
                     q[lane] = f32_to_bf16(x);
                     q[lane + 64] = f32_to_bf16(x2);
@@ -143,6 +143,50 @@ __global__ __launch_bounds__(256) void dense_vt_kernel(RopeKvArgs a) {
         const int d = i >> 6, t = i & 63;
         if (t0 + t < a.M) vt[(int64_t)d * a.s_pad + t0 + t] = f32_to_bf16(tile[t][d]);
     }
+}
+
+// One stream's paged K/V -> dense K rows and V^T (bf16): block (x, h) takes the 64-position
+// groups x, x + gridDim.x, ... of KV head h below p0 + n_new; K rows are copied in 16-byte
+// chunks, V goes through LDS so that the transposed writes (64 positions = 128 bytes per
+// dim row) are coalesced.
+__global__ __launch_bounds__(256) void pool_dense_kernel(PoolDenseArgs a) {
+    __shared__ uint16_t tile[64][128 + 8];
+    const int h = blockIdx.y;
+    const int p0 = min(max(a.pos0[0], 0), a.s_pad - a.n_new);
+    const int n_keys = p0 + a.n_new;
+    const uint16_t *pool = reinterpret_cast<const uint16_t *>(a.pool_layer);
+    for (int t0 = blockIdx.x * 64; t0 < n_keys; t0 += gridDim.x * 64) {
+        // 64 rows x 16 chunks of 16 bytes: 4 per thread, for K and for V
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int idx = threadIdx.x + 256 * c, t = idx >> 4, ch = idx & 15, p = t0 + t;
+            u32x4_t kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+            if (p < n_keys) {
+                const int pi = p / a.page;
+                const int pg = pi < a.max_pages ? a.page_table[pi] : -1;
+                if (pg >= 0 && pg < a.n_pages) {
+                    const int64_t base = (((int64_t)pg * 2 * a.Hkv + h) * a.page + p % a.page) * 128 + ch * 8;
+                    kv = *reinterpret_cast<const u32x4_t *>(pool + base);
+                    vv = *reinterpret_cast<const u32x4_t *>(pool + base + (int64_t)a.Hkv * a.page * 128);
+                }
+                *reinterpret_cast<u32x4_t *>(a.kbuf + ((int64_t)h * a.s_pad + p) * 128 + ch * 8) = kv;
+            }
+            *reinterpret_cast<u32x4_t *>(&tile[t][ch * 8]) = vv;
+        }
+        __syncthreads();
+        uint16_t *vt = a.vtbuf + (int64_t)h * 128 * a.s_pad;
+        for (int i = threadIdx.x; i < 128 * 64; i += 256) {
+            const int d = i >> 6, t = i & 63;
+            if (t0 + t < n_keys) vt[(int64_t)d * a.s_pad + t0 + t] = tile[t][d];
+        }
+        __syncthreads();
+    }
+}
+
+void launch_pool_dense(const PoolDenseArgs &a, hipStream_t s) {
+    if (a.n_new <= 0 || a.n_new > a.s_pad) return;
+    const int groups = min(32, (a.s_pad + 63) / 64);
+    hipLaunchKernelGGL(pool_dense_kernel, dim3(groups, a.Hkv), dim3(256), 0, s, a);
 }
 
 void launch_rope_kv(const RopeKvArgs &a, DType kv_dt, hipStream_t s) {

@@ -118,12 +118,28 @@ struct RopeKvArgs {
     int shared;          // decode mode, prefill of one stream: row m is at position pos[0] + m
                          // and every row uses page-table row 0
     int seg1;            // dense mode, two sequences: rows m >= seg1 > 0 are at position m - seg1
+    int q_bf16;          // decode mode: q_out gets bf16 rows (as in dense mode) instead of fp32
 };
 void launch_rope_kv(const RopeKvArgs &a, DType kv_dt, hipStream_t s);
 // Dense mode fused into the q/k/v projection (g: EPI_STORE product of N = (H + 2 Hkv) *
 // 128 columns): writes q_out / kbuf / vtbuf directly, qkv is not written.  Returns
 // false (nothing launched) when the shape is not taken by the fused kernel (M <= 64).
 bool launch_qkv_dense(const GemmArgs &g, const RopeKvArgs &rk, hipStream_t s);
+
+// Bulk read of one stream's paged K/V into the dense MaskGIT-layout buffers: positions
+// [0, pos0[0] + n_new) of page-table row 0 go to kbuf [Hkv][s_pad][128] (rows) and vtbuf
+// [Hkv][128][s_pad] (transposed), bf16.  pos0 is read on the device and clamped to
+// [0, s_pad - n_new]; a position whose page id is out of range reads as zeros.
+struct PoolDenseArgs {
+    const void *pool_layer;  // [n_pages][2][Hkv][page][128] bf16
+    const int32_t *page_table;
+    int max_pages, n_pages, page, Hkv;
+    const int32_t *pos0;
+    int n_new;
+    uint16_t *kbuf, *vtbuf;
+    int s_pad;
+};
+void launch_pool_dense(const PoolDenseArgs &a, hipStream_t s);
 
 // ---- K5: split-sequence decode attention over the paged pool -----------------------
 struct DecodeAttnArgs {
@@ -182,6 +198,9 @@ struct FlashArgs {
     // attend to keys [0, len0), rows [seg1, seg1 + len1) to keys [seg1, seg1 + len1); rows
     // between len0 and seg1 are padding.  seg1 == 0: one sequence, len0 = S.
     int seg1, len0, len1;
+    // Causal (non-null, seg1 == 0): row i is at position p0 + i, p0 = causal_pos[0] read on
+    // the device and clamped to [0, s_pad - S]; it attends to keys [0, p0 + i].
+    const int32_t *causal_pos;
 };
 void launch_flash_attn(const FlashArgs &a, hipStream_t s);
 

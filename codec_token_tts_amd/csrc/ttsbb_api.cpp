@@ -277,7 +277,8 @@ TTSBB_API ttsbb_status ttsbb_create(const ttsbb_config *cfg, const ttsbb_layer *
 
     const size_t R = (size_t)g.max_rows;
     const size_t hd_all = (size_t)g.n_heads * g.head_dim;
-    c->s_pad_cap = round_up(g.max_rows, 64);
+    // dense K / V^T rows: a MaskGIT pass (max_rows) or a prefilled stream (max_pos)
+    c->s_pad_cap = round_up(g.max_rows > g.max_pos ? g.max_rows : g.max_pos, 64);
     c->rank_cap = g.max_rows * (g.max_head_cols / 2 + 1);
     c->gpart_cap = (int64_t)16 << 20;  // 64 MB of split-K partials
     const size_t RA = R < 64 ? 64 : R;  // activation rows: a fragment-major layout spans 4 x 16
@@ -681,7 +682,7 @@ void maskgit_layers(ttsbb_ctx *ctx, int M, int seg1, int len0, int len1, bool ta
             tap(ctx, TTSBB_TAP_V, ctx->vtbuf, DT_BF16, M, Hkv * hd, 1, (int64_t)hd * s_pad, s_pad, hd);
         }
 
-        FlashArgs f;
+        FlashArgs f = {};
         f.q = reinterpret_cast<const uint16_t *>(ctx->q);
         f.k = ctx->kbuf;
         f.vt = ctx->vtbuf;
@@ -826,6 +827,86 @@ static ttsbb_status paged_forward(ttsbb_ctx *ctx, int32_t batch, float *x, int32
     const int H = g.n_heads, Hkv = g.n_kv_heads, hd = g.head_dim;
     const int hd_all = H * hd;
     const size_t layer_elems = (size_t)n_pages * 2 * Hkv * g.kv_page * hd;
+
+    // A prefill of more than 64 tokens (bf16, untapped) runs its attention as the causal
+    // flash kernel over the stream's whole sequence, read from the pool into the dense
+    // K / V^T buffers (sized for max_pos positions); shorter ones, and tapped runs, go
+    // through the decode attention, each token over its prefix.
+    if (prefill && batch > 64 && ctx->dt == DT_BF16 && ctx->tap_layer < 0 && g.n_layers > 0 &&
+        batch <= ctx->s_pad_cap) {
+        for (int l = 0; l < g.n_layers; ++l) {
+            const ttsbb_layer &L = ctx->layers[l];
+            qkv_projection(ctx, L, x, batch, false);
+            void *pool_l = reinterpret_cast<char *>(kv_pool) + (size_t)l * layer_elems * ctx->esz;
+            RopeKvArgs r = {};
+            r.qkv = ctx->qkv;
+            r.M = batch;
+            r.H = H;
+            r.Hkv = Hkv;
+            r.q_gain = L.q_norm;
+            r.k_gain = L.k_norm;
+            r.eps = g.rms_eps;
+            r.rope = ctx->rope;
+            r.max_pos = g.max_pos;
+            r.q_out = ctx->q;
+            r.q_bf16 = 1;
+            r.pos = positions;
+            r.page_table = page_table;
+            r.max_pages = max_pages;
+            r.n_pages = n_pages;
+            r.page = g.kv_page;
+            r.pool_layer = pool_l;
+            r.flag = ctx->flag;
+            r.shared = 1;
+            {
+                KScope k(ctx, TTSBB_K_ROPE_KV);
+                launch_rope_kv(r, ctx->dt, ctx->stream);
+                PoolDenseArgs pd = {};
+                pd.pool_layer = pool_l;
+                pd.page_table = page_table;
+                pd.max_pages = max_pages;
+                pd.n_pages = n_pages;
+                pd.page = g.kv_page;
+                pd.Hkv = Hkv;
+                pd.pos0 = positions;
+                pd.n_new = batch;
+                pd.kbuf = ctx->kbuf;
+                pd.vtbuf = ctx->vtbuf;
+                pd.s_pad = ctx->s_pad_cap;
+                launch_pool_dense(pd, ctx->stream);
+            }
+            FlashArgs f = {};
+            f.q = reinterpret_cast<const uint16_t *>(ctx->q);
+            f.k = ctx->kbuf;
+            f.vt = ctx->vtbuf;
+            f.S = batch;
+            f.s_pad = ctx->s_pad_cap;
+            f.H = H;
+            f.Hkv = Hkv;
+            f.scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
+            f.out = reinterpret_cast<uint16_t *>(ctx->attn);
+            f.len0 = batch;
+            f.causal_pos = positions;
+            {
+                KScope k(ctx, TTSBB_K_FLASH_ATTN);
+                launch_flash_attn(f, ctx->stream);
+            }
+            post_attention(ctx, L, x, batch, false);
+        }
+        if (!head) flush_residual(ctx, x, batch);
+        if (head) {
+            const int N = n_groups * group_vocab;
+            const bool fold = gemv_rows_fold(ctx, 1);
+            if (fold) flush_residual(ctx, x, batch);
+            else norm_rows(ctx, x, batch, ctx->final_norm);
+            float *lg = logits ? logits : ctx->logits;
+            head_gemm(ctx, head, 1, N, lg, N, batch - 1, fold ? x : nullptr);
+            KScope k(ctx, TTSBB_K_ARGMAX);
+            launch_argmax_groups(lg, 1, N, n_groups, group_vocab, argmax, ctx->flag, ctx->stream);
+        }
+        launch_increment(positions, 1, ctx->stream, batch);
+        return launch_failed() ? TTSBB_DEVICE_ERROR : TTSBB_OK;
+    }
 
     // Split of each stream's positions into chunks for the decode attention: 128
     // positions per wave (measured best on the paged workload), halved while there are

@@ -174,7 +174,11 @@ ttsbb_status ttsbb_decode_step_noalloc(ttsbb_ctx *ctx, int32_t batch, float *x, 
  * prefix and the tokens before it).  x [n_tokens][hidden] fp32 is the embedded input and
  * the final residual stream on return; cache_len int32 [1] is advanced by n_tokens on the
  * device.  With head != NULL the final norm + head + argmax run on the last token only
- * (argmax [n_groups], logits [n_groups*group_vocab] if not NULL).  n_tokens <= max_rows. */
+ * (argmax [n_groups], logits [n_groups*group_vocab] if not NULL).  n_tokens <= max_rows.
+ * bf16 contexts run a prefill of more than 64 tokens (no layer tapped) with the causal
+ * form of the MaskGIT attention kernel over the stream's positions 0 .. cache_len[0] +
+ * n_tokens - 1 read back from the pool (bf16 q and attention weights, as that kernel
+ * keeps them); shorter ones attend token by token with the decode attention. */
 ttsbb_status ttsbb_prefill(ttsbb_ctx *ctx, int32_t n_tokens, float *x, int32_t *cache_len,
                            const int32_t *page_table, int32_t max_pages, void *kv_pool, int32_t n_pages,
                            const void *head, int32_t n_groups, int32_t group_vocab, int32_t *argmax,

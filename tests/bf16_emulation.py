@@ -23,7 +23,9 @@ softmax statistics in fp32):
 * in the MaskGIT attention, each probability weight that multiplies V, taken relative to
   the running reference maximum of the kernel's online softmax (``flash_attention``);
   the normaliser sums the unrounded weights.
-The decode attention keeps q and its weights in fp32 (no rounding there).
+The decode attention keeps q and its weights in fp32 (no rounding there).  A prefill of
+more than 64 tokens runs on the causal form of the MaskGIT attention kernel: bf16 q and
+weights as there (``prefill``).
 Values are rounded as the GPU does: the fp64 value to fp32, then to bf16 by round to
 nearest even.
 """
@@ -139,6 +141,86 @@ def flash_attention(Q, K, V, round_p: bool = True, quarters: int = 4, block: int
         o = (pw * carry) @ V[:, kv]
         out[:, h] = (o / l[:, None])[:S]
     return out
+
+
+def flash_attention_causal(Q, K, V, p0: int, round_p: bool = True, quarters: int = 4, block: int = 32,
+                           tile: int = 32, lazy: float = 8.0) -> np.ndarray:
+    """The causal form of the same kernel (the prefill): query row i is at position p0 + i
+    and sees keys [0, p0 + i] of K, V [p0 + S][Hkv][d].  Each tile of ``tile`` queries
+    takes the keys below p0 + (first query) + tile in blocks of ``block``, dealt to the
+    quarters as above (so the quarters' ranges depend on the tile); keys a query must not
+    see get the score -inf before the block maximum.  In exact arithmetic (round_p False)
+    this is plain causal softmax attention."""
+    Q, K, V = (np.asarray(a, np.float64) for a in (Q, K, V))
+    S, H, d = Q.shape
+    group = H // K.shape[1]
+    c = np.log2(np.e) / np.sqrt(d)
+    out = np.empty((S, H, d))
+    for t0 in range(0, S, tile):
+        rows = np.arange(t0, min(S, t0 + tile))
+        qrows = np.minimum(np.arange(t0, t0 + tile), S - 1)   # past the sequence: copies of the last
+        ke = min(p0 + S, p0 + t0 + tile)
+        NB = (ke + block - 1) // block
+        NBQ = (NB + quarters - 1) // quarters
+        keys = np.arange(ke)
+        visible = keys[None, :] <= (p0 + np.arange(t0, t0 + tile))[:, None]   # [tile][ke]
+        for h in range(H):
+            kv = h // group
+            s = np.where(visible, (Q[qrows, h] @ K[:ke, kv].T) * c, -np.inf)
+            ref = np.full((tile, ke), -np.inf)
+            m_fin = np.full((tile, quarters), -np.inf)
+            for qq in range(quarters):
+                first = qq * NBQ
+                m = np.full(tile, -np.inf)
+                for i in range(max(0, min(NBQ, NB - first))):
+                    k0 = (first + i) * block
+                    k1 = min(ke, k0 + block)
+                    mx = s[:, k0:k1].max(axis=1)
+                    if np.any(mx > m + lazy):
+                        m = np.maximum(m, mx)
+                    ref[:, k0:k1] = m[:, None]
+                m_fin[:, qq] = m
+            M = m_fin.max(axis=1, keepdims=True)     # quarter 0 holds key 0: finite
+            with np.errstate(invalid="ignore"):
+                p = np.where(visible, np.exp2(s - ref), 0.0)
+                carry = np.where(np.isfinite(ref), np.exp2(ref - M), 0.0)
+            l = np.sum(p * carry, axis=1)
+            pw = r16(p) if round_p else p
+            o = (pw * carry) @ V[:ke, kv]
+            out[rows, h] = (o / l[:, None])[:len(rows)]
+    return out
+
+
+def prefill(x, p0: int, cache: O.KVCache, stream: int, layers: List[O.Layer], dims: O.Dims,
+            round_p: bool = True) -> np.ndarray:
+    """A prefill of more than 64 tokens on the causal flash path: tokens at positions
+    p0 .. p0 + S - 1 after the cached prefix of `stream` (bf16 values), with q, the new K
+    and V, the attention output, the norms' outputs and the SwiGLU output rounded to
+    bf16, and the attention accumulated as flash_attention_causal.  Appends the new K, V
+    to the cache."""
+    x = np.asarray(x, np.float64)
+    S = x.shape[0]
+    pos = (p0 + np.arange(S, dtype=np.float64)).reshape(S, 1)
+    for li, L in enumerate(layers):
+        h = r16(O.rms_norm(x, L.attn_norm, dims.eps))
+        q = (h @ L.wq.T).reshape(S, dims.n_heads, dims.head_dim)
+        k = (h @ L.wk.T).reshape(S, dims.n_kv_heads, dims.head_dim)
+        v = (h @ L.wv.T).reshape(S, dims.n_kv_heads, dims.head_dim)
+        q = r16(O.rope(O.rms_norm(q, L.q_norm, dims.eps), pos, dims.theta))
+        k = r16(O.rope(O.rms_norm(k, L.k_norm, dims.eps), pos, dims.theta))
+        v = r16(v)
+        if cache.length(li, stream) != p0:
+            raise ValueError("cache length %d, prefill position %d" % (cache.length(li, stream), p0))
+        kp, vp = cache.k[li][stream], cache.v[li][stream]
+        K = k if kp is None else np.concatenate([kp, k], axis=0)
+        Vv = v if vp is None else np.concatenate([vp, v], axis=0)
+        cache.set(li, stream, K, Vv)
+        o = r16(flash_attention_causal(q, K, Vv, p0, round_p=round_p).reshape(S, -1))
+        x1 = x + o @ L.wo.T
+        h2 = r16(O.rms_norm(x1, L.ffn_norm, dims.eps))
+        m = r16(O.silu(h2 @ L.w_gate.T) * (h2 @ L.w_up.T))
+        x = x1 + m @ L.w_down.T
+    return x
 
 
 def backbone_full(x, layers: List[O.Layer], dims: O.Dims, record_layer: Optional[int] = None,

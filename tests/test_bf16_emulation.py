@@ -80,6 +80,35 @@ def test_emulation_without_roundings_is_the_oracle(monkeypatch):
     ref = O.backbone_full(x, layers, dims)
     got = E.backbone_full(x, layers, dims, round_p=False)
     assert np.max(np.abs(got - ref)) <= 1e-12 * np.max(np.abs(ref))
+    # a prefill on the causal flash path, after a 37-position prefix
+    caches = [O.KVCache(2, 1), O.KVCache(2, 1)]
+    for l in range(2):
+        kp, vp = rng.normal(size=(37, 2, 16)), rng.normal(size=(37, 2, 16))
+        for c in caches:
+            c.set(l, 0, kp, vp)
+    x = rng.normal(size=(75, 64))
+    ref = O.prefill(x, 37, caches[0], 0, layers, dims)
+    got = E.prefill(x, 37, caches[1], 0, layers, dims, round_p=False)
+    assert np.max(np.abs(got - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+@pytest.mark.parametrize("p0,S", [(0, 1), (0, 33), (5, 70), (37, 130), (64, 32)])
+def test_causal_flash_model_is_causal_attention_in_exact_arithmetic(p0, S):
+    """The prefill's attention model: each query i (position p0 + i) against the oracle's
+    attention of one token over keys 0..p0 + i; wide score ranges make the tiles raise
+    their references, and tiles see different numbers of key blocks."""
+    rng = np.random.default_rng(p0 * 1000 + S)
+    H, Hkv, d = 4, 2, 16
+    Q = rng.normal(size=(S, H, d)) * 3.0
+    K = rng.normal(size=(p0 + S, Hkv, d)) * 3.0
+    V = rng.normal(size=(p0 + S, Hkv, d))
+    ref = np.stack([O.attend(Q[i], K[:p0 + i + 1], V[:p0 + i + 1]) for i in range(S)])
+    got = E.flash_attention_causal(Q, K, V, p0, round_p=False)
+    assert np.max(np.abs(got - ref)) <= 1e-12 * np.max(np.abs(ref))
+    got16 = E.flash_attention_causal(Q, K, V, p0, round_p=True)
+    assert nw(got16, ref) <= 2.0 ** -7
+    if p0 + S > 1:  # (one key: its weight is exactly 1)
+        assert nw(got16, ref) > 0
 
 
 def test_r16_is_round_to_nearest_even():

@@ -738,11 +738,15 @@ def test_rvq_decode(n_frames, n_q, cb, dim, out_dim):
 # ---------------------------------------------------------------------------------------
 # Causal prefill of one stream into its paged cache
 # ---------------------------------------------------------------------------------------
-@pytest.mark.parametrize("p0,S", [(0, 5), (21, 37), (0, 100), (300, 64)])
+@pytest.mark.parametrize("p0,S", [(0, 5), (21, 37), (300, 64), (0, 100), (37, 130), (0, 200), (500, 512)])
 def test_prefill_bf16(p0, S):
     """bf16, 2 layers: the prompt's final residual stream, the K/V it leaves in the pool at
     positions p0..p0+S-1, the advanced cache length and the last token's head choice,
-    against the oracle's prefill (which the oracle pins equal to token-by-token decode)."""
+    against the oracle's prefill (which the oracle pins equal to token-by-token decode).
+    Up to 64 tokens the attention is the decode kernel's, token by token; beyond, the
+    causal flash kernel over the pool's positions 0..p0+S-1 (query tiles ending below,
+    at and past a 32-key block, a prefix that is not block-aligned); each is held to the
+    emulation of its own bf16 storage."""
     shape = CFG.Shape(n_layers=2)
     m = Model(shape, 2, True, seed=17, gains="random")
     try:
@@ -777,16 +781,24 @@ def test_prefill_bf16(p0, S):
         _, lg_ref = O.head_logits(out[-1:], m.oracle_final_norm(), widen(head_h), shape.eps)
         lg_gpu = lg.cpu().numpy()
         assert normwise(lg_gpu, lg_ref[0]) <= TOL_LAYER_BF16
-        # the emulation: token by token (causal, so the same values as a prefill) with the
-        # bf16 storage of the decode kernels the prefill runs on
+        # the emulation of the path the prefill runs on: token by token (causal, so the same
+        # values as a prefill) with the decode kernels' bf16 storage, or the causal flash
+        # kernel's
         c16 = O.KVCache(2, 1)
         for l in range(2):
             if p0:
                 k, v = CFG.kv_prefill(seed, shape, l, 0, p0, True)
                 c16.set(l, 0, widen(k), widen(v))
-        xe = None
-        for i in range(S):
-            xe = E.decode_step(x_in[i:i + 1], [p0 + i], c16, m.oracle_layers(), dims_of(shape))
+        if S > 64:
+            xe_all = E.prefill(x_in, p0, c16, 0, m.oracle_layers(), dims_of(shape))
+            print("flash prefill vs emulation %.2e, vs oracle %.2e" % (normwise(x.cpu().numpy(), xe_all),
+                                                                       normwise(x.cpu().numpy(), out)))
+            assert normwise(x.cpu().numpy(), xe_all) <= TOL_EMUL_BF16
+            xe = xe_all[-1:]
+        else:
+            xe = None
+            for i in range(S):
+                xe = E.decode_step(x_in[i:i + 1], [p0 + i], c16, m.oracle_layers(), dims_of(shape))
         assert normwise(x.cpu().numpy()[-1:], xe) <= TOL_EMUL_BF16
         _, lg_emu = E.head_logits(xe, m.oracle_final_norm(), widen(head_h), shape.eps)
         check_argmax_groups(am.cpu().numpy()[None], lg_gpu.reshape(1, G, V), lg_emu.reshape(1, G, V))
