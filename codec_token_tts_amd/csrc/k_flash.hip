@@ -286,3 +286,54 @@ void launch_flash_attn(const FlashArgs &a, hipStream_t s) {
 }
 
 }  // namespace ttsbb
+
+namespace ttsbb {
+
+// fp32 form of the bidirectional attention (the MaskGIT pass of an fp32 context): plain
+// fp32 arithmetic, no MFMA.  One wave per (query row, head): lane l holds dims 2l, 2l + 1
+// of q and of the output; each key's score is a wave sum, the softmax is online (running
+// max m, normaliser l, output rescaled when m rises) with expf.  Rows [0, len0) attend to
+// keys [0, len0); with seg1 > 0, rows [seg1, seg1 + len1) to keys [seg1, seg1 + len1);
+// padding rows between get zeros.
+__global__ __launch_bounds__(256) void attn_f32_kernel(AttnF32Args a) {
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6), head = blockIdx.y;
+    if (row >= a.S) return;
+    const int kvh = head / (a.H / a.Hkv);
+    const bool second = a.seg1 > 0 && row >= a.seg1;
+    const int kb = second ? a.seg1 : 0, ke = kb + (second ? a.len1 : a.len0);
+    float *out = a.out + (int64_t)row * a.H * 128 + head * 128 + 2 * lane;
+    if (row >= ke) {  // padding row
+        out[0] = 0.f;
+        out[1] = 0.f;
+        return;
+    }
+    const float *q = a.q + (int64_t)row * a.H * 128 + head * 128 + 2 * lane;
+    const float q0 = q[0] * a.scale, q1 = q[1] * a.scale;
+    const float *K = a.k + (int64_t)kvh * a.s_pad * 128 + 2 * lane;
+    const float *V = a.v + (int64_t)kvh * a.s_pad * 128 + 2 * lane;
+    float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
+    for (int j = kb; j < ke; ++j) {
+        const float s = wave_sum(fmaf(q0, K[(int64_t)j * 128], q1 * K[(int64_t)j * 128 + 1]));
+        if (s > m) {  // wave-uniform: s is a wave sum
+            const float f = expf(m - s);  // m = -inf at the first key: 0
+            l *= f;
+            o0 *= f;
+            o1 *= f;
+            m = s;
+        }
+        const float p = expf(s - m);
+        l += p;
+        o0 = fmaf(p, V[(int64_t)j * 128], o0);
+        o1 = fmaf(p, V[(int64_t)j * 128 + 1], o1);
+    }
+    out[0] = o0 / l;
+    out[1] = o1 / l;
+}
+
+void launch_attn_f32(const AttnF32Args &a, hipStream_t s) {
+    if (a.S <= 0) return;
+    hipLaunchKernelGGL(attn_f32_kernel, dim3((a.S + 3) / 4, a.H), dim3(256), 0, s, a);
+}
+
+}  // namespace ttsbb

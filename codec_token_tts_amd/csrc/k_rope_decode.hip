@@ -34,8 +34,8 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(RopeKvArgs a) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int width = (a.H + 2 * a.Hkv) * 128;
     const float *row = a.qkv + (int64_t)m * width;
-    // dense mode leaves V to the transpose kernel below
-    const int jobs = a.dense ? a.H + a.Hkv : a.H + 2 * a.Hkv;
+    // dense (bf16) mode leaves V to the transpose kernel below
+    const int jobs = a.dense && !a.dense_f32 ? a.H + a.Hkv : a.H + 2 * a.Hkv;
 
     // Loads complete in order: the position goes first, then all of the first pass's
     // row values (they do not depend on it), and only then the position-dependent
@@ -98,7 +98,7 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(RopeKvArgs a) {
                 x2 = x1 * cs.x + x0 * cs.y;
             }
             if (j < a.H) {
-                if (a.dense || a.q_bf16) {
+                if ((a.dense && !a.dense_f32) || a.q_bf16) {
                     bf16_t *q = reinterpret_cast<bf16_t *>(a.q_out) + (int64_t)m * a.H * 128 + j * 128;
                     q[lane] = f32_to_bf16(x);
                     q[lane + 64] = f32_to_bf16(x2);
@@ -111,7 +111,11 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(RopeKvArgs a) {
             }
             const int kv = j < a.H + a.Hkv ? 0 : 1;
             const int h = j - a.H - kv * a.Hkv;
-            if (a.dense) {
+            if (a.dense_f32) {
+                float *dst = reinterpret_cast<float *>(kv ? a.vtbuf : a.kbuf) + ((int64_t)h * a.s_pad + m) * 128;
+                dst[lane] = x;
+                dst[lane + 64] = x2;
+            } else if (a.dense) {
                 bf16_t *k = a.kbuf + ((int64_t)h * a.s_pad + m) * 128;
                 k[lane] = f32_to_bf16(x);
                 k[lane + 64] = f32_to_bf16(x2);
@@ -191,7 +195,7 @@ void launch_pool_dense(const PoolDenseArgs &a, hipStream_t s) {
 
 void launch_rope_kv(const RopeKvArgs &a, DType kv_dt, hipStream_t s) {
     if (a.M <= 0) return;
-    const bool multi = (a.dense ? a.H + a.Hkv : a.H + 2 * a.Hkv) > 32;
+    const bool multi = (a.dense && !a.dense_f32 ? a.H + a.Hkv : a.H + 2 * a.Hkv) > 32;
     if (kv_dt == DT_BF16 || a.dense) {
         if (multi) hipLaunchKernelGGL((rope_kv_kernel<bf16_t, true>), dim3(a.M), dim3(256), 0, s, a);
         else hipLaunchKernelGGL((rope_kv_kernel<bf16_t, false>), dim3(a.M), dim3(256), 0, s, a);
@@ -199,7 +203,7 @@ void launch_rope_kv(const RopeKvArgs &a, DType kv_dt, hipStream_t s) {
         if (multi) hipLaunchKernelGGL((rope_kv_kernel<float, true>), dim3(a.M), dim3(256), 0, s, a);
         else hipLaunchKernelGGL((rope_kv_kernel<float, false>), dim3(a.M), dim3(256), 0, s, a);
     }
-    if (a.dense)
+    if (a.dense && !a.dense_f32)
         hipLaunchKernelGGL(dense_vt_kernel, dim3((a.M + 63) / 64, a.Hkv), dim3(256), 0, s, a);
 }
 

@@ -119,6 +119,8 @@ struct RopeKvArgs {
                          // and every row uses page-table row 0
     int seg1;            // dense mode, two sequences: rows m >= seg1 > 0 are at position m - seg1
     int q_bf16;          // decode mode: q_out gets bf16 rows (as in dense mode) instead of fp32
+    int dense_f32;       // dense mode in fp32: q_out fp32 [M][H*128], K and V rows fp32
+                         // [Hkv][s_pad][128] in kbuf and vtbuf (V not transposed)
 };
 void launch_rope_kv(const RopeKvArgs &a, DType kv_dt, hipStream_t s);
 // Dense mode fused into the q/k/v projection (g: EPI_STORE product of N = (H + 2 Hkv) *
@@ -203,6 +205,18 @@ struct FlashArgs {
     const int32_t *causal_pos;
 };
 void launch_flash_attn(const FlashArgs &a, hipStream_t s);
+
+// The same attention in fp32 (an fp32 context's MaskGIT pass): q [S][H*128], K and V rows
+// [Hkv][s_pad][128] (V not transposed), out [S][H*128], all fp32; seg1 / len0 / len1 as
+// above; scale = 1 / sqrt(128).
+struct AttnF32Args {
+    const float *q, *k, *v;
+    int S, s_pad, H, Hkv;
+    float scale;
+    float *out;
+    int seg1, len0, len1;
+};
+void launch_attn_f32(const AttnF32Args &a, hipStream_t s);
 
 // ---- K7: greedy choice per group --------------------------------------------------
 // A group holding a NaN raises FLAG_NONFINITE (its choice: the argmax of its other values,

@@ -288,8 +288,8 @@ TTSBB_API ttsbb_status ttsbb_create(const ttsbb_config *cfg, const ttsbb_layer *
               dev_alloc(c, &c->attn, RA * hd_all * c->esz) &&
               dev_alloc(c, &c->mlp, RA * g.ffn * c->esz) &&
               dev_alloc(c, (void **)&c->x, R * g.hidden * 4) &&
-              dev_alloc(c, (void **)&c->kbuf, (size_t)g.n_kv_heads * c->s_pad_cap * g.head_dim * 2) &&
-              dev_alloc(c, (void **)&c->vtbuf, (size_t)g.n_kv_heads * c->s_pad_cap * g.head_dim * 2) &&
+              dev_alloc(c, (void **)&c->kbuf, (size_t)g.n_kv_heads * c->s_pad_cap * g.head_dim * c->esz) &&
+              dev_alloc(c, (void **)&c->vtbuf, (size_t)g.n_kv_heads * c->s_pad_cap * g.head_dim * c->esz) &&
               dev_alloc(c, (void **)&c->part, R * g.n_heads * MAX_CHUNKS * PART_STRIDE * 4) &&
               dev_alloc(c, (void **)&c->logits, R * (size_t)(g.max_head_cols > 0 ? g.max_head_cols : 1) * 4) &&
               dev_alloc(c, (void **)&c->logits_u, R * (size_t)(g.max_head_cols > 0 ? g.max_head_cols : 1) * 4) &&
@@ -310,8 +310,8 @@ TTSBB_API ttsbb_status ttsbb_create(const ttsbb_config *cfg, const ttsbb_layer *
     // Padding keys of the MaskGIT K/V buffers must hold finite values (they meet a zero
     // probability), and the selection's rank counters must start from zero (every
     // selection leaves them zero again): zero them once here.
-    ok = hipMemset(c->kbuf, 0, (size_t)g.n_kv_heads * c->s_pad_cap * g.head_dim * 2) == hipSuccess &&
-         hipMemset(c->vtbuf, 0, (size_t)g.n_kv_heads * c->s_pad_cap * g.head_dim * 2) == hipSuccess &&
+    ok = hipMemset(c->kbuf, 0, (size_t)g.n_kv_heads * c->s_pad_cap * g.head_dim * c->esz) == hipSuccess &&
+         hipMemset(c->vtbuf, 0, (size_t)g.n_kv_heads * c->s_pad_cap * g.head_dim * c->esz) == hipSuccess &&
          hipMemset(c->flag, 0, 256) == hipSuccess &&
          hipMemset(c->rank, 0, (size_t)R * (g.max_head_cols / 2 + 1) * 4) == hipSuccess;
     // RoPE table: angle p * theta^(-2j/d) in double precision, rounded to fp32.
@@ -638,7 +638,7 @@ void maskgit_embed(ttsbb_ctx *ctx, int S, int n_text, const int32_t *text_ids, c
     e.out = ctx->x + (size_t)out_row0 * ctx->cfg.hidden;
     e.flag = ctx->flag;
     KScope k(ctx, TTSBB_K_EMBED);
-    launch_embed(e, DT_BF16, ctx->stream);
+    launch_embed(e, ctx->dt, ctx->stream);
 }
 
 // Every layer over rows [0, M) of ctx->x with bidirectional attention and no cache: one
@@ -671,6 +671,41 @@ void maskgit_layers(ttsbb_ctx *ctx, int M, int seg1, int len0, int len1, bool ta
         r.s_pad = s_pad;
         r.flag = ctx->flag;
         r.seg1 = seg1;
+        if (ctx->dt == DT_F32) {
+            // fp32: the projection, then norms + RoPE into fp32 q / K / V rows, then the fp32
+            // attention kernel
+            r.dense_f32 = 1;
+            qkv_projection(ctx, L, ctx->x, M, tapit);
+            {
+                KScope k(ctx, TTSBB_K_ROPE_KV);
+                launch_rope_kv(r, DT_F32, ctx->stream);
+            }
+            if (tapit) {
+                tap_dense(ctx, TTSBB_TAP_Q, ctx->q, DT_F32, M, hd_all, hd_all);
+                // K, V [Hkv][s_pad][hd] -> [M][Hkv][hd]
+                tap(ctx, TTSBB_TAP_K, ctx->kbuf, DT_F32, M, Hkv * hd, hd, (int64_t)s_pad * hd, 1, hd);
+                tap(ctx, TTSBB_TAP_V, ctx->vtbuf, DT_F32, M, Hkv * hd, hd, (int64_t)s_pad * hd, 1, hd);
+            }
+            AttnF32Args f = {};
+            f.q = reinterpret_cast<const float *>(ctx->q);
+            f.k = reinterpret_cast<const float *>(ctx->kbuf);
+            f.v = reinterpret_cast<const float *>(ctx->vtbuf);
+            f.S = M;
+            f.s_pad = s_pad;
+            f.H = H;
+            f.Hkv = Hkv;
+            f.scale = (float)(1.0 / sqrt((double)hd));
+            f.out = reinterpret_cast<float *>(ctx->attn);
+            f.seg1 = seg1;
+            f.len0 = len0;
+            f.len1 = len1;
+            {
+                KScope k(ctx, TTSBB_K_FLASH_ATTN);
+                launch_attn_f32(f, ctx->stream);
+            }
+            post_attention(ctx, L, ctx->x, M, tapit);
+            continue;
+        }
         if (!qkv_projection(ctx, L, ctx->x, M, tapit, &r)) {
             KScope k(ctx, TTSBB_K_ROPE_KV);
             launch_rope_kv(r, DT_BF16, ctx->stream);
@@ -711,9 +746,9 @@ void maskgit_head(ttsbb_ctx *ctx, int row0, int n_out, const void *heads, int N,
     {
         KScope k(ctx, TTSBB_K_RMSNORM);
         launch_rmsnorm(ctx->x + (size_t)row0 * g.hidden, g.hidden, n_out, g.hidden, ctx->final_norm, g.rms_eps,
-                       ctx->h, DT_BF16, ctx->stream);
+                       ctx->h, ctx->dt, ctx->stream);
     }
-    if (taps && ctx->tap_layer >= 0) tap_dense(ctx, TTSBB_TAP_HEAD_IN, ctx->h, DT_BF16, n_out, g.hidden, g.hidden);
+    if (taps && ctx->tap_layer >= 0) tap_dense(ctx, TTSBB_TAP_HEAD_IN, ctx->h, ctx->dt, n_out, g.hidden, g.hidden);
     head_gemm(ctx, heads, n_out, N, logits, N);
 }
 
@@ -727,7 +762,7 @@ bool maskgit_head_scores(ttsbb_ctx *ctx, int row0, int n_out, const void *heads,
                          float penalty, const int32_t *window, int codes_ld, int32_t *pred, float *conf) {
     const ttsbb_config &g = ctx->cfg;
     const int N = n_cb * V;
-    if (n_out <= 64 || V < 128 || g.hidden % 64 != 0) return false;
+    if (ctx->dt != DT_BF16 || n_out <= 64 || V < 128 || g.hidden % 64 != 0) return false;
     {
         KScope k(ctx, TTSBB_K_RMSNORM);
         launch_rmsnorm(ctx->x + (size_t)row0 * g.hidden, g.hidden, n_out, g.hidden, ctx->final_norm, g.rms_eps,
@@ -1149,7 +1184,6 @@ TTSBB_API ttsbb_status ttsbb_maskgit_pass(ttsbb_ctx *ctx, int32_t n_text, const 
         !ctx->final_norm)
         return TTSBB_INVALID_ARG;
     if (!(layer_penalty == layer_penalty)) return TTSBB_INVALID_ARG;
-    if (ctx->dt != DT_BF16) return TTSBB_UNSUPPORTED;
 
     const int S = n_text + n_frames;
     const int N = n_cb * cb_vocab;
@@ -1190,7 +1224,6 @@ TTSBB_API ttsbb_status ttsbb_maskgit_pass_cfg(ttsbb_ctx *ctx, int32_t n_text, co
         !ctx->final_norm)
         return TTSBB_INVALID_ARG;
     if (!(layer_penalty == layer_penalty) || !(cfg_scale == cfg_scale)) return TTSBB_INVALID_ARG;
-    if (ctx->dt != DT_BF16) return TTSBB_UNSUPPORTED;
 
     const int w0 = n_frames - n_target;
     const int N = n_cb * cb_vocab;
@@ -1234,7 +1267,6 @@ TTSBB_API ttsbb_status ttsbb_maskgit_step(ttsbb_ctx *ctx, const ttsbb_maskgit_st
     const bool draw_class = a->class_temp > 0.f && !a->u_class, draw_pos = a->pos_temp > 0.f && !a->u_pos;
     if (a->class_temp > 0.f && (!(a->top_k_ratio > 0.f) || cb_vocab > 2048)) return TTSBB_INVALID_ARG;
     if ((draw_class || draw_pos) && !a->rng_counter) return TTSBB_INVALID_ARG;
-    if (ctx->dt != DT_BF16) return TTSBB_UNSUPPORTED;
 
     const int S = n_text + n_frames, w0 = n_frames - n_target;
     const int N = n_cb * cb_vocab;

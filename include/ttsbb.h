@@ -198,7 +198,9 @@ ttsbb_status ttsbb_prefill(ttsbb_ctx *ctx, int32_t n_tokens, float *x, int32_t *
  *   text_ids int32 [n_text]; text_table [text_vocab][hidden]; audio_tables and
  *   audio_heads [n_cb*cb_vocab][hidden] (cfg.dtype); codes int32 [n_cb][n_frames]
  *   in/out; pred int32 and conf fp32 [n_cb][n_frames]; picked int32 [n_unmask].
- * Requires cfg.dtype == TTSBB_BF16. */
+ * A bf16 context runs the MFMA kernels (bf16 storage, fp32 accumulation); an fp32 context
+ * computes every step in fp32 (weight-streaming products and a plain fp32 attention
+ * kernel: a reference mode for checking, not a fast path). */
 ttsbb_status ttsbb_maskgit_pass(ttsbb_ctx *ctx, int32_t n_text, const int32_t *text_ids,
                                 const void *text_table, int32_t text_vocab, int32_t n_frames,
                                 int32_t n_cb, int32_t cb_vocab, int32_t mask_id,
@@ -222,7 +224,7 @@ ttsbb_status ttsbb_maskgit_pass(ttsbb_ctx *ctx, int32_t n_text, const int32_t *t
  * When S rounded up to 64 plus n_target fits cfg.max_rows, the two prompts run as one
  * batch of two independent sequences (same results up to rounding order; fewer, larger
  * launches), else as two passes.
- * Requires cfg.dtype == TTSBB_BF16 and 0 < n_target <= n_frames.  With taps on, the
+ * Requires 0 < n_target <= n_frames (bf16 or fp32 as ttsbb_maskgit_pass).  With taps on, the
  * per-layer taps and TTSBB_TAP_LOGITS come from the conditional pass (its rows lead the
  * batch), TTSBB_TAP_LOGITS_U holds u. */
 ttsbb_status ttsbb_maskgit_pass_cfg(ttsbb_ctx *ctx, int32_t n_text, const int32_t *text_ids,

@@ -337,6 +337,71 @@ def test_c4_maskgit_32_step_generation_two_layers():
         m.close()
 
 
+def test_c4_maskgit_fp32_32_steps_two_layers():
+    """fp32 context, the MaskGIT workload's shape (S = 950, 8 x 1025, 3000 masked, 32
+    cosine-schedule steps) with 2 layers, the GPU's codes feeding each next step.  At every
+    step the oracle runs the same step in fp64 on the same codes: the logits agree within
+    1e-4, pred equals the oracle's argmax except at near ties, and the unmask set equals
+    the oracle's except at boundary near ties (both counted, and bounded).  Whether the
+    loop stays identical to the oracle's own free-running loop is reported, not asserted:
+    with 6000 groups per step, an fp32 near tie somewhere in 32 steps is expected."""
+    w = CFG.c4()
+    e = w.extra
+    m = Model(w.shape, 2, False, seed=w.seed)
+    T = m.T
+    try:
+        n_text, n_frames, n_cb, V, mask = e["n_text"], e["n_frames"], e["n_cb"], e["cb_vocab"], e["mask_id"]
+        pen = e["layer_penalty"]
+        text_h = CFG.table(w.seed, gen.KIND_TEXT_TABLE, 0, e["text_vocab"], 1024, False)
+        tab_h = CFG.table(w.seed, gen.KIND_CB_TABLE, 0, n_cb * V, 1024, False)
+        head_h = CFG.table(w.seed, gen.KIND_HEAD, 0, n_cb * V, 1024, False)
+        text_ids, codes0 = CFG.maskgit_text_ids(w), CFG.maskgit_codes(w)
+        sched = T.ttsbb_unmask_schedule(int((codes0 == mask).sum()), e["n_steps"])
+        codes_d = t_i32(codes0)
+        text_d, tab_d, head_d, ids_d = (DEV.host_to_device(text_h), DEV.host_to_device(tab_h),
+                                        DEV.host_to_device(head_h), t_i32(text_ids))
+        pred = torch().empty((n_cb, n_frames), dtype=torch().int32, device="cuda")
+        conf = torch().empty((n_cb, n_frames), dtype=torch().float32, device="cuda")
+        picked = torch().empty(max(sched), dtype=torch().int32, device="cuda")
+        T.ttsbb_set_tap_layer(m.ctx, 1)
+        layers, fn, dims = m.oracle_layers(), m.oracle_final_norm(), dims_of(w.shape)
+        f64 = lambda a: np.asarray(a, np.float64)
+        codes_free = codes0.copy()
+        same_as_free = -1
+        near_pred = near_pick = 0
+        for step, n in enumerate(sched):
+            before = codes_d.cpu().numpy()
+            T.ttsbb_maskgit_pass(m.ctx, n_text, ids_d, text_d, e["text_vocab"], n_frames, n_cb, V, mask, tab_d,
+                                 head_d, codes_d, n, pen, pred, conf, picked)
+            assert T.ttsbb_sync(m.ctx) == T.OK
+            logits = read_tap(m, T.TAP_LOGITS, n_frames, n_cb * V)
+            pred_h, conf_h, picked_h = pred.cpu().numpy(), conf.cpu().numpy(), picked.cpu().numpy()[:n]
+            rec = {}
+            _, pred_r, conf_r, _ = O.maskgit_pass(text_ids, f64(text_h), before, f64(tab_h), f64(head_h), layers, fn,
+                                                  dims, V, mask, pen, n, record=rec)
+            dl = float(np.max(np.abs(logits - rec["logits"])))
+            assert dl <= 1e-4, (step, dl)
+            g = logits.reshape(n_frames, n_cb, V).transpose(1, 0, 2)
+            r = rec["logits"].reshape(n_frames, n_cb, V).transpose(1, 0, 2)
+            near_pred += check_argmax_groups(pred_h, g, r, exclude=mask)
+            near_pick += check_topn(picked_h, conf_h, conf_r, n)
+            after = codes_d.cpu().numpy()
+            assert np.array_equal(after, O.apply_picks(before, pred_h, picked_h)), step
+            if same_as_free == step - 1:
+                codes_free = O.apply_picks(codes_free, pred_r, O.select_top(conf_r.reshape(-1), n))
+                if np.array_equal(after, codes_free):
+                    same_as_free = step
+            print("step %2d: n_unmask %4d, max |dlogit| %.1e" % (step, n, dl))
+        assert int((codes_d.cpu().numpy() == mask).sum()) == 0
+        print("argmax near ties %d, selection boundary near ties %d; identical to the oracle's free-running "
+              "loop through step %d of %d" % (near_pred, near_pick, same_as_free, len(sched) - 1))
+        # (check_topn counts the threshold element itself: at least one per step)
+        assert near_pred <= len(sched) and near_pick <= 2 * len(sched)
+        T.ttsbb_set_tap_layer(m.ctx, -1)
+    finally:
+        m.close()
+
+
 def c5_setup(m, w):
     e = w.extra
     B, K, V = e["batch"], e["n_cb"], e["cb_vocab"]

@@ -340,9 +340,9 @@ def run_maskgit(m: Model, n_text, n_frames, n_cb, V, mask_id, n_unmask, seed, ta
                 text_vocab=500, masked_frac=0.5):
     T = m.T
     shape = m.shape
-    text_h = CFG.table(seed, gen.KIND_TEXT_TABLE, 0, text_vocab, shape.hidden, True)
-    tab_h = CFG.table(seed, gen.KIND_CB_TABLE, 0, n_cb * V, shape.hidden, True)
-    head_h = CFG.table(seed, gen.KIND_HEAD, 0, n_cb * V, shape.hidden, True)
+    text_h = CFG.table(seed, gen.KIND_TEXT_TABLE, 0, text_vocab, shape.hidden, m.bf16)
+    tab_h = CFG.table(seed, gen.KIND_CB_TABLE, 0, n_cb * V, shape.hidden, m.bf16)
+    head_h = CFG.table(seed, gen.KIND_HEAD, 0, n_cb * V, shape.hidden, m.bf16)
     text_ids = gen.uniform_int(seed, stream_id(gen.KIND_TEXT_IDS, 0), (n_text,), text_vocab)
     codes = gen.uniform_int(seed, stream_id(gen.KIND_CODES, 0), (n_cb, n_frames), V - 1)
     perm = gen.permutation(seed, stream_id(gen.KIND_MASK_PERM, 0), n_cb * n_frames)
@@ -377,8 +377,10 @@ def run_maskgit(m: Model, n_text, n_frames, n_cb, V, mask_id, n_unmask, seed, ta
     new_codes, pred_r, conf_r, picked_r = O.maskgit_pass(
         text_ids, widen(text_h), codes, widen(tab_h), widen(head_h), m.oracle_layers(),
         m.oracle_final_norm(), dims_of(shape), V, mask_id, 5.0, n_unmask, record=rec)
-    _, _, l_emul = E.maskgit_logits(text_ids, widen(text_h), codes, widen(tab_h), widen(head_h), m.oracle_layers(),
-                                    m.oracle_final_norm(), dims_of(shape), V)
+    l_emul = None
+    if m.bf16:
+        _, _, l_emul = E.maskgit_logits(text_ids, widen(text_h), codes, widen(tab_h), widen(head_h),
+                                        m.oracle_layers(), m.oracle_final_norm(), dims_of(shape), V)
     ref = dict(codes_in=codes, rec=rec, lrec=lrec, conf=conf_r, pred=pred_r, x0=x0, head=widen(head_h),
                l_emul=l_emul)
     return res, ref
@@ -918,6 +920,93 @@ def test_maskgit_workload_shape_one_layer():
         res, ref = run_maskgit(m, 200, 750, 8, 1025, 1024, 4, w.seed, tap_layer=0)
         check_maskgit(res, ref, 8, 750, 1025, 1024, 4)
         check_attention_teacher_forced(res["taps"], 950, 16, 8)
+    finally:
+        m.close()
+
+
+# ---------------------------------------------------------------------------------------
+# fp32 contexts: every MaskGIT step in fp32 (the reference mode), against the oracle at
+# the fp32 bound
+# ---------------------------------------------------------------------------------------
+@pytest.mark.parametrize("n_text,n_frames,n_heads,n_kv", [(13, 57, 16, 8), (70, 130, 16, 8), (5, 60, 8, 8)])
+def test_maskgit_fp32_layer(n_text, n_frames, n_heads, n_kv):
+    """fp32, one bidirectional layer: every tap (q, K, V after the head norms and RoPE,
+    the attention output, both residual updates, the SwiGLU output) and the logits within
+    1e-4 of the oracle; pred exactly the oracle's argmax except at near ties; conf and the
+    picks as the oracle scores the GPU's own head operand."""
+    shape = CFG.Shape(n_layers=1, n_heads=n_heads, n_kv_heads=n_kv)
+    m = Model(shape, 1, False, seed=51, gains="random")
+    try:
+        n_cb, V, mask, n_unmask = 3, 129, 128, 50
+        res, ref = run_maskgit(m, n_text, n_frames, n_cb, V, mask, n_unmask, 51, tap_layer=0)
+        S = n_text + n_frames
+        lrec = ref["lrec"]
+        for k in ("q", "k", "v", "o", "x1", "m", "x2"):
+            d = float(np.max(np.abs(res["taps"][k] - lrec[k].reshape(S, -1))))
+            print("fp32 %s: max |d| %.2e" % (k, d))
+            assert d <= 1e-4, k
+        assert float(np.max(np.abs(res["logits"] - ref["rec"]["logits"]))) <= 1e-4
+        _, l_y = check_head_teacher_forced(res["head_in"], ref["head"], res["logits"], res["pred"].T, n_cb, V,
+                                          exclude=mask)
+        check_scores_teacher_forced(res["pred"], res["conf"], res["picked"], l_y, ref["codes_in"], n_cb, V, mask,
+                                    5.0, n_unmask)
+        g = res["logits"].reshape(n_frames, n_cb, V).transpose(1, 0, 2)
+        r = ref["rec"]["logits"].reshape(n_frames, n_cb, V).transpose(1, 0, 2)
+        check_argmax_groups(res["pred"], g, r, exclude=mask)
+        fin = np.isfinite(ref["conf"])
+        assert np.array_equal(np.isfinite(res["conf"]), fin)
+        assert float(np.max(np.abs(res["conf"][fin] - ref["conf"][fin]))) <= 2e-4
+        check_topn(res["picked"], res["conf"], ref["conf"], n_unmask)
+    finally:
+        m.close()
+
+
+def test_maskgit_fp32_guided_two_sequences():
+    """fp32 guided step: the two prompts batched as two sequences through the fp32
+    attention kernel give the oracle's logits of both passes (1e-4), its guided scores
+    and its picks."""
+    shape = CFG.Shape(n_layers=1)
+    m = Model(shape, 1, False, seed=53, gains="random")
+    T = m.T
+    try:
+        n_text, n_frames, n_target, n_cb, V, mask, n_unmask, scale = 9, 70, 40, 2, 65, 64, 20, 2.0
+        seed = 53
+        text_h = CFG.table(seed, gen.KIND_TEXT_TABLE, 0, 100, shape.hidden, False)
+        tab_h = CFG.table(seed, gen.KIND_CB_TABLE, 0, n_cb * V, shape.hidden, False)
+        head_h = CFG.table(seed, gen.KIND_HEAD, 0, n_cb * V, shape.hidden, False)
+        text_ids = gen.uniform_int(seed, stream_id(gen.KIND_TEXT_IDS, 0), (n_text,), 100)
+        codes = gen.uniform_int(seed, stream_id(gen.KIND_CODES, 0), (n_cb, n_frames), V - 1)
+        codes[:, n_frames - n_target::2] = mask
+        cd = t_i32(codes)
+        pred = torch().empty((n_cb, n_target), dtype=torch().int32, device="cuda")
+        conf = torch().empty((n_cb, n_target), dtype=torch().float32, device="cuda")
+        picked = torch().empty(n_unmask, dtype=torch().int32, device="cuda")
+        T.ttsbb_set_tap_layer(m.ctx, 0)
+        T.ttsbb_maskgit_pass_cfg(m.ctx, n_text, t_i32(text_ids), DEV.host_to_device(text_h), 100, n_frames,
+                                 n_target, n_cb, V, mask, DEV.host_to_device(tab_h), DEV.host_to_device(head_h), cd,
+                                 n_unmask, 5.0, scale, pred, conf, picked)
+        assert T.ttsbb_sync(m.ctx) == T.OK
+        lg_c = read_tap(m, T.TAP_LOGITS, n_target, n_cb * V)
+        lg_u = read_tap(m, T.TAP_LOGITS_U, n_target, n_cb * V)
+        T.ttsbb_set_tap_layer(m.ctx, -1)
+        layers, fn, dims = m.oracle_layers(), m.oracle_final_norm(), dims_of(shape)
+        w0 = n_frames - n_target
+        f64 = lambda a: np.asarray(a, np.float64)
+        x = O.hybrid_embed(text_ids, f64(text_h), codes, f64(tab_h), V)
+        xc = O.backbone_full(x, layers, dims, causal=False)
+        _, lc = O.head_logits(xc[n_text + w0:], fn, f64(head_h), dims.eps)
+        xu = O.hybrid_embed(np.zeros(0, np.int64), f64(text_h), codes[:, w0:], f64(tab_h), V)
+        xu = O.backbone_full(xu, layers, dims, causal=False)
+        _, lu = O.head_logits(xu, fn, f64(head_h), dims.eps)
+        assert float(np.max(np.abs(lg_c - lc))) <= 1e-4
+        assert float(np.max(np.abs(lg_u - lu))) <= 1e-4
+        gl = lc + scale * (lc - lu)
+        _, conf_r, _ = O.maskgit_scores(gl, codes[:, w0:], n_cb, V, mask, 5.0)
+        fin = np.isfinite(conf_r)
+        c = conf.cpu().numpy()
+        assert np.array_equal(np.isfinite(c), fin)
+        assert float(np.max(np.abs(c[fin] - conf_r[fin]))) <= 1e-3
+        check_topn(picked.cpu().numpy(), c, conf_r, n_unmask)
     finally:
         m.close()
 
