@@ -224,6 +224,7 @@ def cpu_baseline(n_streams=2, n_steps=24):
         pos = [p + 1 for p in pos]
     dt = time.perf_counter() - t1
     return {"value": n_streams * n_steps / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": host_cpu_model(),
             "sample": "%d of the 64 streams (KV %s) for %d consecutive full 28-layer decode steps "
                       "(embed, layers, head, argmax), fp64 numpy; input generation (%.1f s) excluded"
                       % (n_streams, lengths.tolist(), n_steps, setup),
@@ -259,6 +260,18 @@ def cpu_baseline_maskgit():
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_attn_c5_traffic.md")
 TRAFFIC_SOURCES = [os.path.join(ROOT, "codec_token_tts_amd", "csrc", f)
                    for f in ("k_rope_decode.hip", "common.h", "kernels.h")]
+
+
+def host_cpu_model() -> str:
+    """The host CPU's model name (first processor in /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def kernel_source_hash() -> str:
