@@ -27,25 +27,53 @@ namespace ttsbb {
 // A group holding a NaN (no order) has no defined maximum: the kernel raises
 // FLAG_NONFINITE; the choice is the argmax of the group's other values, or class 0 when
 // every value is NaN.
+// One block per (row, group): each thread takes the classes tid, tid + 256, ... and
+// requests up to 16 of them before comparing any, so a 3072-class group costs one round of
+// loads rather than a chain of 48 per lane; the four waves merge through LDS in a fixed
+// order (ties to the lowest class id either way).
 __global__ __launch_bounds__(256) void argmax_groups_kernel(const float *logits, int rows, int ld,
                                                             int n_groups, int V, int32_t *out, int *flag) {
-    const int lane = threadIdx.x & 63;
-    const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (item >= rows * n_groups) return;
+    constexpr int BATCH = 16;
+    __shared__ float red_v[4];
+    __shared__ int red_i[4], red_nan[4];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int item = blockIdx.x;
     const int gi = item % n_groups, r = item / n_groups;
     const float *x = logits + (int64_t)r * ld + (int64_t)gi * V;
     float best = -INFINITY;
     int bi = 0x7FFFFFFF;
     bool nan = false;
-    for (int v = lane; v < V; v += 64) {
-        const float xv = x[v];
-        nan |= xv != xv;
-        argmax_merge(best, bi, xv, v);
+    for (int v0 = 0; v0 < V; v0 += 256 * BATCH) {
+        float xs[BATCH];
+#pragma unroll
+        for (int j = 0; j < BATCH; ++j) {
+            const int v = v0 + j * 256 + tid;
+            xs[j] = v < V ? x[v] : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < BATCH; ++j) {
+            const int v = v0 + j * 256 + tid;
+            if (v < V) {
+                nan |= xs[j] != xs[j];
+                argmax_merge(best, bi, xs[j], v);
+            }
+        }
     }
     wave_argmax(best, bi);
     nan = __any(nan);
     if (lane == 0) {
-        if (nan) raise_flag(flag, FLAG_NONFINITE);
+        red_v[wave] = best;
+        red_i[wave] = bi;
+        red_nan[wave] = nan;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        bool any_nan = red_nan[0];
+        for (int w = 1; w < 4; ++w) {
+            argmax_merge(best, bi, red_v[w], red_i[w]);
+            any_nan |= red_nan[w] != 0;
+        }
+        if (any_nan) raise_flag(flag, FLAG_NONFINITE);
         out[item] = bi == 0x7FFFFFFF ? 0 : bi;
     }
 }
@@ -54,8 +82,8 @@ void launch_argmax_groups(const float *logits, int rows, int ld, int n_groups, i
                           int32_t *out, int *flag, hipStream_t s) {
     const int items = rows * n_groups;
     if (items <= 0) return;
-    hipLaunchKernelGGL(argmax_groups_kernel, dim3((items + 3) / 4), dim3(256), 0, s, logits, rows, ld,
-                       n_groups, group_vocab, out, flag);
+    hipLaunchKernelGGL(argmax_groups_kernel, dim3(items), dim3(256), 0, s, logits, rows, ld, n_groups,
+                       group_vocab, out, flag);
 }
 
 // The choice of a group whose scores have no order (a NaN, or an infinite logit that
