@@ -333,15 +333,15 @@ def run_rvq(T, torch, n_frames, iters):
     try:
         T.ttsbb_rvq_decode(ctx, n_frames, nq, cb, dim, od, codes, emb, w, b, out)
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
+        # the kernel's own duration (events stamped at its start and end): a loop of calls
+        # through the binding would time the host's call overhead instead
+        T.ttsbb_profile_start(ctx, 1 << T.K_NAMES.index("rvq"))
         for _ in range(iters):
             T.ttsbb_rvq_decode(ctx, n_frames, nq, cb, dim, od, codes, emb, w, b, out)
-        e1.record()
-        torch.cuda.synchronize()
-        if T.ttsbb_sync(ctx) != T.OK:
+        ms, n = T.ttsbb_profile_stop(ctx)["rvq"]
+        if T.ttsbb_sync(ctx) != T.OK or n != iters:
             raise RuntimeError("device flag raised by the RVQ decode")
-        return e0.elapsed_time(e1) * 1e3 / iters
+        return ms * 1e3 / iters
     finally:
         T.ttsbb_destroy(ctx)
 
@@ -613,7 +613,9 @@ def run_extras(args, T, torch, dec, mg):
                             "head + argmax on the last token"},
         "rvq_decode": {"us_per_call": round(rvq_us, 2), "frames": mg.e["n_frames"],
                        "gflops_fp32": round(2.0 * mg.e["n_frames"] * 8 * 64 * 1024 / (rvq_us * 1e-6) / 1e9, 1),
-                       "note": "codec RVQ decode, 8 x (1024 x 64) codebooks -> 1024, fp32"},
+                       "mfma_frac_fp32": round(2.0 * mg.e["n_frames"] * 8 * 64 * 1024 / (rvq_us * 1e-6) / 157.3e12, 4),
+                       "note": "codec RVQ decode, 8 x (1024 x 64) codebooks -> 1024, fp32 matrix cores; "
+                               "kernel duration from events stamped at its start and end"},
         "maskgit_sampled": {"ms_per_pass": round(smp_ms, 4),
                             "frames_per_s": round(mg.e["n_frames"] / (smp_ms * 1e-3 * mg.e["n_steps"]), 1),
                             "note": "guided + sampled step: cfg_scale 2.0, top-k ratio 0.1, class and position "

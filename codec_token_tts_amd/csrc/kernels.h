@@ -270,7 +270,8 @@ struct RvqArgs {
     float *out;            // [n_frames][out_dim]
     int *flag;
 };
-void launch_rvq_decode(const RvqArgs &a, hipStream_t s);
+// ev0 / ev1 (optional): events stamped with the kernel's own start and end
+void launch_rvq_decode(const RvqArgs &a, hipStream_t s, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 
 // ---- misc ---------------------------------------------------------------------------
 void launch_increment(int32_t *v, int n, hipStream_t s, int delta = 1);  // v[i] += delta, i < n

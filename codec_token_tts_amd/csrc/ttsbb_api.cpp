@@ -1331,8 +1331,8 @@ TTSBB_API ttsbb_status ttsbb_rvq_decode(ttsbb_ctx *ctx, int32_t n_frames, int32_
     r.out = out;
     r.flag = ctx->flag;
     {
-        KScope k(ctx, TTSBB_K_RVQ);
-        launch_rvq_decode(r, ctx->stream);
+        KScope k(ctx, TTSBB_K_RVQ, true);
+        launch_rvq_decode(r, ctx->stream, k.start(), k.stop());
     }
     return launch_failed() ? TTSBB_DEVICE_ERROR : TTSBB_OK;
 }

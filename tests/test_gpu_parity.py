@@ -706,12 +706,14 @@ def test_maskgit_step_sampler(n_text, n_frames, n_target, cfg_scale, class_temp,
 # Codec RVQ decode
 # ---------------------------------------------------------------------------------------
 @pytest.mark.parametrize("n_frames,n_q,cb,dim,out_dim", [(750, 8, 1024, 64, 1024), (37, 3, 100, 48, 200),
-                                                         (1, 1, 5, 130, 7)])
+                                                         (65, 9, 17, 8, 33), (1, 1, 5, 130, 7)])
 def test_rvq_decode(n_frames, n_q, cb, dim, out_dim):
     """fp32 against the oracle to 1e-4 max-abs (the quantizer accuracy the ncnn port reports
     against PyTorch); the first shape is the 8 x 1024 x 64 -> 1024 quantizer of the
-    OmniVoice codec over 30 s of frames, the others ragged tiles and a codebook dimension
-    that is not a multiple of the 64-wide slices."""
+    OmniVoice codec over 30 s of frames.  The next two take the matrix-core kernel with
+    ragged 32 x 32 tiles, fewer codebooks than its four waves, and a codebook count that is
+    not a multiple of four; the last (a dimension that is not a multiple of 8) the
+    vector kernel."""
     m = Model(CFG.Shape(n_layers=1), 0, False, seed=13)
     try:
         T = m.T
