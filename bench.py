@@ -386,7 +386,10 @@ def run_c3(T, torch, iters):
     """The 5-layer code predictor: 256 frames in lockstep, a 1-token prefill of the frame's
     hidden state at position 0, then 15 q_len = 1 steps, step s embedding code s-1 with
     table s-1 and choosing code s with head s-1 (greedy, fed back on the device).  One
-    frame batch = those 16 calls (and 15 embeddings); returns ms per frame batch.
+    frame batch = those 16 calls (and 15 embeddings), ~720 small kernels.  Timed eagerly
+    and as one HIP graph of the whole frame batch (torch's stream capture on the context's
+    own stream), whose codes must equal the eager run's.  Returns (eager, graph) ms per
+    frame batch.
     Roofline (HBM-bound, ~200 flop/B): the 5 layers' bf16 weights (157.3 MB) in each of
     the 16 calls, the 15 heads (4.2 MB each) and the KV of positions 0..s of every frame
     and layer (4 KB each) in call s: 3.29 GB, 0.412 ms at 8 TB/s."""
@@ -394,7 +397,9 @@ def run_c3(T, torch, iters):
     w = CFG.c3()
     e = w.extra
     F, steps, V = e["batch"], e["steps"], e["cb_vocab"]
-    ctx, keep = make_ctx(T, torch, w.shape, 5, True, w.seed, F, 64, V, DEV, CFG)
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        ctx, keep = make_ctx(T, torch, w.shape, 5, True, w.seed, F, 64, V, DEV, CFG)
     try:
         pt, n_pages = CFG.page_table(w.seed, [16] * F)
         pool = DEV.kv_pool(w.seed, w.shape, 5, [0] * F, pt, n_pages, True)
@@ -406,6 +411,7 @@ def run_c3(T, torch, iters):
         pos = torch.zeros(F, dtype=torch.int32, device="cuda")
         x = torch.empty((F, 1024), dtype=torch.float32, device="cuda")
         codes = torch.empty((steps + 1, F, 1), dtype=torch.int32, device="cuda")
+        torch.cuda.synchronize()
 
         def frame_batch():
             pos.zero_()
@@ -416,17 +422,33 @@ def run_c3(T, torch, iters):
                 T.ttsbb_codebook_embed(ctx, F, 1, codes[s - 1], tabs[s - 1], V, None, None, None, 0, x)
                 T.ttsbb_decode_step(ctx, F, x, pos, pt_d, 1, pool, n_pages, heads[s - 1], 1, V, codes[s])
 
-        frame_batch()
-        torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(iters):
+        with torch.cuda.stream(side):
             frame_batch()
-        e1.record()
-        torch.cuda.synchronize()
+            side.synchronize()
+            e0.record(side)
+            for _ in range(iters):
+                frame_batch()
+            e1.record(side)
+            torch.cuda.synchronize()
+            eager_ms = e0.elapsed_time(e1) / iters
+            codes_eager = codes.clone()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                frame_batch()
+            g.replay()  # warm
+            e0.record(side)
+            for _ in range(iters):
+                g.replay()
+            e1.record(side)
+            torch.cuda.synchronize()
+            graph_ms = e0.elapsed_time(e1) / iters
+        if not torch.equal(codes, codes_eager):
+            raise RuntimeError("graph replay of the code predictor differs from the eager run")
         if T.ttsbb_sync(ctx) != T.OK:
             raise RuntimeError("device flag raised by the code predictor")
-        return e0.elapsed_time(e1) / iters
+        del g
+        return eager_ms, graph_ms
     finally:
         torch.cuda.synchronize()
         T.ttsbb_destroy(ctx)
@@ -595,7 +617,7 @@ def run_extras(args, T, torch, dec, mg):
 
     # The 5-layer code predictor: 256 frames x (1-token prefill + 15 steps)
     log("timed: code predictor")
-    c3_ms = run_c3(T, torch, args.steps)
+    c3_eager_ms, c3_ms = run_c3(T, torch, args.steps)
 
     # Batch-1 decode loop (16 codebooks, 3072 head, KV 1000, 148 steps): eager vs one graph
     c2_eager_ms = c2_graph_ms = None
@@ -621,10 +643,13 @@ def run_extras(args, T, torch, dec, mg):
                             "note": "guided + sampled step: cfg_scale 2.0, top-k ratio 0.1, class and position "
                                     "temperature 1.0, Gumbel uniforms drawn on the device (Philox4x32-10)"},
         "code_predictor": {"ms_per_frame_batch": round(c3_ms, 4), "codes_per_s": round(256 * 15 / (c3_ms * 1e-3), 1),
+                           "eager_ms_per_frame_batch": round(c3_eager_ms, 4),
                            "roofline_ms": round(C3_ROOFLINE_BYTES / (HBM_PEAK_GBS * 1e9) * 1e3, 4),
                            "frac_of_roofline": round(C3_ROOFLINE_BYTES / (HBM_PEAK_GBS * 1e9) * 1e3 / c3_ms, 4),
                            "note": "5 layers, 256 frames: 1-token prefill + 15 steps, 15 tables and 2048-way heads, "
-                                   "argmax fed back on the device; roofline = 3.29 GB of weights, heads and KV at 8 TB/s"},
+                                   "argmax fed back on the device; the frame batch captured as one HIP graph "
+                                   "(replays produce the eager run's codes); roofline = 3.29 GB of weights, "
+                                   "heads and KV at 8 TB/s"},
         "decode_b1_loop": None if c2_graph_ms is None else {
             "eager_ms_per_step": round(c2_eager_ms, 4), "graph_ms_per_step": round(c2_graph_ms, 4),
             "graph_tokens_per_s": round(1.0 / (c2_graph_ms * 1e-3), 1), "steps": 148,

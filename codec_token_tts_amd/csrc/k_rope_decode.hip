@@ -627,13 +627,26 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeAttnArgs a, int
         base = total;
     }
     // page ids of every pair's chunk, one per lane of the attention wave (clamped into the
-    // stream's page-table row); the pairs written above are visible after the barrier
+    // stream's page-table row); the pairs written above are visible after the barrier.
+    // Four entries per thread and round, every load requested before any store: a round
+    // is two dependent loads (the pair, then its page id), not eight.
     __syncthreads();
-    for (int idx = tid; idx < base * 64; idx += 1024) {
-        const int pr = idx >> 6, j = idx & 63;
-        const int4 w = plan[pr];
-        const int32_t *ptab = a.page_table + (int64_t)(a.shared ? 0 : w.x) * a.max_pages;
-        a.plan_pages[idx] = ptab[min(w.y * w.w / a.page + j, a.max_pages - 1)];
+    const int n_ids = base * 64;
+    for (int idx0 = tid; idx0 < n_ids; idx0 += 4 * 1024) {
+        int row[4], pg[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int idx = min(idx0 + u * 1024, n_ids - 1);
+            const int4 w = plan[idx >> 6];
+            row[u] = a.shared ? 0 : w.x;
+            pg[u] = min(w.y * w.w / a.page + (idx & 63), a.max_pages - 1);
+        }
+        int id[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) id[u] = a.page_table[(int64_t)row[u] * a.max_pages + pg[u]];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (idx0 + u * 1024 < n_ids) a.plan_pages[idx0 + u * 1024] = id[u];
     }
     if (tid == 0) {
         plan_n[0] = base;
