@@ -20,6 +20,7 @@
 // positions, each with its page ids, and for q_len = 1 decode a chunk size chosen so that
 // the items fill two workgroups per CU.
 #include <hip/hip_ext.h>
+#include <type_traits>
 #include <math.h>
 
 #include "common.h"
@@ -338,31 +339,63 @@ __device__ __forceinline__ void norm_rope_head(const float *x, const float *gain
 
 // One work item (stream, KV head, chunk) of the decode attention, on one wave; returns
 // false when `item` lies past the step's work list.
-template <typename T, int GROUP, bool FUSED>
+template <typename T, int GROUP, bool FUSED, bool DIRECT>
 __device__ __forceinline__ bool decode_attn_item(const DecodeAttnArgs &a, int item) {
     constexpr int EPL = KVRaw<T>::EPL;
     constexpr int LPR = 128 / EPL;  // lanes per 128-dim row
     constexpr int RPL = 64 / LPR;   // rows (tokens) per wave load
     constexpr int NR = 16 / RPL;    // wave loads per 16-token page block
     const int lane = threadIdx.x & 63;
-    // the step's work list: pair item / Hkv = (stream, chunk, token position); KV heads vary
-    // fastest, so the waves of a block stream neighbouring 4 KB blocks of the same pool
-    // pages (a page holds all heads' K and V contiguously)
+    // pair item / Hkv: a (stream, chunk, token position) of the step's work list, or in
+    // direct mode the stream; KV heads vary fastest, so the waves of a block stream
+    // neighbouring 4 KB blocks of the same pool pages (a page holds all heads' K and V
+    // contiguously)
     const int pair = item / a.Hkv, hk = item % a.Hkv;
-    const int pc = min(pair, a.plan_cap - 1);
+    const int d0 = (lane % LPR) * EPL;
+    const int rsub = lane / LPR;
+    const int cap = a.max_pages * a.page;
     // The chunk's page ids (one per lane) come with the pair, in the same round of loads,
     // and are read once: a page-id load inside the page loop would have to complete before
     // the next page's addresses exist, and loads complete in order, so that wait would also
     // drain the prefetch.
-    const int n_pairs = *a.plan_n;
-    const int4 w = a.plan[pc];
-    const int my_page = a.plan_pages[(int64_t)pc * 64 + lane];
-    if (pair >= n_pairs) return false;
-    const int b = w.x, c = w.y, p_tok = w.z, chunk = w.w;  // p_tok: position of the step's token
-    const int p_begin = c * chunk;
+    int b, c, p_tok, p_begin, chunk, my_page;  // p_tok: position of the step's token
+    if (DIRECT) {
+        // one item per (stream, KV head) over the whole cache: positions and page ids from
+        // the stream's own entries, no work list
+        if (pair >= a.B) return false;
+        b = pair;
+        c = 0;
+        p_begin = 0;
+        chunk = cap;
+        p_tok = a.pos[b];
+        my_page = a.page_table[(int64_t)b * a.max_pages + min(lane, a.max_pages - 1)];
+        const bool bad = p_tok < 0 || p_tok >= a.max_pos || p_tok >= cap;
+        if (bad && hk == 0 && lane == 0) raise_flag(a.flag, FLAG_POSITION);
+        if (p_tok < 0) {  // no cached position: zero rows, as the merge writes for such a stream
+#pragma unroll
+            for (int j = 0; j < GROUP; ++j)
+                if (lane < LPR) {
+                    const int k = (hk * GROUP + j) * 128 + d0;
+                    T *o = reinterpret_cast<T *>(a.out) +
+                           (a.out_mt > 0 ? frag_index(b, k, a.out_mt) : (int64_t)b * a.H * 128 + k);
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) o[e] = from_f32<T>(0.f);
+                }
+            return true;
+        }
+    } else {
+        const int pc = min(pair, a.plan_cap - 1);
+        const int n_pairs = *a.plan_n;
+        const int4 w = a.plan[pc];
+        my_page = a.plan_pages[(int64_t)pc * 64 + lane];
+        if (pair >= n_pairs) return false;
+        b = w.x;
+        c = w.y;
+        p_tok = w.z;
+        chunk = w.w;
+        p_begin = c * chunk;
+    }
     const int pg_first = p_begin / a.page;
-    const int d0 = (lane % LPR) * EPL;
-    const int rsub = lane / LPR;
     // FUSED: the raw q rows and the q gains do not depend on the position either; they
     // are requested in the same round as it
     const float *row = FUSED ? a.qkv + (int64_t)b * (a.H + 2 * a.Hkv) * 128 : nullptr;
@@ -375,7 +408,7 @@ __device__ __forceinline__ bool decode_attn_item(const DecodeAttnArgs &a, int it
 #pragma unroll
             for (int e = 0; e < EPL; ++e) x[j][e] = row[(hk * GROUP + j) * 128 + d0 + e];
     }
-    const int L = min(p_tok + 1, a.max_pages * a.page);  // the plan holds chunks below L only
+    const int L = min(p_tok + 1, cap);  // the plan holds chunks below L only
     const int p_end = min(L, p_begin + chunk);
     // FUSED: the chunk that holds the token's slot takes the token's K / V from registers
     // (rounded to the pool's type, as a read-back would give) and scans only the earlier
@@ -513,6 +546,18 @@ __device__ __forceinline__ bool decode_attn_item(const DecodeAttnArgs &a, int it
             for (int o = LPR; o < 64; o <<= 1) v += __shfl_xor(v, o, WAVE);
             acc[j][e] = v;
         }
+        if (DIRECT) {
+            // the stream's only chunk: its normalised output, as the merge computes it from
+            // one partial (weight 2^0 = 1, sum 1 * lt, then acc * (1 / sum))
+            const float inv = 1.0f / lt;
+            if (lane < LPR) {
+                const int k = (hk * GROUP + j) * 128 + d0;  // EPL contiguous columns in both layouts
+                T *o = reinterpret_cast<T *>(a.out) + (a.out_mt > 0 ? frag_index(b, k, a.out_mt) : (int64_t)b * a.H * 128 + k);
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) o[e] = from_f32<T>(acc[j][e] * inv);
+            }
+            continue;
+        }
         float *part = a.part + (((int64_t)b * a.H + hk * GROUP + j) * a.part_stride + c) * PART_STRIDE;
         if (lane < LPR) {
 #pragma unroll
@@ -530,14 +575,16 @@ __device__ __forceinline__ bool decode_attn_item(const DecodeAttnArgs &a, int it
 // the caches could hold when there is no budget); each wave takes items wave, wave +
 // (waves in the grid), ... -- one item per wave when the list fits the budget, so no
 // workgroup is dispatched without work.
-template <typename T, int GROUP, bool FUSED>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? (FUSED ? 3 : 4) : 2)))
+// DIRECT: a.direct (a separate instantiation, so the work-list kernels keep their
+// registers; short caches are latency-bound, so it takes the 3-wave register budget).
+template <typename T, int GROUP, bool FUSED, bool DIRECT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? (FUSED || DIRECT ? 3 : 4) : 2)))
 void decode_attn_kernel(DecodeAttnArgs a) {
     // wave-uniform by construction; readfirstlane lets the compiler keep the item's
     // indices in scalar registers (no per-lane page-id selection loops)
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     for (int item = blockIdx.x * 4 + wave;; item += gridDim.x * 4)
-        if (!decode_attn_item<T, GROUP, FUSED>(a, item)) break;
+        if (!decode_attn_item<T, GROUP, FUSED, DIRECT>(a, item)) break;
 }
 
 // The split of a stream's L cached positions for the step's chunk bound c (a multiple of
@@ -752,12 +799,18 @@ void launch_decode_attn(const DecodeAttnArgs &a, DType dt, hipStream_t s, hipEve
         else hipLaunchKernelGGL(kernel, grid, block, 0, s, a);  // plain launch (graph capture)
     };
     const bool fused = a.qkv != nullptr && !a.shared;
+    auto pick = [&](auto t, auto g) {
+        using T = decltype(t);
+        constexpr int G = decltype(g)::value;
+        if (a.direct) fused ? go(decode_attn_kernel<T, G, true, true>) : go(decode_attn_kernel<T, G, false, true>);
+        else fused ? go(decode_attn_kernel<T, G, true, false>) : go(decode_attn_kernel<T, G, false, false>);
+    };
     if (dt == DT_BF16) {
-        if (group == 2) fused ? go(decode_attn_kernel<bf16_t, 2, true>) : go(decode_attn_kernel<bf16_t, 2, false>);
-        else fused ? go(decode_attn_kernel<bf16_t, 1, true>) : go(decode_attn_kernel<bf16_t, 1, false>);
+        if (group == 2) pick(bf16_t(), std::integral_constant<int, 2>());
+        else pick(bf16_t(), std::integral_constant<int, 1>());
     } else {
-        if (group == 2) fused ? go(decode_attn_kernel<float, 2, true>) : go(decode_attn_kernel<float, 2, false>);
-        else fused ? go(decode_attn_kernel<float, 1, true>) : go(decode_attn_kernel<float, 1, false>);
+        if (group == 2) pick(float(), std::integral_constant<int, 2>());
+        else pick(float(), std::integral_constant<int, 1>());
     }
 }
 

@@ -162,6 +162,12 @@ struct DecodeAttnArgs {
     int *plan_pages;      // [plan_cap][64]: page ids of each item's chunk (one per lane)
     int plan_cap;
     int target_items;
+    // Direct mode (q_len = 1 decode whose caches fit one chunk: max_pages * page <= chunk):
+    // one item per (stream, KV head) over its whole cache, positions and page ids read from
+    // pos / page_table (no work list), the output rows written by the attention kernel
+    // itself (no partials, no merge; zero rows for a negative position), FLAG_POSITION
+    // raised by it.
+    int direct;
     float *part;          // [B][H][part_stride][132]: m, l, pad, pad, acc[128]
     void *out;            // [B][H*128] operand dtype (out_mt > 0: bf16, fragment-major)
     int out_mt;

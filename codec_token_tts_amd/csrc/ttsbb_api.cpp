@@ -986,9 +986,14 @@ static ttsbb_status paged_forward(ttsbb_ctx *ctx, int32_t batch, float *x, int32
     da.scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
     da.shared = prefill ? 1 : 0;
     da.max_pos = g.max_pos;
-    if (!prefill) da.flag = ctx->flag;  // the prefill's positions are checked by the rope kernel
-    launch_decode_plan(da, ctx->stream);
-    da.flag = nullptr;
+    // caches that fit one chunk: the attention covers each stream whole and writes the
+    // output rows itself (no work list, no merge launch)
+    da.direct = !prefill && n_chunks == 1 ? 1 : 0;
+    if (!da.direct) {
+        if (!prefill) da.flag = ctx->flag;  // the prefill's positions are checked by the rope kernel
+        launch_decode_plan(da, ctx->stream);
+        da.flag = nullptr;
+    }
 
     for (int l = 0; l < g.n_layers; ++l) {
         const ttsbb_layer &L = ctx->layers[l];
@@ -1044,7 +1049,7 @@ static ttsbb_status paged_forward(ttsbb_ctx *ctx, int32_t batch, float *x, int32
             KScope k(ctx, TTSBB_K_DECODE_ATTN, true);
             launch_decode_attn(d, ctx->dt, ctx->stream, k.start(), k.stop());
         }
-        {
+        if (!d.direct) {
             KScope k(ctx, TTSBB_K_DECODE_COMBINE);
             launch_decode_combine(d, ctx->dt, ctx->stream);
         }

@@ -335,6 +335,84 @@ def test_decode_bf16_untapped_fragment_major(lengths):
         m.close()
 
 
+@pytest.mark.parametrize("bf16,lengths,tap", [(True, [(13 * i) % 111 for i in range(40)], None),
+                                              (True, [(7 * i + 3) % 127 for i in range(64)], 1),
+                                              (False, [(11 * i) % 97 for i in range(33)], 0)])
+def test_decode_direct_short_caches(bf16, lengths, tap):
+    """Caches that fit one attention chunk (33 to 64 streams of at most 8 pages): the
+    attention covers each stream whole, reading its position and page ids itself, and
+    writes the output rows directly -- no work list, no merge launch.  Outputs (and the
+    tapped layer's intermediates) against the oracle -- 1e-4 in fp32 -- and the bf16-storage
+    emulation; the positions advance."""
+    shape = CFG.Shape(n_layers=2)
+    m = Model(shape, 2, bf16, seed=17)
+    try:
+        res, ref = run_decode(m, lengths, 17, tap_layer=tap)
+        if bf16:
+            assert normwise(res["x"], ref["x"]) <= TOL_LAYER_BF16
+            assert normwise(res["x"], ref["x_emul"]) <= TOL_EMUL_BF16
+        else:
+            assert np.max(np.abs(res["x"] - ref["x"])) <= 1e-4
+        if tap is not None:
+            rtaps = rec_as_taps(ref["rec"], len(lengths))
+            for k in rtaps:
+                if bf16:
+                    assert normwise(res["taps"][k], rtaps[k]) <= TOL_LAYER_BF16, k
+                else:
+                    assert np.max(np.abs(res["taps"][k] - rtaps[k])) <= 1e-4, k
+        assert res["pos"].tolist() == [n + 1 for n in lengths]
+    finally:
+        m.close()
+
+
+@pytest.mark.parametrize("tap", [False, True])
+def test_decode_direct_negative_position(tap):
+    """Direct mode (40 streams, caches of at most 7 pages) with one stream at position -1:
+    the step raises the device flag, that stream's attention output is zero and nothing is
+    written to the pool for it, and the other streams match the oracle and the emulation."""
+    shape = CFG.Shape(n_layers=1)
+    m = Model(shape, 1, True, seed=41)
+    T = m.T
+    try:
+        B, bad = 40, 7
+        lengths = [(17 * i + 4) % 100 for i in range(B)]
+        lengths[bad] = -1
+        pt, n_pages = CFG.page_table(41, [max(n, 0) + 1 for n in lengths], extra_pages=1)
+        pool = DEV.kv_pool(41, shape, 1, [max(n, 0) for n in lengths], pt, n_pages, True)
+        before = pool.clone()
+        x_in = gen.fast_normal(41, stream_id(gen.KIND_X_IN, 0), (B, shape.hidden), 1.0)
+        x = t_f32(x_in)
+        pos = t_i32(lengths)
+        if tap:
+            T.ttsbb_set_tap_layer(m.ctx, 0)
+        T.ttsbb_decode_step(m.ctx, B, x, pos, t_i32(pt), pt.shape[1], pool, n_pages)
+        assert T.ttsbb_sync(m.ctx) == T.DEVICE_ERROR
+        assert T.ttsbb_sync(m.ctx) == T.OK
+        if tap:
+            o = read_tap(m, T.TAP_ATTN, B, shape.n_heads * 128)
+            assert np.all(o[bad] == 0)
+            T.ttsbb_set_tap_layer(m.ctx, -1)
+        xg = x.cpu().numpy()
+        assert np.all(np.isfinite(xg))
+        assert pos.cpu().numpy()[bad] == 0
+        sel = [b for b in range(B) if b != bad]
+        d = (pool != before).any(dim=-1).nonzero().cpu().numpy()
+        assert sorted({int(r[1]) for r in d}) == sorted({int(pt[b, lengths[b] // 16]) for b in sel})
+        c_ex, c_em = O.KVCache(1, len(sel)), O.KVCache(1, len(sel))
+        for i, b in enumerate(sel):
+            if lengths[b]:
+                k, v = CFG.kv_prefill(41, shape, 0, b, lengths[b], True)
+                c_ex.set(0, i, widen(k), widen(v))
+                c_em.set(0, i, widen(k), widen(v))
+        lens = [lengths[b] for b in sel]
+        out = O.decode_step(x_in[sel], lens, c_ex, m.oracle_layers(), dims_of(shape))
+        out_e = E.decode_step(x_in[sel], lens, c_em, m.oracle_layers(), dims_of(shape))
+        assert normwise(xg[sel], out) <= TOL_LAYER_BF16
+        assert normwise(xg[sel], out_e) <= TOL_EMUL_BF16
+    finally:
+        m.close()
+
+
 # ---------------------------------------------------------------------------------------
 def run_maskgit(m: Model, n_text, n_frames, n_cb, V, mask_id, n_unmask, seed, tap_layer=None,
                 text_vocab=500, masked_frac=0.5):
