@@ -18,7 +18,9 @@
 // fixed order in the combine kernel (deterministic, no atomics).  The items come from a
 // work list built once per step on the device (decode_plan_kernel): only chunks that hold
 // positions, each with its page ids, and for q_len = 1 decode a chunk size chosen so that
-// the items fill two workgroups per CU.
+// the items fill two workgroups per CU.  When every cache fits one chunk (direct mode),
+// a wave covers its stream whole, reads the position and page ids itself and writes the
+// output rows itself: no work list and no merge.
 #include <hip/hip_ext.h>
 #include <type_traits>
 #include <math.h>
@@ -572,9 +574,10 @@ __device__ __forceinline__ bool decode_attn_item(const DecodeAttnArgs &a, int it
 }
 
 // The grid holds as many waves as the work list's budget (target_items, or every chunk
-// the caches could hold when there is no budget); each wave takes items wave, wave +
-// (waves in the grid), ... -- one item per wave when the list fits the budget, so no
-// workgroup is dispatched without work.
+// the caches could hold when there is no budget; in direct mode one per stream and KV
+// head within that budget); each wave takes items wave, wave + (waves in the grid), ...
+// -- one item per wave when the list fits the budget, so no workgroup is dispatched
+// without work.
 // DIRECT: a.direct (a separate instantiation, so the work-list kernels keep their
 // registers; short caches are latency-bound, so it takes the 3-wave register budget).
 template <typename T, int GROUP, bool FUSED, bool DIRECT>
