@@ -817,6 +817,34 @@ def test_rvq_decode(n_frames, n_q, cb, dim, out_dim):
         m.close()
 
 
+def test_rvq_decode_unaligned_tables_take_the_vector_kernel():
+    """Tables that are not 16-byte aligned (views one float into their buffers) cannot be
+    read with the matrix-core kernel's 16-byte loads: the vector kernel runs them, with
+    the same result to the fp32 bound."""
+    m = Model(CFG.Shape(n_layers=1), 0, False, seed=13)
+    try:
+        T = m.T
+        n_frames, n_q, cb, dim, out_dim = 70, 4, 50, 32, 96
+        seed = 14
+        emb = gen.normal_f32(seed, stream_id(gen.KIND_CB_TABLE, 3), (n_q, cb, dim), 1.0)
+        w = gen.normal_f32(seed, stream_id(gen.KIND_HEAD, 3), (n_q, out_dim, dim), 0.05)
+        b = gen.normal_f32(seed, stream_id(gen.KIND_FINAL_NORM, 3), (n_q, out_dim), 0.1)
+        codes = gen.uniform_int(seed, stream_id(gen.KIND_CODES, 3), (n_q, n_frames), cb)
+        emb_buf = torch().zeros(emb.size + 1, dtype=torch().float32, device="cuda")
+        emb_buf[1:] = torch().from_numpy(emb.reshape(-1)).cuda()
+        w_buf = torch().zeros(w.size + 1, dtype=torch().float32, device="cuda")
+        w_buf[1:] = torch().from_numpy(w.reshape(-1)).cuda()
+        emb_v, w_v = emb_buf[1:], w_buf[1:]
+        assert emb_v.data_ptr() % 16 != 0 and w_v.data_ptr() % 16 != 0
+        out = torch().empty((n_frames, out_dim), dtype=torch().float32, device="cuda")
+        T.ttsbb_rvq_decode(m.ctx, n_frames, n_q, cb, dim, out_dim, t_i32(codes), emb_v, w_v, t_f32(b), out)
+        assert T.ttsbb_sync(m.ctx) == T.OK
+        ref = O.rvq_decode(codes, emb, w, b)
+        assert np.max(np.abs(out.cpu().numpy() - ref)) <= 1e-4
+    finally:
+        m.close()
+
+
 # ---------------------------------------------------------------------------------------
 # Causal prefill of one stream into its paged cache
 # ---------------------------------------------------------------------------------------
