@@ -301,7 +301,10 @@ ttsbb_status ttsbb_philox_words(ttsbb_ctx *ctx, uint64_t seed, uint64_t block0, 
  *   codes int32 [n_q][n_frames]; embed fp32 [n_q][codebook_size][codebook_dim];
  *   proj_w fp32 [n_q][out_dim][codebook_dim]; proj_b fp32 [n_q][out_dim];
  *   out fp32 [n_frames][out_dim].  All device pointers; a code outside
- *   [0, codebook_size) is clamped and raises the device flag (ttsbb_sync). */
+ *   [0, codebook_size) is clamped and raises the device flag (ttsbb_sync).  The sums run
+ *   on the fp32 matrix cores when codebook_dim is a multiple of 8 and at most 64, n_q <= 32
+ *   and embed and proj_w are 16-byte aligned; otherwise on the vector units (same result
+ *   within fp32 rounding; the summation order differs from the formula's). */
 ttsbb_status ttsbb_rvq_decode(ttsbb_ctx *ctx, int32_t n_frames, int32_t n_q, int32_t codebook_size,
                               int32_t codebook_dim, int32_t out_dim, const int32_t *codes, const float *embed,
                               const float *proj_w, const float *proj_b, float *out);
