@@ -342,17 +342,14 @@ __device__ __forceinline__ void norm_rope_head(const float *x, const float *gain
 // One work item (stream, KV head, chunk) of the decode attention, on one wave; returns
 // false when `item` lies past the step's work list.
 template <typename T, int GROUP, bool FUSED, bool DIRECT>
-__device__ __forceinline__ bool decode_attn_item(const DecodeAttnArgs &a, int item) {
+__device__ __forceinline__ bool decode_attn_item(const DecodeAttnArgs &a, int pair, int hk, int limit) {
     constexpr int EPL = KVRaw<T>::EPL;
     constexpr int LPR = 128 / EPL;  // lanes per 128-dim row
     constexpr int RPL = 64 / LPR;   // rows (tokens) per wave load
     constexpr int NR = 16 / RPL;    // wave loads per 16-token page block
     const int lane = threadIdx.x & 63;
-    // pair item / Hkv: a (stream, chunk, token position) of the step's work list, or in
-    // direct mode the stream; KV heads vary fastest, so the waves of a block stream
-    // neighbouring 4 KB blocks of the same pool pages (a page holds all heads' K and V
-    // contiguously)
-    const int pair = item / a.Hkv, hk = item % a.Hkv;
+    // pair: an entry of the step's work list (entries at or past `limit` -- plan_n[0] when
+    // limit < 0 -- and empty ones do nothing), or in direct mode the stream
     const int d0 = (lane % LPR) * EPL;
     const int rsub = lane / LPR;
     const int cap = a.max_pages * a.page;
@@ -387,15 +384,15 @@ __device__ __forceinline__ bool decode_attn_item(const DecodeAttnArgs &a, int it
         }
     } else {
         const int pc = min(pair, a.plan_cap - 1);
-        const int n_pairs = *a.plan_n;
+        const int n_pairs = limit >= 0 ? limit : *a.plan_n;
         const int4 w = a.plan[pc];
         my_page = a.plan_pages[(int64_t)pc * 64 + lane];
-        if (pair >= n_pairs) return false;
         b = w.x;
-        c = w.y;
+        c = w.y & 0xFFFF;
+        chunk = (w.y >> 16) * a.page;  // the piece's pages
         p_tok = w.z;
-        chunk = w.w;
-        p_begin = c * chunk;
+        p_begin = w.w;
+        if (pair >= n_pairs || chunk == 0 || b >= a.B || c >= a.part_stride) return false;
     }
     const int pg_first = p_begin / a.page;
     // FUSED: the raw q rows and the q gains do not depend on the position either; they
@@ -586,8 +583,52 @@ void decode_attn_kernel(DecodeAttnArgs a) {
     // wave-uniform by construction; readfirstlane lets the compiler keep the item's
     // indices in scalar registers (no per-lane page-id selection loops)
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    for (int item = blockIdx.x * 4 + wave;; item += gridDim.x * 4)
-        if (!decode_attn_item<T, GROUP, FUSED, DIRECT>(a, item)) break;
+    // segment mode: segment k on workgroups of parity k & 1 (Hkv / 4 of them, one KV head
+    // per wave); KV heads vary fastest, so a block streams neighbouring 4 KB blocks of the
+    // same pool pages (a page holds all heads' K and V contiguously)
+    const bool seg = !DIRECT && a.target_items > 0;
+    int k = 0, hk = 0;
+    int2 more = make_int2(0, 0);
+    if (seg) {
+        if ((a.Hkv & 3) == 0) {
+            const int bps = a.Hkv >> 2, t = blockIdx.x >> 1;
+            k = 2 * (t / bps) + (blockIdx.x & 1);
+            hk = (t % bps) * 4 + wave;
+        } else {
+            const int item = blockIdx.x * 4 + wave;
+            k = item / a.Hkv;
+            hk = item % a.Hkv;
+        }
+        if (k >= a.n_seg) return;
+        more = a.seg_cont[k];  // requested with the first piece's entry
+    }
+    // one call site, so that the item's code is inlined once: segment mode takes the first
+    // piece (entry k), then entries n_seg + more.x + j - 1 (`more` is read only after the
+    // first piece, so its load is not waited for before that piece's loads); otherwise
+    // items wave, wave + (waves in the grid), ...
+    int pair, h, limit, item = 0;
+    if (seg) {
+        pair = k;
+        h = hk;
+        limit = a.n_seg;
+    } else {
+        item = blockIdx.x * 4 + wave;
+        pair = item / a.Hkv;
+        h = item % a.Hkv;
+        limit = -1;
+    }
+    for (int j = 0;; ++j) {
+        if (!decode_attn_item<T, GROUP, FUSED, DIRECT>(a, pair, h, limit)) break;
+        if (seg) {
+            if (j >= more.y) break;
+            pair = a.n_seg + more.x + j;
+            limit = a.plan_cap;
+        } else {
+            item += gridDim.x * 4;
+            pair = item / a.Hkv;
+            h = item % a.Hkv;
+        }
+    }
 }
 
 // The split of a stream's L cached positions for the step's chunk bound c (a multiple of
@@ -607,23 +648,72 @@ __device__ __forceinline__ void stream_split(int L, int c, int page, int &n, int
 }
 
 // The decode attention's work list, built once per step (the positions are the same in
-// every layer): the (stream, chunk) pairs that hold positions, stream by stream, each
-// with its stream's token position and the chunk size, and their number in plan_n[0].
-// The attention launch is sized for the longest possible streams; with the list no wave
-// is started for an empty chunk.  Balanced split (target_items > 0, q_len = 1 decode):
-// the chunk grows from a.chunk, a page at a time, until the step's work items fit
-// target_items -- two workgroups of four waves per CU -- so every item starts at the
-// launch's beginning, no CU holds more items than another and none waits for a slot (at
-// most 64 pages per chunk); plan_n[1] = the chunk.  With a.flag set, a token outside the
-// cache raises FLAG_POSITION (streams with no valid position get no pair).
+// every layer).  Streams with no valid position get no piece; with a.flag set such a
+// token raises FLAG_POSITION.
+//  * target_items == 0 (prefill rows): every stream is cut into ceil(L / chunk) equal
+//    page-aligned pieces (stream_split), entries in stream order.
+//  * target_items > 0 (q_len = 1 decode): the streams' pages laid end to end are cut into
+//    w_eff <= n_seg segments; a piece is a stream's part of a segment, at most 64 pages.
+//    When the segments average at least SEG_WEIGHTED_PAGES pages (bandwidth-bound waves)
+//    their page counts are weighted SEG_WE : SEG_WO between even and odd segments (the
+//    even ones run on the even XCDs, which stream faster), so all waves of the launch
+//    finish at about the same time; shorter segments are equal (latency-bound waves: the
+//    longest chain sets the time).  w_eff starts at min(n_seg, ceil(P / 2)) for P pages
+//    (every segment then holds one or more pages) and drops until each stream's pieces fit its
+//    part_stride partial slots (always true by w_eff = 2: at most ceil(pages / 64) + 1
+//    pieces, and part_stride >= n_chunks + 2).
+constexpr int SEG_WE = 9, SEG_WO = 8;
+constexpr int SEG_WEIGHTED_PAGES = 8;  // least mean segment (pages) that takes the weights
+
+// First page of segment k of w over P pages with weights we (even k) and wo (odd k); P
+// for k >= w.  64-bit products: P can exceed 2^31 / (w * 9).
+__device__ inline int seg_start(int k, int w, int P, int we, int wo) {
+    if (k >= w) return P;
+    auto before = [&](int j) { return (int64_t)(j >> 1) * (we + wo) + (j & 1) * we; };
+    return (int)((int64_t)P * before(k) / before(w));
+}
+
+// The segment that holds page q: the last k < w with start[k] <= q (start[] in LDS,
+// non-decreasing, start[0] = 0).
+__device__ inline int seg_find(const int *start, int w, int q) {
+    int lo = 0, hi = w - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (start[mid] <= q) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// Whether no segment exceeds 64 pages (one piece per segment and stream): a segment's
+// size is at most ceil(P * max(we, wo) / before(w)).
+__device__ inline bool seg_small(int w, int P, int we, int wo) {
+    const int64_t bw = (int64_t)(w >> 1) * (we + wo) + (w & 1) * we;
+    return (int64_t)P * max(we, wo) <= 64 * bw;
+}
+
+// Pieces of a stream whose np > 0 pages start at page `off` of the laid-out sequence (no
+// segment is empty; `small`: seg_small holds, so the count is that of the segments its
+// first and last pages span).
+__device__ inline int seg_pieces(const int *start, int w, int off, int np, bool small) {
+    if (small) return seg_find(start, w, off + np - 1) - seg_find(start, w, off) + 1;
+    int n = 0;
+    for (int q = off, k = seg_find(start, w, off); q < off + np && k < w; ++k) {
+        const int se = min(off + np, start[k + 1]);
+        n += (se - q + 63) / 64;
+        q = max(q, se);
+    }
+    return n;
+}
+
 __global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeAttnArgs a, int4 *plan, int *plan_n) {
     __shared__ int wsum[16];
+    __shared__ int sstart[SEG_MAX + 1];  // q_len = 1 decode: first page of each segment
+    __shared__ int sfirst[SEG_MAX];      // ... and the global index of its first piece
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int cap = a.max_pages * a.page;
-    auto length = [&](int b) {  // positions of stream b in the cache (0 for an invalid token)
-        const int p_tok = a.shared ? a.pos[0] + b : a.pos[b];
-        return max(0, min(p_tok + 1, cap));
-    };
+    auto token = [&](int b) { return a.shared ? a.pos[0] + b : a.pos[b]; };
+    // positions of stream b in the cache (0 for an invalid token)
+    auto length = [&](int b) { return max(0, min(token(b) + 1, cap)); };
     auto block_sum = [&](int v) {
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o, WAVE);
@@ -634,62 +724,149 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeAttnArgs a, int
         for (int k = 0; k < 16; ++k) t += wsum[k];
         return t;
     };
-    int chunk = a.chunk;
-    if (a.target_items > 0) {
-        int tot = 0;
-        for (int b = tid; b < a.B; b += 1024) tot += length(b);
-        tot = block_sum(tot);
-        const int per = (int)(((int64_t)tot * a.Hkv + a.target_items - 1) / a.target_items);
-        chunk = min(max(a.chunk, (per + a.page - 1) / a.page * a.page), 64 * a.page);
-        for (;;) {
-            int n = 0;
-            for (int b = tid; b < a.B; b += 1024) n += (length(b) + chunk - 1) / chunk;
-            n = block_sum(n);
-            if ((int64_t)n * a.Hkv <= a.target_items || chunk >= 64 * a.page) break;
-            chunk += a.page;
-        }
-    }
-    int base = 0;
-    for (int b0 = 0; b0 < a.B; b0 += 1024) {
-        const int b = b0 + tid;
-        int nc = 0, p_tok = 0, len = chunk;
-        if (b < a.B) {
-            p_tok = a.shared ? a.pos[0] + b : a.pos[b];
-            if (a.flag && (p_tok < 0 || p_tok >= a.max_pos || p_tok >= cap)) raise_flag(a.flag, FLAG_POSITION);
-            const int L = min(p_tok + 1, cap);
-            stream_split(L, chunk, a.page, nc, len);  // nc <= ceil(L / chunk) <= n_chunks
-        }
-        int v = nc;  // inclusive scan: inside the wave, then over the waves' totals
+    auto block_max = [&](int v) {
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) v = max(v, __shfl_xor(v, o, WAVE));
+        __syncthreads();
+        if (lane == 0) wsum[wave] = v;
+        __syncthreads();
+        int t = 0;
+        for (int k = 0; k < 16; ++k) t = max(t, wsum[k]);
+        return t;
+    };
+    // exclusive scan over the block's threads; `total` = the sum over all of them
+    auto block_scan = [&](int v, int &total) {
+        int incl = v;
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
-            const int t = __shfl_up(v, o, WAVE);
-            if (lane >= o) v += t;
+            const int t = __shfl_up(incl, o, WAVE);
+            if (lane >= o) incl += t;
         }
-        __syncthreads();  // wsum's previous use is over
-        if (lane == 63) wsum[wave] = v;
         __syncthreads();
-        int off = base + v - nc, total = base;
+        if (lane == 63) wsum[wave] = incl;
+        __syncthreads();
+        int off = incl - v;
+        total = 0;
         for (int k = 0; k < 16; ++k) {
             if (k < wave) off += wsum[k];
             total += wsum[k];
         }
-        for (int c = 0; c < nc; ++c) plan[off + c] = make_int4(b, c, p_tok, len);
-        base = total;
+        return off;
+    };
+    auto check = [&](int b) {
+        const int p_tok = token(b);
+        if (a.flag && (p_tok < 0 || p_tok >= a.max_pos || p_tok >= cap)) raise_flag(a.flag, FLAG_POSITION);
+        return p_tok;
+    };
+
+    int n_entries = 0, info = a.chunk;
+    if (a.target_items == 0) {
+        int base = 0;
+        for (int b0 = 0; b0 < a.B; b0 += 1024) {
+            const int b = b0 + tid;
+            int nc = 0, p_tok = 0, len = a.chunk;
+            if (b < a.B) {
+                p_tok = check(b);
+                stream_split(length(b), a.chunk, a.page, nc, len);  // nc <= n_chunks
+                a.plan_nc[b] = nc;
+            }
+            int total;
+            const int off = base + block_scan(nc, total);
+            for (int c = 0; c < nc; ++c)
+                if (off + c < a.plan_cap) plan[off + c] = make_int4(b, c | ((len / a.page) << 16), p_tok, c * len);
+            base += total;
+        }
+        n_entries = min(base, a.plan_cap);
+    } else {
+        const int W = a.n_seg;  // <= SEG_MAX
+        // streams 0 .. 1023: token and page count read once, kept in a register
+        const int tok0 = tid < a.B ? check(tid) : 0;
+        const int np0 = tid < a.B ? (max(0, min(tok0 + 1, cap)) + a.page - 1) / a.page : 0;
+        auto pages_of = [&](int b0) {
+            const int b = b0 + tid;
+            return b0 == 0 ? np0 : (b < a.B ? (length(b) + a.page - 1) / a.page : 0);
+        };
+        int P = np0;
+        for (int b = 1024 + tid; b < a.B; b += 1024) P += (length(b) + a.page - 1) / a.page;
+        P = block_sum(P);
+        int w = P == 0 ? 0 : min(W, (P + 1) / 2);
+        bool small;
+        while (true) {
+            const bool weighted = w > 0 && P >= SEG_WEIGHTED_PAGES * w;
+            const int we = weighted ? SEG_WE : 1, wo = weighted ? SEG_WO : 1;
+            for (int k = tid; k <= w; k += 1024) sstart[k] = seg_start(k, w, P, we, wo);
+            small = seg_small(w, P, we, wo);
+            __syncthreads();
+            if (w <= 1) break;
+            int worst = 0, base = 0;
+            for (int b0 = 0; b0 < a.B; b0 += 1024) {
+                const int np = pages_of(b0);
+                int total;
+                const int off = base + block_scan(np, total);
+                if (np > 0) worst = max(worst, seg_pieces(sstart, w, off, np, small));
+                base += total;
+            }
+            if (block_max(worst) <= a.part_stride) break;  // (its barriers end the reads of sstart)
+            w -= w > 2 ? 2 : 1;
+        }
+        // the pieces, in stream and position order; G counts them over all streams.  The
+        // first piece of segment k goes to entry k, the others to n_seg + G - (k + 1) (every
+        // segment below w holds pages, so k + 1 first pieces precede), which makes a
+        // segment's further pieces consecutive entries; sfirst[k] = G of segment k's first
+        // piece.
+        int base = 0, gbase = 0;
+        for (int b0 = 0; b0 < a.B; b0 += 1024) {
+            const int b = b0 + tid;
+            const int np = pages_of(b0);
+            const int p_tok = b0 == 0 ? tok0 : (b < a.B ? check(b) : 0);
+            int t1, t2;
+            const int off = base + block_scan(np, t1);
+            const int nc = np > 0 ? seg_pieces(sstart, w, off, np, small) : 0;
+            const int g0 = gbase + block_scan(nc, t2);
+            if (b < a.B) a.plan_nc[b] = nc;
+            int c = 0;
+            for (int q0 = off, k = np > 0 ? seg_find(sstart, w, off) : w; q0 < off + np && k < w; ++k) {
+                const int ks = sstart[k], se = min(off + np, sstart[k + 1]);
+                for (int q = q0; q < se; q += 64) {
+                    const int n = min(64, se - q);
+                    const bool first = q == ks;
+                    const int slot = first ? k : W + g0 + c - (k + 1);
+                    if (slot < a.plan_cap) plan[slot] = make_int4(b, c | (n << 16), p_tok, (q - off) * a.page);
+                    if (first) sfirst[k] = g0 + c;
+                    ++c;
+                }
+                q0 = max(q0, se);
+            }
+            base += t1;
+            gbase += t2;
+        }
+        __syncthreads();  // sfirst is complete
+        for (int k = tid; k < W; k += 1024) {
+            if (k < w) {
+                const int gk = sfirst[k], gn = k + 1 < w ? sfirst[k + 1] : gbase;
+                a.seg_cont[k] = make_int2(gk - k, gn - gk - 1);
+            } else {
+                a.seg_cont[k] = make_int2(0, 0);
+                plan[k] = make_int4(0, 0, 0, 0);  // an empty segment: no pages
+            }
+        }
+        n_entries = min(W + gbase - w, a.plan_cap);
+        info = w;
     }
-    // page ids of every pair's chunk, one per lane of the attention wave (clamped into the
-    // stream's page-table row); the pairs written above are visible after the barrier.
+    // page ids of every entry's piece, one per lane of the attention wave (clamped into the
+    // stream's page-table row); the entries written above are visible after the barrier.
     // Four entries per thread and round, every load requested before any store: a round
-    // is two dependent loads (the pair, then its page id), not eight.
+    // is two dependent loads (the entry, then its page id), not eight.
     __syncthreads();
-    const int n_ids = base * 64;
+    const int n_ids = n_entries * 64;
     for (int idx0 = tid; idx0 < n_ids; idx0 += 4 * 1024) {
         int row[4], pg[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int idx = min(idx0 + u * 1024, n_ids - 1);
-            const int4 w = plan[idx >> 6];
-            row[u] = a.shared ? 0 : w.x;
-            pg[u] = min(w.y * w.w / a.page + (idx & 63), a.max_pages - 1);
+            const int4 e = plan[idx >> 6];
+            row[u] = a.shared ? 0 : e.x;
+            pg[u] = min(e.w / a.page + (idx & 63), a.max_pages - 1);
         }
         int id[4];
 #pragma unroll
@@ -699,8 +876,8 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeAttnArgs a, int
             if (idx0 + u * 1024 < n_ids) a.plan_pages[idx0 + u * 1024] = id[u];
     }
     if (tid == 0) {
-        plan_n[0] = base;
-        plan_n[1] = chunk;
+        plan_n[0] = n_entries;
+        plan_n[1] = info;
     }
 }
 
@@ -756,12 +933,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeAttnArgs a) {
     const int item = blockIdx.x * 4 + wave;
     if (item >= a.B * a.H) return;
     const int h = item % a.H, b = item / a.H;
-    int L = (a.shared ? a.pos[0] + b : a.pos[b]) + 1;
-    const int cap = a.max_pages * a.page;
-    if (L > cap) L = cap;
-    const int chunk = a.plan_n[1];  // the step's chunk bound (from the work list)
-    int nc, len;
-    stream_split(L, chunk, a.page, nc, len);  // the stream's items, as the work list made them
+    const int nc = a.plan_nc[b];  // the stream's pieces (partials), from the work list
     if (nc <= 0) {  // a token outside the cache (flagged by the plan) has no chunks: zeros
         if (lane < 32) {
             const int k = h * 128 + lane * 4;
@@ -796,6 +968,7 @@ void launch_decode_attn(const DecodeAttnArgs &a, DType dt, hipStream_t s, hipEve
     const int group = a.H / a.Hkv;
     int items = a.B * a.Hkv * a.n_chunks;  // at most; the work list holds the real ones
     if (a.target_items > 0 && a.target_items < items) items = a.target_items;  // the list's budget
+    if (a.target_items > 0 && !a.direct) items = a.n_seg * a.Hkv;  // one wave per segment and KV head
     const dim3 grid((items + 3) / 4), block(256);
     auto go = [&](auto kernel) {
         if (ev0 || ev1) hipExtLaunchKernelGGL(kernel, grid, block, 0, s, ev0, ev1, 0, a);

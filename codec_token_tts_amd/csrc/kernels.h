@@ -144,6 +144,8 @@ struct PoolDenseArgs {
 void launch_pool_dense(const PoolDenseArgs &a, hipStream_t s);
 
 // ---- K5: split-sequence decode attention over the paged pool -----------------------
+constexpr int SEG_MAX = 2048;  // most work-list segments of a q_len = 1 decode step
+
 struct DecodeAttnArgs {
     const float *q;  // [B][H*128] fp32
     void *pool_layer;     // [n_pages][2][Hkv][page][128] (written only by the fused step-token path)
@@ -153,15 +155,30 @@ struct DecodeAttnArgs {
     int B, H, Hkv;
     int chunk, n_chunks;  // least positions per chunk (multiple of page), most chunks per stream
     int part_stride;      // chunks per (stream, head) in part: >= n_chunks
-    // the step's work list (launch_decode_plan): plan_n[0] items (stream, chunk index,
-    // token position, chunk size) in dispatch order, plan_n[1] the step's chunk size
-    // (>= chunk); plan_cap >= B * n_chunks entries.  target_items > 0: the plan grows the
-    // chunk until the items fit that many waves.
+    // The step's work list (launch_decode_plan).  An entry is one piece of a stream's
+    // cached positions: (stream, piece index | pages << 16, token position, first
+    // position); plan_pages [plan_cap][64] holds its page ids (one per lane).  A stream's
+    // pieces are numbered 0 .. plan_nc[b] - 1 in position order (its partials).
+    //  * target_items == 0 (prefill rows): each stream cut into equal page-aligned pieces
+    //    of at most `chunk` positions, one wave each, entries 0 .. plan_n[0] - 1 in stream
+    //    order; plan_cap >= B * n_chunks.
+    //  * target_items > 0 (q_len = 1 decode): up to n_seg (even) segments of the streams'
+    //    pages laid end to end; segments that average 8 pages or more are weighted 9 : 8
+    //    between even and odd ones, shorter ones are equal.  Segment k runs on workgroups
+    //    of parity k & 1, i.e. on the even or the odd XCDs (workgroup b runs on XCD b mod
+    //    8, and the odd XCDs stream ~10% slower).  A piece
+    //    is a stream's part of a segment (at most 64 pages): entry k < n_seg is segment
+    //    k's first piece (0 pages: empty), its further pieces are entries n_seg +
+    //    seg_cont[k].x + j, j < seg_cont[k].y.  part_stride >= n_chunks + 2 and
+    //    plan_cap >= B * part_stride + n_seg.
     const int4 *plan;
     const int *plan_n;
-    int *plan_pages;      // [plan_cap][64]: page ids of each item's chunk (one per lane)
+    int *plan_pages;
     int plan_cap;
     int target_items;
+    int n_seg;            // <= SEG_MAX
+    int2 *seg_cont;       // [n_seg]
+    int *plan_nc;         // [B]
     // Direct mode (q_len = 1 decode whose caches fit one chunk: max_pages * page <= chunk):
     // one item per (stream, KV head) over its whole cache, positions and page ids read from
     // pos / page_table (no work list), the output rows written by the attention kernel

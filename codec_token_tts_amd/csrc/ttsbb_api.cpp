@@ -29,6 +29,7 @@ using namespace ttsbb;
 namespace {
 
 constexpr int MAX_CHUNKS = 32;   // decode attention partials per (stream, head)
+constexpr int SEG_PER_CU = 8;    // q_len = 1 decode attention waves per CU (work-list segments)
 constexpr int PART_STRIDE = 132; // floats per partial (m, l, 2 pad, 128 dims)
 
 // The decode step without allocation (ttsbb_decode_step_noalloc): its per-call scratch
@@ -84,9 +85,11 @@ struct ttsbb_ctx {
     int pend_rows = 0;
     float2 *rope = nullptr;
     int *flag = nullptr;
-    int4 *plan = nullptr;     // decode attention work list (work_rows * MAX_CHUNKS pairs)
+    int4 *plan = nullptr;     // decode attention work list (plan_entries(work_rows) entries)
     int *plan_n = nullptr;
-    int *plan_pages = nullptr;  // [work_rows * MAX_CHUNKS][64]
+    int *plan_pages = nullptr;  // [plan_entries][64]
+    int2 *seg_cont = nullptr;   // [SEG_PER_CU * n_cu]
+    int *plan_nc = nullptr;     // [work_rows]
     int work_rows = 0;          // rows the attention work list and partials are sized for
     void *static_scratch = nullptr;  // this device's copy of the static scratch array
     std::vector<void *> allocs;
@@ -95,6 +98,10 @@ struct ttsbb_ctx {
     Tap taps[TTSBB_TAP_COUNT];
     Prof prof;
 };
+
+// Entries of the decode attention's work list for `rows` streams: MAX_CHUNKS pieces per
+// stream plus one first-piece entry per segment.
+static size_t plan_entries(const ttsbb_ctx *c, size_t rows) { return rows * MAX_CHUNKS + (size_t)SEG_PER_CU * c->n_cu; }
 
 // The static scratch of ttsbb_decode_step_noalloc.  Host code never uses this name as an
 // address (it is a host-side stand-in): the device address of each GPU's copy comes from
@@ -298,9 +305,11 @@ TTSBB_API ttsbb_status ttsbb_create(const ttsbb_config *cfg, const ttsbb_layer *
               dev_alloc(c, (void **)&c->gpart, (size_t)c->gpart_cap * 4) &&
               dev_alloc(c, (void **)&c->rope, (size_t)g.max_pos * 64 * sizeof(float2)) &&
               dev_alloc(c, (void **)&c->flag, 256) &&
-              dev_alloc(c, (void **)&c->plan, R * MAX_CHUNKS * sizeof(int4)) &&
+              dev_alloc(c, (void **)&c->plan, plan_entries(c, R) * sizeof(int4)) &&
               dev_alloc(c, (void **)&c->plan_n, 256) &&
-              dev_alloc(c, (void **)&c->plan_pages, R * MAX_CHUNKS * 64 * sizeof(int));
+              dev_alloc(c, (void **)&c->plan_pages, plan_entries(c, R) * 64 * sizeof(int)) &&
+              dev_alloc(c, (void **)&c->seg_cont, (size_t)SEG_PER_CU * c->n_cu * sizeof(int2)) &&
+              dev_alloc(c, (void **)&c->plan_nc, R * sizeof(int));
     if (!ok) {
         free_all(c);
         delete c;
@@ -953,7 +962,10 @@ static ttsbb_status paged_forward(ttsbb_ctx *ctx, int32_t batch, float *x, int32
     while (chunk > g.kv_page && (int64_t)batch * Hkv * ((cap + chunk - 1) / chunk) < 256) chunk /= 2;
     chunk = round_up(chunk, g.kv_page);
     int n_chunks = (cap + chunk - 1) / chunk;
-    while ((int64_t)batch * n_chunks > (int64_t)ctx->work_rows * MAX_CHUNKS) {
+    // q_len = 1 decode: a stream's weighted-segment pieces may number two more than its
+    // chunks (the plan kernel's guarantee), so its partial slots hold n_chunks + 2
+    const int extra = prefill ? 0 : 2;
+    while ((int64_t)batch * (n_chunks + extra) > (int64_t)ctx->work_rows * MAX_CHUNKS) {
         chunk *= 2;
         n_chunks = (cap + chunk - 1) / chunk;
     }
@@ -972,15 +984,20 @@ static ttsbb_status paged_forward(ttsbb_ctx *ctx, int32_t batch, float *x, int32
     da.Hkv = Hkv;
     da.chunk = chunk;
     da.n_chunks = n_chunks;
-    da.part_stride = n_chunks;
+    da.part_stride = n_chunks + extra;
     da.plan = ctx->plan;
     da.plan_n = ctx->plan_n;
     da.plan_pages = ctx->plan_pages;
-    da.plan_cap = (int)(ctx->work_rows * MAX_CHUNKS);
-    // q_len = 1 decode: the work list balances the items over the CUs, two workgroups of
-    // four waves per CU (measured on the 64-stream workload: 97.7 -> 95.1 us; one or three
-    // workgroups per CU, or targets between the multiples, were slower)
-    da.target_items = prefill ? 0 : 8 * ctx->n_cu;
+    da.plan_cap = (int)plan_entries(ctx, ctx->work_rows);
+    da.seg_cont = ctx->seg_cont;
+    da.plan_nc = ctx->plan_nc;
+    // q_len = 1 decode: the streams' pages cut into weighted segments, one wave per segment
+    // and KV head, two workgroups of four waves per CU (measured on the 64-stream workload:
+    // one or three workgroups per CU were slower); an even number of segments, so that
+    // both XCD parities get their share
+    da.target_items = prefill ? 0 : SEG_PER_CU * ctx->n_cu;
+    da.n_seg = (int)std::min<int64_t>({da.target_items / Hkv, (int64_t)batch * n_chunks, SEG_MAX}) & ~1;
+    if (da.n_seg < 2) da.n_seg = 2;
     da.part = ctx->part;
     da.out = ctx->attn;
     da.scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
@@ -1097,18 +1114,21 @@ struct Work {
     int64_t gpart_cap;
     int4 *plan;
     int *plan_n, *plan_pages;
+    int2 *seg_cont;
+    int *plan_nc;
     int work_rows;
 };
 
 Work work_of(const ttsbb_ctx *c) {
     return Work{c->h, c->q, c->attn, c->mlp, c->qkv, c->part, c->logits, c->gpart, c->gpart_cap,
-                c->plan, c->plan_n, c->plan_pages, c->work_rows};
+                c->plan, c->plan_n, c->plan_pages, c->seg_cont, c->plan_nc, c->work_rows};
 }
 
 void set_work(ttsbb_ctx *c, const Work &w) {
     c->h = w.h; c->q = w.q; c->attn = w.attn; c->mlp = w.mlp;
     c->qkv = w.qkv; c->part = w.part; c->logits = w.logits; c->gpart = w.gpart; c->gpart_cap = w.gpart_cap;
     c->plan = w.plan; c->plan_n = w.plan_n; c->plan_pages = w.plan_pages; c->work_rows = w.work_rows;
+    c->seg_cont = w.seg_cont; c->plan_nc = w.plan_nc;
 }
 
 // Carve the static scratch into a decode step's buffers for STATIC_MAX_BATCH rows of this
@@ -1133,9 +1153,11 @@ bool static_work(const ttsbb_ctx *c, Work &w) {
     // only the residual-add products (N = hidden) are split over K on these rows
     w.gpart_cap = (int64_t)STATIC_GPART_SPLITS * R * g.hidden;
     w.gpart = reinterpret_cast<float *>(take((size_t)w.gpart_cap * 4));
-    w.plan = reinterpret_cast<int4 *>(take(R * MAX_CHUNKS * sizeof(int4)));
+    w.plan = reinterpret_cast<int4 *>(take(plan_entries(c, R) * sizeof(int4)));
     w.plan_n = reinterpret_cast<int *>(take(256));
-    w.plan_pages = reinterpret_cast<int *>(take(R * MAX_CHUNKS * 64 * sizeof(int)));
+    w.plan_pages = reinterpret_cast<int *>(take(plan_entries(c, R) * 64 * sizeof(int)));
+    w.seg_cont = reinterpret_cast<int2 *>(take((size_t)SEG_PER_CU * c->n_cu * sizeof(int2)));
+    w.plan_nc = reinterpret_cast<int *>(take(R * sizeof(int)));
     w.work_rows = (int)R;
     return base != nullptr && off <= STATIC_SCRATCH_BYTES;
 }
