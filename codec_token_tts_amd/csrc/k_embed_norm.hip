@@ -47,19 +47,33 @@ __global__ __launch_bounds__(256) void embed_kernel(EmbedArgs a) {
             }
             load4<T>(reinterpret_cast<const T *>(a.text_table) + (int64_t)id * a.hidden + c0, outv);
         } else {
+            // EB codebooks per round: their codes in one round of loads, then their table
+            // rows in one more (indices clamped, so every load is unconditional), then the
+            // sum in codebook order -- two dependent rounds per EB codebooks, not two per
+            // codebook
+            constexpr int EB = 16;
             double acc[4] = {0.0, 0.0, 0.0, 0.0};
+            bool bad = false;
             const int32_t *crow = a.codes + (int64_t)(r - a.audio_row0) * a.code_row_stride;
-            for (int k = 0; k < a.n_cb; ++k) {
-                int code = crow[(int64_t)k * a.code_cb_stride];
-                if (code < 0 || code >= a.cb_vocab) {
-                    if (threadIdx.x == 0 && c0 == 0) raise_flag(a.flag, FLAG_CODE);
-                    code = 0;
-                }
-                float v[4];
-                load4<T>(tables + ((int64_t)k * a.cb_vocab + code) * a.hidden + c0, v);
+            for (int k0 = 0; k0 < a.n_cb; k0 += EB) {
+                int code[EB];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] += (double)v[i];
+                for (int u = 0; u < EB; ++u) code[u] = crow[(int64_t)min(k0 + u, a.n_cb - 1) * a.code_cb_stride];
+                float v[EB][4];
+#pragma unroll
+                for (int u = 0; u < EB; ++u) {
+                    const int k = min(k0 + u, a.n_cb - 1);
+                    const bool ok = code[u] >= 0 && code[u] < a.cb_vocab;
+                    bad |= !ok;
+                    load4<T>(tables + ((int64_t)k * a.cb_vocab + (ok ? code[u] : 0)) * a.hidden + c0, v[u]);
+                }
+#pragma unroll
+                for (int u = 0; u < EB; ++u) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[i] = k0 + u < a.n_cb ? acc[i] + (double)v[u][i] : acc[i];
+                }
             }
+            if (bad && threadIdx.x == 0 && c0 == 0) raise_flag(a.flag, FLAG_CODE);
 #pragma unroll
             for (int i = 0; i < 4; ++i) outv[i] = (float)acc[i];
         }

@@ -709,6 +709,9 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeAttnArgs a, int
     __shared__ int wsum[16];
     __shared__ int sstart[SEG_MAX + 1];  // q_len = 1 decode: first page of each segment
     __shared__ int sfirst[SEG_MAX];      // ... and the global index of its first piece
+    // per stream (at most 1024; per-segment writing): first laid-out page, global index of
+    // its first piece, segment of its first page, token position
+    __shared__ int soff[1025], sg0[1024], skf[1024], stok[1024];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int cap = a.max_pages * a.page;
     auto token = [&](int b) { return a.shared ? a.pos[0] + b : a.pos[b]; };
@@ -814,6 +817,10 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeAttnArgs a, int
         // segment below w holds pages, so k + 1 first pieces precede), which makes a
         // segment's further pieces consecutive entries; sfirst[k] = G of segment k's first
         // piece.
+        // At most 1024 streams and no segment above 64 pages (one piece per stream and
+        // segment): the pieces are written per segment, from the streams' offsets in LDS;
+        // otherwise each stream's thread walks its segments.
+        const bool by_seg = a.B <= 1024 && small;
         int base = 0, gbase = 0;
         for (int b0 = 0; b0 < a.B; b0 += 1024) {
             const int b = b0 + tid;
@@ -824,6 +831,17 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeAttnArgs a, int
             const int nc = np > 0 ? seg_pieces(sstart, w, off, np, small) : 0;
             const int g0 = gbase + block_scan(nc, t2);
             if (b < a.B) a.plan_nc[b] = nc;
+            if (by_seg) {
+                if (b < a.B) {
+                    soff[b] = off;
+                    sg0[b] = g0;
+                    skf[b] = np > 0 ? seg_find(sstart, w, off) : 0;
+                    stok[b] = p_tok;
+                }
+                base += t1;
+                gbase += t2;
+                continue;
+            }
             int c = 0;
             for (int q0 = off, k = np > 0 ? seg_find(sstart, w, off) : w; q0 < off + np && k < w; ++k) {
                 const int ks = sstart[k], se = min(off + np, sstart[k + 1]);
@@ -839,6 +857,32 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeAttnArgs a, int
             }
             base += t1;
             gbase += t2;
+        }
+        if (by_seg) {
+            if (tid == 0) soff[a.B] = base;  // = P
+            __syncthreads();
+            for (int k = tid; k < w; k += 1024) {
+                const int q_end = sstart[k + 1];
+                int q = sstart[k];
+                // the stream that holds page q: the last b with soff[b] <= q (its pages
+                // reach past q)
+                int lo = 0, hi = a.B - 1;
+                while (lo < hi) {
+                    const int mid = (lo + hi + 1) >> 1;
+                    if (soff[mid] <= q) lo = mid; else hi = mid - 1;
+                }
+                for (int b = lo; q < q_end; ++b) {
+                    if (soff[b + 1] <= q) continue;  // a stream without pages
+                    const int se = min(q_end, soff[b + 1]);
+                    const int c = k - skf[b];  // its pieces: one per segment from skf[b] on
+                    const int g = sg0[b] + c;
+                    const bool first = q == sstart[k];
+                    const int slot = first ? k : W + g - (k + 1);
+                    if (slot < a.plan_cap) plan[slot] = make_int4(b, c | ((se - q) << 16), stok[b], (q - soff[b]) * a.page);
+                    if (first) sfirst[k] = g;
+                    q = se;
+                }
+            }
         }
         __syncthreads();  // sfirst is complete
         for (int k = tid; k < W; k += 1024) {

@@ -90,6 +90,14 @@ def test_codebook_embed_bit_exact(bf16):
                                None, None, None, 0, out1)
         assert np.array_equal(out1.cpu().numpy(), widen(tables_h)[codes[:, 0]])
         assert T.ttsbb_codebook_embed(m.ctx, 0, K, None, None, V, None, None, None, 0, None) == T.OK
+        # 21 codebooks: the kernel's second round of codebook loads is ragged (5 of 16)
+        K2, V2 = 21, 64
+        t2_h = CFG.table(0, gen.KIND_CB_TABLE, 1, K2 * V2, 1024, bf16)
+        c2 = gen.uniform_int(0, stream_id(gen.KIND_CODES, 2), (R, K2), V2)
+        out2 = torch().empty((R, 1024), dtype=torch().float32, device="cuda")
+        T.ttsbb_codebook_embed(m.ctx, R, K2, t_i32(c2), DEV.host_to_device(t2_h), V2, None, None, None, 0, out2)
+        assert T.ttsbb_sync(m.ctx) == T.OK
+        assert np.array_equal(out2.cpu().numpy(), O.codebook_embed(c2, widen(t2_h), V2).astype(np.float32))
         # an out-of-range code raises the device flag, reported by ttsbb_sync, then clears
         bad = codes.copy()
         bad[5, 2] = V
