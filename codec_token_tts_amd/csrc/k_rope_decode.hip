@@ -237,13 +237,16 @@ template <typename T, int NR, int RPL>
 __device__ __forceinline__ bool load_page(const T *pool, int page_id, int n_pages, int Hkv, int hk,
                                           int64_t blk, int lane_off, u32x4_t (&kr)[NR], u32x4_t (&vr)[NR]) {
     // An invalid id (flagged by K4) reads page 0, which always exists, and is ignored.
+    // Non-temporal loads: a launch reads each cached K / V byte once, and the streaming
+    // policy keeps it from being allocated through L2 and the memory-side cache (64-stream
+    // decode: 93.8 -> 85.8 us per launch).
     const bool ok = page_id >= 0 && page_id < n_pages;
     const T *kb = pool + (((int64_t)(ok ? page_id : 0) * 2 + 0) * Hkv + hk) * blk + lane_off;
     const T *vb = kb + (int64_t)Hkv * blk;
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
-        kr[r] = *reinterpret_cast<const u32x4_t *>(kb + r * RPL * 128);
-        vr[r] = *reinterpret_cast<const u32x4_t *>(vb + r * RPL * 128);
+        kr[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(kb + r * RPL * 128));
+        vr[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(vb + r * RPL * 128));
     }
     return ok;
 }
