@@ -9,18 +9,20 @@
 // come from a table computed on the host in double precision.
 //
 // K5 (same ncnn section: GQA attention of the q_len=1 step; the new token attends to
-// positions 0..p).  HBM-bound.  Work item = (stream, KV head, chunk of positions);
-// one wave per item reads each 16-token page of K and V once with 16-byte lane loads
-// (a 4 KB bf16 page block is four fully coalesced wave loads) and serves all query
-// heads of the GQA group from those registers.  Scores reduce over the lanes sharing a
-// token with xor-shuffles; each lane keeps an online-softmax state (max, sum, 8 or 4
-// output dims) in base-2 units; lanes of a chunk merge by shuffles; chunks merge in a
-// fixed order in the combine kernel (deterministic, no atomics).  The items come from a
-// work list built once per step on the device (decode_plan_kernel): only chunks that hold
-// positions, each with its page ids, and for q_len = 1 decode a chunk size chosen so that
-// the items fill two workgroups per CU.  When every cache fits one chunk (direct mode),
-// a wave covers its stream whole, reads the position and page ids itself and writes the
-// output rows itself: no work list and no merge.
+// positions 0..p).  HBM-bound.  Work item = (stream, KV head, piece of positions);
+// one wave per item reads each 16-token page of K and V once with 16-byte non-temporal
+// lane loads (a 4 KB bf16 page block is four fully coalesced wave loads) and serves all
+// query heads of the GQA group from those registers.  Scores reduce over the lanes
+// sharing a token with xor-shuffles; each lane keeps an online-softmax state (max, sum,
+// 8 or 4 output dims) in base-2 units; lanes of a piece merge by shuffles; pieces merge
+// in a fixed order in the combine kernel (deterministic, no atomics).  The items come
+// from a work list built once per step on the device (decode_plan_kernel): for prefill
+// rows equal page-aligned chunks of each stream; for q_len = 1 decode the streams' pages
+// laid end to end and cut into one segment per wave and KV head (four waves per CU),
+// weighted between the even and the odd XCDs, a wave taking its segment's pieces.  When
+// every cache fits one chunk (direct mode), a wave covers its stream whole, reads the
+// position and page ids itself and writes the output rows itself: no work list and no
+// merge.
 #include <hip/hip_ext.h>
 #include <type_traits>
 #include <math.h>

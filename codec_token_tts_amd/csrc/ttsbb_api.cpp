@@ -29,7 +29,7 @@ using namespace ttsbb;
 namespace {
 
 constexpr int MAX_CHUNKS = 32;   // decode attention partials per (stream, head)
-constexpr int SEG_PER_CU = 8;    // q_len = 1 decode attention waves per CU (work-list segments)
+constexpr int SEG_PER_CU = 4;    // q_len = 1 decode attention waves per CU (work-list segments)
 constexpr int PART_STRIDE = 132; // floats per partial (m, l, 2 pad, 128 dims)
 
 // The decode step without allocation (ttsbb_decode_step_noalloc): its per-call scratch
@@ -992,9 +992,9 @@ static ttsbb_status paged_forward(ttsbb_ctx *ctx, int32_t batch, float *x, int32
     da.seg_cont = ctx->seg_cont;
     da.plan_nc = ctx->plan_nc;
     // q_len = 1 decode: the streams' pages cut into weighted segments, one wave per segment
-    // and KV head, two workgroups of four waves per CU (measured on the 64-stream workload:
-    // one or three workgroups per CU were slower); an even number of segments, so that
-    // both XCD parities get their share
+    // and KV head, one workgroup of four waves per CU (64-stream workload, µs per launch:
+    // 85.3 against 86.1 with two workgroups per CU, 87.5 with three, 126 with half a
+    // workgroup); an even number of segments, so that both XCD parities get their share
     da.target_items = prefill ? 0 : SEG_PER_CU * ctx->n_cu;
     da.n_seg = (int)std::min<int64_t>({da.target_items / Hkv, (int64_t)batch * n_chunks, SEG_MAX}) & ~1;
     if (da.n_seg < 2) da.n_seg = 2;
