@@ -32,9 +32,53 @@
 
 namespace ttsbb {
 
+constexpr int COPY_GROUPS = 16;  // prefill: workgroups per KV head copying the cached prefix
+
+// Prefill (dense_copy): the stream's cached positions before the prompt, [0, p0), from the
+// paged pool into the dense K rows and V^T (bf16).  Workgroup bx takes KV head bx % Hkv
+// and the 64-position groups bx / Hkv, + COPY_GROUPS, ...; K rows are copied in 16-byte
+// chunks, V goes through LDS so that the transposed writes (64 positions = 128 bytes per
+// dim row) are coalesced.  The prompt's own positions are written by the token blocks.
+__device__ void copy_cached_prefix(const RopeKvArgs &a, int bx) {
+    __shared__ uint16_t tile[64][128 + 8];
+    const int h = bx % a.Hkv, x = bx / a.Hkv;
+    const int p0 = min(max(a.pos[0], 0), a.s_pad - a.M);  // as the flash kernel's rows allow
+    const uint16_t *pool = reinterpret_cast<const uint16_t *>(a.pool_layer);
+    for (int t0 = x * 64; t0 < p0; t0 += COPY_GROUPS * 64) {
+        // 64 rows x 16 chunks of 16 bytes: 4 per thread, for K and for V
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int idx = threadIdx.x + 256 * c, t = idx >> 4, ch = idx & 15, p = t0 + t;
+            u32x4_t kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+            if (p < p0) {
+                const int pi = p / a.page;
+                const int pg = pi < a.max_pages ? a.page_table[pi] : -1;
+                if (pg >= 0 && pg < a.n_pages) {
+                    const int64_t base = (((int64_t)pg * 2 * a.Hkv + h) * a.page + p % a.page) * 128 + ch * 8;
+                    kv = *reinterpret_cast<const u32x4_t *>(pool + base);
+                    vv = *reinterpret_cast<const u32x4_t *>(pool + base + (int64_t)a.Hkv * a.page * 128);
+                }
+                *reinterpret_cast<u32x4_t *>(a.kbuf + ((int64_t)h * a.s_pad + p) * 128 + ch * 8) = kv;
+            }
+            *reinterpret_cast<u32x4_t *>(&tile[t][ch * 8]) = vv;
+        }
+        __syncthreads();
+        uint16_t *vt = a.vtbuf + (int64_t)h * 128 * a.s_pad;
+        for (int i = threadIdx.x; i < 128 * 64; i += 256) {
+            const int d = i >> 6, t = i & 63;
+            if (t0 + t < p0) vt[(int64_t)d * a.s_pad + t0 + t] = tile[t][d];
+        }
+        __syncthreads();
+    }
+}
+
 template <typename TKV, bool MULTI>
 __global__ __launch_bounds__(256) void rope_kv_kernel(RopeKvArgs a) {
     constexpr int MAXJ = 8;  // heads per wave per pass (MULTI: more than 4 * MAXJ heads)
+    if (a.dense_copy && (int)blockIdx.x >= a.M) {
+        copy_cached_prefix(a, blockIdx.x - a.M);
+        return;
+    }
     const int m = blockIdx.x;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int width = (a.H + 2 * a.Hkv) * 128;
@@ -124,11 +168,27 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(RopeKvArgs a) {
                 bf16_t *k = a.kbuf + ((int64_t)h * a.s_pad + m) * 128;
                 k[lane] = f32_to_bf16(x);
                 k[lane + 64] = f32_to_bf16(x2);
-            } else if (ok) {
-                TKV *dst = reinterpret_cast<TKV *>(a.pool_layer) +
-                           ((((int64_t)page_id * 2 + kv) * a.Hkv + h) * a.page + slot) * 128;
-                dst[lane] = from_f32<TKV>(x);
-                dst[lane + 64] = from_f32<TKV>(x2);
+            } else {
+                if (ok) {
+                    TKV *dst = reinterpret_cast<TKV *>(a.pool_layer) +
+                               ((((int64_t)page_id * 2 + kv) * a.Hkv + h) * a.page + slot) * 128;
+                    dst[lane] = from_f32<TKV>(x);
+                    dst[lane + 64] = from_f32<TKV>(x2);
+                }
+                // prefill: the token's K row and V^T column of the dense buffers at its
+                // position (any position below max_pos <= s_pad; the pool write above
+                // also needs a valid page)
+                if (a.dense_copy && p == pc) {
+                    if (kv == 0) {
+                        bf16_t *kd = a.kbuf + ((int64_t)h * a.s_pad + p) * 128;
+                        kd[lane] = f32_to_bf16(x);
+                        kd[lane + 64] = f32_to_bf16(x2);
+                    } else {
+                        bf16_t *vt = a.vtbuf + (int64_t)h * 128 * a.s_pad + p;
+                        vt[(int64_t)lane * a.s_pad] = f32_to_bf16(x);
+                        vt[(int64_t)(lane + 64) * a.s_pad] = f32_to_bf16(x2);
+                    }
+                }
             }
         }
     }
@@ -154,59 +214,16 @@ __global__ __launch_bounds__(256) void dense_vt_kernel(RopeKvArgs a) {
     }
 }
 
-// One stream's paged K/V -> dense K rows and V^T (bf16): block (x, h) takes the 64-position
-// groups x, x + gridDim.x, ... of KV head h below p0 + n_new; K rows are copied in 16-byte
-// chunks, V goes through LDS so that the transposed writes (64 positions = 128 bytes per
-// dim row) are coalesced.
-__global__ __launch_bounds__(256) void pool_dense_kernel(PoolDenseArgs a) {
-    __shared__ uint16_t tile[64][128 + 8];
-    const int h = blockIdx.y;
-    const int p0 = min(max(a.pos0[0], 0), a.s_pad - a.n_new);
-    const int n_keys = p0 + a.n_new;
-    const uint16_t *pool = reinterpret_cast<const uint16_t *>(a.pool_layer);
-    for (int t0 = blockIdx.x * 64; t0 < n_keys; t0 += gridDim.x * 64) {
-        // 64 rows x 16 chunks of 16 bytes: 4 per thread, for K and for V
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int idx = threadIdx.x + 256 * c, t = idx >> 4, ch = idx & 15, p = t0 + t;
-            u32x4_t kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-            if (p < n_keys) {
-                const int pi = p / a.page;
-                const int pg = pi < a.max_pages ? a.page_table[pi] : -1;
-                if (pg >= 0 && pg < a.n_pages) {
-                    const int64_t base = (((int64_t)pg * 2 * a.Hkv + h) * a.page + p % a.page) * 128 + ch * 8;
-                    kv = *reinterpret_cast<const u32x4_t *>(pool + base);
-                    vv = *reinterpret_cast<const u32x4_t *>(pool + base + (int64_t)a.Hkv * a.page * 128);
-                }
-                *reinterpret_cast<u32x4_t *>(a.kbuf + ((int64_t)h * a.s_pad + p) * 128 + ch * 8) = kv;
-            }
-            *reinterpret_cast<u32x4_t *>(&tile[t][ch * 8]) = vv;
-        }
-        __syncthreads();
-        uint16_t *vt = a.vtbuf + (int64_t)h * 128 * a.s_pad;
-        for (int i = threadIdx.x; i < 128 * 64; i += 256) {
-            const int d = i >> 6, t = i & 63;
-            if (t0 + t < n_keys) vt[(int64_t)d * a.s_pad + t0 + t] = tile[t][d];
-        }
-        __syncthreads();
-    }
-}
-
-void launch_pool_dense(const PoolDenseArgs &a, hipStream_t s) {
-    if (a.n_new <= 0 || a.n_new > a.s_pad) return;
-    const int groups = min(32, (a.s_pad + 63) / 64);
-    hipLaunchKernelGGL(pool_dense_kernel, dim3(groups, a.Hkv), dim3(256), 0, s, a);
-}
-
 void launch_rope_kv(const RopeKvArgs &a, DType kv_dt, hipStream_t s) {
     if (a.M <= 0) return;
     const bool multi = (a.dense && !a.dense_f32 ? a.H + a.Hkv : a.H + 2 * a.Hkv) > 32;
+    const dim3 grid(a.M + (a.dense_copy ? a.Hkv * COPY_GROUPS : 0));
     if (kv_dt == DT_BF16 || a.dense) {
-        if (multi) hipLaunchKernelGGL((rope_kv_kernel<bf16_t, true>), dim3(a.M), dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((rope_kv_kernel<bf16_t, false>), dim3(a.M), dim3(256), 0, s, a);
+        if (multi) hipLaunchKernelGGL((rope_kv_kernel<bf16_t, true>), grid, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((rope_kv_kernel<bf16_t, false>), grid, dim3(256), 0, s, a);
     } else {
-        if (multi) hipLaunchKernelGGL((rope_kv_kernel<float, true>), dim3(a.M), dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((rope_kv_kernel<float, false>), dim3(a.M), dim3(256), 0, s, a);
+        if (multi) hipLaunchKernelGGL((rope_kv_kernel<float, true>), grid, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((rope_kv_kernel<float, false>), grid, dim3(256), 0, s, a);
     }
     if (a.dense && !a.dense_f32)
         hipLaunchKernelGGL(dense_vt_kernel, dim3((a.M + 63) / 64, a.Hkv), dim3(256), 0, s, a);

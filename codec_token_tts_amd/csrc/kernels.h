@@ -121,6 +121,10 @@ struct RopeKvArgs {
     int q_bf16;          // decode mode: q_out gets bf16 rows (as in dense mode) instead of fp32
     int dense_f32;       // dense mode in fp32: q_out fp32 [M][H*128], K and V rows fp32
                          // [Hkv][s_pad][128] in kbuf and vtbuf (V not transposed)
+    int dense_copy;      // shared-row (prefill) mode, bf16: also the dense K rows [Hkv][s_pad][128]
+                         // and V^T [Hkv][128][s_pad] of positions [0, pos[0] + M) -- the prompt's
+                         // from its own rows, the cached prefix copied from the pool by extra
+                         // workgroups of the same launch -- for the causal flash kernel
 };
 void launch_rope_kv(const RopeKvArgs &a, DType kv_dt, hipStream_t s);
 // Dense mode fused into the q/k/v projection (g: EPI_STORE product of N = (H + 2 Hkv) *
@@ -128,20 +132,6 @@ void launch_rope_kv(const RopeKvArgs &a, DType kv_dt, hipStream_t s);
 // false (nothing launched) when the shape is not taken by the fused kernel (M <= 64).
 bool launch_qkv_dense(const GemmArgs &g, const RopeKvArgs &rk, hipStream_t s);
 
-// Bulk read of one stream's paged K/V into the dense MaskGIT-layout buffers: positions
-// [0, pos0[0] + n_new) of page-table row 0 go to kbuf [Hkv][s_pad][128] (rows) and vtbuf
-// [Hkv][128][s_pad] (transposed), bf16.  pos0 is read on the device and clamped to
-// [0, s_pad - n_new]; a position whose page id is out of range reads as zeros.
-struct PoolDenseArgs {
-    const void *pool_layer;  // [n_pages][2][Hkv][page][128] bf16
-    const int32_t *page_table;
-    int max_pages, n_pages, page, Hkv;
-    const int32_t *pos0;
-    int n_new;
-    uint16_t *kbuf, *vtbuf;
-    int s_pad;
-};
-void launch_pool_dense(const PoolDenseArgs &a, hipStream_t s);
 
 // ---- K5: split-sequence decode attention over the paged pool -----------------------
 constexpr int SEG_MAX = 2048;  // most work-list segments of a q_len = 1 decode step

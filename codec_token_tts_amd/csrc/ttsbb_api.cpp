@@ -902,22 +902,16 @@ static ttsbb_status paged_forward(ttsbb_ctx *ctx, int32_t batch, float *x, int32
             r.pool_layer = pool_l;
             r.flag = ctx->flag;
             r.shared = 1;
+            // the dense K / V^T rows of positions [0, p0 + batch) for the flash kernel: the
+            // prompt's from its own rows, the cached prefix copied from the pool, in the
+            // same launch (batch <= s_pad_cap, bf16: checked above)
+            r.dense_copy = 1;
+            r.kbuf = ctx->kbuf;
+            r.vtbuf = ctx->vtbuf;
+            r.s_pad = ctx->s_pad_cap;
             {
                 KScope k(ctx, TTSBB_K_ROPE_KV);
                 launch_rope_kv(r, ctx->dt, ctx->stream);
-                PoolDenseArgs pd = {};
-                pd.pool_layer = pool_l;
-                pd.page_table = page_table;
-                pd.max_pages = max_pages;
-                pd.n_pages = n_pages;
-                pd.page = g.kv_page;
-                pd.Hkv = Hkv;
-                pd.pos0 = positions;
-                pd.n_new = batch;
-                pd.kbuf = ctx->kbuf;
-                pd.vtbuf = ctx->vtbuf;
-                pd.s_pad = ctx->s_pad_cap;
-                launch_pool_dense(pd, ctx->stream);
             }
             FlashArgs f = {};
             f.q = reinterpret_cast<const uint16_t *>(ctx->q);

@@ -856,15 +856,18 @@ def test_rvq_decode_unaligned_tables_take_the_vector_kernel():
 # ---------------------------------------------------------------------------------------
 # Causal prefill of one stream into its paged cache
 # ---------------------------------------------------------------------------------------
-@pytest.mark.parametrize("p0,S", [(0, 5), (21, 37), (300, 64), (0, 100), (37, 130), (0, 200), (500, 512)])
+@pytest.mark.parametrize("p0,S", [(0, 5), (21, 37), (300, 64), (0, 100), (37, 130), (0, 200), (500, 512),
+                                  (2085, 70)])
 def test_prefill_bf16(p0, S):
     """bf16, 2 layers: the prompt's final residual stream, the K/V it leaves in the pool at
     positions p0..p0+S-1, the advanced cache length and the last token's head choice,
     against the oracle's prefill (which the oracle pins equal to token-by-token decode).
     Up to 64 tokens the attention is the decode kernel's, token by token; beyond, the
     causal flash kernel over the pool's positions 0..p0+S-1 (query tiles ending below,
-    at and past a 32-key block, a prefix that is not block-aligned); each is held to the
-    emulation of its own bf16 storage."""
+    at and past a 32-key block, a prefix that is not block-aligned), whose dense K / V^T
+    rows the RoPE kernel writes: the prompt's own, and the cached prefix copied from the
+    pool by extra workgroups (2085 positions: 33 groups of 64 over 16 workgroups per KV
+    head, so some take three); each is held to the emulation of its own bf16 storage."""
     shape = CFG.Shape(n_layers=2)
     m = Model(shape, 2, True, seed=17, gains="random")
     try:
