@@ -946,11 +946,12 @@ static ttsbb_status paged_forward(ttsbb_ctx *ctx, int32_t batch, float *x, int32
         return launch_failed() ? TTSBB_DEVICE_ERROR : TTSBB_OK;
     }
 
-    // Split of each stream's positions into chunks for the decode attention: 128
-    // positions per wave (measured best on the paged workload), halved while there are
-    // fewer than 256 (stream, KV head, chunk) work items (batch 1, KV ~1000: 32-position
-    // chunks, measured best against 16 and 64); the partial buffer holds
-    // max_rows * MAX_CHUNKS chunks per head, and a chunk spans at most 64 pages.
+    // The attention's chunk bound: 128 positions, halved while there are fewer than 256
+    // (stream, KV head, chunk) items (batch 1, KV ~1000: 32-position chunks).  Prefill rows
+    // take pieces of at most one chunk; in q_len = 1 decode the chunk count bounds the
+    // number of segments and sizes each stream's partial slots, and caches within one
+    // chunk take the direct mode.  The partial buffer holds max_rows * MAX_CHUNKS slots
+    // per head, and a piece spans at most 64 pages (one page id per lane).
     const int cap = max_pages * g.kv_page;
     int chunk = 128;
     while (chunk > g.kv_page && (int64_t)batch * Hkv * ((cap + chunk - 1) / chunk) < 256) chunk /= 2;

@@ -155,9 +155,9 @@ ttsbb_status ttsbb_decode_step(ttsbb_ctx *ctx, int32_t batch, float *x, int32_t 
  * library, 32 MiB on each GPU it runs on, held until the process ends, instead of the
  * context's workspace.  It allocates nothing.  Limits: batch <= 64 streams and
  * n_groups * group_vocab <= 8200 (TTSBB_UNSUPPORTED beyond; also if the context's shape
- * needs more scratch than the array holds); with max_pages * kv_page > 4096 its
- * attention may cut the caches into longer chunks than ttsbb_decode_step does (the same
- * result up to fp32 rounding order).  Every call of this entry point on one GPU shares
+ * needs more scratch than the array holds); when batch * (ceil(max_pages * kv_page /
+ * 128) + 2) > 2048 its attention may split the caches differently from
+ * ttsbb_decode_step (the same result up to fp32 rounding order).  Every call of this entry point on one GPU shares
  * that GPU's array and leaves its contents behind: calls that overlap on one GPU (other
  * streams, contexts or threads) race. */
 ttsbb_status ttsbb_decode_step_noalloc(ttsbb_ctx *ctx, int32_t batch, float *x, int32_t *positions,
