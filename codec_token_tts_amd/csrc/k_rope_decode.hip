@@ -328,9 +328,6 @@ __device__ __forceinline__ void process_page(const u32x4_t (&kr)[NR], const u32x
     }
 }
 
-// One wave per (stream, KV head, chunk).  The K and V blocks of the next page are
-// loaded into a second register set while the current page is processed, so every
-// wave keeps one page (8 KB in bf16) of loads in flight behind its arithmetic.
 // Value of dimension d +- 64 of the same head (the RoPE partner), held by the lane LPR/2
 // away inside the lane's row group.
 template <int LPR>
@@ -361,8 +358,12 @@ __device__ __forceinline__ void norm_rope_head(const float *x, const float *gain
     }
 }
 
-// One work item (stream, KV head, chunk) of the decode attention, on one wave; returns
-// false when `item` lies past the step's work list.
+// One work item of the decode attention on one wave: a piece of one stream's positions
+// (a work-list entry) for one KV head, or in direct mode the stream's whole cache.  The
+// K and V blocks of the next page are loaded into a second register set while the
+// current page is processed, so the wave keeps one page (8 KB in bf16) of loads in
+// flight behind its arithmetic.  Returns false when `pair` lies past the work list (or
+// the batch) or names an empty entry.
 template <typename T, int GROUP, bool FUSED, bool DIRECT>
 __device__ __forceinline__ bool decode_attn_item(const DecodeAttnArgs &a, int pair, int hk, int limit) {
     constexpr int EPL = KVRaw<T>::EPL;
@@ -375,11 +376,11 @@ __device__ __forceinline__ bool decode_attn_item(const DecodeAttnArgs &a, int pa
     const int d0 = (lane % LPR) * EPL;
     const int rsub = lane / LPR;
     const int cap = a.max_pages * a.page;
-    // The chunk's page ids (one per lane) come with the pair, in the same round of loads,
+    // The piece's page ids (one per lane) come with the pair, in the same round of loads,
     // and are read once: a page-id load inside the page loop would have to complete before
     // the next page's addresses exist, and loads complete in order, so that wait would also
     // drain the prefetch.
-    int b, c, p_tok, p_begin, chunk, my_page;  // p_tok: position of the step's token
+    int b, c, p_tok, p_begin, chunk, my_page;  // chunk: the piece's positions; p_tok: the step token's
     if (DIRECT) {
         // one item per (stream, KV head) over the whole cache: positions and page ids from
         // the stream's own entries, no work list
@@ -429,9 +430,9 @@ __device__ __forceinline__ bool decode_attn_item(const DecodeAttnArgs &a, int pa
 #pragma unroll
             for (int e = 0; e < EPL; ++e) x[j][e] = row[(hk * GROUP + j) * 128 + d0 + e];
     }
-    const int L = min(p_tok + 1, cap);  // the plan holds chunks below L only
+    const int L = min(p_tok + 1, cap);  // the plan holds pieces below L only
     const int p_end = min(L, p_begin + chunk);
-    // FUSED: the chunk that holds the token's slot takes the token's K / V from registers
+    // FUSED: the piece that holds the token's slot takes the token's K / V from registers
     // (rounded to the pool's type, as a read-back would give) and scans only the earlier
     // positions, so its page reads never wait for the slot's store
     const bool tok_here = FUSED && p_tok >= p_begin && p_tok < p_end;
@@ -531,7 +532,7 @@ __device__ __forceinline__ bool decode_attn_item(const DecodeAttnArgs &a, int pa
         ok_a = load_page<T, NR, RPL>(pool, page_of(pg_first), a.n_pages, a.Hkv, hk, blk, lane_off, ka, va);
     }
 
-    // Ping-pong over the chunk's pages.  Every load is issued unconditionally (the index
+    // Ping-pong over the piece's pages.  Every load is issued unconditionally (the index
     // is clamped to the last page, whose re-read hits L2) and every page is processed
     // unconditionally (an invalid page counts no valid token), so no branch forces the
     // outstanding prefetch to drain.
@@ -592,11 +593,10 @@ __device__ __forceinline__ bool decode_attn_item(const DecodeAttnArgs &a, int pa
     return true;
 }
 
-// The grid holds as many waves as the work list's budget (target_items, or every chunk
-// the caches could hold when there is no budget; in direct mode one per stream and KV
-// head within that budget); each wave takes items wave, wave + (waves in the grid), ...
-// -- one item per wave when the list fits the budget, so no workgroup is dispatched
-// without work.
+// The grid: in segment mode (q_len = 1 decode) one wave per segment and KV head; for
+// prefill rows as many waves as the chunks the caches could hold; in direct mode one per
+// stream and KV head.  Outside segment mode each wave takes items wave, wave + (waves in
+// the grid), ... until the list runs out.
 // DIRECT: a.direct (a separate instantiation, so the work-list kernels keep their
 // registers; short caches are latency-bound, so it takes the 3-wave register budget).
 template <typename T, int GROUP, bool FUSED, bool DIRECT>
@@ -990,9 +990,9 @@ __device__ __forceinline__ void combine_pass(const float *part, int c0, int n, i
     M = mn;
 }
 
-// Merge of the chunk partials of one (stream, head): one pass of up to 32 chunks, or
-// passes of 64 for streams split into more (the half-size chunks of the last streams),
-// so a stream of up to 64 chunks costs one round of loads.
+// Merge of the piece partials of one (stream, head), in piece (position) order: one pass
+// of up to 32 partials, or passes of 64 for streams split into more, so a stream of up to
+// 64 pieces costs one round of loads.
 template <typename TO>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeAttnArgs a) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
