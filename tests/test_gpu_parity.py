@@ -373,6 +373,32 @@ def test_decode_direct_short_caches(bf16, lengths, tap):
         m.close()
 
 
+@pytest.mark.parametrize("bf16,tap", [(True, None), (True, 1), (False, None)])
+def test_decode_kv_heads_not_a_multiple_of_four(bf16, tap):
+    """12 query and 6 KV heads (GQA 2), 2 layers: the q_len = 1 work list's waves take
+    (segment, KV head) pairs in the mapping for KV-head counts that are not a multiple of
+    four; five ragged streams (one at position 0) in segment mode.  Outputs (and the tapped
+    layer's intermediates) against the oracle -- fp32: 1e-4 -- and the bf16-storage
+    emulation; the positions advance."""
+    shape = CFG.Shape(n_layers=2, n_heads=12, n_kv_heads=6)
+    m = Model(shape, 2, bf16, seed=31, gains="random")
+    try:
+        lengths = [300, 1000, 37, 0, 150]
+        res, ref = run_decode(m, lengths, 31, tap_layer=tap)
+        if bf16:
+            assert normwise(res["x"], ref["x"]) <= TOL_LAYER_BF16
+            assert normwise(res["x"], ref["x_emul"]) <= TOL_EMUL_BF16
+        else:
+            assert np.max(np.abs(res["x"] - ref["x"])) <= 1e-4
+        if tap is not None:
+            rtaps = rec_as_taps(ref["rec"], len(lengths))
+            for k in rtaps:
+                assert normwise(res["taps"][k], rtaps[k]) <= TOL_LAYER_BF16, k
+        assert res["pos"].tolist() == [n + 1 for n in lengths]
+    finally:
+        m.close()
+
+
 @pytest.mark.parametrize("tap", [False, True])
 def test_decode_direct_negative_position(tap):
     """Direct mode (40 streams, caches of at most 7 pages) with one stream at position -1:
