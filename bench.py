@@ -16,10 +16,10 @@ rates: each MaskGIT product and the flash attention in TF/s and against the bf16
 the decode projections as weight-streaming GB/s, the embeddings in GB/s.
 
 Further figures, each timed on its own after the step: a guided and a guided + sampled
-MaskGIT step, a 200-token causal prefill, the codec RVQ decode of 750 frames, and the
+MaskGIT step, one whole 32-step MaskGIT generation, a 200-token causal prefill, the codec
+RVQ decode of 750 frames, the 5-layer code predictor, and the
 batch-1 decode loop (16 x 2048 codebooks, 3072 head, KV 1000, 148 steps) run eagerly and as
-one captured HIP graph.  The other workloads (batch-1 decode, the 5-layer code predictor,
-the single fp32 layer) are parity-test cases.
+one captured HIP graph.  The single fp32 layer is a parity-test case only.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-graph] [--no-extras]
                     [--copy-calibration MIB]
@@ -585,8 +585,9 @@ def run_c5c4(args, T, torch):
 
 
 def run_extras(args, T, torch, dec, mg):
-    """The figures beside the headline workload: guided and sampled MaskGIT steps, the
-    causal prefill, the RVQ decode, the code predictor and the batch-1 decode loop."""
+    """The figures beside the headline workload: guided and sampled MaskGIT steps, a whole
+    32-step MaskGIT generation, the causal prefill, the RVQ decode, the code predictor and
+    the batch-1 decode loop."""
     # Guided MaskGIT step (classifier-free guidance), timed on its own after the step
     log("timed: %d guided MaskGIT steps" % args.steps)
     mg.step_cfg(0)
@@ -608,6 +609,22 @@ def run_extras(args, T, torch, dec, mg):
     torch.cuda.synchronize()
     smp_ms = e0.elapsed_time(e1) / args.steps
 
+    # One whole MaskGIT generation: the 32 cosine-schedule steps from the initial codes,
+    # each step's codes feeding the next on the device; at the end no position is masked
+    log("timed: one 32-step MaskGIT generation")
+    n_steps = mg.e["n_steps"]
+    for i in range(n_steps):  # warm
+        mg.step(i)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(n_steps):
+        mg.step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    gen_ms = e0.elapsed_time(e1)
+    if int((mg.codes == mg.e["mask_id"]).sum().item()) != 0:
+        raise RuntimeError("positions still masked after the 32-step generation")
+
     # Causal prefill of a 200-token prompt of one stream (28 layers)
     log("timed: prefill")
     pf_ms = run_prefill(T, torch, dec, 200, args.steps)
@@ -625,6 +642,11 @@ def run_extras(args, T, torch, dec, mg):
         log("timed: batch-1 decode loop, eager and as one HIP graph")
         c2_eager_ms, c2_graph_ms = run_c2_graph(T, torch, dec)
     return {
+        "maskgit_generation": {"ms": round(gen_ms, 3), "steps": n_steps,
+                               "frames_per_s": round(mg.e["n_frames"] / (gen_ms * 1e-3), 1),
+                               "note": "one whole generation: 32 cosine-schedule steps (28-layer pass, fused "
+                                       "scoring, top-n unmasking) from the 3000-masked codes, each step's codes "
+                                       "feeding the next on the device; no position masked at the end"},
         "maskgit_cfg": {"ms_per_pass": round(cfg_ms, 4),
                         "frames_per_s": round(mg.e["n_frames"] / (cfg_ms * 1e-3 * mg.e["n_steps"]), 1),
                         "note": "guided step: conditional 950-token prompt + unconditional 750-frame window, "
